@@ -1,0 +1,105 @@
+"""NumPy model of the chunked algorithms the HIP kernels implement (test aid only).
+
+The kernels do not run token by token: they process 64-token chunks with
+matrix products.  This module states those chunk formulas in plain numpy so the
+tests can check the algebra against the oracle on the CPU, independently of
+any GPU.  It is not imported by the library and the library is not imported
+here.
+
+Delta rule (GDN / DeltaNet), one chunk of C tokens with keys K [C, dk], values
+V [C, dv], write weights b, log gates a, within-chunk inclusive prefix
+G_t = sum_{s<=t} a_s, start state S0 and start transition U0:
+    M0    = strict_lower(diag(b) K K^T)
+    N     = (I + M0)^-1                        (unit lower triangular)
+    A0    = N diag(b)
+    Abar  = Gamma o A0,  Gamma_ts = exp(G_t - G_s)  (t >= s)
+    U1    = U0 - K^T (A0 (K U0))
+    Z     = Abar (V - diag(exp(G)) K S0)
+    S1    = exp(G_C) S0 + K^T diag(exp(G_C - G)) Z
+    O     = diag(exp(G)) Q S0 + (tril(Q K^T) o Gamma) Z      (seam outputs)
+Scalar / diagonal families, per chunk:
+    S1    = diag(exp(G_C)) S0 + (K o exp(G_C - G))^T V
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def blocked_unit_lower_inverse(M, bs=16):
+    """(I + M)^-1 for strictly lower M, by 16x16 diagonal blocks (forward
+    substitution) and off-diagonal blocks N_ij = -N_ii sum_{k=j}^{i-1} M_ik N_kj."""
+    C = M.shape[0]
+    nb = C // bs
+    N = np.zeros_like(M)
+    blk = lambda i: slice(i * bs, (i + 1) * bs)
+    for i in range(nb):
+        Mi = M[blk(i), blk(i)]
+        Ni = np.zeros((bs, bs))
+        for r in range(bs):
+            Ni[r, r] = 1.0
+            for c in range(r):
+                Ni[r, c] = -Mi[r, c:r] @ Ni[c:r, c]
+        N[blk(i), blk(i)] = Ni
+    for i in range(1, nb):
+        for j in range(i):
+            T = sum(M[blk(i), blk(kk)] @ N[blk(kk), blk(j)] for kk in range(j, i))
+            N[blk(i), blk(j)] = -N[blk(i), blk(i)] @ T
+    return N
+
+
+def delta_chunk(K, V, b, a, S0, U0, Q=None, blocked=True):
+    C = K.shape[0]
+    G = np.cumsum(a)
+    M0 = np.tril(b[:, None] * (K @ K.T), -1)
+    N = blocked_unit_lower_inverse(M0) if (blocked and C % 16 == 0) else np.linalg.inv(np.eye(C) + M0)
+    A0 = N * b[None, :]
+    Gam = np.tril(np.exp(G[:, None] - G[None, :]))
+    Abar = Gam * A0
+    U1 = U0 - K.T @ (A0 @ (K @ U0))
+    Z = Abar @ (V - np.exp(G)[:, None] * (K @ S0))
+    S1 = np.exp(G[-1]) * S0 + K.T @ (np.exp(G[-1] - G)[:, None] * Z)
+    O = None
+    if Q is not None:
+        O = np.exp(G)[:, None] * (Q @ S0) + (np.tril(Q @ K.T) * Gam) @ Z
+    return S1, U1, G[-1], O
+
+
+def delta_build(k, v, b, a, C=64):
+    """Chunked build of one unit: k [L, dk], v [L, dv]; tail chunk zero-padded."""
+    L, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv))
+    U = np.eye(dk)
+    g = 0.0
+    for c0 in range(0, L, C):
+        n = min(C, L - c0)
+        K = np.zeros((C, dk)); K[:n] = k[c0:c0 + n]
+        V = np.zeros((C, dv)); V[:n] = v[c0:c0 + n]
+        bb = np.zeros(C); bb[:n] = b[c0:c0 + n]
+        aa = np.zeros(C)
+        if a is not None:
+            aa[:n] = a[c0:c0 + n]
+        S, U, gc, _ = delta_chunk(K, V, bb, aa, S, U)
+        g += gc
+    return g, U, S
+
+
+def scalar_diag_build(k, v, lg, C=64):
+    """Chunked build for scalar (lg [L]) or diagonal (lg [L, dk]) gates, or naive (lg None)."""
+    L, dk = k.shape
+    S = np.zeros((dk, v.shape[1]))
+    g = np.zeros(dk) if (lg is not None and lg.ndim == 2) else 0.0
+    for c0 in range(0, L, C):
+        K = k[c0:c0 + C]
+        V = v[c0:c0 + C]
+        if lg is None:
+            S = S + K.T @ V
+            continue
+        A = lg[c0:c0 + C]
+        G = np.cumsum(A, axis=0)
+        GC = G[-1]
+        W = np.exp(GC - G)
+        Kt = K * (W if W.ndim == 2 else W[:, None])
+        S = (np.exp(GC)[:, None] if np.ndim(GC) == 1 else np.exp(GC)) * S + Kt.T @ V
+        g = g + GC
+    return g, S

@@ -1,0 +1,63 @@
+"""The chunk formulas the kernels use, checked against the oracle in fp64 (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import SCALAR, DIAG, DELTA, NAIVE
+from segment_scan_amd import synth
+from tests import chunk_model
+
+
+def rel(a, b):
+    return np.linalg.norm(np.asarray(a) - np.asarray(b)) / max(np.linalg.norm(b), 1e-300)
+
+
+def test_blocked_inverse():
+    r = np.random.default_rng(0)
+    M = np.tril(r.standard_normal((64, 64)) * 0.1, -1)
+    N = chunk_model.blocked_unit_lower_inverse(M)
+    np.testing.assert_allclose(N @ (np.eye(64) + M), np.eye(64), atol=1e-12)
+
+
+@pytest.mark.parametrize("gate_scale", [1.0, 1.0 / 64, 0.0])
+@pytest.mark.parametrize("L", [256, 200, 64, 5])
+def test_delta_chunked_build_matches_oracle(gate_scale, L):
+    tk = synth.gdn_tiny(n_seg=1, L=L, gate_scale=gate_scale)
+    g, U, S = oracle.build_pairs(DELTA, tk.offsets, tk.k, tk.v, tk.beta, tk.log_gate)
+    gm, Um, Sm = chunk_model.delta_build(tk.k[:, 0], tk.v[:, 0], tk.beta[:, 0],
+                                          None if tk.log_gate is None else tk.log_gate[:, 0])
+    assert rel(Sm, S[0, 0]) < 1e-11
+    assert rel(Um, U[0, 0]) < 1e-11
+    assert abs(gm - g[0, 0]) < 1e-10 * max(1, abs(g[0, 0]))
+
+
+def test_delta_chunk_outputs_match_oracle_seam():
+    r = np.random.default_rng(3)
+    w, dk = 8, 16
+    tk = synth.gdn_tiny(n_seg=1, L=w)
+    k = tk.k[:, :, :dk] / np.linalg.norm(tk.k[:, :, :dk], axis=-1, keepdims=True)
+    q = r.standard_normal((w, 1, dk))
+    v = tk.v[:, :, :dk]
+    S0 = r.standard_normal((1, dk, dk))
+    res = oracle.seam(DELTA, 1, w, q, k, v, tk.beta, tk.log_gate, S_run=S0)
+    S1, _, _, O = chunk_model.delta_chunk(k[:, 0], v[:, 0], tk.beta[:, 0], tk.log_gate[:, 0], S0[0],
+                                          np.eye(dk), Q=q[:, 0], blocked=False)
+    assert rel(S1, res["S_run"][0]) < 1e-12
+    assert rel(O, res["o"][:, 0]) < 1e-12
+
+
+@pytest.mark.parametrize("fam", [NAIVE, SCALAR, DIAG])
+def test_scalar_diag_chunked_build_matches_oracle(fam):
+    if fam == DIAG:
+        tk = synth.gla(n_seg=1, L=200, n_chain=1, d=32)
+        lg = tk.log_gate[:, 0]
+    elif fam == SCALAR:
+        tk = synth.mamba2_like(n_seg=1, L=200, n_chain=1, d=32)
+        lg = tk.log_gate[:, 0]
+    else:
+        tk = synth.naive(n_seg=1, L=200, n_chain=1, d=32)
+        lg = None
+    g, _, S = oracle.build_pairs(fam, tk.offsets, tk.k, tk.v, tk.beta, tk.log_gate)
+    gm, Sm = chunk_model.scalar_diag_build(tk.k[:, 0], tk.v[:, 0], lg)
+    assert rel(Sm, S[0, 0]) < 1e-12
+    np.testing.assert_allclose(gm, g[0, 0], rtol=1e-12, atol=1e-14)
