@@ -1,0 +1,197 @@
+/*
+ * hypic.h -- C ABI of the MI355X (gfx950) library for the linear-attention hot
+ * path of position-independent caching: per-segment build of the cached pair
+ * (T_C, S(C|0)), ordered composition of cached pairs, and the seam-window step.
+ *
+ * Pages cited (by title):
+ *   [youleyou] "小红书联合北大上交提出HYPIC，位置无关缓存降低首token延迟3.25倍" (youleyou.com)
+ *   [hwlabs]   "HYPIC: 하이브리드 어텐션 LLM 서빙에서 포지션 독립적 캐싱으로 TTFT를 2.45배
+ *              낮추는 방법" (llm-wiki.hwlabs.dev)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned,
+ *    allocated and owned by the caller.  The library never allocates or frees
+ *    device memory and keeps no pointer after the call returns.  `seg_offsets`
+ *    of hypic_seg_build is the only HOST pointer.
+ *  - Calls are asynchronous: HYPIC_OK means "validated and enqueued on
+ *    `stream`" (a hipStream_t passed as void*; NULL = the null stream).  Results
+ *    are ready once the stream reaches that point.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    nonzero status means nothing was enqueued (except HYPIC_E_HIP, which
+ *    reports a failed launch).  The library never aborts or throws.  The
+ *    message of the last failure on the calling thread is in hypic_last_error().
+ *  - Non-finite input values are not checked: NaN in gives NaN out.
+ *  - Per head the state is S in R^{d_k x d_v} (d_v contiguous) and a token's
+ *    output is o_t = S_t^T q_t, taken after the token's own update.  Layers and
+ *    heads are folded into one "chain" index (chain = layer * heads + head).
+ *  - Supported sizes: d_k = d_v = d with d in {64, 128}.  Other sizes return
+ *    HYPIC_E_UNSUPPORTED.
+ *  - Token tensors are token-major, [n_tok, n_chain, d] (d contiguous);
+ *    per-token scalars are [n_tok, n_chain].
+ *
+ * Families (per-token transition A_t and write weight b_t; the pages name the
+ * families -- naive linear attention, RetNet, Mamba2, GLA, DeltaNet, GDN -- but
+ * print no per-token formula, so the standard published forms are used):
+ *   HYPIC_NAIVE  : A_t = I,                            b_t = 1
+ *   HYPIC_SCALAR : A_t = exp(lg_t) I       (RetNet, Mamba2), b_t = 1
+ *   HYPIC_DIAG   : A_t = diag(exp(lg_t))   (GLA),    b_t = 1
+ *   HYPIC_DELTA  : A_t = exp(lg_t)(I - beta_t k_t k_t^T) (DeltaNet: lg = 0; GDN),
+ *                  b_t = beta_t
+ *   and S_t = A_t S_{t-1} + b_t k_t v_t^T.
+ *
+ * Cached pair layout (fp32).  The segment transition T_C = A_L ... A_1 is kept
+ * factored so that it cannot underflow (the scalar gate commutes with the
+ * Householder-like factors):
+ *   T_C = exp(g) U  (NAIVE: g = 0, U = I; SCALAR: U = I; DELTA: U = prod(I - beta k k^T))
+ *   T_C = diag(exp(g))  (DIAG: g has d_k entries)
+ *   g : [n_seg, n_chain]  (DIAG: [n_seg, n_chain, d_k])
+ *   U : [n_seg, n_chain, d_k, d_k]  (DELTA only; NULL for the other families)
+ *   S : [n_seg, n_chain, d_k, d_v]  = S(C|0)
+ */
+#ifndef HYPIC_H
+#define HYPIC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYPIC_ABI_VERSION 1
+
+typedef enum {
+  HYPIC_OK = 0,
+  HYPIC_E_INVALID = 1,     /* malformed arguments; nothing enqueued */
+  HYPIC_E_UNSUPPORTED = 2, /* well-formed but not built (size, dtype/family combination) */
+  HYPIC_E_HIP = 3          /* the HIP runtime reported an error at launch */
+} hypic_status;
+
+typedef enum { HYPIC_NAIVE = 0, HYPIC_SCALAR = 1, HYPIC_DIAG = 2, HYPIC_DELTA = 3 } hypic_family;
+
+typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
+
+/* Token inputs (device pointers).  `dtype` applies to q, k, v, beta and
+ * log_gate, except that a per-chain SCALAR gate is always fp32. */
+typedef struct {
+  hypic_dtype dtype;
+  const void* q;        /* [n_tok, n_chain, d_k]; seam step only (NULL for builds) */
+  const void* k;        /* [n_tok, n_chain, d_k] */
+  const void* v;        /* [n_tok, n_chain, d_v] */
+  const void* beta;     /* [n_tok, n_chain]; DELTA only, NULL otherwise */
+  const void* log_gate; /* natural log of the gate, <= 0:
+                           SCALAR: [n_tok, n_chain], or fp32 [n_chain] if gate_per_chain (RetNet)
+                           DIAG  : [n_tok, n_chain, d_k]
+                           DELTA : [n_tok, n_chain], or NULL (DeltaNet, gate = 1)
+                           NAIVE : NULL */
+  int gate_per_chain;   /* SCALAR only: 1 = one constant gate per chain */
+} hypic_tokens;
+
+/* Cached pairs written by the library (layout above). */
+typedef struct {
+  float* g;
+  float* U;
+  float* S;
+} hypic_pairs;
+
+/* Cached pairs read by the library (layout above). */
+typedef struct {
+  const float* g;
+  const float* U;
+  const float* S;
+} hypic_cpairs;
+
+/*
+ * hypic_seg_build -- build (T_C, S(C|0)) of every (segment, chain) unit.
+ *
+ * [youleyou, linear-layer paragraph]: T_C is the product of all per-token
+ * transition matrices of the segment and S(C|0) its final state from a zero
+ * start; both depend only on the segment's own tokens, so every unit is built
+ * independently and all of them run concurrently.
+ * [hwlabs, section 병렬 콜드 프리필]: a segment may itself be split into pieces
+ * joined by composition; inside a unit the kernels run 64-token chunks joined
+ * the same way.
+ *
+ *   fam          family (above).
+ *   n_seg        number of segments, >= 1.
+ *   seg_offsets  HOST array of n_seg + 1 token offsets: segment s is tokens
+ *                [seg_offsets[s], seg_offsets[s+1]); seg_offsets[0] = 0 and the
+ *                offsets strictly increase (every segment has >= 1 token).
+ *                Segment lengths may differ (ragged batches).
+ *   n_chain      chains (layers x heads), >= 1.
+ *   d_k, d_v     head sizes (d_k = d_v in {64, 128}).
+ *   in           token inputs; q is ignored.
+ *   out          g, S required; U required for DELTA (NULL otherwise).  Every
+ *                output element is written.
+ *   stream       hipStream_t or NULL.
+ * Errors: HYPIC_E_INVALID for NULL required pointers, misaligned pointers,
+ * bad offsets, a field that does not match the family, or outputs that
+ * overlap inputs or each other; HYPIC_E_UNSUPPORTED for other sizes.
+ */
+hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain,
+                             int d_k, int d_v, const hypic_tokens* in, const hypic_pairs* out,
+                             void* stream);
+
+/*
+ * hypic_compose -- ordered composition of cached pairs along every chain.
+ *
+ * [youleyou, linear-layer paragraph]: S(C1.C2) = T(C2) S(C1) + S(C2), i.e.
+ * left-multiply by T_C and add; [hwlabs, section 세그먼트 누적 전이 연산자]:
+ * T_ABC = T_C T_B T_A and e_ABC = T_C (T_B e_A + e_B) + e_C.
+ * For i = 0 .. n_seg-1 (index order): S <- T_i S + S_i, starting from S_init.
+ *
+ *   in             pairs [n_seg, n_chain, ...] (layout above); U only for DELTA.
+ *   S_init         [n_chain, d_k, d_v] or NULL (zero start).
+ *   S_out          [n_chain, d_k, d_v]; may be the same pointer as S_init
+ *                  (in-place update), no other overlap.
+ *   prefix_states  NULL or [n_seg, n_chain, d_k, d_v]: the running state
+ *                  BEFORE segment i (prefix_states[0] = S_init or 0).
+ *   g_total        NULL or [n_chain] (DIAG: [n_chain, d_k]): sum of g_i.
+ *   U_total        NULL or [n_chain, d_k, d_k] (DELTA only): U_{n-1} ... U_0.
+ *                  With S_init = NULL, (g_total, U_total, S_out) is the pair
+ *                  of the concatenated segments.
+ * Errors as for hypic_seg_build.
+ */
+hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v,
+                           const hypic_cpairs* in, const float* S_init, float* S_out,
+                           float* prefix_states, float* g_total, float* U_total, void* stream);
+
+/*
+ * hypic_seam_step -- advance the running state through each segment's seam
+ * window, emitting the window tokens' outputs, then apply the segment's cached
+ * body pair.
+ *
+ * [youleyou, full-attention paragraph]: the first w tokens of each reused
+ * segment (default w = 8) are kept out of its cache entry and recomputed under
+ * the full prefix; to do so the linear layers compute the window's own T and S
+ * on the fly, advance the running state, and forward each seam token's output
+ * to the full-attention layer above.
+ * For each segment i in order: for its w window tokens t (rows i*w .. i*w+w-1
+ * of the seam tensors) S <- A_t S + b_t k_t v_t^T and o_t = S^T q_t; then, if
+ * body pairs are given, S <- T_{B_i} S + S_{B_i}.
+ *
+ *   n_seg, w       segments and window length (w >= 1).
+ *   seam           window tokens [n_seg * w, n_chain, d] (q required).
+ *   body           NULL (windows only) or cached body pairs [n_seg, n_chain, ...].
+ *   S_run          [n_chain, d_k, d_v], read and overwritten with the final state.
+ *   o_out          [n_seg * w, n_chain, d_v] fp32.
+ *   window_out     NULL, or each window's own pair (T_W, S(W|0)) written to
+ *                  g [n_seg, n_chain](DIAG: [.., d_k]), U (DELTA), S [n_seg, n_chain, d_k, d_v].
+ * Errors as for hypic_seg_build.
+ */
+hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, int d_k, int d_v,
+                             const hypic_tokens* seam, const hypic_cpairs* body, float* S_run,
+                             float* o_out, const hypic_pairs* window_out, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  The string is
+ * owned by the library and valid until the next call on this thread. */
+const char* hypic_last_error(void);
+
+/* HYPIC_ABI_VERSION of the loaded library. */
+int hypic_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYPIC_H */

@@ -1,0 +1,187 @@
+"""Thin Python binding of the C ABI in include/hypic.h (libhypic.so).
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+contiguity, their data pointers and the current HIP stream are handed to the
+library, and missing outputs are allocated with torch.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback path.  If
+the library is missing the first call raises HypicError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+import torch
+
+from .synth import NAIVE, SCALAR, DIAG, DELTA
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhypic.so")
+
+HYPIC_OK, HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_HIP = 0, 1, 2, 3
+HYPIC_F32, HYPIC_BF16 = 0, 1
+STATUS_NAMES = {0: "HYPIC_OK", 1: "HYPIC_E_INVALID", 2: "HYPIC_E_UNSUPPORTED", 3: "HYPIC_E_HIP"}
+
+
+class HypicError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), msg))
+        self.status = status
+
+
+class Tokens(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("log_gate", ctypes.c_void_p), ("gate_per_chain", ctypes.c_int)]
+
+
+class Pairs(ctypes.Structure):
+    _fields_ = [("g", ctypes.c_void_p), ("U", ctypes.c_void_p), ("S", ctypes.c_void_p)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libhypic.so and declare its entry points (no GPU needed)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise HypicError(HYPIC_E_UNSUPPORTED,
+                             "%s is not built; run `python -m segment_scan_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        lib.hypic_seg_build.argtypes = [I, I, P, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P]
+        lib.hypic_compose.argtypes = [I, I, I, I, I, ctypes.POINTER(Pairs), P, P, P, P, P, P]
+        lib.hypic_seam_step.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P, P,
+                                        ctypes.POINTER(Pairs), P]
+        for f in (lib.hypic_seg_build, lib.hypic_compose, lib.hypic_seam_step):
+            f.restype = I
+        lib.hypic_last_error.restype = ctypes.c_char_p
+        lib.hypic_last_error.argtypes = []
+        lib.hypic_abi_version.restype = I
+        _lib = lib
+        return lib
+
+
+def last_error() -> str:
+    return load_library().hypic_last_error().decode()
+
+
+def _check(status: int):
+    if status != HYPIC_OK:
+        raise HypicError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HYPIC_BF16
+    if t.dtype == torch.float32:
+        return HYPIC_F32
+    raise ValueError("token tensors must be bfloat16 or float32 (got %s)" % t.dtype)
+
+
+def _tokens(k, v, q=None, beta=None, log_gate=None, gate_per_chain=False) -> Tokens:
+    dt = _dtype_code(k)
+    for name, t in (("v", v), ("q", q), ("beta", beta)):
+        if t is not None and t.dtype != k.dtype:
+            raise ValueError("%s must have the dtype of k" % name)
+    if log_gate is not None:
+        want = torch.float32 if gate_per_chain else k.dtype
+        if log_gate.dtype != want:
+            raise ValueError("log_gate must be %s" % want)
+    return Tokens(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_gate), int(bool(gate_per_chain)))
+
+
+def _gate_shape(fam, lead, d):
+    return tuple(lead) + ((d,) if fam == DIAG else ())
+
+
+def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor, beta=None, log_gate=None,
+              gate_per_chain: bool = False, out=None, stream=None):
+    """Build (g, U, S) of every (segment, chain): k, v [n_tok, n_chain, d] on the GPU.
+
+    offsets: n_seg + 1 host integers.  Returns (g, U or None, S); `out` may pass
+    preallocated (g, U, S)."""
+    off = (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
+    n_seg = len(offsets) - 1
+    n_tok, n_chain, d = k.shape
+    if out is None:
+        dev = k.device
+        g = torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32)
+        U = torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam == DELTA else None
+        S = torch.empty((n_seg, n_chain, d, v.shape[2]), device=dev, dtype=torch.float32)
+    else:
+        g, U, S = out
+    tk = _tokens(k, v, None, beta, log_gate, gate_per_chain)
+    pr = Pairs(_ptr(g), _ptr(U), _ptr(S))
+    _check(load_library().hypic_seg_build(fam, n_seg, off, n_chain, d, v.shape[2], ctypes.byref(tk),
+                                          ctypes.byref(pr), _stream(stream)))
+    return g, U, S
+
+
+def compose(fam: int, g, U, S, S_init=None, S_out=None, prefix_states=None, g_total=None, U_total=None,
+            want_prefix: bool = False, want_total: bool = False, stream=None):
+    """Ordered composition of pairs [n_seg, n_chain, ...]; returns dict of outputs."""
+    n_seg, n_chain, dk, dv = S.shape
+    dev = S.device
+    if S_out is None:
+        S_out = torch.empty((n_chain, dk, dv), device=dev, dtype=torch.float32)
+    if want_prefix and prefix_states is None:
+        prefix_states = torch.empty((n_seg, n_chain, dk, dv), device=dev, dtype=torch.float32)
+    if want_total and g_total is None:
+        g_total = torch.empty(_gate_shape(fam, (n_chain,), dk), device=dev, dtype=torch.float32)
+    if want_total and fam == DELTA and U_total is None:
+        U_total = torch.empty((n_chain, dk, dk), device=dev, dtype=torch.float32)
+    pr = Pairs(_ptr(g), _ptr(U), _ptr(S))
+    _check(load_library().hypic_compose(fam, n_seg, n_chain, dk, dv, ctypes.byref(pr), _ptr(S_init), _ptr(S_out),
+                                        _ptr(prefix_states), _ptr(g_total), _ptr(U_total), _stream(stream)))
+    return {"S_out": S_out, "prefix": prefix_states, "g_tot": g_total, "U_tot": U_total}
+
+
+def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chain=False, body=None,
+              S_run=None, o_out=None, window_out=None, want_window_pairs=False, stream=None):
+    """Seam-window step over [n_seg * w, n_chain, d] window tokens; S_run is updated in place.
+
+    body: None or (g, U, S) cached body pairs.  Returns dict with S_run, o and window pairs."""
+    n_tok, n_chain, d = k.shape
+    if n_tok % w:
+        raise ValueError("window tokens must be n_seg * w")
+    n_seg = n_tok // w
+    dev = k.device
+    if S_run is None:
+        S_run = torch.zeros((n_chain, d, v.shape[2]), device=dev, dtype=torch.float32)
+    if o_out is None:
+        o_out = torch.empty((n_tok, n_chain, v.shape[2]), device=dev, dtype=torch.float32)
+    if want_window_pairs and window_out is None:
+        window_out = (torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32),
+                      torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam == DELTA else None,
+                      torch.empty((n_seg, n_chain, d, v.shape[2]), device=dev, dtype=torch.float32))
+    tk = _tokens(k, v, q, beta, log_gate, gate_per_chain)
+    bp = ctypes.byref(Pairs(_ptr(body[0]), _ptr(body[1]), _ptr(body[2]))) if body is not None else None
+    wp = ctypes.byref(Pairs(*[_ptr(x) for x in window_out])) if window_out is not None else None
+    _check(load_library().hypic_seam_step(fam, n_seg, w, n_chain, d, v.shape[2], ctypes.byref(tk), bp,
+                                          _ptr(S_run), _ptr(o_out), wp, _stream(stream)))
+    res = {"S_run": S_run, "o": o_out}
+    if window_out is not None:
+        res.update(wg=window_out[0], wU=window_out[1], wS=window_out[2])
+    return res

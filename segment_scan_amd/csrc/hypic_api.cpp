@@ -1,0 +1,305 @@
+// hypic_api.cpp -- the C ABI of include/hypic.h: host-side validation and
+// dispatch to the gfx950 kernels.  Every argument check runs before any HIP
+// call, so malformed calls are rejected without touching the device.
+#include "../../include/hypic.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hypic_status fail(hypic_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hypic_status ok() {
+  g_err.clear();
+  return HYPIC_OK;
+}
+
+hypic_status hip_fail(hipError_t e, const char* what) {
+  return fail(HYPIC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// outputs must not overlap inputs or each other
+hypic_status check_overlaps(const std::vector<Range>& ins, const std::vector<Range>& outs) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return fail(HYPIC_E_INVALID, "output %s overlaps input %s", outs[i].name, r.name);
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(HYPIC_E_INVALID, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+  }
+  return HYPIC_OK;
+}
+
+hypic_status check_aligned(const void* p, const char* name) {
+  if (((uintptr_t)p) & 15u) return fail(HYPIC_E_INVALID, "%s is not 16-byte aligned", name);
+  return HYPIC_OK;
+}
+
+#define TRY(x)                           \
+  do {                                   \
+    hypic_status _st = (x);              \
+    if (_st != HYPIC_OK) return _st;     \
+  } while (0)
+
+hypic_status check_common(int fam, int n_seg, int n_chain, int d_k, int d_v) {
+  if (fam < HYPIC_NAIVE || fam > HYPIC_DELTA) return fail(HYPIC_E_INVALID, "unknown family %d", fam);
+  if (n_seg < 1) return fail(HYPIC_E_INVALID, "n_seg must be >= 1 (got %d)", n_seg);
+  if (n_chain < 1) return fail(HYPIC_E_INVALID, "n_chain must be >= 1 (got %d)", n_chain);
+  if (d_k < 1 || d_v < 1) return fail(HYPIC_E_INVALID, "d_k and d_v must be >= 1");
+  if (d_k != d_v || (d_k != 64 && d_k != 128))
+    return fail(HYPIC_E_UNSUPPORTED, "only d_k = d_v in {64, 128} is built (got %d, %d)", d_k, d_v);
+  return HYPIC_OK;
+}
+
+size_t gate_len(int fam, int d) { return fam == HYPIC_DIAG ? (size_t)d : 1; }
+
+// Validates the token inputs of a build or seam call and returns their byte ranges.
+hypic_status check_tokens(int fam, const hypic_tokens* t, size_t n_tok, int n_chain, int d, bool need_q,
+                          std::vector<Range>* ranges) {
+  if (!t) return fail(HYPIC_E_INVALID, "token struct is NULL");
+  if (t->dtype != HYPIC_F32 && t->dtype != HYPIC_BF16) return fail(HYPIC_E_INVALID, "unknown dtype %d", (int)t->dtype);
+  const size_t es = t->dtype == HYPIC_F32 ? 4 : 2;
+  const size_t rows = n_tok * (size_t)n_chain;
+  if (!t->k) return fail(HYPIC_E_INVALID, "k is NULL");
+  if (!t->v) return fail(HYPIC_E_INVALID, "v is NULL");
+  if (need_q && !t->q) return fail(HYPIC_E_INVALID, "q is NULL");
+  if (fam == HYPIC_DELTA) {
+    if (!t->beta) return fail(HYPIC_E_INVALID, "beta is required for the delta family");
+  } else if (t->beta) {
+    return fail(HYPIC_E_INVALID, "beta is only defined for the delta family");
+  }
+  if (fam == HYPIC_SCALAR || fam == HYPIC_DIAG) {
+    if (!t->log_gate) return fail(HYPIC_E_INVALID, "log_gate is required for this family");
+  }
+  if (fam == HYPIC_NAIVE && t->log_gate) return fail(HYPIC_E_INVALID, "log_gate must be NULL for the naive family");
+  if (t->gate_per_chain && fam != HYPIC_SCALAR)
+    return fail(HYPIC_E_INVALID, "gate_per_chain is only defined for the scalar family");
+  TRY(check_aligned(t->k, "k"));
+  TRY(check_aligned(t->v, "v"));
+  if (need_q) TRY(check_aligned(t->q, "q"));
+  if (t->beta) TRY(check_aligned(t->beta, "beta"));
+  if (t->log_gate) TRY(check_aligned(t->log_gate, "log_gate"));
+  ranges->push_back({t->k, rows * d * es, "k"});
+  ranges->push_back({t->v, rows * d * es, "v"});
+  if (need_q) ranges->push_back({t->q, rows * d * es, "q"});
+  if (t->beta) ranges->push_back({t->beta, rows * es, "beta"});
+  if (t->log_gate) {
+    size_t bytes;
+    if (fam == HYPIC_SCALAR && t->gate_per_chain)
+      bytes = (size_t)n_chain * 4;
+    else if (fam == HYPIC_DIAG)
+      bytes = rows * d * es;
+    else
+      bytes = rows * es;
+    ranges->push_back({t->log_gate, bytes, "log_gate"});
+  }
+  return HYPIC_OK;
+}
+
+hypic_status check_cpairs(int fam, const hypic_cpairs* p, int n_seg, int n_chain, int d, const char* what,
+                          std::vector<Range>* ranges) {
+  const size_t units = (size_t)n_seg * n_chain;
+  if (!p->S) return fail(HYPIC_E_INVALID, "%s.S is NULL", what);
+  if (fam != HYPIC_NAIVE && !p->g) return fail(HYPIC_E_INVALID, "%s.g is NULL", what);
+  if (fam == HYPIC_DELTA && !p->U) return fail(HYPIC_E_INVALID, "%s.U is required for the delta family", what);
+  if (fam != HYPIC_DELTA && p->U) return fail(HYPIC_E_INVALID, "%s.U is only defined for the delta family", what);
+  TRY(check_aligned(p->S, "pairs.S"));
+  if (p->g) TRY(check_aligned(p->g, "pairs.g"));
+  if (p->U) TRY(check_aligned(p->U, "pairs.U"));
+  ranges->push_back({p->S, units * d * d * 4, "pairs.S"});
+  if (p->g) ranges->push_back({p->g, units * gate_len(fam, d) * 4, "pairs.g"});
+  if (p->U) ranges->push_back({p->U, units * d * d * 4, "pairs.U"});
+  return HYPIC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hypic_last_error(void) { return g_err.c_str(); }
+
+int hypic_abi_version(void) { return HYPIC_ABI_VERSION; }
+
+hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d_k,
+                             int d_v, const hypic_tokens* in, const hypic_pairs* out, void* stream) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  const int d = d_k;
+  if (!seg_offsets) return fail(HYPIC_E_INVALID, "seg_offsets is NULL");
+  if (seg_offsets[0] != 0) return fail(HYPIC_E_INVALID, "seg_offsets[0] must be 0 (got %d)", seg_offsets[0]);
+  for (int s = 0; s < n_seg; ++s)
+    if (seg_offsets[s + 1] <= seg_offsets[s])
+      return fail(HYPIC_E_INVALID, "seg_offsets must strictly increase (segment %d is empty or negative)", s);
+  const size_t n_tok = (size_t)seg_offsets[n_seg];
+  std::vector<Range> ins, outs;
+  TRY(check_tokens(fam, in, n_tok, n_chain, d, false, &ins));
+  if (!out) return fail(HYPIC_E_INVALID, "out is NULL");
+  if (!out->S) return fail(HYPIC_E_INVALID, "out.S is NULL");
+  if (!out->g) return fail(HYPIC_E_INVALID, "out.g is NULL");
+  if (fam == HYPIC_DELTA && !out->U) return fail(HYPIC_E_INVALID, "out.U is required for the delta family");
+  if (fam != HYPIC_DELTA && out->U) return fail(HYPIC_E_INVALID, "out.U is only defined for the delta family");
+  TRY(check_aligned(out->S, "out.S"));
+  TRY(check_aligned(out->g, "out.g"));
+  if (out->U) TRY(check_aligned(out->U, "out.U"));
+  const size_t units = (size_t)n_seg * n_chain;
+  outs.push_back({out->S, units * d * d * 4, "out.S"});
+  outs.push_back({out->g, units * gate_len(fam, d) * 4, "out.g"});
+  if (out->U) outs.push_back({out->U, units * d * d * 4, "out.U"});
+  TRY(check_overlaps(ins, outs));
+
+  const bool f32 = in->dtype == HYPIC_F32;
+  hypic::BuildArgs a;
+  a.k = in->k;
+  a.v = in->v;
+  a.beta = in->beta;
+  a.lg = in->log_gate;
+  a.g = out->g;
+  a.U = out->U;
+  a.S = out->S;
+  a.n_chain = n_chain;
+  a.gate_per_chain = in->gate_per_chain ? 1 : 0;
+  for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
+    const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
+    a.seg.n_seg = ns;
+    a.seg.seg_base = s0;
+    for (int i = 0; i <= ns; ++i) a.seg.off[i] = seg_offsets[s0 + i];
+    const int blocks = ns * n_chain;
+    hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, (hipStream_t)stream)
+                                        : hypic::launch_build_sd(fam, d, f32, a, blocks, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
+  }
+  return ok();
+}
+
+hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v, const hypic_cpairs* in,
+                           const float* S_init, float* S_out, float* prefix_states, float* g_total,
+                           float* U_total, void* stream) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  const int d = d_k;
+  if (!in) return fail(HYPIC_E_INVALID, "in is NULL");
+  std::vector<Range> ins, outs;
+  TRY(check_cpairs(fam, in, n_seg, n_chain, d, "in", &ins));
+  if (!S_out) return fail(HYPIC_E_INVALID, "S_out is NULL");
+  if (U_total && fam != HYPIC_DELTA) return fail(HYPIC_E_INVALID, "U_total is only defined for the delta family");
+  TRY(check_aligned(S_out, "S_out"));
+  if (S_init) TRY(check_aligned(S_init, "S_init"));
+  if (prefix_states) TRY(check_aligned(prefix_states, "prefix_states"));
+  if (g_total) TRY(check_aligned(g_total, "g_total"));
+  if (U_total) TRY(check_aligned(U_total, "U_total"));
+  const size_t sbytes = (size_t)n_chain * d * d * 4;
+  // S_out may be exactly S_init (in-place); any other overlap is rejected
+  if (S_init && S_init != S_out) ins.push_back({S_init, sbytes, "S_init"});
+  outs.push_back({S_out, sbytes, "S_out"});
+  if (S_init == S_out) {
+    // the in-place state must still not overlap anything else
+    if (prefix_states) ins.push_back({S_init, sbytes, "S_init"});
+  }
+  if (prefix_states) outs.push_back({prefix_states, (size_t)n_seg * sbytes, "prefix_states"});
+  if (g_total) outs.push_back({g_total, (size_t)n_chain * gate_len(fam, d) * 4, "g_total"});
+  if (U_total) outs.push_back({U_total, (size_t)n_chain * d * d * 4, "U_total"});
+  TRY(check_overlaps(ins, outs));
+
+  hypic::ComposeArgs a;
+  a.g = in->g;
+  a.U = in->U;
+  a.S = in->S;
+  a.S_init = S_init;
+  a.S_out = S_out;
+  a.prefix = prefix_states;
+  a.g_tot = g_total;
+  a.U_tot = U_total;
+  a.n_seg = n_seg;
+  a.n_chain = n_chain;
+  hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_compose_dense(d, a, (hipStream_t)stream)
+                                      : hypic::launch_compose_elem(fam, d, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hypic_compose launch");
+  return ok();
+}
+
+hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, int d_k, int d_v,
+                             const hypic_tokens* seam, const hypic_cpairs* body, float* S_run, float* o_out,
+                             const hypic_pairs* window_out, void* stream) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  const int d = d_k;
+  if (w < 1) return fail(HYPIC_E_INVALID, "w must be >= 1 (got %d)", w);
+  std::vector<Range> ins, outs;
+  const size_t n_tok = (size_t)n_seg * w;
+  TRY(check_tokens(fam, seam, n_tok, n_chain, d, true, &ins));
+  if (body) TRY(check_cpairs(fam, body, n_seg, n_chain, d, "body", &ins));
+  if (!S_run) return fail(HYPIC_E_INVALID, "S_run is NULL");
+  if (!o_out) return fail(HYPIC_E_INVALID, "o_out is NULL");
+  TRY(check_aligned(S_run, "S_run"));
+  TRY(check_aligned(o_out, "o_out"));
+  outs.push_back({S_run, (size_t)n_chain * d * d * 4, "S_run"});
+  outs.push_back({o_out, n_tok * n_chain * d * 4, "o_out"});
+  if (window_out) {
+    if (!window_out->S || (fam != HYPIC_NAIVE && !window_out->g))
+      return fail(HYPIC_E_INVALID, "window_out needs S and g");
+    if (fam == HYPIC_DELTA && !window_out->U) return fail(HYPIC_E_INVALID, "window_out.U is required for delta");
+    if (fam != HYPIC_DELTA && window_out->U) return fail(HYPIC_E_INVALID, "window_out.U is only defined for delta");
+    TRY(check_aligned(window_out->S, "window_out.S"));
+    if (window_out->g) TRY(check_aligned(window_out->g, "window_out.g"));
+    if (window_out->U) TRY(check_aligned(window_out->U, "window_out.U"));
+    const size_t units = (size_t)n_seg * n_chain;
+    outs.push_back({window_out->S, units * d * d * 4, "window_out.S"});
+    if (window_out->g) outs.push_back({window_out->g, units * gate_len(fam, d) * 4, "window_out.g"});
+    if (window_out->U) outs.push_back({window_out->U, units * d * d * 4, "window_out.U"});
+  }
+  TRY(check_overlaps(ins, outs));
+
+  hypic::SeamArgs a;
+  a.q = seam->q;
+  a.k = seam->k;
+  a.v = seam->v;
+  a.beta = seam->beta;
+  a.lg = seam->log_gate;
+  a.gate_per_chain = seam->gate_per_chain ? 1 : 0;
+  a.bg = body ? body->g : nullptr;
+  a.bU = body ? body->U : nullptr;
+  a.bS = body ? body->S : nullptr;
+  a.S_run = S_run;
+  a.o = o_out;
+  a.wg = window_out ? window_out->g : nullptr;
+  a.wU = window_out ? window_out->U : nullptr;
+  a.wS = window_out ? window_out->S : nullptr;
+  a.n_seg = n_seg;
+  a.w = w;
+  a.n_chain = n_chain;
+  hipError_t e = hypic::launch_seam(fam, d, seam->dtype == HYPIC_F32, a, (hipStream_t)stream);
+  if (e == hipErrorInvalidValue)
+    return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_step: this family/option combination is not built");
+  if (e != hipSuccess) return hip_fail(e, "hypic_seam_step launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// build_sd.hip -- segment build for the naive, scalar-decay and diagonal-gate
+// families: emits S(C|0) and the log-transition g of every (segment, chain).
+//
+// [youleyou, linear-layer paragraph] T_C is the product of the segment's
+// per-token transitions and S(C|0) its final state from a zero start.  For
+// these families the transition is (a diagonal of) exponentials of summed log
+// gates, and the zero-start state has the closed form
+//     S(C|0) = sum_t diag(exp(g - G_t)) k_t v_t^T,   g = G_L,
+// where G_t is the inclusive prefix sum of the log gates.  The kernel streams
+// 64-token chunks and joins them with the composition law of the same
+// paragraph: S <- diag(exp(G_chunk)) S + Ktil_c^T V_c, Ktil weighted to the
+// chunk end.  The chunk product is a d x 64 x d contraction over tokens, run on
+// MFMA with the decay-weighted keys split into bf16 terms (values are exact
+// bf16 inputs).
+//
+// Grid: one workgroup (4 waves) per (segment, chain) unit.  Per chunk: the
+// 64 x d key and value tiles are loaded with 16-byte loads (8 tokens x 8
+// channels per thread), transposed in registers and written to LDS as
+// [channel][token] tiles, so each MFMA operand is one 16-byte LDS read.
+#include "common.h"
+#include "../launch.h"
+
+namespace hypic {
+
+namespace {
+
+constexpr int C = 64;  // tokens per chunk
+
+template <int FAM, int D, bool IN_F32>
+__global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
+  constexpr int NTK = IN_F32 ? 3 : 2;  // bf16 terms of decay-weighted keys
+  constexpr int NTV = IN_F32 ? 3 : 1;  // bf16 terms of values (bf16 inputs are exact)
+  constexpr int NRT = D / 32;          // 32-row tiles along d
+  constexpr int TPW = NRT * NRT / 4;   // accumulator tiles per wave
+  constexpr bool DIAG = (FAM == 2);
+  constexpr bool GATED = (FAM == 1 || FAM == 2);
+
+  __shared__ __attribute__((aligned(16))) bf16_t sK[NTK][D * C];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[NTV][D * C];
+  __shared__ float sW[C];        // scalar: weight exp(G_C - G_t)
+  __shared__ float sTot[8][D];   // diag: per-8-token block sums of log gates
+  __shared__ float sGC[D];       // chunk log-transition (scalar: entry 0)
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int n_chain = a.n_chain;
+  const int u_local = blockIdx.x;
+  const int s_local = u_local / n_chain;
+  const int h = u_local % n_chain;
+  const int t_begin = a.seg.off[s_local];
+  const int t_end = a.seg.off[s_local + 1];
+  const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + h;
+
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = zero16();
+
+  double g_acc = 0.0;  // scalar: lane 0 of wave 0; diag: thread tid < D for channel tid
+
+  // staging role: threads [0, D) stage keys, [D, 2D) values; block (tb, db)
+  const bool is_k = tid < D;
+  const bool is_v = tid >= D && tid < 2 * D;
+  const int sid = is_k ? tid : tid - D;
+  const int tb = sid & 7;   // 8-token block
+  const int db = sid >> 3;  // 8-channel block
+
+  for (int c0 = t_begin; c0 < t_end; c0 += C) {
+    const int nv = min(C, t_end - c0);
+
+    // ---- gates: scalar prefix over the chunk (wave 0) -------------------------
+    if constexpr (FAM == 1) {
+      if (wave == 0) {
+        float lgt = 0.f;
+        if (lane < nv) {
+          if (a.gate_per_chain)
+            lgt = reinterpret_cast<const float*>(a.lg)[h];
+          else
+            lgt = load1<IN_F32>(a.lg, (size_t)(c0 + lane) * n_chain + h);
+        }
+        const float G = wave_incl_scan(lgt);
+        const float GC = __shfl(G, 63, 64);
+        sW[lane] = expf(GC - G);
+        if (lane == 0) {
+          sGC[0] = GC;
+          g_acc += (double)GC;
+        }
+      }
+    }
+
+    // ---- gates: diagonal prefix per channel (key-staging threads) ---------------
+    float wdiag[8][8];  // [token in block][channel in block]
+    if constexpr (DIAG) {
+      if (is_k) {
+        float run[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) run[c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = tb * 8 + r;
+          float x[8];
+          if (t < nv) {
+            load8<IN_F32>(a.lg, ((size_t)(c0 + t) * n_chain + h) * D + db * 8, x);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = 0.f;
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            run[c] += x[c];
+            wdiag[r][c] = run[c];  // local inclusive prefix
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sTot[tb][db * 8 + c] = run[c];
+      }
+      __syncthreads();
+      if (is_k) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float pre = 0.f, tot = 0.f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const float x = sTot[b][db * 8 + c];
+            tot += x;
+            if (b < tb) pre += x;
+          }
+#pragma unroll
+          for (int r = 0; r < 8; ++r) wdiag[r][c] = expf(tot - (pre + wdiag[r][c]));
+          if (tb == 0) sGC[db * 8 + c] = tot;
+        }
+      }
+    }
+    if constexpr (FAM == 1) __syncthreads();
+
+    // ---- stage keys (decay-weighted, split) and values, transposed -------------
+    if (is_k || is_v) {
+      const void* src = is_k ? a.k : a.v;
+      float x[8][8];  // [token r][channel c]
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int t = tb * 8 + r;
+        if (t < nv) {
+          load8<IN_F32>(src, ((size_t)(c0 + t) * n_chain + h) * D + db * 8, x[r]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) x[r][c] = 0.f;
+        }
+      }
+      if (is_k && GATED) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            if constexpr (DIAG)
+              x[r][c] *= wdiag[r][c];
+            else
+              x[r][c] *= sW[tb * 8 + r];
+          }
+      }
+      // column c of the block = 8 tokens of channel db*8+c -> one 16-byte LDS row chunk
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float col[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) col[r] = x[r][c];
+        const int row = db * 8 + c;
+        if (is_k) {
+          Frag<NTK> f = split8<NTK>(col);
+#pragma unroll
+          for (int i = 0; i < NTK; ++i) *reinterpret_cast<bf16x8*>(&sK[i][swz64(row, tb)]) = f.t[i];
+        } else {
+          Frag<NTV> f = split8<NTV>(col);
+#pragma unroll
+          for (int i = 0; i < NTV; ++i) *reinterpret_cast<bf16x8*>(&sV[i][swz64(row, tb)]) = f.t[i];
+        }
+      }
+    }
+    __syncthreads();
+
+    if constexpr (DIAG) {
+      if (tid < D) g_acc += (double)sGC[tid];
+    }
+
+    // ---- decay the running state to the chunk end, then add Ktil^T V ----------
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tt = wave * TPW + i;
+      const int rt = tt / NRT;
+      if constexpr (FAM == 1) {
+        const float e = expf(sGC[0]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= e;
+      } else if constexpr (DIAG) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= expf(sGC[32 * rt + acc_row(r, lane)]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < C / 16; ++ks) {
+      const int chunk = 2 * ks + (lane >> 5);
+      // all tiles of a wave share one row tile when TPW == NRT (d = 128)
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int tt = wave * TPW + i;
+        const int rt = tt / NRT, ct = tt % NRT;
+        Frag<NTK> fa;
+        Frag<NTV> fb;
+#pragma unroll
+        for (int j = 0; j < NTK; ++j)
+          fa.t[j] = *reinterpret_cast<const bf16x8*>(&sK[j][swz64(32 * rt + (lane & 31), chunk)]);
+#pragma unroll
+        for (int j = 0; j < NTV; ++j)
+          fb.t[j] = *reinterpret_cast<const bf16x8*>(&sV[j][swz64(32 * ct + (lane & 31), chunk)]);
+        mma<NTK, NTV>(acc[i], fa, fb);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- write S(C|0) and g ------------------------------------------------------
+  float* S = a.S + unit * D * D;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tt = wave * TPW + i;
+    const int rt = tt / NRT, ct = tt % NRT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[(size_t)(32 * rt + acc_row(r, lane)) * D + 32 * ct + (lane & 31)] = acc[i][r];
+  }
+  if constexpr (DIAG) {
+    if (tid < D) a.g[unit * D + tid] = (float)g_acc;
+  } else {
+    if (tid == 0) a.g[unit] = (float)g_acc;  // naive: 0
+  }
+}
+
+template <int FAM, int D, bool F32>
+hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32>), dim3(n_blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int FAM>
+hipError_t launch_fam(int d, bool f32, const BuildArgs& a, int n_blocks, hipStream_t stream) {
+  if (d == 128) return f32 ? launch_t<FAM, 128, true>(a, n_blocks, stream) : launch_t<FAM, 128, false>(a, n_blocks, stream);
+  if (d == 64) return f32 ? launch_t<FAM, 64, true>(a, n_blocks, stream) : launch_t<FAM, 64, false>(a, n_blocks, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_build_sd(int fam, int d, bool in_f32, const BuildArgs& a, int n_blocks,
+                           hipStream_t stream) {
+  switch (fam) {
+    case 0: return launch_fam<0>(d, in_f32, a, n_blocks, stream);
+    case 1: return launch_fam<1>(d, in_f32, a, n_blocks, stream);
+    case 2: return launch_fam<2>(d, in_f32, a, n_blocks, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hypic

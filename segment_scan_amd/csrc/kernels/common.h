@@ -1,0 +1,157 @@
+// common.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Matrix products run on the CDNA4 matrix cores with
+// v_mfma_f32_32x32x16_bf16 (wave64; A 32x16, B 16x32, fp32 accumulate 32x32).
+// fp32 operands are fed as sums of bf16 terms ("split-bf16"): x = t0 + t1 (+ t2),
+// each term the round-to-nearest-even bf16 of the remaining residual.  A
+// product of an NA-term by an NB-term operand keeps the term pairs with
+// i + j < max(NA, NB), which drops only products below the last kept term's
+// precision: 1 term ~ 2^-9, 2 terms ~ 2^-17, 3 terms ~ 2^-25 relative.
+//
+// Register layout of one 32x32 fp32 accumulator tile (f32x16 per lane):
+//   lane l holds column (l & 31); element r holds row
+//   8*(r >> 2) + 4*(l >> 5) + (r & 3).
+// Operand layout of one MFMA step (8 bf16 per lane):
+//   A (32 rows x 16 k): lane l holds row (l & 31), k = 8*(l >> 5) + j, j = 0..7
+//   B (16 k x 32 cols): lane l holds col (l & 31), k = 8*(l >> 5) + j.
+// The k order only has to agree between A and B, which lets an accumulator
+// tile be reused as a B operand without moving data: elements 8m .. 8m+7 of a
+// tile hold, for lane half h = l >> 5, the tile rows
+//   16m + 8*(j >> 2) + 4h + (j & 3),  j = 0..7,
+// so the matching A operand reads those k indices (two runs of 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hypic {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row of accumulator element r for this lane (column is lane & 31).
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// NT-term bf16 operand fragment.
+template <int NT>
+struct Frag {
+  bf16x8 t[NT];
+};
+
+// Split 8 fp32 values into NT bf16 terms.
+template <int NT>
+__device__ __forceinline__ Frag<NT> split8(const float (&x)[8]) {
+  Frag<NT> f;
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = x[j];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16_t h = (bf16_t)r[j];
+      f.t[i][j] = h;
+      if (i + 1 < NT) r[j] -= (float)h;
+    }
+  }
+  return f;
+}
+
+// Elements 8m .. 8m+7 of an accumulator tile as an NT-term B fragment.
+template <int NT>
+__device__ __forceinline__ Frag<NT> acc_as_b(const f32x16& acc, int m, float scale = 1.f) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = acc[8 * m + j] * scale;
+  return split8<NT>(x);
+}
+
+// acc += A * B with split operands (small products first).
+template <int NA, int NB>
+__device__ __forceinline__ void mma(f32x16& acc, const Frag<NA>& a, const Frag<NB>& b) {
+  constexpr int N = NA > NB ? NA : NB;
+#pragma unroll
+  for (int s = N - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int j = s - i;
+      if (j >= 0 && j < NB) acc = mfma32(a.t[i], b.t[j], acc);
+    }
+  }
+}
+
+// bf16 bit patterns <-> float.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Load 8 consecutive input elements (bf16 or fp32) as floats.
+template <bool IN_F32>
+__device__ __forceinline__ void load8(const void* base, size_t idx, float (&x)[8]) {
+  if constexpr (IN_F32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + idx);
+    f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+}
+
+template <bool IN_F32>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+  if constexpr (IN_F32) {
+    return reinterpret_cast<const float*>(base)[idx];
+  } else {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  }
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float y = __shfl_up(x, o, 64);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
+// LDS tile of bf16 with 64 columns (128 B rows), 16-byte column chunks
+// XOR-swizzled by (row & 7): consecutive rows read at the same logical chunk
+// hit distinct banks, and an 8-row transposed write does too.
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+}  // namespace hypic

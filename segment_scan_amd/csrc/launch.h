@@ -1,0 +1,75 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to libhypic).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hypic {
+
+// Segments handled by one launch of a build kernel; their offsets travel by
+// value in the kernel arguments (no device-side table to allocate).
+constexpr int kMaxSegPerLaunch = 240;
+
+struct SegTable {
+  int32_t off[kMaxSegPerLaunch + 1];  // token offsets of this launch's segments
+  int n_seg;                          // segments in this launch
+  int seg_base;                       // global index of the first one
+};
+
+struct BuildArgs {
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* lg;
+  float* g;
+  float* U;
+  float* S;
+  int n_chain;
+  int gate_per_chain;
+  SegTable seg;
+};
+
+struct ComposeArgs {
+  const float* g;  // [n_seg, n_chain] or [n_seg, n_chain, d] (diag)
+  const float* U;  // [n_seg, n_chain, d, d] (delta)
+  const float* S;  // [n_seg, n_chain, d, d]
+  const float* S_init;
+  float* S_out;
+  float* prefix;
+  float* g_tot;
+  float* U_tot;
+  int n_seg;
+  int n_chain;
+};
+
+struct SeamArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* lg;
+  int gate_per_chain;
+  const float* bg;  // body pairs (bS == nullptr: none)
+  const float* bU;
+  const float* bS;
+  float* S_run;
+  float* o;
+  float* wg;  // window pairs (wS == nullptr: none)
+  float* wU;
+  float* wS;
+  int n_seg;
+  int w;
+  int n_chain;
+};
+
+// fam: 0 naive, 1 scalar, 2 diag, 3 delta.  d in {64, 128}.
+hipError_t launch_build_sd(int fam, int d, bool in_f32, const BuildArgs& a, int n_blocks,
+                           hipStream_t stream);
+hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_blocks,
+                              hipStream_t stream);
+hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t stream);
+hipError_t launch_compose_dense(int d, const ComposeArgs& a, hipStream_t stream);
+// Returns hipErrorInvalidValue for combinations not built.
+hipError_t launch_seam(int fam, int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
+
+}  // namespace hypic

@@ -1,0 +1,178 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library loads on a host without a GPU; every call below is malformed, so
+the library must reject it during host-side validation, before any HIP call,
+with the documented status and a message.  Pointers are fake, aligned
+integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import threading
+
+import pytest
+
+from segment_scan_amd import api
+from segment_scan_amd.api import Pairs, Tokens
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hypic.h")
+
+INVALID, UNSUPPORTED = api.HYPIC_E_INVALID, api.HYPIC_E_UNSUPPORTED
+NAIVE, SCALAR, DIAG, DELTA = 0, 1, 2, 3
+BF16, F32 = api.HYPIC_BF16, api.HYPIC_F32
+
+# fake device addresses, 16-byte aligned, far apart (1 TiB) so nothing overlaps by accident
+A = {name: (i + 1) << 40 for i, name in enumerate(
+    ["q", "k", "v", "beta", "lg", "g", "U", "S", "Sinit", "Sout", "prefix", "gtot", "Utot", "o", "wg", "wU", "wS"])}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        from segment_scan_amd import build
+        build.build()
+    return api.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    with open(HEADER) as f:
+        text = f.read()
+    declared = set(re.findall(r"\b(hypic_[a-z_]+)\s*\(", text))
+    assert {"hypic_seg_build", "hypic_compose", "hypic_seam_step", "hypic_last_error",
+            "hypic_abi_version"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\b(hypic_[a-z_]+)\b", out))
+    assert declared <= exported, declared - exported
+    for name in declared:
+        getattr(lib, name)
+    assert lib.hypic_abi_version() == 1
+
+
+def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
+    if beta is None:
+        beta = fam == DELTA
+    if lg is None:
+        lg = fam in (SCALAR, DIAG, DELTA)
+    return Tokens(dtype, A["q"] if q else None, A["k"], A["v"], A["beta"] if beta else None,
+                  A["lg"] if lg else None, gate_per_chain)
+
+
+def pairs(fam, g=True, U=None, S=True):
+    if U is None:
+        U = fam == DELTA
+    return Pairs(A["g"] if g else None, A["U"] if U else None, A["S"] if S else None)
+
+
+def build_call(lib, fam=DELTA, n_seg=2, offsets=(0, 64, 128), n_chain=2, dk=128, dv=128, t=None, p=None):
+    off = (ctypes.c_int32 * len(offsets))(*offsets) if offsets is not None else None
+    t = toks(fam) if t is None else t
+    p = pairs(fam) if p is None else p
+    return lib.hypic_seg_build(fam, n_seg, off, n_chain, dk, dv, ctypes.byref(t), ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(fam=7), INVALID, "unknown family"),
+    (dict(n_seg=0, offsets=(0,)), INVALID, "n_seg"),
+    (dict(n_chain=0), INVALID, "n_chain"),
+    (dict(dk=96, dv=96), UNSUPPORTED, "64, 128"),
+    (dict(dk=128, dv=64), UNSUPPORTED, "64, 128"),
+    (dict(offsets=None), INVALID, "seg_offsets is NULL"),
+    (dict(offsets=(1, 64, 128)), INVALID, "seg_offsets[0]"),
+    (dict(offsets=(0, 64, 64)), INVALID, "strictly increase"),
+    (dict(offsets=(0, 70, 60)), INVALID, "strictly increase"),
+    (dict(fam=SCALAR, t=Tokens(BF16, None, A["k"], A["v"], A["beta"], A["lg"], 0), p=pairs(SCALAR)), INVALID,
+     "beta is only defined"),
+    (dict(fam=DELTA, t=toks(DELTA, beta=False)), INVALID, "beta is required"),
+    (dict(fam=DIAG, t=toks(DIAG, lg=False), p=pairs(DIAG)), INVALID, "log_gate is required"),
+    (dict(fam=NAIVE, t=toks(NAIVE, lg=True), p=pairs(NAIVE)), INVALID, "must be NULL"),
+    (dict(fam=DELTA, t=toks(DELTA, gate_per_chain=1)), INVALID, "gate_per_chain"),
+    (dict(t=Tokens(BF16, None, None, A["v"], A["beta"], A["lg"], 0)), INVALID, "k is NULL"),
+    (dict(t=Tokens(BF16, None, A["k"] + 8, A["v"], A["beta"], A["lg"], 0)), INVALID, "aligned"),
+    (dict(t=Tokens(9, None, A["k"], A["v"], A["beta"], A["lg"], 0)), INVALID, "dtype"),
+    (dict(fam=SCALAR, t=toks(SCALAR), p=pairs(SCALAR, U=True)), INVALID, "only defined for the delta"),
+    (dict(fam=DELTA, p=pairs(DELTA, U=False)), INVALID, "required for the delta"),
+    (dict(p=Pairs(A["g"], A["U"], None)), INVALID, "out.S is NULL"),
+    (dict(p=Pairs(None, A["U"], A["S"])), INVALID, "out.g is NULL"),
+    (dict(p=Pairs(A["g"], A["U"], A["k"] + 4096)), INVALID, "overlaps input k"),
+    (dict(p=Pairs(A["g"], A["S"] + 4096, A["S"])), INVALID, "overlap"),
+])
+def test_seg_build_rejects(lib, kwargs, status, msg):
+    st = build_call(lib, **kwargs)
+    assert st == status
+    assert msg in api.last_error()
+
+
+def compose_call(lib, fam=DELTA, n_seg=3, n_chain=2, d=128, p=None, S_init=None, S_out=A["Sout"], prefix=None,
+                 gtot=None, Utot=None):
+    p = pairs(fam) if p is None else p
+    return lib.hypic_compose(fam, n_seg, n_chain, d, d, ctypes.byref(p), S_init, S_out, prefix, gtot, Utot, None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(n_seg=0), INVALID, "n_seg"),
+    (dict(d=32), UNSUPPORTED, "64, 128"),
+    (dict(S_out=None), INVALID, "S_out is NULL"),
+    (dict(p=Pairs(A["g"], A["U"], None)), INVALID, "in.S is NULL"),
+    (dict(p=Pairs(None, A["U"], A["S"])), INVALID, "in.g is NULL"),
+    (dict(fam=DELTA, p=Pairs(A["g"], None, A["S"])), INVALID, "required for the delta"),
+    (dict(fam=DIAG, p=pairs(DIAG, U=True)), INVALID, "only defined for the delta"),
+    (dict(fam=SCALAR, p=pairs(SCALAR), Utot=A["Utot"]), INVALID, "U_total is only defined"),
+    (dict(S_out=A["S"] + 64), INVALID, "overlaps input pairs.S"),
+    (dict(S_init=A["Sinit"], S_out=A["Sinit"] + 16), INVALID, "overlaps input S_init"),
+    (dict(prefix=A["Sout"] + 16), INVALID, "overlap"),
+    (dict(S_init=A["Sinit"], S_out=A["Sinit"], prefix=A["Sinit"] + 1024), INVALID, "overlaps input S_init"),
+    (dict(gtot=A["gtot"] + 2), INVALID, "aligned"),
+])
+def test_compose_rejects(lib, kwargs, status, msg):
+    assert compose_call(lib, **kwargs) == status
+    assert msg in api.last_error()
+
+
+def seam_call(lib, fam=DELTA, n_seg=4, w=8, n_chain=2, d=128, t=None, body="default", S_run=A["Sinit"], o=A["o"],
+              win=None):
+    t = toks(fam, q=True) if t is None else t
+    b = pairs(fam) if body == "default" else body
+    return lib.hypic_seam_step(fam, n_seg, w, n_chain, d, d, ctypes.byref(t),
+                               ctypes.byref(b) if b is not None else None, S_run, o,
+                               ctypes.byref(win) if win is not None else None, None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(w=0), INVALID, "w must be"),
+    (dict(t=toks(DELTA, q=False)), INVALID, "q is NULL"),
+    (dict(S_run=None), INVALID, "S_run is NULL"),
+    (dict(o=None), INVALID, "o_out is NULL"),
+    (dict(o=A["k"] + 128), INVALID, "overlaps input k"),
+    (dict(S_run=A["S"]), INVALID, "overlaps input pairs.S"),
+    (dict(body=Pairs(A["g"], None, A["S"])), INVALID, "required for the delta"),
+    (dict(win=Pairs(A["wg"], None, A["wS"])), INVALID, "window_out.U"),
+    (dict(d=256), UNSUPPORTED, "64, 128"),
+])
+def test_seam_rejects(lib, kwargs, status, msg):
+    assert seam_call(lib, **kwargs) == status
+    assert msg in api.last_error()
+
+
+def test_last_error_is_per_thread(lib):
+    assert build_call(lib, fam=9) == INVALID
+    assert "unknown family" in api.last_error()
+    seen = {}
+
+    def other():
+        seen["msg"] = api.last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "unknown family" in api.last_error()
+
+
+def test_binding_requires_gpu_tensors(lib):
+    import torch
+    k = torch.zeros((4, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        api.seg_build(NAIVE, [0, 4], k, k)

@@ -1,0 +1,119 @@
+"""GPU parity: scalar / diagonal / naive segment build and elementwise compose vs the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from segment_scan_amd import api, synth
+from segment_scan_amd.synth import NAIVE, SCALAR, DIAG
+from tests.gpu_util import (TOL, announce, assert_g_close, assert_units_close, dev_f32, host,
+                            upload_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_build(tk, offsets=None):
+    offsets = tk.offsets if offsets is None else offsets
+    d = upload_tokens(tk)
+    g, U, S = api.seg_build(tk.fam, list(offsets), d["k"], d["v"], d["beta"], d["log_gate"], tk.gate_per_chain)
+    import torch
+    torch.cuda.synchronize()
+    return host(g), host(U), host(S)
+
+
+def _check_build(tk, name, offsets=None):
+    offsets = tk.offsets if offsets is None else np.asarray(offsets, np.int32)
+    announce(name, "fam", tk.fam, "dtype", tk.dtype, "chains", tk.n_chain, "segs", len(offsets) - 1, "d", tk.dk)
+    g, U, S = _run_build(tk, offsets)
+    rg, rU, rS = oracle.build_pairs(tk.fam, offsets, tk.k, tk.v, tk.beta, tk.log_gate, tk.gate_per_chain)
+    tol = TOL[tk.dtype]
+    err = assert_units_close(name + ".S", S, rS, tol)
+    assert_g_close(name + ".g", g, rg, tol)
+    return err
+
+
+def test_retnet_scalar_build_full_size():
+    """8 heads, d = 128, 16 segments x 1024 tokens, bf16, per-head gamma in [0.9, 0.9999]."""
+    tk = synth.retnet()
+    _check_build(tk, "retnet")
+
+
+def test_gla_diag_build():
+    """16 heads, d = 128, 8 of the 64 x 512-token segments, bf16, per-channel gates."""
+    tk = synth.gla(n_seg=8)
+    _check_build(tk, "gla")
+
+
+@pytest.mark.parametrize("scale", [1.0 / 16, 1.0 / 1024, 0.0])
+def test_gla_gate_scales(scale):
+    tk = synth.gla(n_seg=2, L=200, n_chain=4, gate_scale=scale)
+    _check_build(tk, "gla_scale_%g" % scale)
+
+
+def test_mamba2_scalar_per_token_gates_ragged():
+    tk = synth.mamba2_like(n_seg=4, L=256, n_chain=4)
+    offsets = synth.ragged_offsets([1, 63, 65, 871])
+    _check_build(tk, "mamba2_ragged", offsets)
+
+
+@pytest.mark.parametrize("fam,d,dtype", [(NAIVE, 128, "bf16"), (NAIVE, 64, "f32"), (SCALAR, 64, "bf16"),
+                                         (SCALAR, 128, "f32"), (DIAG, 64, "bf16"), (DIAG, 128, "f32")])
+def test_build_sizes_and_dtypes(fam, d, dtype):
+    if fam == NAIVE:
+        tk = synth.naive(n_seg=3, L=130, n_chain=3, d=d, dtype=dtype)
+    elif fam == SCALAR:
+        tk = synth.mamba2_like(n_seg=3, L=130, n_chain=3, d=d, dtype=dtype)
+    else:
+        tk = synth.gla(n_seg=3, L=130, n_chain=3, d=d, dtype=dtype)
+    _check_build(tk, "sizes")
+
+
+def test_many_segments_span_launches():
+    """More segments than one launch carries (offsets travel by value per launch)."""
+    lengths = [1 + (i * 37) % 90 for i in range(300)]
+    n_tok = sum(lengths)
+    tk = synth.naive(n_seg=1, L=n_tok, n_chain=2, d=64)
+    _check_build(tk, "many_segs", synth.ragged_offsets(lengths))
+
+
+# ----------------------------------------------------------------- compose
+
+
+def _check_compose(fam, g, U, S, S_init, name, tol):
+    import torch
+    announce(name, "fam", fam, "segs", S.shape[0], "chains", S.shape[1])
+    res = api.compose(fam, dev_f32(g), None if U is None else dev_f32(U), dev_f32(S),
+                      S_init=None if S_init is None else dev_f32(S_init), want_prefix=True, want_total=True)
+    torch.cuda.synchronize()
+    ref = oracle.compose(fam, g, U, S, S_init=S_init, want_prefix=True, want_total=True)
+    assert_units_close(name + ".S_out", host(res["S_out"]), ref["S_out"], tol, unit_dims=1)
+    assert_units_close(name + ".prefix", host(res["prefix"]), ref["prefix"], tol)
+    assert_g_close(name + ".g_tot", host(res["g_tot"]), ref["g_tot"], tol)
+
+
+@pytest.mark.parametrize("fam", [NAIVE, SCALAR, DIAG])
+def test_compose_elementwise_on_oracle_pairs(fam):
+    """Composing fp32 pairs is an fp32-class operation (1e-5)."""
+    if fam == SCALAR:
+        tk = synth.retnet(n_seg=16, L=64)
+    elif fam == DIAG:
+        tk = synth.gla(n_seg=64, L=16, n_chain=16)
+    else:
+        tk = synth.naive(n_seg=8, L=32, n_chain=4)
+    g, U, S = oracle.build_pairs(fam, tk.offsets, tk.k, tk.v, tk.beta, tk.log_gate, tk.gate_per_chain)
+    g32 = g.astype(np.float32).astype(np.float64)
+    S32 = S.astype(np.float32).astype(np.float64)
+    S_init = np.random.default_rng(1).standard_normal(S.shape[1:]).astype(np.float32).astype(np.float64)
+    _check_compose(fam, g32, None, S32, S_init, "compose_elem", 1e-5)
+    _check_compose(fam, g32[:1], None, S32[:1], None, "compose_elem_one_seg", 1e-5)
+
+
+def test_retnet_build_then_compose_matches_sequential():
+    """End to end: GPU build of all 16 segments, GPU compose, vs straight recurrence."""
+    import torch
+    tk = synth.retnet(n_seg=16, L=1024)
+    d = upload_tokens(tk)
+    g, U, S = api.seg_build(SCALAR, list(tk.offsets), d["k"], d["v"], None, d["log_gate"], True)
+    res = api.compose(SCALAR, g, None, S)
+    torch.cuda.synchronize()
+    Sseq, _ = oracle.sequential(SCALAR, tk.k, tk.v, None, tk.log_gate, True)
+    assert_units_close("retnet_e2e", host(res["S_out"]), Sseq, TOL["bf16"], unit_dims=1)

@@ -1,0 +1,48 @@
+"""GPU parity: dense (delta-family) ordered composition vs the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from segment_scan_amd import api, synth
+from segment_scan_amd.synth import DELTA
+from tests.gpu_util import announce, assert_g_close, assert_units_close, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(g, U, S, S_init, name, tol=1e-5, want_total=True):
+    import torch
+    announce(name, "segs", S.shape[0], "chains", S.shape[1], "d", S.shape[2])
+    res = api.compose(DELTA, dev_f32(g), dev_f32(U), dev_f32(S),
+                      S_init=None if S_init is None else dev_f32(S_init), want_prefix=True,
+                      want_total=want_total)
+    torch.cuda.synchronize()
+    ref = oracle.compose(DELTA, g, U, S, S_init=S_init, want_prefix=True, want_total=want_total)
+    assert_units_close(name + ".S_out", host(res["S_out"]), ref["S_out"], tol, unit_dims=1)
+    assert_units_close(name + ".prefix", host(res["prefix"]), ref["prefix"], tol)
+    if want_total:
+        assert_g_close(name + ".g_tot", host(res["g_tot"]), ref["g_tot"], tol)
+        assert_units_close(name + ".U_tot", host(res["U_tot"]), ref["U_tot"], tol, unit_dims=1)
+
+
+def test_compose_dense_random_pairs_warm_layer():
+    """Random cached pairs of the warm-reuse recipe (g = 0, U ~ N(0, 1/(4d)), S ~ N(0,1)):
+    each step roughly halves ||S||, so every step is numerically non-trivial."""
+    g, U, S = synth.warm_pairs_layer(0, n_seg=24, n_head=6)
+    _check(g, U, S, None, "warm_pairs")
+
+
+def test_compose_dense_gated_built_pairs_with_init():
+    """Pairs from the oracle's build of slow-gated GDN tokens (T not negligible)."""
+    tk = synth.gdn_cold(n_seg=6, L=64, n_chain=4, gate_scale=1.0 / 64)
+    g, U, S = oracle.build_pairs(DELTA, tk.offsets, tk.k, tk.v, tk.beta, tk.log_gate)
+    f32 = lambda x: x.astype(np.float32).astype(np.float64)
+    S_init = f32(np.random.default_rng(2).standard_normal(S.shape[1:]))
+    _check(f32(g), f32(U), f32(S), S_init, "gated_pairs")
+
+
+def test_compose_dense_d64_one_segment():
+    g, U, S = synth.warm_pairs_layer(1, n_seg=1, n_head=3, d=64)
+    _check(g, U, S, None, "d64_one")
+    g, U, S = synth.warm_pairs_layer(2, n_seg=5, n_head=3, d=64)
+    _check(g, U, S, None, "d64_five", want_total=False)
