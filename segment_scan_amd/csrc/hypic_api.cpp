@@ -276,6 +276,9 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
     if (window_out->U) outs.push_back({window_out->U, units * d * d * 4, "window_out.U"});
   }
   TRY(check_overlaps(ins, outs));
+  if (!hypic::seam_supported(fam, d, window_out != nullptr))
+    return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_step: family %d%s is not built", (int)fam,
+                window_out ? " with window pairs" : "");
 
   hypic::SeamArgs a;
   a.q = seam->q;
@@ -296,8 +299,6 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   a.w = w;
   a.n_chain = n_chain;
   hipError_t e = hypic::launch_seam(fam, d, seam->dtype == HYPIC_F32, a, (hipStream_t)stream);
-  if (e == hipErrorInvalidValue)
-    return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_step: this family/option combination is not built");
   if (e != hipSuccess) return hip_fail(e, "hypic_seam_step launch");
   return ok();
 }

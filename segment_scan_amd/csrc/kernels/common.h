@@ -36,6 +36,16 @@ typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// A copy of `x` the optimiser cannot see through.  Per-lane indices are taken
+// through this at the top of a long loop so that values derived from them
+// (addresses, masks) are recomputed where used instead of being hoisted out of
+// the loop and kept live -- in the kernels that hold a large state in
+// registers that hoisting costs more registers than it saves instructions.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {

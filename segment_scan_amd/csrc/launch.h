@@ -69,7 +69,8 @@ hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_bloc
                               hipStream_t stream);
 hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t stream);
 hipError_t launch_compose_dense(int d, const ComposeArgs& a, hipStream_t stream);
-// Returns hipErrorInvalidValue for combinations not built.
+// Whether the seam step is built for this family / size / option.
+bool seam_supported(int fam, int d, bool window_pairs);
 hipError_t launch_seam(int fam, int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 
 }  // namespace hypic

@@ -1,0 +1,107 @@
+"""GPU parity: delta-rule (DeltaNet / GDN) segment build vs the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from segment_scan_amd import api, synth
+from segment_scan_amd.synth import DELTA
+from tests.gpu_util import TOL, announce, assert_g_close, assert_units_close, host, upload_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_build(tk, offsets=None):
+    import torch
+    offsets = tk.offsets if offsets is None else offsets
+    d = upload_tokens(tk)
+    g, U, S = api.seg_build(DELTA, list(offsets), d["k"], d["v"], d["beta"], d["log_gate"])
+    torch.cuda.synchronize()
+    return g, U, S
+
+
+def check_build(tk, name, offsets=None):
+    offsets = tk.offsets if offsets is None else np.asarray(offsets, np.int32)
+    announce(name, "dtype", tk.dtype, "chains", tk.n_chain, "segs", len(offsets) - 1, "d", tk.dk)
+    g, U, S = gpu_build(tk, offsets)
+    rg, rU, rS = oracle.build_pairs(DELTA, offsets, tk.k, tk.v, tk.beta, tk.log_gate)
+    tol = TOL[tk.dtype]
+    eS = assert_units_close(name + ".S", host(S), rS, tol)
+    eU = assert_units_close(name + ".U", host(U), rU, tol)
+    assert_g_close(name + ".g", host(g), rg, tol)
+    print("  max rel err S %.2e U %.2e" % (eS, eU), flush=True)
+    return g, U, S
+
+
+@pytest.mark.parametrize("gate_scale", [1.0, 1.0 / 64, 0.0])
+def test_gdn_tiny_fp32(gate_scale):
+    """1 head, d = 64, 4 x 256 tokens, fp32 (fp32 tolerance); slow-gate variants keep T_C non-negligible."""
+    tk = synth.gdn_tiny(gate_scale=gate_scale)
+    check_build(tk, "gdn_tiny_%g" % gate_scale)
+
+
+def test_gdn_tiny_fp32_compose_vs_sequential():
+    import torch
+    tk = synth.gdn_tiny(gate_scale=1.0 / 64)
+    g, U, S = gpu_build(tk)
+    res = api.compose(DELTA, g, U, S)
+    torch.cuda.synchronize()
+    Sseq, _ = oracle.sequential(DELTA, tk.k, tk.v, tk.beta, tk.log_gate)
+    assert_units_close("gdn_tiny_e2e", host(res["S_out"]), Sseq, TOL["f32"], unit_dims=1)
+
+
+def test_gdn_cold_bf16_reduced():
+    """32 heads, d = 128, 4 of the 64 x 512-token segments, bf16."""
+    tk = synth.gdn_cold(n_seg=4)
+    check_build(tk, "gdn_cold_4seg")
+
+
+@pytest.mark.parametrize("gate_scale", [1.0 / 64, 0.0])
+def test_gdn_cold_slow_gates(gate_scale):
+    tk = synth.gdn_cold(n_seg=2, n_chain=4, gate_scale=gate_scale)
+    check_build(tk, "gdn_slow_%g" % gate_scale)
+
+
+def test_gdn_ragged_segments():
+    """Segment lengths that are not multiples of the 64-token chunk, incl. 1 token."""
+    lengths = [1, 63, 64, 65, 200, 130]
+    tk = synth.gdn_cold(n_seg=1, L=sum(lengths), n_chain=3, gate_scale=1.0 / 16)
+    check_build(tk, "gdn_ragged", synth.ragged_offsets(lengths))
+
+
+def test_gdn_d64_bf16_and_d128_fp32():
+    tk = synth.gdn_cold(n_seg=3, L=100, n_chain=2, d=64)
+    check_build(tk, "gdn_d64_bf16")
+    tk = synth.gdn_cold(n_seg=2, L=100, n_chain=2, d=128, dtype="f32", gate_scale=1.0 / 16)
+    check_build(tk, "gdn_d128_f32")
+
+
+def test_gdn_cold_full_size_sampled_units():
+    """The 32k-token cold request at full size (32 heads x 64 segments x 512), in
+    the launch the benchmark times; the oracle recomputes a sample of units one by one."""
+    tk = synth.gdn_cold()
+    announce("gdn_cold_full", "units", 64 * 32)
+    g, U, S = gpu_build(tk)
+    g, U, S = host(g), host(U), host(S)
+    rng = np.random.default_rng(0)
+    units = [(0, 0), (63, 31), (31, 7)] + [tuple(x) for x in zip(rng.integers(0, 64, 9), rng.integers(0, 32, 9))]
+    for s, hh in units:
+        sub = tk.chains([hh])
+        t0, t1 = tk.offsets[s], tk.offsets[s + 1]
+        rg, rU, rS = oracle.build_pairs(DELTA, np.array([0, t1 - t0], np.int32), sub.k[t0:t1], sub.v[t0:t1],
+                                        sub.beta[t0:t1], sub.log_gate[t0:t1])
+        assert_units_close("full.S(%d,%d)" % (s, hh), S[s:s + 1, hh:hh + 1], rS, TOL["bf16"])
+        assert_units_close("full.U(%d,%d)" % (s, hh), U[s:s + 1, hh:hh + 1], rU, TOL["bf16"])
+        assert_g_close("full.g(%d,%d)" % (s, hh), g[s, hh], rg[0, 0], TOL["bf16"])
+
+
+def test_gdn_build_then_compose_matches_sequential():
+    """Cold path end to end on the GPU (build of every segment, ordered compose)
+    against straight recurrence over the whole request, slow gates so that
+    every segment's T_C matters."""
+    import torch
+    tk = synth.gdn_cold(n_seg=8, L=256, n_chain=4, gate_scale=1.0 / 64)
+    g, U, S = gpu_build(tk)
+    res = api.compose(DELTA, g, U, S)
+    torch.cuda.synchronize()
+    Sseq, _ = oracle.sequential(DELTA, tk.k, tk.v, tk.beta, tk.log_gate)
+    assert_units_close("gdn_e2e", host(res["S_out"]), Sseq, TOL["bf16"], unit_dims=1)
