@@ -1,0 +1,370 @@
+"""Benchmark of the linear-attention hot path of position-independent caching on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the hot path over one batch of synthetic input already
+resident in HBM.  The default workload is one 32k-token cold request of a GDN
+layer: 32 heads, d = 128, 64 segments x 512 tokens, bf16 tokens with fp32
+accumulation -- every (segment, head) pair (T_C, S(C|0)) built concurrently
+(hypic_seg_build), then the 64 pairs of every head composed in order
+(hypic_compose).  Other workloads (`--workload`):
+  retnet        8 heads x 16 segments x 1024, scalar decay: build + compose
+  gla           16 heads x 64 segments x 512, diagonal gates: build + compose
+  gdn_warm100k  30 layers x 16 heads, 196 cached segments, w = 8: seam step fused
+                with the composition of every cached body pair
+Prints one JSON line.  `value` is segment-tokens/s of the whole step; the
+`roofline` object is for the step's dominant kernel, timed with HIP events on
+the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "segment-tokens/s for (T_C,S) build + composed segs/s; % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "build_delta": "segment_scan_amd/csrc/kernels/build_delta.hip",
+    "build_sd": "segment_scan_amd/csrc/kernels/build_sd.hip",
+    "seam": "segment_scan_amd/csrc/kernels/seam.hip",
+    "compose": "segment_scan_amd/csrc/kernels/compose.hip",
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[kernel], "segment_scan_amd/csrc/kernels/common.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
+    taken on the current source of the kernel; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel") != kernel or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def to_dev(arr, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+# ------------------------------------------------------------------ workloads
+
+
+class Workload:
+    name = ""
+    kernel = ""          # dominant kernel for the roofline
+    tokens = 0           # segment-tokens per step
+    composed = 0         # composed segments per step (per chain-group, see config)
+
+    def setup(self):
+        raise NotImplementedError
+
+    def step(self, ev0, ev1):
+        """Enqueue one step; records ev0/ev1 around the dominant kernel."""
+        raise NotImplementedError
+
+    def cpu_sample(self):
+        """Run the oracle on a bounded sample; returns (seconds, sample tokens, description)."""
+        raise NotImplementedError
+
+
+def _build_bytes(fam, L, d, es, gate_bytes_per_tok, u_out):
+    per_tok = 2 * d * es + gate_bytes_per_tok
+    out = d * d * 4 * (2 if u_out else 1) + 4 * (d if fam == 2 else 1)
+    return L * per_tok + out
+
+
+class ColdRequest(Workload):
+    """GDN dense transition, one 32k-token cold request (32 heads, 64 x 512, bf16)."""
+    name = "gdn_cold32k"
+    kernel = "build_delta"
+
+    def __init__(self):
+        self.n_seg, self.L, self.H, self.d = 64, 512, 32, 128
+        self.tokens = self.n_seg * self.L
+        self.composed = self.n_seg
+        units = self.n_seg * self.H
+        self.alg_bytes = units * _build_bytes(3, self.L, self.d, 2, 4, True)
+        self.alg_flops = units * 8.0 * self.L * self.d ** 2
+        # executed MFMA flops of the chunked kernel: per 64-token chunk per unit,
+        # Gram 3 tiles x 8 steps, and per wave (4 waves) K Z 64, A Y 36, K^T X 64
+        # 32x32x16 MFMAs (split-bf16 terms included)
+        chunks = units * (self.L // 64)
+        self.exec_flops = chunks * (24 + 4 * (64 + 36 + 64)) * 32 * 32 * 16 * 2.0
+
+    def setup(self):
+        import torch
+        from segment_scan_amd import api, synth
+        self.api, self.synth = api, synth
+        tk = synth.gdn_cold(want_q=False)
+        self.tk = tk
+        self.k, self.v = to_dev(tk.k, "bf16"), to_dev(tk.v, "bf16")
+        self.beta, self.lg = to_dev(tk.beta, "bf16"), to_dev(tk.log_gate, "bf16")
+        self.offsets = [int(x) for x in tk.offsets]
+        dev = "cuda"
+        self.g = torch.empty((self.n_seg, self.H), device=dev)
+        self.U = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
+        self.S = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
+        self.S_out = torch.empty((self.H, self.d, self.d), device=dev)
+
+    def step(self, ev0, ev1):
+        from segment_scan_amd.synth import DELTA
+        ev0.record()
+        self.api.seg_build(DELTA, self.offsets, self.k, self.v, self.beta, self.lg, out=(self.g, self.U, self.S))
+        ev1.record()
+        self.api.compose(DELTA, self.g, self.U, self.S, S_out=self.S_out)
+
+    def cpu_sample(self):
+        import oracle
+        from segment_scan_amd.synth import DELTA
+        ns = self.n_seg  # the whole request: every segment and head, built and composed
+        t1 = int(self.tk.offsets[ns])
+        sl = slice(0, t1)
+        t = time.perf_counter()
+        g, U, S = oracle.build_pairs(DELTA, self.tk.offsets[:ns + 1], self.tk.k[sl], self.tk.v[sl],
+                                     self.tk.beta[sl], self.tk.log_gate[sl])
+        oracle.compose(DELTA, g, U, S)
+        dt = time.perf_counter() - t
+        return dt, ns * self.L, "whole request (64 segments x 32 heads = 2048 units): build + ordered compose"
+
+    def config(self):
+        return {"workload": self.name, "family": "gdn", "heads": self.H, "d": self.d, "segments": self.n_seg,
+                "segment_len": self.L, "tokens": self.tokens, "inputs": "bf16", "accumulate": "fp32",
+                "step": "hypic_seg_build (2048 units) + hypic_compose (32 chains x 64)"}
+
+
+class ScalarOrDiag(Workload):
+    def __init__(self, name, fam, n_seg, L, H, d):
+        self.name, self.fam = name, fam
+        self.kernel = "build_sd"
+        self.n_seg, self.L, self.H, self.d = n_seg, L, H, d
+        self.tokens = n_seg * L
+        self.composed = n_seg
+        units = n_seg * H
+        gate = 2 * d if fam == 2 else 0
+        self.alg_bytes = units * _build_bytes(fam, L, d, 2, gate, False)
+        self.alg_flops = units * 2.0 * L * d ** 2
+        self.exec_flops = self.alg_flops * 2  # decay-weighted keys in two bf16 terms
+
+    def setup(self):
+        import torch
+        from segment_scan_amd import api, synth
+        self.api = api
+        tk = synth.retnet() if self.fam == 1 else synth.gla()
+        tk.q = None
+        self.tk = tk
+        self.k, self.v = to_dev(tk.k, "bf16"), to_dev(tk.v, "bf16")
+        if tk.gate_per_chain:
+            self.lg = to_dev(tk.log_gate, "f32")
+        else:
+            self.lg = to_dev(tk.log_gate, "bf16")
+        self.offsets = [int(x) for x in tk.offsets]
+        dev = "cuda"
+        gshape = (self.n_seg, self.H, self.d) if self.fam == 2 else (self.n_seg, self.H)
+        self.g = torch.empty(gshape, device=dev)
+        self.S = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
+        self.S_out = torch.empty((self.H, self.d, self.d), device=dev)
+
+    def step(self, ev0, ev1):
+        ev0.record()
+        self.api.seg_build(self.fam, self.offsets, self.k, self.v, None, self.lg, self.tk.gate_per_chain,
+                           out=(self.g, None, self.S))
+        ev1.record()
+        self.api.compose(self.fam, self.g, None, self.S, S_out=self.S_out)
+
+    def cpu_sample(self):
+        import oracle
+        ns = self.n_seg
+        t1 = int(self.tk.offsets[ns])
+        sl = slice(0, t1)
+        lg = self.tk.log_gate if self.tk.gate_per_chain else self.tk.log_gate[sl]
+        t = time.perf_counter()
+        g, U, S = oracle.build_pairs(self.fam, self.tk.offsets[:ns + 1], self.tk.k[sl], self.tk.v[sl], None, lg,
+                                     self.tk.gate_per_chain)
+        oracle.compose(self.fam, g, U, S)
+        dt = time.perf_counter() - t
+        return dt, ns * self.L, "whole workload (%d segments x %d heads): build + ordered compose" % (
+            self.n_seg, self.H)
+
+    def config(self):
+        return {"workload": self.name, "family": "retnet" if self.fam == 1 else "gla", "heads": self.H, "d": self.d,
+                "segments": self.n_seg, "segment_len": self.L, "tokens": self.tokens, "inputs": "bf16",
+                "accumulate": "fp32", "step": "hypic_seg_build + hypic_compose"}
+
+
+class WarmRequest(Workload):
+    """Warm reuse of a 100k-token request: 30 GDN layers x 16 heads, 196 cached segments, w = 8."""
+    name = "gdn_warm100k"
+    kernel = "seam"
+
+    def __init__(self):
+        from segment_scan_amd import synth
+        self.layers, self.H, self.n_seg, self.w, self.d = (synth.WARM_LAYERS, synth.WARM_HEADS, synth.WARM_SEGS,
+                                                           synth.WARM_W, synth.WARM_D)
+        self.chains = self.layers * self.H
+        self.tokens = self.n_seg * (512 + self.w)
+        self.composed = self.n_seg * self.layers  # (layer, segment) compositions
+        d, n = self.d, self.chains
+        ntok = self.n_seg * self.w
+        self.alg_bytes = (self.n_seg * n * (2 * d * d * 4 + 4) + ntok * n * (3 * d * 2 + 4) + ntok * n * d * 4
+                          + 2 * n * d * d * 4)
+        self.alg_flops = self.n_seg * n * 2.0 * d ** 3 + ntok * n * 6.0 * d * d
+        self.exec_flops = self.n_seg * n * 6 * 2.0 * d ** 3 + ntok * n * 6.0 * d * d * 2
+
+    def setup(self):
+        import torch
+        from segment_scan_amd import api, synth
+        self.api, self.synth = api, synth
+        H, d, n_seg, w, n = self.H, self.d, self.n_seg, self.w, self.chains
+        # seam tokens and pairs of every layer from the seeded recipe, drawn on the GPU
+        gen = torch.Generator(device="cuda").manual_seed(20260701)
+        nt = n_seg * w
+        f = torch.nn.functional
+        self.q = f.normalize(torch.randn((nt, n, d), device="cuda", generator=gen), dim=-1).to(torch.bfloat16)
+        self.k = f.normalize(torch.randn((nt, n, d), device="cuda", generator=gen), dim=-1).to(torch.bfloat16)
+        self.v = torch.randn((nt, n, d), device="cuda", generator=gen).to(torch.bfloat16)
+        self.beta = torch.sigmoid(torch.randn((nt, n), device="cuda", generator=gen)).to(torch.bfloat16)
+        self.lg = (-f.softplus(torch.randn((nt, n), device="cuda", generator=gen)) / 8).to(torch.bfloat16)
+        self.U = torch.randn((n_seg, n, d, d), device="cuda", generator=gen) * (0.5 / np.sqrt(d))
+        self.S = torch.randn((n_seg, n, d, d), device="cuda", generator=gen)
+        self.g = torch.zeros((n_seg, n), device="cuda")
+        self.S_run = torch.zeros((n, d, d), device="cuda")
+        self.o = torch.empty((nt, n, d), device="cuda")
+
+    def step(self, ev0, ev1):
+        from segment_scan_amd.synth import DELTA
+        self.S_run.zero_()
+        ev0.record()
+        self.api.seam_step(DELTA, self.w, self.q, self.k, self.v, self.beta, self.lg, body=(self.g, self.U, self.S),
+                           S_run=self.S_run, o_out=self.o)
+        ev1.record()
+
+    def cpu_sample(self):
+        import oracle
+        from segment_scan_amd import synth
+        from segment_scan_amd.synth import DELTA
+        n_layers = 2  # layers 0 and 1 in full (196 segments x 16 heads each)
+        dt = 0.0
+        for layer in range(n_layers):
+            tk = synth.warm_seam_layer(layer)
+            body = synth.warm_pairs_layer(layer)
+            t = time.perf_counter()
+            oracle.seam(DELTA, self.n_seg, self.w, tk.q, tk.k, tk.v, tk.beta, tk.log_gate, body=body)
+            dt += time.perf_counter() - t
+        # the sample is n_layers / 30 of the request's work
+        return dt, self.tokens * n_layers / self.layers, "layers 0-1 of 30 in full (seam + compose), scaled"
+
+    def config(self):
+        return {"workload": self.name, "family": "gdn", "layers": self.layers, "heads": self.H, "d": self.d,
+                "segments": self.n_seg, "w": self.w, "tokens": self.tokens, "pairs": "fp32", "seam_inputs": "bf16",
+                "step": "hypic_seam_step over 480 chains (seam windows + body-pair composition)"}
+
+
+WORKLOADS = {
+    "gdn_cold32k": ColdRequest,
+    "retnet": lambda: ScalarOrDiag("retnet", 1, 16, 1024, 8, 128),
+    "gla": lambda: ScalarOrDiag("gla", 2, 64, 512, 16, 128),
+    "gdn_warm100k": WarmRequest,
+}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gdn_cold32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the method's multi-worker form "
+              "is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]()
+    print("[bench] setting up %s" % wl.name, file=sys.stderr, flush=True)
+    wl.setup()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps + args.warmup)]
+    for i in range(args.warmup):
+        wl.step(*evs[i])
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step(*evs[args.warmup + i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs[args.warmup:]]
+    k_ms = float(np.mean(kern_ms))
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    if args.copy_calibration:
+        n = (1 << 30) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    value = wl.tokens / (ms_per_step / 1e3)
+    achieved = wl.alg_bytes / (k_ms / 1e3) / 1e9
+    traffic = measured_traffic(wl.name, wl.kernel)
+    roofline = {"bound": "hbm", "kernel": wl.kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": wl.alg_bytes, "kernel_ms": round(k_ms, 4),
+                "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 4),
+                "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 4),
+                "mfma_alg_tflops": round(wl.alg_flops / (k_ms / 1e3) / 1e12, 1),
+                "mfma_exec_tflops": round(wl.exec_flops / (k_ms / 1e3) / 1e12, 1),
+                "mfma_exec_frac": round(wl.exec_flops / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
+        dt, tokens, desc = wl.cpu_sample()
+        cpu = {"value": round(tokens / dt, 2), "unit": "segment-tokens/s", "cores": oracle.max_threads(),
+               "kind": "oracle", "sample": desc, "seconds": round(dt, 2)}
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "segment-tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": wl.config(),
+           "composed_segs_per_s": round(wl.composed / (ms_per_step / 1e3), 1),
+           "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

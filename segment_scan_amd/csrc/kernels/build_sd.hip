@@ -26,6 +26,42 @@ namespace {
 
 constexpr int C = 64;  // tokens per chunk
 
+// Raw (unconverted) 8 consecutive input elements: 16 bytes of bf16 or 32 of fp32.
+template <bool IN_F32>
+struct Raw8 {
+  uint4 w[IN_F32 ? 2 : 1];
+};
+
+template <bool IN_F32>
+__device__ __forceinline__ Raw8<IN_F32> ldraw8(const void* base, size_t idx, bool valid) {
+  Raw8<IN_F32> r;
+  if constexpr (IN_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + idx);
+    r.w[0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
+    r.w[1] = valid ? p[1] : make_uint4(0, 0, 0, 0);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    r.w[0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
+  }
+  return r;
+}
+
+template <bool IN_F32>
+__device__ __forceinline__ void cvt8(const Raw8<IN_F32>& r, float (&x)[8]) {
+  if constexpr (IN_F32) {
+    const uint32_t u[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(u[j]);
+  } else {
+    const uint32_t u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(u[j] << 16);
+      x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+    }
+  }
+}
+
 template <int FAM, int D, bool IN_F32>
 __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
   constexpr int NTK = IN_F32 ? 3 : 2;  // bf16 terms of decay-weighted keys
@@ -40,6 +76,7 @@ __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
   __shared__ float sW[C];        // scalar: weight exp(G_C - G_t)
   __shared__ float sTot[8][D];   // diag: per-8-token block sums of log gates
   __shared__ float sGC[D];       // chunk log-transition (scalar: entry 0)
+  __shared__ float sEGC[D];      // exp of it
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -58,38 +95,66 @@ __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
 
   double g_acc = 0.0;  // scalar: lane 0 of wave 0; diag: thread tid < D for channel tid
 
-  // staging role: threads [0, D) stage keys, [D, 2D) values; block (tb, db)
+  // staging role: threads [0, D) stage keys (and diagonal gates), [D, 2D) values
   const bool is_k = tid < D;
   const bool is_v = tid >= D && tid < 2 * D;
   const int sid = is_k ? tid : tid - D;
   const int tb = sid & 7;   // 8-token block
   const int db = sid >> 3;  // 8-channel block
+  const void* src = is_k ? a.k : a.v;
+
+  // raw inputs of the chunk being staged; the next chunk's are loaded while the
+  // matrix cores work on this one
+  Raw8<IN_F32> rx[8];
+  Raw8<IN_F32> rg[8];
+  float lg_scalar = 0.f;
+  auto issue_loads = [&](int c0) {
+    const int nv = min(C, t_end - c0);
+    if (is_k || is_v) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int t = tb * 8 + r;
+        rx[r] = ldraw8<IN_F32>(src, ((size_t)(c0 + min(t, nv - 1)) * n_chain + h) * D + db * 8, t < nv);
+      }
+    }
+    if constexpr (DIAG) {
+      if (is_k) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = tb * 8 + r;
+          rg[r] = ldraw8<IN_F32>(a.lg, ((size_t)(c0 + min(t, nv - 1)) * n_chain + h) * D + db * 8, t < nv);
+        }
+      }
+    }
+    if constexpr (FAM == 1) {
+      if (wave == 0) {
+        lg_scalar = 0.f;
+        if (lane < nv)
+          lg_scalar = a.gate_per_chain ? reinterpret_cast<const float*>(a.lg)[h]
+                                       : load1<IN_F32>(a.lg, (size_t)(c0 + lane) * n_chain + h);
+      }
+    }
+  };
+  issue_loads(t_begin);
 
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
-    const int nv = min(C, t_end - c0);
-
     // ---- gates: scalar prefix over the chunk (wave 0) -------------------------
     if constexpr (FAM == 1) {
       if (wave == 0) {
-        float lgt = 0.f;
-        if (lane < nv) {
-          if (a.gate_per_chain)
-            lgt = reinterpret_cast<const float*>(a.lg)[h];
-          else
-            lgt = load1<IN_F32>(a.lg, (size_t)(c0 + lane) * n_chain + h);
-        }
-        const float G = wave_incl_scan(lgt);
+        const float G = wave_incl_scan(lg_scalar);
         const float GC = __shfl(G, 63, 64);
         sW[lane] = expf(GC - G);
         if (lane == 0) {
           sGC[0] = GC;
+          sEGC[0] = expf(GC);
           g_acc += (double)GC;
         }
       }
+      __syncthreads();
     }
 
     // ---- gates: diagonal prefix per channel (key-staging threads) ---------------
-    float wdiag[8][8];  // [token in block][channel in block]
+    float pre[8], tot[8];
     if constexpr (DIAG) {
       if (is_k) {
         float run[8];
@@ -97,19 +162,10 @@ __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
         for (int c = 0; c < 8; ++c) run[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          const int t = tb * 8 + r;
           float x[8];
-          if (t < nv) {
-            load8<IN_F32>(a.lg, ((size_t)(c0 + t) * n_chain + h) * D + db * 8, x);
-          } else {
+          cvt8<IN_F32>(rg[r], x);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[c] = 0.f;
-          }
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            run[c] += x[c];
-            wdiag[r][c] = run[c];  // local inclusive prefix
-          }
+          for (int c = 0; c < 8; ++c) run[c] += x[c];
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) sTot[tb][db * 8 + c] = run[c];
@@ -118,45 +174,46 @@ __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
       if (is_k) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          float pre = 0.f, tot = 0.f;
+          float p = 0.f, t = 0.f;
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
             const float x = sTot[b][db * 8 + c];
-            tot += x;
-            if (b < tb) pre += x;
+            t += x;
+            if (b < tb) p += x;
           }
-#pragma unroll
-          for (int r = 0; r < 8; ++r) wdiag[r][c] = expf(tot - (pre + wdiag[r][c]));
-          if (tb == 0) sGC[db * 8 + c] = tot;
+          pre[c] = p;
+          tot[c] = t;
+          if (tb == 0) {
+            sGC[db * 8 + c] = t;
+            sEGC[db * 8 + c] = expf(t);
+          }
         }
       }
     }
-    if constexpr (FAM == 1) __syncthreads();
 
     // ---- stage keys (decay-weighted, split) and values, transposed -------------
     if (is_k || is_v) {
-      const void* src = is_k ? a.k : a.v;
       float x[8][8];  // [token r][channel c]
+      float run[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) run[c] = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int t = tb * 8 + r;
-        if (t < nv) {
-          load8<IN_F32>(src, ((size_t)(c0 + t) * n_chain + h) * D + db * 8, x[r]);
-        } else {
+        cvt8<IN_F32>(rx[r], x[r]);
+        if (is_k && GATED) {
+          if constexpr (DIAG) {
+            float lgr[8];
+            cvt8<IN_F32>(rg[r], lgr);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) x[r][c] = 0.f;
-        }
-      }
-      if (is_k && GATED) {
+            for (int c = 0; c < 8; ++c) {
+              run[c] += lgr[c];
+              x[r][c] *= expf(tot[c] - (pre[c] + run[c]));
+            }
+          } else {
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            if constexpr (DIAG)
-              x[r][c] *= wdiag[r][c];
-            else
-              x[r][c] *= sW[tb * 8 + r];
+            for (int c = 0; c < 8; ++c) x[r][c] *= sW[tb * 8 + r];
           }
+        }
       }
       // column c of the block = 8 tokens of channel db*8+c -> one 16-byte LDS row chunk
 #pragma unroll
@@ -176,6 +233,7 @@ __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
         }
       }
     }
+    if (c0 + C < t_end) issue_loads(c0 + C);
     __syncthreads();
 
     if constexpr (DIAG) {
@@ -188,18 +246,17 @@ __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
       const int tt = wave * TPW + i;
       const int rt = tt / NRT;
       if constexpr (FAM == 1) {
-        const float e = expf(sGC[0]);
+        const float e = sEGC[0];
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] *= e;
       } else if constexpr (DIAG) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] *= expf(sGC[32 * rt + acc_row(r, lane)]);
+        for (int r = 0; r < 16; ++r) acc[i][r] *= sEGC[32 * rt + acc_row(r, lane)];
       }
     }
 #pragma unroll
     for (int ks = 0; ks < C / 16; ++ks) {
       const int chunk = 2 * ks + (lane >> 5);
-      // all tiles of a wave share one row tile when TPW == NRT (d = 128)
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int tt = wave * TPW + i;

@@ -40,11 +40,21 @@ def round_f32(x) -> np.ndarray:
     return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
 
 
+def _rne_bf16_u32(u: np.ndarray) -> np.ndarray:
+    """In place: fp32 bit patterns (uint32) rounded to bf16 (nearest, ties to even),
+    low 16 bits cleared.  Finite inputs only."""
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    u += t
+    u &= np.uint32(0xFFFF0000)
+    return u
+
+
 def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    u = np.array(x32, dtype=np.float32).view(np.uint32)
+    return (_rne_bf16_u32(u) >> 16).astype(np.uint16)
 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
@@ -52,8 +62,8 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 
 def round_bf16(x) -> np.ndarray:
-    x32 = np.asarray(x, np.float64).astype(np.float32)
-    return bf16_bits_to_f64(f32_to_bf16_bits(x32))
+    u = np.asarray(x, np.float64).astype(np.float32).view(np.uint32)
+    return _rne_bf16_u32(u).view(np.float32).astype(np.float64)
 
 
 def round_to(x, dtype: str) -> np.ndarray:
@@ -194,10 +204,10 @@ def naive(n_seg=4, L=256, n_chain=4, d=128, dtype="bf16") -> Tokens:
                   {"workload": "naive", "n_seg": n_seg, "L": L})
 
 
-def gdn_cold(n_seg=64, L=512, n_chain=32, d=128, dtype="bf16", gate_scale=1.0 / 8) -> Tokens:
+def gdn_cold(n_seg=64, L=512, n_chain=32, d=128, dtype="bf16", gate_scale=1.0 / 8, want_q=True) -> Tokens:
     """GDN dense transition, one 32k-token cold request: 32 heads x 64 segments x 512 tokens."""
     n_tok = n_seg * L
-    q, k, v, beta, lg = _draw_delta_tokens(4, n_tok, n_chain, d, dtype, gate_scale)
+    q, k, v, beta, lg = _draw_delta_tokens(4, n_tok, n_chain, d, dtype, gate_scale, want_q=want_q)
     return Tokens(DELTA, dtype, n_chain, d, d, k, v, q, beta, lg, False, even_offsets(n_seg, L),
                   {"workload": "gdn_cold32k", "n_seg": n_seg, "L": L, "gate_scale": gate_scale})
 
