@@ -37,16 +37,16 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "build_delta": "segment_scan_amd/csrc/kernels/build_delta.hip",
-    "build_sd": "segment_scan_amd/csrc/kernels/build_sd.hip",
-    "seam": "segment_scan_amd/csrc/kernels/seam.hip",
-    "compose": "segment_scan_amd/csrc/kernels/compose.hip",
+    "build_delta": ["segment_scan_amd/csrc/kernels/build_delta2.hip"],
+    "build_sd": ["segment_scan_amd/csrc/kernels/build_sd.hip"],
+    "seam": ["segment_scan_amd/csrc/kernels/seam.hip"],
+    "compose": ["segment_scan_amd/csrc/kernels/compose.hip"],
 }
 
 
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[kernel], "segment_scan_amd/csrc/kernels/common.h"):
+    for rel in KERNEL_SOURCES[kernel] + ["segment_scan_amd/csrc/kernels/common.h"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -110,11 +110,11 @@ class ColdRequest(Workload):
         units = self.n_seg * self.H
         self.alg_bytes = units * _build_bytes(3, self.L, self.d, 2, 4, True)
         self.alg_flops = units * 8.0 * self.L * self.d ** 2
-        # executed MFMA flops of the chunked kernel: per 64-token chunk per unit,
-        # Gram 3 tiles x 8 steps, and per wave (4 waves) K Z 64, A Y 36, K^T X 64
-        # 32x32x16 MFMAs (split-bf16 terms included)
+        # executed MFMA flops of the two build kernels, 32x32x16 fp16 MFMAs per
+        # 64-token chunk and unit: Gram 3 tiles x 8 k-steps (prep), and per wave
+        # (4 waves, 2 column tiles each) K Z 16, A R 6, K^T X 16 (state)
         chunks = units * (self.L // 64)
-        self.exec_flops = chunks * (24 + 4 * (64 + 36 + 64)) * 32 * 32 * 16 * 2.0
+        self.exec_flops = chunks * (24 + 4 * 2 * (16 + 6 + 16)) * 32 * 32 * 16 * 2.0
 
     def setup(self):
         import torch
@@ -130,11 +130,14 @@ class ColdRequest(Workload):
         self.U = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
         self.S = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
         self.S_out = torch.empty((self.H, self.d, self.d), device=dev)
+        n_ws = api.seg_build_workspace_size(synth.DELTA, self.offsets, self.H, self.d, torch.bfloat16)
+        self.ws = torch.empty(max(n_ws, 16), device=dev, dtype=torch.uint8)
 
     def step(self, ev0, ev1):
         from segment_scan_amd.synth import DELTA
         ev0.record()
-        self.api.seg_build(DELTA, self.offsets, self.k, self.v, self.beta, self.lg, out=(self.g, self.U, self.S))
+        self.api.seg_build(DELTA, self.offsets, self.k, self.v, self.beta, self.lg, out=(self.g, self.U, self.S),
+                           workspace=self.ws)
         ev1.record()
         self.api.compose(DELTA, self.g, self.U, self.S, S_out=self.S_out)
 

@@ -13,7 +13,9 @@
  *  - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned,
  *    allocated and owned by the caller.  The library never allocates or frees
  *    device memory and keeps no pointer after the call returns.  `seg_offsets`
- *    of hypic_seg_build is the only HOST pointer.
+ *    of hypic_seg_build (and of hypic_seg_build_workspace_size) is the only
+ *    HOST pointer.  Scratch memory, where a call needs any, is a caller
+ *    workspace sized by a query function.
  *  - Calls are asynchronous: HYPIC_OK means "validated and enqueued on
  *    `stream`" (a hipStream_t passed as void*; NULL = the null stream).  Results
  *    are ready once the stream reaches that point.
@@ -52,13 +54,14 @@
 #ifndef HYPIC_H
 #define HYPIC_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 1
+#define HYPIC_ABI_VERSION 2
 
 typedef enum {
   HYPIC_OK = 0,
@@ -123,14 +126,34 @@ typedef struct {
  *   in           token inputs; q is ignored.
  *   out          g, S required; U required for DELTA (NULL otherwise).  Every
  *                output element is written.
+ *   workspace    device scratch of at least workspace_bytes bytes, as returned
+ *                by hypic_seg_build_workspace_size for the same fam, n_seg,
+ *                seg_offsets, n_chain, d_k, d_v and in->dtype; may be NULL when
+ *                that size is 0.  Its contents on entry are ignored and on exit
+ *                undefined; it is in use until the stream passes the call, so
+ *                calls that overlap in time need workspaces of their own.
  *   stream       hipStream_t or NULL.
  * Errors: HYPIC_E_INVALID for NULL required pointers, misaligned pointers,
- * bad offsets, a field that does not match the family, or outputs that
- * overlap inputs or each other; HYPIC_E_UNSUPPORTED for other sizes.
+ * bad offsets, a field that does not match the family, outputs or workspace
+ * that overlap inputs or each other, or a workspace smaller than required;
+ * HYPIC_E_UNSUPPORTED for other sizes.
  */
 hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain,
                              int d_k, int d_v, const hypic_tokens* in, const hypic_pairs* out,
-                             void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hypic_seg_build_workspace_size -- bytes of workspace hypic_seg_build needs.
+ *
+ * Only the DELTA family with d = 128 and bf16 tokens uses one (segments up to
+ * 2048 tokens): per 64-token chunk and chain it holds that chunk's WY factor
+ * (about 8.5 KiB), i.e. about 136 bytes per token and chain.  Every other
+ * combination returns 0.  Arguments as for hypic_seg_build (seg_offsets is
+ * validated the same way); *bytes receives the size.  Enqueues nothing.
+ */
+hypic_status hypic_seg_build_workspace_size(hypic_family fam, int n_seg, const int32_t* seg_offsets,
+                                            int n_chain, int d_k, int d_v, hypic_dtype dtype,
+                                            size_t* bytes);
 
 /*
  * hypic_compose -- ordered composition of cached pairs along every chain.

@@ -55,11 +55,13 @@ def load_library(path: str = LIB_PATH):
                              "%s is not built; run `python -m segment_scan_amd.build`" % path)
         lib = ctypes.CDLL(path)
         P, I = ctypes.c_void_p, ctypes.c_int
-        lib.hypic_seg_build.argtypes = [I, I, P, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P]
+        lib.hypic_seg_build.argtypes = [I, I, P, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P,
+                                        ctypes.c_size_t, P]
+        lib.hypic_seg_build_workspace_size.argtypes = [I, I, P, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.hypic_compose.argtypes = [I, I, I, I, I, ctypes.POINTER(Pairs), P, P, P, P, P, P]
         lib.hypic_seam_step.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P, P,
                                         ctypes.POINTER(Pairs), P]
-        for f in (lib.hypic_seg_build, lib.hypic_compose, lib.hypic_seam_step):
+        for f in (lib.hypic_seg_build, lib.hypic_seg_build_workspace_size, lib.hypic_compose, lib.hypic_seam_step):
             f.restype = I
         lib.hypic_last_error.restype = ctypes.c_char_p
         lib.hypic_last_error.argtypes = []
@@ -116,26 +118,48 @@ def _gate_shape(fam, lead, d):
     return tuple(lead) + ((d,) if fam == DIAG else ())
 
 
+def _offsets(offsets: Sequence[int]):
+    return (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
+
+
+def seg_build_workspace_size(fam: int, offsets: Sequence[int], n_chain: int, d: int, dtype: torch.dtype) -> int:
+    """Bytes of device workspace seg_build needs for this batch (0: none)."""
+    out = ctypes.c_size_t(0)
+    code = HYPIC_F32 if dtype == torch.float32 else HYPIC_BF16
+    _check(load_library().hypic_seg_build_workspace_size(fam, len(offsets) - 1, _offsets(offsets), n_chain, d, d,
+                                                         code, ctypes.byref(out)))
+    return out.value
+
+
 def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor, beta=None, log_gate=None,
-              gate_per_chain: bool = False, out=None, stream=None):
+              gate_per_chain: bool = False, out=None, workspace: Optional[torch.Tensor] = None, stream=None):
     """Build (g, U, S) of every (segment, chain): k, v [n_tok, n_chain, d] on the GPU.
 
     offsets: n_seg + 1 host integers.  Returns (g, U or None, S); `out` may pass
-    preallocated (g, U, S)."""
-    off = (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
+    preallocated (g, U, S) and `workspace` a uint8 device buffer of at least
+    seg_build_workspace_size() bytes (otherwise one is taken from torch's
+    allocator for the call)."""
+    off = _offsets(offsets)
     n_seg = len(offsets) - 1
     n_tok, n_chain, d = k.shape
+    dev = k.device
     if out is None:
-        dev = k.device
         g = torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32)
         U = torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam == DELTA else None
         S = torch.empty((n_seg, n_chain, d, v.shape[2]), device=dev, dtype=torch.float32)
     else:
         g, U, S = out
+    ws_bytes = 0
+    if workspace is None:
+        need = seg_build_workspace_size(fam, offsets, n_chain, d, k.dtype) if fam == DELTA else 0
+        if need:
+            workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
     tk = _tokens(k, v, None, beta, log_gate, gate_per_chain)
     pr = Pairs(_ptr(g), _ptr(U), _ptr(S))
     _check(load_library().hypic_seg_build(fam, n_seg, off, n_chain, d, v.shape[2], ctypes.byref(tk),
-                                          ctypes.byref(pr), _stream(stream)))
+                                          ctypes.byref(pr), _ptr(workspace), ws_bytes, _stream(stream)))
     return g, U, S
 
 

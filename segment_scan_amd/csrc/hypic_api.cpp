@@ -143,6 +143,35 @@ hypic_status check_cpairs(int fam, const hypic_cpairs* p, int n_seg, int n_chain
   return HYPIC_OK;
 }
 
+hypic_status check_offsets(int n_seg, const int32_t* seg_offsets) {
+  if (!seg_offsets) return fail(HYPIC_E_INVALID, "seg_offsets is NULL");
+  if (seg_offsets[0] != 0) return fail(HYPIC_E_INVALID, "seg_offsets[0] must be 0 (got %d)", seg_offsets[0]);
+  for (int s = 0; s < n_seg; ++s)
+    if (seg_offsets[s + 1] <= seg_offsets[s])
+      return fail(HYPIC_E_INVALID, "seg_offsets must strictly increase (segment %d is empty or negative)", s);
+  return HYPIC_OK;
+}
+
+// Fills the launch table of segments [s0, s0 + ns).
+void fill_seg_table(hypic::SegTable* t, const int32_t* seg_offsets, int s0, int ns) {
+  t->n_seg = ns;
+  t->seg_base = s0;
+  for (int i = 0; i <= ns; ++i) t->off[i] = seg_offsets[s0 + i];
+}
+
+// Workspace of a build: the largest any of its launches needs (launches run in
+// stream order and reuse it).
+size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
+  if (fam != HYPIC_DELTA) return 0;
+  size_t need = 0;
+  hypic::SegTable t;
+  for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
+    fill_seg_table(&t, seg_offsets, s0, std::min(hypic::kMaxSegPerLaunch, n_seg - s0));
+    need = std::max(need, hypic::build_delta_workspace(d, f32, t, n_chain));
+  }
+  return need;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,15 +180,22 @@ const char* hypic_last_error(void) { return g_err.c_str(); }
 
 int hypic_abi_version(void) { return HYPIC_ABI_VERSION; }
 
+hypic_status hypic_seg_build_workspace_size(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain,
+                                            int d_k, int d_v, hypic_dtype dtype, size_t* bytes) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  TRY(check_offsets(n_seg, seg_offsets));
+  if (dtype != HYPIC_F32 && dtype != HYPIC_BF16) return fail(HYPIC_E_INVALID, "unknown dtype %d", (int)dtype);
+  if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
+  *bytes = build_workspace(fam, n_seg, seg_offsets, n_chain, d_k, dtype == HYPIC_F32);
+  return ok();
+}
+
 hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d_k,
-                             int d_v, const hypic_tokens* in, const hypic_pairs* out, void* stream) {
+                             int d_v, const hypic_tokens* in, const hypic_pairs* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   const int d = d_k;
-  if (!seg_offsets) return fail(HYPIC_E_INVALID, "seg_offsets is NULL");
-  if (seg_offsets[0] != 0) return fail(HYPIC_E_INVALID, "seg_offsets[0] must be 0 (got %d)", seg_offsets[0]);
-  for (int s = 0; s < n_seg; ++s)
-    if (seg_offsets[s + 1] <= seg_offsets[s])
-      return fail(HYPIC_E_INVALID, "seg_offsets must strictly increase (segment %d is empty or negative)", s);
+  TRY(check_offsets(n_seg, seg_offsets));
   const size_t n_tok = (size_t)seg_offsets[n_seg];
   std::vector<Range> ins, outs;
   TRY(check_tokens(fam, in, n_tok, n_chain, d, false, &ins));
@@ -175,9 +211,17 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
   outs.push_back({out->S, units * d * d * 4, "out.S"});
   outs.push_back({out->g, units * gate_len(fam, d) * 4, "out.g"});
   if (out->U) outs.push_back({out->U, units * d * d * 4, "out.U"});
+  const bool f32 = in->dtype == HYPIC_F32;
+  const size_t ws_need = build_workspace(fam, n_seg, seg_offsets, n_chain, d, f32);
+  if (ws_need > 0) {
+    if (!workspace) return fail(HYPIC_E_INVALID, "workspace is NULL (%zu bytes required)", ws_need);
+    if (workspace_bytes < ws_need)
+      return fail(HYPIC_E_INVALID, "workspace too small: %zu bytes given, %zu required", workspace_bytes, ws_need);
+    TRY(check_aligned(workspace, "workspace"));
+    outs.push_back({workspace, ws_need, "workspace"});
+  }
   TRY(check_overlaps(ins, outs));
 
-  const bool f32 = in->dtype == HYPIC_F32;
   hypic::BuildArgs a;
   a.k = in->k;
   a.v = in->v;
@@ -190,11 +234,9 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
   a.gate_per_chain = in->gate_per_chain ? 1 : 0;
   for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
     const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
-    a.seg.n_seg = ns;
-    a.seg.seg_base = s0;
-    for (int i = 0; i <= ns; ++i) a.seg.off[i] = seg_offsets[s0 + i];
+    fill_seg_table(&a.seg, seg_offsets, s0, ns);
     const int blocks = ns * n_chain;
-    hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, (hipStream_t)stream)
+    hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, workspace, (hipStream_t)stream)
                                         : hypic::launch_build_sd(fam, d, f32, a, blocks, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
   }

@@ -1,0 +1,546 @@
+// build_delta2.hip -- delta-rule segment build (DeltaNet, GDN), bf16 tokens,
+// d = 128, in two kernels: a per-chunk WY preparation and a per-unit state pass.
+//
+// [youleyou, linear-layer paragraph] T_C is the ordered product of the
+// segment's per-token transitions a_t (I - beta_t k_t k_t^T), kept as exp(g) U,
+// and S(C|0) is its final state from a zero start.  The segment is processed in
+// 64-token chunks joined by the composition law of the same paragraph; a
+// chunk's 64 rank-1 factors are applied in the compact WY/UT form
+//   N    = (I + strict_lower(diag(b) K K^T))^-1,  A0 = N diag(b)
+//   Abar = Gamma o A0,  Gamma_ts = exp(G_t - G_s)   (G: within-chunk gate prefix)
+//   U   <- U - K^T (A0 (K U))
+//   S   <- exp(G_C) S + K^T diag(exp(G_C - G)) (Abar (V - diag(exp(G)) K S))
+//
+// Nothing in A0 depends on the running state, so the per-chunk factors are a
+// separate, fully parallel job:
+//  - delta_prep: one workgroup per (segment, chunk, chain) -- thousands of
+//    independent tasks, several workgroups per CU -- builds the Gram matrix on
+//    MFMA, inverts (I + M0) in 16 x 16 blocks in fp32, and writes A0 (fp16,
+//    each row scaled by a power of two) with the gate prefix G to a workspace;
+//  - delta_state: one workgroup per (segment, chain) keeps [U | S] in MFMA
+//    accumulators (4 waves x 64 columns) and, per chunk, stages K (row-major
+//    and transposed), V and A0 / Abar in LDS and runs the three products.
+// The workspace makes the state pass a plain stream with two barriers per
+// chunk and lets the latency-bound inverse hide behind other workgroups.
+//
+// Operands enter the matrix cores as fp16 (fp32 accumulate).  bf16 keys are
+// exact in fp16 within its normal range (normalised delta-rule keys are);
+// derived operands are rounded once, each block scaled by a power of two
+// chosen from its largest magnitude (f16_scale_exp in common.h; A0 per row),
+// so only rounding error remains: about 2^-12 per product, near 4e-4 relative
+// on 512-token GDN segments.  Longer segments use build_delta.hip.
+#include "common.h"
+#include "../launch.h"
+
+namespace hypic {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int C = 64;
+constexpr int KP = D + 4;  // 16-bit pitch of K [t][d] (fp16) and V [t][d] (bf16)
+constexpr int TP = C + 4;  // 16-bit pitch of K^T [d][t] and of A [t][t'] (fp16)
+constexpr int NP = 65;     // fp32 pitch of the inverse work array
+
+// Workspace record of one (chunk, chain): A0 (fp16, scaled rows), the row
+// scales (2^e as float) and the inclusive gate prefix G.
+constexpr int REC_A = 0;
+constexpr int REC_RS = C * C * 2;
+constexpr int REC_G = REC_RS + C * 4;
+constexpr int REC_BYTES = REC_G + C * 4;
+
+// Records are dense over the launch's chunks: record (chunk_base[s] + c) * n_chain
+// + chain holds chunk c of segment s on that chain.
+struct ChunkTable {
+  int32_t base[kMaxSegPerLaunch + 1];  // chunk_base[s]: chunks of the segments before s
+};
+
+__device__ __forceinline__ uint32_t pk_f16_from_bf16x2(uint32_t w) {
+  // exact conversion of two bf16 values, so the packing rounding mode is irrelevant
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)));
+}
+
+// A fragment in the accumulator-as-B k order (see common.h): k = off + {0..3}, off + 8 + {0..3}.
+__device__ __forceinline__ f16x8 lds_a_perm_h(const f16_t* p, int off) {
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(p + off);
+  const f16x4 hi = *reinterpret_cast<const f16x4*>(p + off + 8);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Standard-order fragment: 8 consecutive k from off.
+__device__ __forceinline__ f16x8 lds_frag_h(const f16_t* p, int off) {
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(p + off);
+  const f16x4 hi = *reinterpret_cast<const f16x4*>(p + off + 4);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Elements 8m .. 8m+7 of an accumulator tile, times s, as an fp16 B fragment.
+__device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, float s) {
+  f16x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (f16_t)(acc[8 * m + j] * s);
+  return f;
+}
+
+// =====================================================================================
+// delta_prep: per (chunk, chain) A0 = (I + strict_lower(diag(b) K K^T))^-1 diag(b)
+// =====================================================================================
+
+struct PrepLds {
+  static constexpr int K_B = C * KP * 2;
+  static constexpr int OFF_N = K_B;
+  static constexpr int OFF_T = OFF_N + C * NP * 4;
+  static constexpr int OFF_P = OFF_T + 3 * 16 * 17 * 4;
+  static constexpr int LDS = OFF_P + 3 * C * 4;
+};
+
+__global__ __launch_bounds__(256) void delta_prep_kernel(const BuildArgs a, const ChunkTable cks, unsigned char* ws) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PrepLds::LDS];
+  f16_t* sK = reinterpret_cast<f16_t*>(smem);
+  float* sN = reinterpret_cast<float*>(smem + PrepLds::OFF_N);
+  float* sT = reinterpret_cast<float*>(smem + PrepLds::OFF_T);
+  float* sBeta = reinterpret_cast<float*>(smem + PrepLds::OFF_P);
+  float* sLg = sBeta + C;
+  float* sG = sLg + C;
+
+  // workgroup -> (chunk of the launch, chain): consecutive workgroups take the
+  // chains of one chunk, which share the rows of the token-major inputs
+  const int n_chain = a.n_chain;
+  const int gchunk = blockIdx.x / n_chain, chain = blockIdx.x % n_chain;
+  int lo = 0, hi = a.seg.n_seg;  // segment: last s with base[s] <= gchunk (uniform search)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cks.base[mid] <= gchunk) lo = mid; else hi = mid;
+  }
+  const int c0 = a.seg.off[lo] + (gchunk - cks.base[lo]) * C;
+  const int nv = min(C, a.seg.off[lo + 1] - c0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  // ---- keys (fp16) and per-token scalars into LDS ---------------------------------
+  if (tid < 128) {
+    const int tb = tid & 7, db = tid >> 3;
+    const bf16_t* src = reinterpret_cast<const bf16_t*>(a.k);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int t = tb * 8 + r;
+      uint4 u = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
+      if (t >= nv) u = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint2*>(sK + t * KP + db * 8) = make_uint2(pk_f16_from_bf16x2(u.x), pk_f16_from_bf16x2(u.y));
+      *reinterpret_cast<uint2*>(sK + t * KP + db * 8 + 4) = make_uint2(pk_f16_from_bf16x2(u.z), pk_f16_from_bf16x2(u.w));
+    }
+  } else if (tid < 128 + C) {
+    const int t = tid - 128;
+    float b = 0.f, lg = 0.f;
+    if (t < nv) {
+      const size_t idx = (size_t)(c0 + t) * n_chain + chain;
+      b = load1<false>(a.beta, idx);
+      if (a.lg) lg = load1<false>(a.lg, idx);
+    }
+    sBeta[t] = b;
+    sLg[t] = lg;
+  }
+  __syncthreads();
+
+  // ---- gate prefix (wave 3) and Gram tiles t > t' (waves 0-2) -> M0 --------------
+  if (wave == 3) {
+    sG[lane] = wave_incl_scan(sLg[lane]);
+  } else {
+    const int tt = (wave == 0) ? 0 : 1;
+    const int tp = (wave == 2) ? 1 : 0;
+    const f16_t* pKg = sK + l32 * KP + 8 * h;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      acc = mfma32h(lds_frag_h(pKg + 32 * tt * KP, 16 * ks), lds_frag_h(pKg + 32 * tp * KP, 16 * ks), acc);
+    const int cc = 32 * tp + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 32 * tt + acc_row(r, lane);
+      sN[rr * NP + cc] = (rr > cc) ? sBeta[rr] * acc[r] : 0.f;
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sN[acc_row(r, lane) * NP + 32 + l32] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- N = (I + M0)^-1: four 16 x 16 diagonal blocks, one per wave -----------------
+  // lane (column c, part p): partial sums over k = p (mod 4), combined across the
+  // four parts with xor-shuffles, so each row costs ~r/4 FMAs and two exchanges.
+  {
+    const int b = wave;
+    const int cl = lane & 15, p = lane >> 4;
+    const float* Mb = sN + (16 * b) * NP + 16 * b;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < r; ++k)
+        if ((k & 3) == p && k >= cl) acc = fmaf(Mb[r * NP + k], x[k], acc);
+      acc += __shfl_xor(acc, 16, 64);
+      acc += __shfl_xor(acc, 32, 64);
+      x[r] = (r < cl) ? 0.f : ((r == cl) ? 1.f : -acc);
+    }
+    __syncthreads();  // every wave has read its block of M0
+    if (p == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sN[(16 * b + r) * NP + 16 * b + cl] = x[r];
+    }
+  }
+  // ---- block rows i = 1..3: T_ij = sum_{k=j}^{i-1} M_ik N_kj, N_ij = -N_ii T_ij ------
+  {
+    const int r = tid >> 4, cc = tid & 15;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      __syncthreads();
+      for (int j = 0; j < i; ++j) {
+        float acc = 0.f;
+        const float* Mrow = sN + (16 * i + r) * NP;
+        for (int k = j; k < i; ++k)
+#pragma unroll
+          for (int m = 0; m < 16; ++m) acc = fmaf(Mrow[16 * k + m], sN[(16 * k + m) * NP + 16 * j + cc], acc);
+        sT[(j * 16 + r) * 17 + cc] = acc;
+      }
+      __syncthreads();
+      for (int j = 0; j < i; ++j) {
+        float acc = 0.f;
+        const float* Nrow = sN + (16 * i + r) * NP + 16 * i;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc = fmaf(Nrow[m], sT[(j * 16 + m) * 17 + cc], acc);
+        sN[(16 * i + r) * NP + 16 * j + cc] = -acc;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- A0 = N diag(b), rows scaled by powers of two, to the workspace --------------
+  unsigned char* rec = ws + (size_t)blockIdx.x * REC_BYTES;
+  {
+    const int t = tid >> 2;
+    const int cb = (tid & 3) * 16;
+    float v[16];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int tp = cb + j;
+      v[j] = (tp <= t) ? sN[t * NP + tp] * sBeta[tp] : 0.f;
+      m = fmaxf(m, fabsf(v[j]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    int e = 0;
+    if (m > 0.f) {
+      frexpf(m, &e);
+      e -= 14;  // row maximum into [2^13, 2^14)
+    }
+    const float s = ldexpf(1.f, -e);
+    f16x8 h0, h1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h0[j] = (f16_t)(v[j] * s);
+      h1[j] = (f16_t)(v[8 + j] * s);
+    }
+    f16x8* dst = reinterpret_cast<f16x8*>(rec + REC_A + (t * C + cb) * 2);
+    dst[0] = h0;
+    dst[1] = h1;
+    if ((tid & 3) == 0) reinterpret_cast<float*>(rec + REC_RS)[t] = ldexpf(1.f, e);
+    if (tid < C) reinterpret_cast<float*>(rec + REC_G)[tid] = sG[tid];
+  }
+}
+
+// =====================================================================================
+// delta_state: per unit, [U | S] in registers, three MFMA products per chunk
+// =====================================================================================
+
+struct StateLds {
+  static constexpr int O_K = 0;
+  static constexpr int O_KT = O_K + C * KP * 2;
+  static constexpr int O_V = O_KT + D * TP * 2;
+  static constexpr int O_A0 = O_V + C * KP * 2;
+  static constexpr int O_AB = O_A0 + C * TP * 2;
+  static constexpr int O_SM = O_AB + C * TP * 2;   // eG[64], fac0[64], facb[64], misc[64]
+  static constexpr int LDS = O_SM + 4 * C * 4;
+};
+
+__global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, const ChunkTable cks,
+                                                              const unsigned char* ws) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  f16_t* sK = reinterpret_cast<f16_t*>(smem + StateLds::O_K);
+  f16_t* sKt = reinterpret_cast<f16_t*>(smem + StateLds::O_KT);
+  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + StateLds::O_V);
+  f16_t* sA0 = reinterpret_cast<f16_t*>(smem + StateLds::O_A0);
+  f16_t* sAb = reinterpret_cast<f16_t*>(smem + StateLds::O_AB);
+  float* sEG = reinterpret_cast<float*>(smem + StateLds::O_SM);
+  float* sFac0 = sEG + C;  // -row scale of A0                 (U waves: X' = -X)
+  float* sFacB = sFac0 + C;  // row scale * exp(G_C - G_t)     (S waves)
+  float* sMisc = sFacB + C;  // [0] = exp(G_C)
+
+  const int wave = threadIdx.x >> 6;
+  const bool s_wave = wave >= 2;
+  const int col0 = (wave & 1) * 64;
+  const int n_chain = a.n_chain;
+  const int s_local = blockIdx.x / n_chain;
+  const int chain = blockIdx.x % n_chain;
+  const int t_begin = a.seg.off[s_local], t_end = a.seg.off[s_local + 1];
+  const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + chain;
+
+  f32x16 Z[4][2];
+  {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rt + acc_row(r, lane);
+          const int col = col0 + 32 * ct + (lane & 31);
+          Z[rt][ct][r] = (!s_wave && row == col) ? 1.f : 0.f;
+        }
+  }
+  f32x16 W[2];  // Y = K Z after step 1, X' after step 2
+  double g_acc = 0.0;
+
+  for (int c = 0, c0 = t_begin; c0 < t_end; ++c, c0 += C) {
+    const int nv = min(C, t_end - c0);
+    const unsigned char* rec = ws + ((size_t)(cks.base[s_local] + c) * n_chain + chain) * REC_BYTES;
+    {
+      // ---- stage the chunk ----------------------------------------------------------
+      const int tid = opaque(threadIdx.x);
+      if (tid < 128) {  // keys: fp16 row-major and transposed (8 tokens x 8 channels per thread)
+        const int tb = tid & 7, db = tid >> 3;
+        const bf16_t* src = reinterpret_cast<const bf16_t*>(a.k);
+        uint32_t kd[8][4];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = tb * 8 + r;
+          uint4 u = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
+          const uint32_t keep = (t < nv) ? 0xffffffffu : 0u;
+          kd[r][0] = pk_f16_from_bf16x2(u.x & keep);
+          kd[r][1] = pk_f16_from_bf16x2(u.y & keep);
+          kd[r][2] = pk_f16_from_bf16x2(u.z & keep);
+          kd[r][3] = pk_f16_from_bf16x2(u.w & keep);
+          *reinterpret_cast<uint2*>(sK + t * KP + db * 8) = make_uint2(kd[r][0], kd[r][1]);
+          *reinterpret_cast<uint2*>(sK + t * KP + db * 8 + 4) = make_uint2(kd[r][2], kd[r][3]);
+        }
+        // 8 x 8 transpose of 16-bit elements: dword j of column cc packs element cc
+        // of rows 2j (low half) and 2j+1 (high half)
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+          uint32_t o[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(kd[2 * j + 1][cc >> 1], kd[2 * j][cc >> 1], sel);
+          *reinterpret_cast<uint2*>(sKt + (db * 8 + cc) * TP + tb * 8) = make_uint2(o[0], o[1]);
+          *reinterpret_cast<uint2*>(sKt + (db * 8 + cc) * TP + tb * 8 + 4) = make_uint2(o[2], o[3]);
+        }
+      } else {  // values: bf16 row-major (rows past the segment end only meet zero weights)
+        const int sid = tid - 128;
+        const int tb = sid & 7, db = sid >> 3;
+        const bf16_t* src = reinterpret_cast<const bf16_t*>(a.v);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = tb * 8 + r;
+          const uint4 u = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
+          *reinterpret_cast<uint2*>(sV + t * KP + db * 8) = make_uint2(u.x, u.y);
+          *reinterpret_cast<uint2*>(sV + t * KP + db * 8 + 4) = make_uint2(u.z, u.w);
+        }
+      }
+      // A0 and Abar = Gamma o A0 (same row scales: Gamma <= 1 and Gamma_tt = 1)
+      {
+        const int t = tid >> 2, cb = (tid & 3) * 16;
+        const float* G = reinterpret_cast<const float*>(rec + REC_G);
+        const f16x8* src = reinterpret_cast<const f16x8*>(rec + REC_A + (t * C + cb) * 2);
+        const f16x8 a0 = src[0], a1 = src[1];
+        const float Gt = G[t];
+        f16x8 b0, b1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int tp0 = cb + j, tp1 = cb + 8 + j;
+          b0[j] = (f16_t)((float)a0[j] * ((tp0 <= t) ? __expf(Gt - G[tp0]) : 0.f));
+          b1[j] = (f16_t)((float)a1[j] * ((tp1 <= t) ? __expf(Gt - G[tp1]) : 0.f));
+        }
+        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb) = __builtin_shufflevector(a0, a0, 0, 1, 2, 3);
+        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 4) = __builtin_shufflevector(a0, a0, 4, 5, 6, 7);
+        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 8) = __builtin_shufflevector(a1, a1, 0, 1, 2, 3);
+        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 12) = __builtin_shufflevector(a1, a1, 4, 5, 6, 7);
+        *reinterpret_cast<f16x4*>(sAb + t * TP + cb) = __builtin_shufflevector(b0, b0, 0, 1, 2, 3);
+        *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 4) = __builtin_shufflevector(b0, b0, 4, 5, 6, 7);
+        *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 8) = __builtin_shufflevector(b1, b1, 0, 1, 2, 3);
+        *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 12) = __builtin_shufflevector(b1, b1, 4, 5, 6, 7);
+        if (tid < C) {
+          const float GC = G[C - 1];
+          const float rs = reinterpret_cast<const float*>(rec + REC_RS)[tid];
+          sEG[tid] = __expf(G[tid]);
+          sFac0[tid] = -rs;
+          sFacB[tid] = rs * __expf(GC - G[tid]);
+          if (tid == 0) {
+            sMisc[0] = __expf(GC);
+            g_acc += (double)GC;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    const int lane = opaque(threadIdx.x) & 63;
+    const int h = lane >> 5, l32 = lane & 31;
+    const float eGC = sMisc[0];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      // ---- step 1: Y = K Z[:, ct] ------------------------------------------------
+      {
+        float m = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(Z[rt][ct][r]));
+        const int ez = f16_scale_exp(wave_max(m));
+        const float fz = ldexpf(1.f, -ez);
+        const f16_t* pK = sK + l32 * KP + 4 * h;
+        W[0] = zero16();
+        W[1] = zero16();
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const f16x8 fb = acc_as_b_h(Z[rt][ct], mm, fz);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
+          }
+        if (ez != 0) {
+          const float f = ldexpf(1.f, ez);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) W[tt][r] *= f;
+        }
+      }
+      // ---- step 2: R = V - exp(G) Y (S) or Y (U);  X' = fac (A R) -----------------------
+      {
+        if (s_wave) {
+          const bf16_t* pV = sV + col0 + 32 * ct + l32;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int t = 32 * tt + acc_row(r, lane);
+              W[tt][r] = (float)pV[t * KP] - sEG[t] * W[tt][r];
+            }
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
+        const int er = f16_scale_exp(wave_max(m));
+        const float fr = ldexpf(1.f, -er);
+        const f16_t* pA = (s_wave ? sAb : sA0) + l32 * TP + 4 * h;
+        f16x8 fb[2][2];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) fb[tp][mm] = acc_as_b_h(W[tp], mm, fr);
+        W[0] = zero16();
+        W[1] = zero16();
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int tt = tp; tt < 2; ++tt)
+              W[tt] = mfma32h(lds_a_perm_h(pA, 32 * tt * TP + 32 * tp + 16 * mm), fb[tp][mm], W[tt]);
+        const float f_er = ldexpf(1.f, er);
+        const float* fac = s_wave ? sFacB : sFac0;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) W[tt][r] *= fac[32 * tt + acc_row(r, lane)] * f_er;
+      }
+      // ---- step 3: Z = (exp(G_C) | 1) Z + K^T X' ----------------------------------------
+      {
+        float m = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
+        const int ex = f16_scale_exp(wave_max(m));
+        const float fx = ldexpf(1.f, -ex);
+        const float pre = (s_wave ? eGC : 1.f) * fx;
+        if (s_wave || ex != 0) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Z[rt][ct][r] *= pre;
+        }
+        const f16_t* pKt = sKt + l32 * TP + 4 * h;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const f16x8 fb = acc_as_b_h(W[tt], mm, fx);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+              Z[rt][ct] = mfma32h(lds_a_perm_h(pKt, 32 * rt * TP + 32 * tt + 16 * mm), fb, Z[rt][ct]);
+          }
+        if (ex != 0) {
+          const float f = ldexpf(1.f, ex);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Z[rt][ct][r] *= f;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  const int lane = threadIdx.x & 63;
+  float* dst = (s_wave ? a.S : a.U) + unit * D * D;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dst[(size_t)(32 * rt + acc_row(r, lane)) * D + col0 + 32 * ct + (lane & 31)] = Z[rt][ct][r];
+  if (threadIdx.x == 0) a.g[unit] = (float)g_acc;
+}
+
+}  // namespace
+
+namespace {
+int chunks_of(const SegTable& seg, ChunkTable* ct) {
+  int n = 0;
+  for (int s = 0; s < seg.n_seg; ++s) {
+    if (ct) ct->base[s] = n;
+    n += (seg.off[s + 1] - seg.off[s] + C - 1) / C;
+  }
+  if (ct) ct->base[seg.n_seg] = n;
+  return n;
+}
+}  // namespace
+
+size_t delta2_workspace_bytes(const SegTable& seg, int n_chain) {
+  return (size_t)chunks_of(seg, nullptr) * n_chain * REC_BYTES;
+}
+
+hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&delta_state_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, StateLds::LDS);
+  if (attr != hipSuccess) return attr;
+  ChunkTable ct;
+  const int n_chunks = chunks_of(a.seg, &ct);
+  unsigned char* w = reinterpret_cast<unsigned char*>(ws);
+  hipLaunchKernelGGL(delta_prep_kernel, dim3(n_chunks * a.n_chain), dim3(256), 0, stream, a, ct, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(delta_state_kernel, dim3(a.seg.n_seg * a.n_chain), dim3(256), StateLds::LDS, stream, a, ct,
+                     (const unsigned char*)w);
+  return hipGetLastError();
+}
+
+}  // namespace hypic

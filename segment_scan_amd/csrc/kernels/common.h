@@ -32,6 +32,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef _Float16 f16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 
 constexpr int kWave = 64;
 
@@ -48,8 +51,17 @@ __device__ __forceinline__ int opaque(int x) {
 }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Compiler-only fence: memory operations are not moved across it.  Used inside
+// unrolled MFMA loops to bound how far ahead LDS fragments are loaded (and so
+// how many registers they hold).
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -146,6 +158,25 @@ __device__ __forceinline__ float load1(const void* base, size_t idx) {
   } else {
     return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
   }
+}
+
+// Maximum across the 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Power-of-two scaling of an fp16 operand block whose largest magnitude is m:
+// returns the exponent e such that the block is converted as x * 2^-e.  Blocks
+// already inside [2^-6, 2^12] are left unscaled (e = 0): there every value that
+// matters to the block's norm is a normal fp16 number with headroom for the
+// products it feeds; otherwise the largest magnitude is mapped into [2^11, 2^12).
+__device__ __forceinline__ int f16_scale_exp(float m) {
+  if (!(m > 0.f) || (m >= 0x1p-6f && m <= 0x1p12f)) return 0;
+  int e;
+  frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
+  return e - 12;
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave.

@@ -65,8 +65,17 @@ struct SeamArgs {
 // fam: 0 naive, 1 scalar, 2 diag, 3 delta.  d in {64, 128}.
 hipError_t launch_build_sd(int fam, int d, bool in_f32, const BuildArgs& a, int n_blocks,
                            hipStream_t stream);
-hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_blocks,
+// Delta build.  For d = 128 with bf16 tokens and segments of at most
+// kDelta2MaxSegLen tokens it runs as two kernels that hand per-chunk factors
+// over through a caller workspace of build_delta_workspace() bytes; otherwise
+// one kernel that needs no workspace (ws may then be NULL).
+constexpr int kDelta2MaxSegLen = 2048;
+size_t build_delta_workspace(int d, bool in_f32, const SegTable& seg, int n_chain);
+hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_blocks, void* ws,
                               hipStream_t stream);
+// the two-kernel path (build_delta2.hip)
+size_t delta2_workspace_bytes(const SegTable& seg, int n_chain);
+hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream);
 hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t stream);
 hipError_t launch_compose_dense(int d, const ComposeArgs& a, hipStream_t stream);
 // Whether the seam step is built for this family / size / option.

@@ -47,6 +47,28 @@ def blocked_unit_lower_inverse(M, bs=16):
     return N
 
 
+def blocked_inverse_in_place(M, bs=16):
+    """The same inverse computed in place in one array, in the order the GPU
+    kernels use: diagonal blocks first, then block rows i = 1, 2, ... where all
+    T_ij of row i are formed from row i's M blocks before N_ij overwrite them."""
+    W = np.array(M, dtype=np.float64)
+    nb = W.shape[0] // bs
+    blk = lambda i: slice(i * bs, (i + 1) * bs)
+    for i in range(nb):
+        Mi = W[blk(i), blk(i)].copy()
+        Ni = np.zeros((bs, bs))
+        for r in range(bs):
+            Ni[r, r] = 1.0
+            for c in range(r):
+                Ni[r, c] = -Mi[r, c:r] @ Ni[c:r, c]
+        W[blk(i), blk(i)] = Ni
+    for i in range(1, nb):
+        T = [sum(W[blk(i), blk(k)] @ W[blk(k), blk(j)] for k in range(j, i)) for j in range(i)]
+        for j in range(i):
+            W[blk(i), blk(j)] = -W[blk(i), blk(i)] @ T[j]
+    return np.tril(W)
+
+
 def delta_chunk(K, V, b, a, S0, U0, Q=None, blocked=True):
     C = K.shape[0]
     G = np.cumsum(a)

@@ -25,7 +25,9 @@ BF16, F32 = api.HYPIC_BF16, api.HYPIC_F32
 
 # fake device addresses, 16-byte aligned, far apart (1 TiB) so nothing overlaps by accident
 A = {name: (i + 1) << 40 for i, name in enumerate(
-    ["q", "k", "v", "beta", "lg", "g", "U", "S", "Sinit", "Sout", "prefix", "gtot", "Utot", "o", "wg", "wU", "wS"])}
+    ["q", "k", "v", "beta", "lg", "g", "U", "S", "Sinit", "Sout", "prefix", "gtot", "Utot", "o", "wg", "wU", "wS",
+     "ws"])}
+WS_BYTES = 1 << 36
 
 
 @pytest.fixture(scope="module")
@@ -40,15 +42,15 @@ def test_library_exports_every_declared_symbol(lib):
     with open(HEADER) as f:
         text = f.read()
     declared = set(re.findall(r"\b(hypic_[a-z_]+)\s*\(", text))
-    assert {"hypic_seg_build", "hypic_compose", "hypic_seam_step", "hypic_last_error",
-            "hypic_abi_version"} <= declared
+    assert {"hypic_seg_build", "hypic_seg_build_workspace_size", "hypic_compose", "hypic_seam_step",
+            "hypic_last_error", "hypic_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\b(hypic_[a-z_]+)\b", out))
     assert declared <= exported, declared - exported
     for name in declared:
         getattr(lib, name)
-    assert lib.hypic_abi_version() == 1
+    assert lib.hypic_abi_version() == 2
 
 
 def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
@@ -66,11 +68,41 @@ def pairs(fam, g=True, U=None, S=True):
     return Pairs(A["g"] if g else None, A["U"] if U else None, A["S"] if S else None)
 
 
-def build_call(lib, fam=DELTA, n_seg=2, offsets=(0, 64, 128), n_chain=2, dk=128, dv=128, t=None, p=None):
+def build_call(lib, fam=DELTA, n_seg=2, offsets=(0, 64, 128), n_chain=2, dk=128, dv=128, t=None, p=None,
+               ws=A["ws"], ws_bytes=WS_BYTES):
     off = (ctypes.c_int32 * len(offsets))(*offsets) if offsets is not None else None
     t = toks(fam) if t is None else t
     p = pairs(fam) if p is None else p
-    return lib.hypic_seg_build(fam, n_seg, off, n_chain, dk, dv, ctypes.byref(t), ctypes.byref(p), None)
+    return lib.hypic_seg_build(fam, n_seg, off, n_chain, dk, dv, ctypes.byref(t), ctypes.byref(p), ws, ws_bytes,
+                               None)
+
+
+def ws_size(lib, fam=DELTA, offsets=(0, 64, 128), n_chain=2, d=128, dtype=BF16):
+    off = (ctypes.c_int32 * len(offsets))(*offsets)
+    out = ctypes.c_size_t(123)
+    st = lib.hypic_seg_build_workspace_size(fam, len(offsets) - 1, off, n_chain, d, d, dtype, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size(lib):
+    """Only the d = 128 bf16 delta build takes a workspace: one 8704-byte WY record
+    (fp16 A0 [64 x 64], 64 row scales, 64 gate prefixes) per 64-token chunk and chain."""
+    lib_ = lib
+    assert ws_size(lib_) == (0, 2 * 2 * 8704)
+    assert ws_size(lib_, offsets=(0, 1, 65, 200), n_chain=3) == (0, (1 + 1 + 3) * 3 * 8704)
+    assert ws_size(lib_, dtype=F32) == (0, 0)
+    assert ws_size(lib_, d=64) == (0, 0)
+    assert ws_size(lib_, fam=SCALAR) == (0, 0)
+    # segments longer than 2048 tokens take the single-kernel path
+    assert ws_size(lib_, offsets=(0, 2048)) == (0, 32 * 2 * 8704)
+    assert ws_size(lib_, offsets=(0, 2049)) == (0, 0)
+    # launches of at most 240 segments reuse one workspace: the largest launch sets the size
+    offs = [64 * i for i in range(301)]
+    assert ws_size(lib_, offsets=offs, n_chain=1) == (0, 240 * 8704)
+    assert ws_size(lib_, offsets=(0, 64, 64))[0] == INVALID
+    assert "strictly increase" in api.last_error()
+    assert lib_.hypic_seg_build_workspace_size(DELTA, 1, (ctypes.c_int32 * 2)(0, 64), 1, 128, 128, BF16,
+                                               None) == INVALID
 
 
 @pytest.mark.parametrize("kwargs,status,msg", [
@@ -98,6 +130,11 @@ def build_call(lib, fam=DELTA, n_seg=2, offsets=(0, 64, 128), n_chain=2, dk=128,
     (dict(p=Pairs(None, A["U"], A["S"])), INVALID, "out.g is NULL"),
     (dict(p=Pairs(A["g"], A["U"], A["k"] + 4096)), INVALID, "overlaps input k"),
     (dict(p=Pairs(A["g"], A["S"] + 4096, A["S"])), INVALID, "overlap"),
+    (dict(ws=None), INVALID, "workspace is NULL"),
+    (dict(ws_bytes=2 * 2 * 8704 - 1), INVALID, "workspace too small"),
+    (dict(ws=A["ws"] + 8), INVALID, "workspace is not 16-byte aligned"),
+    (dict(ws=A["k"] + 64), INVALID, "output workspace overlaps input k"),
+    (dict(ws=A["S"] + 64), INVALID, "overlap"),
 ])
 def test_seg_build_rejects(lib, kwargs, status, msg):
     st = build_call(lib, **kwargs)

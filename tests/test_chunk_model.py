@@ -19,6 +19,14 @@ def test_blocked_inverse():
     np.testing.assert_allclose(N @ (np.eye(64) + M), np.eye(64), atol=1e-12)
 
 
+def test_in_place_inverse_order():
+    """The in-place block order of the kernels (block rows, T before N) gives the inverse."""
+    r = np.random.default_rng(1)
+    M = np.tril(r.standard_normal((64, 64)) * 0.1, -1)
+    N = chunk_model.blocked_inverse_in_place(M)
+    np.testing.assert_allclose(N @ (np.eye(64) + M), np.eye(64), atol=1e-12)
+
+
 @pytest.mark.parametrize("gate_scale", [1.0, 1.0 / 64, 0.0])
 @pytest.mark.parametrize("L", [256, 200, 64, 5])
 def test_delta_chunked_build_matches_oracle(gate_scale, L):

@@ -105,3 +105,48 @@ def test_gdn_build_then_compose_matches_sequential():
     torch.cuda.synchronize()
     Sseq, _ = oracle.sequential(DELTA, tk.k, tk.v, tk.beta, tk.log_gate)
     assert_units_close("gdn_e2e", host(res["S_out"]), Sseq, TOL["bf16"], unit_dims=1)
+
+
+def test_gdn_segment_length_limits():
+    """A 2048-token segment (longest of the two-kernel fp16 path, where its
+    rounding error accumulates most) and a 2049-token one (single-kernel path)."""
+    for L in (2048, 2049):
+        tk = synth.gdn_cold(n_seg=1, L=L, n_chain=2, gate_scale=1.0 / 64)
+        check_build(tk, "gdn_long_%d" % L)
+
+
+def test_gdn_many_ragged_segments_two_launches():
+    """300 ragged segments (1..130 tokens): two launches that reuse one workspace."""
+    rng = np.random.default_rng(5)
+    lengths = [int(x) for x in rng.integers(1, 131, 300)]
+    tk = synth.gdn_cold(n_seg=1, L=sum(lengths), n_chain=2, gate_scale=1.0 / 16)
+    check_build(tk, "gdn_300seg", synth.ragged_offsets(lengths))
+
+
+def test_deltanet_ungated_d128():
+    """DeltaNet (no gate, log_gate NULL) through the d = 128 bf16 path."""
+    tk = synth.gdn_cold(n_seg=3, L=192, n_chain=2)
+    tk.log_gate = None
+    check_build(tk, "deltanet_d128")
+
+
+def test_explicit_workspace_reused_across_calls():
+    """A caller-owned workspace of the queried size serves two different batches;
+    results equal those of calls with their own workspace."""
+    import torch
+    tk = synth.gdn_cold(n_seg=4, L=256, n_chain=2)
+    announce("explicit_ws")
+    d = upload_tokens(tk)
+    off = list(tk.offsets)
+    need = api.seg_build_workspace_size(DELTA, off, 2, 128, torch.bfloat16)
+    assert need == 4 * 4 * 2 * 8704
+    ws = torch.full((need,), 0xAB, device="cuda", dtype=torch.uint8)
+    g1, U1, S1 = api.seg_build(DELTA, off, d["k"], d["v"], d["beta"], d["log_gate"], workspace=ws)
+    g2, U2, S2 = api.seg_build(DELTA, off[:3], d["k"][:off[2]], d["v"][:off[2]], d["beta"][:off[2]],
+                               d["log_gate"][:off[2]], workspace=ws)
+    g0, U0, S0 = api.seg_build(DELTA, off, d["k"], d["v"], d["beta"], d["log_gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S0) and torch.equal(U1, U0) and torch.equal(g1, g0)
+    assert torch.equal(S2, S0[:2]) and torch.equal(U2, U0[:2])
+    with pytest.raises(api.HypicError, match="workspace too small"):
+        api.seg_build(DELTA, off, d["k"], d["v"], d["beta"], d["log_gate"], workspace=ws[:need - 16])
