@@ -65,6 +65,63 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
+# device kernels that make up each timed operation (substrings of their symbol names)
+KERNEL_SYMBOLS = {
+    "build_delta": ["delta_prep_kernel", "delta_state_kernel", "build_delta_kernel"],
+    "build_sd": ["build_sd_kernel"],
+    "seam": ["seam_kernel"],
+    "compose": ["compose_dense_kernel", "compose_elem_kernel"],
+}
+CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
+CALIBRATION_BYTES = 1 << 30  # each reads and writes this many bytes
+
+
+def ingest_counters(workload: str, kernel: str, fetch_csv: str, write_csv: str, steps: int, cmds):
+    """Turns two rocprofv3 --pmc runs of `bench.py --copy-calibration` (FETCH_SIZE,
+    then WRITE_SIZE; counter_collection.csv files) into HBM bytes per launch of the
+    timed operation, each counter scaled by what it reads for the plain 1 GiB copy
+    kernel that ends the run, and records them in profiles/traffic.json."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                d = int(r["Dispatch_Id"])
+                name, val = r["Kernel_Name"], float(r["Counter_Value"])
+                rows[d] = (name, rows.get(d, (name, 0.0))[1] + val)
+        return [rows[d] for d in sorted(rows)]
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = per_dispatch(path, counter)
+        cal = disp[-CALIBRATION_COPIES:]
+        assert len(cal) == CALIBRATION_COPIES and len({n for n, _ in cal}) == 1 and "hypic" not in cal[0][0], \
+            "calibration copies not found at the end of %s" % path
+        kib_copy = float(np.median([v for _, v in cal]))
+        factor = CALIBRATION_BYTES / (kib_copy * 1024.0)
+        ops = [(n, v) for n, v in disp[:-CALIBRATION_COPIES] if any(k in n for k in KERNEL_SYMBOLS[kernel])]
+        n_kern = len({n for n, _ in ops})
+        timed = ops[-steps * n_kern:]  # the timed launches (each launch = n_kern dispatches)
+        kib = sum(v for _, v in timed) / steps
+        out[counter] = {"kib_per_launch": round(kib, 1), "copy_kib": round(kib_copy, 1),
+                        "scale": round(factor, 4), "bytes_per_launch": int(kib * 1024 * factor),
+                        "dispatches_per_launch": n_kern}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        db = {}
+    db[workload] = {"kernel": kernel, "source_hash": source_hash(kernel),
+                    "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
+                    "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"], "commands": cmds}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+    return db[workload]
+
+
 def to_dev(arr, dtype):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
@@ -303,8 +360,17 @@ def main():
     ap.add_argument("--workload", default="gdn_cold32k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+                    help="end with three plain 1 GiB device copies (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="record HBM traffic of --workload from two rocprofv3 counter runs (no GPU needed)")
+    ap.add_argument("--counter-commands", nargs="*", default=[], help="the rocprofv3 commands, for the record")
     args = ap.parse_args()
+    if args.ingest_counters:
+        wl = WORKLOADS[args.workload]()
+        rec = ingest_counters(wl.name, wl.kernel, args.ingest_counters[0], args.ingest_counters[1], args.steps,
+                              args.counter_commands)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the method's multi-worker form "
               "is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
@@ -333,11 +399,11 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
 
     if args.copy_calibration:
-        n = (1 << 30) // 4
+        n = CALIBRATION_BYTES // 4
         src = torch.ones(n, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        for _ in range(CALIBRATION_COPIES):  # an elementwise kernel (a same-dtype copy_ may become a DMA copy)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
 
     value = wl.tokens / (ms_per_step / 1e3)
