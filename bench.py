@@ -39,8 +39,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "build_delta": ["segment_scan_amd/csrc/kernels/build_delta2.hip"],
     "build_sd": ["segment_scan_amd/csrc/kernels/build_sd.hip"],
-    "seam": ["segment_scan_amd/csrc/kernels/seam.hip"],
-    "compose": ["segment_scan_amd/csrc/kernels/compose.hip"],
+    "seam": ["segment_scan_amd/csrc/kernels/chain.hip"],
+    "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
 }
 
 
@@ -69,8 +69,8 @@ def measured_traffic(workload: str, kernel: str):
 KERNEL_SYMBOLS = {
     "build_delta": ["delta_prep_kernel", "delta_state_kernel", "build_delta_kernel"],
     "build_sd": ["build_sd_kernel"],
-    "seam": ["seam_kernel"],
-    "compose": ["compose_dense_kernel", "compose_elem_kernel"],
+    "seam": ["chain_kernel"],
+    "compose": ["chain_kernel", "compose_elem_kernel"],
 }
 CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
 CALIBRATION_BYTES = 1 << 30  # each reads and writes this many bytes
@@ -293,7 +293,9 @@ class WarmRequest(Workload):
         self.alg_bytes = (self.n_seg * n * (2 * d * d * 4 + 4) + ntok * n * (3 * d * 2 + 4) + ntok * n * d * 4
                           + 2 * n * d * d * 4)
         self.alg_flops = self.n_seg * n * 2.0 * d ** 3 + ntok * n * 6.0 * d * d
-        self.exec_flops = self.n_seg * n * 6 * 2.0 * d ** 3 + ntok * n * 6.0 * d * d * 2
+        # body products as three fp16 MFMA passes (hi*hi, hi*lo, lo*hi); the
+        # window arithmetic runs on the vector ALUs
+        self.exec_flops = self.n_seg * n * 3 * 2.0 * d ** 3
 
     def setup(self):
         import torch

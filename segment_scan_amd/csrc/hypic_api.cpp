@@ -262,13 +262,10 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   // S_out may be exactly S_init (in-place); any other overlap is rejected
   if (S_init && S_init != S_out) ins.push_back({S_init, sbytes, "S_init"});
   outs.push_back({S_out, sbytes, "S_out"});
-  if (S_init == S_out) {
-    // the in-place state must still not overlap anything else
-    if (prefix_states) ins.push_back({S_init, sbytes, "S_init"});
-  }
   if (prefix_states) outs.push_back({prefix_states, (size_t)n_seg * sbytes, "prefix_states"});
   if (g_total) outs.push_back({g_total, (size_t)n_chain * gate_len(fam, d) * 4, "g_total"});
   if (U_total) outs.push_back({U_total, (size_t)n_chain * d * d * 4, "U_total"});
+  // (an in-place S_init is covered as S_out: it may overlap nothing else)
   TRY(check_overlaps(ins, outs));
 
   hypic::ComposeArgs a;
@@ -282,7 +279,7 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   a.U_tot = U_total;
   a.n_seg = n_seg;
   a.n_chain = n_chain;
-  hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_compose_dense(d, a, (hipStream_t)stream)
+  hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_compose_chain(d, a, (hipStream_t)stream)
                                       : hypic::launch_compose_elem(fam, d, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hypic_compose launch");
   return ok();
@@ -340,7 +337,7 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   a.n_seg = n_seg;
   a.w = w;
   a.n_chain = n_chain;
-  hipError_t e = hypic::launch_seam(fam, d, seam->dtype == HYPIC_F32, a, (hipStream_t)stream);
+  hipError_t e = hypic::launch_seam_chain(d, seam->dtype == HYPIC_F32, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hypic_seam_step launch");
   return ok();
 }

@@ -77,9 +77,10 @@ hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_bloc
 size_t delta2_workspace_bytes(const SegTable& seg, int n_chain);
 hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream);
 hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t stream);
-hipError_t launch_compose_dense(int d, const ComposeArgs& a, hipStream_t stream);
+// dense composition and the delta seam step on the column-split chain kernel (chain.hip)
+hipError_t launch_compose_chain(int d, const ComposeArgs& a, hipStream_t stream);
+hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 // Whether the seam step is built for this family / size / option.
 bool seam_supported(int fam, int d, bool window_pairs);
-hipError_t launch_seam(int fam, int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 
 }  // namespace hypic

@@ -160,7 +160,7 @@ def compose_call(lib, fam=DELTA, n_seg=3, n_chain=2, d=128, p=None, S_init=None,
     (dict(S_out=A["S"] + 64), INVALID, "overlaps input pairs.S"),
     (dict(S_init=A["Sinit"], S_out=A["Sinit"] + 16), INVALID, "overlaps input S_init"),
     (dict(prefix=A["Sout"] + 16), INVALID, "overlap"),
-    (dict(S_init=A["Sinit"], S_out=A["Sinit"], prefix=A["Sinit"] + 1024), INVALID, "overlaps input S_init"),
+    (dict(S_init=A["Sinit"], S_out=A["Sinit"], prefix=A["Sinit"] + 1024), INVALID, "outputs S_out and prefix_states overlap"),
     (dict(gtot=A["gtot"] + 2), INVALID, "aligned"),
 ])
 def test_compose_rejects(lib, kwargs, status, msg):

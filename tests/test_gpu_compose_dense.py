@@ -46,3 +46,24 @@ def test_compose_dense_d64_one_segment():
     _check(g, U, S, None, "d64_one")
     g, U, S = synth.warm_pairs_layer(2, n_seg=5, n_head=3, d=64)
     _check(g, U, S, None, "d64_five", want_total=False)
+
+
+def test_compose_dense_many_chains_in_place():
+    """70 chains (one workgroup per chain; a count that is not a multiple of 8),
+    S_out the same buffer as S_init, prefix states and totals."""
+    import torch
+    g, U, S = synth.warm_pairs_layer(4, n_seg=3, n_head=70)
+    g = g - 0.01 * np.arange(g.size).reshape(g.shape) / g.size  # nonzero gates
+    g = g.astype(np.float32).astype(np.float64)
+    S_init = np.random.default_rng(4).standard_normal(S.shape[1:]).astype(np.float32).astype(np.float64)
+    announce("many_chains_in_place", "chains", 70)
+    st = dev_f32(S_init)
+    res = api.compose(DELTA, dev_f32(g), dev_f32(U), dev_f32(S), S_init=st, S_out=st, want_prefix=True,
+                      want_total=True)
+    torch.cuda.synchronize()
+    assert res["S_out"].data_ptr() == st.data_ptr()
+    ref = oracle.compose(DELTA, g, U, S, S_init=S_init, want_prefix=True, want_total=True)
+    assert_units_close("inplace.S_out", host(st), ref["S_out"], 1e-5, unit_dims=1)
+    assert_units_close("inplace.prefix", host(res["prefix"]), ref["prefix"], 1e-5)
+    assert_g_close("inplace.g_tot", host(res["g_tot"]), ref["g_tot"], 1e-5)
+    assert_units_close("inplace.U_tot", host(res["U_tot"]), ref["U_tot"], 1e-5, unit_dims=1)

@@ -107,3 +107,12 @@ def test_warm_reuse_full_size_layers_0_and_29():
         ow = o[:, sl].reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
         rw = ref["o"].reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
         assert_units_close("full.o.l%d" % layer, ow, rw, TOL["bf16"])
+
+
+def test_seam_many_chains_ragged_window():
+    """72 chains (one workgroup per chain), w = 13 (a full and a partial
+    8-token sub-chunk), random body pairs, nonzero start state."""
+    tk = synth.warm_seam_layer(9, n_seg=3, w=13, n_head=72)
+    body = synth.warm_pairs_layer(9, n_seg=3, n_head=72)
+    S0 = np.random.default_rng(9).standard_normal((72, 128, 128)).astype(np.float32).astype(np.float64)
+    check_seam(tk, 13, body, S0, "many_chains_w13", TOL["bf16"])
