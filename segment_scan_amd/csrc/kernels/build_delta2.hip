@@ -40,7 +40,6 @@ constexpr int D = 128;
 constexpr int C = 64;
 constexpr int KP = D + 4;  // 16-bit pitch of K [t][d] (fp16) and V [t][d] (bf16)
 constexpr int TP = C + 4;  // 16-bit pitch of K^T [d][t] and of A [t][t'] (fp16)
-constexpr int NP = 65;     // fp32 pitch of the inverse work array
 
 // Workspace record of one (chunk, chain): A0 (fp16, scaled rows), the row
 // scales (2^e as float) and the inclusive gate prefix G.
@@ -67,13 +66,6 @@ __device__ __forceinline__ f16x8 lds_a_perm_h(const f16_t* p, int off) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Standard-order fragment: 8 consecutive k from off.
-__device__ __forceinline__ f16x8 lds_frag_h(const f16_t* p, int off) {
-  const f16x4 lo = *reinterpret_cast<const f16x4*>(p + off);
-  const f16x4 hi = *reinterpret_cast<const f16x4*>(p + off + 4);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Elements 8m .. 8m+7 of an accumulator tile, times s, as an fp16 B fragment.
 __device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, float s) {
   f16x8 f;
@@ -86,22 +78,13 @@ __device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, float s) {
 // delta_prep: per (chunk, chain) A0 = (I + strict_lower(diag(b) K K^T))^-1 diag(b)
 // =====================================================================================
 
-struct PrepLds {
-  static constexpr int K_B = C * KP * 2;
-  static constexpr int OFF_N = K_B;
-  static constexpr int OFF_T = OFF_N + C * NP * 4;
-  static constexpr int OFF_P = OFF_T + 3 * 16 * 17 * 4;
-  static constexpr int LDS = OFF_P + 3 * C * 4;
-};
+// One wave per (chunk, chain): no barriers between its phases, and several
+// independent waves per SIMD to hide each one's latencies.
+constexpr int MP = C + 4;  // fp32 pitch of the M / A0 work array (16-byte rows)
 
-__global__ __launch_bounds__(256) void delta_prep_kernel(const BuildArgs a, const ChunkTable cks, unsigned char* ws) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[PrepLds::LDS];
-  f16_t* sK = reinterpret_cast<f16_t*>(smem);
-  float* sN = reinterpret_cast<float*>(smem + PrepLds::OFF_N);
-  float* sT = reinterpret_cast<float*>(smem + PrepLds::OFF_T);
-  float* sBeta = reinterpret_cast<float*>(smem + PrepLds::OFF_P);
-  float* sLg = sBeta + C;
-  float* sG = sLg + C;
+__global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, const ChunkTable cks, unsigned char* ws) {
+  __shared__ __attribute__((aligned(16))) float sM[C * MP];
+  __shared__ float sBeta[C];
 
   // workgroup -> (chunk of the launch, chain): consecutive workgroups take the
   // chains of one chunk, which share the rows of the token-major inputs
@@ -114,140 +97,109 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const BuildArgs a, cons
   }
   const int c0 = a.seg.off[lo] + (gchunk - cks.base[lo]) * C;
   const int nv = min(C, a.seg.off[lo + 1] - c0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int h = lane >> 5, l32 = lane & 31;
 
-  // ---- keys (fp16) and per-token scalars into LDS ---------------------------------
-  if (tid < 128) {
-    const int tb = tid & 7, db = tid >> 3;
-    const bf16_t* src = reinterpret_cast<const bf16_t*>(a.k);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int t = tb * 8 + r;
-      uint4 u = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
-      if (t >= nv) u = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint2*>(sK + t * KP + db * 8) = make_uint2(pk_f16_from_bf16x2(u.x), pk_f16_from_bf16x2(u.y));
-      *reinterpret_cast<uint2*>(sK + t * KP + db * 8 + 4) = make_uint2(pk_f16_from_bf16x2(u.z), pk_f16_from_bf16x2(u.w));
-    }
-  } else if (tid < 128 + C) {
-    const int t = tid - 128;
-    float b = 0.f, lg = 0.f;
-    if (t < nv) {
-      const size_t idx = (size_t)(c0 + t) * n_chain + chain;
-      b = load1<false>(a.beta, idx);
-      if (a.lg) lg = load1<false>(a.lg, idx);
-    }
-    sBeta[t] = b;
-    sLg[t] = lg;
+  // ---- per-token scalars: lane t holds token t; gate prefix by a wave scan --------
+  float beta = 0.f, lg = 0.f;
+  if (lane < nv) {
+    const size_t idx = (size_t)(c0 + lane) * n_chain + chain;
+    beta = load1<false>(a.beta, idx);
+    if (a.lg) lg = load1<false>(a.lg, idx);
   }
-  __syncthreads();
+  const float G = wave_incl_scan(lg);
+  sBeta[lane] = beta;
 
-  // ---- gate prefix (wave 3) and Gram tiles t > t' (waves 0-2) -> M0 --------------
-  if (wave == 3) {
-    sG[lane] = wave_incl_scan(sLg[lane]);
-  } else {
-    const int tt = (wave == 0) ? 0 : 1;
-    const int tp = (wave == 2) ? 1 : 0;
-    const f16_t* pKg = sK + l32 * KP + 8 * h;
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      acc = mfma32h(lds_frag_h(pKg + 32 * tt * KP, 16 * ks), lds_frag_h(pKg + 32 * tp * KP, 16 * ks), acc);
-    const int cc = 32 * tp + l32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = 32 * tt + acc_row(r, lane);
-      sN[rr * NP + cc] = (rr > cc) ? sBeta[rr] * acc[r] : 0.f;
-    }
-    if (wave == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sN[acc_row(r, lane) * NP + 32 + l32] = 0.f;
-    }
-  }
-  __syncthreads();
-
-  // ---- N = (I + M0)^-1: four 16 x 16 diagonal blocks, one per wave -----------------
-  // lane (column c, part p): partial sums over k = p (mod 4), combined across the
-  // four parts with xor-shuffles, so each row costs ~r/4 FMAs and two exchanges.
+  // ---- Gram K K^T on bf16 MFMA (exact products), fragments straight from HBM -------
+  // A and B fragments of a 32-token block are the same registers: lane l holds
+  // token 32 tb + (l & 31), channels 16 ks + 8h .. +7.
+  f32x16 g00 = zero16(), g10 = zero16(), g11 = zero16();
   {
-    const int b = wave;
-    const int cl = lane & 15, p = lane >> 4;
-    const float* Mb = sN + (16 * b) * NP + 16 * b;
-    float x[16];
+    const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.k);
+    const int t0 = min(l32, nv - 1), t1 = min(32 + l32, nv - 1);
+    const bool z0 = l32 >= nv, z1 = 32 + l32 >= nv;
+    const bf16_t* r0 = kb + ((size_t)(c0 + t0) * n_chain + chain) * D + 8 * h;
+    const bf16_t* r1 = kb + ((size_t)(c0 + t1) * n_chain + chain) * D + 8 * h;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < r; ++k)
-        if ((k & 3) == p && k >= cl) acc = fmaf(Mb[r * NP + k], x[k], acc);
-      acc += __shfl_xor(acc, 16, 64);
-      acc += __shfl_xor(acc, 32, 64);
-      x[r] = (r < cl) ? 0.f : ((r == cl) ? 1.f : -acc);
-    }
-    __syncthreads();  // every wave has read its block of M0
-    if (p == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sN[(16 * b + r) * NP + 16 * b + cl] = x[r];
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8 f0 = *reinterpret_cast<const bf16x8*>(r0 + 16 * ks);
+      bf16x8 f1 = *reinterpret_cast<const bf16x8*>(r1 + 16 * ks);
+      if (z0) f0 = bf16x8{};
+      if (z1) f1 = bf16x8{};
+      g00 = mfma32(f0, f0, g00);
+      g10 = mfma32(f1, f0, g10);
+      g11 = mfma32(f1, f1, g11);
     }
   }
-  // ---- block rows i = 1..3: T_ij = sum_{k=j}^{i-1} M_ik N_kj, N_ij = -N_ii T_ij ------
-  {
-    const int r = tid >> 4, cc = tid & 15;
+  // M = strict_lower(diag(beta) K K^T) into LDS (row-major; upper part unused)
+  __syncthreads();
 #pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      __syncthreads();
-      for (int j = 0; j < i; ++j) {
-        float acc = 0.f;
-        const float* Mrow = sN + (16 * i + r) * NP;
-        for (int k = j; k < i; ++k)
-#pragma unroll
-          for (int m = 0; m < 16; ++m) acc = fmaf(Mrow[16 * k + m], sN[(16 * k + m) * NP + 16 * j + cc], acc);
-        sT[(j * 16 + r) * 17 + cc] = acc;
-      }
-      __syncthreads();
-      for (int j = 0; j < i; ++j) {
-        float acc = 0.f;
-        const float* Nrow = sN + (16 * i + r) * NP + 16 * i;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) acc = fmaf(Nrow[m], sT[(j * 16 + m) * 17 + cc], acc);
-        sN[(16 * i + r) * NP + 16 * j + cc] = -acc;
-      }
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int row = acc_row(r, lane);
+    sM[row * MP + l32] = (row > l32) ? sBeta[row] * g00[r] : 0.f;
+    sM[(32 + row) * MP + l32] = sBeta[32 + row] * g10[r];
+    sM[(32 + row) * MP + 32 + l32] = (row > l32) ? sBeta[32 + row] * g11[r] : 0.f;
   }
   __syncthreads();
 
-  // ---- A0 = N diag(b), rows scaled by powers of two, to the workspace --------------
+  // ---- N = (I + M)^-1 by forward substitution: lane c owns column c -----------------
+  // N[r][c] = delta_rc - sum_{k<r} M[r][k] N[k][c]; rows of M are read as LDS
+  // broadcasts.  Entries above the diagonal are zero, so the sums need no mask.
+  const int c = lane;
+  float x[C];
+#pragma unroll
+  for (int r = 0; r < C; ++r) {
+    float acc0 = 0.f, acc1 = 0.f;
+    const float* Mr = sM + r * MP;
+#pragma unroll
+    for (int k4 = 0; k4 < r / 4; ++k4) {
+      const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
+      acc0 = fmaf(m4[0], x[4 * k4], acc0);
+      acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
+      acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
+      acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
+    }
+#pragma unroll
+    for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
+    x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
+  }
+  __syncthreads();  // every lane is done reading M
+
+  // ---- A0 = N diag(beta): column c scaled by beta_c; rows to fp16 with row scales --
+#pragma unroll
+  for (int r = 0; r < C; ++r) sM[r * MP + c] = x[r] * beta;
+  __syncthreads();
   unsigned char* rec = ws + (size_t)blockIdx.x * REC_BYTES;
   {
-    const int t = tid >> 2;
-    const int cb = (tid & 3) * 16;
-    float v[16];
+    const int t = lane;  // row of A0
+    const float* Ar = sM + t * MP;
     float m = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int tp = cb + j;
-      v[j] = (tp <= t) ? sN[t * NP + tp] * sBeta[tp] : 0.f;
-      m = fmaxf(m, fabsf(v[j]));
+    for (int j4 = 0; j4 < C / 4; ++j4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(Ar + 4 * j4);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
     int e = 0;
     if (m > 0.f) {
       frexpf(m, &e);
       e -= 14;  // row maximum into [2^13, 2^14)
     }
     const float s = ldexpf(1.f, -e);
-    f16x8 h0, h1;
+    f16x8* dst = reinterpret_cast<f16x8*>(rec + REC_A + t * C * 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h0[j] = (f16_t)(v[j] * s);
-      h1[j] = (f16_t)(v[8 + j] * s);
+    for (int j8 = 0; j8 < C / 8; ++j8) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(Ar + 8 * j8);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(Ar + 8 * j8 + 4);
+      f16x8 hv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hv[j] = (f16_t)(v0[j] * s);
+        hv[4 + j] = (f16_t)(v1[j] * s);
+      }
+      dst[j8] = hv;
     }
-    f16x8* dst = reinterpret_cast<f16x8*>(rec + REC_A + (t * C + cb) * 2);
-    dst[0] = h0;
-    dst[1] = h1;
-    if ((tid & 3) == 0) reinterpret_cast<float*>(rec + REC_RS)[t] = ldexpf(1.f, e);
-    if (tid < C) reinterpret_cast<float*>(rec + REC_G)[tid] = sG[tid];
+    reinterpret_cast<float*>(rec + REC_RS)[t] = ldexpf(1.f, e);
+    reinterpret_cast<float*>(rec + REC_G)[t] = G;
   }
 }
 
@@ -535,7 +487,7 @@ hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream)
   ChunkTable ct;
   const int n_chunks = chunks_of(a.seg, &ct);
   unsigned char* w = reinterpret_cast<unsigned char*>(ws);
-  hipLaunchKernelGGL(delta_prep_kernel, dim3(n_chunks * a.n_chain), dim3(256), 0, stream, a, ct, w);
+  hipLaunchKernelGGL(delta_prep_kernel, dim3(n_chunks * a.n_chain), dim3(64), 0, stream, a, ct, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(delta_state_kernel, dim3(a.seg.n_seg * a.n_chain), dim3(256), StateLds::LDS, stream, a, ct,
