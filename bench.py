@@ -189,6 +189,8 @@ class ColdRequest(Workload):
         self.S_out = torch.empty((self.H, self.d, self.d), device=dev)
         n_ws = api.seg_build_workspace_size(synth.DELTA, self.offsets, self.H, self.d, torch.bfloat16)
         self.ws = torch.empty(max(n_ws, 16), device=dev, dtype=torch.uint8)
+        n_cws = api.compose_workspace_size(synth.DELTA, self.n_seg, self.H, self.d)
+        self.cws = torch.empty(n_cws, device=dev, dtype=torch.uint8) if n_cws else None
 
     def step(self, ev0, ev1):
         from segment_scan_amd.synth import DELTA
@@ -196,7 +198,7 @@ class ColdRequest(Workload):
         self.api.seg_build(DELTA, self.offsets, self.k, self.v, self.beta, self.lg, out=(self.g, self.U, self.S),
                            workspace=self.ws)
         ev1.record()
-        self.api.compose(DELTA, self.g, self.U, self.S, S_out=self.S_out)
+        self.api.compose(DELTA, self.g, self.U, self.S, S_out=self.S_out, workspace=self.cws)
 
     def cpu_sample(self):
         import oracle

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 2
+#define HYPIC_ABI_VERSION 3
 
 typedef enum {
   HYPIC_OK = 0,
@@ -173,11 +173,30 @@ hypic_status hypic_seg_build_workspace_size(hypic_family fam, int n_seg, const i
  *   U_total        NULL or [n_chain, d_k, d_k] (DELTA only): U_{n-1} ... U_0.
  *                  With S_init = NULL, (g_total, U_total, S_out) is the pair
  *                  of the concatenated segments.
- * Errors as for hypic_seg_build.
+ *   workspace      NULL, or device scratch of workspace_bytes bytes, at least
+ *                  hypic_compose_workspace_size(); contents ignored on entry and
+ *                  undefined on exit, in use until the stream passes the call.
+ *                  For the DELTA family with few chains and no prefix states
+ *                  it lets the composition run in two levels: blocks of
+ *                  consecutive segments are composed in parallel (by
+ *                  associativity, [hwlabs, section 세그먼트 누적 전이 연산자]) and
+ *                  each chain then composes its block pairs in order.  The
+ *                  result equals the single-pass one up to rounding.
+ * Errors as for hypic_seg_build (a workspace that is smaller than required or
+ * overlaps another argument is HYPIC_E_INVALID).
  */
 hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v,
                            const hypic_cpairs* in, const float* S_init, float* S_out,
-                           float* prefix_states, float* g_total, float* U_total, void* stream);
+                           float* prefix_states, float* g_total, float* U_total,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hypic_compose_workspace_size -- bytes of workspace that enable the two-level
+ * schedule of hypic_compose for these sizes (0: not used).  want_prefix: 1 if
+ * prefix_states will be requested.  *bytes receives the size; enqueues nothing.
+ */
+hypic_status hypic_compose_workspace_size(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v,
+                                          int want_prefix, size_t* bytes);
 
 /*
  * hypic_seam_step -- advance the running state through each segment's seam

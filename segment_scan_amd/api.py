@@ -58,10 +58,12 @@ def load_library(path: str = LIB_PATH):
         lib.hypic_seg_build.argtypes = [I, I, P, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P,
                                         ctypes.c_size_t, P]
         lib.hypic_seg_build_workspace_size.argtypes = [I, I, P, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
-        lib.hypic_compose.argtypes = [I, I, I, I, I, ctypes.POINTER(Pairs), P, P, P, P, P, P]
+        lib.hypic_compose.argtypes = [I, I, I, I, I, ctypes.POINTER(Pairs), P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.hypic_compose_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.hypic_seam_step.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P, P,
                                         ctypes.POINTER(Pairs), P]
-        for f in (lib.hypic_seg_build, lib.hypic_seg_build_workspace_size, lib.hypic_compose, lib.hypic_seam_step):
+        for f in (lib.hypic_seg_build, lib.hypic_seg_build_workspace_size, lib.hypic_compose,
+                  lib.hypic_compose_workspace_size, lib.hypic_seam_step):
             f.restype = I
         lib.hypic_last_error.restype = ctypes.c_char_p
         lib.hypic_last_error.argtypes = []
@@ -163,9 +165,20 @@ def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor
     return g, U, S
 
 
+def compose_workspace_size(fam: int, n_seg: int, n_chain: int, d: int, want_prefix: bool = False) -> int:
+    """Bytes of device workspace that enable compose's two-level schedule (0: none)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().hypic_compose_workspace_size(fam, n_seg, n_chain, d, d, int(bool(want_prefix)),
+                                                       ctypes.byref(out)))
+    return out.value
+
+
 def compose(fam: int, g, U, S, S_init=None, S_out=None, prefix_states=None, g_total=None, U_total=None,
-            want_prefix: bool = False, want_total: bool = False, stream=None):
-    """Ordered composition of pairs [n_seg, n_chain, ...]; returns dict of outputs."""
+            want_prefix: bool = False, want_total: bool = False, workspace="auto", stream=None):
+    """Ordered composition of pairs [n_seg, n_chain, ...]; returns dict of outputs.
+
+    workspace: "auto" takes one of the size compose_workspace_size() reports from
+    torch's allocator, None runs the single-pass schedule, or a uint8 tensor."""
     n_seg, n_chain, dk, dv = S.shape
     dev = S.device
     if S_out is None:
@@ -176,9 +189,14 @@ def compose(fam: int, g, U, S, S_init=None, S_out=None, prefix_states=None, g_to
         g_total = torch.empty(_gate_shape(fam, (n_chain,), dk), device=dev, dtype=torch.float32)
     if want_total and fam == DELTA and U_total is None:
         U_total = torch.empty((n_chain, dk, dk), device=dev, dtype=torch.float32)
+    if isinstance(workspace, str):
+        need = compose_workspace_size(fam, n_seg, n_chain, dk, prefix_states is not None) if fam == DELTA else 0
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     pr = Pairs(_ptr(g), _ptr(U), _ptr(S))
     _check(load_library().hypic_compose(fam, n_seg, n_chain, dk, dv, ctypes.byref(pr), _ptr(S_init), _ptr(S_out),
-                                        _ptr(prefix_states), _ptr(g_total), _ptr(U_total), _stream(stream)))
+                                        _ptr(prefix_states), _ptr(g_total), _ptr(U_total), _ptr(workspace),
+                                        ws_bytes, _stream(stream)))
     return {"S_out": S_out, "prefix": prefix_states, "g_tot": g_total, "U_tot": U_total}
 
 

@@ -243,9 +243,17 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
   return ok();
 }
 
+hypic_status hypic_compose_workspace_size(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v,
+                                          int want_prefix, size_t* bytes) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
+  *bytes = fam == HYPIC_DELTA ? hypic::compose_workspace_bytes(d_k, n_seg, n_chain, want_prefix != 0) : 0;
+  return ok();
+}
+
 hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v, const hypic_cpairs* in,
                            const float* S_init, float* S_out, float* prefix_states, float* g_total,
-                           float* U_total, void* stream) {
+                           float* U_total, void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   const int d = d_k;
   if (!in) return fail(HYPIC_E_INVALID, "in is NULL");
@@ -266,6 +274,14 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   if (g_total) outs.push_back({g_total, (size_t)n_chain * gate_len(fam, d) * 4, "g_total"});
   if (U_total) outs.push_back({U_total, (size_t)n_chain * d * d * 4, "U_total"});
   // (an in-place S_init is covered as S_out: it may overlap nothing else)
+  const size_t ws_need =
+      fam == HYPIC_DELTA ? hypic::compose_workspace_bytes(d, n_seg, n_chain, prefix_states != nullptr) : 0;
+  if (workspace && ws_need > 0) {
+    if (workspace_bytes < ws_need)
+      return fail(HYPIC_E_INVALID, "workspace too small: %zu bytes given, %zu required", workspace_bytes, ws_need);
+    TRY(check_aligned(workspace, "workspace"));
+    outs.push_back({workspace, ws_need, "workspace"});
+  }
   TRY(check_overlaps(ins, outs));
 
   hypic::ComposeArgs a;
@@ -279,7 +295,9 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   a.U_tot = U_total;
   a.n_seg = n_seg;
   a.n_chain = n_chain;
-  hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_compose_chain(d, a, (hipStream_t)stream)
+  hipError_t e = (fam == HYPIC_DELTA)
+                     ? hypic::launch_compose_chain(d, a, ws_need > 0 ? workspace : nullptr, workspace_bytes,
+                                                   (hipStream_t)stream)
                                       : hypic::launch_compose_elem(fam, d, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hypic_compose launch");
   return ok();

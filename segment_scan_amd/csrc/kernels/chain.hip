@@ -23,7 +23,7 @@
 // running state lives in LDS as fp32 (column-major, so a B fragment is 32
 // contiguous bytes) and is split into hi + lo with a per-column power-of-two
 // scale taken from the column maxima its writers leave behind.  The product
-// keeps hi*hi + hi*lo + lo*hi on 32x32x16 fp16 MFMA: ~2^-21 relative per
+// keeps hi*hi + hi*lo + lo*hi on 32x32x16 fp16 MFMA: ~2^-22 relative per
 // operand, fp32 class, in three products where three-term bf16 needs six.  The
 // next pair's U and S tile are in flight during the current product.
 //
@@ -35,6 +35,8 @@
 //   S'   = exp(G_n) S + (Abar^T diag(exp(G_n - G)) K)^T R
 //   O    = diag(exp(G)) Q S + ((tril(Q K^T) o Gamma) Abar) R
 // so that both the new state and the outputs are one pass over R.
+#include <algorithm>
+
 #include "common.h"
 #include "../launch.h"
 
@@ -92,6 +94,14 @@ struct ChainArgs {
   int n_seg;
   int n_chain;
   int w;
+  // Blocked composition: when blk_len > 0 the grid holds n_units =
+  // ceil(n_seg / blk_len) * n_chain units; unit u composes segments
+  // [b * blk_len, min((b + 1) * blk_len, n_seg)) of chain c (b = u / n_chain,
+  // c = u % n_chain) from a zero state, and its outputs (S_out, U_tot, g_tot)
+  // are indexed by u -- a pairs array of the blocks.  blk_len = 0: one unit
+  // per chain over all segments.
+  int blk_len;
+  int n_units;
 };
 
 // power-of-two exponent that maps a block maximum m into [2^14, 2^15)
@@ -102,21 +112,14 @@ __device__ __forceinline__ int split_exp(float m) {
   return e - 15;
 }
 
-__device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-// 8 floats -> fp16 hi and lo fragments (x ~ hi + lo to ~2^-21 relative)
+// 8 floats -> fp16 hi and lo fragments, both rounded to nearest: |x - hi| <=
+// 2^-11 |x| and |x - hi - lo| <= 2^-22 |x| (within fp16's normal range)
 __device__ __forceinline__ void split_pair8(const float (&x)[8], f16x8& hi, f16x8& lo) {
-  uint32_t h[4], l[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    h[j] = pk_rtz(x[2 * j], x[2 * j + 1]);
-    const auto hv = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, h[j]);
-    l[j] = pk_rtz(x[2 * j] - (float)hv[0], x[2 * j + 1] - (float)hv[1]);
+  for (int j = 0; j < 8; ++j) {
+    hi[j] = (f16_t)x[j];
+    lo[j] = (f16_t)(x[j] - (float)hi[j]);
   }
-  hi = __builtin_bit_cast(f16x8, make_uint4(h[0], h[1], h[2], h[3]));
-  lo = __builtin_bit_cast(f16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 template <int D, int NCB, bool SEAM, bool IN_F32>
@@ -143,12 +146,17 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
     const int blk = blockIdx.x / (8 * NCG), rem = blockIdx.x % (8 * NCG);
     cgrp = rem / 8;
     chain = blk * 8 + (rem % 8);
-    if (chain >= a.n_chain) return;  // padding of the chain count to a multiple of 8
+    if (chain >= a.n_units) return;  // padding of the unit count to a multiple of 8
   }
   const bool ut = blockIdx.y == 1;  // this workgroup composes U_total instead of S
   const int n_chain = a.n_chain;
   const int col0 = cgrp * COLS;     // first state column of the workgroup
-  const size_t chain_off = (size_t)chain * D * D;
+  // pairs of this unit: index pidx + s * n_chain for its segments s < nseg
+  const int blk = a.blk_len > 0 ? chain / n_chain : 0;
+  const int pidx = a.blk_len > 0 ? blk * a.blk_len * n_chain + chain % n_chain : chain;
+  const int nseg = a.blk_len > 0 ? min(a.blk_len, a.n_seg - blk * a.blk_len) : a.n_seg;
+  const size_t chain_off = (size_t)chain * D * D;  // outputs, start state, tokens: by unit
+  const size_t pair_off = (size_t)pidx * D * D;
   const size_t seg_stride = (size_t)n_chain * D * D;
   const bool pairs = a.S != nullptr;
 
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   // ---- helpers ---------------------------------------------------------------------
   f32x4 ureg[LDU];
   auto issue_U = [&](int s) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.U + (size_t)s * seg_stride + chain_off);
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.U + (size_t)s * seg_stride + pair_off);
 #pragma unroll
     for (int i = 0; i < LDU; ++i) ureg[i] = src[i * NTH + tid];
   };
@@ -185,14 +193,15 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
       for (int o = 1; o < D / 4; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       const int e = split_exp(m);
       const float s = ldexpf(1.f, -e);
-      const float x0 = ureg[i][0] * s, x1 = ureg[i][1] * s, x2 = ureg[i][2] * s, x3 = ureg[i][3] * s;
-      const uint32_t h01 = pk_rtz(x0, x1), h23 = pk_rtz(x2, x3);
-      const auto v01 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, h01);
-      const auto v23 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, h23);
-      const uint32_t l01 = pk_rtz(x0 - (float)v01[0], x1 - (float)v01[1]);
-      const uint32_t l23 = pk_rtz(x2 - (float)v23[0], x3 - (float)v23[1]);
-      *reinterpret_cast<uint2*>(sUh + row * UP + 4 * c4) = make_uint2(h01, h23);
-      *reinterpret_cast<uint2*>(sUl + row * UP + 4 * c4) = make_uint2(l01, l23);
+      f16x4 hv, lv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float xs = ureg[i][j] * s;
+        hv[j] = (f16_t)xs;
+        lv[j] = (f16_t)(xs - (float)hv[j]);
+      }
+      *reinterpret_cast<f16x4*>(sUh + row * UP + 4 * c4) = hv;
+      *reinterpret_cast<f16x4*>(sUl + row * UP + 4 * c4) = lv;
       if (c4 == 0) sRF[row] = ldexpf(1.f, e);
     }
   };
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   };
   f32x16 Si;  // S tile of the next pair
   auto issue_Si = [&](int s) {
-    const float* p = tile_ptr(a.S + (size_t)s * seg_stride + chain_off);
+    const float* p = tile_ptr(a.S + (size_t)s * seg_stride + pair_off);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -248,13 +257,13 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   if (pairs) {
     issue_U(0);
     if (!ut) issue_Si(0);
-    g_next = ut ? 0.f : a.g[chain];
+    g_next = ut ? 0.f : a.g[pidx];
     store_U();
-    if (a.n_seg > 1) issue_U(1);
+    if (nseg > 1) issue_U(1);
   }
   __syncthreads();
 
-  for (int seg = 0; seg < a.n_seg; ++seg) {
+  for (int seg = 0; seg < nseg; ++seg) {
     refresh();
     // ---- seam window of this segment -----------------------------------------------
     if constexpr (SEAM) {
@@ -489,14 +498,14 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
       }
       __syncthreads();  // every wave is done with sU and the state
       put_tile(St);
-      if (seg + 1 < a.n_seg) {
+      if (seg + 1 < nseg) {
         if (!ut && a.prefix) store_tile(a.prefix + (size_t)(seg + 1) * seg_stride + chain_off, St);
         store_U();
         if (!ut) {
           issue_Si(seg + 1);
-          g_next = a.g[(size_t)(seg + 1) * n_chain + chain];
+          g_next = a.g[pidx + (size_t)(seg + 1) * n_chain];
         }
-        if (seg + 2 < a.n_seg) issue_U(seg + 2);
+        if (seg + 2 < nseg) issue_U(seg + 2);
       }
       __syncthreads();
     }
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   }
   if (!ut && a.g_tot && cgrp == 0 && tid == 0) {
     double acc = 0.0;
-    for (int s = 0; s < a.n_seg; ++s) acc += (double)a.g[(size_t)s * n_chain + chain];
+    for (int s = 0; s < nseg; ++s) acc += (double)a.g[pidx + (size_t)s * n_chain];
     a.g_tot[chain] = (float)acc;
   }
 }
@@ -523,7 +532,7 @@ hipError_t launch_chain_t(const ChainArgs& a, bool want_ut, hipStream_t stream) 
       reinterpret_cast<const void*>(&chain_kernel<D, NCB, SEAM, IN_F32>),
       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (attr != hipSuccess) return attr;
-  const int nx = Cfg::NCG == 1 ? a.n_chain : ((a.n_chain + 7) / 8) * 8 * Cfg::NCG;
+  const int nx = Cfg::NCG == 1 ? a.n_units : ((a.n_units + 7) / 8) * 8 * Cfg::NCG;
   hipLaunchKernelGGL((chain_kernel<D, NCB, SEAM, IN_F32>), dim3(nx, want_ut ? 2 : 1), dim3(Cfg::NTH), Cfg::LDS,
                      stream, a);
   return hipGetLastError();
@@ -534,14 +543,78 @@ hipError_t launch_chain_t(const ChainArgs& a, bool want_ut, hipStream_t stream) 
 template <int D, bool SEAM, bool IN_F32>
 hipError_t launch_chain_d(const ChainArgs& a, bool want_ut, hipStream_t stream) {
   constexpr int NCBT = D / 32;
-  if (a.n_chain * NCBT <= 256) return launch_chain_t<D, 1, SEAM, IN_F32>(a, want_ut, stream);
+  if (a.n_units * NCBT <= 256) return launch_chain_t<D, 1, SEAM, IN_F32>(a, want_ut, stream);
   return launch_chain_t<D, NCBT, SEAM, IN_F32>(a, want_ut, stream);
 }
 
 }  // namespace
 
-hipError_t launch_compose_chain(int d, const ComposeArgs& c, hipStream_t stream) {
+namespace {
+// Two-level schedule for few chains: about 128 (block, chain) units compose
+// their blocks in parallel, then each chain composes its block pairs in order.
+bool tree_plan(int d, int n_seg, int n_chain, bool prefix, int* blk_len, int* n_blocks) {
+  if (prefix || n_seg < 8 || n_chain * (d / 32) > 256) return false;
+  int nb = std::max(2, std::min(n_seg / 4, 128 / n_chain));
+  const int bl = (n_seg + nb - 1) / nb;
+  *blk_len = bl;
+  *n_blocks = (n_seg + bl - 1) / bl;
+  return *n_blocks >= 2;
+}
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+size_t compose_workspace_bytes(int d, int n_seg, int n_chain, bool prefix) {
+  int bl, nb;
+  if (!tree_plan(d, n_seg, n_chain, prefix, &bl, &nb)) return 0;
+  const size_t units = (size_t)nb * n_chain;
+  return align256(units * 4) + 2 * units * d * d * 4;
+}
+
+hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int bl, nb;
+  const size_t need = compose_workspace_bytes(d, c.n_seg, c.n_chain, c.prefix != nullptr);
+  if (need > 0 && ws != nullptr && ws_bytes >= need &&
+      tree_plan(d, c.n_seg, c.n_chain, c.prefix != nullptr, &bl, &nb)) {
+    const size_t units = (size_t)nb * c.n_chain;
+    float* wg = reinterpret_cast<float*>(ws);
+    float* wU = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + align256(units * 4));
+    float* wS = wU + units * d * d;
+    ChainArgs a1{};  // level 1: every (block, chain) from a zero state, with its U product and gate sum
+    a1.g = c.g;
+    a1.U = c.U;
+    a1.S = c.S;
+    a1.S_out = wS;
+    a1.g_tot = wg;
+    a1.U_tot = wU;
+    a1.n_seg = c.n_seg;
+    a1.n_chain = c.n_chain;
+    a1.blk_len = bl;
+    a1.n_units = (int)units;
+    ChainArgs a2{};  // level 2: the block pairs of each chain in order
+    a2.g = wg;
+    a2.U = wU;
+    a2.S = wS;
+    a2.S_in = c.S_init;
+    a2.S_out = c.S_out;
+    a2.g_tot = c.g_tot;
+    a2.U_tot = c.U_tot;
+    a2.n_seg = nb;
+    a2.n_chain = c.n_chain;
+    a2.n_units = c.n_chain;
+    hipError_t e;
+    if (d == 128) {
+      e = launch_chain_d<128, false, false>(a1, true, stream);
+      if (e == hipSuccess) e = launch_chain_d<128, false, false>(a2, c.U_tot != nullptr, stream);
+    } else if (d == 64) {
+      e = launch_chain_d<64, false, false>(a1, true, stream);
+      if (e == hipSuccess) e = launch_chain_d<64, false, false>(a2, c.U_tot != nullptr, stream);
+    } else {
+      e = hipErrorInvalidValue;
+    }
+    return e;
+  }
   ChainArgs a{};
+  a.n_units = c.n_chain;
   a.g = c.g;
   a.U = c.U;
   a.S = c.S;
@@ -564,6 +637,7 @@ bool seam_supported(int fam, int d, bool window_pairs) {
 
 hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& s, hipStream_t stream) {
   ChainArgs a{};
+  a.n_units = s.n_chain;
   a.g = s.bg;
   a.U = s.bU;
   a.S = s.bS;

@@ -78,7 +78,10 @@ size_t delta2_workspace_bytes(const SegTable& seg, int n_chain);
 hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream);
 hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t stream);
 // dense composition and the delta seam step on the column-split chain kernel (chain.hip)
-hipError_t launch_compose_chain(int d, const ComposeArgs& a, hipStream_t stream);
+// With a workspace of compose_workspace_bytes() (0 when the schedule does not
+// apply), few-chain compositions without prefix states run in two levels.
+size_t compose_workspace_bytes(int d, int n_seg, int n_chain, bool prefix);
+hipError_t launch_compose_chain(int d, const ComposeArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 // Whether the seam step is built for this family / size / option.
 bool seam_supported(int fam, int d, bool window_pairs);

@@ -42,15 +42,15 @@ def test_library_exports_every_declared_symbol(lib):
     with open(HEADER) as f:
         text = f.read()
     declared = set(re.findall(r"\b(hypic_[a-z_]+)\s*\(", text))
-    assert {"hypic_seg_build", "hypic_seg_build_workspace_size", "hypic_compose", "hypic_seam_step",
-            "hypic_last_error", "hypic_abi_version"} <= declared
+    assert {"hypic_seg_build", "hypic_seg_build_workspace_size", "hypic_compose", "hypic_compose_workspace_size",
+            "hypic_seam_step", "hypic_last_error", "hypic_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\b(hypic_[a-z_]+)\b", out))
     assert declared <= exported, declared - exported
     for name in declared:
         getattr(lib, name)
-    assert lib.hypic_abi_version() == 2
+    assert lib.hypic_abi_version() == 3
 
 
 def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
@@ -82,6 +82,22 @@ def ws_size(lib, fam=DELTA, offsets=(0, 64, 128), n_chain=2, d=128, dtype=BF16):
     out = ctypes.c_size_t(123)
     st = lib.hypic_seg_build_workspace_size(fam, len(offsets) - 1, off, n_chain, d, d, dtype, ctypes.byref(out))
     return st, out.value
+
+
+def test_compose_workspace_size(lib):
+    """The two-level schedule applies to the dense family with few chains and no
+    prefix states: one block pair (g, U, S) per (block, chain), about 128 units."""
+    def cws(fam=DELTA, n_seg=64, n_chain=32, d=128, prefix=0):
+        out = ctypes.c_size_t(7)
+        st = lib.hypic_compose_workspace_size(fam, n_seg, n_chain, d, d, prefix, ctypes.byref(out))
+        return st, out.value
+    units = 4 * 32  # 64 segments in 4 blocks of 16, 32 chains
+    assert cws() == (0, ((units * 4 + 255) // 256) * 256 + 2 * units * 128 * 128 * 4)
+    assert cws(prefix=1) == (0, 0)
+    assert cws(n_chain=480) == (0, 0)
+    assert cws(n_seg=4) == (0, 0)
+    assert cws(fam=SCALAR) == (0, 0)
+    assert cws(d=96)[0] == UNSUPPORTED
 
 
 def test_workspace_size(lib):
@@ -143,9 +159,10 @@ def test_seg_build_rejects(lib, kwargs, status, msg):
 
 
 def compose_call(lib, fam=DELTA, n_seg=3, n_chain=2, d=128, p=None, S_init=None, S_out=A["Sout"], prefix=None,
-                 gtot=None, Utot=None):
+                 gtot=None, Utot=None, ws=None, ws_bytes=0):
     p = pairs(fam) if p is None else p
-    return lib.hypic_compose(fam, n_seg, n_chain, d, d, ctypes.byref(p), S_init, S_out, prefix, gtot, Utot, None)
+    return lib.hypic_compose(fam, n_seg, n_chain, d, d, ctypes.byref(p), S_init, S_out, prefix, gtot, Utot, ws,
+                             ws_bytes, None)
 
 
 @pytest.mark.parametrize("kwargs,status,msg", [
@@ -162,6 +179,9 @@ def compose_call(lib, fam=DELTA, n_seg=3, n_chain=2, d=128, p=None, S_init=None,
     (dict(prefix=A["Sout"] + 16), INVALID, "overlap"),
     (dict(S_init=A["Sinit"], S_out=A["Sinit"], prefix=A["Sinit"] + 1024), INVALID, "outputs S_out and prefix_states overlap"),
     (dict(gtot=A["gtot"] + 2), INVALID, "aligned"),
+    (dict(n_seg=64, ws=A["ws"], ws_bytes=1024), INVALID, "workspace too small"),
+    (dict(n_seg=64, ws=A["ws"] + 8, ws_bytes=WS_BYTES), INVALID, "workspace is not 16-byte aligned"),
+    (dict(n_seg=64, ws=A["S"] + 64, ws_bytes=WS_BYTES), INVALID, "overlap"),
 ])
 def test_compose_rejects(lib, kwargs, status, msg):
     assert compose_call(lib, **kwargs) == status

@@ -67,3 +67,26 @@ def test_compose_dense_many_chains_in_place():
     assert_units_close("inplace.prefix", host(res["prefix"]), ref["prefix"], 1e-5)
     assert_g_close("inplace.g_tot", host(res["g_tot"]), ref["g_tot"], 1e-5)
     assert_units_close("inplace.U_tot", host(res["U_tot"]), ref["U_tot"], 1e-5, unit_dims=1)
+
+
+def test_compose_dense_two_level_schedule():
+    """Few chains, no prefix states: with a workspace the composition runs in two
+    levels (37 segments -> 8 blocks of up to 5, the last one ragged); S_out,
+    g_total and U_total must match the oracle, and the single-pass schedule."""
+    import torch
+    g, U, S = synth.warm_pairs_layer(5, n_seg=37, n_head=5)
+    g = (g - 0.02 * np.arange(g.size).reshape(g.shape) / g.size).astype(np.float32).astype(np.float64)
+    S_init = np.random.default_rng(5).standard_normal(S.shape[1:]).astype(np.float32).astype(np.float64)
+    need = api.compose_workspace_size(DELTA, 37, 5, 128)
+    assert need > 0
+    announce("two_level", "segs", 37, "chains", 5, "workspace", need)
+    dg, dU, dS, dI = dev_f32(g), dev_f32(U), dev_f32(S), dev_f32(S_init)
+    ws = torch.full((need,), 0x7F, device="cuda", dtype=torch.uint8)
+    tree = api.compose(DELTA, dg, dU, dS, S_init=dI, want_total=True, workspace=ws)
+    flat = api.compose(DELTA, dg, dU, dS, S_init=dI, want_total=True, workspace=None)
+    torch.cuda.synchronize()
+    ref = oracle.compose(DELTA, g, U, S, S_init=S_init, want_total=True)
+    for name, res in (("tree", tree), ("flat", flat)):
+        assert_units_close(name + ".S_out", host(res["S_out"]), ref["S_out"], 1e-5, unit_dims=1)
+        assert_g_close(name + ".g_tot", host(res["g_tot"]), ref["g_tot"], 1e-5)
+        assert_units_close(name + ".U_tot", host(res["U_tot"]), ref["U_tot"], 1e-5, unit_dims=1)
