@@ -217,8 +217,11 @@ hypic_status hypic_compose_workspace_size(hypic_family fam, int n_seg, int n_cha
  *   body           NULL (windows only) or cached body pairs [n_seg, n_chain, ...].
  *   S_run          [n_chain, d_k, d_v], read and overwritten with the final state.
  *   o_out          [n_seg * w, n_chain, d_v] fp32.
- *   window_out     NULL, or each window's own pair (T_W, S(W|0)) written to
- *                  g [n_seg, n_chain](DIAG: [.., d_k]), U (DELTA), S [n_seg, n_chain, d_k, d_v].
+ *   window_out     NULL, or each window's own pair (T_W, S(W|0)), the pair a
+ *                  segment build of the window tokens would give: g [n_seg,
+ *                  n_chain] (DIAG: [.., d_k]) and S [n_seg, n_chain, d_k, d_v]
+ *                  required, U [n_seg, n_chain, d_k, d_k] for DELTA only.  It
+ *                  satisfies S_after = T_W S_before + S(W|0) for each window.
  * Errors as for hypic_seg_build.
  */
 hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, int d_k, int d_v,

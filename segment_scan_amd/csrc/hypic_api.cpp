@@ -320,8 +320,7 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   outs.push_back({S_run, (size_t)n_chain * d * d * 4, "S_run"});
   outs.push_back({o_out, n_tok * n_chain * d * 4, "o_out"});
   if (window_out) {
-    if (!window_out->S || (fam != HYPIC_NAIVE && !window_out->g))
-      return fail(HYPIC_E_INVALID, "window_out needs S and g");
+    if (!window_out->S || !window_out->g) return fail(HYPIC_E_INVALID, "window_out needs S and g");
     if (fam == HYPIC_DELTA && !window_out->U) return fail(HYPIC_E_INVALID, "window_out.U is required for delta");
     if (fam != HYPIC_DELTA && window_out->U) return fail(HYPIC_E_INVALID, "window_out.U is only defined for delta");
     TRY(check_aligned(window_out->S, "window_out.S"));
@@ -333,9 +332,7 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
     if (window_out->U) outs.push_back({window_out->U, units * d * d * 4, "window_out.U"});
   }
   TRY(check_overlaps(ins, outs));
-  if (!hypic::seam_supported(fam, d, window_out != nullptr))
-    return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_step: family %d%s is not built", (int)fam,
-                window_out ? " with window pairs" : "");
+  const bool f32 = seam->dtype == HYPIC_F32;
 
   hypic::SeamArgs a;
   a.q = seam->q;
@@ -355,8 +352,32 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   a.n_seg = n_seg;
   a.w = w;
   a.n_chain = n_chain;
-  hipError_t e = hypic::launch_seam_chain(d, seam->dtype == HYPIC_F32, a, (hipStream_t)stream);
+  hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_seam_chain(d, f32, a, (hipStream_t)stream)
+                                      : hypic::launch_seam_elem(fam, d, f32, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hypic_seam_step launch");
+  if (window_out) {
+    // each window's own pair depends only on its tokens: the segment build of
+    // the windows (segments of w tokens), on the single-kernel delta path
+    hypic::BuildArgs b;
+    b.k = seam->k;
+    b.v = seam->v;
+    b.beta = seam->beta;
+    b.lg = seam->log_gate;
+    b.g = window_out->g;
+    b.U = window_out->U;
+    b.S = window_out->S;
+    b.n_chain = n_chain;
+    b.gate_per_chain = seam->gate_per_chain ? 1 : 0;
+    for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
+      const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
+      b.seg.n_seg = ns;
+      b.seg.seg_base = s0;
+      for (int i = 0; i <= ns; ++i) b.seg.off[i] = (s0 + i) * w;
+      e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta_single(d, f32, b, ns * n_chain, (hipStream_t)stream)
+                               : hypic::launch_build_sd(fam, d, f32, b, ns * n_chain, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "hypic_seam_step window pairs launch");
+    }
+  }
   return ok();
 }
 

@@ -456,12 +456,16 @@ size_t build_delta_workspace(int d, bool in_f32, const SegTable& seg, int n_chai
   return use_delta2(d, in_f32, seg) ? delta2_workspace_bytes(seg, n_chain) : 0;
 }
 
-hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_blocks, void* ws,
-                              hipStream_t stream) {
-  if (use_delta2(d, in_f32, a.seg)) return launch_build_delta2(a, ws, stream);
+hipError_t launch_build_delta_single(int d, bool in_f32, const BuildArgs& a, int n_blocks, hipStream_t stream) {
   if (d == 128) return in_f32 ? launch_t<128, true>(a, n_blocks, stream) : launch_t<128, false>(a, n_blocks, stream);
   if (d == 64) return in_f32 ? launch_t<64, true>(a, n_blocks, stream) : launch_t<64, false>(a, n_blocks, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_blocks, void* ws,
+                              hipStream_t stream) {
+  if (use_delta2(d, in_f32, a.seg)) return launch_build_delta2(a, ws, stream);
+  return launch_build_delta_single(d, in_f32, a, n_blocks, stream);
 }
 
 }  // namespace hypic

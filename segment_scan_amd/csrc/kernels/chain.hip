@@ -631,10 +631,6 @@ hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws
   return hipErrorInvalidValue;
 }
 
-bool seam_supported(int fam, int d, bool window_pairs) {
-  return fam == 3 && (d == 64 || d == 128) && !window_pairs;
-}
-
 hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& s, hipStream_t stream) {
   ChainArgs a{};
   a.n_units = s.n_chain;

@@ -73,6 +73,8 @@ constexpr int kDelta2MaxSegLen = 2048;
 size_t build_delta_workspace(int d, bool in_f32, const SegTable& seg, int n_chain);
 hipError_t launch_build_delta(int d, bool in_f32, const BuildArgs& a, int n_blocks, void* ws,
                               hipStream_t stream);
+// the single-kernel path for any size (no workspace)
+hipError_t launch_build_delta_single(int d, bool in_f32, const BuildArgs& a, int n_blocks, hipStream_t stream);
 // the two-kernel path (build_delta2.hip)
 size_t delta2_workspace_bytes(const SegTable& seg, int n_chain);
 hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream);
@@ -83,7 +85,7 @@ hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t
 size_t compose_workspace_bytes(int d, int n_seg, int n_chain, bool prefix);
 hipError_t launch_compose_chain(int d, const ComposeArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
-// Whether the seam step is built for this family / size / option.
-bool seam_supported(int fam, int d, bool window_pairs);
+// seam step of the naive, scalar and diagonal families (seam_elem.hip)
+hipError_t launch_seam_elem(int fam, int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 
 }  // namespace hypic

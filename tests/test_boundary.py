@@ -206,6 +206,10 @@ def seam_call(lib, fam=DELTA, n_seg=4, w=8, n_chain=2, d=128, t=None, body="defa
     (dict(S_run=A["S"]), INVALID, "overlaps input pairs.S"),
     (dict(body=Pairs(A["g"], None, A["S"])), INVALID, "required for the delta"),
     (dict(win=Pairs(A["wg"], None, A["wS"])), INVALID, "window_out.U"),
+    (dict(fam=NAIVE, t=toks(NAIVE, q=True), body=pairs(NAIVE), win=Pairs(None, None, A["wS"])), INVALID,
+     "window_out needs S and g"),
+    (dict(fam=SCALAR, t=toks(SCALAR, q=True), body=pairs(SCALAR), win=Pairs(A["wg"], A["wU"], A["wS"])), INVALID,
+     "only defined for delta"),
     (dict(d=256), UNSUPPORTED, "64, 128"),
 ])
 def test_seam_rejects(lib, kwargs, status, msg):

@@ -116,3 +116,55 @@ def test_seam_many_chains_ragged_window():
     body = synth.warm_pairs_layer(9, n_seg=3, n_head=72)
     S0 = np.random.default_rng(9).standard_normal((72, 128, 128)).astype(np.float32).astype(np.float64)
     check_seam(tk, 13, body, S0, "many_chains_w13", TOL["bf16"])
+
+
+def _family_tokens(kind, n_seg, L, n_chain, d=128, dtype="bf16"):
+    if kind == "naive":
+        return synth.naive(n_seg=n_seg, L=L, n_chain=n_chain, d=d, dtype=dtype)
+    if kind == "retnet":
+        return synth.retnet(n_seg=n_seg, L=L, n_chain=n_chain, d=d, dtype=dtype)
+    if kind == "mamba2":
+        return synth.mamba2_like(n_seg=n_seg, L=L, n_chain=n_chain, d=d, dtype=dtype)
+    if kind == "gla":
+        return synth.gla(n_seg=n_seg, L=L, n_chain=n_chain, d=d, dtype=dtype)
+    return synth.warm_seam_layer(11, n_seg=n_seg, w=L, n_head=n_chain, d=d, dtype=dtype, gate_scale=1.0 / 16)
+
+
+def _check_family_seam(kind, w, d, dtype, tol):
+    import torch
+    n_seg, H = 5, 4
+    tw = _family_tokens(kind, n_seg, w, H, d, dtype)  # the windows
+    tb = _family_tokens(kind, n_seg, 40, H, d, dtype)  # segment bodies -> cached pairs
+    fam = tw.fam
+    offs = synth.even_offsets(n_seg, 40)
+    body = oracle.build_pairs(fam, offs, tb.k, tb.v, tb.beta, tb.log_gate, bool(tb.gate_per_chain))
+    body32 = tuple(None if x is None else x.astype(np.float32).astype(np.float64) for x in body)
+    S0 = np.random.default_rng(3).standard_normal((H, d, d)).astype(np.float32).astype(np.float64)
+    announce("family_seam", kind, "w", w, "d", d, dtype)
+    up = upload_tokens(tw, with_q=True)
+    res = api.seam_step(fam, w, up["q"], up["k"], up["v"], up["beta"], up["log_gate"], bool(tw.gate_per_chain),
+                        body=tuple(None if x is None else dev_f32(x) for x in body32), S_run=dev_f32(S0),
+                        want_window_pairs=True)
+    torch.cuda.synchronize()
+    ref = oracle.seam(fam, n_seg, w, tw.q, tw.k, tw.v, tw.beta, tw.log_gate, bool(tw.gate_per_chain), body=body32,
+                      S_run=S0, want_window_pairs=True)
+    assert_units_close(kind + ".S_run", host(res["S_run"]), ref["S_run"], tol, unit_dims=1)
+    ow = host(res["o"]).reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
+    rw = ref["o"].reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
+    assert_units_close(kind + ".o", ow, rw, tol)
+    assert_units_close(kind + ".wS", host(res["wS"]), ref["wS"], tol)
+    np.testing.assert_allclose(host(res["wg"]), ref["wg"], rtol=tol, atol=tol)
+    if ref["wU"] is not None:
+        assert_units_close(kind + ".wU", host(res["wU"]), ref["wU"], tol)
+
+
+@pytest.mark.parametrize("kind", ["naive", "retnet", "mamba2", "gla", "gdn"])
+@pytest.mark.parametrize("w", [8, 13])
+def test_seam_every_family_with_window_pairs(kind, w):
+    """Window recurrence + body pairs of every family, and each window's own pair."""
+    _check_family_seam(kind, w, 128, "bf16", TOL["bf16"])
+
+
+@pytest.mark.parametrize("kind", ["retnet", "gla", "gdn"])
+def test_seam_families_fp32_d64(kind):
+    _check_family_seam(kind, 5, 64, "f32", TOL["f32"])
