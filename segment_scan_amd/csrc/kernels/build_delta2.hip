@@ -66,11 +66,18 @@ __device__ __forceinline__ f16x8 lds_a_perm_h(const f16_t* p, int off) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Elements 8m .. 8m+7 of an accumulator tile, times s, as an fp16 B fragment.
-__device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, float s) {
+// Elements 8m .. 8m+7 of an accumulator tile, times 2^-e, as an fp16 B fragment
+// (e is wave-uniform; e = 0 skips the multiply).
+__device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, int e) {
   f16x8 f;
+  if (e == 0) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = (f16_t)(acc[8 * m + j] * s);
+    for (int j = 0; j < 8; ++j) f[j] = (f16_t)acc[8 * m + j];
+  } else {
+    const float s = ldexpf(1.f, -e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (f16_t)(acc[8 * m + j] * s);
+  }
   return f;
 }
 
@@ -207,151 +214,182 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
 // delta_state: per unit, [U | S] in registers, three MFMA products per chunk
 // =====================================================================================
 
-struct StateLds {
+struct StateLds {  // one staging buffer; the kernel keeps two
   static constexpr int O_K = 0;
   static constexpr int O_KT = O_K + C * KP * 2;
   static constexpr int O_V = O_KT + D * TP * 2;
-  static constexpr int O_A0 = O_V + C * KP * 2;
+  static constexpr int O_A0 = O_V + D * TP * 2;
   static constexpr int O_AB = O_A0 + C * TP * 2;
   static constexpr int O_SM = O_AB + C * TP * 2;   // eG[64], fac0[64], facb[64], misc[64]
-  static constexpr int LDS = O_SM + 4 * C * 4;
+  static constexpr int BUF = O_SM + 4 * C * 4;
+  static constexpr int LDS = 2 * BUF;
 };
 
-__global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, const ChunkTable cks,
+// 8 x 8 transpose of 16-bit elements held as 8 rows of 4 dwords: dword j of
+// output column cc packs element cc of rows 2j (low half) and 2j+1 (high half).
+__device__ __forceinline__ void store_transposed8(const uint4 (&rows)[8], f16_t* dst, int pitch) {
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+    auto w = [&](int r) {
+      const uint4 u = rows[r];
+      return (cc >> 1) == 0 ? u.x : (cc >> 1) == 1 ? u.y : (cc >> 1) == 2 ? u.z : u.w;
+    };
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(w(2 * j + 1), w(2 * j), sel);
+    *reinterpret_cast<uint2*>(dst + cc * pitch) = make_uint2(o[0], o[1]);
+    *reinterpret_cast<uint2*>(dst + cc * pitch + 4) = make_uint2(o[2], o[3]);
+  }
+}
+
+// 8 waves: wave w keeps the 32 state columns 32 (w & 3) .. of U (w < 4) or S
+// (w >= 4) in accumulators.  Chunk c is computed from one LDS buffer while the
+// loads of chunk c+1 are in flight and then staged into the other one, so each
+// chunk costs one barrier and its memory latency hides behind the products.
+__global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, const ChunkTable cks,
                                                               const unsigned char* ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  f16_t* sK = reinterpret_cast<f16_t*>(smem + StateLds::O_K);
-  f16_t* sKt = reinterpret_cast<f16_t*>(smem + StateLds::O_KT);
-  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + StateLds::O_V);
-  f16_t* sA0 = reinterpret_cast<f16_t*>(smem + StateLds::O_A0);
-  f16_t* sAb = reinterpret_cast<f16_t*>(smem + StateLds::O_AB);
-  float* sEG = reinterpret_cast<float*>(smem + StateLds::O_SM);
-  float* sFac0 = sEG + C;  // -row scale of A0                 (U waves: X' = -X)
-  float* sFacB = sFac0 + C;  // row scale * exp(G_C - G_t)     (S waves)
-  float* sMisc = sFacB + C;  // [0] = exp(G_C)
 
   const int wave = threadIdx.x >> 6;
-  const bool s_wave = wave >= 2;
-  const int col0 = (wave & 1) * 64;
+  const bool s_wave = wave >= 4;
+  const int col0 = (wave & 3) * 32;
   const int n_chain = a.n_chain;
   const int s_local = blockIdx.x / n_chain;
   const int chain = blockIdx.x % n_chain;
   const int t_begin = a.seg.off[s_local], t_end = a.seg.off[s_local + 1];
+  const int n_ck = (t_end - t_begin + C - 1) / C;
   const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + chain;
 
-  f32x16 Z[4][2];
+  f32x16 Z[4];
   {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * rt + acc_row(r, lane);
-          const int col = col0 + 32 * ct + (lane & 31);
-          Z[rt][ct][r] = (!s_wave && row == col) ? 1.f : 0.f;
-        }
+      for (int r = 0; r < 16; ++r)
+        Z[rt][r] = (!s_wave && 32 * rt + acc_row(r, lane) == col0 + (lane & 31)) ? 1.f : 0.f;
   }
-  f32x16 W[2];  // Y = K Z after step 1, X' after step 2
   double g_acc = 0.0;
 
-  for (int c = 0, c0 = t_begin; c0 < t_end; ++c, c0 += C) {
+  // ---- staging of one chunk: loads into registers, then conversion into LDS ---------
+  // threads 0..127: an 8 x 8 block of K; 128..255: of V; 256..511: a quarter
+  // row of A0 with its gate prefixes (and, for the first 64, the row factors)
+  uint4 raw[8];
+  auto load_chunk = [&](int c) {
+    const int tid = opaque(threadIdx.x);
+    const int c0 = t_begin + c * C;
     const int nv = min(C, t_end - c0);
     const unsigned char* rec = ws + ((size_t)(cks.base[s_local] + c) * n_chain + chain) * REC_BYTES;
-    {
-      // ---- stage the chunk ----------------------------------------------------------
-      const int tid = opaque(threadIdx.x);
-      if (tid < 128) {  // keys: fp16 row-major and transposed (8 tokens x 8 channels per thread)
-        const int tb = tid & 7, db = tid >> 3;
-        const bf16_t* src = reinterpret_cast<const bf16_t*>(a.k);
-        uint32_t kd[8][4];
+    if (tid < 256) {
+      const int id = tid & 127, tb = id & 7, db = id >> 3;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(tid < 128 ? a.k : a.v);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int t = tb * 8 + r;
-          uint4 u = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
-          const uint32_t keep = (t < nv) ? 0xffffffffu : 0u;
-          kd[r][0] = pk_f16_from_bf16x2(u.x & keep);
-          kd[r][1] = pk_f16_from_bf16x2(u.y & keep);
-          kd[r][2] = pk_f16_from_bf16x2(u.z & keep);
-          kd[r][3] = pk_f16_from_bf16x2(u.w & keep);
-          *reinterpret_cast<uint2*>(sK + t * KP + db * 8) = make_uint2(kd[r][0], kd[r][1]);
-          *reinterpret_cast<uint2*>(sK + t * KP + db * 8 + 4) = make_uint2(kd[r][2], kd[r][3]);
-        }
-        // 8 x 8 transpose of 16-bit elements: dword j of column cc packs element cc
-        // of rows 2j (low half) and 2j+1 (high half)
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-          uint32_t o[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(kd[2 * j + 1][cc >> 1], kd[2 * j][cc >> 1], sel);
-          *reinterpret_cast<uint2*>(sKt + (db * 8 + cc) * TP + tb * 8) = make_uint2(o[0], o[1]);
-          *reinterpret_cast<uint2*>(sKt + (db * 8 + cc) * TP + tb * 8 + 4) = make_uint2(o[2], o[3]);
-        }
-      } else {  // values: bf16 row-major (rows past the segment end only meet zero weights)
-        const int sid = tid - 128;
-        const int tb = sid & 7, db = sid >> 3;
-        const bf16_t* src = reinterpret_cast<const bf16_t*>(a.v);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int t = tb * 8 + r;
-          const uint4 u = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
-          *reinterpret_cast<uint2*>(sV + t * KP + db * 8) = make_uint2(u.x, u.y);
-          *reinterpret_cast<uint2*>(sV + t * KP + db * 8 + 4) = make_uint2(u.z, u.w);
-        }
+      for (int r = 0; r < 8; ++r) {
+        const int t = tb * 8 + r;
+        raw[r] = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
+        if (t >= nv) raw[r] = make_uint4(0, 0, 0, 0);  // keys past the end must be zero
       }
-      // A0 and Abar = Gamma o A0 (same row scales: Gamma <= 1 and Gamma_tt = 1)
-      {
-        const int t = tid >> 2, cb = (tid & 3) * 16;
-        const float* G = reinterpret_cast<const float*>(rec + REC_G);
-        const f16x8* src = reinterpret_cast<const f16x8*>(rec + REC_A + (t * C + cb) * 2);
-        const f16x8 a0 = src[0], a1 = src[1];
-        const float Gt = G[t];
-        f16x8 b0, b1;
+    } else {
+      const int u = tid - 256, t = u >> 2, cb = (u & 3) * 16;
+      const uint4* ar = reinterpret_cast<const uint4*>(rec + REC_A + (t * C + cb) * 2);
+      raw[0] = ar[0];
+      raw[1] = ar[1];
+      const uint4* gr = reinterpret_cast<const uint4*>(rec + REC_G + cb * 4);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int tp0 = cb + j, tp1 = cb + 8 + j;
-          b0[j] = (f16_t)((float)a0[j] * ((tp0 <= t) ? __expf(Gt - G[tp0]) : 0.f));
-          b1[j] = (f16_t)((float)a1[j] * ((tp1 <= t) ? __expf(Gt - G[tp1]) : 0.f));
-        }
-        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb) = __builtin_shufflevector(a0, a0, 0, 1, 2, 3);
-        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 4) = __builtin_shufflevector(a0, a0, 4, 5, 6, 7);
-        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 8) = __builtin_shufflevector(a1, a1, 0, 1, 2, 3);
-        *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 12) = __builtin_shufflevector(a1, a1, 4, 5, 6, 7);
-        *reinterpret_cast<f16x4*>(sAb + t * TP + cb) = __builtin_shufflevector(b0, b0, 0, 1, 2, 3);
-        *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 4) = __builtin_shufflevector(b0, b0, 4, 5, 6, 7);
-        *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 8) = __builtin_shufflevector(b1, b1, 0, 1, 2, 3);
-        *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 12) = __builtin_shufflevector(b1, b1, 4, 5, 6, 7);
-        if (tid < C) {
-          const float GC = G[C - 1];
-          const float rs = reinterpret_cast<const float*>(rec + REC_RS)[tid];
-          sEG[tid] = __expf(G[tid]);
-          sFac0[tid] = -rs;
-          sFacB[tid] = rs * __expf(GC - G[tid]);
-          if (tid == 0) {
-            sMisc[0] = __expf(GC);
-            g_acc += (double)GC;
-          }
+      for (int j = 0; j < 4; ++j) raw[2 + j] = gr[j];
+      const float* G = reinterpret_cast<const float*>(rec + REC_G);
+      const int uu = u & 63;
+      raw[6] = make_uint4(__float_as_uint(G[t]), __float_as_uint(reinterpret_cast<const float*>(rec + REC_RS)[uu]),
+                          __float_as_uint(G[uu]), __float_as_uint(G[C - 1]));
+    }
+  };
+  auto store_chunk = [&](int buf) {
+    const int tid = opaque(threadIdx.x);
+    unsigned char* base = smem + buf * StateLds::BUF;
+    f16_t* sK = reinterpret_cast<f16_t*>(base + StateLds::O_K);
+    f16_t* sKt = reinterpret_cast<f16_t*>(base + StateLds::O_KT);
+    f16_t* sVt = reinterpret_cast<f16_t*>(base + StateLds::O_V);
+    if (tid < 128) {  // keys: fp16 row-major and transposed
+      const int tb = tid & 7, db = tid >> 3;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        raw[r] = make_uint4(pk_f16_from_bf16x2(raw[r].x), pk_f16_from_bf16x2(raw[r].y),
+                            pk_f16_from_bf16x2(raw[r].z), pk_f16_from_bf16x2(raw[r].w));
+        *reinterpret_cast<uint4*>(sK + (tb * 8 + r) * KP + db * 8) = raw[r];
+      }
+      store_transposed8(raw, sKt + (db * 8) * TP + tb * 8, TP);
+    } else if (tid < 256) {  // values: bf16, transposed
+      const int id = tid - 128, tb = id & 7, db = id >> 3;
+      store_transposed8(raw, sVt + (db * 8) * TP + tb * 8, TP);
+    } else {  // A0 and Abar = Gamma o A0 (same row scales: Gamma <= 1, Gamma_tt = 1)
+      f16_t* sA0 = reinterpret_cast<f16_t*>(base + StateLds::O_A0);
+      f16_t* sAb = reinterpret_cast<f16_t*>(base + StateLds::O_AB);
+      float* sEG = reinterpret_cast<float*>(base + StateLds::O_SM);
+      const int u = tid - 256, t = u >> 2, cb = (u & 3) * 16;
+      const f16x8 a0 = __builtin_bit_cast(f16x8, raw[0]), a1 = __builtin_bit_cast(f16x8, raw[1]);
+      float Gc[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Gc[4 * j] = __uint_as_float(raw[2 + j].x);
+        Gc[4 * j + 1] = __uint_as_float(raw[2 + j].y);
+        Gc[4 * j + 2] = __uint_as_float(raw[2 + j].z);
+        Gc[4 * j + 3] = __uint_as_float(raw[2 + j].w);
+      }
+      const float Gt = __uint_as_float(raw[6].x);
+      f16x8 b0, b1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        b0[j] = (f16_t)((float)a0[j] * ((cb + j <= t) ? __expf(Gt - Gc[j]) : 0.f));
+        b1[j] = (f16_t)((float)a1[j] * ((cb + 8 + j <= t) ? __expf(Gt - Gc[8 + j]) : 0.f));
+      }
+      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb) = __builtin_shufflevector(a0, a0, 0, 1, 2, 3);
+      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 4) = __builtin_shufflevector(a0, a0, 4, 5, 6, 7);
+      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 8) = __builtin_shufflevector(a1, a1, 0, 1, 2, 3);
+      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 12) = __builtin_shufflevector(a1, a1, 4, 5, 6, 7);
+      *reinterpret_cast<f16x4*>(sAb + t * TP + cb) = __builtin_shufflevector(b0, b0, 0, 1, 2, 3);
+      *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 4) = __builtin_shufflevector(b0, b0, 4, 5, 6, 7);
+      *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 8) = __builtin_shufflevector(b1, b1, 0, 1, 2, 3);
+      *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 12) = __builtin_shufflevector(b1, b1, 4, 5, 6, 7);
+      if (u < C) {  // per-row factors of row u
+        const float rs = __uint_as_float(raw[6].y), Gu = __uint_as_float(raw[6].z), GC = __uint_as_float(raw[6].w);
+        sEG[u] = __expf(Gu);
+        sEG[C + u] = -rs;                      // U waves: X' = -A0 R
+        sEG[2 * C + u] = rs * __expf(GC - Gu);  // S waves: X' = diag(exp(G_C - G)) Abar R
+        if (u == 0) {
+          sEG[3 * C] = __expf(GC);
+          g_acc += (double)GC;
         }
       }
     }
-    __syncthreads();
+  };
 
-    const int lane = opaque(threadIdx.x) & 63;
-    const int h = lane >> 5, l32 = lane & 31;
-    const float eGC = sMisc[0];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      // ---- step 1: Y = K Z[:, ct] ------------------------------------------------
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+
+  for (int c = 0; c < n_ck; ++c) {
+    if (c + 1 < n_ck) load_chunk(c + 1);
+    {
+      const unsigned char* base = smem + (c & 1) * StateLds::BUF;
+      const f16_t* sK = reinterpret_cast<const f16_t*>(base + StateLds::O_K);
+      const f16_t* sKt = reinterpret_cast<const f16_t*>(base + StateLds::O_KT);
+      const bf16_t* sVt = reinterpret_cast<const bf16_t*>(base + StateLds::O_V);
+      const f16_t* sA0 = reinterpret_cast<const f16_t*>(base + StateLds::O_A0);
+      const f16_t* sAb = reinterpret_cast<const f16_t*>(base + StateLds::O_AB);
+      const float* sEG = reinterpret_cast<const float*>(base + StateLds::O_SM);
+      const int lane = opaque(threadIdx.x) & 63;
+      const int h = lane >> 5, l32 = lane & 31;
+      const float eGC = sEG[3 * C];
+      f32x16 W[2];
+      // ---- step 1: Y = K Z ----------------------------------------------------------
       {
         float m = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(Z[rt][ct][r]));
-        const int ez = f16_scale_exp(wave_max(m));
-        const float fz = ldexpf(1.f, -ez);
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(Z[rt][r]));
+        const int ez = f16_scale_exp(wave_max_uniform(m));
         const f16_t* pK = sK + l32 * KP + 4 * h;
         W[0] = zero16();
         W[1] = zero16();
@@ -359,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, 
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) {
-            const f16x8 fb = acc_as_b_h(Z[rt][ct], mm, fz);
+            const f16x8 fb = acc_as_b_h(Z[rt], mm, ez);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
           }
@@ -371,16 +409,21 @@ __global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, 
             for (int r = 0; r < 16; ++r) W[tt][r] *= f;
         }
       }
-      // ---- step 2: R = V - exp(G) Y (S) or Y (U);  X' = fac (A R) -----------------------
+      // ---- step 2: R = V - exp(G) Y (S) or Y (U);  X' = fac (A R) ---------------------
       {
         if (s_wave) {
-          const bf16_t* pV = sV + col0 + 32 * ct + l32;
+          // elements 4q .. 4q+3 of tile tt are tokens 32 tt + 8q + 4h + 0..3 of the lane's column
+          const bf16_t* pV = sVt + (col0 + l32) * TP + 4 * h;
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int t = 32 * tt + acc_row(r, lane);
-              W[tt][r] = (float)pV[t * KP] - sEG[t] * W[tt][r];
+            for (int q = 0; q < 4; ++q) {
+              const uint2 vv = *reinterpret_cast<const uint2*>(pV + 32 * tt + 8 * q);
+              const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + 32 * tt + 8 * q + 4 * h);
+              const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                                   __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] = v4[j] - eg[j] * W[tt][4 * q + j];
             }
         }
         float m = 0.f;
@@ -388,14 +431,13 @@ __global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, 
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
-        const int er = f16_scale_exp(wave_max(m));
-        const float fr = ldexpf(1.f, -er);
+        const int er = f16_scale_exp(wave_max_uniform(m));
         const f16_t* pA = (s_wave ? sAb : sA0) + l32 * TP + 4 * h;
         f16x8 fb[2][2];
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) fb[tp][mm] = acc_as_b_h(W[tp], mm, fr);
+          for (int mm = 0; mm < 2; ++mm) fb[tp][mm] = acc_as_b_h(W[tp], mm, er);
         W[0] = zero16();
         W[1] = zero16();
 #pragma unroll
@@ -406,11 +448,16 @@ __global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, 
             for (int tt = tp; tt < 2; ++tt)
               W[tt] = mfma32h(lds_a_perm_h(pA, 32 * tt * TP + 32 * tp + 16 * mm), fb[tp][mm], W[tt]);
         const float f_er = ldexpf(1.f, er);
-        const float* fac = s_wave ? sFacB : sFac0;
+        const float* fac = sEG + (s_wave ? 2 * C : C) + 4 * h;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) W[tt][r] *= fac[32 * tt + acc_row(r, lane)] * f_er;
+          for (int q = 0; q < 4; ++q) {
+            f32x4 f4 = *reinterpret_cast<const f32x4*>(fac + 32 * tt + 8 * q);
+            if (er != 0) f4 = f4 * f_er;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) W[tt][4 * q + j] *= f4[j];
+          }
       }
       // ---- step 3: Z = (exp(G_C) | 1) Z + K^T X' ----------------------------------------
       {
@@ -419,34 +466,34 @@ __global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, 
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
-        const int ex = f16_scale_exp(wave_max(m));
-        const float fx = ldexpf(1.f, -ex);
-        const float pre = (s_wave ? eGC : 1.f) * fx;
+        const int ex = f16_scale_exp(wave_max_uniform(m));
+        const float pre = (s_wave ? eGC : 1.f) * ldexpf(1.f, -ex);
         if (s_wave || ex != 0) {
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Z[rt][ct][r] *= pre;
+            for (int r = 0; r < 16; ++r) Z[rt][r] *= pre;
         }
         const f16_t* pKt = sKt + l32 * TP + 4 * h;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) {
-            const f16x8 fb = acc_as_b_h(W[tt], mm, fx);
+            const f16x8 fb = acc_as_b_h(W[tt], mm, ex);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-              Z[rt][ct] = mfma32h(lds_a_perm_h(pKt, 32 * rt * TP + 32 * tt + 16 * mm), fb, Z[rt][ct]);
+              Z[rt] = mfma32h(lds_a_perm_h(pKt, 32 * rt * TP + 32 * tt + 16 * mm), fb, Z[rt]);
           }
         if (ex != 0) {
           const float f = ldexpf(1.f, ex);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Z[rt][ct][r] *= f;
+            for (int r = 0; r < 16; ++r) Z[rt][r] *= f;
         }
       }
     }
+    if (c + 1 < n_ck) store_chunk((c + 1) & 1);
     __syncthreads();
   }
 
@@ -455,11 +502,8 @@ __global__ __launch_bounds__(256, 2) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        dst[(size_t)(32 * rt + acc_row(r, lane)) * D + col0 + 32 * ct + (lane & 31)] = Z[rt][ct][r];
-  if (threadIdx.x == 0) a.g[unit] = (float)g_acc;
+    for (int r = 0; r < 16; ++r) dst[(size_t)(32 * rt + acc_row(r, lane)) * D + col0 + (lane & 31)] = Z[rt][r];
+  if (threadIdx.x == 256) a.g[unit] = (float)g_acc;
 }
 
 }  // namespace
@@ -490,7 +534,7 @@ hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream)
   hipLaunchKernelGGL(delta_prep_kernel, dim3(n_chunks * a.n_chain), dim3(64), 0, stream, a, ct, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(delta_state_kernel, dim3(a.seg.n_seg * a.n_chain), dim3(256), StateLds::LDS, stream, a, ct,
+  hipLaunchKernelGGL(delta_state_kernel, dim3(a.seg.n_seg * a.n_chain), dim3(512), StateLds::LDS, stream, a, ct,
                      (const unsigned char*)w);
   return hipGetLastError();
 }

@@ -167,6 +167,32 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// The same with DPP moves inside each 16-lane row (swap neighbours, swap
+// pairs, mirror within 8, mirror within 16) and the four row maxima read into
+// scalar registers: no LDS traffic.  The result is wave-uniform.
+__device__ __forceinline__ float dpp_max_step(float x, int ctrl_sel) {
+  int y;
+  const int xi = __builtin_bit_cast(int, x);
+  switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+    case 1: y = __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+    case 2: y = __builtin_amdgcn_mov_dpp(xi, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: y = __builtin_amdgcn_mov_dpp(xi, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return fmaxf(x, __builtin_bit_cast(float, y));
+}
+__device__ __forceinline__ float wave_max_uniform(float x) {
+  x = dpp_max_step(x, 0);
+  x = dpp_max_step(x, 1);
+  x = dpp_max_step(x, 2);
+  x = dpp_max_step(x, 3);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Power-of-two scaling of an fp16 operand block whose largest magnitude is m:
 // returns the exponent e such that the block is converted as x * 2^-e.  Blocks
 // already inside [2^-6, 2^12] are left unscaled (e = 0): there every value that
