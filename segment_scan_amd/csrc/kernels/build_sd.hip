@@ -63,7 +63,7 @@ __device__ __forceinline__ void cvt8(const Raw8<IN_F32>& r, float (&x)[8]) {
 }
 
 template <int FAM, int D, bool IN_F32>
-__global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
+__global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
   constexpr int NTK = IN_F32 ? 3 : 2;  // bf16 terms of decay-weighted keys
   constexpr int NTV = IN_F32 ? 3 : 1;  // bf16 terms of values (bf16 inputs are exact)
   constexpr int NRT = D / 32;          // 32-row tiles along d
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void build_sd_kernel(const BuildArgs a) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
               run[c] += lgr[c];
-              x[r][c] *= expf(tot[c] - (pre[c] + run[c]));
+              x[r][c] *= __expf(tot[c] - (pre[c] + run[c]));
             }
           } else {
 #pragma unroll
