@@ -318,13 +318,15 @@ class WarmRequest(Workload):
         self.g = torch.zeros((n_seg, n), device="cuda")
         self.S_run = torch.zeros((n, d, d), device="cuda")
         self.o = torch.empty((nt, n, d), device="cuda")
+        self.ws = torch.empty(api.seam_step_workspace_size(synth.DELTA, n_seg, w, n, d), device="cuda",
+                              dtype=torch.uint8)
 
     def step(self, ev0, ev1):
         from segment_scan_amd.synth import DELTA
         self.S_run.zero_()
         ev0.record()
         self.api.seam_step(DELTA, self.w, self.q, self.k, self.v, self.beta, self.lg, body=(self.g, self.U, self.S),
-                           S_run=self.S_run, o_out=self.o)
+                           S_run=self.S_run, o_out=self.o, workspace=self.ws)
         ev1.record()
 
     def cpu_sample(self):

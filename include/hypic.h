@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 3
+#define HYPIC_ABI_VERSION 4
 
 typedef enum {
   HYPIC_OK = 0,
@@ -222,11 +222,29 @@ hypic_status hypic_compose_workspace_size(hypic_family fam, int n_seg, int n_cha
  *                  n_chain] (DIAG: [.., d_k]) and S [n_seg, n_chain, d_k, d_v]
  *                  required, U [n_seg, n_chain, d_k, d_k] for DELTA only.  It
  *                  satisfies S_after = T_W S_before + S(W|0) for each window.
+ *   workspace      device scratch of at least workspace_bytes bytes, as returned
+ *                  by hypic_seam_step_workspace_size for the same fam, n_seg, w
+ *                  and n_chain; may be NULL when that size is 0.  Contents
+ *                  ignored on entry and undefined on exit; in use until the
+ *                  stream passes the call.
  * Errors as for hypic_seg_build.
  */
 hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, int d_k, int d_v,
                              const hypic_tokens* seam, const hypic_cpairs* body, float* S_run,
-                             float* o_out, const hypic_pairs* window_out, void* stream);
+                             float* o_out, const hypic_pairs* window_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * hypic_seam_step_workspace_size -- bytes of workspace hypic_seam_step needs.
+ *
+ * Only the DELTA family uses one: the part of each window's update that does
+ * not depend on the running state (the window's inverse factor and gate
+ * weights, 576 bytes per 8-token sub-window and chain) is formed for all
+ * windows at once before the ordered pass.  Other families return 0.
+ * *bytes receives the size; enqueues nothing.
+ */
+hypic_status hypic_seam_step_workspace_size(hypic_family fam, int n_seg, int w, int n_chain, int d_k,
+                                            int d_v, size_t* bytes);
 
 /* Message of the last failed call on this thread ("" if none).  The string is
  * owned by the library and valid until the next call on this thread. */

@@ -61,9 +61,10 @@ def load_library(path: str = LIB_PATH):
         lib.hypic_compose.argtypes = [I, I, I, I, I, ctypes.POINTER(Pairs), P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.hypic_compose_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.hypic_seam_step.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P, P,
-                                        ctypes.POINTER(Pairs), P]
+                                        ctypes.POINTER(Pairs), P, ctypes.c_size_t, P]
+        lib.hypic_seam_step_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
         for f in (lib.hypic_seg_build, lib.hypic_seg_build_workspace_size, lib.hypic_compose,
-                  lib.hypic_compose_workspace_size, lib.hypic_seam_step):
+                  lib.hypic_compose_workspace_size, lib.hypic_seam_step, lib.hypic_seam_step_workspace_size):
             f.restype = I
         lib.hypic_last_error.restype = ctypes.c_char_p
         lib.hypic_last_error.argtypes = []
@@ -200,11 +201,20 @@ def compose(fam: int, g, U, S, S_init=None, S_out=None, prefix_states=None, g_to
     return {"S_out": S_out, "prefix": prefix_states, "g_tot": g_total, "U_tot": U_total}
 
 
+def seam_step_workspace_size(fam: int, n_seg: int, w: int, n_chain: int, d: int) -> int:
+    """Bytes of device workspace seam_step needs (0: none)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().hypic_seam_step_workspace_size(fam, n_seg, w, n_chain, d, d, ctypes.byref(out)))
+    return out.value
+
+
 def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chain=False, body=None,
-              S_run=None, o_out=None, window_out=None, want_window_pairs=False, stream=None):
+              S_run=None, o_out=None, window_out=None, want_window_pairs=False, workspace=None, stream=None):
     """Seam-window step over [n_seg * w, n_chain, d] window tokens; S_run is updated in place.
 
-    body: None or (g, U, S) cached body pairs.  Returns dict with S_run, o and window pairs."""
+    body: None or (g, U, S) cached body pairs.  workspace: a uint8 device buffer
+    of at least seam_step_workspace_size() bytes, or None to take one from
+    torch's allocator for the call.  Returns dict with S_run, o and window pairs."""
     n_tok, n_chain, d = k.shape
     if n_tok % w:
         raise ValueError("window tokens must be n_seg * w")
@@ -218,11 +228,17 @@ def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chai
         window_out = (torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32),
                       torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam == DELTA else None,
                       torch.empty((n_seg, n_chain, d, v.shape[2]), device=dev, dtype=torch.float32))
+    if workspace is None:
+        need = seam_step_workspace_size(fam, n_seg, w, n_chain, d)
+        if need:
+            workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     tk = _tokens(k, v, q, beta, log_gate, gate_per_chain)
     bp = ctypes.byref(Pairs(_ptr(body[0]), _ptr(body[1]), _ptr(body[2]))) if body is not None else None
     wp = ctypes.byref(Pairs(*[_ptr(x) for x in window_out])) if window_out is not None else None
     _check(load_library().hypic_seam_step(fam, n_seg, w, n_chain, d, v.shape[2], ctypes.byref(tk), bp,
-                                          _ptr(S_run), _ptr(o_out), wp, _stream(stream)))
+                                          _ptr(S_run), _ptr(o_out), wp, _ptr(workspace), ws_bytes,
+                                          _stream(stream)))
     res = {"S_run": S_run, "o": o_out}
     if window_out is not None:
         res.update(wg=window_out[0], wU=window_out[1], wS=window_out[2])

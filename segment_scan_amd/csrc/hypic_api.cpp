@@ -303,9 +303,19 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   return ok();
 }
 
+hypic_status hypic_seam_step_workspace_size(hypic_family fam, int n_seg, int w, int n_chain, int d_k, int d_v,
+                                            size_t* bytes) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  if (w < 1) return fail(HYPIC_E_INVALID, "w must be >= 1 (got %d)", w);
+  if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
+  *bytes = fam == HYPIC_DELTA ? hypic::seam_workspace_bytes(n_seg, w, n_chain) : 0;
+  return ok();
+}
+
 hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, int d_k, int d_v,
                              const hypic_tokens* seam, const hypic_cpairs* body, float* S_run, float* o_out,
-                             const hypic_pairs* window_out, void* stream) {
+                             const hypic_pairs* window_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   const int d = d_k;
   if (w < 1) return fail(HYPIC_E_INVALID, "w must be >= 1 (got %d)", w);
@@ -331,6 +341,14 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
     if (window_out->g) outs.push_back({window_out->g, units * gate_len(fam, d) * 4, "window_out.g"});
     if (window_out->U) outs.push_back({window_out->U, units * d * d * 4, "window_out.U"});
   }
+  const size_t ws_need = fam == HYPIC_DELTA ? hypic::seam_workspace_bytes(n_seg, w, n_chain) : 0;
+  if (ws_need > 0) {
+    if (!workspace) return fail(HYPIC_E_INVALID, "workspace is NULL (%zu bytes required)", ws_need);
+    if (workspace_bytes < ws_need)
+      return fail(HYPIC_E_INVALID, "workspace too small: %zu bytes given, %zu required", workspace_bytes, ws_need);
+    TRY(check_aligned(workspace, "workspace"));
+    outs.push_back({workspace, ws_need, "workspace"});
+  }
   TRY(check_overlaps(ins, outs));
   const bool f32 = seam->dtype == HYPIC_F32;
 
@@ -352,8 +370,17 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   a.n_seg = n_seg;
   a.w = w;
   a.n_chain = n_chain;
-  hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_seam_chain(d, f32, a, (hipStream_t)stream)
-                                      : hypic::launch_seam_elem(fam, d, f32, a, (hipStream_t)stream);
+  a.wrec = nullptr;
+  hipError_t e;
+  if (fam == HYPIC_DELTA) {
+    float* rec = reinterpret_cast<float*>(workspace);
+    e = hypic::launch_seam_prep(d, f32, a, rec, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seam_step window factor launch");
+    a.wrec = rec;
+    e = hypic::launch_seam_chain(d, f32, a, (hipStream_t)stream);
+  } else {
+    e = hypic::launch_seam_elem(fam, d, f32, a, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "hypic_seam_step launch");
   if (window_out) {
     // each window's own pair depends only on its tokens: the segment build of

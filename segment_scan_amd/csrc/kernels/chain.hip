@@ -70,7 +70,7 @@ struct ChainCfg {
   static constexpr int OFF_WV = OFF_WKZ + SUB * D * 4;
   static constexpr int OFF_WR = OFF_WV + SUB * COLS * 4;
   static constexpr int OFF_WSM = OFF_WR + SUB * COLS * 4;
-  static constexpr int WSM_FLOATS = 5 * SUB + 4 * SUB * SUB;
+  static constexpr int WSM_FLOATS = SEAM_REC_FLOATS;
   static constexpr int LDS = SEAM ? OFF_WSM + WSM_FLOATS * 4 : OFF_W;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(D * D / 4 % NTH == 0, "U staging");
@@ -90,6 +90,7 @@ struct ChainArgs {
   const void* v;
   const void* beta;
   const void* lg;     // nullptr: no gate
+  const float* wrec;  // per-window records of seam_prep
   float* o;
   int n_seg;
   int n_chain;
@@ -272,20 +273,16 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
       float* sKz = reinterpret_cast<float*>(smem + Cfg::OFF_WKZ);
       float* sV = reinterpret_cast<float*>(smem + Cfg::OFF_WV);
       float* sR = reinterpret_cast<float*>(smem + Cfg::OFF_WR);
-      float* sB = reinterpret_cast<float*>(smem + Cfg::OFF_WSM);
-      float* sLg = sB + SUB;
-      float* sG = sLg + SUB;
-      float* sEG = sG + SUB;
-      float* sEW = sEG + SUB;
-      float* sKK = sEW + SUB;      // [t][s]: k_t . k_s
-      float* sQK = sKK + SUB * SUB;  // [t][s]: q_t . k_s
-      float* sW2 = sQK + SUB * SUB;  // (Omega Abar)[t][s]
-      float* sC = sW2 + SUB * SUB;   // [s][t]: Abar[t][s] exp(G_n - G_t)
-      for (int t0 = 0; t0 < a.w; t0 += SUB) {
+      float* sRec = reinterpret_cast<float*>(smem + Cfg::OFF_WSM);
+      const float* sC = sRec;                  // [s][t]: Abar[t][s] exp(G_n - G_t)
+      const float* sW2 = sRec + SUB * SUB;     // ((tril(Q K^T) o Gamma) Abar)[t][s]
+      const float* sEG = sRec + 2 * SUB * SUB;  // exp(G_t); [SUB] = exp(G_n)
+      const int n_sub = (a.w + SUB - 1) / SUB;
+      for (int t0 = 0, sub = 0; t0 < a.w; t0 += SUB, ++sub) {
         refresh();
         const int n = min(SUB, a.w - t0);
         const size_t tok0 = (size_t)seg * a.w + t0;
-        // W1: window tokens -> LDS (fp32), zero past n
+        // W1: window tokens -> LDS (fp32), zero past n; the window's record
         for (int i = tid; i < 2 * SUB * (D / 8) + SUB * (COLS / 8); i += NTH) {
           float x[8];
           float* dst;
@@ -313,72 +310,8 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
           *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
           *reinterpret_cast<f32x4*>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
         }
-        if (tid < SUB) {
-          const size_t idx = (tok0 + tid) * n_chain + chain;
-          sB[tid] = tid < n ? load1<IN_F32>(a.beta, idx) : 0.f;
-          sLg[tid] = (tid < n && a.lg) ? load1<IN_F32>(a.lg, idx) : 0.f;
-        }
-        __syncthreads();
-        // W2: gate prefix; dot products k_t.k_s (s < t) and q_t.k_s (s <= t)
-        {
-          constexpr int TPP = NTH / 64;  // threads per dot product
-          const int p = tid / TPP, part = tid % TPP;
-          int t, s;
-          const float* x;
-          if (p < SUB * (SUB - 1) / 2) {  // 28 (t, s) with s < t
-            t = 1;
-            int r = p;
-            while (r >= t) { r -= t; ++t; }
-            s = r;
-            x = sK;
-          } else {  // 36 (t, s) with s <= t
-            t = 0;
-            int r = p - SUB * (SUB - 1) / 2;
-            while (r > t) { r -= t + 1; ++t; }
-            s = r;
-            x = sQ;
-          }
-          float acc = 0.f;
-#pragma unroll 4
-          for (int d = part; d < D; d += TPP) acc = fmaf(x[t * D + d], sK[s * D + d], acc);
-#pragma unroll
-          for (int o = 1; o < TPP; o <<= 1) acc += __shfl_xor(acc, o, 64);
-          if (part == 0) (x == sK ? sKK : sQK)[t * SUB + s] = acc;
-          if (tid < SUB) {
-            float G = 0.f, Gn = 0.f;
-            for (int u = 0; u < SUB; ++u) {
-              Gn += sLg[u];
-              if (u == tid) G = Gn;
-            }
-            sG[tid] = G;
-            sEG[tid] = __expf(G);
-            sEW[tid] = __expf(Gn - G);
-          }
-        }
-        __syncthreads();
-        // W3: lane s of wave 0 solves column s of (I + M)^-1, M_ts = b_t Gamma_ts k_t.k_s
-        if (tid < SUB) {
-          const int s = tid;
-          float x[SUB];
-#pragma unroll
-          for (int t = 0; t < SUB; ++t) {
-            float acc = 0.f;
-#pragma unroll
-            for (int u = 0; u < t; ++u) acc = fmaf(sB[t] * __expf(sG[t] - sG[u]) * sKK[t * SUB + u], x[u], acc);
-            x[t] = (t < s) ? 0.f : ((t == s) ? 1.f : -acc);
-          }
-          const float bs = sB[s];
-#pragma unroll
-          for (int t = 0; t < SUB; ++t) {
-            const float ab = x[t] * bs;  // Abar[t][s]
-            sC[s * SUB + t] = ab * sEW[t];
-            // (Omega Abar)[t][s] = sum_{s <= u <= t} Gamma_tu (q_t . k_u) Abar[u][s]
-            float w2 = 0.f;
-#pragma unroll
-            for (int u = 0; u <= t; ++u) w2 = fmaf(__expf(sG[t] - sG[u]) * sQK[t * SUB + u], x[u] * bs, w2);
-            sW2[t * SUB + s] = w2;
-          }
-        }
+        for (int i = tid; i < SEAM_REC_FLOATS; i += NTH)
+          sRec[i] = a.wrec[((size_t)(seg * n_sub + sub) * n_chain + chain) * SEAM_REC_FLOATS + i];
         __syncthreads();
         // W4: Kz = Abar^T diag(exp(G_n - G)) K;  X = K S, P = Q S;  R = V - exp(G) X
         for (int i = tid; i < SUB * D; i += NTH) {
@@ -430,7 +363,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
           }
         }
         {
-          const float eGn = sEG[SUB - 1];
+          const float eGn = sEG[SUB];
           for (int i = tid; i < COLS * (D / 16); i += NTH) {
             const int c = i / (D / 16), dq = i % (D / 16);
             float rr[SUB];
@@ -645,6 +578,7 @@ hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& s, hipStream_t 
   a.beta = s.beta;
   a.lg = s.lg;
   a.o = s.o;
+  a.wrec = s.wrec;
   a.n_seg = s.n_seg;
   a.n_chain = s.n_chain;
   a.w = s.w;

@@ -60,6 +60,7 @@ struct SeamArgs {
   int n_seg;
   int w;
   int n_chain;
+  const float* wrec;  // delta family: per-window records of seam_prep (see below)
 };
 
 // fam: 0 naive, 1 scalar, 2 diag, 3 delta.  d in {64, 128}.
@@ -85,6 +86,13 @@ hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t
 size_t compose_workspace_bytes(int d, int n_seg, int n_chain, bool prefix);
 hipError_t launch_compose_chain(int d, const ComposeArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
+// Delta seam step: the state-independent part of every window (8-token
+// sub-chunks) is formed first into a workspace of seam_workspace_bytes(), one
+// record of SEAM_REC_FLOATS floats per (segment, sub-chunk, chain):
+// C[8][8], W2[8][8], exp(G)[8], exp(G_n) (seam_prep.hip).
+constexpr int SEAM_REC_FLOATS = 144;
+size_t seam_workspace_bytes(int n_seg, int w, int n_chain);
+hipError_t launch_seam_prep(int d, bool in_f32, const SeamArgs& a, float* ws, hipStream_t stream);
 // seam step of the naive, scalar and diagonal families (seam_elem.hip)
 hipError_t launch_seam_elem(int fam, int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 

@@ -43,14 +43,14 @@ def test_library_exports_every_declared_symbol(lib):
         text = f.read()
     declared = set(re.findall(r"\b(hypic_[a-z_]+)\s*\(", text))
     assert {"hypic_seg_build", "hypic_seg_build_workspace_size", "hypic_compose", "hypic_compose_workspace_size",
-            "hypic_seam_step", "hypic_last_error", "hypic_abi_version"} <= declared
+            "hypic_seam_step", "hypic_seam_step_workspace_size", "hypic_last_error", "hypic_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\b(hypic_[a-z_]+)\b", out))
     assert declared <= exported, declared - exported
     for name in declared:
         getattr(lib, name)
-    assert lib.hypic_abi_version() == 3
+    assert lib.hypic_abi_version() == 4
 
 
 def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
@@ -98,6 +98,21 @@ def test_compose_workspace_size(lib):
     assert cws(n_seg=4) == (0, 0)
     assert cws(fam=SCALAR) == (0, 0)
     assert cws(d=96)[0] == UNSUPPORTED
+
+
+def test_seam_workspace_size(lib):
+    """The delta seam step takes one 576-byte record (inverse factor, gate weights)
+    per 8-token sub-window and chain; the other families none."""
+    def sws(fam=DELTA, n_seg=196, w=8, n_chain=480, d=128):
+        out = ctypes.c_size_t(7)
+        st = lib.hypic_seam_step_workspace_size(fam, n_seg, w, n_chain, d, d, ctypes.byref(out))
+        return st, out.value
+    assert sws() == (0, 196 * 480 * 576)
+    assert sws(w=9, n_seg=3, n_chain=2) == (0, 3 * 2 * 2 * 576)
+    assert sws(w=1, n_seg=1, n_chain=1, d=64) == (0, 576)
+    assert sws(fam=DIAG) == (0, 0)
+    assert sws(w=0)[0] == INVALID
+    assert sws(d=96)[0] == UNSUPPORTED
 
 
 def test_workspace_size(lib):
@@ -189,12 +204,12 @@ def test_compose_rejects(lib, kwargs, status, msg):
 
 
 def seam_call(lib, fam=DELTA, n_seg=4, w=8, n_chain=2, d=128, t=None, body="default", S_run=A["Sinit"], o=A["o"],
-              win=None):
+              win=None, ws=A["ws"], ws_bytes=WS_BYTES):
     t = toks(fam, q=True) if t is None else t
     b = pairs(fam) if body == "default" else body
     return lib.hypic_seam_step(fam, n_seg, w, n_chain, d, d, ctypes.byref(t),
                                ctypes.byref(b) if b is not None else None, S_run, o,
-                               ctypes.byref(win) if win is not None else None, None)
+                               ctypes.byref(win) if win is not None else None, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kwargs,status,msg", [
@@ -211,6 +226,10 @@ def seam_call(lib, fam=DELTA, n_seg=4, w=8, n_chain=2, d=128, t=None, body="defa
     (dict(fam=SCALAR, t=toks(SCALAR, q=True), body=pairs(SCALAR), win=Pairs(A["wg"], A["wU"], A["wS"])), INVALID,
      "only defined for delta"),
     (dict(d=256), UNSUPPORTED, "64, 128"),
+    (dict(ws=None), INVALID, "workspace is NULL"),
+    (dict(ws_bytes=1024), INVALID, "workspace too small"),
+    (dict(ws=A["ws"] + 8), INVALID, "workspace is not 16-byte aligned"),
+    (dict(ws=A["o"] + 64), INVALID, "overlap"),
 ])
 def test_seam_rejects(lib, kwargs, status, msg):
     assert seam_call(lib, **kwargs) == status
