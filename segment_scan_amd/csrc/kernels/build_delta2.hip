@@ -149,41 +149,90 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
   }
   __syncthreads();
 
-  // ---- N = (I + M)^-1 by forward substitution: lane c owns column c -----------------
-  // N[r][c] = delta_rc - sum_{k<r} M[r][k] N[k][c]; rows of M are read as LDS
-  // broadcasts.  Entries above the diagonal are zero, so the sums need no mask.
-  const int c = lane;
-  float x[C];
+  // ---- N = (I + M)^-1 in 32 x 32 blocks ---------------------------------------------
+  // Diagonal blocks by forward substitution, lane 32 b + c owning column c of
+  // block b: N_bb[r][c] = delta_rc - sum_{k<r} M_bb[r][k] N_bb[k][c], rows of
+  // M read as LDS broadcasts (entries on and above the diagonal are zero).
+  {
+    const int b = lane >> 5, c = l32;
+    const float* Mb = sM + 32 * b * MP + 32 * b;
+    float x[32];
 #pragma unroll
-  for (int r = 0; r < C; ++r) {
-    float acc0 = 0.f, acc1 = 0.f;
-    const float* Mr = sM + r * MP;
+    for (int r = 0; r < 32; ++r) {
+      float acc0 = 0.f, acc1 = 0.f;
+      const float* Mr = Mb + r * MP;
 #pragma unroll
-    for (int k4 = 0; k4 < r / 4; ++k4) {
-      const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
-      acc0 = fmaf(m4[0], x[4 * k4], acc0);
-      acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
-      acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
-      acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
+      for (int k4 = 0; k4 < r / 4; ++k4) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
+        acc0 = fmaf(m4[0], x[4 * k4], acc0);
+        acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
+        acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
+        acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
+      }
+#pragma unroll
+      for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
+      x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
     }
+    __syncthreads();  // every lane is done reading M_bb
+    float* Nb = sM + 32 * b * MP + 32 * b;
 #pragma unroll
-    for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
-    x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
+    for (int r = 0; r < 32; ++r) Nb[r * MP + c] = x[r];
+    // the upper-right block of N is zero
+    if (b == 0) {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) sM[r * MP + 32 + c] = 0.f;
+    }
   }
-  __syncthreads();  // every lane is done reading M
-
-  // ---- A0 = N diag(beta): column c scaled by beta_c; rows to fp16 with row scales --
-#pragma unroll
-  for (int r = 0; r < C; ++r) sM[r * MP + c] = x[r] * beta;
   __syncthreads();
+  // Off-diagonal block N_10 = -N_11 (M_10 N_00): two 32 x 32 x 32 products on
+  // bf16 MFMA with both operands split into two terms (about 2^-16 relative).
+  auto prod = [&](const float* Ab, const float* Bb) {
+    // Ab, Bb: 32 x 32 blocks of sM (pitch MP); returns Ab Bb in accumulator layout
+    f32x16 P = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float xa[8], xb[8];
+      const float* ar = Ab + l32 * MP + 16 * ks + 8 * h;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(ar);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(ar + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xa[j] = a0[j];
+        xa[4 + j] = a1[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xb[j] = Bb[(16 * ks + 8 * h + j) * MP + l32];
+      mma<2, 2>(P, split8<2>(xa), split8<2>(xb));
+    }
+    return P;
+  };
+  {
+    const f32x16 P = prod(sM + 32 * MP, sM);  // M_10 N_00
+    __syncthreads();                          // M_10 is read; its block now holds P
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sM[(32 + acc_row(r, lane)) * MP + l32] = P[r];
+  }
+  __syncthreads();
+  {
+    const f32x16 Q = prod(sM + 32 * MP + 32, sM + 32 * MP);  // N_11 P
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sM[(32 + acc_row(r, lane)) * MP + l32] = -Q[r];
+  }
+  __syncthreads();
+
+  // ---- A0 = N diag(beta) (column j scaled by beta_j); rows to fp16 with row scales --
   unsigned char* rec = ws + (size_t)blockIdx.x * REC_BYTES;
   {
     const int t = lane;  // row of A0
-    const float* Ar = sM + t * MP;
+    float* Ar = sM + t * MP;
     float m = 0.f;
 #pragma unroll
     for (int j4 = 0; j4 < C / 4; ++j4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(Ar + 4 * j4);
+      f32x4 v = *reinterpret_cast<const f32x4*>(Ar + 4 * j4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] *= sBeta[4 * j4 + j];
+      *reinterpret_cast<f32x4*>(Ar + 4 * j4) = v;
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
     int e = 0;
