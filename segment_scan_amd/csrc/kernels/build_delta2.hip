@@ -6,21 +6,24 @@
 // and S(C|0) is its final state from a zero start.  The segment is processed in
 // 64-token chunks joined by the composition law of the same paragraph; a
 // chunk's 64 rank-1 factors are applied in the compact WY/UT form
-//   N    = (I + strict_lower(diag(b) K K^T))^-1,  A0 = N diag(b)
-//   Abar = Gamma o A0,  Gamma_ts = exp(G_t - G_s)   (G: within-chunk gate prefix)
-//   U   <- U - K^T (A0 (K U))
-//   S   <- exp(G_C) S + K^T diag(exp(G_C - G)) (Abar (V - diag(exp(G)) K S))
+//   A0 = (I + strict_lower(diag(b) K K^T))^-1 diag(b)
+//   U <- U - K^T (A0 (K U))
+//   S <- exp(G_C) S + K^T (A0 (diag(exp(G_C - G)) V - exp(G_C) K S))
+// (G: inclusive gate prefix within the chunk, G_C its total).  The S update is
+// the ungated rule on values exp(-G_t) v_t in the frame scaled by exp(-G),
+// moved back by exp(G_C): both halves share A0, and every factor is <= 1.
 //
 // Nothing in A0 depends on the running state, so the per-chunk factors are a
 // separate, fully parallel job:
-//  - delta_prep: one workgroup per (segment, chunk, chain) -- thousands of
-//    independent tasks, several workgroups per CU -- builds the Gram matrix on
-//    MFMA, inverts (I + M0) in 16 x 16 blocks in fp32, and writes A0 (fp16,
-//    each row scaled by a power of two) with the gate prefix G to a workspace;
+//  - delta_prep: one wave per (segment, chunk, chain) builds the Gram matrix on
+//    MFMA, inverts (I + M) in 32 x 32 blocks (diagonal blocks by forward
+//    substitution in fp32, the off-diagonal block by two MFMA products), and
+//    writes A0 (fp16, each row scaled by a power of two) with the gate prefix G
+//    to a workspace;
 //  - delta_state: one workgroup per (segment, chain) keeps [U | S] in MFMA
-//    accumulators (4 waves x 64 columns) and, per chunk, stages K (row-major
-//    and transposed), V and A0 / Abar in LDS and runs the three products.
-// The workspace makes the state pass a plain stream with two barriers per
+//    accumulators (8 waves x 32 columns) and, per chunk, stages K (row-major
+//    and transposed), V and A0 in LDS and runs the three products.
+// The workspace makes the state pass a plain stream with one barrier per
 // chunk and lets the latency-bound inverse hide behind other workgroups.
 //
 // Operands enter the matrix cores as fp16 (fp32 accumulate).  bf16 keys are
@@ -268,9 +271,8 @@ struct StateLds {  // one staging buffer; the kernel keeps two
   static constexpr int O_KT = O_K + C * KP * 2;
   static constexpr int O_V = O_KT + D * TP * 2;
   static constexpr int O_A0 = O_V + D * TP * 2;
-  static constexpr int O_AB = O_A0 + C * TP * 2;
-  static constexpr int O_SM = O_AB + C * TP * 2;   // eG[64], fac0[64], facb[64], misc[64]
-  static constexpr int BUF = O_SM + 4 * C * 4;
+  static constexpr int O_SM = O_A0 + C * TP * 2;  // eW[64] = exp(G_C - G_t), rs[64], exp(G_C)
+  static constexpr int BUF = O_SM + (2 * C + 4) * 4;
   static constexpr int LDS = 2 * BUF;
 };
 
@@ -292,6 +294,11 @@ __device__ __forceinline__ void store_transposed8(const uint4 (&rows)[8], f16_t*
   }
 }
 
+// Per chunk, in the frame scaled by the chunk's gate (the gated delta rule is
+// the ungated one on values v_t exp(-G_t), then scaled by exp(G_C)):
+//   U <- U + K^T (-A0 (K U))
+//   S <- exp(G_C) S + K^T (A0 (diag(exp(G_C - G)) V - exp(G_C) K S))
+// so both halves share A0 and every gate factor is at most 1.
 // 8 waves: wave w keeps the 32 state columns 32 (w & 3) .. of U (w < 4) or S
 // (w >= 4) in accumulators.  Chunk c is computed from one LDS buffer while the
 // loads of chunk c+1 are in flight and then staged into the other one, so each
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
 
   // ---- staging of one chunk: loads into registers, then conversion into LDS ---------
   // threads 0..127: an 8 x 8 block of K; 128..255: of V; 256..511: a quarter
-  // row of A0 with its gate prefixes (and, for the first 64, the row factors)
+  // row of A0 (and, for the first 64, the token's factors)
   uint4 raw[8];
   auto load_chunk = [&](int c) {
     const int tid = opaque(threadIdx.x);
@@ -344,13 +351,11 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
       const uint4* ar = reinterpret_cast<const uint4*>(rec + REC_A + (t * C + cb) * 2);
       raw[0] = ar[0];
       raw[1] = ar[1];
-      const uint4* gr = reinterpret_cast<const uint4*>(rec + REC_G + cb * 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) raw[2 + j] = gr[j];
-      const float* G = reinterpret_cast<const float*>(rec + REC_G);
-      const int uu = u & 63;
-      raw[6] = make_uint4(__float_as_uint(G[t]), __float_as_uint(reinterpret_cast<const float*>(rec + REC_RS)[uu]),
-                          __float_as_uint(G[uu]), __float_as_uint(G[C - 1]));
+      if (u < C) {
+        const float* G = reinterpret_cast<const float*>(rec + REC_G);
+        raw[2] = make_uint4(__float_as_uint(G[u]), __float_as_uint(G[C - 1]),
+                            __float_as_uint(reinterpret_cast<const float*>(rec + REC_RS)[u]), 0u);
+      }
     }
   };
   auto store_chunk = [&](int buf) {
@@ -371,42 +376,18 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
     } else if (tid < 256) {  // values: bf16, transposed
       const int id = tid - 128, tb = id & 7, db = id >> 3;
       store_transposed8(raw, sVt + (db * 8) * TP + tb * 8, TP);
-    } else {  // A0 and Abar = Gamma o A0 (same row scales: Gamma <= 1, Gamma_tt = 1)
+    } else {  // A0 rows and the token factors
       f16_t* sA0 = reinterpret_cast<f16_t*>(base + StateLds::O_A0);
-      f16_t* sAb = reinterpret_cast<f16_t*>(base + StateLds::O_AB);
-      float* sEG = reinterpret_cast<float*>(base + StateLds::O_SM);
       const int u = tid - 256, t = u >> 2, cb = (u & 3) * 16;
-      const f16x8 a0 = __builtin_bit_cast(f16x8, raw[0]), a1 = __builtin_bit_cast(f16x8, raw[1]);
-      float Gc[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Gc[4 * j] = __uint_as_float(raw[2 + j].x);
-        Gc[4 * j + 1] = __uint_as_float(raw[2 + j].y);
-        Gc[4 * j + 2] = __uint_as_float(raw[2 + j].z);
-        Gc[4 * j + 3] = __uint_as_float(raw[2 + j].w);
-      }
-      const float Gt = __uint_as_float(raw[6].x);
-      f16x8 b0, b1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        b0[j] = (f16_t)((float)a0[j] * ((cb + j <= t) ? __expf(Gt - Gc[j]) : 0.f));
-        b1[j] = (f16_t)((float)a1[j] * ((cb + 8 + j <= t) ? __expf(Gt - Gc[8 + j]) : 0.f));
-      }
-      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb) = __builtin_shufflevector(a0, a0, 0, 1, 2, 3);
-      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 4) = __builtin_shufflevector(a0, a0, 4, 5, 6, 7);
-      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 8) = __builtin_shufflevector(a1, a1, 0, 1, 2, 3);
-      *reinterpret_cast<f16x4*>(sA0 + t * TP + cb + 12) = __builtin_shufflevector(a1, a1, 4, 5, 6, 7);
-      *reinterpret_cast<f16x4*>(sAb + t * TP + cb) = __builtin_shufflevector(b0, b0, 0, 1, 2, 3);
-      *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 4) = __builtin_shufflevector(b0, b0, 4, 5, 6, 7);
-      *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 8) = __builtin_shufflevector(b1, b1, 0, 1, 2, 3);
-      *reinterpret_cast<f16x4*>(sAb + t * TP + cb + 12) = __builtin_shufflevector(b1, b1, 4, 5, 6, 7);
-      if (u < C) {  // per-row factors of row u
-        const float rs = __uint_as_float(raw[6].y), Gu = __uint_as_float(raw[6].z), GC = __uint_as_float(raw[6].w);
-        sEG[u] = __expf(Gu);
-        sEG[C + u] = -rs;                      // U waves: X' = -A0 R
-        sEG[2 * C + u] = rs * __expf(GC - Gu);  // S waves: X' = diag(exp(G_C - G)) Abar R
+      *reinterpret_cast<uint4*>(sA0 + t * TP + cb) = raw[0];
+      *reinterpret_cast<uint4*>(sA0 + t * TP + cb + 8) = raw[1];
+      if (u < C) {
+        float* sF = reinterpret_cast<float*>(base + StateLds::O_SM);
+        const float Gt = __uint_as_float(raw[2].x), GC = __uint_as_float(raw[2].y);
+        sF[u] = __expf(GC - Gt);                // value weight to the chunk end
+        sF[C + u] = __uint_as_float(raw[2].z);  // row scale of A0
         if (u == 0) {
-          sEG[3 * C] = __expf(GC);
+          sF[2 * C] = __expf(GC);
           g_acc += (double)GC;
         }
       }
@@ -425,11 +406,10 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
       const f16_t* sKt = reinterpret_cast<const f16_t*>(base + StateLds::O_KT);
       const bf16_t* sVt = reinterpret_cast<const bf16_t*>(base + StateLds::O_V);
       const f16_t* sA0 = reinterpret_cast<const f16_t*>(base + StateLds::O_A0);
-      const f16_t* sAb = reinterpret_cast<const f16_t*>(base + StateLds::O_AB);
-      const float* sEG = reinterpret_cast<const float*>(base + StateLds::O_SM);
+      const float* sF = reinterpret_cast<const float*>(base + StateLds::O_SM);
       const int lane = opaque(threadIdx.x) & 63;
       const int h = lane >> 5, l32 = lane & 31;
-      const float eGC = sEG[3 * C];
+      const float eGC = sF[2 * C];
       f32x16 W[2];
       // ---- step 1: Y = K Z ----------------------------------------------------------
       {
@@ -458,7 +438,7 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
             for (int r = 0; r < 16; ++r) W[tt][r] *= f;
         }
       }
-      // ---- step 2: R = V - exp(G) Y (S) or Y (U);  X' = fac (A R) ---------------------
+      // ---- step 2: R = diag(eW) V - exp(G_C) Y (S) or Y (U);  X' = (-)diag(rs) A0 R -----
       {
         if (s_wave) {
           // elements 4q .. 4q+3 of tile tt are tokens 32 tt + 8q + 4h + 0..3 of the lane's column
@@ -468,11 +448,11 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const uint2 vv = *reinterpret_cast<const uint2*>(pV + 32 * tt + 8 * q);
-              const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + 32 * tt + 8 * q + 4 * h);
+              const f32x4 ew = *reinterpret_cast<const f32x4*>(sF + 32 * tt + 8 * q + 4 * h);
               const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
                                    __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
 #pragma unroll
-              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] = v4[j] - eg[j] * W[tt][4 * q + j];
+              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] = fmaf(ew[j], v4[j], -eGC * W[tt][4 * q + j]);
             }
         }
         float m = 0.f;
@@ -481,7 +461,7 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
         const int er = f16_scale_exp(wave_max_uniform(m));
-        const f16_t* pA = (s_wave ? sAb : sA0) + l32 * TP + 4 * h;
+        const f16_t* pA = sA0 + l32 * TP + 4 * h;
         f16x8 fb[2][2];
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp)
@@ -496,14 +476,13 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
             for (int tt = tp; tt < 2; ++tt)
               W[tt] = mfma32h(lds_a_perm_h(pA, 32 * tt * TP + 32 * tp + 16 * mm), fb[tp][mm], W[tt]);
-        const float f_er = ldexpf(1.f, er);
-        const float* fac = sEG + (s_wave ? 2 * C : C) + 4 * h;
+        const float f_er = (s_wave ? 1.f : -1.f) * ldexpf(1.f, er);
+        const float* fac = sF + C + 4 * h;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            f32x4 f4 = *reinterpret_cast<const f32x4*>(fac + 32 * tt + 8 * q);
-            if (er != 0) f4 = f4 * f_er;
+            const f32x4 f4 = *reinterpret_cast<const f32x4*>(fac + 32 * tt + 8 * q) * f_er;
 #pragma unroll
             for (int j = 0; j < 4; ++j) W[tt][4 * q + j] *= f4[j];
           }
