@@ -273,26 +273,7 @@ struct StateLds {  // one staging buffer; the kernel keeps two
   static constexpr int O_A0 = O_V + D * TP * 2;
   static constexpr int O_SM = O_A0 + C * TP * 2;  // eW[64] = exp(G_C - G_t), rs[64], exp(G_C)
   static constexpr int BUF = O_SM + (2 * C + 4) * 4;
-  static constexpr int LDS = 2 * BUF;
 };
-
-// 8 x 8 transpose of 16-bit elements held as 8 rows of 4 dwords: dword j of
-// output column cc packs element cc of rows 2j (low half) and 2j+1 (high half).
-__device__ __forceinline__ void store_transposed8(const uint4 (&rows)[8], f16_t* dst, int pitch) {
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-    auto w = [&](int r) {
-      const uint4 u = rows[r];
-      return (cc >> 1) == 0 ? u.x : (cc >> 1) == 1 ? u.y : (cc >> 1) == 2 ? u.z : u.w;
-    };
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(w(2 * j + 1), w(2 * j), sel);
-    *reinterpret_cast<uint2*>(dst + cc * pitch) = make_uint2(o[0], o[1]);
-    *reinterpret_cast<uint2*>(dst + cc * pitch + 4) = make_uint2(o[2], o[3]);
-  }
-}
 
 // Per chunk, in the frame scaled by the chunk's gate (the gated delta rule is
 // the ungated one on values v_t exp(-G_t), then scaled by exp(G_C)):
@@ -300,11 +281,15 @@ __device__ __forceinline__ void store_transposed8(const uint4 (&rows)[8], f16_t*
 //   S <- exp(G_C) S + K^T (A0 (diag(exp(G_C - G)) V - exp(G_C) K S))
 // so both halves share A0 and every gate factor is at most 1.
 // 8 waves: wave w keeps the 32 state columns 32 (w & 3) .. of U (w < 4) or S
-// (w >= 4) in accumulators.  Chunk c is computed from one LDS buffer while the
-// loads of chunk c+1 are in flight and then staged into the other one, so each
-// chunk costs one barrier and its memory latency hides behind the products.
-__global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, const ChunkTable cks,
-                                                              const unsigned char* ws) {
+// (w >= 4) in accumulators.  The loads of chunk c+1 are in flight while chunk c
+// is computed.  NBUF = 2: chunk c+1 is staged into the other LDS buffer (one
+// barrier per chunk, one workgroup per CU); NBUF = 1: into the same buffer
+// after a barrier (two per chunk), at half the LDS and at most 128 registers,
+// so that two workgroups share a CU and cover each other's waits.
+template <int NBUF>
+__global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(const BuildArgs a,
+                                                                             const ChunkTable cks,
+                                                                             const unsigned char* ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int wave = threadIdx.x >> 6;
@@ -327,69 +312,74 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
         Z[rt][r] = (!s_wave && 32 * rt + acc_row(r, lane) == col0 + (lane & 31)) ? 1.f : 0.f;
   }
   double g_acc = 0.0;
+  float fin[3];  // threads < 64: G_t, G_C and the row scale of A0 row t
 
   // ---- staging of one chunk: loads into registers, then conversion into LDS ---------
-  // threads 0..127: an 8 x 8 block of K; 128..255: of V; 256..511: a quarter
-  // row of A0 (and, for the first 64, the token's factors)
-  uint4 raw[8];
+  // threads 0..255: a 4-token x 8-channel block of K; 256..511: of V; every
+  // thread 8 entries of A0, and the first 64 the factors of token tid
+  uint4 raw[5];
   auto load_chunk = [&](int c) {
     const int tid = opaque(threadIdx.x);
     const int c0 = t_begin + c * C;
     const int nv = min(C, t_end - c0);
     const unsigned char* rec = ws + ((size_t)(cks.base[s_local] + c) * n_chain + chain) * REC_BYTES;
-    if (tid < 256) {
-      const int id = tid & 127, tb = id & 7, db = id >> 3;
-      const uint16_t* src = reinterpret_cast<const uint16_t*>(tid < 128 ? a.k : a.v);
+    const int id = tid & 255, tb = id & 15, db = id >> 4;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(tid < 256 ? a.k : a.v);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int t = tb * 8 + r;
-        raw[r] = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
-        if (t >= nv) raw[r] = make_uint4(0, 0, 0, 0);  // keys past the end must be zero
-      }
-    } else {
-      const int u = tid - 256, t = u >> 2, cb = (u & 3) * 16;
-      const uint4* ar = reinterpret_cast<const uint4*>(rec + REC_A + (t * C + cb) * 2);
-      raw[0] = ar[0];
-      raw[1] = ar[1];
-      if (u < C) {
-        const float* G = reinterpret_cast<const float*>(rec + REC_G);
-        raw[2] = make_uint4(__float_as_uint(G[u]), __float_as_uint(G[C - 1]),
-                            __float_as_uint(reinterpret_cast<const float*>(rec + REC_RS)[u]), 0u);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int t = tb * 4 + r;
+      raw[r] = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
+      if (t >= nv) raw[r] = make_uint4(0, 0, 0, 0);  // tokens past the end must be zero
+    }
+    raw[4] = *reinterpret_cast<const uint4*>(rec + REC_A + tid * 16);  // A0 row tid / 8, entries 8 (tid % 8) ..
+    fin[0] = fin[1] = fin[2] = 0.f;
+    if (tid < C) {
+      const float* G = reinterpret_cast<const float*>(rec + REC_G);
+      fin[0] = G[tid];
+      fin[1] = G[C - 1];
+      fin[2] = reinterpret_cast<const float*>(rec + REC_RS)[tid];
     }
   };
   auto store_chunk = [&](int buf) {
     const int tid = opaque(threadIdx.x);
     unsigned char* base = smem + buf * StateLds::BUF;
-    f16_t* sK = reinterpret_cast<f16_t*>(base + StateLds::O_K);
-    f16_t* sKt = reinterpret_cast<f16_t*>(base + StateLds::O_KT);
-    f16_t* sVt = reinterpret_cast<f16_t*>(base + StateLds::O_V);
-    if (tid < 128) {  // keys: fp16 row-major and transposed
-      const int tb = tid & 7, db = tid >> 3;
+    const int id = tid & 255, tb = id & 15, db = id >> 4;
+    if (tid < 256) {  // keys: exact bf16 -> fp16, row-major
+      f16_t* sK = reinterpret_cast<f16_t*>(base + StateLds::O_K);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int r = 0; r < 4; ++r) {
         raw[r] = make_uint4(pk_f16_from_bf16x2(raw[r].x), pk_f16_from_bf16x2(raw[r].y),
                             pk_f16_from_bf16x2(raw[r].z), pk_f16_from_bf16x2(raw[r].w));
-        *reinterpret_cast<uint4*>(sK + (tb * 8 + r) * KP + db * 8) = raw[r];
+        f16_t* row = sK + (tb * 4 + r) * KP + db * 8;
+        *reinterpret_cast<uint2*>(row) = make_uint2(raw[r].x, raw[r].y);
+        *reinterpret_cast<uint2*>(row + 4) = make_uint2(raw[r].z, raw[r].w);
       }
-      store_transposed8(raw, sKt + (db * 8) * TP + tb * 8, TP);
-    } else if (tid < 256) {  // values: bf16, transposed
-      const int id = tid - 128, tb = id & 7, db = id >> 3;
-      store_transposed8(raw, sVt + (db * 8) * TP + tb * 8, TP);
-    } else {  // A0 rows and the token factors
-      f16_t* sA0 = reinterpret_cast<f16_t*>(base + StateLds::O_A0);
-      const int u = tid - 256, t = u >> 2, cb = (u & 3) * 16;
-      *reinterpret_cast<uint4*>(sA0 + t * TP + cb) = raw[0];
-      *reinterpret_cast<uint4*>(sA0 + t * TP + cb + 8) = raw[1];
-      if (u < C) {
-        float* sF = reinterpret_cast<float*>(base + StateLds::O_SM);
-        const float Gt = __uint_as_float(raw[2].x), GC = __uint_as_float(raw[2].y);
-        sF[u] = __expf(GC - Gt);                // value weight to the chunk end
-        sF[C + u] = __uint_as_float(raw[2].z);  // row scale of A0
-        if (u == 0) {
-          sF[2 * C] = __expf(GC);
-          g_acc += (double)GC;
-        }
+    }
+    // keys (fp16) or values (bf16) transposed: channel cc of the block holds its
+    // 4 tokens as two dwords (element cc of rows 0, 1 and of rows 2, 3)
+    uint16_t* sT = reinterpret_cast<uint16_t*>(base + (tid < 256 ? StateLds::O_KT : StateLds::O_V));
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+      auto w = [&](int r) {
+        const uint4 q = raw[r];
+        return (cc >> 1) == 0 ? q.x : (cc >> 1) == 1 ? q.y : (cc >> 1) == 2 ? q.z : q.w;
+      };
+      *reinterpret_cast<uint2*>(sT + (db * 8 + cc) * TP + tb * 4) =
+          make_uint2(__builtin_amdgcn_perm(w(1), w(0), sel), __builtin_amdgcn_perm(w(3), w(2), sel));
+    }
+    {
+      f16_t* sA = reinterpret_cast<f16_t*>(base + StateLds::O_A0) + (tid >> 3) * TP + (tid & 7) * 8;
+      *reinterpret_cast<uint2*>(sA) = make_uint2(raw[4].x, raw[4].y);
+      *reinterpret_cast<uint2*>(sA + 4) = make_uint2(raw[4].z, raw[4].w);
+    }
+    if (tid < C) {
+      float* sF = reinterpret_cast<float*>(base + StateLds::O_SM);
+      sF[tid] = __expf(fin[1] - fin[0]);  // value weight to the chunk end
+      sF[C + tid] = fin[2];               // row scale of A0
+      if (tid == 0) {
+        sF[2 * C] = __expf(fin[1]);
+        g_acc += (double)fin[1];
       }
     }
   };
@@ -399,9 +389,12 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
   __syncthreads();
 
   for (int c = 0; c < n_ck; ++c) {
-    if (c + 1 < n_ck) load_chunk(c + 1);
+    // NBUF = 2: the next chunk's loads fly during this chunk's products; NBUF = 1:
+    // they are issued after them (no staging registers live across the products)
+    // and the other workgroup on the CU runs meanwhile.
+    if (NBUF == 2 && c + 1 < n_ck) load_chunk(c + 1);
     {
-      const unsigned char* base = smem + (c & 1) * StateLds::BUF;
+      const unsigned char* base = smem + (NBUF == 2 ? (c & 1) : 0) * StateLds::BUF;
       const f16_t* sK = reinterpret_cast<const f16_t*>(base + StateLds::O_K);
       const f16_t* sKt = reinterpret_cast<const f16_t*>(base + StateLds::O_KT);
       const bf16_t* sVt = reinterpret_cast<const bf16_t*>(base + StateLds::O_V);
@@ -521,7 +514,15 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
         }
       }
     }
-    if (c + 1 < n_ck) store_chunk((c + 1) & 1);
+    if (c + 1 < n_ck) {  // (one branch, so the staging registers die with it)
+      if (NBUF == 1) {
+        load_chunk(c + 1);
+        __syncthreads();  // every wave is done with the buffer
+      }
+      store_chunk(NBUF == 2 ? (c + 1) & 1 : 0);
+    } else if (NBUF == 1) {
+      __syncthreads();
+    }
     __syncthreads();
   }
 
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(512, 2) void delta_state_kernel(const BuildArgs a, 
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dst[(size_t)(32 * rt + acc_row(r, lane)) * D + col0 + (lane & 31)] = Z[rt][r];
-  if (threadIdx.x == 256) a.g[unit] = (float)g_acc;
+  if (threadIdx.x == 0) a.g[unit] = (float)g_acc;
 }
 
 }  // namespace
@@ -553,8 +554,10 @@ size_t delta2_workspace_bytes(const SegTable& seg, int n_chain) {
 }
 
 hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&delta_state_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, StateLds::LDS);
+  constexpr int NBUF = 1;
+  constexpr int lds = NBUF * StateLds::BUF;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&delta_state_kernel<NBUF>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   ChunkTable ct;
   const int n_chunks = chunks_of(a.seg, &ct);
@@ -562,7 +565,7 @@ hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream)
   hipLaunchKernelGGL(delta_prep_kernel, dim3(n_chunks * a.n_chain), dim3(64), 0, stream, a, ct, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(delta_state_kernel, dim3(a.seg.n_seg * a.n_chain), dim3(512), StateLds::LDS, stream, a, ct,
+  hipLaunchKernelGGL((delta_state_kernel<NBUF>), dim3(a.seg.n_seg * a.n_chain), dim3(512), lds, stream, a, ct,
                      (const unsigned char*)w);
   return hipGetLastError();
 }
