@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64) void seam_prep_kernel(const SeamArgs a, float* 
     const float bs = sB[s];
 #pragma unroll
     for (int t = 0; t < SUB; ++t) {
-      rec[s * SUB + t] = x[t] * bs * __expf(Gn - sG[t]);  // C[s][t]
+      rec[t * SUB + s] = x[t] * bs * __expf(Gn - sG[t]);  // C^T[t][s] = Abar[t][s] exp(G_n - G_t)
       float w2 = 0.f;
 #pragma unroll
       for (int u = 0; u <= t; ++u) w2 = fmaf(__expf(sG[t] - sG[u]) * sQK[t * SUB + u], x[u] * bs, w2);

@@ -89,7 +89,7 @@ hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& a, hipStream_t 
 // Delta seam step: the state-independent part of every window (8-token
 // sub-chunks) is formed first into a workspace of seam_workspace_bytes(), one
 // record of SEAM_REC_FLOATS floats per (segment, sub-chunk, chain):
-// C[8][8], W2[8][8], exp(G)[8], exp(G_n) (seam_prep.hip).
+// C^T[8][8], W2[8][8], exp(G)[8], exp(G_n) (seam_prep.hip).
 constexpr int SEAM_REC_FLOATS = 144;
 size_t seam_workspace_bytes(int n_seg, int w, int n_chain);
 hipError_t launch_seam_prep(int d, bool in_f32, const SeamArgs& a, float* ws, hipStream_t stream);
