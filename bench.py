@@ -39,7 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "build_delta": ["segment_scan_amd/csrc/kernels/build_delta2.hip"],
     "build_sd": ["segment_scan_amd/csrc/kernels/build_sd.hip"],
-    "seam": ["segment_scan_amd/csrc/kernels/chain.hip"],
+    "seam": ["segment_scan_amd/csrc/kernels/chain.hip", "segment_scan_amd/csrc/kernels/seam_prep.hip"],
     "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
 }
 
@@ -69,7 +69,7 @@ def measured_traffic(workload: str, kernel: str):
 KERNEL_SYMBOLS = {
     "build_delta": ["delta_prep_kernel", "delta_state_kernel", "build_delta_kernel"],
     "build_sd": ["build_sd_kernel"],
-    "seam": ["chain_kernel"],
+    "seam": ["seam_prep_kernel", "chain_kernel"],
     "compose": ["chain_kernel", "compose_elem_kernel"],
 }
 CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
@@ -167,11 +167,12 @@ class ColdRequest(Workload):
         units = self.n_seg * self.H
         self.alg_bytes = units * _build_bytes(3, self.L, self.d, 2, 4, True)
         self.alg_flops = units * 8.0 * self.L * self.d ** 2
-        # executed MFMA flops of the two build kernels, 32x32x16 fp16 MFMAs per
-        # 64-token chunk and unit: Gram 3 tiles x 8 k-steps (prep), and per wave
-        # (4 waves, 2 column tiles each) K Z 16, A R 6, K^T X 16 (state)
+        # executed MFMA flops of the two build kernels, 32x32x16 MFMAs per 64-token
+        # chunk and unit: factor pass Gram 3 tiles x 8 k-steps and the inverse's two
+        # 32 x 32 x 32 products in split form (2 x 2 k-steps x 3); state pass per
+        # wave (8 waves, one 32-column tile each) K Z 16, A0 R 6, K^T X 16
         chunks = units * (self.L // 64)
-        self.exec_flops = chunks * (24 + 4 * 2 * (16 + 6 + 16)) * 32 * 32 * 16 * 2.0
+        self.exec_flops = chunks * (24 + 12 + 8 * (16 + 6 + 16)) * 32 * 32 * 16 * 2.0
 
     def setup(self):
         import torch

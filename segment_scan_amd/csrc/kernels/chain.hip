@@ -183,18 +183,20 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   refresh();
 
   // ---- U: loads, then the split into LDS -----------------------------------------
-  // thread t holds row t / TPR, elements 4 LDU (t % TPR) .. (contiguous)
+  // thread t holds row t / TPR, float4 columns (t % TPR) + TPR i: the TPR
+  // threads of a row read whole 128-byte lines with each load instruction
   f32x4 ureg[LDU];
   // (in two halves: the first flies through the whole previous segment, the
   // second only through its product, which keeps the window phase lighter)
   auto issue_U = [&](int s, int i0, int i1) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.U + (size_t)s * seg_stride + pair_off) + tid * LDU;
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.U + (size_t)s * seg_stride + pair_off) +
+                       (tid / TPR) * (D / 4) + tid % TPR;
 #pragma unroll
     for (int i = 0; i < LDU; ++i)
-      if (i >= i0 && i < i1) ureg[i] = src[i];
+      if (i >= i0 && i < i1) ureg[i] = src[TPR * i];
   };
   auto store_U = [&]() {
-    const int row = tid / TPR, c0 = (tid % TPR) * (4 * LDU);
+    const int row = tid / TPR, c0 = 4 * (tid % TPR);
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < LDU; ++i)
@@ -205,16 +207,16 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
     const int e = split_exp(m);
     const float s = ldexpf(1.f, -e);
 #pragma unroll
-    for (int q = 0; q < LDU / 2; ++q) {
-      f16x8 hv, lv;
+    for (int i = 0; i < LDU; ++i) {
+      f16x4 hv, lv;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = ureg[2 * q + j / 4][j % 4] * s;
+      for (int j = 0; j < 4; ++j) {
+        const float x = ureg[i][j] * s;
         hv[j] = hi_h(x);
         lv[j] = lo_h(x, hv[j]);
       }
-      *reinterpret_cast<f16x8*>(sUh + row * UP + c0 + 8 * q) = hv;
-      *reinterpret_cast<f16x8*>(sUl + row * UP + c0 + 8 * q) = lv;
+      *reinterpret_cast<f16x4*>(sUh + row * UP + c0 + 4 * TPR * i) = hv;
+      *reinterpret_cast<f16x4*>(sUl + row * UP + c0 + 4 * TPR * i) = lv;
     }
     if (tid % TPR == 0) sRE[row] = e;
   };
@@ -455,6 +457,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
                 XP[ct] = mfma16h(fal, fbh, XP[ct]);
               }
             }
+            sched_fence();  // bounds how far ahead fragments are loaded
           }
           // lane (l16, g), tile ct: column 32 cb + 16 ct + l16, rows 4g + j: X of
           // token 4g + j (g < 2) or P of token 4(g - 2) + j (g >= 2).  Every lane
