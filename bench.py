@@ -38,7 +38,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "build_delta": ["segment_scan_amd/csrc/kernels/build_delta2.hip"],
-    "build_sd": ["segment_scan_amd/csrc/kernels/build_sd.hip"],
+    "build_sd": ["segment_scan_amd/csrc/kernels/build_sd.hip", "segment_scan_amd/csrc/kernels/compose.hip"],
     "seam": ["segment_scan_amd/csrc/kernels/chain.hip", "segment_scan_amd/csrc/kernels/seam_prep.hip"],
     "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
 }
@@ -68,7 +68,7 @@ def measured_traffic(workload: str, kernel: str):
 # device kernels that make up each timed operation (substrings of their symbol names)
 KERNEL_SYMBOLS = {
     "build_delta": ["delta_prep_kernel", "delta_state_kernel", "build_delta_kernel"],
-    "build_sd": ["build_sd_kernel"],
+    "build_sd": ["build_sd_kernel", "compose_elem_kernel"],
     "seam": ["seam_prep_kernel", "chain_kernel"],
     "compose": ["chain_kernel", "compose_elem_kernel"],
 }
@@ -251,11 +251,13 @@ class ScalarOrDiag(Workload):
         self.g = torch.empty(gshape, device=dev)
         self.S = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
         self.S_out = torch.empty((self.H, self.d, self.d), device=dev)
+        n_ws = api.seg_build_workspace_size(self.fam, self.offsets, self.H, self.d, torch.bfloat16)
+        self.ws = torch.empty(max(n_ws, 16), device=dev, dtype=torch.uint8)
 
     def step(self, ev0, ev1):
         ev0.record()
         self.api.seg_build(self.fam, self.offsets, self.k, self.v, None, self.lg, self.tk.gate_per_chain,
-                           out=(self.g, None, self.S))
+                           out=(self.g, None, self.S), workspace=self.ws)
         ev1.record()
         self.api.compose(self.fam, self.g, None, self.S, S_out=self.S_out)
 

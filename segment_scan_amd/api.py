@@ -154,7 +154,7 @@ def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor
         g, U, S = out
     ws_bytes = 0
     if workspace is None:
-        need = seg_build_workspace_size(fam, offsets, n_chain, d, k.dtype) if fam == DELTA else 0
+        need = seg_build_workspace_size(fam, offsets, n_chain, d, k.dtype)
         if need:
             workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     if workspace is not None:

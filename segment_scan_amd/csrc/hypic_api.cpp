@@ -159,10 +159,9 @@ void fill_seg_table(hypic::SegTable* t, const int32_t* seg_offsets, int s0, int 
   for (int i = 0; i <= ns; ++i) t->off[i] = seg_offsets[s0 + i];
 }
 
-// Workspace of a build: the largest any of its launches needs (launches run in
-// stream order and reuse it).
-size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
-  if (fam != HYPIC_DELTA) return 0;
+// Workspace of a delta build: the largest any of its launches needs (launches
+// run in stream order and reuse it).
+size_t delta_workspace(int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
   size_t need = 0;
   hypic::SegTable t;
   for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
@@ -170,6 +169,32 @@ size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_cha
     need = std::max(need, hypic::build_delta_workspace(d, f32, t, n_chain));
   }
   return need;
+}
+
+// Piece split of a naive / scalar / diagonal build with few units: each
+// segment is cut into P pieces of whole 64-token chunks, built concurrently,
+// and the pieces of every segment are joined by the composition law (the same
+// law that joins segments) -- so few long segments still occupy the GPU.
+// Returns P (1: no split).
+int piece_count(int fam, int n_seg, const int32_t* seg_offsets, int n_chain) {
+  if (fam == HYPIC_DELTA) return 1;
+  const long units = (long)n_seg * n_chain;
+  int p = (int)std::min<long>(4, 512 / std::max<long>(units, 1));
+  for (int s = 0; s < n_seg && p > 1; ++s) p = std::min(p, (seg_offsets[s + 1] - seg_offsets[s] + 63) / 64);
+  return p >= 2 ? p : 1;
+}
+
+// Pieces: (g, S) of every (segment, piece, chain), then nothing else.
+size_t piece_bytes(int fam, int n_seg, int P, int n_chain, int d) {
+  const size_t pairs = (size_t)n_seg * P * n_chain;
+  const size_t gbytes = pairs * gate_len(fam, d) * 4;
+  return ((gbytes + 255) & ~(size_t)255) + pairs * d * d * 4;
+}
+
+size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
+  if (fam == HYPIC_DELTA) return delta_workspace(n_seg, seg_offsets, n_chain, d, f32);
+  const int P = piece_count(fam, n_seg, seg_offsets, n_chain);
+  return P > 1 ? piece_bytes(fam, n_seg, P, n_chain, d) : 0;
 }
 
 }  // namespace
@@ -232,6 +257,40 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
   a.S = out->S;
   a.n_chain = n_chain;
   a.gate_per_chain = in->gate_per_chain ? 1 : 0;
+  const int P = piece_count(fam, n_seg, seg_offsets, n_chain);
+  if (P > 1) {
+    // build the pieces into the workspace, then compose each segment's pieces
+    std::vector<int32_t> poff((size_t)n_seg * P + 1);
+    for (int s = 0; s < n_seg; ++s) {
+      const int nc = (seg_offsets[s + 1] - seg_offsets[s] + 63) / 64;
+      for (int p = 0; p < P; ++p) poff[(size_t)s * P + p] = seg_offsets[s] + 64 * (int)((long)p * nc / P);
+    }
+    poff[(size_t)n_seg * P] = seg_offsets[n_seg];
+    const size_t n_pairs = (size_t)n_seg * P * n_chain;
+    float* pg = reinterpret_cast<float*>(workspace);
+    float* pS = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) +
+                                         ((n_pairs * gate_len(fam, d) * 4 + 255) & ~(size_t)255));
+    a.g = pg;
+    a.S = pS;
+    const int n_piece = n_seg * P;
+    for (int s0 = 0; s0 < n_piece; s0 += hypic::kMaxSegPerLaunch) {
+      const int ns = std::min(hypic::kMaxSegPerLaunch, n_piece - s0);
+      fill_seg_table(&a.seg, poff.data(), s0, ns);
+      hipError_t e = hypic::launch_build_sd(fam, d, f32, a, ns * n_chain, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
+    }
+    hypic::ComposeArgs c{};
+    c.g = pg;
+    c.S = pS;
+    c.S_out = out->S;
+    c.g_tot = out->g;
+    c.n_seg = P;
+    c.n_chain = n_chain;
+    c.n_out = n_seg * n_chain;
+    hipError_t e = hypic::launch_compose_elem(fam, d, c, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build piece composition launch");
+    return ok();
+  }
   for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
     const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
     fill_seg_table(&a.seg, seg_offsets, s0, ns);
@@ -295,6 +354,7 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   a.U_tot = U_total;
   a.n_seg = n_seg;
   a.n_chain = n_chain;
+  a.n_out = n_chain;
   hipError_t e = (fam == HYPIC_DELTA)
                      ? hypic::launch_compose_chain(d, a, ws_need > 0 ? workspace : nullptr, workspace_bytes,
                                                    (hipStream_t)stream)

@@ -23,11 +23,13 @@ template <int FAM, int D>
 __global__ __launch_bounds__(256) void compose_elem_kernel(const ComposeArgs a) {
   constexpr int V4_PER_CHAIN = D * D / 4;
   constexpr int BLOCKS_PER_CHAIN = V4_PER_CHAIN / 256;
-  const int h = blockIdx.x / BLOCKS_PER_CHAIN;
-  const int v4 = (blockIdx.x % BLOCKS_PER_CHAIN) * 256 + threadIdx.x;  // float4 index in the chain
+  const int h = blockIdx.x / BLOCKS_PER_CHAIN;  // output (chain, or group of pairs of a chain)
+  const int v4 = (blockIdx.x % BLOCKS_PER_CHAIN) * 256 + threadIdx.x;  // float4 index in the state
   const int row = (v4 * 4) / D;
   const int n_chain = a.n_chain;
-  const size_t chain_off = (size_t)h * D * D;
+  const size_t chain_off = (size_t)h * D * D;  // outputs and start state
+  // the output's first pair: group h / n_chain of chain h % n_chain
+  const size_t pair0 = (size_t)(h / n_chain) * a.n_seg * n_chain + h % n_chain;
   const size_t seg_stride = (size_t)n_chain * D * D;
   constexpr int GL = (FAM == 2) ? D : 1;
 
@@ -37,16 +39,16 @@ __global__ __launch_bounds__(256) void compose_elem_kernel(const ComposeArgs a) 
   } else {
     cur = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const f32x4* Sp = reinterpret_cast<const f32x4*>(a.S + chain_off) + v4;
+  const f32x4* Sp = reinterpret_cast<const f32x4*>(a.S + pair0 * D * D) + v4;
   f32x4 nxt = Sp[0];
   float gn = 0.f;
-  if constexpr (FAM != 0) gn = a.g[(size_t)h * GL + (FAM == 2 ? row : 0)];
+  if constexpr (FAM != 0) gn = a.g[pair0 * GL + (FAM == 2 ? row : 0)];
   for (int s = 0; s < a.n_seg; ++s) {
     const f32x4 Si = nxt;
     const float gi = gn;
     if (s + 1 < a.n_seg) {
       nxt = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Sp) + (size_t)(s + 1) * seg_stride);
-      if constexpr (FAM != 0) gn = a.g[((size_t)(s + 1) * n_chain + h) * GL + (FAM == 2 ? row : 0)];
+      if constexpr (FAM != 0) gn = a.g[(pair0 + (size_t)(s + 1) * n_chain) * GL + (FAM == 2 ? row : 0)];
     }
     if (a.prefix) {
       reinterpret_cast<f32x4*>(a.prefix + (size_t)s * seg_stride + chain_off)[v4] = cur;
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void compose_elem_kernel(const ComposeArgs a) 
   if (a.g_tot && (blockIdx.x % BLOCKS_PER_CHAIN) == 0 && threadIdx.x < GL) {
     double acc = 0.0;
     if constexpr (FAM != 0) {
-      for (int s = 0; s < a.n_seg; ++s) acc += (double)a.g[((size_t)s * n_chain + h) * GL + threadIdx.x];
+      for (int s = 0; s < a.n_seg; ++s) acc += (double)a.g[(pair0 + (size_t)s * n_chain) * GL + threadIdx.x];
     }
     a.g_tot[(size_t)h * GL + threadIdx.x] = (float)acc;
   }
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void compose_elem_kernel(const ComposeArgs a) 
 
 template <int FAM, int D>
 hipError_t launch_elem_t(const ComposeArgs& a, hipStream_t stream) {
-  const int blocks = a.n_chain * (D * D / 4 / 256);
+  const int blocks = a.n_out * (D * D / 4 / 256);
   hipLaunchKernelGGL((compose_elem_kernel<FAM, D>), dim3(blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -40,6 +40,10 @@ struct ComposeArgs {
   float* U_tot;
   int n_seg;
   int n_chain;
+  // Grouped composition (elementwise families): n_out outputs, output h composes
+  // the n_seg consecutive pairs (h / n_chain) * n_seg + i, i < n_seg, of chain
+  // h % n_chain.  n_out = n_chain is the plain composition of all pairs.
+  int n_out;
 };
 
 struct SeamArgs {

@@ -115,6 +115,18 @@ def test_seam_workspace_size(lib):
     assert sws(d=96)[0] == UNSUPPORTED
 
 
+def test_piece_split_workspace_size(lib):
+    """Few long scalar or diagonal units are built as pieces of whole 64-token
+    chunks (at most 4, at most 512 piece units) into the workspace: (g, S) of
+    every (segment, piece, chain), the g block padded to 256 bytes."""
+    assert ws_size(lib, fam=SCALAR, offsets=(0, 1024, 2048)) == (0, 256 + 2 * 4 * 2 * 128 * 128 * 4)
+    assert ws_size(lib, fam=DIAG, offsets=(0, 1024, 2048)) == (0, 2 * 4 * 2 * 128 * 4 + 2 * 4 * 2 * 128 * 128 * 4)
+    assert ws_size(lib, fam=NAIVE, offsets=(0, 192), n_chain=1, d=64) == (0, 256 + 3 * 64 * 64 * 4)  # 3 chunks
+    assert ws_size(lib, fam=SCALAR, offsets=(0, 64, 1024)) == (0, 0)  # a one-chunk segment: no split
+    assert ws_size(lib, fam=SCALAR, offsets=(0, 1024), n_chain=256) == (0, 2 * 256 * 4 + 2 * 256 * 128 * 128 * 4)
+    assert ws_size(lib, fam=SCALAR, offsets=(0, 1024), n_chain=512) == (0, 0)  # enough units already
+
+
 def test_workspace_size(lib):
     """Only the d = 128 bf16 delta build takes a workspace: one 8704-byte WY record
     (fp16 A0 [64 x 64], 64 row scales, 64 gate prefixes) per 64-token chunk and chain."""
