@@ -145,11 +145,17 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
 /*
  * hypic_seg_build_workspace_size -- bytes of workspace hypic_seg_build needs.
  *
- * Only the DELTA family with d = 128 and bf16 tokens uses one (segments up to
- * 2048 tokens): per 64-token chunk and chain it holds that chunk's WY factor
- * (about 8.5 KiB), i.e. about 136 bytes per token and chain.  Every other
- * combination returns 0.  Arguments as for hypic_seg_build (seg_offsets is
- * validated the same way); *bytes receives the size.  Enqueues nothing.
+ *  - DELTA with d = 128 and bf16 tokens (segments up to 2048 tokens): per
+ *    64-token chunk and chain the chunk's WY factor (8,704 bytes), i.e. about
+ *    136 bytes per token and chain.
+ *  - NAIVE, SCALAR, DIAG when there are few (segment, chain) units (fewer than
+ *    256) and every segment has at least two 64-token chunks: the segments are
+ *    built as P = min(4, 512 / units, shortest segment's chunks) pieces of whole
+ *    chunks, joined by the composition law [youleyou, linear-layer paragraph];
+ *    the workspace holds the pieces' pairs: g (padded to 256 bytes) and S.
+ *  - 0 otherwise.
+ * Arguments as for hypic_seg_build (seg_offsets is validated the same way);
+ * *bytes receives the size.  Enqueues nothing.
  */
 hypic_status hypic_seg_build_workspace_size(hypic_family fam, int n_seg, const int32_t* seg_offsets,
                                             int n_chain, int d_k, int d_v, hypic_dtype dtype,
