@@ -120,22 +120,38 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
   const float G = wave_incl_scan(lg);
   sBeta[lane] = beta;
 
-  // ---- Gram K K^T on bf16 MFMA (exact products), fragments straight from HBM -------
+  // ---- the chunk's keys into LDS (bf16 rows, in the space M takes later) ----------
+  // Instruction i loads rows 4i .. 4i + 3 whole (lane l: row 4i + l / 16,
+  // channels 8 (l % 16) ..), so every load touches only four key rows.
+  constexpr int KSP = D + 8;  // 16-bit pitch of the staged rows (272 bytes)
+  static_assert(C * KSP * 2 <= C * MP * 4, "key staging fits in the M array");
+  bf16_t* sKs = reinterpret_cast<bf16_t*>(sM);
+  {
+    const uint4* kb = reinterpret_cast<const uint4*>(a.k);
+    uint4 kr[C / 4];
+#pragma unroll
+    for (int i = 0; i < C / 4; ++i) {
+      const int t = 4 * i + (lane >> 4);
+      kr[i] = kb[((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * (D / 8) + (lane & 15)];
+      if (t >= nv) kr[i] = make_uint4(0, 0, 0, 0);  // tokens past the end must be zero
+    }
+#pragma unroll
+    for (int i = 0; i < C / 4; ++i)
+      *reinterpret_cast<uint4*>(sKs + (4 * i + (lane >> 4)) * KSP + 8 * (lane & 15)) = kr[i];
+  }
+  __syncthreads();
+
+  // ---- Gram K K^T on bf16 MFMA (exact products) ------------------------------------
   // A and B fragments of a 32-token block are the same registers: lane l holds
   // token 32 tb + (l & 31), channels 16 ks + 8h .. +7.
   f32x16 g00 = zero16(), g10 = zero16(), g11 = zero16();
   {
-    const bf16_t* kb = reinterpret_cast<const bf16_t*>(a.k);
-    const int t0 = min(l32, nv - 1), t1 = min(32 + l32, nv - 1);
-    const bool z0 = l32 >= nv, z1 = 32 + l32 >= nv;
-    const bf16_t* r0 = kb + ((size_t)(c0 + t0) * n_chain + chain) * D + 8 * h;
-    const bf16_t* r1 = kb + ((size_t)(c0 + t1) * n_chain + chain) * D + 8 * h;
+    const bf16_t* r0 = sKs + l32 * KSP + 8 * h;
+    const bf16_t* r1 = sKs + (32 + l32) * KSP + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8 f0 = *reinterpret_cast<const bf16x8*>(r0 + 16 * ks);
-      bf16x8 f1 = *reinterpret_cast<const bf16x8*>(r1 + 16 * ks);
-      if (z0) f0 = bf16x8{};
-      if (z1) f1 = bf16x8{};
+      const bf16x8 f0 = *reinterpret_cast<const bf16x8*>(r0 + 16 * ks);
+      const bf16x8 f1 = *reinterpret_cast<const bf16x8*>(r1 + 16 * ks);
       g00 = mfma32(f0, f0, g00);
       g10 = mfma32(f1, f0, g10);
       g11 = mfma32(f1, f1, g11);
