@@ -12,6 +12,7 @@ accumulation -- every (segment, head) pair (T_C, S(C|0)) built concurrently
   gla           16 heads x 64 segments x 512, diagonal gates: build + compose
   gdn_warm100k  30 layers x 16 heads, 196 cached segments, w = 8: seam step fused
                 with the composition of every cached body pair
+  gdn_ragged32k the cold request with uneven segments (58 .. 2048 tokens)
 Prints one JSON line.  `value` is segment-tokens/s of the whole step; the
 `roofline` object is for the step's dominant kernel, timed with HIP events on
 the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
@@ -178,7 +179,7 @@ class ColdRequest(Workload):
         import torch
         from segment_scan_amd import api, synth
         self.api, self.synth = api, synth
-        tk = synth.gdn_cold(want_q=False)
+        tk = self._tokens()
         self.tk = tk
         self.k, self.v = to_dev(tk.k, "bf16"), to_dev(tk.v, "bf16")
         self.beta, self.lg = to_dev(tk.beta, "bf16"), to_dev(tk.log_gate, "bf16")
@@ -192,6 +193,9 @@ class ColdRequest(Workload):
         self.ws = torch.empty(max(n_ws, 16), device=dev, dtype=torch.uint8)
         n_cws = api.compose_workspace_size(synth.DELTA, self.n_seg, self.H, self.d)
         self.cws = torch.empty(n_cws, device=dev, dtype=torch.uint8) if n_cws else None
+
+    def _tokens(self):
+        return self.synth.gdn_cold(want_q=False)
 
     def step(self, ev0, ev1):
         from segment_scan_amd.synth import DELTA
@@ -218,6 +222,30 @@ class ColdRequest(Workload):
         return {"workload": self.name, "family": "gdn", "heads": self.H, "d": self.d, "segments": self.n_seg,
                 "segment_len": self.L, "tokens": self.tokens, "inputs": "bf16", "accumulate": "fp32",
                 "step": "hypic_seg_build (2048 units) + hypic_compose (32 chains x 64)"}
+
+
+class RaggedRequest(ColdRequest):
+    """The cold GDN request with uneven segments: 32 heads, 64 segments of 58 .. 2048
+    tokens (log-normal lengths, median 366), 32,768 tokens; built longest first."""
+    name = "gdn_ragged32k"
+
+    def __init__(self):
+        from segment_scan_amd import synth
+        super().__init__()
+        lens = synth.ragged_lengths(self.n_seg, self.tokens)
+        self.alg_bytes = self.H * sum(_build_bytes(3, int(L), self.d, 2, 4, True) for L in lens)
+        self.alg_flops = self.H * 8.0 * self.tokens * self.d ** 2
+        chunks = self.H * sum((int(L) + 63) // 64 for L in lens)
+        self.exec_flops = chunks * (24 + 12 + 8 * (16 + 6 + 16)) * 32 * 32 * 16 * 2.0
+
+    def _tokens(self):
+        return self.synth.gdn_ragged(want_q=False)
+
+    def config(self):
+        c = super().config()
+        c.update(workload=self.name, segment_len="58..2048 (log-normal, median 366)",
+                 step="hypic_seg_build (2048 ragged units, longest first) + hypic_compose (32 chains x 64)")
+        return c
 
 
 class ScalarOrDiag(Workload):
@@ -358,6 +386,7 @@ WORKLOADS = {
     "retnet": lambda: ScalarOrDiag("retnet", 1, 16, 1024, 8, 128),
     "gla": lambda: ScalarOrDiag("gla", 2, 64, 512, 16, 128),
     "gdn_warm100k": WarmRequest,
+    "gdn_ragged32k": RaggedRequest,
 }
 
 

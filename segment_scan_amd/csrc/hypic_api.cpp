@@ -152,11 +152,19 @@ hypic_status check_offsets(int n_seg, const int32_t* seg_offsets) {
   return HYPIC_OK;
 }
 
-// Fills the launch table of segments [s0, s0 + ns).
+// Fills the launch table of segments [s0, s0 + ns), with the longest-first
+// workgroup order [youleyou, segment-parallelism paragraph: LPT scheduling of
+// uneven segments].
 void fill_seg_table(hypic::SegTable* t, const int32_t* seg_offsets, int s0, int ns) {
   t->n_seg = ns;
   t->seg_base = s0;
   for (int i = 0; i <= ns; ++i) t->off[i] = seg_offsets[s0 + i];
+  int idx[hypic::kMaxSegPerLaunch];
+  for (int i = 0; i < ns; ++i) idx[i] = i;
+  std::stable_sort(idx, idx + ns, [&](int x, int y) {
+    return t->off[x + 1] - t->off[x] > t->off[y + 1] - t->off[y];
+  });
+  for (int i = 0; i < ns; ++i) t->order[i] = (uint8_t)idx[i];
 }
 
 // Workspace of a delta build: the largest any of its launches needs (launches
@@ -455,11 +463,11 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
     b.S = window_out->S;
     b.n_chain = n_chain;
     b.gate_per_chain = seam->gate_per_chain ? 1 : 0;
+    std::vector<int32_t> woff((size_t)n_seg + 1);
+    for (int i = 0; i <= n_seg; ++i) woff[i] = i * w;
     for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
       const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
-      b.seg.n_seg = ns;
-      b.seg.seg_base = s0;
-      for (int i = 0; i <= ns; ++i) b.seg.off[i] = (s0 + i) * w;
+      fill_seg_table(&b.seg, woff.data(), s0, ns);
       e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta_single(d, f32, b, ns * n_chain, (hipStream_t)stream)
                                : hypic::launch_build_sd(fam, d, f32, b, ns * n_chain, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "hypic_seam_step window pairs launch");

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256, (IN_F32 ? 1 : 2)) void build_delta_kernel(cons
   const int lane0 = lane_id();
   const int wave = wave_id();
   const int n_chain = a.n_chain;
-  const int s_local = blockIdx.x / n_chain;
+  const int s_local = a.seg.order[blockIdx.x / n_chain];  // longest segments first
   const int chain = blockIdx.x % n_chain;
   const int t_begin = a.seg.off[s_local];
   const int t_end = a.seg.off[s_local + 1];

@@ -312,7 +312,7 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
   const bool s_wave = wave >= 4;
   const int col0 = (wave & 3) * 32;
   const int n_chain = a.n_chain;
-  const int s_local = blockIdx.x / n_chain;
+  const int s_local = a.seg.order[blockIdx.x / n_chain];  // longest segments first
   const int chain = blockIdx.x % n_chain;
   const int t_begin = a.seg.off[s_local], t_end = a.seg.off[s_local + 1];
   const int n_ck = (t_end - t_begin + C - 1) / C;

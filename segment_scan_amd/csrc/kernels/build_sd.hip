@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
   const int wave = wave_id();
   const int n_chain = a.n_chain;
   const int u_local = blockIdx.x;
-  const int s_local = u_local / n_chain;
+  const int s_local = a.seg.order[u_local / n_chain];  // longest segments first
   const int h = u_local % n_chain;
   const int t_begin = a.seg.off[s_local];
   const int t_end = a.seg.off[s_local + 1];

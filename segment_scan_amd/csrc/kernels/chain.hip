@@ -186,8 +186,9 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   // thread t holds row t / TPR, float4 columns (t % TPR) + TPR i: the TPR
   // threads of a row read whole 128-byte lines with each load instruction
   f32x4 ureg[LDU];
-  // (in two halves: the first flies through the whole previous segment, the
-  // second only through its product, which keeps the window phase lighter)
+  // (seam mode: in two halves, the first flying through the whole previous
+  // segment, the second only through its product, which keeps the window phase
+  // lighter; compose mode: whole, one segment ahead)
   auto issue_U = [&](int s, int i0, int i1) {
     const f32x4* src = reinterpret_cast<const f32x4*>(a.U + (size_t)s * seg_stride + pair_off) +
                        (tid / TPR) * (D / 4) + tid % TPR;
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   put_B(St, (SEAM || !pairs) ? 1.f : __expf(g_next));
   if (pairs) {
     store_U();
-    if (nseg > 1) issue_U(1, 0, LDU / 2);
+    if (nseg > 1) issue_U(1, 0, SEAM ? LDU / 2 : LDU);
   }
   if constexpr (SEAM) stage_window();
   __syncthreads();
@@ -540,15 +541,17 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
     // ---- body pair: S <- exp(g) U S + S_B (or U_total <- U U_total) ----------------
     if (pairs) {
       refresh();
-      if (seg + 1 < nseg) issue_U(seg + 1, LDU / 2, LDU);
-      // T = U (exp(g) S) 2^-ec / 2^e_row + S_B 2^-ec / 2^e_row: the pair's state
-      // enters as the accumulator's start (all factors are powers of two)
+      if (SEAM && seg + 1 < nseg) issue_U(seg + 1, LDU / 2, LDU);
+      // T = U (exp(g) S) 2^-ec / 2^e_row (+ S_B 2^-ec / 2^e_row): in seam mode the
+      // pair's state enters as the accumulator's start (all factors are powers of
+      // two), which frees its registers during the product; in compose mode it is
+      // added afterwards, which gives its loads the product's time to land
       f32x16 T;
       int er[16];  // the product's scale exponent per element (row and column)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         er[r] = sRE[32 * rb + acc_row(r, lane)] + ec;
-        T[r] = ut ? 0.f : ldexpf(Si[r], -er[r]);
+        T[r] = (ut || !SEAM) ? 0.f : ldexpf(Si[r], -er[r]);
       }
       {
         const f16_t* ah = sUh + (32 * rb + l32) * UP + 8 * h;
@@ -568,7 +571,10 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) St[r] = ldexpf(T[r], er[r]);
+      for (int r = 0; r < 16; ++r) {
+        St[r] = ldexpf(T[r], er[r]);
+        if (!SEAM && !ut) St[r] += Si[r];
+      }
       put_cmax(St);
       if (seg + 1 < nseg) {
         if (!ut && a.prefix) store_tile(a.prefix + (size_t)(seg + 1) * seg_stride + chain_off, St);
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
         if constexpr (SEAM) stage_window();
         // the next pair's loads, after the staging work of this interval
         if (!ut) issue_Si(seg + 1);
-        if (seg + 2 < nseg) issue_U(seg + 2, 0, LDU / 2);
+        if (seg + 2 < nseg) issue_U(seg + 2, 0, SEAM ? LDU / 2 : LDU);
       }
       __syncthreads();
     } else if constexpr (SEAM) {

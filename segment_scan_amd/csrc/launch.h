@@ -12,9 +12,15 @@ constexpr int kMaxSegPerLaunch = 240;
 
 struct SegTable {
   int32_t off[kMaxSegPerLaunch + 1];  // token offsets of this launch's segments
-  int n_seg;                          // segments in this launch
-  int seg_base;                       // global index of the first one
+  // Longest-processing-time order: workgroup row i of the launch builds segment
+  // order[i] (the segments sorted by length, longest first, ties by index), so
+  // that in a ragged batch the long units start first and the short ones fill
+  // the tail.
+  uint8_t order[kMaxSegPerLaunch];
+  int n_seg;     // segments in this launch
+  int seg_base;  // global index of the first one
 };
+static_assert(kMaxSegPerLaunch <= 256, "order entries are 8-bit");
 
 struct BuildArgs {
   const void* k;

@@ -28,7 +28,7 @@ NAIVE, SCALAR, DIAG, DELTA = 0, 1, 2, 3
 FAMILY_NAMES = {NAIVE: "naive", SCALAR: "scalar", DIAG: "diag", DELTA: "delta"}
 
 # tensor ids inside the seed sequence
-T_Q, T_K, T_V, T_BETA, T_GATE, T_PG, T_PU, T_PS, T_SINIT = range(9)
+T_Q, T_K, T_V, T_BETA, T_GATE, T_PG, T_PU, T_PS, T_SINIT, T_LEN = range(10)
 SEED_ROOT = 20260701
 
 
@@ -210,6 +210,31 @@ def gdn_cold(n_seg=64, L=512, n_chain=32, d=128, dtype="bf16", gate_scale=1.0 / 
     q, k, v, beta, lg = _draw_delta_tokens(4, n_tok, n_chain, d, dtype, gate_scale, want_q=want_q)
     return Tokens(DELTA, dtype, n_chain, d, d, k, v, q, beta, lg, False, even_offsets(n_seg, L),
                   {"workload": "gdn_cold32k", "n_seg": n_seg, "L": L, "gate_scale": gate_scale})
+
+
+def ragged_lengths(n_seg: int, total: int, workload: int = 12, sigma: float = 0.9, min_len: int = 32,
+                   max_len: int = 2048):
+    """Uneven segment lengths summing to `total`: log-normal shares (log-sd
+    sigma), clipped to [min_len, max_len]; the rounding remainder goes to the
+    segments in index order, each up to max_len."""
+    w = np.exp(rng(workload, T_LEN).standard_normal(n_seg) * sigma)
+    lens = np.clip(np.floor(w / w.sum() * total), min_len, max_len).astype(np.int64)
+    rest = total - int(lens.sum())
+    for i in range(n_seg):
+        step = int(np.clip(rest, min_len - lens[i], max_len - lens[i]))
+        lens[i] += step
+        rest -= step
+    assert rest == 0 and lens.min() >= min_len and lens.max() <= max_len and int(lens.sum()) == total
+    return lens
+
+
+def gdn_ragged(n_seg=64, n_chain=32, d=128, total=32768, dtype="bf16", gate_scale=1.0 / 8, want_q=False) -> Tokens:
+    """The 32k-token cold GDN request with uneven segments (ragged_lengths)."""
+    tk = gdn_cold(n_seg=n_seg, L=total // n_seg, n_chain=n_chain, d=d, dtype=dtype, gate_scale=gate_scale,
+                  want_q=want_q)
+    t = with_offsets(tk, ragged_offsets(ragged_lengths(n_seg, total)))
+    t.meta = {**tk.meta, "workload": "gdn_ragged32k", "lengths": "log-normal, sigma 0.9"}
+    return t
 
 
 def ragged_offsets(lengths) -> np.ndarray:

@@ -268,3 +268,13 @@ def test_binding_requires_gpu_tensors(lib):
     k = torch.zeros((4, 1, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         api.seg_build(NAIVE, [0, 4], k, k)
+
+
+def test_ragged_lengths_recipe():
+    """The seeded ragged-segment recipe: exact total, bounds, and a long tail."""
+    from segment_scan_amd import synth
+    import numpy as np
+    lens = synth.ragged_lengths(64, 32768)
+    assert int(lens.sum()) == 32768 and lens.min() >= 32 and lens.max() <= 2048
+    assert np.array_equal(lens, synth.ragged_lengths(64, 32768))  # seeded
+    assert lens.max() / np.median(lens) > 4

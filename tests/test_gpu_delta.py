@@ -150,3 +150,13 @@ def test_explicit_workspace_reused_across_calls():
     assert torch.equal(S2, S0[:2]) and torch.equal(U2, U0[:2])
     with pytest.raises(api.HypicError, match="workspace too small"):
         api.seg_build(DELTA, off, d["k"], d["v"], d["beta"], d["log_gate"], workspace=ws[:need - 16])
+
+
+def test_gdn_ragged_request_longest_first():
+    """The ragged 32k-token cold request (64 segments of 58 .. 2048 tokens, 32
+    heads), built with the longest segments' workgroups first: every unit
+    against the oracle."""
+    tk = synth.gdn_ragged()
+    lens = np.diff(tk.offsets)
+    assert lens.min() < 100 and lens.max() == 2048
+    check_build(tk, "gdn_ragged32k")
