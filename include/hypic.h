@@ -182,12 +182,14 @@ hypic_status hypic_seg_build_workspace_size(hypic_family fam, int n_seg, const i
  *   workspace      NULL, or device scratch of workspace_bytes bytes, at least
  *                  hypic_compose_workspace_size(); contents ignored on entry and
  *                  undefined on exit, in use until the stream passes the call.
- *                  For the DELTA family with few chains and no prefix states
- *                  it lets the composition run in two levels: blocks of
- *                  consecutive segments are composed in parallel (by
- *                  associativity, [hwlabs, section 세그먼트 누적 전이 연산자]) and
- *                  each chain then composes its block pairs in order.  The
- *                  result equals the single-pass one up to rounding.
+ *                  For the DELTA family with few chains (at most 256 / (d / 32))
+ *                  and at least 8 segments it lets the composition run as a
+ *                  scan: blocks of consecutive segments are composed in
+ *                  parallel (by associativity, [hwlabs, section 세그먼트 누적
+ *                  전이 연산자]), each chain then composes its block pairs in
+ *                  order, and, if prefix_states are requested, every block is
+ *                  run again from its start state in parallel to emit them.
+ *                  The result equals the single-pass one up to rounding.
  * Errors as for hypic_seg_build (a workspace that is smaller than required or
  * overlaps another argument is HYPIC_E_INVALID).
  */
@@ -197,9 +199,10 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * hypic_compose_workspace_size -- bytes of workspace that enable the two-level
- * schedule of hypic_compose for these sizes (0: not used).  want_prefix: 1 if
- * prefix_states will be requested.  *bytes receives the size; enqueues nothing.
+ * hypic_compose_workspace_size -- bytes of workspace that enable the blocked
+ * schedule of hypic_compose for these sizes (0: not used): per (block, chain)
+ * its g, U and S, and with want_prefix = 1 (prefix_states will be requested)
+ * also its start state.  *bytes receives the size; enqueues nothing.
  */
 hypic_status hypic_compose_workspace_size(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v,
                                           int want_prefix, size_t* bytes);

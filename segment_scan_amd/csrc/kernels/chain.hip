@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
       St[r] = a.S_in ? a.S_in[chain_off + row * D + col0 + tcol] : 0.f;
     }
   }
-  if (!ut && a.prefix) store_tile(a.prefix + chain_off, St);
+  if (!ut && a.prefix) store_tile(a.prefix + pair_off, St);  // prefix states follow the pairs' layout
   put_cmax(St);
   float g_next = 0.f;
   if (pairs) {
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
       }
       put_cmax(St);
       if (seg + 1 < nseg) {
-        if (!ut && a.prefix) store_tile(a.prefix + (size_t)(seg + 1) * seg_stride + chain_off, St);
+        if (!ut && a.prefix) store_tile(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off, St);
         if (!ut) g_next = a.g[pidx + (size_t)(seg + 1) * n_chain];
       }
       __syncthreads();  // every wave is done with sU and sB
@@ -637,8 +637,11 @@ hipError_t launch_chain_d(const ChainArgs& a, bool want_ut, hipStream_t stream) 
 namespace {
 // Two-level schedule for few chains: about 128 (block, chain) units compose
 // their blocks in parallel, then each chain composes its block pairs in order.
-bool tree_plan(int d, int n_seg, int n_chain, bool prefix, int* blk_len, int* n_blocks) {
-  if (prefix || n_seg < 8 || n_chain * (d / 32) > 256) return false;
+// With prefix states a third level re-runs every block from its start state in
+// parallel (a three-phase scan [hwlabs, section 세그먼트 누적 전이 연산자: the
+// composition is associative]).
+bool tree_plan(int d, int n_seg, int n_chain, bool /*prefix*/, int* blk_len, int* n_blocks) {
+  if (n_seg < 8 || n_chain * (d / 32) > 256) return false;
   int nb = std::max(2, std::min(n_seg / 4, 128 / n_chain));
   const int bl = (n_seg + nb - 1) / nb;
   *blk_len = bl;
@@ -652,7 +655,7 @@ size_t compose_workspace_bytes(int d, int n_seg, int n_chain, bool prefix) {
   int bl, nb;
   if (!tree_plan(d, n_seg, n_chain, prefix, &bl, &nb)) return 0;
   const size_t units = (size_t)nb * n_chain;
-  return align256(units * 4) + 2 * units * d * d * 4;
+  return align256(units * 4) + (prefix ? 3 : 2) * units * d * d * 4;  // g, U, S (and start state) per block
 }
 
 hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -675,24 +678,41 @@ hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws
     a1.n_chain = c.n_chain;
     a1.blk_len = bl;
     a1.n_units = (int)units;
-    ChainArgs a2{};  // level 2: the block pairs of each chain in order
+    ChainArgs a2{};  // level 2: the block pairs of each chain in order (and each block's start state)
+    float* wP = c.prefix ? wS + units * d * d : nullptr;
     a2.g = wg;
     a2.U = wU;
     a2.S = wS;
     a2.S_in = c.S_init;
     a2.S_out = c.S_out;
+    a2.prefix = wP;
     a2.g_tot = c.g_tot;
     a2.U_tot = c.U_tot;
     a2.n_seg = nb;
     a2.n_chain = c.n_chain;
     a2.n_units = c.n_chain;
+    // level 3 (prefix states only): every block again from its start state, in
+    // parallel, emitting the state before each of its segments
+    ChainArgs a3{};
+    a3.g = c.g;
+    a3.U = c.U;
+    a3.S = c.S;
+    a3.S_in = wP;
+    a3.S_out = wS;  // the block pairs are spent by now
+    a3.prefix = c.prefix;
+    a3.n_seg = c.n_seg;
+    a3.n_chain = c.n_chain;
+    a3.blk_len = bl;
+    a3.n_units = (int)units;
     hipError_t e;
     if (d == 128) {
       e = launch_chain_d<128, false, false>(a1, true, stream);
       if (e == hipSuccess) e = launch_chain_d<128, false, false>(a2, c.U_tot != nullptr, stream);
+      if (e == hipSuccess && wP) e = launch_chain_d<128, false, false>(a3, false, stream);
     } else if (d == 64) {
       e = launch_chain_d<64, false, false>(a1, true, stream);
       if (e == hipSuccess) e = launch_chain_d<64, false, false>(a2, c.U_tot != nullptr, stream);
+      if (e == hipSuccess && wP) e = launch_chain_d<64, false, false>(a3, false, stream);
     } else {
       e = hipErrorInvalidValue;
     }

@@ -85,15 +85,16 @@ def ws_size(lib, fam=DELTA, offsets=(0, 64, 128), n_chain=2, d=128, dtype=BF16):
 
 
 def test_compose_workspace_size(lib):
-    """The two-level schedule applies to the dense family with few chains and no
-    prefix states: one block pair (g, U, S) per (block, chain), about 128 units."""
+    """The blocked schedule applies to the dense family with few chains: one block
+    pair (g, U, S) per (block, chain), about 128 units, and with prefix states
+    each block's start state too."""
     def cws(fam=DELTA, n_seg=64, n_chain=32, d=128, prefix=0):
         out = ctypes.c_size_t(7)
         st = lib.hypic_compose_workspace_size(fam, n_seg, n_chain, d, d, prefix, ctypes.byref(out))
         return st, out.value
     units = 4 * 32  # 64 segments in 4 blocks of 16, 32 chains
     assert cws() == (0, ((units * 4 + 255) // 256) * 256 + 2 * units * 128 * 128 * 4)
-    assert cws(prefix=1) == (0, 0)
+    assert cws(prefix=1) == (0, ((units * 4 + 255) // 256) * 256 + 3 * units * 128 * 128 * 4)
     assert cws(n_chain=480) == (0, 0)
     assert cws(n_seg=4) == (0, 0)
     assert cws(fam=SCALAR) == (0, 0)

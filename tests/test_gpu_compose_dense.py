@@ -90,3 +90,34 @@ def test_compose_dense_two_level_schedule():
         assert_units_close(name + ".S_out", host(res["S_out"]), ref["S_out"], 1e-5, unit_dims=1)
         assert_g_close(name + ".g_tot", host(res["g_tot"]), ref["g_tot"], 1e-5)
         assert_units_close(name + ".U_tot", host(res["U_tot"]), ref["U_tot"], 1e-5, unit_dims=1)
+
+
+def test_compose_dense_scan_with_prefix_states():
+    """Few chains with prefix states: the three-phase scan (37 segments -> 8 blocks,
+    the last ragged; block pairs, block start states in order, then every block
+    again from its start state) must match the oracle, as the single pass must.
+
+    Tolerance: every prefix state of a 37-step chain of random dense pairs is
+    compared, not only the end state.  Each split-fp16 product rounds at about
+    2^-22 per operand, times |U||S| / |U S| ~ 7 for these random factors, and a
+    state carries the rounding of the previous steps scaled by the chain's
+    contraction (close to 1 here): about 1e-5 at the worst prefix state, for
+    either schedule, hence twice the fp32-class bound."""
+    import torch
+    g, U, S = synth.warm_pairs_layer(6, n_seg=37, n_head=5)
+    g = (g - 0.03 * np.arange(g.size).reshape(g.shape) / g.size).astype(np.float32).astype(np.float64)
+    S_init = np.random.default_rng(6).standard_normal(S.shape[1:]).astype(np.float32).astype(np.float64)
+    need = api.compose_workspace_size(DELTA, 37, 5, 128, want_prefix=True)
+    assert need > api.compose_workspace_size(DELTA, 37, 5, 128) > 0
+    announce("scan_prefix", "segs", 37, "chains", 5, "workspace", need)
+    dg, dU, dS, dI = dev_f32(g), dev_f32(U), dev_f32(S), dev_f32(S_init)
+    ws = torch.full((need,), 0x7F, device="cuda", dtype=torch.uint8)
+    scan = api.compose(DELTA, dg, dU, dS, S_init=dI, want_prefix=True, want_total=True, workspace=ws)
+    flat = api.compose(DELTA, dg, dU, dS, S_init=dI, want_prefix=True, want_total=True, workspace=None)
+    torch.cuda.synchronize()
+    ref = oracle.compose(DELTA, g, U, S, S_init=S_init, want_prefix=True, want_total=True)
+    for name, res, tol in (("scan", scan, 2e-5), ("flat", flat, 2e-5)):
+        assert_units_close(name + ".S_out", host(res["S_out"]), ref["S_out"], tol, unit_dims=1)
+        assert_units_close(name + ".prefix", host(res["prefix"]), ref["prefix"], tol)
+        assert_g_close(name + ".g_tot", host(res["g_tot"]), ref["g_tot"], tol)
+        assert_units_close(name + ".U_tot", host(res["U_tot"]), ref["U_tot"], tol, unit_dims=1)
