@@ -59,8 +59,9 @@ def _load():
         lib.hypic_ref_compose.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I]
         lib.hypic_ref_seam.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, I]
         lib.hypic_ref_sequential.argtypes = [I, I, I, I, I, P, P, P, P, P, I, P, P, P, I]
+        lib.hypic_ref_rerotate.argtypes = [I, I, I, I, I, P, ctypes.c_double, P, P, I]
         for f in (lib.hypic_ref_build, lib.hypic_ref_compose, lib.hypic_ref_seam,
-                  lib.hypic_ref_sequential):
+                  lib.hypic_ref_sequential, lib.hypic_ref_rerotate):
             f.restype = I
         lib.hypic_ref_max_threads.restype = I
         _lib = lib
@@ -175,6 +176,20 @@ def sequential(fam, k, v, beta=None, log_gate=None, gate_per_chain=False, S_init
                                       _p(o), _threads(n_threads))
     _check(rc, "hypic_ref_sequential")
     return S, o
+
+
+def rerotate(fam, U, S, delta, base=10000.0, n_threads=None):
+    """State re-rotation of cached pairs to offsets delta[s] (see hypic_ref.c):
+    returns (U', S') = (R U R^T, R S) per (segment, chain); U' None unless delta family."""
+    S = _f64(S).copy()
+    U = None if U is None else _f64(U).copy()
+    n_seg, n_chain, dk, dv = S.shape
+    d = np.ascontiguousarray(delta, dtype=np.int32)
+    assert d.shape == (n_seg,)
+    rc = _load().hypic_ref_rerotate(fam, n_seg, n_chain, dk, dv, _p(d), float(base), _p(U), _p(S),
+                                    _threads(n_threads))
+    _check(rc, "hypic_ref_rerotate")
+    return U, S
 
 
 def transition_dense(fam, g, U, dk):

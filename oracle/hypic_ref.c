@@ -57,8 +57,13 @@
  *   pairs U         : [n_seg, n_chain, d_k, d_k] (delta only)
  *   pairs S, states : [.., n_chain, d_k, d_v]
  *
+ * Rotary re-rotation (hypic_ref_rerotate, below): the pages name a state
+ * re-rotation step for linear layers that carry rotary position encoding but
+ * give no formula; the reading taken is stated at that function.
+ *
  * Parity pins (see the tests): brute-force matrix products on tiny inputs,
  * the composition law against straight recurrence over the concatenation,
+ * re-rotation against a build from keys rotated at the new positions,
  * closed forms of the scalar and diagonal families, the one-token and
  * overwrite cases of the delta rule, Householder orthogonality, and the size
  * of the naive-addition error on a slow-decay head.
@@ -450,6 +455,83 @@ int hypic_ref_sequential(int fam, int n_tok, int n_chain, int dk, int dv, const 
       }
     }
     free(work);
+  }
+  return status;
+}
+
+/*
+ * State re-rotation of cached pairs to a new position [youleyou, linear-layer
+ * paragraph: for linear layers with RoPE a "state re-rotation" patch aligns a
+ * cached segment exactly; the pages give no formula].  Reading taken: keys
+ * carry the rotary encoding of RoFormer -- pairs (2i, 2i+1) of the d_k axis
+ * rotated by the angle pos * theta_i, theta_i = base^(-2i/d_k) -- at their
+ * position within the segment when the pair was cached.  Reused with its first
+ * token at offset p, every key becomes R(p) R(t) k = R(p) k_cached, so each
+ * per-token transition a (I - beta k k^T) becomes R(p) A_t R(p)^T and each write
+ * R(p) k v^T; hence
+ *     T' = R(p) T R(p)^T,   S'(C|0) = R(p) S(C|0).
+ * For the naive and scalar families T is a multiple of I and stays put; for the
+ * delta family U <- R U R^T (g unchanged).  A diagonal transition does not stay
+ * diagonal under R (unless its gates agree within each pair), so that family
+ * is refused.  delta[s] is segment s's offset p (any sign); pairs are updated
+ * in place.  Plain dense products with the explicit rotation matrix.
+ */
+static void rope_matrix(double* R, int dk, long p, double base) {
+  for (int i = 0; i < dk * dk; ++i) R[i] = 0.0;
+  for (int i = 0; i < dk / 2; ++i) {
+    const double theta = pow(base, -2.0 * i / dk);
+    const double ang = (double)p * theta;
+    const double c = cos(ang), sn = sin(ang);
+    R[(2 * i) * dk + 2 * i] = c;
+    R[(2 * i) * dk + 2 * i + 1] = -sn;
+    R[(2 * i + 1) * dk + 2 * i] = sn;
+    R[(2 * i + 1) * dk + 2 * i + 1] = c;
+  }
+}
+
+int hypic_ref_rerotate(int fam, int n_seg, int n_chain, int dk, int dv, const int32_t* delta, double base,
+                       double* U, double* S, int n_threads) {
+  if (!fam_ok(fam) || fam == REF_DIAG || dk < 2 || dk % 2 || !S || !delta || !(base > 0.0)) return 1;
+  if (fam == REF_DELTA && !U) return 1;
+  int status = 0;
+#pragma omp parallel num_threads(n_threads > 0 ? n_threads : 1)
+  {
+    double* R = (double*)malloc(sizeof(double) * dk * dk);
+    double* tmp = (double*)malloc(sizeof(double) * dk * (dk > dv ? dk : dv));
+    if (!R || !tmp) {
+#pragma omp atomic write
+      status = 2;
+    } else {
+#pragma omp for schedule(dynamic)
+      for (long u = 0; u < (long)n_seg * n_chain; ++u) {
+        rope_matrix(R, dk, delta[u / n_chain], base);
+        double* Su = S + (size_t)u * dk * dv;  /* S <- R S */
+        for (int i = 0; i < dk; ++i)
+          for (int c = 0; c < dv; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) acc += R[i * dk + j] * Su[(size_t)j * dv + c];
+            tmp[(size_t)i * dv + c] = acc;
+          }
+        memcpy(Su, tmp, sizeof(double) * dk * dv);
+        if (fam == REF_DELTA) {  /* U <- R U R^T */
+          double* Uu = U + (size_t)u * dk * dk;
+          for (int i = 0; i < dk; ++i)
+            for (int c = 0; c < dk; ++c) {
+              double acc = 0.0;
+              for (int j = 0; j < dk; ++j) acc += R[i * dk + j] * Uu[(size_t)j * dk + c];
+              tmp[(size_t)i * dk + c] = acc;
+            }
+          for (int i = 0; i < dk; ++i)
+            for (int c = 0; c < dk; ++c) {
+              double acc = 0.0;
+              for (int j = 0; j < dk; ++j) acc += tmp[(size_t)i * dk + j] * R[c * dk + j];
+              Uu[(size_t)i * dk + c] = acc;
+            }
+        }
+      }
+    }
+    free(R);
+    free(tmp);
   }
   return status;
 }

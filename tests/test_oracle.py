@@ -357,3 +357,79 @@ def test_gdn_tiny_workload_compose_vs_sequential():
         c = oracle.compose(DELTA, g, U, S)
         Sseq, _ = oracle.sequential(DELTA, tk.k, tk.v, tk.beta, tk.log_gate)
         assert rel(c["S_out"], Sseq) < 1e-11, scale
+
+
+# ------------------------------------------------------- rotary re-rotation
+
+
+def rope_keys(k, pos, base):
+    """Rotary encoding of keys at positions pos (RoFormer, pairs (2i, 2i+1) turned
+    by pos * base^(-2i/d)), written with complex numbers rather than matrices."""
+    dk = k.shape[-1]
+    theta = base ** (-np.arange(dk // 2) * 2.0 / dk)
+    z = (k[..., 0::2] + 1j * k[..., 1::2]) * np.exp(1j * np.asarray(pos, np.float64)[:, None, None] * theta)
+    out = np.empty_like(k)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+@pytest.mark.parametrize("fam", [NAIVE, SCALAR, DELTA])
+@pytest.mark.parametrize("base", [10000.0, 500.0])
+def test_rerotation_equals_building_at_the_new_offset(fam, base):
+    # A pair built from keys rotated at positions 0..L-1 of its segment, then
+    # re-rotated to offset p, must equal the pair built from the keys rotated at
+    # p .. p+L-1 [youleyou, linear-layer paragraph: re-rotation aligns a cached
+    # segment exactly].
+    dk, dv = 8, 5
+    offsets = np.array([0, 5, 6, 16, 23], np.int32)
+    x = rand_tokens(fam, 23, 3, dk, dv, seed=4100 + fam)
+    local = np.concatenate([np.arange(offsets[s + 1] - offsets[s]) for s in range(4)])
+    p = np.array([7, 0, -3, 40961], np.int32)
+    absolute = local + np.repeat(p, np.diff(offsets))
+    g0, U0, S0 = oracle.build_pairs(fam, offsets, rope_keys(x["k"], local, base), x["v"], x["beta"], x["log_gate"])
+    g1, U1, S1 = oracle.build_pairs(fam, offsets, rope_keys(x["k"], absolute, base), x["v"], x["beta"],
+                                    x["log_gate"])
+    Ur, Sr = oracle.rerotate(fam, U0, S0, p, base)
+    assert rel(Sr, S1) < 1e-11
+    if fam == DELTA:
+        assert rel(Ur, U1) < 1e-11
+    assert np.array_equal(g0, g1)
+
+
+def test_rerotation_closed_form_two_dims():
+    # d_k = 2: R(p) is the plane rotation by angle p (theta_0 = 1).
+    S = np.array([[[[1.0, 2.0, -1.0], [0.5, -3.0, 4.0]]]])
+    U = np.array([[[[2.0, 1.0], [-1.0, 0.25]]]])
+    p = 3
+    c, s = np.cos(p), np.sin(p)
+    R = np.array([[c, -s], [s, c]])
+    Ur, Sr = oracle.rerotate(DELTA, U, S, [p])
+    np.testing.assert_allclose(Sr[0, 0], R @ S[0, 0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(Ur[0, 0], R @ U[0, 0] @ R.T, rtol=0, atol=1e-14)
+
+
+def test_rerotation_group_law_and_composition():
+    # R(0) = I, R(p) R(q) = R(p + q), and re-rotating every pair of a chain by
+    # one offset re-rotates the composed state and transition by that offset.
+    dk, dv = 8, 8
+    x = rand_tokens(DELTA, 20, 2, dk, dv, seed=4200)
+    offsets = np.array([0, 4, 11, 20], np.int32)
+    g, U, S = oracle.build_pairs(DELTA, offsets, x["k"], x["v"], x["beta"], x["log_gate"])
+    U0, S0 = oracle.rerotate(DELTA, U, S, [0, 0, 0])
+    assert np.array_equal(U0, U) and np.array_equal(S0, S)
+    Ua, Sa = oracle.rerotate(DELTA, *oracle.rerotate(DELTA, U, S, [5, -2, 100]), [-12, 9, 3])
+    Ub, Sb = oracle.rerotate(DELTA, U, S, [-7, 7, 103])
+    assert rel(Sa, Sb) < 1e-12 and rel(Ua, Ub) < 1e-12
+    Ur, Sr = oracle.rerotate(DELTA, U, S, [31, 31, 31])
+    a = oracle.compose(DELTA, g, U, S, want_total=True)
+    b = oracle.compose(DELTA, g, Ur, Sr, want_total=True)
+    Ut_r, Sc_r = oracle.rerotate(DELTA, a["U_tot"][None], a["S_out"][None], [31])
+    assert rel(b["S_out"], Sc_r[0]) < 1e-12 and rel(b["U_tot"], Ut_r[0]) < 1e-12
+    assert np.array_equal(a["g_tot"], b["g_tot"])
+
+
+def test_rerotation_refuses_diagonal_family():
+    S = np.zeros((1, 1, 4, 4))
+    with pytest.raises(ValueError):
+        oracle.rerotate(DIAG, None, S, [3])

@@ -91,6 +91,18 @@ MUTANTS = {
     "seam_body_skipped_for_last_segment": (
         "      if (body_S) {\n        apply_T(",
         "      if (body_S && s + 1 < n_seg) {\n        apply_T("),
+    "rope_sin_sign": (
+        "R[(2 * i) * dk + 2 * i + 1] = -sn;",
+        "R[(2 * i) * dk + 2 * i + 1] = sn;"),
+    "rope_frequency_exponent": (
+        "pow(base, -2.0 * i / dk)",
+        "pow(base, -1.0 * i / dk)"),
+    "rope_transition_rotated_on_one_side": (
+        "acc += tmp[(size_t)i * dk + j] * R[c * dk + j];",
+        "acc += tmp[(size_t)i * dk + j] * (j == c);"),
+    "rope_offset_of_wrong_segment": (
+        "rope_matrix(R, dk, delta[u / n_chain], base);",
+        "rope_matrix(R, dk, delta[u % n_seg], base);"),
 }
 
 
