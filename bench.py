@@ -13,6 +13,8 @@ accumulation -- every (segment, head) pair (T_C, S(C|0)) built concurrently
   gdn_warm100k  30 layers x 16 heads, 196 cached segments, w = 8: seam step fused
                 with the composition of every cached body pair
   gdn_ragged32k the cold request with uneven segments (58 .. 2048 tokens)
+  gdn_warm100k_rerotate  rotary re-rotation of the warm request's cached pairs
+                to new offsets
 Prints one JSON line.  `value` is segment-tokens/s of the whole step; the
 `roofline` object is for the step's dominant kernel, timed with HIP events on
 the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
@@ -42,6 +44,7 @@ KERNEL_SOURCES = {
     "build_sd": ["segment_scan_amd/csrc/kernels/build_sd.hip", "segment_scan_amd/csrc/kernels/compose.hip"],
     "seam": ["segment_scan_amd/csrc/kernels/chain.hip", "segment_scan_amd/csrc/kernels/seam_prep.hip"],
     "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
+    "rerotate": ["segment_scan_amd/csrc/kernels/rerotate.hip"],
 }
 
 
@@ -72,6 +75,7 @@ KERNEL_SYMBOLS = {
     "build_sd": ["build_sd_kernel", "compose_elem_kernel"],
     "seam": ["seam_prep_kernel", "chain_kernel"],
     "compose": ["chain_kernel", "compose_elem_kernel"],
+    "rerotate": ["rerotate_kernel"],
 }
 CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
 CALIBRATION_BYTES = 1 << 30  # each reads and writes this many bytes
@@ -381,12 +385,67 @@ class WarmRequest(Workload):
                 "step": "hypic_seam_step over 480 chains (seam windows + body-pair composition)"}
 
 
+class WarmRerotate(Workload):
+    """Rotary re-rotation of the warm 100k-token request's cached pairs (30 GDN
+    layers x 16 heads x 196 segments, d = 128, fp32 U and S) to new offsets."""
+    name = "gdn_warm100k_rerotate"
+    kernel = "rerotate"
+
+    def __init__(self):
+        from segment_scan_amd import synth
+        self.layers, self.H, self.n_seg, self.d = synth.WARM_LAYERS, synth.WARM_HEADS, synth.WARM_SEGS, synth.WARM_D
+        self.chains = self.layers * self.H
+        self.tokens = self.n_seg * 512  # cached body tokens moved
+        self.composed = 0
+        units = self.n_seg * self.chains
+        # U and S of every unit read and written once, plus the offsets
+        self.alg_bytes = units * 2 * 2 * self.d * self.d * 4 + self.n_seg * 4
+        self.alg_flops = 0.0
+        self.exec_flops = 0.0
+
+    def setup(self):
+        import torch
+        from segment_scan_amd import api
+        self.api = api
+        n_seg, n, d = self.n_seg, self.chains, self.d
+        gen = torch.Generator(device="cuda").manual_seed(20260702)
+        self.U = torch.randn((n_seg, n, d, d), device="cuda", generator=gen) * (0.5 / np.sqrt(d))
+        self.S = torch.randn((n_seg, n, d, d), device="cuda", generator=gen)
+        self.pos = torch.randint(-(1 << 20), 1 << 20, (n_seg,), device="cuda", generator=gen, dtype=torch.int32)
+
+    def step(self, ev0, ev1):
+        from segment_scan_amd.synth import DELTA
+        ev0.record()
+        self.api.rerotate(DELTA, self.pos, self.S, self.U)
+        ev1.record()
+
+    def cpu_sample(self):
+        import oracle
+        from segment_scan_amd import synth
+        from segment_scan_amd.synth import DELTA
+        n_layers = 2
+        pos = np.random.default_rng(20260702).integers(-(1 << 20), 1 << 20, self.n_seg)
+        dt = 0.0
+        for layer in range(n_layers):
+            _, U, S = synth.warm_pairs_layer(layer)
+            t = time.perf_counter()
+            oracle.rerotate(DELTA, U, S, pos)
+            dt += time.perf_counter() - t
+        return dt, self.tokens * n_layers / self.layers, "layers 0-1 of 30 in full (196 segments x 16 heads), scaled"
+
+    def config(self):
+        return {"workload": self.name, "family": "gdn", "layers": self.layers, "heads": self.H, "d": self.d,
+                "segments": self.n_seg, "pairs": "fp32", "rope_base": 10000.0,
+                "step": "hypic_rerotate of 196 x 480 cached pairs in place (U <- R U R^T, S <- R S)"}
+
+
 WORKLOADS = {
     "gdn_cold32k": ColdRequest,
     "retnet": lambda: ScalarOrDiag("retnet", 1, 16, 1024, 8, 128),
     "gla": lambda: ScalarOrDiag("gla", 2, 64, 512, 16, 128),
     "gdn_warm100k": WarmRequest,
     "gdn_ragged32k": RaggedRequest,
+    "gdn_warm100k_rerotate": WarmRerotate,
 }
 
 

@@ -1,7 +1,8 @@
 /*
  * hypic.h -- C ABI of the MI355X (gfx950) library for the linear-attention hot
  * path of position-independent caching: per-segment build of the cached pair
- * (T_C, S(C|0)), ordered composition of cached pairs, and the seam-window step.
+ * (T_C, S(C|0)), ordered composition of cached pairs, the seam-window step, and
+ * the rotary re-rotation of cached pairs to a new position.
  *
  * Pages cited (by title):
  *   [youleyou] "小红书联合北大上交提出HYPIC，位置无关缓存降低首token延迟3.25倍" (youleyou.com)
@@ -14,8 +15,9 @@
  *    allocated and owned by the caller.  The library never allocates or frees
  *    device memory and keeps no pointer after the call returns.  `seg_offsets`
  *    of hypic_seg_build (and of hypic_seg_build_workspace_size) is the only
- *    HOST pointer.  Scratch memory, where a call needs any, is a caller
- *    workspace sized by a query function.
+ *    HOST pointer (the positions of hypic_rerotate are on the device).
+ *    Scratch memory, where a call needs any, is a caller workspace sized by a
+ *    query function.
  *  - Calls are asynchronous: HYPIC_OK means "validated and enqueued on
  *    `stream`" (a hipStream_t passed as void*; NULL = the null stream).  Results
  *    are ready once the stream reaches that point.
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 4
+#define HYPIC_ABI_VERSION 5
 
 typedef enum {
   HYPIC_OK = 0,
@@ -254,6 +256,39 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
  */
 hypic_status hypic_seam_step_workspace_size(hypic_family fam, int n_seg, int w, int n_chain, int d_k,
                                             int d_v, size_t* bytes);
+
+/*
+ * hypic_rerotate -- move cached pairs to a new position under rotary position
+ * encoding, in place.
+ *
+ * [youleyou, linear-layer paragraph]: for linear layers whose keys carry a
+ * rotary encoding, a cached segment reused at another position is aligned
+ * exactly by re-rotating its state.  The pages give no formula; the reading
+ * implemented: keys carry the RoFormer encoding -- the pairs (2i, 2i+1) of the
+ * d_k axis turned by the angle pos * theta_i, theta_i = rope_base^(-2i/d_k) --
+ * at positions counted from the segment's first token when the pair was
+ * built.  Reused with its first token at position p, every key becomes R(p) k,
+ * every per-token transition R(p) A_t R(p)^T and every write R(p) k v^T, so
+ *   DELTA:         U <- R(p) U R(p)^T   (g unchanged)
+ *   every family:  S <- R(p) S
+ * NAIVE and SCALAR transitions are multiples of I and do not change.  A DIAG
+ * transition does not stay diagonal under R(p) (unless its gates agree within
+ * each pair), so that family returns HYPIC_E_UNSUPPORTED.
+ *
+ *   positions   DEVICE [n_seg] int32: the offset p of segment s, any sign.
+ *               Rotations add (R(a) R(b) = R(a + b)), so a pair already moved
+ *               to p0 and rotated by p ends at p0 + p.
+ *   rope_base   the rotary base, positive and finite (e.g. 10000).
+ *   pairs       S [n_seg, n_chain, d_k, d_v] (required) and U [n_seg, n_chain,
+ *               d_k, d_k] (DELTA only, NULL otherwise) are updated in place; g
+ *               is neither read nor written (may be NULL).
+ * The angles and their cosines and sines are formed in fp64 on the device (so
+ * offsets far beyond 2^24 tokens keep full accuracy); the rotation is fp32.
+ * Errors as for hypic_compose; positions overlapping S or U is HYPIC_E_INVALID.
+ */
+hypic_status hypic_rerotate(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v,
+                            const int32_t* positions, double rope_base, const hypic_pairs* pairs,
+                            void* stream);
 
 /* Message of the last failed call on this thread ("" if none).  The string is
  * owned by the library and valid until the next call on this thread. */

@@ -63,8 +63,10 @@ def load_library(path: str = LIB_PATH):
         lib.hypic_seam_step.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P, P,
                                         ctypes.POINTER(Pairs), P, ctypes.c_size_t, P]
         lib.hypic_seam_step_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+        lib.hypic_rerotate.argtypes = [I, I, I, I, I, P, ctypes.c_double, ctypes.POINTER(Pairs), P]
         for f in (lib.hypic_seg_build, lib.hypic_seg_build_workspace_size, lib.hypic_compose,
-                  lib.hypic_compose_workspace_size, lib.hypic_seam_step, lib.hypic_seam_step_workspace_size):
+                  lib.hypic_compose_workspace_size, lib.hypic_seam_step, lib.hypic_seam_step_workspace_size,
+                  lib.hypic_rerotate):
             f.restype = I
         lib.hypic_last_error.restype = ctypes.c_char_p
         lib.hypic_last_error.argtypes = []
@@ -243,3 +245,17 @@ def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chai
     if window_out is not None:
         res.update(wg=window_out[0], wU=window_out[1], wS=window_out[2])
     return res
+
+
+def rerotate(fam: int, positions: torch.Tensor, S: torch.Tensor, U: Optional[torch.Tensor] = None,
+             rope_base: float = 10000.0, stream=None):
+    """Rotary re-rotation of pairs [n_seg, n_chain, ...] in place: S <- R(p) S and,
+    for the delta family, U <- R(p) U R(p)^T, with p = positions[s] (int32 on the
+    GPU).  Returns (U, S)."""
+    n_seg, n_chain, dk, dv = S.shape
+    if positions.dtype != torch.int32 or positions.shape != (n_seg,):
+        raise ValueError("positions must be int32 of shape (n_seg,)")
+    pr = Pairs(None, _ptr(U), _ptr(S))
+    _check(load_library().hypic_rerotate(fam, n_seg, n_chain, dk, dv, _ptr(positions), float(rope_base),
+                                         ctypes.byref(pr), _stream(stream)))
+    return U, S

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -473,6 +474,35 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
       if (e != hipSuccess) return hip_fail(e, "hypic_seam_step window pairs launch");
     }
   }
+  return ok();
+}
+
+hypic_status hypic_rerotate(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v, const int32_t* positions,
+                            double rope_base, const hypic_pairs* pairs, void* stream) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  const int d = d_k;
+  if (fam == HYPIC_DIAG)
+    return fail(HYPIC_E_UNSUPPORTED, "a diagonal transition does not stay diagonal under the rotation");
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+    return fail(HYPIC_E_INVALID, "rope_base must be positive and finite");
+  if (!positions) return fail(HYPIC_E_INVALID, "positions is NULL");
+  if (!pairs) return fail(HYPIC_E_INVALID, "pairs is NULL");
+  if (!pairs->S) return fail(HYPIC_E_INVALID, "pairs.S is NULL");
+  if (fam == HYPIC_DELTA && !pairs->U) return fail(HYPIC_E_INVALID, "pairs.U is required for the delta family");
+  if (fam != HYPIC_DELTA && pairs->U) return fail(HYPIC_E_INVALID, "pairs.U is only defined for the delta family");
+  if ((int64_t)n_seg * n_chain * (pairs->U ? 2 : 1) > INT32_MAX)
+    return fail(HYPIC_E_INVALID, "too many pairs for one launch (%d x %d)", n_seg, n_chain);
+  TRY(check_aligned(pairs->S, "pairs.S"));
+  if (pairs->U) TRY(check_aligned(pairs->U, "pairs.U"));
+  const size_t mbytes = (size_t)n_seg * n_chain * d * d * 4;
+  std::vector<Range> ins, outs;
+  ins.push_back({positions, (size_t)n_seg * 4, "positions"});
+  outs.push_back({pairs->S, mbytes, "pairs.S"});
+  if (pairs->U) outs.push_back({pairs->U, mbytes, "pairs.U"});
+  TRY(check_overlaps(ins, outs));
+  hipError_t e = hypic::launch_rerotate(d, pairs->S, pairs->U, positions, n_seg, n_chain, rope_base,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hypic_rerotate launch");
   return ok();
 }
 

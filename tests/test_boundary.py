@@ -43,14 +43,15 @@ def test_library_exports_every_declared_symbol(lib):
         text = f.read()
     declared = set(re.findall(r"\b(hypic_[a-z_]+)\s*\(", text))
     assert {"hypic_seg_build", "hypic_seg_build_workspace_size", "hypic_compose", "hypic_compose_workspace_size",
-            "hypic_seam_step", "hypic_seam_step_workspace_size", "hypic_last_error", "hypic_abi_version"} <= declared
+            "hypic_seam_step", "hypic_seam_step_workspace_size", "hypic_rerotate", "hypic_last_error",
+            "hypic_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\b(hypic_[a-z_]+)\b", out))
     assert declared <= exported, declared - exported
     for name in declared:
         getattr(lib, name)
-    assert lib.hypic_abi_version() == 4
+    assert lib.hypic_abi_version() == 5
 
 
 def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
@@ -279,3 +280,30 @@ def test_ragged_lengths_recipe():
     assert int(lens.sum()) == 32768 and lens.min() >= 32 and lens.max() <= 2048
     assert np.array_equal(lens, synth.ragged_lengths(64, 32768))  # seeded
     assert lens.max() / np.median(lens) > 4
+
+
+def rerotate_call(lib, fam=DELTA, n_seg=2, n_chain=2, dk=128, dv=128, pos=A["q"], base=10000.0, p=None):
+    p = pairs(fam, g=False) if p is None else p
+    return lib.hypic_rerotate(fam, n_seg, n_chain, dk, dv, pos, base, ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(fam=DIAG), UNSUPPORTED),
+    (dict(dk=96, dv=96), UNSUPPORTED),
+    (dict(n_seg=0), INVALID),
+    (dict(base=0.0), INVALID),
+    (dict(base=-2.0), INVALID),
+    (dict(base=float("inf")), INVALID),
+    (dict(base=float("nan")), INVALID),
+    (dict(pos=None), INVALID),
+    (dict(p=Pairs(None, A["U"], None)), INVALID),                  # S missing
+    (dict(p=Pairs(None, None, A["S"])), INVALID),                  # delta without U
+    (dict(fam=SCALAR, p=Pairs(None, A["U"], A["S"])), INVALID),    # U outside the delta family
+    (dict(p=Pairs(None, A["U"] + 4, A["S"])), INVALID),            # misaligned
+    (dict(pos=A["S"] + 64), INVALID),                              # positions inside S
+    (dict(p=Pairs(None, A["S"] + 2 * 128 * 128 * 4, A["S"])), INVALID),  # U overlaps S
+    (dict(n_seg=1 << 16, n_chain=1 << 15), INVALID),               # more workgroups than one launch holds
+])
+def test_rerotate_rejects(lib, case, status):
+    assert rerotate_call(lib, **case) == status
+    assert lib.hypic_last_error()
