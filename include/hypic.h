@@ -30,7 +30,9 @@
  *    output is o_t = S_t^T q_t, taken after the token's own update.  Layers and
  *    heads are folded into one "chain" index (chain = layer * heads + head).
  *  - Supported sizes: d_k = d_v = d with d in {64, 128}.  Other sizes return
- *    HYPIC_E_UNSUPPORTED.
+ *    HYPIC_E_UNSUPPORTED.  The KDA build is built for d = 64 and for d = 128
+ *    with bf16 tokens; the seam step and the re-rotation are not built for KDA
+ *    (HYPIC_E_UNSUPPORTED); its pairs compose like DELTA pairs.
  *  - Token tensors are token-major, [n_tok, n_chain, d] (d contiguous);
  *    per-token scalars are [n_tok, n_chain].
  *
@@ -42,15 +44,21 @@
  *   HYPIC_DIAG   : A_t = diag(exp(lg_t))   (GLA),    b_t = 1
  *   HYPIC_DELTA  : A_t = exp(lg_t)(I - beta_t k_t k_t^T) (DeltaNet: lg = 0; GDN),
  *                  b_t = beta_t
- *   and S_t = A_t S_{t-1} + b_t k_t v_t^T.
+ *   HYPIC_KDA    : A_t = (I - beta_t k_t k_t^T) diag(exp(lg_t)) (KDA: the delta rule
+ *                  with one gate per key channel), b_t = beta_t
+ *   and S_t = A_t S_{t-1} + b_t k_t v_t^T.  [youleyou, linear-layer paragraph] lists
+ *   KDA among the families whose transition is a dense matrix.
  *
  * Cached pair layout (fp32).  The segment transition T_C = A_L ... A_1 is kept
  * factored so that it cannot underflow (the scalar gate commutes with the
  * Householder-like factors):
  *   T_C = exp(g) U  (NAIVE: g = 0, U = I; SCALAR: U = I; DELTA: U = prod(I - beta k k^T))
  *   T_C = diag(exp(g))  (DIAG: g has d_k entries)
+ *   T_C = exp(g) U  (KDA: the channel gates do not commute with the erase factors,
+ *                    so U is the dense product and g only a scale that keeps U in
+ *                    range; only exp(g) U is defined, the split is the library's)
  *   g : [n_seg, n_chain]  (DIAG: [n_seg, n_chain, d_k])
- *   U : [n_seg, n_chain, d_k, d_k]  (DELTA only; NULL for the other families)
+ *   U : [n_seg, n_chain, d_k, d_k]  (DELTA and KDA; NULL for the other families)
  *   S : [n_seg, n_chain, d_k, d_v]  = S(C|0)
  */
 #ifndef HYPIC_H
@@ -63,7 +71,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 5
+#define HYPIC_ABI_VERSION 6
 
 typedef enum {
   HYPIC_OK = 0,
@@ -72,7 +80,7 @@ typedef enum {
   HYPIC_E_HIP = 3          /* the HIP runtime reported an error at launch */
 } hypic_status;
 
-typedef enum { HYPIC_NAIVE = 0, HYPIC_SCALAR = 1, HYPIC_DIAG = 2, HYPIC_DELTA = 3 } hypic_family;
+typedef enum { HYPIC_NAIVE = 0, HYPIC_SCALAR = 1, HYPIC_DIAG = 2, HYPIC_DELTA = 3, HYPIC_KDA = 4 } hypic_family;
 
 typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
 
@@ -83,10 +91,10 @@ typedef struct {
   const void* q;        /* [n_tok, n_chain, d_k]; seam step only (NULL for builds) */
   const void* k;        /* [n_tok, n_chain, d_k] */
   const void* v;        /* [n_tok, n_chain, d_v] */
-  const void* beta;     /* [n_tok, n_chain]; DELTA only, NULL otherwise */
+  const void* beta;     /* [n_tok, n_chain]; DELTA and KDA, NULL otherwise */
   const void* log_gate; /* natural log of the gate, <= 0:
                            SCALAR: [n_tok, n_chain], or fp32 [n_chain] if gate_per_chain (RetNet)
-                           DIAG  : [n_tok, n_chain, d_k]
+                           DIAG, KDA: [n_tok, n_chain, d_k]
                            DELTA : [n_tok, n_chain], or NULL (DeltaNet, gate = 1)
                            NAIVE : NULL */
   int gate_per_chain;   /* SCALAR only: 1 = one constant gate per chain */
@@ -171,20 +179,20 @@ hypic_status hypic_seg_build_workspace_size(hypic_family fam, int n_seg, const i
  * T_ABC = T_C T_B T_A and e_ABC = T_C (T_B e_A + e_B) + e_C.
  * For i = 0 .. n_seg-1 (index order): S <- T_i S + S_i, starting from S_init.
  *
- *   in             pairs [n_seg, n_chain, ...] (layout above); U only for DELTA.
+ *   in             pairs [n_seg, n_chain, ...] (layout above); U for DELTA and KDA.
  *   S_init         [n_chain, d_k, d_v] or NULL (zero start).
  *   S_out          [n_chain, d_k, d_v]; may be the same pointer as S_init
  *                  (in-place update), no other overlap.
  *   prefix_states  NULL or [n_seg, n_chain, d_k, d_v]: the running state
  *                  BEFORE segment i (prefix_states[0] = S_init or 0).
  *   g_total        NULL or [n_chain] (DIAG: [n_chain, d_k]): sum of g_i.
- *   U_total        NULL or [n_chain, d_k, d_k] (DELTA only): U_{n-1} ... U_0.
+ *   U_total        NULL or [n_chain, d_k, d_k] (DELTA, KDA): U_{n-1} ... U_0.
  *                  With S_init = NULL, (g_total, U_total, S_out) is the pair
  *                  of the concatenated segments.
  *   workspace      NULL, or device scratch of workspace_bytes bytes, at least
  *                  hypic_compose_workspace_size(); contents ignored on entry and
  *                  undefined on exit, in use until the stream passes the call.
- *                  For the DELTA family with few chains (at most 256 / (d / 32))
+ *                  For the DELTA and KDA families with few chains (at most 256 / (d / 32))
  *                  and at least 8 segments it lets the composition run as a
  *                  scan: blocks of consecutive segments are composed in
  *                  parallel (by associativity, [hwlabs, section 세그먼트 누적

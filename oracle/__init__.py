@@ -19,7 +19,8 @@ import subprocess
 
 import numpy as np
 
-NAIVE, SCALAR, DIAG, DELTA = 0, 1, 2, 3
+NAIVE, SCALAR, DIAG, DELTA, KDA = 0, 1, 2, 3, 4
+DENSE = (DELTA, KDA)  # families whose transition is a dense exp(g) U
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hypic_ref.c")
@@ -110,7 +111,7 @@ def build_pairs(fam, offsets, k, v, beta=None, log_gate=None, gate_per_chain=Fal
     dv = v.shape[2]
     gl = gate_len(fam, dk)
     g = np.zeros((n_seg, n_chain) + ((dk,) if gl > 1 else ()), np.float64)
-    U = np.zeros((n_seg, n_chain, dk, dk), np.float64) if (fam == DELTA and want_U) else None
+    U = np.zeros((n_seg, n_chain, dk, dk), np.float64) if (fam in DENSE and want_U) else None
     S = np.zeros((n_seg, n_chain, dk, dv), np.float64)
     rc = _load().hypic_ref_build(fam, n_seg, _p(off), n_chain, dk, dv, _p(k), _p(v), _p(beta),
                                  _p(log_gate), int(bool(gate_per_chain)), _p(g), _p(U), _p(S),
@@ -127,7 +128,7 @@ def compose(fam, g, U, S, S_init=None, want_prefix=False, want_total=False, n_th
     S_out = np.zeros((n_chain, dk, dv), np.float64)
     prefix = np.zeros((n_seg, n_chain, dk, dv), np.float64) if want_prefix else None
     g_tot = np.zeros((n_chain,) + ((dk,) if gl > 1 else ()), np.float64) if want_total else None
-    U_tot = np.zeros((n_chain, dk, dk), np.float64) if (want_total and fam == DELTA) else None
+    U_tot = np.zeros((n_chain, dk, dk), np.float64) if (want_total and fam in DENSE) else None
     rc = _load().hypic_ref_compose(fam, n_seg, n_chain, dk, dv, _p(g), _p(U), _p(S), _p(S_init),
                                    _p(S_out), _p(prefix), _p(g_tot), _p(U_tot),
                                    _threads(n_threads))
@@ -154,7 +155,7 @@ def seam(fam, n_seg, w, q, k, v, beta=None, log_gate=None, gate_per_chain=False,
     wg = wU = wS = None
     if want_window_pairs:
         wg = np.zeros((n_seg, n_chain) + ((dk,) if gl > 1 else ()), np.float64)
-        wU = np.zeros((n_seg, n_chain, dk, dk), np.float64) if fam == DELTA else None
+        wU = np.zeros((n_seg, n_chain, dk, dk), np.float64) if fam in DENSE else None
         wS = np.zeros((n_seg, n_chain, dk, dv), np.float64)
     rc = _load().hypic_ref_seam(fam, n_seg, w, n_chain, dk, dv, _p(q), _p(k), _p(v), _p(beta),
                                 _p(log_gate), int(bool(gate_per_chain)), _p(bg), _p(bU), _p(bS),

@@ -42,19 +42,24 @@
  *     scalar: S <- a_t S + k v^T                       (RetNet, Mamba2)
  *     diag  : S <- diag(alpha_t) S + k v^T             (GLA)
  *     delta : S <- a_t (I - beta_t k k^T) S + beta_t k v^T   (DeltaNet a=1, GDN)
+ *     kda   : S <- (I - beta_t k k^T) diag(alpha_t) S + beta_t k v^T   (KDA:
+ *             the delta rule with one gate per key channel)
  *   with a_t = exp(log_gate_t).  The transition operator is kept factored as
  *   T = exp(g) * U (scalar/delta: g scalar; diag: T = diag(exp(g)), U = I;
  *   delta: U = prod (I - beta k k^T)) so that it cannot underflow; the scalar
  *   gate commutes with the Householder-like factors, so the factorisation is
- *   exact.
+ *   exact.  For KDA the per-channel gates do not commute with the erase
+ *   factors, so T = exp(g) U is a dense product whose scalar g is only a scale:
+ *   each token moves its largest channel gate into g.  Only the product
+ *   exp(g) U is defined; a different split of it is an equal pair.
  *
  * Layouts (row-major, fp64):
  *   tokens  k, v, q : [n_tok, n_chain, d]   (token-major, d contiguous)
  *   beta            : [n_tok, n_chain]
  *   log_gate        : scalar/delta [n_tok, n_chain] (or [n_chain] when
- *                     gate_per_chain), diag [n_tok, n_chain, d_k], else NULL
+ *                     gate_per_chain), diag/kda [n_tok, n_chain, d_k], else NULL
  *   pairs g         : [n_seg, n_chain] (diag: [n_seg, n_chain, d_k])
- *   pairs U         : [n_seg, n_chain, d_k, d_k] (delta only)
+ *   pairs U         : [n_seg, n_chain, d_k, d_k] (delta and kda)
  *   pairs S, states : [.., n_chain, d_k, d_v]
  *
  * Rotary re-rotation (hypic_ref_rerotate, below): the pages name a state
@@ -77,7 +82,10 @@
 #include <omp.h>
 #endif
 
-enum { REF_NAIVE = 0, REF_SCALAR = 1, REF_DIAG = 2, REF_DELTA = 3 };
+enum { REF_NAIVE = 0, REF_SCALAR = 1, REF_DIAG = 2, REF_DELTA = 3, REF_KDA = 4 };
+
+/* Families whose transition is a dense matrix, kept as T = exp(g) U. */
+#define REF_DENSE(fam) ((fam) == REF_DELTA || (fam) == REF_KDA)
 
 #define REF_OK 0
 #define REF_EINVAL 1
@@ -89,7 +97,7 @@ typedef struct {
   const double* v;   /* d_v */
   double beta;       /* delta only */
   double lg;         /* scalar/delta log gate (0 when absent) */
-  const double* lgv; /* diag per-channel log gates (d_k) */
+  const double* lgv; /* diag and KDA per-channel log gates (d_k) */
 } tok_t;
 
 static tok_t get_tok(int fam, int t, int h, int n_chain, int dk, int dv,
@@ -98,17 +106,26 @@ static tok_t get_tok(int fam, int t, int h, int n_chain, int dk, int dv,
   tok_t x;
   x.k = k + ((size_t)t * n_chain + h) * dk;
   x.v = v + ((size_t)t * n_chain + h) * dv;
-  x.beta = (fam == REF_DELTA) ? beta[(size_t)t * n_chain + h] : 1.0;
+  x.beta = REF_DENSE(fam) ? beta[(size_t)t * n_chain + h] : 1.0;
   x.lg = 0.0;
   x.lgv = NULL;
   if (fam == REF_SCALAR) {
     x.lg = gate_per_chain ? lg[h] : lg[(size_t)t * n_chain + h];
   } else if (fam == REF_DELTA && lg != NULL) {
     x.lg = lg[(size_t)t * n_chain + h];
-  } else if (fam == REF_DIAG) {
+  } else if (fam == REF_DIAG || fam == REF_KDA) {
     x.lgv = lg + ((size_t)t * n_chain + h) * dk;
   }
   return x;
+}
+
+/* U <- (I - beta k k^T) U, one rank-1 step, column by column. */
+static void erase_rank1(int dk, const tok_t* x, double* U) {
+  for (int j = 0; j < dk; ++j) {
+    double dot = 0.0;
+    for (int i = 0; i < dk; ++i) dot += x->k[i] * U[(size_t)i * dk + j];
+    for (int i = 0; i < dk; ++i) U[(size_t)i * dk + j] -= x->beta * x->k[i] * dot;
+  }
 }
 
 /*
@@ -154,21 +171,43 @@ static void token_step(int fam, int dk, int dv, const tok_t* x, double* S,
           S[(size_t)i * dv + j] =
               a * (s - x->beta * x->k[i] * work[j]) + x->beta * x->k[i] * x->v[j];
         }
-      if (U) {
-        /* U <- (I - beta k k^T) U, one rank-1 step, column by column. */
-        for (j = 0; j < dk; ++j) {
-          double dot = 0.0;
-          for (i = 0; i < dk; ++i) dot += x->k[i] * U[(size_t)i * dk + j];
-          for (i = 0; i < dk; ++i) U[(size_t)i * dk + j] -= x->beta * x->k[i] * dot;
-        }
-      }
+      if (U) erase_rank1(dk, x, U);
       if (g) g[0] += x->lg;
+      break;
+    }
+    case REF_KDA: {
+      /* S <- (I - beta k k^T) diag(alpha) S + beta k v^T: decay each row
+       * (channel) of S first, then the delta-rule erase and write. */
+      for (i = 0; i < dk; ++i) {
+        const double a = exp(x->lgv[i]);
+        for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
+      }
+      for (j = 0; j < dv; ++j) work[j] = 0.0;
+      for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j) work[j] += x->k[i] * S[(size_t)i * dv + j];
+      for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j)
+          S[(size_t)i * dv + j] += x->beta * x->k[i] * (x->v[j] - work[j]);
+      if (U) {
+        /* T = exp(g) U and T <- (I - beta k k^T) diag(alpha) T.  The largest
+         * channel gate m of the token moves into g, so U is scaled by
+         * diag(exp(lg - m)) <= 1 and cannot overflow. */
+        double m = x->lgv[0];
+        for (i = 1; i < dk; ++i)
+          if (x->lgv[i] > m) m = x->lgv[i];
+        for (i = 0; i < dk; ++i) {
+          const double a = exp(x->lgv[i] - m);
+          for (j = 0; j < dk; ++j) U[(size_t)i * dk + j] *= a;
+        }
+        erase_rank1(dk, x, U);
+        if (g) g[0] += m;
+      }
       break;
     }
   }
 }
 
-static int fam_ok(int fam) { return fam >= REF_NAIVE && fam <= REF_DELTA; }
+static int fam_ok(int fam) { return fam >= REF_NAIVE && fam <= REF_KDA; }
 
 /* Per-chain gate accumulators live on the stack; d_k is bounded accordingly. */
 #define REF_MAX_D 4096
@@ -195,8 +234,8 @@ int hypic_ref_build(int fam, int n_seg, const int32_t* offsets, int n_chain, int
   if (!fam_ok(fam) || n_seg < 1 || n_chain < 1 || dk < 1 || dv < 1 || dk > REF_MAX_D || !offsets || !k ||
       !v || !g_out || !S_out)
     return REF_EINVAL;
-  if (fam == REF_DELTA && !beta) return REF_EINVAL;
-  if ((fam == REF_SCALAR || fam == REF_DIAG) && !lg) return REF_EINVAL;
+  if (REF_DENSE(fam) && !beta) return REF_EINVAL;
+  if ((fam == REF_SCALAR || fam == REF_DIAG || fam == REF_KDA) && !lg) return REF_EINVAL;
   if (offsets[0] != 0) return REF_EINVAL;
   for (int s = 0; s < n_seg; ++s)
     if (offsets[s + 1] <= offsets[s]) return REF_EINVAL;
@@ -207,8 +246,8 @@ int hypic_ref_build(int fam, int n_seg, const int32_t* offsets, int n_chain, int
   for (long u = 0; u < n_units; ++u) {
     const int s = (int)(u / n_chain), h = (int)(u % n_chain);
     double* work = (double*)malloc(sizeof(double) * (size_t)(dv > dk ? dv : dk));
-    double* U = (fam == REF_DELTA) ? (double*)malloc(sizeof(double) * (size_t)dk * dk) : NULL;
-    if (!work || (fam == REF_DELTA && !U)) {
+    double* U = REF_DENSE(fam) ? (double*)malloc(sizeof(double) * (size_t)dk * dk) : NULL;
+    if (!work || (REF_DENSE(fam) && !U)) {
       status = REF_ENOMEM;
       free(work);
       free(U);
@@ -251,7 +290,8 @@ static void apply_T(int fam, int dk, int dv, const double* g, const double* U, d
         for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
       }
       break;
-    case REF_DELTA: {
+    case REF_DELTA:
+    case REF_KDA: {
       double a = exp(g[0]);
       for (i = 0; i < dk; ++i)
         for (j = 0; j < dv; ++j) {
@@ -280,7 +320,7 @@ int hypic_ref_compose(int fam, int n_seg, int n_chain, int dk, int dv, const dou
   if (!fam_ok(fam) || n_seg < 1 || n_chain < 1 || dk < 1 || dv < 1 || dk > REF_MAX_D || !g ||
       !S || !S_out)
     return REF_EINVAL;
-  if (fam == REF_DELTA && !U) return REF_EINVAL;
+  if (REF_DENSE(fam) && !U) return REF_EINVAL;
   const int gl = gate_len(fam, dk);
   int status = REF_OK;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
@@ -288,8 +328,8 @@ int hypic_ref_compose(int fam, int n_seg, int n_chain, int dk, int dv, const dou
     const size_t sz = (size_t)dk * dv;
     double* cur = (double*)malloc(sizeof(double) * sz);
     double* tmp = (double*)malloc(sizeof(double) * sz);
-    double* ut = (U_tot && fam == REF_DELTA) ? (double*)malloc(sizeof(double) * (size_t)dk * dk * 2) : NULL;
-    if (!cur || !tmp || (U_tot && fam == REF_DELTA && !ut)) {
+    double* ut = (U_tot && REF_DENSE(fam)) ? (double*)malloc(sizeof(double) * (size_t)dk * dk * 2) : NULL;
+    if (!cur || !tmp || (U_tot && REF_DENSE(fam) && !ut)) {
       status = REF_ENOMEM;
       free(cur);
       free(tmp);
@@ -306,7 +346,7 @@ int hypic_ref_compose(int fam, int n_seg, int n_chain, int dk, int dv, const dou
     for (int s = 0; s < n_seg; ++s) {
       const size_t pu = (size_t)s * n_chain + h;
       if (prefix) memcpy(prefix + pu * sz, cur, sizeof(double) * sz);
-      apply_T(fam, dk, dv, g + pu * gl, fam == REF_DELTA ? U + pu * dk * dk : NULL, cur, tmp);
+      apply_T(fam, dk, dv, g + pu * gl, REF_DENSE(fam) ? U + pu * dk * dk : NULL, cur, tmp);
       const double* Si = S + pu * sz;
       for (size_t e = 0; e < sz; ++e) cur[e] += Si[e];
       for (int i = 0; i < gl; ++i) gacc[i] += g[pu * gl + i];
@@ -354,9 +394,9 @@ int hypic_ref_seam(int fam, int n_seg, int w, int n_chain, int dk, int dv, const
       !q || !k ||
       !v || !S_run || !o_out)
     return REF_EINVAL;
-  if (fam == REF_DELTA && !beta) return REF_EINVAL;
-  if ((fam == REF_SCALAR || fam == REF_DIAG) && !lg) return REF_EINVAL;
-  if (body_S && (!body_g || (fam == REF_DELTA && !body_U))) return REF_EINVAL;
+  if (REF_DENSE(fam) && !beta) return REF_EINVAL;
+  if ((fam == REF_SCALAR || fam == REF_DIAG || fam == REF_KDA) && !lg) return REF_EINVAL;
+  if (body_S && (!body_g || (REF_DENSE(fam) && !body_U))) return REF_EINVAL;
   const int gl = gate_len(fam, dk);
   int status = REF_OK;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
@@ -384,7 +424,7 @@ int hypic_ref_seam(int fam, int n_seg, int w, int n_chain, int dk, int dv, const
         const int t = s * w + j;
         tok_t x = get_tok(fam, t, h, n_chain, dk, dv, k, v, beta, lg, gate_per_chain);
         token_step(fam, dk, dv, &x, S, NULL, NULL, work);
-        if (wS || wU || wg) token_step(fam, dk, dv, &x, pS, pg, fam == REF_DELTA ? pU : NULL, work);
+        if (wS || wU || wg) token_step(fam, dk, dv, &x, pS, pg, REF_DENSE(fam) ? pU : NULL, work);
         const double* qt = q + ((size_t)t * n_chain + h) * dk;
         double* ot = o_out + ((size_t)t * n_chain + h) * dv;
         for (int c = 0; c < dv; ++c) {
@@ -395,11 +435,11 @@ int hypic_ref_seam(int fam, int n_seg, int w, int n_chain, int dk, int dv, const
       }
       const size_t pu = (size_t)s * n_chain + h;
       if (wS) memcpy(wS + pu * sz, pS, sizeof(double) * sz);
-      if (wU && fam == REF_DELTA) memcpy(wU + pu * dk * dk, pU, sizeof(double) * (size_t)dk * dk);
+      if (wU && REF_DENSE(fam)) memcpy(wU + pu * dk * dk, pU, sizeof(double) * (size_t)dk * dk);
       if (wg)
         for (int i = 0; i < gl; ++i) wg[pu * gl + i] = pg[i];
       if (body_S) {
-        apply_T(fam, dk, dv, body_g + pu * gl, fam == REF_DELTA ? body_U + pu * dk * dk : NULL,
+        apply_T(fam, dk, dv, body_g + pu * gl, REF_DENSE(fam) ? body_U + pu * dk * dk : NULL,
                 S, tmp);
         const double* Sb = body_S + pu * sz;
         for (size_t e = 0; e < sz; ++e) S[e] += Sb[e];
@@ -424,8 +464,8 @@ int hypic_ref_sequential(int fam, int n_tok, int n_chain, int dk, int dv, const 
                          double* S_out, double* o_out, int n_threads) {
   if (!fam_ok(fam) || n_tok < 0 || n_chain < 1 || dk < 1 || dv < 1 || !k || !v || !S_out)
     return REF_EINVAL;
-  if (fam == REF_DELTA && !beta) return REF_EINVAL;
-  if ((fam == REF_SCALAR || fam == REF_DIAG) && !lg) return REF_EINVAL;
+  if (REF_DENSE(fam) && !beta) return REF_EINVAL;
+  if ((fam == REF_SCALAR || fam == REF_DIAG || fam == REF_KDA) && !lg) return REF_EINVAL;
   if (o_out && !q) return REF_EINVAL;
   int status = REF_OK;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
@@ -491,7 +531,7 @@ static void rope_matrix(double* R, int dk, long p, double base) {
 
 int hypic_ref_rerotate(int fam, int n_seg, int n_chain, int dk, int dv, const int32_t* delta, double base,
                        double* U, double* S, int n_threads) {
-  if (!fam_ok(fam) || fam == REF_DIAG || dk < 2 || dk % 2 || !S || !delta || !(base > 0.0)) return 1;
+  if (!fam_ok(fam) || fam == REF_DIAG || fam == REF_KDA || dk < 2 || dk % 2 || !S || !delta || !(base > 0.0)) return 1;
   if (fam == REF_DELTA && !U) return 1;
   int status = 0;
 #pragma omp parallel num_threads(n_threads > 0 ? n_threads : 1)

@@ -15,7 +15,9 @@ from typing import Optional, Sequence
 
 import torch
 
-from .synth import NAIVE, SCALAR, DIAG, DELTA
+from .synth import NAIVE, SCALAR, DIAG, DELTA, KDA
+
+DENSE = (DELTA, KDA)  # families whose pairs carry a dense U
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhypic.so")
@@ -150,7 +152,7 @@ def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor
     dev = k.device
     if out is None:
         g = torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32)
-        U = torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam == DELTA else None
+        U = torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam in DENSE else None
         S = torch.empty((n_seg, n_chain, d, v.shape[2]), device=dev, dtype=torch.float32)
     else:
         g, U, S = out
@@ -190,10 +192,10 @@ def compose(fam: int, g, U, S, S_init=None, S_out=None, prefix_states=None, g_to
         prefix_states = torch.empty((n_seg, n_chain, dk, dv), device=dev, dtype=torch.float32)
     if want_total and g_total is None:
         g_total = torch.empty(_gate_shape(fam, (n_chain,), dk), device=dev, dtype=torch.float32)
-    if want_total and fam == DELTA and U_total is None:
+    if want_total and fam in DENSE and U_total is None:
         U_total = torch.empty((n_chain, dk, dk), device=dev, dtype=torch.float32)
     if isinstance(workspace, str):
-        need = compose_workspace_size(fam, n_seg, n_chain, dk, prefix_states is not None) if fam == DELTA else 0
+        need = compose_workspace_size(fam, n_seg, n_chain, dk, prefix_states is not None) if fam in DENSE else 0
         workspace = torch.empty(need, device=dev, dtype=torch.uint8) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     pr = Pairs(_ptr(g), _ptr(U), _ptr(S))

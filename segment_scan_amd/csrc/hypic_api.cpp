@@ -74,7 +74,7 @@ hypic_status check_aligned(const void* p, const char* name) {
   } while (0)
 
 hypic_status check_common(int fam, int n_seg, int n_chain, int d_k, int d_v) {
-  if (fam < HYPIC_NAIVE || fam > HYPIC_DELTA) return fail(HYPIC_E_INVALID, "unknown family %d", fam);
+  if (fam < HYPIC_NAIVE || fam > HYPIC_KDA) return fail(HYPIC_E_INVALID, "unknown family %d", fam);
   if (n_seg < 1) return fail(HYPIC_E_INVALID, "n_seg must be >= 1 (got %d)", n_seg);
   if (n_chain < 1) return fail(HYPIC_E_INVALID, "n_chain must be >= 1 (got %d)", n_chain);
   if (d_k < 1 || d_v < 1) return fail(HYPIC_E_INVALID, "d_k and d_v must be >= 1");
@@ -84,6 +84,9 @@ hypic_status check_common(int fam, int n_seg, int n_chain, int d_k, int d_v) {
 }
 
 size_t gate_len(int fam, int d) { return fam == HYPIC_DIAG ? (size_t)d : 1; }
+
+// Families whose transition is a dense exp(g) U (pairs carry U).
+bool dense(int fam) { return fam == HYPIC_DELTA || fam == HYPIC_KDA; }
 
 // Validates the token inputs of a build or seam call and returns their byte ranges.
 hypic_status check_tokens(int fam, const hypic_tokens* t, size_t n_tok, int n_chain, int d, bool need_q,
@@ -95,12 +98,12 @@ hypic_status check_tokens(int fam, const hypic_tokens* t, size_t n_tok, int n_ch
   if (!t->k) return fail(HYPIC_E_INVALID, "k is NULL");
   if (!t->v) return fail(HYPIC_E_INVALID, "v is NULL");
   if (need_q && !t->q) return fail(HYPIC_E_INVALID, "q is NULL");
-  if (fam == HYPIC_DELTA) {
-    if (!t->beta) return fail(HYPIC_E_INVALID, "beta is required for the delta family");
+  if (dense(fam)) {
+    if (!t->beta) return fail(HYPIC_E_INVALID, "beta is required for the delta and KDA families");
   } else if (t->beta) {
-    return fail(HYPIC_E_INVALID, "beta is only defined for the delta family");
+    return fail(HYPIC_E_INVALID, "beta is only defined for the delta and KDA families");
   }
-  if (fam == HYPIC_SCALAR || fam == HYPIC_DIAG) {
+  if (fam == HYPIC_SCALAR || fam == HYPIC_DIAG || fam == HYPIC_KDA) {
     if (!t->log_gate) return fail(HYPIC_E_INVALID, "log_gate is required for this family");
   }
   if (fam == HYPIC_NAIVE && t->log_gate) return fail(HYPIC_E_INVALID, "log_gate must be NULL for the naive family");
@@ -119,7 +122,7 @@ hypic_status check_tokens(int fam, const hypic_tokens* t, size_t n_tok, int n_ch
     size_t bytes;
     if (fam == HYPIC_SCALAR && t->gate_per_chain)
       bytes = (size_t)n_chain * 4;
-    else if (fam == HYPIC_DIAG)
+    else if (fam == HYPIC_DIAG || fam == HYPIC_KDA)
       bytes = rows * d * es;
     else
       bytes = rows * es;
@@ -133,8 +136,8 @@ hypic_status check_cpairs(int fam, const hypic_cpairs* p, int n_seg, int n_chain
   const size_t units = (size_t)n_seg * n_chain;
   if (!p->S) return fail(HYPIC_E_INVALID, "%s.S is NULL", what);
   if (fam != HYPIC_NAIVE && !p->g) return fail(HYPIC_E_INVALID, "%s.g is NULL", what);
-  if (fam == HYPIC_DELTA && !p->U) return fail(HYPIC_E_INVALID, "%s.U is required for the delta family", what);
-  if (fam != HYPIC_DELTA && p->U) return fail(HYPIC_E_INVALID, "%s.U is only defined for the delta family", what);
+  if (dense(fam) && !p->U) return fail(HYPIC_E_INVALID, "%s.U is required for the delta and KDA families", what);
+  if (!dense(fam) && p->U) return fail(HYPIC_E_INVALID, "%s.U is only defined for the delta and KDA families", what);
   TRY(check_aligned(p->S, "pairs.S"));
   if (p->g) TRY(check_aligned(p->g, "pairs.g"));
   if (p->U) TRY(check_aligned(p->U, "pairs.U"));
@@ -186,7 +189,7 @@ size_t delta_workspace(int n_seg, const int32_t* seg_offsets, int n_chain, int d
 // law that joins segments) -- so few long segments still occupy the GPU.
 // Returns P (1: no split).
 int piece_count(int fam, int n_seg, const int32_t* seg_offsets, int n_chain) {
-  if (fam == HYPIC_DELTA) return 1;
+  if (dense(fam)) return 1;
   const long units = (long)n_seg * n_chain;
   int p = (int)std::min<long>(4, 512 / std::max<long>(units, 1));
   for (int s = 0; s < n_seg && p > 1; ++s) p = std::min(p, (seg_offsets[s + 1] - seg_offsets[s] + 63) / 64);
@@ -236,8 +239,8 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
   if (!out) return fail(HYPIC_E_INVALID, "out is NULL");
   if (!out->S) return fail(HYPIC_E_INVALID, "out.S is NULL");
   if (!out->g) return fail(HYPIC_E_INVALID, "out.g is NULL");
-  if (fam == HYPIC_DELTA && !out->U) return fail(HYPIC_E_INVALID, "out.U is required for the delta family");
-  if (fam != HYPIC_DELTA && out->U) return fail(HYPIC_E_INVALID, "out.U is only defined for the delta family");
+  if (dense(fam) && !out->U) return fail(HYPIC_E_INVALID, "out.U is required for the delta and KDA families");
+  if (!dense(fam) && out->U) return fail(HYPIC_E_INVALID, "out.U is only defined for the delta and KDA families");
   TRY(check_aligned(out->S, "out.S"));
   TRY(check_aligned(out->g, "out.g"));
   if (out->U) TRY(check_aligned(out->U, "out.U"));
@@ -246,6 +249,8 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
   outs.push_back({out->g, units * gate_len(fam, d) * 4, "out.g"});
   if (out->U) outs.push_back({out->U, units * d * d * 4, "out.U"});
   const bool f32 = in->dtype == HYPIC_F32;
+  if (fam == HYPIC_KDA && !hypic::kda_build_supported(d, f32))
+    return fail(HYPIC_E_UNSUPPORTED, "the KDA build is built for d = 64 and for d = 128 with bf16 tokens");
   const size_t ws_need = build_workspace(fam, n_seg, seg_offsets, n_chain, d, f32);
   if (ws_need > 0) {
     if (!workspace) return fail(HYPIC_E_INVALID, "workspace is NULL (%zu bytes required)", ws_need);
@@ -305,6 +310,7 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
     fill_seg_table(&a.seg, seg_offsets, s0, ns);
     const int blocks = ns * n_chain;
     hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, workspace, (hipStream_t)stream)
+                   : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, a, blocks, (hipStream_t)stream)
                                         : hypic::launch_build_sd(fam, d, f32, a, blocks, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
   }
@@ -315,7 +321,7 @@ hypic_status hypic_compose_workspace_size(hypic_family fam, int n_seg, int n_cha
                                           int want_prefix, size_t* bytes) {
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
-  *bytes = fam == HYPIC_DELTA ? hypic::compose_workspace_bytes(d_k, n_seg, n_chain, want_prefix != 0) : 0;
+  *bytes = dense(fam) ? hypic::compose_workspace_bytes(d_k, n_seg, n_chain, want_prefix != 0) : 0;
   return ok();
 }
 
@@ -328,7 +334,8 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   std::vector<Range> ins, outs;
   TRY(check_cpairs(fam, in, n_seg, n_chain, d, "in", &ins));
   if (!S_out) return fail(HYPIC_E_INVALID, "S_out is NULL");
-  if (U_total && fam != HYPIC_DELTA) return fail(HYPIC_E_INVALID, "U_total is only defined for the delta family");
+  if (U_total && !dense(fam))
+    return fail(HYPIC_E_INVALID, "U_total is only defined for the delta and KDA families");
   TRY(check_aligned(S_out, "S_out"));
   if (S_init) TRY(check_aligned(S_init, "S_init"));
   if (prefix_states) TRY(check_aligned(prefix_states, "prefix_states"));
@@ -343,7 +350,7 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   if (U_total) outs.push_back({U_total, (size_t)n_chain * d * d * 4, "U_total"});
   // (an in-place S_init is covered as S_out: it may overlap nothing else)
   const size_t ws_need =
-      fam == HYPIC_DELTA ? hypic::compose_workspace_bytes(d, n_seg, n_chain, prefix_states != nullptr) : 0;
+      dense(fam) ? hypic::compose_workspace_bytes(d, n_seg, n_chain, prefix_states != nullptr) : 0;
   if (workspace && ws_need > 0) {
     if (workspace_bytes < ws_need)
       return fail(HYPIC_E_INVALID, "workspace too small: %zu bytes given, %zu required", workspace_bytes, ws_need);
@@ -364,7 +371,7 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
   a.n_seg = n_seg;
   a.n_chain = n_chain;
   a.n_out = n_chain;
-  hipError_t e = (fam == HYPIC_DELTA)
+  hipError_t e = dense(fam)
                      ? hypic::launch_compose_chain(d, a, ws_need > 0 ? workspace : nullptr, workspace_bytes,
                                                    (hipStream_t)stream)
                                       : hypic::launch_compose_elem(fam, d, a, (hipStream_t)stream);
@@ -377,6 +384,7 @@ hypic_status hypic_seam_step_workspace_size(hypic_family fam, int n_seg, int w, 
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   if (w < 1) return fail(HYPIC_E_INVALID, "w must be >= 1 (got %d)", w);
   if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
+  if (fam == HYPIC_KDA) return fail(HYPIC_E_UNSUPPORTED, "the seam step is not built for the KDA family");
   *bytes = fam == HYPIC_DELTA ? hypic::seam_workspace_bytes(n_seg, w, n_chain) : 0;
   return ok();
 }
@@ -388,6 +396,7 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   const int d = d_k;
   if (w < 1) return fail(HYPIC_E_INVALID, "w must be >= 1 (got %d)", w);
+  if (fam == HYPIC_KDA) return fail(HYPIC_E_UNSUPPORTED, "the seam step is not built for the KDA family");
   std::vector<Range> ins, outs;
   const size_t n_tok = (size_t)n_seg * w;
   TRY(check_tokens(fam, seam, n_tok, n_chain, d, true, &ins));
@@ -481,8 +490,8 @@ hypic_status hypic_rerotate(hypic_family fam, int n_seg, int n_chain, int d_k, i
                             double rope_base, const hypic_pairs* pairs, void* stream) {
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   const int d = d_k;
-  if (fam == HYPIC_DIAG)
-    return fail(HYPIC_E_UNSUPPORTED, "a diagonal transition does not stay diagonal under the rotation");
+  if (fam == HYPIC_DIAG || fam == HYPIC_KDA)
+    return fail(HYPIC_E_UNSUPPORTED, "a per-channel gate does not commute with the rotation");
   if (!(rope_base > 0.0) || !std::isfinite(rope_base))
     return fail(HYPIC_E_INVALID, "rope_base must be positive and finite");
   if (!positions) return fail(HYPIC_E_INVALID, "positions is NULL");

@@ -43,40 +43,6 @@ namespace {
 
 constexpr int C = 64;  // tokens per chunk
 
-// Two 8-byte LDS reads (k = off .. off+3 and off+8 .. off+11) joined into one
-// A fragment: the k order that matches an accumulator tile used as B (see
-// common.h).  `p` already holds the lane's row and 4*(lane >> 5) offset, so
-// every address is a base register plus an immediate.
-template <int NT>
-__device__ __forceinline__ Frag<NT> lds_a_perm(const bf16_t* p, int term_stride, int off) {
-  Frag<NT> f;
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + i * term_stride + off);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + i * term_stride + off + 8);
-    f.t[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-  return f;
-}
-
-// Standard-order fragment: 8 consecutive k starting at `off` (two 8-byte reads).
-template <int NT>
-__device__ __forceinline__ Frag<NT> lds_frag(const bf16_t* p, int term_stride, int off) {
-  Frag<NT> f;
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + i * term_stride + off);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + i * term_stride + off + 4);
-    f.t[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-  return f;
-}
-
-__device__ __forceinline__ void st8(bf16_t* p, const bf16x8& v) {
-  *reinterpret_cast<bf16x4*>(p) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
-  *reinterpret_cast<bf16x4*>(p + 4) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
-}
-
 template <int D, bool IN_F32>
 struct DeltaCfg {
   static constexpr int NTI = IN_F32 ? 3 : 1;  // bf16 terms of input operands (K)

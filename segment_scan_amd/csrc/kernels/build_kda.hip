@@ -1,0 +1,516 @@
+// build_kda.hip -- segment build for the KDA family (the delta rule with one
+// gate per key channel): emits T_C = exp(g) U and S(C|0) of every
+// (segment, chain).
+//
+// [youleyou, linear-layer paragraph] T_C is the product of the segment's
+// per-token transitions, here A_t = (I - beta_t k_t k_t^T) diag(alpha_t), and
+// S(C|0) the final state from a zero start.  The channel gates do not commute
+// with the erase factors, so T_C is a dense product; g is a scale that keeps U
+// in range: the sum over tokens of each token's largest channel gate, which
+// bounds the decay of every product of the factors.
+//
+// Chunk form (64 tokens; within the chunk the per-channel inclusive gate
+// prefixes G [C][d], the summed largest gates mu_t, and H = G - mu, which is
+// <= 0 and non-increasing along t in every channel; G_C, H_C, mu_C the last
+// rows): in the frame diag(exp(-mu_t)) the chunk's product of rank-1 factors
+// is a generalised WY product whose two sides carry the keys decayed in
+// opposite directions:
+//   M[i,j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc)   (i > j),  X = (I + M)^-1 diag(b)
+//   Kb = K o exp(H),  Kd = (K o exp(H_C - H))^T
+//   U <- diag(exp(G_C - mu_C)) U - Kd X (Kb U),   g += mu_C
+//   S <- diag(exp(G_C)) S + Kd X (diag(exp(mu_C - mu)) V - exp(mu_C) Kb S)
+// Every factor is at most 1 whatever the gates, and the result equals running
+// the tokens one by one (the tests check this algebra against the token-by-
+// token oracle).  The Gram terms exp(H_ic - H_jc) are formed without overflow:
+// blocks of earlier tokens are scaled against a reference token between the
+// two blocks (both factors <= 1), and the four 16-token diagonal blocks are
+// summed term by term.
+//
+// Mapping (one workgroup of 4 waves per unit, as the delta build): the state
+// [U | S] (d x 2d fp32) lives in MFMA accumulators for the whole segment,
+// waves 0-1 holding U and waves 2-3 S, d/2 columns each.  Per chunk the keys,
+// gate prefixes, the decayed key copies (split into bf16 terms) and X sit in
+// LDS; the off-diagonal Gram blocks run on bf16 MFMA with operands decayed on
+// the fly, the 64 x 64 inverse in fp32 on the VALU.
+#include <type_traits>
+
+#include "common.h"
+#include "../launch.h"
+
+namespace hypic {
+
+namespace {
+
+constexpr int C = 64;  // tokens per chunk
+
+template <int D, bool IN_F32>
+struct KdaCfg {
+  static constexpr int NTK = IN_F32 ? 3 : 2;  // bf16 terms of the decayed keys and Gram operands
+  static constexpr int NTD = IN_F32 ? 3 : 2;  // bf16 terms of X and of accumulators used as B
+  static constexpr int NRT = D / 32;          // row tiles of the state
+  static constexpr int CT = D / 64;           // 32-column tiles per wave (d/2 columns)
+  static constexpr int CPW = D / 2;
+  static constexpr int FP = D + 4;            // pitch of the staged keys and gate prefixes [t][d]
+  static constexpr int KP = D + 4;            // bf16 pitch of Kb [t][d]
+  static constexpr int TP = C + 4;            // bf16 pitch of Kd [d][t] and of X [t][t']
+  static constexpr int NP = 65;               // fp32 pitch of the Gram / inverse array
+  using KT = typename std::conditional<IN_F32, float, bf16_t>::type;  // staged keys (exact)
+  static constexpr int KF_BYTES = (C * FP * (int)sizeof(KT) + 15) / 16 * 16;
+  static constexpr int G_BYTES = C * FP * 4;
+  static constexpr int KB_BYTES = NTK * C * KP * 2;
+  static constexpr int KD_BYTES = NTK * D * TP * 2;
+  static constexpr int A_BYTES_BF = NTD * C * TP * 2;
+  static constexpr int N_BYTES = C * NP * 4;  // the fp32 Gram / inverse (aliases X)
+  static constexpr int A_BYTES = ((A_BYTES_BF > N_BYTES ? A_BYTES_BF : N_BYTES) + 15) / 16 * 16;
+  static constexpr int T_BYTES = 3 * 16 * 17 * 4;  // block-row scratch of the inverse
+  static constexpr int OFF_KF = 0;
+  static constexpr int OFF_G = OFF_KF + KF_BYTES;
+  static constexpr int OFF_KB = OFF_G + G_BYTES;
+  static constexpr int OFF_KD = OFF_KB + KB_BYTES;
+  static constexpr int OFF_A = OFF_KD + KD_BYTES;
+  static constexpr int OFF_T = OFF_A + A_BYTES;
+  static constexpr int OFF_SMALL = OFF_T + T_BYTES;
+  // beta, token max gate, mu, exp(mu_C - mu), G_C, exp(G_C), exp(G_C - mu_C), misc
+  static constexpr int SMALL_BYTES = (4 * C + 3 * D + 4) * 4;
+  static constexpr int LDS = OFF_SMALL + SMALL_BYTES;
+  static_assert(LDS <= 160 * 1024, "one workgroup's LDS");
+};
+
+// Key channels c0 .. c0+7 of token t decayed against token `ref` in the
+// shifted prefixes H = G - mu: k * exp(H_t - H_ref) (toward = true) or
+// k * exp(H_ref - H_t), split into NT terms.
+template <int NT, typename KT>
+__device__ __forceinline__ Frag<NT> decayed_frag(const KT* sKf, const float* sG, const float* sMu, int FP, int t,
+                                                 int ref, int c0, bool toward) {
+  const float dmu = sMu[t] - sMu[ref];
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float d = (sG[t * FP + c0 + j] - sG[ref * FP + c0 + j]) - dmu;
+    x[j] = (float)sKf[t * FP + c0 + j] * __expf(toward ? d : -d);
+  }
+  return split8<NT>(x);
+}
+
+template <int NT>
+__device__ __forceinline__ void split4_store(bf16_t* p, int term_stride, const float (&x)[4]) {
+  float r[4] = {x[0], x[1], x[2], x[3]};
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    bf16x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16_t hb = (bf16_t)r[j];
+      v[j] = hb;
+      if (i + 1 < NT) r[j] -= (float)hb;
+    }
+    *reinterpret_cast<bf16x4*>(p + i * term_stride) = v;
+  }
+}
+
+template <int D, bool IN_F32>
+__global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
+  using Cfg = KdaCfg<D, IN_F32>;
+  using KT = typename Cfg::KT;
+  constexpr int NTK = Cfg::NTK, NTD = Cfg::NTD, NRT = Cfg::NRT, CT = Cfg::CT, CPW = Cfg::CPW;
+  constexpr int FP = Cfg::FP, KP = Cfg::KP, TP = Cfg::TP, NP = Cfg::NP;
+  constexpr int KBS = C * KP;  // term stride (elements) of Kb
+  constexpr int KDS = D * TP;  // term stride of Kd
+  constexpr int ATS = C * TP;  // term stride of X
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  KT* sKf = reinterpret_cast<KT*>(smem + Cfg::OFF_KF);
+  float* sG = reinterpret_cast<float*>(smem + Cfg::OFF_G);
+  bf16_t* sKb = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KB);
+  bf16_t* sKd = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KD);
+  bf16_t* sA = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_A);
+  float* sN = reinterpret_cast<float*>(smem + Cfg::OFF_A);  // aliases sA
+  float* sT = reinterpret_cast<float*>(smem + Cfg::OFF_T);
+  float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_SMALL);
+  float* sMax = sBeta + C;  // largest channel gate of each token
+  float* sMu = sMax + C;    // mu_t: inclusive prefix of sMax
+  float* sVf = sMu + C;     // exp(mu_C - mu_t): value factors
+  float* sGC = sVf + C;     // G_C per channel
+  float* sRS = sGC + D;     // exp(G_C): row factors of S
+  float* sRU = sRS + D;     // exp(G_C - mu_C): row factors of U
+  float* sMisc = sRU + D;   // [0] = mu_C, [1] = exp(mu_C)
+
+  const int lane0 = lane_id();
+  const int wave = wave_id();
+  const int n_chain = a.n_chain;
+  const int s_local = a.seg.order[blockIdx.x / n_chain];  // longest segments first
+  const int chain = blockIdx.x % n_chain;
+  const int t_begin = a.seg.off[s_local];
+  const int t_end = a.seg.off[s_local + 1];
+  const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + chain;
+  const bool s_wave = wave >= 2;
+  const int col0 = (wave & 1) * CPW;
+
+  // ---- running state: U = I (waves 0-1), S = 0 (waves 2-3) -------------------
+  f32x16 Z[NRT][CT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * rt + acc_row(r, lane0);
+        const int col = col0 + 32 * ct + (lane0 & 31);
+        Z[rt][ct][r] = (!s_wave && row == col) ? 1.f : 0.f;
+      }
+  double g_acc = 0.0;
+
+  for (int c0 = t_begin; c0 < t_end; c0 += C) {
+    const int nv = min(C, t_end - c0);
+    const int tid = opaque(threadIdx.x);
+    const int lane = tid & 63;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- stage keys and per-channel log gates (zero past the segment end) ------
+    // and each token's largest gate (its D/8 channel groups are consecutive lanes)
+    static_assert((C * (D / 8)) % 256 == 0, "every lane runs every staging step");
+    for (int it = tid; it < C * (D / 8); it += 256) {
+      const int t = it / (D / 8), db = it % (D / 8);
+      float x[8], lg[8];
+      if (t < nv) {
+        const size_t idx = ((size_t)(c0 + t) * n_chain + chain) * D + db * 8;
+        load8<IN_F32>(a.k, idx, x);
+        load8<IN_F32>(a.lg, idx, lg);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = lg[j] = 0.f;
+      }
+      float mx = lg[0];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sKf[t * FP + db * 8 + j] = (KT)x[j];
+        sG[t * FP + db * 8 + j] = lg[j];
+        mx = fmaxf(mx, lg[j]);
+      }
+#pragma unroll
+      for (int o = 1; o < D / 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      if (db == 0) sMax[t] = mx;
+    }
+    if (tid < C) sBeta[tid] = (tid < nv) ? load1<IN_F32>(a.beta, (size_t)(c0 + tid) * n_chain + chain) : 0.f;
+    __syncthreads();
+
+    // ---- per-channel inclusive prefix G (one thread per channel) --------------
+    if (tid < D) {
+      float lgc[C];
+#pragma unroll
+      for (int t = 0; t < C; ++t) lgc[t] = sG[t * FP + tid];
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < C; ++t) {
+        acc += lgc[t];
+        sG[t * FP + tid] = acc;
+      }
+      sGC[tid] = acc;
+    }
+    if (wave == 3) {  // mu_t (free wave: the scan uses at most waves 0-1)
+      const float mu = wave_incl_scan(sMax[lane]);
+      sMu[lane] = mu;
+      const float muC = __shfl(mu, 63, 64);
+      sVf[lane] = __expf(muC - mu);
+      if (lane == 0) {
+        sMisc[0] = muC;
+        sMisc[1] = __expf(muC);
+      }
+    }
+    __syncthreads();
+
+    // ---- Gram M0[i][j] = b_i sum_c k_ic k_jc exp(G_ic - G_jc), i > j -----------
+    if (wave == 0) {
+      g_acc += (double)sMisc[0];  // mu_C; every lane of wave 0 keeps the same sum
+      // rows 32..63 against columns 0..31, both decayed against token 31
+      f32x16 acc = zero16();
+#pragma unroll 2
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int cc = 16 * ks + 8 * h;
+        const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, sMu, FP, 32 + l32, 31, cc, true);
+        const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, sMu, FP, l32, 31, cc, false);
+        mma<NTK, NTK>(acc, fa, fb);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 32 + acc_row(r, lane);
+        sN[i * NP + l32] = sBeta[i] * acc[r];
+      }
+    } else if (wave == 1) {
+      // rows 16..31 against columns 0..15 (reference token 15) and rows 48..63
+      // against columns 32..47 (reference token 47), as one 32 x 32 tile whose
+      // two cross quadrants are discarded (their factors are <= 1 as well)
+      const int ra = l32 < 16 ? 16 + l32 : 32 + l32;
+      const int rb = l32 < 16 ? l32 : 16 + l32;
+      const int ref = l32 < 16 ? 15 : 47;
+      f32x16 acc = zero16();
+#pragma unroll 2
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int cc = 16 * ks + 8 * h;
+        const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, sMu, FP, ra, ref, cc, true);
+        const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, sMu, FP, rb, ref, cc, false);
+        mma<NTK, NTK>(acc, fa, fb);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rho = acc_row(r, lane);
+        if ((rho < 16) == (l32 < 16)) {
+          const int i = rho < 16 ? 16 + rho : 32 + rho;
+          sN[i * NP + rb] = sBeta[i] * acc[r];
+        }
+      }
+    } else {
+      // the four 16-token diagonal blocks, term by term: wave 2 blocks 0-1,
+      // wave 3 blocks 2-3; lane = (row i, channel quarter q)
+      const int i = lane & 15, q = lane >> 4;
+      constexpr int QC = D / 4;
+#pragma unroll 1
+      for (int bb = 0; bb < 2; ++bb) {
+        const int b0 = 16 * (2 * (wave - 2) + bb);
+        const int ti = b0 + i;
+        const float mui = sMu[ti];
+        float acc[15];
+#pragma unroll
+        for (int j = 0; j < 15; ++j) acc[j] = 0.f;
+#pragma unroll 1
+        for (int cc = 0; cc < QC; cc += 4) {
+          const int c = q * QC + cc;
+          float ki[4], gi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ki[e] = (float)sKf[ti * FP + c + e];
+            gi[e] = sG[ti * FP + c + e] - mui;
+          }
+#pragma unroll
+          for (int j = 0; j < 15; ++j) {
+            if (j < i) {
+              const int tj = b0 + j;
+              const float muj = sMu[tj];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[j] = fmaf(ki[e] * (float)sKf[tj * FP + c + e], __expf(gi[e] - (sG[tj * FP + c + e] - muj)),
+                              acc[j]);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+          acc[j] += __shfl_xor(acc[j], 16, 64);
+          acc[j] += __shfl_xor(acc[j], 32, 64);
+        }
+        if (q == 0) {
+          const float bi = sBeta[ti];
+#pragma unroll
+          for (int j = 0; j < 15; ++j)
+            if (j < i) sN[ti * NP + b0 + j] = bi * acc[j];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- N = (I + M0)^-1: 16 x 16 diagonal blocks (wave 0) -------------------
+    if (wave == 0) {
+      const int b = lane >> 4, c = lane & 15;
+      const float* Mb = sN + (16 * b) * NP + 16 * b;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < r; ++k)
+          if (k >= c) acc = fmaf(Mb[r * NP + k], x[k], acc);
+        x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sN[(16 * b + r) * NP + 16 * b + c] = x[r];
+    }
+    // ---- block rows i = 1..3: N_ij = -N_ii sum_{k=j}^{i-1} M_ik N_kj ----------
+    {
+      const int r = tid >> 4, c = tid & 15;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+          float acc = 0.f;
+          const float* Mrow = sN + (16 * i + r) * NP;
+          for (int k = j; k < i; ++k)
+#pragma unroll 4
+            for (int m = 0; m < 16; ++m) acc = fmaf(Mrow[16 * k + m], sN[(16 * k + m) * NP + 16 * j + c], acc);
+          sT[(j * 16 + r) * 17 + c] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+          float acc = 0.f;
+          const float* Nrow = sN + (16 * i + r) * NP + 16 * i;
+#pragma unroll
+          for (int m = 0; m < 16; ++m) acc = fmaf(Nrow[m], sT[(j * 16 + m) * 17 + c], acc);
+          sN[(16 * i + r) * NP + 16 * j + c] = -acc;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- X = N diag(beta) split to bf16 terms; decayed key copies ------------
+    {
+      const int t = tid >> 2;
+      const int cb = (tid & 3) * 16;
+      float nv16[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int tp = cb + j;
+        nv16[j] = (tp <= t) ? sN[t * NP + tp] : 0.f;
+      }
+      __syncthreads();  // sN is overwritten below
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float x0[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x0[j] = nv16[8 * half + j] * sBeta[cb + 8 * half + j];
+        const Frag<NTD> f0 = split8<NTD>(x0);
+#pragma unroll
+        for (int i = 0; i < NTD; ++i) st8(sA + i * ATS + t * TP + cb + 8 * half, f0.t[i]);
+      }
+    }
+    if (tid < 16 * (D / 8)) {
+      // tokens 4*tq .. 4*tq+3, channels 8*db .. 8*db+7
+      const int tq = tid & 15, db = tid >> 4;
+      const float muC = sMisc[0];
+      float kd[8][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * tq + r;
+        const float mut = sMu[t];
+        float kb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = 8 * db + j;
+          const float kv = (float)sKf[t * FP + c];
+          const float hv = sG[t * FP + c] - mut;  // H_t
+          kb[j] = kv * __expf(hv);
+          kd[j][r] = kv * __expf((sGC[c] - muC) - hv);
+        }
+        const Frag<NTK> f = split8<NTK>(kb);
+#pragma unroll
+        for (int i = 0; i < NTK; ++i) st8(sKb + i * KBS + t * KP + 8 * db, f.t[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split4_store<NTK>(sKd + (8 * db + j) * TP + 4 * tq, KDS, kd[j]);
+    }
+    if (tid < D) {
+      sRS[tid] = __expf(sGC[tid]);
+      sRU[tid] = __expf(sGC[tid] - sMisc[0]);
+    }
+    __syncthreads();
+
+    // ---- per wave: Y = Kb Z, W = X R, Z = diag(row factor) Z + Kd W -------------
+    {
+      const bf16_t* pKb = sKb + l32 * KP + 4 * h;
+      const bf16_t* pKd = sKd + l32 * TP + 4 * h;
+      const bf16_t* pA = sA + l32 * TP + 4 * h;
+      const float* rowf = s_wave ? sRS : sRU;
+      const float emuC = sMisc[1];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int gcol = col0 + 32 * ct + l32;
+        using VT = typename std::conditional<IN_F32, float, bf16_t>::type;
+        VT vv[2][16];
+        if (s_wave) {
+          const VT* vsrc = reinterpret_cast<const VT*>(a.v) + ((size_t)c0 * n_chain + chain) * D + gcol;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int t = 32 * tt + acc_row(r, lane);
+              vv[tt][r] = (t < nv) ? vsrc[(size_t)t * n_chain * D] : (VT)0.f;
+            }
+        }
+        // Y[tt] = Kb[tt rows] * Z[:, ct]
+        f32x16 Y[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const Frag<NTD> fb = acc_as_b<NTD>(Z[rt][ct], m);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const Frag<NTK> fa = lds_a_perm<NTK>(pKb, KBS, 32 * tt * KP + 32 * rt + 16 * m);
+              mma<NTK, NTD>(Y[tt], fa, fb);
+            }
+          }
+        if (s_wave) {  // R = diag(exp(mu_C - mu)) V - exp(mu_C) Kb S;  U waves: R = -Kb U
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              Y[tt][r] = sVf[32 * tt + acc_row(r, lane)] * (float)vv[tt][r] - emuC * Y[tt][r];
+        }
+        // W[tt] = sum_{tp <= tt} X[tt, tp] Y[tp]  (X lower triangular)
+        f32x16 W[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const Frag<NTD> fb = acc_as_b<NTD>(Y[tp], m, s_wave ? 1.f : -1.f);
+#pragma unroll
+            for (int tt = tp; tt < 2; ++tt) {
+              const Frag<NTD> fa = lds_a_perm<NTD>(pA, ATS, 32 * tt * TP + 32 * tp + 16 * m);
+              mma<NTD, NTD>(W[tt], fa, fb);
+            }
+          }
+        // Z = diag(row factor) Z + Kd W
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Z[rt][ct][r] *= rowf[32 * rt + acc_row(r, lane)];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const Frag<NTD> fb = acc_as_b<NTD>(W[tt], m);
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+              const Frag<NTK> fa = lds_a_perm<NTK>(pKd, KDS, 32 * rt * TP + 32 * tt + 16 * m);
+              mma<NTK, NTD>(Z[rt][ct], fa, fb);
+            }
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- write U (waves 0-1) or S (waves 2-3), and g -----------------------------
+  float* dst = (s_wave ? a.S : a.U) + unit * D * D;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dst[(size_t)(32 * rt + acc_row(r, lane0)) * D + col0 + 32 * ct + (lane0 & 31)] = Z[rt][ct][r];
+  if (wave == 0 && lane0 == 0) a.g[unit] = (float)g_acc;
+}
+
+template <int D, bool F32>
+hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
+  constexpr int lds = KdaCfg<D, F32>::LDS;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_kda_kernel<D, F32>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((build_kda_kernel<D, F32>), dim3(n_blocks), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool kda_build_supported(int d, bool in_f32) { return d == 64 || (d == 128 && !in_f32); }
+
+hipError_t launch_build_kda(int d, bool in_f32, const BuildArgs& a, int n_blocks, hipStream_t stream) {
+  if (d == 128 && !in_f32) return launch_t<128, false>(a, n_blocks, stream);
+  if (d == 64) return in_f32 ? launch_t<64, true>(a, n_blocks, stream) : launch_t<64, false>(a, n_blocks, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hypic

@@ -24,8 +24,8 @@ from typing import Optional
 
 import numpy as np
 
-NAIVE, SCALAR, DIAG, DELTA = 0, 1, 2, 3
-FAMILY_NAMES = {NAIVE: "naive", SCALAR: "scalar", DIAG: "diag", DELTA: "delta"}
+NAIVE, SCALAR, DIAG, DELTA, KDA = 0, 1, 2, 3, 4
+FAMILY_NAMES = {NAIVE: "naive", SCALAR: "scalar", DIAG: "diag", DELTA: "delta", KDA: "kda"}
 
 # tensor ids inside the seed sequence
 T_Q, T_K, T_V, T_BETA, T_GATE, T_PG, T_PU, T_PS, T_SINIT, T_LEN = range(10)
@@ -210,6 +210,17 @@ def gdn_cold(n_seg=64, L=512, n_chain=32, d=128, dtype="bf16", gate_scale=1.0 / 
     q, k, v, beta, lg = _draw_delta_tokens(4, n_tok, n_chain, d, dtype, gate_scale, want_q=want_q)
     return Tokens(DELTA, dtype, n_chain, d, d, k, v, q, beta, lg, False, even_offsets(n_seg, L),
                   {"workload": "gdn_cold32k", "n_seg": n_seg, "L": L, "gate_scale": gate_scale})
+
+
+def kda(n_seg=64, L=512, n_chain=32, d=128, dtype="bf16", gate_scale=1.0 / 8, want_q=False) -> Tokens:
+    """KDA (delta rule with per-channel gates), the cold request's shape: unit
+    keys and queries, v ~ N(0,1), beta = sigmoid(N), log alpha = -softplus(N) *
+    scale drawn per token and key channel."""
+    n_tok = n_seg * L
+    q, k, v, beta, _ = _draw_delta_tokens(14, n_tok, n_chain, d, dtype, None, want_q=want_q)
+    lg = round_to(-_softplus(rng(14, T_GATE).standard_normal((n_tok, n_chain, d))) * gate_scale, dtype)
+    return Tokens(KDA, dtype, n_chain, d, d, k, v, q, beta, lg, False, even_offsets(n_seg, L),
+                  {"workload": "kda_cold32k", "n_seg": n_seg, "L": L, "gate_scale": gate_scale})
 
 
 def ragged_lengths(n_seg: int, total: int, workload: int = 12, sigma: float = 0.9, min_len: int = 32,

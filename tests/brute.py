@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-NAIVE, SCALAR, DIAG, DELTA = 0, 1, 2, 3
+NAIVE, SCALAR, DIAG, DELTA, KDA = 0, 1, 2, 3, 4
 
 
 def token_matrix(fam, k, beta=None, lg=None, lgv=None):
@@ -29,6 +29,8 @@ def token_matrix(fam, k, beta=None, lg=None, lgv=None):
         return np.exp(lg) * eye, 1.0
     if fam == DIAG:
         return np.diag(np.exp(lgv)), 1.0
+    if fam == KDA:  # erase after the per-channel decay
+        return (eye - beta * np.outer(k, k)) @ np.diag(np.exp(lgv)), beta
     a = 1.0 if lg is None else np.exp(lg)
     return a * (eye - beta * np.outer(k, k)), beta
 
@@ -45,6 +47,8 @@ def unit_matrices(fam, k, beta, log_gate, gate_per_chain, t0, t1, h):
         elif fam == DELTA:
             lg = None if log_gate is None else log_gate[t, h]
             mats.append(token_matrix(fam, kt, beta=beta[t, h], lg=lg))
+        elif fam == KDA:
+            mats.append(token_matrix(fam, kt, beta=beta[t, h], lgv=log_gate[t, h]))
         else:
             mats.append(token_matrix(fam, kt))
     return mats

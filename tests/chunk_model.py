@@ -17,6 +17,20 @@ G_t = sum_{s<=t} a_s, start state S0 and start transition U0:
     Z     = Abar (V - diag(exp(G)) K S0)
     S1    = exp(G_C) S0 + K^T diag(exp(G_C - G)) Z
     O     = diag(exp(G)) Q S0 + (tril(Q K^T) o Gamma) Z      (seam outputs)
+KDA (delta rule with one gate per key channel), one chunk with per-channel
+inclusive prefixes G [C, dk], the per-token largest gate summed, mu_t =
+sum_{s<=t} max_c lg_sc, and the shifted prefixes H = G - mu (per channel
+non-increasing in t, <= 0); H_C, mu_C, G_C are the chunk's last rows:
+    M[i,j]  = b_i sum_c k_ic k_jc exp(H_ic - H_jc)   (i > j, every term <= |k_i k_j|)
+              16-token diagonal blocks term by term; block row I > 0 against
+              the earlier tokens as (K_I o exp(H_I - H_r)) (K_<I o exp(H_r - H_<I))^T
+              with r = 16 I - 1, both factors <= |k|
+    X       = (I + M)^-1 diag(b)
+    Kb      = K o exp(H),  Kd = (K o exp(H_C - H))^T            (both <= |k|)
+    U1      = diag(exp(G_C - mu_C)) U0 - Kd X (Kb U0),  g += mu_C   (T = exp(g) U)
+    S1      = diag(exp(G_C)) S0 + Kd X (diag(exp(mu_C - mu)) V - exp(mu_C) Kb S0)
+Every factor is at most 1 whatever the gates; in the frame diag(exp(-mu)) the
+Gram is that of the scalar-gated delta rule with the channel spread left over.
 Scalar / diagonal families, per chunk:
     S1    = diag(exp(G_C)) S0 + (K o exp(G_C - G))^T V
 """
@@ -125,3 +139,51 @@ def scalar_diag_build(k, v, lg, C=64):
         S = (np.exp(GC)[:, None] if np.ndim(GC) == 1 else np.exp(GC)) * S + Kt.T @ V
         g = g + GC
     return g, S
+
+
+def kda_gram(K, b, H, bs=16):
+    """Strictly lower M[i,j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc) as the kernel forms it."""
+    C = K.shape[0]
+    M = np.zeros((C, C))
+    for I in range(C // bs):
+        rows = slice(bs * I, bs * (I + 1))
+        for i in range(bs * I, bs * (I + 1)):
+            for j in range(bs * I, i):
+                M[i, j] = b[i] * np.sum(K[i] * K[j] * np.exp(H[i] - H[j]))
+        if I > 0:
+            r = bs * I - 1
+            Kb = K[rows] * np.exp(H[rows] - H[r])
+            Ka = K[:bs * I] * np.exp(H[r] - H[:bs * I])
+            M[rows, :bs * I] = b[rows, None] * (Kb @ Ka.T)
+    return M
+
+
+def kda_chunk(K, V, b, LG, S0, U0):
+    G = np.cumsum(LG, axis=0)
+    mu = np.cumsum(LG.max(axis=1))
+    H = G - mu[:, None]
+    GC, HC, muC = G[-1], H[-1], mu[-1]
+    X = blocked_unit_lower_inverse(kda_gram(K, b, H)) * b[None, :]
+    Kb = K * np.exp(H)
+    Kd = (K * np.exp(HC - H)).T
+    U1 = np.exp(GC - muC)[:, None] * U0 - Kd @ (X @ (Kb @ U0))
+    S1 = np.exp(GC)[:, None] * S0 + Kd @ (X @ (np.exp(muC - mu)[:, None] * V - np.exp(muC) * (Kb @ S0)))
+    return S1, U1, muC
+
+
+def kda_build(k, v, b, lg, C=64):
+    """Chunked KDA build of one unit: k [L, dk], v [L, dv], b [L], lg [L, dk]; tail zero-padded."""
+    L, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv))
+    U = np.eye(dk)
+    g = 0.0
+    for c0 in range(0, L, C):
+        n = min(C, L - c0)
+        K = np.zeros((C, dk)); K[:n] = k[c0:c0 + n]
+        V = np.zeros((C, dv)); V[:n] = v[c0:c0 + n]
+        bb = np.zeros(C); bb[:n] = b[c0:c0 + n]
+        LG = np.zeros((C, dk)); LG[:n] = lg[c0:c0 + n]
+        S, U, m = kda_chunk(K, V, bb, LG, S, U)
+        g += m
+    return g, U, S

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hypic.h")
 
 INVALID, UNSUPPORTED = api.HYPIC_E_INVALID, api.HYPIC_E_UNSUPPORTED
-NAIVE, SCALAR, DIAG, DELTA = 0, 1, 2, 3
+NAIVE, SCALAR, DIAG, DELTA, KDA = 0, 1, 2, 3, 4
 BF16, F32 = api.HYPIC_BF16, api.HYPIC_F32
 
 # fake device addresses, 16-byte aligned, far apart (1 TiB) so nothing overlaps by accident
@@ -51,21 +51,21 @@ def test_library_exports_every_declared_symbol(lib):
     assert declared <= exported, declared - exported
     for name in declared:
         getattr(lib, name)
-    assert lib.hypic_abi_version() == 5
+    assert lib.hypic_abi_version() == 6
 
 
 def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
     if beta is None:
-        beta = fam == DELTA
+        beta = fam in (DELTA, KDA)
     if lg is None:
-        lg = fam in (SCALAR, DIAG, DELTA)
+        lg = fam in (SCALAR, DIAG, DELTA, KDA)
     return Tokens(dtype, A["q"] if q else None, A["k"], A["v"], A["beta"] if beta else None,
                   A["lg"] if lg else None, gate_per_chain)
 
 
 def pairs(fam, g=True, U=None, S=True):
     if U is None:
-        U = fam == DELTA
+        U = fam in (DELTA, KDA)
     return Pairs(A["g"] if g else None, A["U"] if U else None, A["S"] if S else None)
 
 
@@ -129,6 +129,20 @@ def test_piece_split_workspace_size(lib):
     assert ws_size(lib, fam=SCALAR, offsets=(0, 1024), n_chain=512) == (0, 0)  # enough units already
 
 
+def test_kda_workspace_sizes(lib):
+    """The KDA build takes no workspace; its dense composition takes the delta
+    family's; its seam step is not built."""
+    assert ws_size(lib, fam=KDA) == (0, 0)
+    assert ws_size(lib, fam=KDA, d=64, dtype=F32) == (0, 0)
+    for want_prefix in (0, 1):
+        a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert lib.hypic_compose_workspace_size(KDA, 64, 32, 128, 128, want_prefix, ctypes.byref(a)) == 0
+        assert lib.hypic_compose_workspace_size(DELTA, 64, 32, 128, 128, want_prefix, ctypes.byref(b)) == 0
+        assert a.value == b.value > 0
+    out = ctypes.c_size_t(0)
+    assert lib.hypic_seam_step_workspace_size(KDA, 4, 8, 2, 128, 128, ctypes.byref(out)) == UNSUPPORTED
+
+
 def test_workspace_size(lib):
     """Only the d = 128 bf16 delta build takes a workspace: one 8704-byte WY record
     (fp16 A0 [64 x 64], 64 row scales, 64 gate prefixes) per 64-token chunk and chain."""
@@ -171,6 +185,10 @@ def test_workspace_size(lib):
     (dict(t=Tokens(9, None, A["k"], A["v"], A["beta"], A["lg"], 0)), INVALID, "dtype"),
     (dict(fam=SCALAR, t=toks(SCALAR), p=pairs(SCALAR, U=True)), INVALID, "only defined for the delta"),
     (dict(fam=DELTA, p=pairs(DELTA, U=False)), INVALID, "required for the delta"),
+    (dict(fam=KDA, p=pairs(KDA, U=False), t=toks(KDA)), INVALID, "required for the delta and KDA"),
+    (dict(fam=KDA, t=toks(KDA, beta=False), p=pairs(KDA)), INVALID, "beta is required"),
+    (dict(fam=KDA, t=toks(KDA, lg=False), p=pairs(KDA)), INVALID, "log_gate is required"),
+    (dict(fam=KDA, t=toks(KDA, dtype=F32), p=pairs(KDA)), UNSUPPORTED, "KDA build"),
     (dict(p=Pairs(A["g"], A["U"], None)), INVALID, "out.S is NULL"),
     (dict(p=Pairs(None, A["U"], A["S"])), INVALID, "out.g is NULL"),
     (dict(p=Pairs(A["g"], A["U"], A["k"] + 4096)), INVALID, "overlaps input k"),
@@ -203,6 +221,7 @@ def compose_call(lib, fam=DELTA, n_seg=3, n_chain=2, d=128, p=None, S_init=None,
     (dict(fam=DELTA, p=Pairs(A["g"], None, A["S"])), INVALID, "required for the delta"),
     (dict(fam=DIAG, p=pairs(DIAG, U=True)), INVALID, "only defined for the delta"),
     (dict(fam=SCALAR, p=pairs(SCALAR), Utot=A["Utot"]), INVALID, "U_total is only defined"),
+    (dict(fam=KDA, p=Pairs(A["g"], None, A["S"])), INVALID, "required for the delta and KDA"),
     (dict(S_out=A["S"] + 64), INVALID, "overlaps input pairs.S"),
     (dict(S_init=A["Sinit"], S_out=A["Sinit"] + 16), INVALID, "overlaps input S_init"),
     (dict(prefix=A["Sout"] + 16), INVALID, "overlap"),
@@ -240,6 +259,7 @@ def seam_call(lib, fam=DELTA, n_seg=4, w=8, n_chain=2, d=128, t=None, body="defa
     (dict(fam=SCALAR, t=toks(SCALAR, q=True), body=pairs(SCALAR), win=Pairs(A["wg"], A["wU"], A["wS"])), INVALID,
      "only defined for delta"),
     (dict(d=256), UNSUPPORTED, "64, 128"),
+    (dict(fam=KDA, t=toks(KDA, q=True), body=pairs(KDA)), UNSUPPORTED, "not built for the KDA"),
     (dict(ws=None), INVALID, "workspace is NULL"),
     (dict(ws_bytes=1024), INVALID, "workspace too small"),
     (dict(ws=A["ws"] + 8), INVALID, "workspace is not 16-byte aligned"),
@@ -289,6 +309,7 @@ def rerotate_call(lib, fam=DELTA, n_seg=2, n_chain=2, dk=128, dv=128, pos=A["q"]
 
 @pytest.mark.parametrize("case,status", [
     (dict(fam=DIAG), UNSUPPORTED),
+    (dict(fam=KDA), UNSUPPORTED),
     (dict(dk=96, dv=96), UNSUPPORTED),
     (dict(n_seg=0), INVALID),
     (dict(base=0.0), INVALID),

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import SCALAR, DIAG, DELTA, NAIVE
+from oracle import SCALAR, DIAG, DELTA, NAIVE, KDA
 from segment_scan_amd import synth
 from tests import chunk_model
 
@@ -69,3 +69,46 @@ def test_scalar_diag_chunked_build_matches_oracle(fam):
     gm, Sm = chunk_model.scalar_diag_build(tk.k[:, 0], tk.v[:, 0], lg)
     assert rel(Sm, S[0, 0]) < 1e-12
     np.testing.assert_allclose(gm, g[0, 0], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("gate_scale", [1.0, 1.0 / 8, 0.0])
+@pytest.mark.parametrize("L", [192, 150, 64, 7])
+def test_kda_chunked_build_matches_oracle(gate_scale, L):
+    """The KDA chunk form (per-token largest gate as the frame, sub-block Gram
+    with reference tokens, decayed key copies) equals the token loop, including
+    the split of T into exp(g) U."""
+    r = np.random.default_rng(1000 + L)
+    dk = dv = 16
+    k = r.standard_normal((L, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = r.standard_normal((L, dv))
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal(L)))
+    lg = -np.log1p(np.exp(r.standard_normal((L, dk)))) * gate_scale
+    g, U, S = oracle.build_pairs(KDA, np.array([0, L], np.int32), k[:, None], v[:, None], b[:, None], lg[:, None])
+    gm, Um, Sm = chunk_model.kda_build(k, v, b, lg)
+    assert rel(Sm, S[0, 0]) < 1e-11
+    assert rel(Um, U[0, 0]) < 1e-11
+    assert abs(gm - g[0, 0]) < 1e-12 * max(1.0, abs(g[0, 0]))
+
+
+@pytest.mark.parametrize("pattern", ["half", "all"])
+def test_kda_strong_gates_stay_finite(pattern):
+    """Channel gates of -30 per token (on a random half of the entries, or on
+    every entry): every factor of the chunk form stays within [0, 1] and the
+    chunked build equals the token loop (U of magnitude e^-1000 stays in range
+    because the decay is carried by g)."""
+    r = np.random.default_rng(5)
+    L, dk = 150, 8
+    k = r.standard_normal((L, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = r.standard_normal((L, dk))
+    b = np.full(L, 0.5)
+    lg = np.full((L, dk), -30.0)
+    if pattern == "half":
+        lg = lg * (r.random((L, dk)) < 0.5)
+    with np.errstate(over="raise", invalid="raise"):
+        gm, Um, Sm = chunk_model.kda_build(k, v, b, lg)
+    g, U, S = oracle.build_pairs(KDA, np.array([0, L], np.int32), k[:, None], v[:, None], b[:, None], lg[:, None])
+    assert np.isfinite(Um).all() and np.isfinite(Sm).all()
+    assert rel(Um, U[0, 0]) < 1e-11 and rel(Sm, S[0, 0]) < 1e-11
+    assert abs(gm - g[0, 0]) < 1e-12 * abs(g[0, 0]) + 1e-12

@@ -1,0 +1,107 @@
+"""GPU parity: KDA (delta rule with per-channel gates) segment build vs the oracle.
+
+The library and the oracle split T_C = exp(g) U the same way (g is the sum
+over tokens of each token's largest channel gate), so g, U and S(C|0) are
+compared directly; U is also compared as exp(g_gpu - g_ref) U_gpu, the
+transition on the oracle's scale.  Tolerances as for the other families: 2e-3
+for bf16 tokens, 1e-5 for fp32 tokens (relative Frobenius per unit).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from segment_scan_amd import api, synth
+from segment_scan_amd.synth import KDA
+from tests.gpu_util import TOL, announce, assert_g_close, assert_units_close, host, upload_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_build(tk, offsets):
+    import torch
+    d = upload_tokens(tk)
+    g, U, S = api.seg_build(KDA, list(offsets), d["k"], d["v"], d["beta"], d["log_gate"])
+    torch.cuda.synchronize()
+    return host(g), host(U), host(S)
+
+
+def compare(name, g, U, S, rg, rU, rS, tol):
+    eS = assert_units_close(name + ".S", S, rS, tol)
+    assert_g_close(name + ".g", g, rg, tol)
+    assert_units_close(name + ".U", U, rU, tol)
+    Ts = np.exp(g - rg)[..., None, None] * U
+    eT = assert_units_close(name + ".T", Ts, rU, tol)
+    print("  max rel err S %.2e T %.2e" % (eS, eT), flush=True)
+
+
+def check_build(tk, name, offsets=None):
+    offsets = tk.offsets if offsets is None else np.asarray(offsets, np.int32)
+    announce(name, "dtype", tk.dtype, "chains", tk.n_chain, "segs", len(offsets) - 1, "d", tk.dk)
+    g, U, S = gpu_build(tk, offsets)
+    rg, rU, rS = oracle.build_pairs(KDA, offsets, tk.k, tk.v, tk.beta, tk.log_gate)
+    compare(name, g, U, S, rg, rU, rS, TOL[tk.dtype])
+    return g, U, S
+
+
+def test_kda_bf16_d128():
+    """The cold request's recipe, 4 segments x 512 tokens, 4 heads."""
+    tk = synth.kda(n_seg=4, n_chain=4)
+    check_build(tk, "kda_bf16_d128")
+
+
+@pytest.mark.parametrize("gate_scale", [1.0, 1.0 / 8, 1.0 / 64])
+def test_kda_fp32_d64_ragged(gate_scale):
+    """fp32 tokens (fp32 tolerance), segments of 1, 63, 64, 65, 130 and 200 tokens."""
+    lengths = [1, 63, 64, 65, 130, 200]
+    tk = synth.kda(n_seg=1, L=sum(lengths), n_chain=3, d=64, dtype="f32", gate_scale=gate_scale)
+    check_build(tk, "kda_f32_%g" % gate_scale, synth.ragged_offsets(lengths))
+
+
+def test_kda_bf16_d64():
+    tk = synth.kda(n_seg=3, L=100, n_chain=2, d=64)
+    check_build(tk, "kda_bf16_d64")
+
+
+@pytest.mark.parametrize("pattern", ["half", "all"])
+def test_kda_strong_and_zero_gates(pattern):
+    """Gates of e^-30 per token on a random half of the (token, channel)
+    entries and 1 on the rest, or e^-30 everywhere: every factor of the chunk
+    form stays within [0, 1], so nothing overflows, and the decay is carried by
+    g (hundreds of e-folds over a segment)."""
+    tk = synth.kda(n_seg=2, L=130, n_chain=2, d=64, dtype="f32")
+    r = np.random.default_rng(11)
+    mask = (r.random(tk.log_gate.shape) < 0.5) if pattern == "half" else np.ones(tk.log_gate.shape, bool)
+    tk.log_gate = np.where(mask, -30.0, 0.0)
+    check_build(tk, "kda_strong_gates_" + pattern)
+
+
+def test_kda_build_then_compose_matches_sequential():
+    """Cold path end to end on the GPU (KDA build, ordered dense composition)
+    against straight recurrence over the whole request, with slow gates."""
+    import torch
+    tk = synth.kda(n_seg=6, L=192, n_chain=3, gate_scale=1.0 / 64)
+    announce("kda_e2e")
+    d = upload_tokens(tk)
+    g, U, S = api.seg_build(KDA, list(tk.offsets), d["k"], d["v"], d["beta"], d["log_gate"])
+    res = api.compose(KDA, g, U, S, want_prefix=True)
+    torch.cuda.synchronize()
+    Sseq, _ = oracle.sequential(KDA, tk.k, tk.v, tk.beta, tk.log_gate)
+    assert_units_close("kda_e2e", host(res["S_out"]), Sseq, TOL["bf16"], unit_dims=1)
+
+
+def test_kda_cold_full_size_sampled_units():
+    """The cold request's shape (32 heads x 64 segments x 512 tokens, d = 128,
+    bf16) in the launch the benchmark times; the oracle recomputes a sample of
+    units one by one."""
+    tk = synth.kda()
+    announce("kda_full", "units", 64 * 32)
+    g, U, S = gpu_build(tk, tk.offsets)
+    rng = np.random.default_rng(1)
+    units = [(0, 0), (63, 31), (17, 5)] + [tuple(x) for x in zip(rng.integers(0, 64, 5), rng.integers(0, 32, 5))]
+    for s, hh in units:
+        sub = tk.chains([hh])
+        t0, t1 = tk.offsets[s], tk.offsets[s + 1]
+        rg, rU, rS = oracle.build_pairs(KDA, np.array([0, t1 - t0], np.int32), sub.k[t0:t1], sub.v[t0:t1],
+                                        sub.beta[t0:t1], sub.log_gate[t0:t1])
+        compare("full(%d,%d)" % (s, hh), g[s:s + 1, hh:hh + 1], U[s:s + 1, hh:hh + 1], S[s:s + 1, hh:hh + 1],
+                rg, rU, rS, TOL["bf16"])

@@ -14,10 +14,10 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import NAIVE, SCALAR, DIAG, DELTA
+from oracle import NAIVE, SCALAR, DIAG, DELTA, KDA, DENSE
 from tests import brute
 
-FAMS = [NAIVE, SCALAR, DIAG, DELTA]
+FAMS = [NAIVE, SCALAR, DIAG, DELTA, KDA]
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -45,6 +45,9 @@ def rand_tokens(fam, n_tok, n_chain, dk, dv, seed, gate_scale=1.0, delta_gate=Tr
         beta = 1.0 / (1.0 + np.exp(-r.standard_normal((n_tok, n_chain))))
         if delta_gate:
             lg = -np.abs(r.standard_normal((n_tok, n_chain))) * 0.3 * gate_scale
+    elif fam == KDA:
+        beta = 1.0 / (1.0 + np.exp(-r.standard_normal((n_tok, n_chain))))
+        lg = -np.abs(r.standard_normal((n_tok, n_chain, dk))) * 0.3 * gate_scale
     return dict(q=q, k=k, v=v, beta=beta, log_gate=lg)
 
 
@@ -150,13 +153,13 @@ def test_associativity_and_identity(fam):
                            None if U is None else np.stack([U[0], c12["U_tot"]]),
                            np.stack([S[0], c12["S_out"]]), want_total=True)
     assert rel(left["S_out"], right["S_out"]) < 1e-13
-    if fam == DELTA:
+    if fam in DENSE:
         assert rel(left["U_tot"], right["U_tot"]) < 1e-13
     np.testing.assert_allclose(left["g_tot"], right["g_tot"], rtol=1e-14, atol=1e-15)
     # identity pair (T = I, S = 0) leaves the state unchanged
     gl = oracle.gate_len(fam, dk)
     gi = np.zeros((1, 2) + ((dk,) if gl > 1 else ()))
-    Ui = np.broadcast_to(np.eye(dk), (1, 2, dk, dk)).copy() if fam == DELTA else None
+    Ui = np.broadcast_to(np.eye(dk), (1, 2, dk, dk)).copy() if fam in DENSE else None
     Si = np.zeros((1, 2, dk, dv))
     St = np.random.default_rng(1).standard_normal((2, dk, dv))
     out = oracle.compose(fam, gi, Ui, Si, S_init=St)
@@ -303,6 +306,59 @@ def test_naive_addition_error_matches_pages_22_percent():
     assert abs(frac - fx["pages_fraction"]) <= fx["tolerance"], frac
 
 
+def test_kda_with_equal_channel_gates_is_gdn():
+    """KDA whose gate is the same on every channel is the gated delta rule: the
+    scalar gate commutes with the erase factor."""
+    dk, dv = 6, 5
+    x = rand_tokens(DELTA, 19, 2, dk, dv, seed=4300)
+    lgv = np.repeat(x["log_gate"][:, :, None], dk, axis=2)
+    off = np.array([0, 7, 19], np.int32)
+    gd, Ud, Sd = oracle.build_pairs(DELTA, off, x["k"], x["v"], x["beta"], x["log_gate"])
+    gk, Uk, Sk = oracle.build_pairs(KDA, off, x["k"], x["v"], x["beta"], lgv)
+    assert rel(Sk, Sd) < 1e-13
+    assert rel(oracle.transition_dense(KDA, gk, Uk, dk), oracle.transition_dense(DELTA, gd, Ud, dk)) < 1e-13
+    np.testing.assert_allclose(gk, gd, rtol=1e-13)  # the largest channel gate is the gate
+
+
+def test_kda_without_erase_is_gla():
+    """beta -> 0 removes the erase and the write: T is the diagonal family's diag(exp(sum lg));
+    with keys orthogonal to each other the erase of one token does not touch the others'
+    writes, so S is the diagonal family's state with values scaled by beta."""
+    dk, dv = 4, 3
+    x = rand_tokens(KDA, 4, 1, dk, dv, seed=4301)
+    off = np.array([0, 4], np.int32)
+    beta0 = np.zeros_like(x["beta"])
+    g, U, S = oracle.build_pairs(KDA, off, x["k"], x["v"], beta0, x["log_gate"])
+    gd, _, _ = oracle.build_pairs(DIAG, off, x["k"], x["v"], None, x["log_gate"])
+    assert rel(oracle.transition_dense(KDA, g, U, dk), oracle.transition_dense(DIAG, gd, None, dk)) < 1e-14
+    assert np.abs(S).max() == 0.0
+    # orthonormal keys (one basis vector per token): the erase of token t only
+    # touches channel t, which holds no earlier write
+    k = np.eye(dk)[:, None, :]
+    b = np.full((dk, 1), 0.7)
+    _, _, Sk = oracle.build_pairs(KDA, off, k, x["v"], b, x["log_gate"])
+    _, _, Sg = oracle.build_pairs(DIAG, off, k, 0.7 * x["v"], None, x["log_gate"])
+    assert rel(Sk, Sg) < 1e-14
+
+
+def test_kda_decay_applies_before_the_erase():
+    """One token from a nonzero state: S' = (I - b k k^T) diag(a) S + b k v^T, written
+    out by hand (the order of decay and erase matters when the gates differ)."""
+    dk, dv = 3, 2
+    k = np.array([[[0.6, 0.8, 0.0]]])
+    v = np.array([[[1.0, -2.0]]])
+    b = np.array([[0.5]])
+    lg = np.log(np.array([[[0.5, 0.9, 0.2]]]))
+    S0 = np.array([[[1.0, 2.0], [3.0, -1.0], [0.5, 0.5]]])
+    S1, _ = oracle.sequential(KDA, k, v, b, lg, S_init=S0)
+    D = np.diag([0.5, 0.9, 0.2])
+    kk = k[0, 0]
+    want = (np.eye(3) - 0.5 * np.outer(kk, kk)) @ D @ S0[0] + 0.5 * np.outer(kk, v[0, 0])
+    assert rel(S1[0], want) < 1e-15
+    wrong = D @ ((np.eye(3) - 0.5 * np.outer(kk, kk)) @ S0[0]) + 0.5 * np.outer(kk, v[0, 0])
+    assert rel(want, wrong) > 1e-2  # the test tells the two orders apart
+
+
 # ---------------------------------------------------------------- seam step
 
 
@@ -340,7 +396,7 @@ def test_seam_step_equals_sequential_over_windows_and_bodies(fam):
                                         None if xw["log_gate"] is None else xw["log_gate"][sl])
         assert rel(res["wS"][s], Sw[0]) < 1e-13
         np.testing.assert_allclose(res["wg"][s], gw[0], rtol=1e-13, atol=1e-15)
-        if fam == DELTA:
+        if fam in DENSE:
             assert rel(res["wU"][s], Uw[0]) < 1e-13
 
 

@@ -45,12 +45,12 @@ MUTANTS = {
         "acc += U[(size_t)i * dk + l] * S[(size_t)l * dv + j];",
         "acc += U[(size_t)l * dk + i] * S[(size_t)l * dv + j];"),
     "compose_add_before_transition": (
-        "      apply_T(fam, dk, dv, g + pu * gl, fam == REF_DELTA ? U + pu * dk * dk : NULL, cur, tmp);\n"
+        "      apply_T(fam, dk, dv, g + pu * gl, REF_DENSE(fam) ? U + pu * dk * dk : NULL, cur, tmp);\n"
         "      const double* Si = S + pu * sz;\n"
         "      for (size_t e = 0; e < sz; ++e) cur[e] += Si[e];",
         "      const double* Si = S + pu * sz;\n"
         "      for (size_t e = 0; e < sz; ++e) cur[e] += Si[e];\n"
-        "      apply_T(fam, dk, dv, g + pu * gl, fam == REF_DELTA ? U + pu * dk * dk : NULL, cur, tmp);"),
+        "      apply_T(fam, dk, dv, g + pu * gl, REF_DENSE(fam) ? U + pu * dk * dk : NULL, cur, tmp);"),
     "compose_total_order_reversed": (
         "acc += Us[(size_t)i * dk + l] * ut[(size_t)l * dk + j];",
         "acc += ut[(size_t)i * dk + l] * Us[(size_t)l * dk + j];"),
@@ -59,10 +59,10 @@ MUTANTS = {
         "gacc[i] = g[pu * gl + i];"),
     "compose_prefix_after_update": (
         "      if (prefix) memcpy(prefix + pu * sz, cur, sizeof(double) * sz);\n"
-        "      apply_T(fam, dk, dv, g + pu * gl, fam == REF_DELTA ? U + pu * dk * dk : NULL, cur, tmp);\n"
+        "      apply_T(fam, dk, dv, g + pu * gl, REF_DENSE(fam) ? U + pu * dk * dk : NULL, cur, tmp);\n"
         "      const double* Si = S + pu * sz;\n"
         "      for (size_t e = 0; e < sz; ++e) cur[e] += Si[e];",
-        "      apply_T(fam, dk, dv, g + pu * gl, fam == REF_DELTA ? U + pu * dk * dk : NULL, cur, tmp);\n"
+        "      apply_T(fam, dk, dv, g + pu * gl, REF_DENSE(fam) ? U + pu * dk * dk : NULL, cur, tmp);\n"
         "      const double* Si = S + pu * sz;\n"
         "      for (size_t e = 0; e < sz; ++e) cur[e] += Si[e];\n"
         "      if (prefix) memcpy(prefix + pu * sz, cur, sizeof(double) * sz);"),
@@ -71,7 +71,7 @@ MUTANTS = {
         "for (int t = offsets[s] + 1; t < offsets[s + 1]; ++t)"),
     "seam_output_before_update": (
         "        token_step(fam, dk, dv, &x, S, NULL, NULL, work);\n"
-        "        if (wS || wU || wg) token_step(fam, dk, dv, &x, pS, pg, fam == REF_DELTA ? pU : NULL, work);\n"
+        "        if (wS || wU || wg) token_step(fam, dk, dv, &x, pS, pg, REF_DENSE(fam) ? pU : NULL, work);\n"
         "        const double* qt = q + ((size_t)t * n_chain + h) * dk;\n"
         "        double* ot = o_out + ((size_t)t * n_chain + h) * dv;\n"
         "        for (int c = 0; c < dv; ++c) {\n"
@@ -79,7 +79,7 @@ MUTANTS = {
         "          for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + c] * qt[i];\n"
         "          ot[c] = acc;\n"
         "        }\n",
-        "        if (wS || wU || wg) token_step(fam, dk, dv, &x, pS, pg, fam == REF_DELTA ? pU : NULL, work);\n"
+        "        if (wS || wU || wg) token_step(fam, dk, dv, &x, pS, pg, REF_DENSE(fam) ? pU : NULL, work);\n"
         "        const double* qt = q + ((size_t)t * n_chain + h) * dk;\n"
         "        double* ot = o_out + ((size_t)t * n_chain + h) * dv;\n"
         "        for (int c = 0; c < dv; ++c) {\n"
@@ -91,6 +91,35 @@ MUTANTS = {
     "seam_body_skipped_for_last_segment": (
         "      if (body_S) {\n        apply_T(",
         "      if (body_S && s + 1 < n_seg) {\n        apply_T("),
+    "kda_erase_before_decay": (
+        "      for (i = 0; i < dk; ++i) {\n"
+        "        const double a = exp(x->lgv[i]);\n"
+        "        for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;\n"
+        "      }\n"
+        "      for (j = 0; j < dv; ++j) work[j] = 0.0;\n"
+        "      for (i = 0; i < dk; ++i)\n"
+        "        for (j = 0; j < dv; ++j) work[j] += x->k[i] * S[(size_t)i * dv + j];\n"
+        "      for (i = 0; i < dk; ++i)\n"
+        "        for (j = 0; j < dv; ++j)\n"
+        "          S[(size_t)i * dv + j] += x->beta * x->k[i] * (x->v[j] - work[j]);\n",
+        "      for (j = 0; j < dv; ++j) work[j] = 0.0;\n"
+        "      for (i = 0; i < dk; ++i)\n"
+        "        for (j = 0; j < dv; ++j) work[j] += x->k[i] * S[(size_t)i * dv + j];\n"
+        "      for (i = 0; i < dk; ++i)\n"
+        "        for (j = 0; j < dv; ++j)\n"
+        "          S[(size_t)i * dv + j] -= x->beta * x->k[i] * work[j];\n"
+        "      for (i = 0; i < dk; ++i) {\n"
+        "        const double a = exp(x->lgv[i]);\n"
+        "        for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;\n"
+        "      }\n"
+        "      for (i = 0; i < dk; ++i)\n"
+        "        for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] += x->beta * x->k[i] * x->v[j];\n"),
+    "kda_scale_not_moved_into_g": (
+        "        if (g) g[0] += m;",
+        "        if (g) g[0] += 0.0;"),
+    "kda_gate_of_wrong_channel": (
+        "          const double a = exp(x->lgv[i] - m);",
+        "          const double a = exp(x->lgv[dk - 1 - i] - m);"),
     "rope_sin_sign": (
         "R[(2 * i) * dk + 2 * i + 1] = -sn;",
         "R[(2 * i) * dk + 2 * i + 1] = sn;"),
