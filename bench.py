@@ -15,6 +15,8 @@ accumulation -- every (segment, head) pair (T_C, S(C|0)) built concurrently
   gdn_ragged32k the cold request with uneven segments (58 .. 2048 tokens)
   gdn_warm100k_rerotate  rotary re-rotation of the warm request's cached pairs
                 to new offsets
+  kda_cold32k   the cold request's shape with KDA (per-channel gated delta rule):
+                build + compose
 Prints one JSON line.  `value` is segment-tokens/s of the whole step; the
 `roofline` object is for the step's dominant kernel, timed with HIP events on
 the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
@@ -45,6 +47,7 @@ KERNEL_SOURCES = {
     "seam": ["segment_scan_amd/csrc/kernels/chain.hip", "segment_scan_amd/csrc/kernels/seam_prep.hip"],
     "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
     "rerotate": ["segment_scan_amd/csrc/kernels/rerotate.hip"],
+    "build_kda": ["segment_scan_amd/csrc/kernels/build_kda.hip"],
 }
 
 
@@ -76,6 +79,7 @@ KERNEL_SYMBOLS = {
     "seam": ["seam_prep_kernel", "chain_kernel"],
     "compose": ["chain_kernel", "compose_elem_kernel"],
     "rerotate": ["rerotate_kernel"],
+    "build_kda": ["build_kda_kernel"],
 }
 CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
 CALIBRATION_BYTES = 1 << 30  # each reads and writes this many bytes
@@ -164,6 +168,7 @@ class ColdRequest(Workload):
     """GDN dense transition, one 32k-token cold request (32 heads, 64 x 512, bf16)."""
     name = "gdn_cold32k"
     kernel = "build_delta"
+    fam = 3  # delta
 
     def __init__(self):
         self.n_seg, self.L, self.H, self.d = 64, 512, 32, 128
@@ -193,32 +198,30 @@ class ColdRequest(Workload):
         self.U = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
         self.S = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
         self.S_out = torch.empty((self.H, self.d, self.d), device=dev)
-        n_ws = api.seg_build_workspace_size(synth.DELTA, self.offsets, self.H, self.d, torch.bfloat16)
+        n_ws = api.seg_build_workspace_size(self.fam, self.offsets, self.H, self.d, torch.bfloat16)
         self.ws = torch.empty(max(n_ws, 16), device=dev, dtype=torch.uint8)
-        n_cws = api.compose_workspace_size(synth.DELTA, self.n_seg, self.H, self.d)
+        n_cws = api.compose_workspace_size(self.fam, self.n_seg, self.H, self.d)
         self.cws = torch.empty(n_cws, device=dev, dtype=torch.uint8) if n_cws else None
 
     def _tokens(self):
         return self.synth.gdn_cold(want_q=False)
 
     def step(self, ev0, ev1):
-        from segment_scan_amd.synth import DELTA
         ev0.record()
-        self.api.seg_build(DELTA, self.offsets, self.k, self.v, self.beta, self.lg, out=(self.g, self.U, self.S),
+        self.api.seg_build(self.fam, self.offsets, self.k, self.v, self.beta, self.lg, out=(self.g, self.U, self.S),
                            workspace=self.ws)
         ev1.record()
-        self.api.compose(DELTA, self.g, self.U, self.S, S_out=self.S_out, workspace=self.cws)
+        self.api.compose(self.fam, self.g, self.U, self.S, S_out=self.S_out, workspace=self.cws)
 
     def cpu_sample(self):
         import oracle
-        from segment_scan_amd.synth import DELTA
         ns = self.n_seg  # the whole request: every segment and head, built and composed
         t1 = int(self.tk.offsets[ns])
         sl = slice(0, t1)
         t = time.perf_counter()
-        g, U, S = oracle.build_pairs(DELTA, self.tk.offsets[:ns + 1], self.tk.k[sl], self.tk.v[sl],
+        g, U, S = oracle.build_pairs(self.fam, self.tk.offsets[:ns + 1], self.tk.k[sl], self.tk.v[sl],
                                      self.tk.beta[sl], self.tk.log_gate[sl])
-        oracle.compose(DELTA, g, U, S)
+        oracle.compose(self.fam, g, U, S)
         dt = time.perf_counter() - t
         return dt, ns * self.L, "whole request (64 segments x 32 heads = 2048 units): build + ordered compose"
 
@@ -249,6 +252,34 @@ class RaggedRequest(ColdRequest):
         c = super().config()
         c.update(workload=self.name, segment_len="58..2048 (log-normal, median 366)",
                  step="hypic_seg_build (2048 ragged units, longest first) + hypic_compose (32 chains x 64)")
+        return c
+
+
+class KdaRequest(ColdRequest):
+    """KDA (delta rule with per-channel gates) at the cold request's shape: 32 heads,
+    64 x 512 tokens, d = 128, bf16 tokens and per-channel gates."""
+    name = "kda_cold32k"
+    kernel = "build_kda"
+    fam = 4  # kda
+
+    def __init__(self):
+        super().__init__()
+        units = self.n_seg * self.H
+        # per token: k, v and the d channel gates (bf16) and beta
+        self.alg_bytes = units * _build_bytes(4, self.L, self.d, 2, 2 * self.d + 2, True)
+        # executed MFMAs per 64-token chunk and unit (32x32x16, two bf16 terms per
+        # operand = 3 products each): Gram 2 tiles x 8 k-steps; per wave and 32-column
+        # tile Kb Z 4 x 2 x 2, X R 3 x 2, Kd W 2 x 2 x 4; 4 waves x 2 tiles
+        chunks = units * (self.L // 64)
+        self.exec_flops = chunks * 3 * (2 * 8 + 8 * (16 + 6 + 16)) * 32 * 32 * 16 * 2.0
+
+    def _tokens(self):
+        return self.synth.kda()
+
+    def config(self):
+        c = super().config()
+        c.update(workload=self.name, family="kda", gates="per token and key channel (bf16)",
+                 step="hypic_seg_build (2048 KDA units) + hypic_compose (32 chains x 64)")
         return c
 
 
@@ -446,6 +477,7 @@ WORKLOADS = {
     "gdn_warm100k": WarmRequest,
     "gdn_ragged32k": RaggedRequest,
     "gdn_warm100k_rerotate": WarmRerotate,
+    "kda_cold32k": KdaRequest,
 }
 
 

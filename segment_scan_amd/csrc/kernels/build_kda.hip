@@ -50,12 +50,15 @@ struct KdaCfg {
   static constexpr int NRT = D / 32;          // row tiles of the state
   static constexpr int CT = D / 64;           // 32-column tiles per wave (d/2 columns)
   static constexpr int CPW = D / 2;
-  static constexpr int FP = D + 4;            // pitch of the staged keys and gate prefixes [t][d]
+  static constexpr int FP = D + 8;            // pitch of the staged keys and gate prefixes [t][d]
+                                              // (rows 16-byte aligned for vector reads)
   static constexpr int KP = D + 4;            // bf16 pitch of Kb [t][d]
   static constexpr int TP = C + 4;            // bf16 pitch of Kd [d][t] and of X [t][t']
   static constexpr int NP = 65;               // fp32 pitch of the Gram / inverse array
   using KT = typename std::conditional<IN_F32, float, bf16_t>::type;  // staged keys (exact)
   static constexpr int KF_BYTES = (C * FP * (int)sizeof(KT) + 15) / 16 * 16;
+  static constexpr int VP = D + 8;            // pitch of the staged values [t][d]
+  static constexpr int V_BYTES = (C * VP * (int)sizeof(KT) + 15) / 16 * 16;
   static constexpr int G_BYTES = C * FP * 4;
   static constexpr int KB_BYTES = NTK * C * KP * 2;
   static constexpr int KD_BYTES = NTK * D * TP * 2;
@@ -64,7 +67,8 @@ struct KdaCfg {
   static constexpr int A_BYTES = ((A_BYTES_BF > N_BYTES ? A_BYTES_BF : N_BYTES) + 15) / 16 * 16;
   static constexpr int T_BYTES = 3 * 16 * 17 * 4;  // block-row scratch of the inverse
   static constexpr int OFF_KF = 0;
-  static constexpr int OFF_G = OFF_KF + KF_BYTES;
+  static constexpr int OFF_V = OFF_KF + KF_BYTES;
+  static constexpr int OFF_G = OFF_V + V_BYTES;
   static constexpr int OFF_KB = OFF_G + G_BYTES;
   static constexpr int OFF_KD = OFF_KB + KB_BYTES;
   static constexpr int OFF_A = OFF_KD + KD_BYTES;
@@ -77,18 +81,33 @@ struct KdaCfg {
 };
 
 // Key channels c0 .. c0+7 of token t decayed against token `ref` in the
-// shifted prefixes H = G - mu: k * exp(H_t - H_ref) (toward = true) or
+// shifted prefixes H: k * exp(H_t - H_ref) (toward = true) or
 // k * exp(H_ref - H_t), split into NT terms.
-template <int NT, typename KT>
-__device__ __forceinline__ Frag<NT> decayed_frag(const KT* sKf, const float* sG, const float* sMu, int FP, int t,
-                                                 int ref, int c0, bool toward) {
-  const float dmu = sMu[t] - sMu[ref];
-  float x[8];
+// Eight consecutive staged keys as floats (one 16-byte LDS read for bf16).
+__device__ __forceinline__ void lds_keys8(const bf16_t* p, float (&x)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float d = (sG[t * FP + c0 + j] - sG[ref * FP + c0 + j]) - dmu;
-    x[j] = (float)sKf[t * FP + c0 + j] * __expf(toward ? d : -d);
+  for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+}
+__device__ __forceinline__ void lds_keys8(const float* p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a[j];
+    x[4 + j] = b[j];
   }
+}
+__device__ __forceinline__ void lds_f8(const float* p, float (&x)[8]) { lds_keys8(p, x); }
+
+template <int NT, typename KT>
+__device__ __forceinline__ Frag<NT> decayed_frag(const KT* sKf, const float* sH, int FP, int t, int ref, int c0,
+                                                 bool toward) {
+  float k[8], ht[8], hr[8], x[8];
+  lds_keys8(sKf + t * FP + c0, k);
+  lds_f8(sH + t * FP + c0, ht);
+  lds_f8(sH + ref * FP + c0, hr);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = k[j] * __expf(toward ? ht[j] - hr[j] : hr[j] - ht[j]);
   return split8<NT>(x);
 }
 
@@ -113,13 +132,14 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   using Cfg = KdaCfg<D, IN_F32>;
   using KT = typename Cfg::KT;
   constexpr int NTK = Cfg::NTK, NTD = Cfg::NTD, NRT = Cfg::NRT, CT = Cfg::CT, CPW = Cfg::CPW;
-  constexpr int FP = Cfg::FP, KP = Cfg::KP, TP = Cfg::TP, NP = Cfg::NP;
+  constexpr int FP = Cfg::FP, KP = Cfg::KP, TP = Cfg::TP, NP = Cfg::NP, VP = Cfg::VP;
   constexpr int KBS = C * KP;  // term stride (elements) of Kb
   constexpr int KDS = D * TP;  // term stride of Kd
   constexpr int ATS = C * TP;  // term stride of X
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   KT* sKf = reinterpret_cast<KT*>(smem + Cfg::OFF_KF);
+  KT* sV = reinterpret_cast<KT*>(smem + Cfg::OFF_V);
   float* sG = reinterpret_cast<float*>(smem + Cfg::OFF_G);
   bf16_t* sKb = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KB);
   bf16_t* sKd = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KD);
@@ -167,144 +187,163 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    // ---- stage keys and per-channel log gates (zero past the segment end) ------
-    // and each token's largest gate (its D/8 channel groups are consecutive lanes)
-    static_assert((C * (D / 8)) % 256 == 0, "every lane runs every staging step");
-    for (int it = tid; it < C * (D / 8); it += 256) {
-      const int t = it / (D / 8), db = it % (D / 8);
-      float x[8], lg[8];
-      if (t < nv) {
-        const size_t idx = ((size_t)(c0 + t) * n_chain + chain) * D + db * 8;
-        load8<IN_F32>(a.k, idx, x);
-        load8<IN_F32>(a.lg, idx, lg);
-      } else {
+    // ---- stage keys, values and per-channel log gates (zero past the segment
+    // end) and each token's largest gate (its D/8 channel groups are consecutive
+    // lanes); every load of the chunk is issued before the first store
+    constexpr int NIT = C * (D / 8) / 256;
+    static_assert(NIT * 256 == C * (D / 8), "every lane runs every staging step");
+    {
+      float x[NIT][8], lg[NIT][8], vx[NIT][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = lg[j] = 0.f;
+      for (int k = 0; k < NIT; ++k) {
+        const int it = tid + 256 * k;
+        const int t = it / (D / 8), db = it % (D / 8);
+        if (t < nv) {
+          const size_t idx = ((size_t)(c0 + t) * n_chain + chain) * D + db * 8;
+          load8<IN_F32>(a.k, idx, x[k]);
+          load8<IN_F32>(a.lg, idx, lg[k]);
+          load8<IN_F32>(a.v, idx, vx[k]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[k][j] = lg[k][j] = vx[k][j] = 0.f;
+        }
       }
-      float mx = lg[0];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sKf[t * FP + db * 8 + j] = (KT)x[j];
-        sG[t * FP + db * 8 + j] = lg[j];
-        mx = fmaxf(mx, lg[j]);
+      for (int k = 0; k < NIT; ++k) {
+        const int it = tid + 256 * k;
+        const int t = it / (D / 8), db = it % (D / 8);
+        float mx = lg[k][0];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sKf[t * FP + db * 8 + j] = (KT)x[k][j];
+          sV[t * VP + db * 8 + j] = (KT)vx[k][j];
+          sG[t * FP + db * 8 + j] = lg[k][j];
+          mx = fmaxf(mx, lg[k][j]);
+        }
+#pragma unroll
+        for (int o = 1; o < D / 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if (db == 0) sMax[t] = mx;
       }
-#pragma unroll
-      for (int o = 1; o < D / 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      if (db == 0) sMax[t] = mx;
     }
     if (tid < C) sBeta[tid] = (tid < nv) ? load1<IN_F32>(a.beta, (size_t)(c0 + tid) * n_chain + chain) : 0.f;
     __syncthreads();
 
-    // ---- per-channel inclusive prefix G (one thread per channel) --------------
+    // ---- per-channel prefixes (one thread per channel): G_C, and in place of
+    // the gates H_t = G_t - mu_t, with mu_t (the same in every thread: the
+    // same sums in the same order) recorded by thread 0
     if (tid < D) {
-      float lgc[C];
+      float lgc[C], mxs[C];
 #pragma unroll
-      for (int t = 0; t < C; ++t) lgc[t] = sG[t * FP + tid];
-      float acc = 0.f;
+      for (int t = 0; t < C; ++t) {
+        lgc[t] = sG[t * FP + tid];
+        mxs[t] = sMax[t];
+      }
+      float acc = 0.f, mu = 0.f;
 #pragma unroll
       for (int t = 0; t < C; ++t) {
         acc += lgc[t];
-        sG[t * FP + tid] = acc;
+        mu += mxs[t];
+        sG[t * FP + tid] = acc - mu;
+        if (tid == 0) sMu[t] = mu;
       }
       sGC[tid] = acc;
-    }
-    if (wave == 3) {  // mu_t (free wave: the scan uses at most waves 0-1)
-      const float mu = wave_incl_scan(sMax[lane]);
-      sMu[lane] = mu;
-      const float muC = __shfl(mu, 63, 64);
-      sVf[lane] = __expf(muC - mu);
-      if (lane == 0) {
-        sMisc[0] = muC;
-        sMisc[1] = __expf(muC);
+      if (tid == 0) {
+        sMisc[0] = mu;
+        sMisc[1] = __expf(mu);
       }
     }
     __syncthreads();
 
-    // ---- Gram M0[i][j] = b_i sum_c k_ic k_jc exp(G_ic - G_jc), i > j -----------
-    if (wave == 0) {
-      g_acc += (double)sMisc[0];  // mu_C; every lane of wave 0 keeps the same sum
-      // rows 32..63 against columns 0..31, both decayed against token 31
+    // ---- Gram M[i][j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc), i > j ------------
+    // Waves 0-2: one 32 x 32 MFMA tile each of products of decayed keys, both
+    // factors decayed against a reference token between the row and the column
+    // tokens (so both are <= |k|); parts of a tile whose row and column refer to
+    // different references are discarded (their factors are <= |k| as well):
+    //   wave 0: rows 32..63 x columns 0..31, reference 31
+    //   wave 1: rows 16a+16..16a+31 x columns 16a..16a+15 (a = 0, 2 in 16-row
+    //           halves), references 15 and 47
+    //   wave 2: rows 16a+8..16a+15 x columns 16a..16a+7 (a = 0..3), references 16a+7
+    if (wave == 0) g_acc += (double)sMisc[0];  // mu_C; every lane of wave 0 keeps the same sum
+    if (wave < 3) {
+      int ra, rb, ref;
+      if (wave == 0) {
+        ra = 32 + l32;
+        rb = l32;
+        ref = 31;
+      } else if (wave == 1) {
+        ra = l32 < 16 ? 16 + l32 : 32 + l32;
+        rb = l32 < 16 ? l32 : 16 + l32;
+        ref = l32 < 16 ? 15 : 47;
+      } else {
+        const int qa = l32 >> 3;
+        ra = 16 * qa + 8 + (l32 & 7);
+        rb = 16 * qa + (l32 & 7);
+        ref = 16 * qa + 7;
+      }
       f32x16 acc = zero16();
 #pragma unroll 2
       for (int ks = 0; ks < D / 16; ++ks) {
         const int cc = 16 * ks + 8 * h;
-        const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, sMu, FP, 32 + l32, 31, cc, true);
-        const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, sMu, FP, l32, 31, cc, false);
-        mma<NTK, NTK>(acc, fa, fb);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 + acc_row(r, lane);
-        sN[i * NP + l32] = sBeta[i] * acc[r];
-      }
-    } else if (wave == 1) {
-      // rows 16..31 against columns 0..15 (reference token 15) and rows 48..63
-      // against columns 32..47 (reference token 47), as one 32 x 32 tile whose
-      // two cross quadrants are discarded (their factors are <= 1 as well)
-      const int ra = l32 < 16 ? 16 + l32 : 32 + l32;
-      const int rb = l32 < 16 ? l32 : 16 + l32;
-      const int ref = l32 < 16 ? 15 : 47;
-      f32x16 acc = zero16();
-#pragma unroll 2
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int cc = 16 * ks + 8 * h;
-        const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, sMu, FP, ra, ref, cc, true);
-        const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, sMu, FP, rb, ref, cc, false);
+        const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, FP, ra, ref, cc, true);
+        const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, rb, ref, cc, false);
         mma<NTK, NTK>(acc, fa, fb);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rho = acc_row(r, lane);
-        if ((rho < 16) == (l32 < 16)) {
-          const int i = rho < 16 ? 16 + rho : 32 + rho;
-          sN[i * NP + rb] = sBeta[i] * acc[r];
+        int i;
+        bool keep;
+        if (wave == 0) {
+          i = 32 + rho;
+          keep = true;
+        } else if (wave == 1) {
+          i = rho < 16 ? 16 + rho : 32 + rho;
+          keep = (rho < 16) == (l32 < 16);
+        } else {
+          i = 16 * (rho >> 3) + 8 + (rho & 7);
+          keep = (rho >> 3) == (l32 >> 3);
+        }
+        if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
+      }
+    }
+    // The eight 8-token diagonal blocks term by term, two per wave; lane =
+    // (block, row i, channel quarter q).  Every lane reads every column token
+    // (straight-line loads); terms with j >= i are masked.
+    {
+      const int q = lane & 3, i = (lane >> 2) & 7;
+      const int b0 = 8 * (2 * wave + (lane >> 5));
+      const int ti = b0 + i;
+      constexpr int QC = D / 4;
+      float acc[7];
+#pragma unroll
+      for (int j = 0; j < 7; ++j) acc[j] = 0.f;
+#pragma unroll 1
+      for (int cc = 0; cc < QC; cc += 8) {
+        const int c = q * QC + cc;
+        float ki[8], hi[8];
+        lds_keys8(sKf + ti * FP + c, ki);
+        lds_f8(sG + ti * FP + c, hi);
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+          float kj[8], hj[8];
+          lds_keys8(sKf + (b0 + j) * FP + c, kj);
+          lds_f8(sG + (b0 + j) * FP + c, hj);
+          float term = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) term = fmaf(ki[e] * kj[e], __expf(hi[e] - hj[e]), term);
+          acc[j] += (j < i) ? term : 0.f;
         }
       }
-    } else {
-      // the four 16-token diagonal blocks, term by term: wave 2 blocks 0-1,
-      // wave 3 blocks 2-3; lane = (row i, channel quarter q)
-      const int i = lane & 15, q = lane >> 4;
-      constexpr int QC = D / 4;
-#pragma unroll 1
-      for (int bb = 0; bb < 2; ++bb) {
-        const int b0 = 16 * (2 * (wave - 2) + bb);
-        const int ti = b0 + i;
-        const float mui = sMu[ti];
-        float acc[15];
 #pragma unroll
-        for (int j = 0; j < 15; ++j) acc[j] = 0.f;
-#pragma unroll 1
-        for (int cc = 0; cc < QC; cc += 4) {
-          const int c = q * QC + cc;
-          float ki[4], gi[4];
+      for (int j = 0; j < 7; ++j) {
+        acc[j] += __shfl_xor(acc[j], 1, 64);
+        acc[j] += __shfl_xor(acc[j], 2, 64);
+      }
+      if (q == 0) {
+        const float bi = sBeta[ti];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ki[e] = (float)sKf[ti * FP + c + e];
-            gi[e] = sG[ti * FP + c + e] - mui;
-          }
-#pragma unroll
-          for (int j = 0; j < 15; ++j) {
-            if (j < i) {
-              const int tj = b0 + j;
-              const float muj = sMu[tj];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                acc[j] = fmaf(ki[e] * (float)sKf[tj * FP + c + e], __expf(gi[e] - (sG[tj * FP + c + e] - muj)),
-                              acc[j]);
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 15; ++j) {
-          acc[j] += __shfl_xor(acc[j], 16, 64);
-          acc[j] += __shfl_xor(acc[j], 32, 64);
-        }
-        if (q == 0) {
-          const float bi = sBeta[ti];
-#pragma unroll
-          for (int j = 0; j < 15; ++j)
-            if (j < i) sN[ti * NP + b0 + j] = bi * acc[j];
-        }
+        for (int j = 0; j < 7; ++j)
+          if (j < i) sN[ti * NP + b0 + j] = bi * acc[j];
       }
     }
     __syncthreads();
@@ -377,20 +416,19 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
     if (tid < 16 * (D / 8)) {
       // tokens 4*tq .. 4*tq+3, channels 8*db .. 8*db+7
       const int tq = tid & 15, db = tid >> 4;
-      const float muC = sMisc[0];
+      float hC[8];
+      lds_f8(sG + (C - 1) * FP + 8 * db, hC);
       float kd[8][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * tq + r;
-        const float mut = sMu[t];
-        float kb[8];
+        float kv[8], hv[8], kb[8];
+        lds_keys8(sKf + t * FP + 8 * db, kv);
+        lds_f8(sG + t * FP + 8 * db, hv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int c = 8 * db + j;
-          const float kv = (float)sKf[t * FP + c];
-          const float hv = sG[t * FP + c] - mut;  // H_t
-          kb[j] = kv * __expf(hv);
-          kd[j][r] = kv * __expf((sGC[c] - muC) - hv);
+          kb[j] = kv[j] * __expf(hv[j]);
+          kd[j][r] = kv[j] * __expf(hC[j] - hv[j]);
         }
         const Frag<NTK> f = split8<NTK>(kb);
 #pragma unroll
@@ -403,6 +441,7 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
       sRS[tid] = __expf(sGC[tid]);
       sRU[tid] = __expf(sGC[tid] - sMisc[0]);
     }
+    if (tid < C) sVf[tid] = __expf(sMisc[0] - sMu[tid]);
     __syncthreads();
 
     // ---- per wave: Y = Kb Z, W = X R, Z = diag(row factor) Z + Kd W -------------
@@ -415,18 +454,6 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int gcol = col0 + 32 * ct + l32;
-        using VT = typename std::conditional<IN_F32, float, bf16_t>::type;
-        VT vv[2][16];
-        if (s_wave) {
-          const VT* vsrc = reinterpret_cast<const VT*>(a.v) + ((size_t)c0 * n_chain + chain) * D + gcol;
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int t = 32 * tt + acc_row(r, lane);
-              vv[tt][r] = (t < nv) ? vsrc[(size_t)t * n_chain * D] : (VT)0.f;
-            }
-        }
         // Y[tt] = Kb[tt rows] * Z[:, ct]
         f32x16 Y[2] = {zero16(), zero16()};
 #pragma unroll
@@ -445,7 +472,8 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
           for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              Y[tt][r] = sVf[32 * tt + acc_row(r, lane)] * (float)vv[tt][r] - emuC * Y[tt][r];
+              Y[tt][r] = sVf[32 * tt + acc_row(r, lane)] * (float)sV[(32 * tt + acc_row(r, lane)) * VP + gcol] -
+                         emuC * Y[tt][r];
         }
         // W[tt] = sum_{tp <= tt} X[tt, tp] Y[tp]  (X lower triangular)
         f32x16 W[2] = {zero16(), zero16()};
