@@ -30,9 +30,10 @@
  *    output is o_t = S_t^T q_t, taken after the token's own update.  Layers and
  *    heads are folded into one "chain" index (chain = layer * heads + head).
  *  - Supported sizes: d_k = d_v = d with d in {64, 128}.  Other sizes return
- *    HYPIC_E_UNSUPPORTED.  The KDA build is built for d = 64 and for d = 128
- *    with bf16 tokens; the seam step and the re-rotation are not built for KDA
- *    (HYPIC_E_UNSUPPORTED); its pairs compose like DELTA pairs.
+ *    HYPIC_E_UNSUPPORTED.  The KDA build (and the KDA seam step's optional
+ *    window pairs) is built for d = 64 and for d = 128 with bf16 tokens; the
+ *    re-rotation is not defined for KDA (HYPIC_E_UNSUPPORTED); KDA pairs
+ *    compose like DELTA pairs.
  *  - Token tensors are token-major, [n_tok, n_chain, d] (d contiguous);
  *    per-token scalars are [n_tok, n_chain].
  *

@@ -230,7 +230,7 @@ def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chai
         o_out = torch.empty((n_tok, n_chain, v.shape[2]), device=dev, dtype=torch.float32)
     if want_window_pairs and window_out is None:
         window_out = (torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32),
-                      torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam == DELTA else None,
+                      torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam in DENSE else None,
                       torch.empty((n_seg, n_chain, d, v.shape[2]), device=dev, dtype=torch.float32))
     if workspace is None:
         need = seam_step_workspace_size(fam, n_seg, w, n_chain, d)

@@ -384,7 +384,6 @@ hypic_status hypic_seam_step_workspace_size(hypic_family fam, int n_seg, int w, 
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   if (w < 1) return fail(HYPIC_E_INVALID, "w must be >= 1 (got %d)", w);
   if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
-  if (fam == HYPIC_KDA) return fail(HYPIC_E_UNSUPPORTED, "the seam step is not built for the KDA family");
   *bytes = fam == HYPIC_DELTA ? hypic::seam_workspace_bytes(n_seg, w, n_chain) : 0;
   return ok();
 }
@@ -396,7 +395,6 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
   const int d = d_k;
   if (w < 1) return fail(HYPIC_E_INVALID, "w must be >= 1 (got %d)", w);
-  if (fam == HYPIC_KDA) return fail(HYPIC_E_UNSUPPORTED, "the seam step is not built for the KDA family");
   std::vector<Range> ins, outs;
   const size_t n_tok = (size_t)n_seg * w;
   TRY(check_tokens(fam, seam, n_tok, n_chain, d, true, &ins));
@@ -409,8 +407,12 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
   outs.push_back({o_out, n_tok * n_chain * d * 4, "o_out"});
   if (window_out) {
     if (!window_out->S || !window_out->g) return fail(HYPIC_E_INVALID, "window_out needs S and g");
-    if (fam == HYPIC_DELTA && !window_out->U) return fail(HYPIC_E_INVALID, "window_out.U is required for delta");
-    if (fam != HYPIC_DELTA && window_out->U) return fail(HYPIC_E_INVALID, "window_out.U is only defined for delta");
+    if (dense(fam) && !window_out->U)
+      return fail(HYPIC_E_INVALID, "window_out.U is required for the delta and KDA families");
+    if (!dense(fam) && window_out->U)
+      return fail(HYPIC_E_INVALID, "window_out.U is only defined for the delta and KDA families");
+    if (fam == HYPIC_KDA && !hypic::kda_build_supported(d, seam->dtype == HYPIC_F32))
+      return fail(HYPIC_E_UNSUPPORTED, "KDA window pairs are built for d = 64 and for d = 128 with bf16 tokens");
     TRY(check_aligned(window_out->S, "window_out.S"));
     if (window_out->g) TRY(check_aligned(window_out->g, "window_out.g"));
     if (window_out->U) TRY(check_aligned(window_out->U, "window_out.U"));
@@ -456,6 +458,8 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
     if (e != hipSuccess) return hip_fail(e, "hypic_seam_step window factor launch");
     a.wrec = rec;
     e = hypic::launch_seam_chain(d, f32, a, (hipStream_t)stream);
+  } else if (fam == HYPIC_KDA) {
+    e = hypic::launch_seam_kda(d, f32, a, (hipStream_t)stream);
   } else {
     e = hypic::launch_seam_elem(fam, d, f32, a, (hipStream_t)stream);
   }
@@ -479,6 +483,7 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
       const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
       fill_seg_table(&b.seg, woff.data(), s0, ns);
       e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta_single(d, f32, b, ns * n_chain, (hipStream_t)stream)
+          : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, b, ns * n_chain, (hipStream_t)stream)
                                : hypic::launch_build_sd(fam, d, f32, b, ns * n_chain, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "hypic_seam_step window pairs launch");
     }

@@ -109,6 +109,8 @@ hipError_t launch_seam_elem(int fam, int d, bool in_f32, const SeamArgs& a, hipS
 // d = 64 (bf16 or fp32 tokens) and d = 128 (bf16 tokens).
 bool kda_build_supported(int d, bool in_f32);
 hipError_t launch_build_kda(int d, bool in_f32, const BuildArgs& a, int n_blocks, hipStream_t stream);
+// seam step of the KDA family (seam_kda.hip): no workspace
+hipError_t launch_seam_kda(int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 // rotary re-rotation of n_seg x n_chain pairs in place (rerotate.hip): S <- R S,
 // and U <- R U R^T when U is not NULL; pos: device [n_seg].
 hipError_t launch_rerotate(int d, float* S, float* U, const int32_t* pos, int n_seg, int n_chain, double base,

@@ -130,8 +130,8 @@ def test_piece_split_workspace_size(lib):
 
 
 def test_kda_workspace_sizes(lib):
-    """The KDA build takes no workspace; its dense composition takes the delta
-    family's; its seam step is not built."""
+    """The KDA build and seam step take no workspace; its dense composition
+    takes the delta family's."""
     assert ws_size(lib, fam=KDA) == (0, 0)
     assert ws_size(lib, fam=KDA, d=64, dtype=F32) == (0, 0)
     for want_prefix in (0, 1):
@@ -139,8 +139,9 @@ def test_kda_workspace_sizes(lib):
         assert lib.hypic_compose_workspace_size(KDA, 64, 32, 128, 128, want_prefix, ctypes.byref(a)) == 0
         assert lib.hypic_compose_workspace_size(DELTA, 64, 32, 128, 128, want_prefix, ctypes.byref(b)) == 0
         assert a.value == b.value > 0
-    out = ctypes.c_size_t(0)
-    assert lib.hypic_seam_step_workspace_size(KDA, 4, 8, 2, 128, 128, ctypes.byref(out)) == UNSUPPORTED
+    out = ctypes.c_size_t(1)
+    assert lib.hypic_seam_step_workspace_size(KDA, 4, 8, 2, 128, 128, ctypes.byref(out)) == 0
+    assert out.value == 0
 
 
 def test_workspace_size(lib):
@@ -257,9 +258,12 @@ def seam_call(lib, fam=DELTA, n_seg=4, w=8, n_chain=2, d=128, t=None, body="defa
     (dict(fam=NAIVE, t=toks(NAIVE, q=True), body=pairs(NAIVE), win=Pairs(None, None, A["wS"])), INVALID,
      "window_out needs S and g"),
     (dict(fam=SCALAR, t=toks(SCALAR, q=True), body=pairs(SCALAR), win=Pairs(A["wg"], A["wU"], A["wS"])), INVALID,
-     "only defined for delta"),
+     "only defined for the delta"),
     (dict(d=256), UNSUPPORTED, "64, 128"),
-    (dict(fam=KDA, t=toks(KDA, q=True), body=pairs(KDA)), UNSUPPORTED, "not built for the KDA"),
+    (dict(fam=KDA, t=toks(KDA, q=True, dtype=F32), body=pairs(KDA), win=Pairs(A["wg"], A["wU"], A["wS"]),
+          ws=None, ws_bytes=0), UNSUPPORTED, "KDA window pairs"),
+    (dict(fam=KDA, t=toks(KDA, q=True), body=pairs(KDA), win=Pairs(A["wg"], None, A["wS"])), INVALID,
+     "window_out.U is required"),
     (dict(ws=None), INVALID, "workspace is NULL"),
     (dict(ws_bytes=1024), INVALID, "workspace too small"),
     (dict(ws=A["ws"] + 8), INVALID, "workspace is not 16-byte aligned"),

@@ -105,3 +105,33 @@ def test_kda_cold_full_size_sampled_units():
                                         sub.beta[t0:t1], sub.log_gate[t0:t1])
         compare("full(%d,%d)" % (s, hh), g[s:s + 1, hh:hh + 1], U[s:s + 1, hh:hh + 1], S[s:s + 1, hh:hh + 1],
                 rg, rU, rS, TOL["bf16"])
+
+
+def test_kda_seam_with_built_bodies_equals_sequential():
+    """Warm reuse of a KDA layer end to end on the GPU: bodies built by the KDA
+    build, then the seam step (window tokens on the running state, then each
+    body pair) against straight recurrence over [window_0, body_0, window_1, ...]."""
+    import torch
+    n_seg, w, L, H = 5, 8, 100, 3
+    tw = synth.kda(n_seg=n_seg, L=w, n_chain=H, gate_scale=1.0 / 32, want_q=True)
+    tb = synth.kda(n_seg=n_seg, L=L, n_chain=H, gate_scale=1.0 / 32)
+    tb.k, tb.v, tb.beta, tb.log_gate = tb.k[::-1].copy(), tb.v[::-1].copy(), tb.beta[::-1].copy(), \
+        tb.log_gate[::-1].copy()  # other tokens than the windows'
+    announce("kda_seam_e2e")
+    db = upload_tokens(tb)
+    body = api.seg_build(KDA, list(tb.offsets), db["k"], db["v"], db["beta"], db["log_gate"])
+    dw = upload_tokens(tw, with_q=True)
+    res = api.seam_step(KDA, w, dw["q"], dw["k"], dw["v"], dw["beta"], dw["log_gate"], body=body)
+    torch.cuda.synchronize()
+    order = []
+    for s in range(n_seg):
+        order += [("w", s * w + j) for j in range(w)]
+        order += [("b", t) for t in range(tb.offsets[s], tb.offsets[s + 1])]
+    cat = lambda key: np.stack([getattr(tw if src == "w" else tb, key)[i] for src, i in order])
+    q = np.stack([tw.q[i] if src == "w" else np.zeros_like(tw.q[0]) for src, i in order])  # bodies emit nothing
+    Sseq, oseq = oracle.sequential(KDA, cat("k"), cat("v"), cat("beta"), cat("log_gate"), q=q)
+    assert_units_close("kda_seam_e2e.S", host(res["S_run"]), Sseq, TOL["bf16"], unit_dims=1)
+    wpos = [p for p, (src, _) in enumerate(order) if src == "w"]
+    ow = host(res["o"]).reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
+    rw = oseq[wpos].reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
+    assert_units_close("kda_seam_e2e.o", ow, rw, TOL["bf16"])

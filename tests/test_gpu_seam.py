@@ -127,6 +127,8 @@ def _family_tokens(kind, n_seg, L, n_chain, d=128, dtype="bf16"):
         return synth.mamba2_like(n_seg=n_seg, L=L, n_chain=n_chain, d=d, dtype=dtype)
     if kind == "gla":
         return synth.gla(n_seg=n_seg, L=L, n_chain=n_chain, d=d, dtype=dtype)
+    if kind == "kda":
+        return synth.kda(n_seg=n_seg, L=L, n_chain=n_chain, d=d, dtype=dtype, want_q=True)
     return synth.warm_seam_layer(11, n_seg=n_seg, w=L, n_head=n_chain, d=d, dtype=dtype, gate_scale=1.0 / 16)
 
 
@@ -158,13 +160,13 @@ def _check_family_seam(kind, w, d, dtype, tol):
         assert_units_close(kind + ".wU", host(res["wU"]), ref["wU"], tol)
 
 
-@pytest.mark.parametrize("kind", ["naive", "retnet", "mamba2", "gla", "gdn"])
+@pytest.mark.parametrize("kind", ["naive", "retnet", "mamba2", "gla", "gdn", "kda"])
 @pytest.mark.parametrize("w", [8, 13])
 def test_seam_every_family_with_window_pairs(kind, w):
     """Window recurrence + body pairs of every family, and each window's own pair."""
     _check_family_seam(kind, w, 128, "bf16", TOL["bf16"])
 
 
-@pytest.mark.parametrize("kind", ["retnet", "gla", "gdn"])
+@pytest.mark.parametrize("kind", ["retnet", "gla", "gdn", "kda"])
 def test_seam_families_fp32_d64(kind):
     _check_family_seam(kind, 5, 64, "f32", TOL["f32"])
