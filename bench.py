@@ -17,6 +17,7 @@ accumulation -- every (segment, head) pair (T_C, S(C|0)) built concurrently
                 to new offsets
   kda_cold32k   the cold request's shape with KDA (per-channel gated delta rule):
                 build + compose
+  kda_warm100k  the warm request with KDA layers: seam step
 Prints one JSON line.  `value` is segment-tokens/s of the whole step; the
 `roofline` object is for the step's dominant kernel, timed with HIP events on
 the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
@@ -48,6 +49,7 @@ KERNEL_SOURCES = {
     "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
     "rerotate": ["segment_scan_amd/csrc/kernels/rerotate.hip"],
     "build_kda": ["segment_scan_amd/csrc/kernels/build_kda.hip"],
+    "seam_kda": ["segment_scan_amd/csrc/kernels/seam_kda.hip"],
 }
 
 
@@ -80,6 +82,7 @@ KERNEL_SYMBOLS = {
     "compose": ["chain_kernel", "compose_elem_kernel"],
     "rerotate": ["rerotate_kernel"],
     "build_kda": ["build_kda_kernel"],
+    "seam_kda": ["seam_kda_kernel"],
 }
 CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
 CALIBRATION_BYTES = 1 << 30  # each reads and writes this many bytes
@@ -416,6 +419,59 @@ class WarmRequest(Workload):
                 "step": "hypic_seam_step over 480 chains (seam windows + body-pair composition)"}
 
 
+class KdaWarmRequest(WarmRequest):
+    """The warm 100k-token request with KDA layers: 30 layers x 16 heads, 196 cached
+    segments, w = 8, window gates per token and key channel."""
+    name = "kda_warm100k"
+    kernel = "seam_kda"
+
+    def __init__(self):
+        super().__init__()
+        d, n = self.d, self.chains
+        ntok = self.n_seg * self.w
+        # as the GDN warm request plus the per-channel window gates (bf16)
+        self.alg_bytes += ntok * n * (2 * d - 2)
+        # body products on MFMA in two bf16 terms (three products); windows on the VALU
+        self.exec_flops = self.n_seg * n * 3 * 2.0 * d ** 3
+
+    def setup(self):
+        import torch
+        super().setup()
+        gen = torch.Generator(device="cuda").manual_seed(20260703)
+        nt, n, d = self.n_seg * self.w, self.chains, self.d
+        f = torch.nn.functional
+        self.lg = (-f.softplus(torch.randn((nt, n, d), device="cuda", generator=gen)) / 8).to(torch.bfloat16)
+        self.ws = None
+
+    def step(self, ev0, ev1):
+        from segment_scan_amd.synth import KDA
+        self.S_run.zero_()
+        ev0.record()
+        self.api.seam_step(KDA, self.w, self.q, self.k, self.v, self.beta, self.lg, body=(self.g, self.U, self.S),
+                           S_run=self.S_run, o_out=self.o)
+        ev1.record()
+
+    def cpu_sample(self):
+        import oracle
+        from segment_scan_amd import synth
+        from segment_scan_amd.synth import KDA
+        n_layers = 2
+        dt = 0.0
+        for layer in range(n_layers):
+            tk = synth.kda(n_seg=self.n_seg, L=self.w, n_chain=self.H, want_q=True)
+            body = synth.warm_pairs_layer(layer)
+            t = time.perf_counter()
+            oracle.seam(KDA, self.n_seg, self.w, tk.q, tk.k, tk.v, tk.beta, tk.log_gate, body=body)
+            dt += time.perf_counter() - t
+        return dt, self.tokens * n_layers / self.layers, "layers 0-1 of 30 in full (seam + compose), scaled"
+
+    def config(self):
+        c = super().config()
+        c.update(workload=self.name, family="kda",
+                 step="hypic_seam_step (KDA) over 480 chains (seam windows + body-pair composition)")
+        return c
+
+
 class WarmRerotate(Workload):
     """Rotary re-rotation of the warm 100k-token request's cached pairs (30 GDN
     layers x 16 heads x 196 segments, d = 128, fp32 U and S) to new offsets."""
@@ -478,6 +534,7 @@ WORKLOADS = {
     "gdn_ragged32k": RaggedRequest,
     "gdn_warm100k_rerotate": WarmRerotate,
     "kda_cold32k": KdaRequest,
+    "kda_warm100k": KdaWarmRequest,
 }
 
 
