@@ -127,7 +127,9 @@ __device__ __forceinline__ void split4_store(bf16_t* p, int term_stride, const f
   }
 }
 
-template <int D, bool IN_F32>
+// ORDERED: workgroup rows follow the launch's longest-first order (ragged
+// launches only; equal lengths use the index order without the lookup).
+template <int D, bool IN_F32, bool ORDERED>
 __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   using Cfg = KdaCfg<D, IN_F32>;
   using KT = typename Cfg::KT;
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   const int lane0 = lane_id();
   const int wave = wave_id();
   const int n_chain = a.n_chain;
-  const int s_local = a.seg.order[blockIdx.x / n_chain];  // longest segments first
+  const int s_local = ORDERED ? a.seg.order[blockIdx.x / n_chain] : (int)blockIdx.x / n_chain;
   const int chain = blockIdx.x % n_chain;
   const int t_begin = a.seg.off[s_local];
   const int t_end = a.seg.off[s_local + 1];
@@ -521,14 +523,20 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   if (wave == 0 && lane0 == 0) a.g[unit] = (float)g_acc;
 }
 
+template <int D, bool F32, bool ORDERED>
+hipError_t launch_o(const BuildArgs& a, int n_blocks, hipStream_t stream) {
+  constexpr int lds = KdaCfg<D, F32>::LDS;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&build_kda_kernel<D, F32, ORDERED>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((build_kda_kernel<D, F32, ORDERED>), dim3(n_blocks), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, bool F32>
 hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
-  constexpr int lds = KdaCfg<D, F32>::LDS;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_kda_kernel<D, F32>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((build_kda_kernel<D, F32>), dim3(n_blocks), dim3(256), lds, stream, a);
-  return hipGetLastError();
+  return seg_uniform(a.seg) ? launch_o<D, F32, false>(a, n_blocks, stream) : launch_o<D, F32, true>(a, n_blocks, stream);
 }
 
 }  // namespace

@@ -62,7 +62,11 @@ __device__ __forceinline__ void cvt8(const Raw8<IN_F32>& r, float (&x)[8]) {
   }
 }
 
-template <int FAM, int D, bool IN_F32>
+// ORDERED: workgroup rows follow the launch's longest-first order (ragged
+// launches); launches of equal-length segments use the index order directly,
+// which keeps the table lookup (and the registers it costs this register-bound
+// kernel) out of their code.
+template <int FAM, int D, bool IN_F32, bool ORDERED>
 __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
   constexpr int NTK = IN_F32 ? 3 : 2;  // bf16 terms of decay-weighted keys
   constexpr int NTV = IN_F32 ? 3 : 1;  // bf16 terms of values (bf16 inputs are exact)
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
   const int wave = wave_id();
   const int n_chain = a.n_chain;
   const int u_local = blockIdx.x;
-  const int s_local = a.seg.order[u_local / n_chain];  // longest segments first
+  const int s_local = ORDERED ? a.seg.order[u_local / n_chain] : u_local / n_chain;
   const int h = u_local % n_chain;
   const int t_begin = a.seg.off[s_local];
   const int t_end = a.seg.off[s_local + 1];
@@ -293,7 +297,10 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
 
 template <int FAM, int D, bool F32>
 hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32>), dim3(n_blocks), dim3(256), 0, stream, a);
+  if (seg_uniform(a.seg))
+    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, false>), dim3(n_blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, true>), dim3(n_blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

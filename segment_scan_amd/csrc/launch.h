@@ -22,6 +22,14 @@ struct SegTable {
 };
 static_assert(kMaxSegPerLaunch <= 256, "order entries are 8-bit");
 
+// True when every segment of the launch has the same length: the longest-first
+// order is then the index order and kernels may skip the table lookup.
+inline bool seg_uniform(const SegTable& t) {
+  for (int s = 1; s < t.n_seg; ++s)
+    if (t.off[s + 1] - t.off[s] != t.off[1] - t.off[0]) return false;
+  return true;
+}
+
 struct BuildArgs {
   const void* k;
   const void* v;
