@@ -88,12 +88,15 @@ CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
 CALIBRATION_BYTES = 1 << 30  # each reads and writes this many bytes
 
 
-def ingest_counters(workload: str, kernel: str, fetch_csv: str, write_csv: str, steps: int, cmds):
+def ingest_counters(wl, fetch_csv: str, write_csv: str, steps: int, cmds):
     """Turns two rocprofv3 --pmc runs of `bench.py --copy-calibration` (FETCH_SIZE,
     then WRITE_SIZE; counter_collection.csv files) into HBM bytes per launch of the
     timed operation, each counter scaled by what it reads for the plain 1 GiB copy
-    kernel that ends the run, and records them in profiles/traffic.json."""
+    kernel that ends the run, and records them in profiles/traffic.json.  The
+    library's dispatches are cut into steps of `wl.step_dispatches`; the first
+    `wl.op_dispatches` of each of the last `steps` steps are the timed operation."""
     import csv
+    workload, kernel = wl.name, wl.kernel
 
     def per_dispatch(path, counter):
         rows = {}
@@ -114,13 +117,19 @@ def ingest_counters(workload: str, kernel: str, fetch_csv: str, write_csv: str, 
             "calibration copies not found at the end of %s" % path
         kib_copy = float(np.median([v for _, v in cal]))
         factor = CALIBRATION_BYTES / (kib_copy * 1024.0)
-        ops = [(n, v) for n, v in disp[:-CALIBRATION_COPIES] if any(k in n for k in KERNEL_SYMBOLS[kernel])]
-        n_kern = len({n for n, _ in ops})
-        timed = ops[-steps * n_kern:]  # the timed launches (each launch = n_kern dispatches)
+        lib = [(n, v) for n, v in disp[:-CALIBRATION_COPIES] if "hypic" in n]
+        sd, od = wl.step_dispatches, wl.op_dispatches
+        assert len(lib) % sd == 0 and len(lib) // sd >= steps, \
+            "%d library dispatches in %s are not whole steps of %d" % (len(lib), path, sd)
+        timed = []
+        for i in range(len(lib) - steps * sd, len(lib), sd):
+            op = lib[i:i + od]
+            assert all(any(k in n for k in KERNEL_SYMBOLS[kernel]) for n, _ in op), [n for n, _ in op]
+            timed += op
         kib = sum(v for _, v in timed) / steps
         out[counter] = {"kib_per_launch": round(kib, 1), "copy_kib": round(kib_copy, 1),
                         "scale": round(factor, 4), "bytes_per_launch": int(kib * 1024 * factor),
-                        "dispatches_per_launch": n_kern}
+                        "dispatches_per_launch": od}
     try:
         with open(TRAFFIC_FILE) as f:
             db = json.load(f)
@@ -146,6 +155,8 @@ def to_dev(arr, dtype):
 class Workload:
     name = ""
     kernel = ""          # dominant kernel for the roofline
+    op_dispatches = 1    # library dispatches of the timed operation per step
+    step_dispatches = 1  # library dispatches per step (the timed operation first)
     tokens = 0           # segment-tokens per step
     composed = 0         # composed segments per step (per chain-group, see config)
 
@@ -172,6 +183,8 @@ class ColdRequest(Workload):
     name = "gdn_cold32k"
     kernel = "build_delta"
     fam = 3  # delta
+    op_dispatches = 2    # factor pass, state pass
+    step_dispatches = 4  # + the two-level composition
 
     def __init__(self):
         self.n_seg, self.L, self.H, self.d = 64, 512, 32, 128
@@ -264,6 +277,8 @@ class KdaRequest(ColdRequest):
     name = "kda_cold32k"
     kernel = "build_kda"
     fam = 4  # kda
+    op_dispatches = 1
+    step_dispatches = 3  # + the two-level composition
 
     def __init__(self):
         super().__init__()
@@ -288,9 +303,16 @@ class KdaRequest(ColdRequest):
 
 class ScalarOrDiag(Workload):
     def __init__(self, name, fam, n_seg, L, H, d):
+        import torch
+        from segment_scan_amd import api, synth
         self.name, self.fam = name, fam
         self.kernel = "build_sd"
         self.n_seg, self.L, self.H, self.d = n_seg, L, H, d
+        # few units: the build runs as pieces joined by a grouped composition (a
+        # second dispatch, which needs a workspace); the ordered compose follows
+        split = api.seg_build_workspace_size(fam, list(synth.even_offsets(n_seg, L)), H, d, torch.bfloat16) > 0
+        self.op_dispatches = 2 if split else 1
+        self.step_dispatches = self.op_dispatches + 1
         self.tokens = n_seg * L
         self.composed = n_seg
         units = n_seg * H
@@ -351,6 +373,8 @@ class WarmRequest(Workload):
     """Warm reuse of a 100k-token request: 30 GDN layers x 16 heads, 196 cached segments, w = 8."""
     name = "gdn_warm100k"
     kernel = "seam"
+    op_dispatches = 2    # window factor pre-pass, chain
+    step_dispatches = 2
 
     def __init__(self):
         from segment_scan_amd import synth
@@ -424,6 +448,8 @@ class KdaWarmRequest(WarmRequest):
     segments, w = 8, window gates per token and key channel."""
     name = "kda_warm100k"
     kernel = "seam_kda"
+    op_dispatches = 1
+    step_dispatches = 1
 
     def __init__(self):
         super().__init__()
@@ -553,7 +579,7 @@ def main():
     args = ap.parse_args()
     if args.ingest_counters:
         wl = WORKLOADS[args.workload]()
-        rec = ingest_counters(wl.name, wl.kernel, args.ingest_counters[0], args.ingest_counters[1], args.steps,
+        rec = ingest_counters(wl, args.ingest_counters[0], args.ingest_counters[1], args.steps,
                               args.counter_commands)
         print(json.dumps(rec))
         return
