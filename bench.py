@@ -143,6 +143,17 @@ def ingest_counters(wl, fetch_csv: str, write_csv: str, steps: int, cmds):
     return db[workload]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def to_dev(arr, dtype):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
@@ -328,26 +339,32 @@ class ScalarOrDiag(Workload):
         tk = synth.retnet() if self.fam == 1 else synth.gla()
         tk.q = None
         self.tk = tk
-        self.k, self.v = to_dev(tk.k, "bf16"), to_dev(tk.v, "bf16")
-        if tk.gate_per_chain:
-            self.lg = to_dev(tk.log_gate, "f32")
-        else:
-            self.lg = to_dev(tk.log_gate, "bf16")
+        k, v = to_dev(tk.k, "bf16"), to_dev(tk.v, "bf16")
+        lg = to_dev(tk.log_gate, "f32") if tk.gate_per_chain else to_dev(tk.log_gate, "bf16")
         self.offsets = [int(x) for x in tk.offsets]
         dev = "cuda"
         gshape = (self.n_seg, self.H, self.d) if self.fam == 2 else (self.n_seg, self.H)
-        self.g = torch.empty(gshape, device=dev)
-        self.S = torch.empty((self.n_seg, self.H, self.d, self.d), device=dev)
-        self.S_out = torch.empty((self.H, self.d, self.d), device=dev)
+        # Rotate input/output sets whose total exceeds twice the 256 MB last-level
+        # cache (MALL), so that repeated steps stream from HBM
+        self.n_sets = max(1, -(-2 * (256 << 20) // self.alg_bytes) + 1)
+        self.sets = []
+        for i in range(self.n_sets):
+            self.sets.append(dict(k=k if i == 0 else k.clone(), v=v if i == 0 else v.clone(),
+                                  lg=lg if i == 0 else lg.clone(), g=torch.empty(gshape, device=dev),
+                                  S=torch.empty((self.n_seg, self.H, self.d, self.d), device=dev),
+                                  S_out=torch.empty((self.H, self.d, self.d), device=dev)))
+        self.i_set = 0
         n_ws = api.seg_build_workspace_size(self.fam, self.offsets, self.H, self.d, torch.bfloat16)
         self.ws = torch.empty(max(n_ws, 16), device=dev, dtype=torch.uint8)
 
     def step(self, ev0, ev1):
+        b = self.sets[self.i_set]
+        self.i_set = (self.i_set + 1) % self.n_sets
         ev0.record()
-        self.api.seg_build(self.fam, self.offsets, self.k, self.v, None, self.lg, self.tk.gate_per_chain,
-                           out=(self.g, None, self.S), workspace=self.ws)
+        self.api.seg_build(self.fam, self.offsets, b["k"], b["v"], None, b["lg"], self.tk.gate_per_chain,
+                           out=(b["g"], None, b["S"]), workspace=self.ws)
         ev1.record()
-        self.api.compose(self.fam, self.g, None, self.S, S_out=self.S_out)
+        self.api.compose(self.fam, b["g"], None, b["S"], S_out=b["S_out"])
 
     def cpu_sample(self):
         import oracle
@@ -366,6 +383,7 @@ class ScalarOrDiag(Workload):
     def config(self):
         return {"workload": self.name, "family": "retnet" if self.fam == 1 else "gla", "heads": self.H, "d": self.d,
                 "segments": self.n_seg, "segment_len": self.L, "tokens": self.tokens, "inputs": "bf16",
+                "buffer_sets": getattr(self, "n_sets", None),
                 "accumulate": "fp32", "step": "hypic_seg_build + hypic_compose"}
 
 
@@ -617,6 +635,24 @@ def main():
         for _ in range(CALIBRATION_COPIES):  # an elementwise kernel (a same-dtype copy_ may become a DMA copy)
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
+        del src, dst
+
+    # achievable HBM bandwidth on this machine: an elementwise kernel reading and
+    # writing 1 GiB each (out of place), timed with events
+    copy_gbs = None
+    if not args.copy_calibration:
+        n = CALIBRATION_BYTES // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = round(5 * 2 * CALIBRATION_BYTES / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
+        del src, dst
 
     value = wl.tokens / (ms_per_step / 1e3)
     achieved = wl.alg_bytes / (k_ms / 1e3) / 1e9
@@ -624,11 +660,14 @@ def main():
     roofline = {"bound": "hbm", "kernel": wl.kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": wl.alg_bytes, "kernel_ms": round(k_ms, 4),
+                "kernel_ms_median": round(float(np.median(kern_ms)), 4),
                 "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 4),
                 "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 4),
                 "mfma_alg_tflops": round(wl.alg_flops / (k_ms / 1e3) / 1e12, 1),
                 "mfma_exec_tflops": round(wl.exec_flops / (k_ms / 1e3) / 1e12, 1),
-                "mfma_exec_frac": round(wl.exec_flops / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                "mfma_exec_frac": round(wl.exec_flops / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "copy_gbs": copy_gbs,
+                "frac_of_copy": None if not copy_gbs else round(achieved / copy_gbs, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -636,7 +675,7 @@ def main():
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
         dt, tokens, desc = wl.cpu_sample()
         cpu = {"value": round(tokens / dt, 2), "unit": "segment-tokens/s", "cores": oracle.max_threads(),
-               "kind": "oracle", "sample": desc, "seconds": round(dt, 2)}
+               "kind": "oracle", "sample": desc, "seconds": round(dt, 2), "cpu_model": cpu_model()}
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "segment-tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
