@@ -406,9 +406,10 @@ class WarmRequest(Workload):
         self.alg_bytes = (self.n_seg * n * (2 * d * d * 4 + 4) + ntok * n * (3 * d * 2 + 4) + ntok * n * d * 4
                           + 2 * n * d * d * 4)
         self.alg_flops = self.n_seg * n * 2.0 * d ** 3 + ntok * n * 6.0 * d * d
-        # body products as three fp16 MFMA passes (hi*hi, hi*lo, lo*hi); the
-        # window arithmetic runs on the vector ALUs
-        self.exec_flops = self.n_seg * n * 3 * 2.0 * d ** 3
+        # body products as three fp16 MFMA passes (hi*hi, hi*lo, lo*hi), and per
+        # window [K; Q] S (16 rows) and the rank-8 update, three passes each
+        # (within 2 % of the MFMA op counters)
+        self.exec_flops = self.n_seg * n * 3 * 2.0 * (d ** 3 + (16 + 8) * d * d)
 
     def setup(self):
         import torch
