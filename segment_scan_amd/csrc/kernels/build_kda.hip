@@ -31,7 +31,8 @@
 // waves 0-1 holding U and waves 2-3 S, d/2 columns each.  Per chunk the keys,
 // gate prefixes, the decayed key copies (split into bf16 terms) and X sit in
 // LDS; the off-diagonal Gram blocks run on bf16 MFMA with operands decayed on
-// the fly, the 64 x 64 inverse in fp32 on the VALU.
+// the fly; the 64 x 64 inverse takes its 32 x 32 diagonal blocks by forward
+// substitution and the off-diagonal block by two MFMA products.
 #include <type_traits>
 
 #include "common.h"
@@ -54,7 +55,7 @@ struct KdaCfg {
                                               // (rows 16-byte aligned for vector reads)
   static constexpr int KP = D + 4;            // bf16 pitch of Kb [t][d]
   static constexpr int TP = C + 4;            // bf16 pitch of Kd [d][t] and of X [t][t']
-  static constexpr int NP = 65;               // fp32 pitch of the Gram / inverse array
+  static constexpr int NP = C + 4;            // fp32 pitch of the Gram / inverse array (16-byte rows)
   using KT = typename std::conditional<IN_F32, float, bf16_t>::type;  // staged keys (exact)
   static constexpr int KF_BYTES = (C * FP * (int)sizeof(KT) + 15) / 16 * 16;
   static constexpr int VP = D + 8;            // pitch of the staged values [t][d]
@@ -65,15 +66,13 @@ struct KdaCfg {
   static constexpr int A_BYTES_BF = NTD * C * TP * 2;
   static constexpr int N_BYTES = C * NP * 4;  // the fp32 Gram / inverse (aliases X)
   static constexpr int A_BYTES = ((A_BYTES_BF > N_BYTES ? A_BYTES_BF : N_BYTES) + 15) / 16 * 16;
-  static constexpr int T_BYTES = 3 * 16 * 17 * 4;  // block-row scratch of the inverse
   static constexpr int OFF_KF = 0;
   static constexpr int OFF_V = OFF_KF + KF_BYTES;
   static constexpr int OFF_G = OFF_V + V_BYTES;
   static constexpr int OFF_KB = OFF_G + G_BYTES;
   static constexpr int OFF_KD = OFF_KB + KB_BYTES;
   static constexpr int OFF_A = OFF_KD + KD_BYTES;
-  static constexpr int OFF_T = OFF_A + A_BYTES;
-  static constexpr int OFF_SMALL = OFF_T + T_BYTES;
+  static constexpr int OFF_SMALL = OFF_A + A_BYTES;
   // beta, token max gate, mu, exp(mu_C - mu), G_C, exp(G_C), exp(G_C - mu_C), misc
   static constexpr int SMALL_BYTES = (4 * C + 3 * D + 4) * 4;
   static constexpr int LDS = OFF_SMALL + SMALL_BYTES;
@@ -98,6 +97,18 @@ __device__ __forceinline__ void lds_keys8(const float* p, float (&x)[8]) {
   }
 }
 __device__ __forceinline__ void lds_f8(const float* p, float (&x)[8]) { lds_keys8(p, x); }
+
+// Eight floats into LDS as one 16-byte row piece (bf16) or two (fp32).
+__device__ __forceinline__ void st_row8(bf16_t* p, const float (&x)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (bf16_t)x[j];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void st_row8(float* p, const float (&x)[8]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
 
 template <int NT, typename KT>
 __device__ __forceinline__ Frag<NT> decayed_frag(const KT* sKf, const float* sH, int FP, int t, int ref, int c0,
@@ -147,7 +158,6 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   bf16_t* sKd = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KD);
   bf16_t* sA = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_A);
   float* sN = reinterpret_cast<float*>(smem + Cfg::OFF_A);  // aliases sA
-  float* sT = reinterpret_cast<float*>(smem + Cfg::OFF_T);
   float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_SMALL);
   float* sMax = sBeta + C;  // largest channel gate of each token
   float* sMu = sMax + C;    // mu_t: inclusive prefix of sMax
@@ -216,14 +226,15 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
         const int t = it / (D / 8), db = it % (D / 8);
         float mx = lg[k][0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          sKf[t * FP + db * 8 + j] = (KT)x[k][j];
-          sV[t * VP + db * 8 + j] = (KT)vx[k][j];
-          sG[t * FP + db * 8 + j] = lg[k][j];
-          mx = fmaxf(mx, lg[k][j]);
-        }
-#pragma unroll
-        for (int o = 1; o < D / 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, lg[k][j]);
+        st_row8(sKf + t * FP + db * 8, x[k]);
+        st_row8(sV + t * VP + db * 8, vx[k]);
+        st_row8(sG + t * FP + db * 8, lg[k]);
+        // maximum over the token's D/8 lanes (aligned groups of 8 or 16 lanes)
+        mx = dpp_max_step(mx, 0);
+        mx = dpp_max_step(mx, 1);
+        mx = dpp_max_step(mx, 2);
+        if constexpr (D / 8 == 16) mx = dpp_max_step(mx, 3);
         if (db == 0) sMax[t] = mx;
       }
     }
@@ -350,46 +361,72 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
     }
     __syncthreads();
 
-    // ---- N = (I + M0)^-1: 16 x 16 diagonal blocks (wave 0) -------------------
+    // ---- N = (I + M)^-1 in 32 x 32 blocks, by wave 0 (the others wait) ---------
+    // Diagonal blocks by forward substitution, lane 32 b + c owning column c of
+    // block b: N_bb[r][c] = delta_rc - sum_{k<r} M_bb[r][k] N_bb[k][c], rows of M
+    // read as LDS broadcasts (only entries below the diagonal are read); then
+    // N_10 = -N_11 (M_10 N_00) as two 32 x 32 x 32 products on MFMA with both
+    // operands split into bf16 terms.
     if (wave == 0) {
-      const int b = lane >> 4, c = lane & 15;
-      const float* Mb = sN + (16 * b) * NP + 16 * b;
-      float x[16];
+      const int b = lane >> 5, c = l32;
+      const float* Mb = sN + 32 * b * NP + 32 * b;
+      float x[32];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = 0.f;
+      for (int r = 0; r < 32; ++r) {
+        float acc0 = 0.f, acc1 = 0.f;
+        const float* Mr = Mb + r * NP;
 #pragma unroll
-        for (int k = 0; k < r; ++k)
-          if (k >= c) acc = fmaf(Mb[r * NP + k], x[k], acc);
-        x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -acc);
+        for (int k4 = 0; k4 < r / 4; ++k4) {
+          const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
+          acc0 = fmaf(m4[0], x[4 * k4], acc0);
+          acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
+          acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
+          acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
+        }
+#pragma unroll
+        for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
+        x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
       }
+      // (the wave's lanes have all read M_bb: a wave runs in lockstep, and the
+      // writes below touch only N_bb's own block)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sN[(16 * b + r) * NP + 16 * b + c] = x[r];
+      for (int r = 0; r < 32; ++r) sN[(32 * b + r) * NP + 32 * b + c] = x[r];
     }
-    // ---- block rows i = 1..3: N_ij = -N_ii sum_{k=j}^{i-1} M_ik N_kj ----------
+    __syncthreads();
     {
-      const int r = tid >> 4, c = tid & 15;
+      auto prod = [&](const float* Ab, const float* Bb) {  // 32 x 32 blocks of sN; Ab Bb
+        f32x16 P = zero16();
 #pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        __syncthreads();
+        for (int ks = 0; ks < 2; ++ks) {
+          float xa[8], xb[8];
+          const float* ar = Ab + l32 * NP + 16 * ks + 8 * h;
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(ar);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(ar + 4);
 #pragma unroll
-        for (int j = 0; j < i; ++j) {
-          float acc = 0.f;
-          const float* Mrow = sN + (16 * i + r) * NP;
-          for (int k = j; k < i; ++k)
-#pragma unroll 4
-            for (int m = 0; m < 16; ++m) acc = fmaf(Mrow[16 * k + m], sN[(16 * k + m) * NP + 16 * j + c], acc);
-          sT[(j * 16 + r) * 17 + c] = acc;
+          for (int j = 0; j < 4; ++j) {
+            xa[j] = a0[j];
+            xa[4 + j] = a1[j];
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xb[j] = Bb[(16 * ks + 8 * h + j) * NP + l32];
+          mma<NTD, NTD>(P, split8<NTD>(xa), split8<NTD>(xb));
         }
-        __syncthreads();
+        return P;
+      };
+      if (wave == 0) {
+        const f32x16 P = prod(sN + 32 * NP, sN);  // M_10 N_00
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-        for (int j = 0; j < i; ++j) {
-          float acc = 0.f;
-          const float* Nrow = sN + (16 * i + r) * NP + 16 * i;
+        for (int r = 0; r < 16; ++r) sN[(32 + acc_row(r, lane)) * NP + l32] = P[r];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const f32x16 Q = prod(sN + 32 * NP + 32, sN + 32 * NP);  // N_11 P
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-          for (int m = 0; m < 16; ++m) acc = fmaf(Nrow[m], sT[(j * 16 + m) * 17 + c], acc);
-          sN[(16 * i + r) * NP + 16 * j + c] = -acc;
-        }
+        for (int r = 0; r < 16; ++r) sN[(32 + acc_row(r, lane)) * NP + l32] = -Q[r];
       }
     }
     __syncthreads();
