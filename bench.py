@@ -603,8 +603,8 @@ def main():
         print(json.dumps(rec))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the method's multi-worker form "
-              "is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (how the work would shard across "
+              "GPUs is a design note only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
