@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256, (IN_F32 ? 1 : 2)) void build_delta_kernel(cons
             vv[tt][r] = (t < nv) ? vsrc[(size_t)t * n_chain * D] : (VT)0.f;
           }
       }
-      // P1: Y[tt] = K[tt rows] * Z[:, ct]
+      // product 1: Y[tt] = K[tt rows] * Z[:, ct]
       f32x16 Y[2] = {zero16(), zero16()};
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, (IN_F32 ? 1 : 2)) void build_delta_kernel(cons
 #pragma unroll
           for (int r = 0; r < 16; ++r) Y[tt][r] = (float)vv[tt][r] - sEG[32 * tt + acc_row(r, lane)] * Y[tt][r];
       }
-      // P2: X[tt] = sum_{tp <= tt} A[tt, tp] * Y[tp]  (A lower triangular)
+      // product 2: X[tt] = sum_{tp <= tt} A[tt, tp] * Y[tp]  (A lower triangular)
       f32x16 X[2] = {zero16(), zero16()};
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp)
