@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
     "seam": ["segment_scan_amd/csrc/kernels/chain.hip", "segment_scan_amd/csrc/kernels/seam_prep.hip"],
     "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
     "rerotate": ["segment_scan_amd/csrc/kernels/rerotate.hip"],
-    "build_kda": ["segment_scan_amd/csrc/kernels/build_kda.hip"],
+    "build_kda": ["segment_scan_amd/csrc/kernels/build_kda.hip", "segment_scan_amd/csrc/kernels/build_delta2.hip"],
     "seam_kda": ["segment_scan_amd/csrc/kernels/seam_kda.hip"],
 }
 
@@ -81,7 +81,7 @@ KERNEL_SYMBOLS = {
     "seam": ["seam_prep_kernel", "chain_kernel"],
     "compose": ["chain_kernel", "compose_elem_kernel"],
     "rerotate": ["rerotate_kernel"],
-    "build_kda": ["build_kda_kernel"],
+    "build_kda": ["kda_prep_kernel", "delta_state_kernel", "build_kda_kernel"],
     "seam_kda": ["seam_kda_kernel"],
 }
 CALIBRATION_COPIES = 3       # final dispatches of a --copy-calibration run
@@ -288,19 +288,20 @@ class KdaRequest(ColdRequest):
     name = "kda_cold32k"
     kernel = "build_kda"
     fam = 4  # kda
-    op_dispatches = 1
-    step_dispatches = 3  # + the two-level composition
+    op_dispatches = 2    # factor pass, state pass
+    step_dispatches = 4  # + the two-level composition
 
     def __init__(self):
         super().__init__()
         units = self.n_seg * self.H
         # per token: k, v and the d channel gates (bf16) and beta
         self.alg_bytes = units * _build_bytes(4, self.L, self.d, 2, 2 * self.d + 2, True)
-        # executed MFMAs per 64-token chunk and unit (32x32x16, two bf16 terms per
-        # operand = 3 products each): Gram 2 tiles x 8 k-steps; per wave and 32-column
-        # tile Kb Z 4 x 2 x 2, X R 3 x 2, Kd W 2 x 2 x 4; 4 waves x 2 tiles
+        # executed 32x32x16 MFMAs per 64-token chunk and unit: factor pass Gram 3
+        # tiles x 8 k-steps and the inverse's two 32 x 32 x 32 products (2 k-steps),
+        # each in two bf16 terms (3 products); state pass as the delta one, fp16
+        # (8 waves: K Z 16, X R 6, K^T X 16)
         chunks = units * (self.L // 64)
-        self.exec_flops = chunks * 3 * (2 * 8 + 8 * (16 + 6 + 16)) * 32 * 32 * 16 * 2.0
+        self.exec_flops = chunks * (3 * (3 * 8 + 2 * 2) + 8 * (16 + 6 + 16)) * 32 * 32 * 16 * 2.0
 
     def _tokens(self):
         return self.synth.kda()

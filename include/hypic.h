@@ -159,6 +159,10 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
  *  - DELTA with d = 128 and bf16 tokens (segments up to 2048 tokens): per
  *    64-token chunk and chain the chunk's WY factor (8,704 bytes), i.e. about
  *    136 bytes per token and chain.
+ *  - KDA with d = 128 and bf16 tokens (segments up to 2048 tokens): per
+ *    64-token chunk and chain a 42,512-byte factor record (the chunk's two
+ *    decayed key copies and X as fp16, its gate factors), about 664 bytes per
+ *    token and chain.
  *  - NAIVE, SCALAR, DIAG when there are few (segment, chain) units (fewer than
  *    256) and every segment has at least two 64-token chunks: the segments are
  *    built as P = min(4, 512 / units, shortest segment's chunks) pieces of whole

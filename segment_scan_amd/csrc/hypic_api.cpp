@@ -183,6 +183,17 @@ size_t delta_workspace(int n_seg, const int32_t* seg_offsets, int n_chain, int d
   return need;
 }
 
+// The same for the KDA build's factor records.
+size_t kda_workspace(int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
+  size_t need = 0;
+  hypic::SegTable t;
+  for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
+    fill_seg_table(&t, seg_offsets, s0, std::min(hypic::kMaxSegPerLaunch, n_seg - s0));
+    need = std::max(need, hypic::kda_workspace_bytes(d, f32, t, n_chain));
+  }
+  return need;
+}
+
 // Piece split of a naive / scalar / diagonal build with few units: each
 // segment is cut into P pieces of whole 64-token chunks, built concurrently,
 // and the pieces of every segment are joined by the composition law (the same
@@ -205,6 +216,7 @@ size_t piece_bytes(int fam, int n_seg, int P, int n_chain, int d) {
 
 size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
   if (fam == HYPIC_DELTA) return delta_workspace(n_seg, seg_offsets, n_chain, d, f32);
+  if (fam == HYPIC_KDA) return kda_workspace(n_seg, seg_offsets, n_chain, d, f32);
   const int P = piece_count(fam, n_seg, seg_offsets, n_chain);
   return P > 1 ? piece_bytes(fam, n_seg, P, n_chain, d) : 0;
 }
@@ -310,7 +322,7 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
     fill_seg_table(&a.seg, seg_offsets, s0, ns);
     const int blocks = ns * n_chain;
     hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, workspace, (hipStream_t)stream)
-                   : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, a, blocks, (hipStream_t)stream)
+                   : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, a, blocks, workspace, (hipStream_t)stream)
                                         : hypic::launch_build_sd(fam, d, f32, a, blocks, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
   }
@@ -483,7 +495,7 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
       const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
       fill_seg_table(&b.seg, woff.data(), s0, ns);
       e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta_single(d, f32, b, ns * n_chain, (hipStream_t)stream)
-          : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, b, ns * n_chain, (hipStream_t)stream)
+          : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, b, ns * n_chain, nullptr, (hipStream_t)stream)
                                : hypic::launch_build_sd(fam, d, f32, b, ns * n_chain, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "hypic_seam_step window pairs launch");
     }

@@ -51,11 +51,6 @@ constexpr int REC_RS = C * C * 2;
 constexpr int REC_G = REC_RS + C * 4;
 constexpr int REC_BYTES = REC_G + C * 4;
 
-// Records are dense over the launch's chunks: record (chunk_base[s] + c) * n_chain
-// + chain holds chunk c of segment s on that chain.
-struct ChunkTable {
-  int32_t base[kMaxSegPerLaunch + 1];  // chunk_base[s]: chunks of the segments before s
-};
 
 __device__ __forceinline__ uint32_t pk_f16_from_bf16x2(uint32_t w) {
   // exact conversion of two bf16 values, so the packing rounding mode is irrelevant
@@ -282,13 +277,15 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
 // delta_state: per unit, [U | S] in registers, three MFMA products per chunk
 // =====================================================================================
 
-struct StateLds {  // one staging buffer; the kernel keeps two
+template <bool KDA>
+struct StateLdsT {  // one staging buffer
   static constexpr int O_K = 0;
   static constexpr int O_KT = O_K + C * KP * 2;
   static constexpr int O_V = O_KT + D * TP * 2;
   static constexpr int O_A0 = O_V + D * TP * 2;
   static constexpr int O_SM = O_A0 + C * TP * 2;  // eW[64] = exp(G_C - G_t), rs[64], exp(G_C)
-  static constexpr int BUF = O_SM + (2 * C + 4) * 4;
+  static constexpr int O_RF = O_SM + (2 * C + 4) * 4;  // KDA: row factors of S [128], of U [128]
+  static constexpr int BUF = O_RF + (KDA ? 2 * D * 4 : 0);
 };
 
 // Per chunk, in the frame scaled by the chunk's gate (the gated delta rule is
@@ -296,16 +293,23 @@ struct StateLds {  // one staging buffer; the kernel keeps two
 //   U <- U + K^T (-A0 (K U))
 //   S <- exp(G_C) S + K^T (A0 (diag(exp(G_C - G)) V - exp(G_C) K S))
 // so both halves share A0 and every gate factor is at most 1.
+// KDA mode: the same three products over the records of the KDA factor pass,
+// with the decayed keys Kb (for K Z) and Kd (for K^T X) in place of K, the value
+// weights exp(mu_C - mu_t), exp(mu_C) in place of exp(G_C - G_t), exp(G_C), and
+// per-row factors exp(G_C) (S) and exp(G_C - mu_C) (U) in place of the scalar
+// exp(G_C) in step 3; g accumulates mu_C.
 // 8 waves: wave w keeps the 32 state columns 32 (w & 3) .. of U (w < 4) or S
 // (w >= 4) in accumulators.  The loads of chunk c+1 are in flight while chunk c
 // is computed.  NBUF = 2: chunk c+1 is staged into the other LDS buffer (one
 // barrier per chunk, one workgroup per CU); NBUF = 1: into the same buffer
 // after a barrier (two per chunk), at half the LDS and at most 128 registers,
 // so that two workgroups share a CU and cover each other's waits.
-template <int NBUF>
+template <int NBUF, bool KDA>
 __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(const BuildArgs a,
                                                                              const ChunkTable cks,
                                                                              const unsigned char* ws) {
+  using StateLds = StateLdsT<KDA>;
+  constexpr int RB = KDA ? KREC_BYTES : REC_BYTES;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int wave = threadIdx.x >> 6;
@@ -328,28 +332,53 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
         Z[rt][r] = (!s_wave && 32 * rt + acc_row(r, lane) == col0 + (lane & 31)) ? 1.f : 0.f;
   }
   double g_acc = 0.0;
-  float fin[3];  // threads < 64: G_t, G_C and the row scale of A0 row t
+  // threads < 64: G_t, G_C and the row scale of A0 row t (KDA: the value weight,
+  // mu_C, the row scale; threads < 128 the two row factors; thread 0 exp(mu_C))
+  float fin[KDA ? 6 : 3];
 
   // ---- staging of one chunk: loads into registers, then conversion into LDS ---------
   // threads 0..255: a 4-token x 8-channel block of K; 256..511: of V; every
   // thread 8 entries of A0, and the first 64 the factors of token tid
-  uint4 raw[5];
+  uint4 raw[KDA ? 7 : 5];
   auto load_chunk = [&](int c) {
     const int tid = opaque(threadIdx.x);
     const int c0 = t_begin + c * C;
     const int nv = min(C, t_end - c0);
-    const unsigned char* rec = ws + ((size_t)(cks.base[s_local] + c) * n_chain + chain) * REC_BYTES;
+    const unsigned char* rec = ws + ((size_t)(cks.base[s_local] + c) * n_chain + chain) * RB;
     const int id = tid & 255, tb = id & 15, db = id >> 4;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(tid < 256 ? a.k : a.v);
+    if (KDA && tid < 256) {  // decayed keys Kb, rows of fp16 (zero past the end)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = tb * 4 + r;
-      raw[r] = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
-      if (t >= nv) raw[r] = make_uint4(0, 0, 0, 0);  // tokens past the end must be zero
+      for (int r = 0; r < 4; ++r)
+        raw[r] = *reinterpret_cast<const uint4*>(rec + KREC_KB + ((tb * 4 + r) * D + db * 8) * 2);
+    } else {
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(tid < 256 ? a.k : a.v);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb * 4 + r;
+        raw[r] = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
+        if (t >= nv) raw[r] = make_uint4(0, 0, 0, 0);  // tokens past the end must be zero
+      }
     }
-    raw[4] = *reinterpret_cast<const uint4*>(rec + REC_A + tid * 16);  // A0 row tid / 8, entries 8 (tid % 8) ..
-    fin[0] = fin[1] = fin[2] = 0.f;
-    if (tid < C) {
+    // A0 (X) row tid / 8, entries 8 (tid % 8) ..
+    raw[4] = *reinterpret_cast<const uint4*>(rec + (KDA ? KREC_X : REC_A) + tid * 16);
+    if constexpr (KDA) {  // Kd: 16-byte pieces 2 tid, 2 tid + 1 of the [128][64] fp16 rows
+      raw[5] = *reinterpret_cast<const uint4*>(rec + KREC_KD + (2 * tid) * 16);
+      raw[6] = *reinterpret_cast<const uint4*>(rec + KREC_KD + (2 * tid + 1) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < (KDA ? 6 : 3); ++i) fin[i] = 0.f;
+    if constexpr (KDA) {
+      if (tid < C) {
+        fin[0] = reinterpret_cast<const float*>(rec + KREC_VF)[tid];
+        fin[1] = reinterpret_cast<const float*>(rec + KREC_M)[0];
+        fin[2] = reinterpret_cast<const float*>(rec + KREC_XS)[tid];
+        fin[5] = reinterpret_cast<const float*>(rec + KREC_M)[1];
+      }
+      if (tid < D) {
+        fin[3] = reinterpret_cast<const float*>(rec + KREC_RS)[tid];
+        fin[4] = reinterpret_cast<const float*>(rec + KREC_RU)[tid];
+      }
+    } else if (tid < C) {
       const float* G = reinterpret_cast<const float*>(rec + REC_G);
       fin[0] = G[tid];
       fin[1] = G[C - 1];
@@ -360,29 +389,43 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
     const int tid = opaque(threadIdx.x);
     unsigned char* base = smem + buf * StateLds::BUF;
     const int id = tid & 255, tb = id & 15, db = id >> 4;
-    if (tid < 256) {  // keys: exact bf16 -> fp16, row-major
+    if (tid < 256) {  // keys: exact bf16 -> fp16 (KDA: Kb, already fp16), row-major
       f16_t* sK = reinterpret_cast<f16_t*>(base + StateLds::O_K);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        raw[r] = make_uint4(pk_f16_from_bf16x2(raw[r].x), pk_f16_from_bf16x2(raw[r].y),
-                            pk_f16_from_bf16x2(raw[r].z), pk_f16_from_bf16x2(raw[r].w));
+        if constexpr (!KDA)
+          raw[r] = make_uint4(pk_f16_from_bf16x2(raw[r].x), pk_f16_from_bf16x2(raw[r].y),
+                              pk_f16_from_bf16x2(raw[r].z), pk_f16_from_bf16x2(raw[r].w));
         f16_t* row = sK + (tb * 4 + r) * KP + db * 8;
         *reinterpret_cast<uint2*>(row) = make_uint2(raw[r].x, raw[r].y);
         *reinterpret_cast<uint2*>(row + 4) = make_uint2(raw[r].z, raw[r].w);
       }
     }
     // keys (fp16) or values (bf16) transposed: channel cc of the block holds its
-    // 4 tokens as two dwords (element cc of rows 0, 1 and of rows 2, 3)
-    uint16_t* sT = reinterpret_cast<uint16_t*>(base + (tid < 256 ? StateLds::O_KT : StateLds::O_V));
+    // 4 tokens as two dwords (element cc of rows 0, 1 and of rows 2, 3).  KDA:
+    // only the values; the transposed keys are Kd, copied as they are.
+    if (!KDA || tid >= 256) {
+      uint16_t* sT = reinterpret_cast<uint16_t*>(base + (tid < 256 ? StateLds::O_KT : StateLds::O_V));
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-      auto w = [&](int r) {
-        const uint4 q = raw[r];
-        return (cc >> 1) == 0 ? q.x : (cc >> 1) == 1 ? q.y : (cc >> 1) == 2 ? q.z : q.w;
-      };
-      *reinterpret_cast<uint2*>(sT + (db * 8 + cc) * TP + tb * 4) =
-          make_uint2(__builtin_amdgcn_perm(w(1), w(0), sel), __builtin_amdgcn_perm(w(3), w(2), sel));
+      for (int cc = 0; cc < 8; ++cc) {
+        const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+        auto w = [&](int r) {
+          const uint4 q = raw[r];
+          return (cc >> 1) == 0 ? q.x : (cc >> 1) == 1 ? q.y : (cc >> 1) == 2 ? q.z : q.w;
+        };
+        *reinterpret_cast<uint2*>(sT + (db * 8 + cc) * TP + tb * 4) =
+            make_uint2(__builtin_amdgcn_perm(w(1), w(0), sel), __builtin_amdgcn_perm(w(3), w(2), sel));
+      }
+    }
+    if constexpr (KDA) {
+      f16_t* sKt = reinterpret_cast<f16_t*>(base + StateLds::O_KT);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int piece = 2 * tid + i, row = piece >> 3, col8 = piece & 7;
+        f16_t* dst = sKt + row * TP + col8 * 8;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(raw[5 + i].x, raw[5 + i].y);
+        *reinterpret_cast<uint2*>(dst + 4) = make_uint2(raw[5 + i].z, raw[5 + i].w);
+      }
     }
     {
       f16_t* sA = reinterpret_cast<f16_t*>(base + StateLds::O_A0) + (tid >> 3) * TP + (tid & 7) * 8;
@@ -391,11 +434,18 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
     }
     if (tid < C) {
       float* sF = reinterpret_cast<float*>(base + StateLds::O_SM);
-      sF[tid] = __expf(fin[1] - fin[0]);  // value weight to the chunk end
-      sF[C + tid] = fin[2];               // row scale of A0
+      sF[tid] = KDA ? fin[0] : __expf(fin[1] - fin[0]);  // value weight to the chunk end
+      sF[C + tid] = fin[2];                               // row scale of A0
       if (tid == 0) {
-        sF[2 * C] = __expf(fin[1]);
+        sF[2 * C] = KDA ? fin[5] : __expf(fin[1]);
         g_acc += (double)fin[1];
+      }
+    }
+    if constexpr (KDA) {
+      if (tid < D) {
+        float* sR = reinterpret_cast<float*>(base + StateLds::O_RF);
+        sR[tid] = fin[3];
+        sR[D + tid] = fin[4];
       }
     }
   };
@@ -504,12 +554,25 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
         const int ex = f16_scale_exp(wave_max_uniform(m));
-        const float pre = (s_wave ? eGC : 1.f) * ldexpf(1.f, -ex);
-        if (s_wave || ex != 0) {
+        if constexpr (KDA) {  // per-row factors exp(G_C) (S) or exp(G_C - mu_C) (U)
+          const float sc = ldexpf(1.f, -ex);
+          const float* rf = reinterpret_cast<const float*>(base + StateLds::O_RF) + (s_wave ? 0 : D) + 4 * h;
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Z[rt][r] *= pre;
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 f4 = *reinterpret_cast<const f32x4*>(rf + 32 * rt + 8 * q) * sc;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) Z[rt][4 * q + j] *= f4[j];
+            }
+        } else {
+          const float pre = (s_wave ? eGC : 1.f) * ldexpf(1.f, -ex);
+          if (s_wave || ex != 0) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) Z[rt][r] *= pre;
+          }
         }
         const f16_t* pKt = sKt + l32 * TP + 4 * h;
 #pragma unroll
@@ -553,37 +616,40 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
 
 }  // namespace
 
+size_t delta2_workspace_bytes(const SegTable& seg, int n_chain) {
+  return (size_t)chunk_table(seg, nullptr) * n_chain * REC_BYTES;
+}
+
 namespace {
-int chunks_of(const SegTable& seg, ChunkTable* ct) {
-  int n = 0;
-  for (int s = 0; s < seg.n_seg; ++s) {
-    if (ct) ct->base[s] = n;
-    n += (seg.off[s + 1] - seg.off[s] + C - 1) / C;
-  }
-  if (ct) ct->base[seg.n_seg] = n;
-  return n;
+// The delta state pass keeps one staging buffer (two workgroups per CU); the KDA
+// mode stages three more 16-byte pieces per thread (its transposed keys come
+// from the record), which at the one-buffer register budget spills, so it keeps
+// two buffers and one workgroup per CU.
+template <bool KDA>
+hipError_t launch_state(const BuildArgs& a, const ChunkTable& ct, const unsigned char* w, hipStream_t stream) {
+  constexpr int NBUF = KDA ? 2 : 1;
+  constexpr int lds = NBUF * StateLdsT<KDA>::BUF;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&delta_state_kernel<NBUF, KDA>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((delta_state_kernel<NBUF, KDA>), dim3(a.seg.n_seg * a.n_chain), dim3(512), lds, stream, a, ct,
+                     w);
+  return hipGetLastError();
 }
 }  // namespace
 
-size_t delta2_workspace_bytes(const SegTable& seg, int n_chain) {
-  return (size_t)chunks_of(seg, nullptr) * n_chain * REC_BYTES;
-}
-
 hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream) {
-  constexpr int NBUF = 1;
-  constexpr int lds = NBUF * StateLds::BUF;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&delta_state_kernel<NBUF>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
   ChunkTable ct;
-  const int n_chunks = chunks_of(a.seg, &ct);
+  const int n_chunks = chunk_table(a.seg, &ct);
   unsigned char* w = reinterpret_cast<unsigned char*>(ws);
   hipLaunchKernelGGL(delta_prep_kernel, dim3(n_chunks * a.n_chain), dim3(64), 0, stream, a, ct, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((delta_state_kernel<NBUF>), dim3(a.seg.n_seg * a.n_chain), dim3(512), lds, stream, a, ct,
-                     (const unsigned char*)w);
-  return hipGetLastError();
+  return launch_state<false>(a, ct, w, stream);
+}
+
+hipError_t launch_kda_state(const BuildArgs& a, const ChunkTable& ct, const void* ws, hipStream_t stream) {
+  return launch_state<true>(a, ct, reinterpret_cast<const unsigned char*>(ws), stream);
 }
 
 }  // namespace hypic

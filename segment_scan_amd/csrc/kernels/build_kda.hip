@@ -138,6 +138,258 @@ __device__ __forceinline__ void split4_store(bf16_t* p, int term_stride, const f
   }
 }
 
+// The factor phases of one 64-token chunk, shared by the single-kernel build and
+// the factor pass: stage the chunk's keys (and values), gates and weights;
+// per-channel prefixes in place as H = G - mu; the strictly lower Gram
+// M = diag(b) (K o e^H)(K o e^-H)^T formed without overflow; and N = (I + M)^-1,
+// left in sN.  Every thread of the 256-thread workgroup calls it (it holds
+// barriers); on return sKf, sG (= H), sN, sBeta, sMu, sGC and sMisc ([0] = mu_C,
+// [1] = exp(mu_C)) are valid.
+template <int D, bool IN_F32, bool WITH_V, typename KT>
+__device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, int nv, int chain, KT* sKf, KT* sV,
+                                                  float* sG, float* sN, float* sBeta, float* sMax, float* sMu,
+                                                  float* sGC, float* sMisc) {
+  using Cfg = KdaCfg<D, IN_F32>;
+  constexpr int NTK = Cfg::NTK, NTD = Cfg::NTD, FP = Cfg::FP, VP = Cfg::VP, NP = Cfg::NP;
+  const int n_chain = a.n_chain;
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int wave = tid >> 6;
+  (void)VP;
+  // ---- stage keys, values and per-channel log gates (zero past the segment
+  // end) and each token's largest gate (its D/8 channel groups are consecutive
+  // lanes); every load of the chunk is issued before the first store
+  constexpr int NIT = C * (D / 8) / 256;
+  static_assert(NIT * 256 == C * (D / 8), "every lane runs every staging step");
+  {
+    float x[NIT][8], lg[NIT][8], vx[NIT][8];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int it = tid + 256 * k;
+      const int t = it / (D / 8), db = it % (D / 8);
+      if (t < nv) {
+        const size_t idx = ((size_t)(c0 + t) * n_chain + chain) * D + db * 8;
+        load8<IN_F32>(a.k, idx, x[k]);
+        load8<IN_F32>(a.lg, idx, lg[k]);
+        if constexpr (WITH_V) load8<IN_F32>(a.v, idx, vx[k]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[k][j] = lg[k][j] = vx[k][j] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int it = tid + 256 * k;
+      const int t = it / (D / 8), db = it % (D / 8);
+      float mx = lg[k][0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, lg[k][j]);
+      st_row8(sKf + t * FP + db * 8, x[k]);
+      if constexpr (WITH_V) st_row8(sV + t * VP + db * 8, vx[k]);
+      st_row8(sG + t * FP + db * 8, lg[k]);
+      // maximum over the token's D/8 lanes (aligned groups of 8 or 16 lanes)
+      mx = dpp_max_step(mx, 0);
+      mx = dpp_max_step(mx, 1);
+      mx = dpp_max_step(mx, 2);
+      if constexpr (D / 8 == 16) mx = dpp_max_step(mx, 3);
+      if (db == 0) sMax[t] = mx;
+    }
+  }
+  if (tid < C) sBeta[tid] = (tid < nv) ? load1<IN_F32>(a.beta, (size_t)(c0 + tid) * n_chain + chain) : 0.f;
+  __syncthreads();
+
+  // ---- per-channel prefixes (one thread per channel): G_C, and in place of
+  // the gates H_t = G_t - mu_t, with mu_t (the same in every thread: the
+  // same sums in the same order) recorded by thread 0
+  if (tid < D) {
+    float lgc[C], mxs[C];
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+      lgc[t] = sG[t * FP + tid];
+      mxs[t] = sMax[t];
+    }
+    float acc = 0.f, mu = 0.f;
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+      acc += lgc[t];
+      mu += mxs[t];
+      sG[t * FP + tid] = acc - mu;
+      if (tid == 0) sMu[t] = mu;
+    }
+    sGC[tid] = acc;
+    if (tid == 0) {
+      sMisc[0] = mu;
+      sMisc[1] = __expf(mu);
+    }
+  }
+  __syncthreads();
+
+  // ---- Gram M[i][j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc), i > j ------------
+  // Waves 0-2: one 32 x 32 MFMA tile each of products of decayed keys, both
+  // factors decayed against a reference token between the row and the column
+  // tokens (so both are <= |k|); parts of a tile whose row and column refer to
+  // different references are discarded (their factors are <= |k| as well):
+  //   wave 0: rows 32..63 x columns 0..31, reference 31
+  //   wave 1: rows 16a+16..16a+31 x columns 16a..16a+15 (a = 0, 2 in 16-row
+  //           halves), references 15 and 47
+  //   wave 2: rows 16a+8..16a+15 x columns 16a..16a+7 (a = 0..3), references 16a+7
+  if (wave < 3) {
+    int ra, rb, ref;
+    if (wave == 0) {
+      ra = 32 + l32;
+      rb = l32;
+      ref = 31;
+    } else if (wave == 1) {
+      ra = l32 < 16 ? 16 + l32 : 32 + l32;
+      rb = l32 < 16 ? l32 : 16 + l32;
+      ref = l32 < 16 ? 15 : 47;
+    } else {
+      const int qa = l32 >> 3;
+      ra = 16 * qa + 8 + (l32 & 7);
+      rb = 16 * qa + (l32 & 7);
+      ref = 16 * qa + 7;
+    }
+    f32x16 acc = zero16();
+#pragma unroll 2
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int cc = 16 * ks + 8 * h;
+      const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, FP, ra, ref, cc, true);
+      const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, rb, ref, cc, false);
+      mma<NTK, NTK>(acc, fa, fb);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rho = acc_row(r, lane);
+      int i;
+      bool keep;
+      if (wave == 0) {
+        i = 32 + rho;
+        keep = true;
+      } else if (wave == 1) {
+        i = rho < 16 ? 16 + rho : 32 + rho;
+        keep = (rho < 16) == (l32 < 16);
+      } else {
+        i = 16 * (rho >> 3) + 8 + (rho & 7);
+        keep = (rho >> 3) == (l32 >> 3);
+      }
+      if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
+    }
+  }
+  // The eight 8-token diagonal blocks term by term, two per wave; lane =
+  // (block, row i, channel quarter q).  Every lane reads every column token
+  // (straight-line loads); terms with j >= i are masked.
+  {
+    const int q = lane & 3, i = (lane >> 2) & 7;
+    const int b0 = 8 * (2 * wave + (lane >> 5));
+    const int ti = b0 + i;
+    constexpr int QC = D / 4;
+    float acc[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) acc[j] = 0.f;
+#pragma unroll 1
+    for (int cc = 0; cc < QC; cc += 8) {
+      const int c = q * QC + cc;
+      float ki[8], hi[8];
+      lds_keys8(sKf + ti * FP + c, ki);
+      lds_f8(sG + ti * FP + c, hi);
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        float kj[8], hj[8];
+        lds_keys8(sKf + (b0 + j) * FP + c, kj);
+        lds_f8(sG + (b0 + j) * FP + c, hj);
+        float term = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) term = fmaf(ki[e] * kj[e], __expf(hi[e] - hj[e]), term);
+        acc[j] += (j < i) ? term : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      acc[j] += __shfl_xor(acc[j], 1, 64);
+      acc[j] += __shfl_xor(acc[j], 2, 64);
+    }
+    if (q == 0) {
+      const float bi = sBeta[ti];
+#pragma unroll
+      for (int j = 0; j < 7; ++j)
+        if (j < i) sN[ti * NP + b0 + j] = bi * acc[j];
+    }
+  }
+  __syncthreads();
+
+  // ---- N = (I + M)^-1 in 32 x 32 blocks, by wave 0 (the others wait) ---------
+  // Diagonal blocks by forward substitution, lane 32 b + c owning column c of
+  // block b: N_bb[r][c] = delta_rc - sum_{k<r} M_bb[r][k] N_bb[k][c], rows of M
+  // read as LDS broadcasts (only entries below the diagonal are read); then
+  // N_10 = -N_11 (M_10 N_00) as two 32 x 32 x 32 products on MFMA with both
+  // operands split into bf16 terms.
+  if (wave == 0) {
+    const int b = lane >> 5, c = l32;
+    const float* Mb = sN + 32 * b * NP + 32 * b;
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      float acc0 = 0.f, acc1 = 0.f;
+      const float* Mr = Mb + r * NP;
+#pragma unroll
+      for (int k4 = 0; k4 < r / 4; ++k4) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
+        acc0 = fmaf(m4[0], x[4 * k4], acc0);
+        acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
+        acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
+        acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
+      }
+#pragma unroll
+      for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
+      x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
+    }
+    // (the wave's lanes have all read M_bb: a wave runs in lockstep, and the
+    // writes below touch only N_bb's own block)
+#pragma unroll
+    for (int r = 0; r < 32; ++r) sN[(32 * b + r) * NP + 32 * b + c] = x[r];
+  }
+  __syncthreads();
+  {
+    auto prod = [&](const float* Ab, const float* Bb) {  // 32 x 32 blocks of sN; Ab Bb
+      f32x16 P = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float xa[8], xb[8];
+        const float* ar = Ab + l32 * NP + 16 * ks + 8 * h;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ar);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ar + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xa[j] = a0[j];
+          xa[4 + j] = a1[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xb[j] = Bb[(16 * ks + 8 * h + j) * NP + l32];
+        mma<NTD, NTD>(P, split8<NTD>(xa), split8<NTD>(xb));
+      }
+      return P;
+    };
+    if (wave == 0) {
+      const f32x16 P = prod(sN + 32 * NP, sN);  // M_10 N_00
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sN[(32 + acc_row(r, lane)) * NP + l32] = P[r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const f32x16 Q = prod(sN + 32 * NP + 32, sN + 32 * NP);  // N_11 P
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sN[(32 + acc_row(r, lane)) * NP + l32] = -Q[r];
+    }
+  }
+  __syncthreads();
+}
+
 // ORDERED: workgroup rows follow the launch's longest-first order (ragged
 // launches only; equal lengths use the index order without the lookup).
 template <int D, bool IN_F32, bool ORDERED>
@@ -199,237 +451,8 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    // ---- stage keys, values and per-channel log gates (zero past the segment
-    // end) and each token's largest gate (its D/8 channel groups are consecutive
-    // lanes); every load of the chunk is issued before the first store
-    constexpr int NIT = C * (D / 8) / 256;
-    static_assert(NIT * 256 == C * (D / 8), "every lane runs every staging step");
-    {
-      float x[NIT][8], lg[NIT][8], vx[NIT][8];
-#pragma unroll
-      for (int k = 0; k < NIT; ++k) {
-        const int it = tid + 256 * k;
-        const int t = it / (D / 8), db = it % (D / 8);
-        if (t < nv) {
-          const size_t idx = ((size_t)(c0 + t) * n_chain + chain) * D + db * 8;
-          load8<IN_F32>(a.k, idx, x[k]);
-          load8<IN_F32>(a.lg, idx, lg[k]);
-          load8<IN_F32>(a.v, idx, vx[k]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[k][j] = lg[k][j] = vx[k][j] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < NIT; ++k) {
-        const int it = tid + 256 * k;
-        const int t = it / (D / 8), db = it % (D / 8);
-        float mx = lg[k][0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, lg[k][j]);
-        st_row8(sKf + t * FP + db * 8, x[k]);
-        st_row8(sV + t * VP + db * 8, vx[k]);
-        st_row8(sG + t * FP + db * 8, lg[k]);
-        // maximum over the token's D/8 lanes (aligned groups of 8 or 16 lanes)
-        mx = dpp_max_step(mx, 0);
-        mx = dpp_max_step(mx, 1);
-        mx = dpp_max_step(mx, 2);
-        if constexpr (D / 8 == 16) mx = dpp_max_step(mx, 3);
-        if (db == 0) sMax[t] = mx;
-      }
-    }
-    if (tid < C) sBeta[tid] = (tid < nv) ? load1<IN_F32>(a.beta, (size_t)(c0 + tid) * n_chain + chain) : 0.f;
-    __syncthreads();
-
-    // ---- per-channel prefixes (one thread per channel): G_C, and in place of
-    // the gates H_t = G_t - mu_t, with mu_t (the same in every thread: the
-    // same sums in the same order) recorded by thread 0
-    if (tid < D) {
-      float lgc[C], mxs[C];
-#pragma unroll
-      for (int t = 0; t < C; ++t) {
-        lgc[t] = sG[t * FP + tid];
-        mxs[t] = sMax[t];
-      }
-      float acc = 0.f, mu = 0.f;
-#pragma unroll
-      for (int t = 0; t < C; ++t) {
-        acc += lgc[t];
-        mu += mxs[t];
-        sG[t * FP + tid] = acc - mu;
-        if (tid == 0) sMu[t] = mu;
-      }
-      sGC[tid] = acc;
-      if (tid == 0) {
-        sMisc[0] = mu;
-        sMisc[1] = __expf(mu);
-      }
-    }
-    __syncthreads();
-
-    // ---- Gram M[i][j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc), i > j ------------
-    // Waves 0-2: one 32 x 32 MFMA tile each of products of decayed keys, both
-    // factors decayed against a reference token between the row and the column
-    // tokens (so both are <= |k|); parts of a tile whose row and column refer to
-    // different references are discarded (their factors are <= |k| as well):
-    //   wave 0: rows 32..63 x columns 0..31, reference 31
-    //   wave 1: rows 16a+16..16a+31 x columns 16a..16a+15 (a = 0, 2 in 16-row
-    //           halves), references 15 and 47
-    //   wave 2: rows 16a+8..16a+15 x columns 16a..16a+7 (a = 0..3), references 16a+7
+    kda_chunk_factors<D, IN_F32, true>(a, c0, nv, chain, sKf, sV, sG, sN, sBeta, sMax, sMu, sGC, sMisc);
     if (wave == 0) g_acc += (double)sMisc[0];  // mu_C; every lane of wave 0 keeps the same sum
-    if (wave < 3) {
-      int ra, rb, ref;
-      if (wave == 0) {
-        ra = 32 + l32;
-        rb = l32;
-        ref = 31;
-      } else if (wave == 1) {
-        ra = l32 < 16 ? 16 + l32 : 32 + l32;
-        rb = l32 < 16 ? l32 : 16 + l32;
-        ref = l32 < 16 ? 15 : 47;
-      } else {
-        const int qa = l32 >> 3;
-        ra = 16 * qa + 8 + (l32 & 7);
-        rb = 16 * qa + (l32 & 7);
-        ref = 16 * qa + 7;
-      }
-      f32x16 acc = zero16();
-#pragma unroll 2
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int cc = 16 * ks + 8 * h;
-        const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, FP, ra, ref, cc, true);
-        const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, rb, ref, cc, false);
-        mma<NTK, NTK>(acc, fa, fb);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rho = acc_row(r, lane);
-        int i;
-        bool keep;
-        if (wave == 0) {
-          i = 32 + rho;
-          keep = true;
-        } else if (wave == 1) {
-          i = rho < 16 ? 16 + rho : 32 + rho;
-          keep = (rho < 16) == (l32 < 16);
-        } else {
-          i = 16 * (rho >> 3) + 8 + (rho & 7);
-          keep = (rho >> 3) == (l32 >> 3);
-        }
-        if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
-      }
-    }
-    // The eight 8-token diagonal blocks term by term, two per wave; lane =
-    // (block, row i, channel quarter q).  Every lane reads every column token
-    // (straight-line loads); terms with j >= i are masked.
-    {
-      const int q = lane & 3, i = (lane >> 2) & 7;
-      const int b0 = 8 * (2 * wave + (lane >> 5));
-      const int ti = b0 + i;
-      constexpr int QC = D / 4;
-      float acc[7];
-#pragma unroll
-      for (int j = 0; j < 7; ++j) acc[j] = 0.f;
-#pragma unroll 1
-      for (int cc = 0; cc < QC; cc += 8) {
-        const int c = q * QC + cc;
-        float ki[8], hi[8];
-        lds_keys8(sKf + ti * FP + c, ki);
-        lds_f8(sG + ti * FP + c, hi);
-#pragma unroll
-        for (int j = 0; j < 7; ++j) {
-          float kj[8], hj[8];
-          lds_keys8(sKf + (b0 + j) * FP + c, kj);
-          lds_f8(sG + (b0 + j) * FP + c, hj);
-          float term = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) term = fmaf(ki[e] * kj[e], __expf(hi[e] - hj[e]), term);
-          acc[j] += (j < i) ? term : 0.f;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        acc[j] += __shfl_xor(acc[j], 1, 64);
-        acc[j] += __shfl_xor(acc[j], 2, 64);
-      }
-      if (q == 0) {
-        const float bi = sBeta[ti];
-#pragma unroll
-        for (int j = 0; j < 7; ++j)
-          if (j < i) sN[ti * NP + b0 + j] = bi * acc[j];
-      }
-    }
-    __syncthreads();
-
-    // ---- N = (I + M)^-1 in 32 x 32 blocks, by wave 0 (the others wait) ---------
-    // Diagonal blocks by forward substitution, lane 32 b + c owning column c of
-    // block b: N_bb[r][c] = delta_rc - sum_{k<r} M_bb[r][k] N_bb[k][c], rows of M
-    // read as LDS broadcasts (only entries below the diagonal are read); then
-    // N_10 = -N_11 (M_10 N_00) as two 32 x 32 x 32 products on MFMA with both
-    // operands split into bf16 terms.
-    if (wave == 0) {
-      const int b = lane >> 5, c = l32;
-      const float* Mb = sN + 32 * b * NP + 32 * b;
-      float x[32];
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        float acc0 = 0.f, acc1 = 0.f;
-        const float* Mr = Mb + r * NP;
-#pragma unroll
-        for (int k4 = 0; k4 < r / 4; ++k4) {
-          const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
-          acc0 = fmaf(m4[0], x[4 * k4], acc0);
-          acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
-          acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
-          acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
-        }
-#pragma unroll
-        for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
-        x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
-      }
-      // (the wave's lanes have all read M_bb: a wave runs in lockstep, and the
-      // writes below touch only N_bb's own block)
-#pragma unroll
-      for (int r = 0; r < 32; ++r) sN[(32 * b + r) * NP + 32 * b + c] = x[r];
-    }
-    __syncthreads();
-    {
-      auto prod = [&](const float* Ab, const float* Bb) {  // 32 x 32 blocks of sN; Ab Bb
-        f32x16 P = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float xa[8], xb[8];
-          const float* ar = Ab + l32 * NP + 16 * ks + 8 * h;
-          const f32x4 a0 = *reinterpret_cast<const f32x4*>(ar);
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(ar + 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            xa[j] = a0[j];
-            xa[4 + j] = a1[j];
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xb[j] = Bb[(16 * ks + 8 * h + j) * NP + l32];
-          mma<NTD, NTD>(P, split8<NTD>(xa), split8<NTD>(xb));
-        }
-        return P;
-      };
-      if (wave == 0) {
-        const f32x16 P = prod(sN + 32 * NP, sN);  // M_10 N_00
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sN[(32 + acc_row(r, lane)) * NP + l32] = P[r];
-      }
-      __syncthreads();
-      if (wave == 0) {
-        const f32x16 Q = prod(sN + 32 * NP + 32, sN + 32 * NP);  // N_11 P
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sN[(32 + acc_row(r, lane)) * NP + l32] = -Q[r];
-      }
-    }
-    __syncthreads();
 
     // ---- X = N diag(beta) split to bf16 terms; decayed key copies ------------
     {
@@ -576,11 +599,156 @@ hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
   return seg_uniform(a.seg) ? launch_o<D, F32, false>(a, n_blocks, stream) : launch_o<D, F32, true>(a, n_blocks, stream);
 }
 
+// ---------------------------------------------------------------------------------
+// Factor pass of the two-kernel build (d = 128, bf16 tokens): one 256-thread
+// workgroup per (chunk, chain), all independent, so the latency of the scans,
+// the Gram and the inverse hides behind other workgroups (72 KB of LDS: two per
+// CU).  It writes the chunk's record (layout in launch.h): the decayed keys as
+// fp16 (every factor <= 1, so no scaling), X with a power-of-two scale per row
+// (row maximum into [2^13, 2^14)), and the gate factors; the state pass then
+// runs the delta state kernel's three products on them.
+struct KdaPrepLds {
+  using Cfg = KdaCfg<128, false>;
+  static constexpr int OFF_KF = 0;
+  static constexpr int OFF_G = OFF_KF + Cfg::KF_BYTES;
+  static constexpr int OFF_N = OFF_G + Cfg::G_BYTES;
+  static constexpr int OFF_SMALL = OFF_N + C * Cfg::NP * 4;
+  static constexpr int LDS = OFF_SMALL + (4 * C + 3 * 128 + 4) * 4;
+  static_assert(LDS <= 80 * 1024, "two workgroups per CU");
+  static_assert(KREC_BYTES % 16 == 0 && KREC_KD % 16 == 0 && KREC_X % 16 == 0, "16-byte record pieces");
+};
+
+__global__ __launch_bounds__(256, 2) void kda_prep_kernel(const BuildArgs a, const ChunkTable cks, unsigned char* ws) {
+  constexpr int D = 128;
+  using Cfg = KdaCfg<D, false>;
+  constexpr int FP = Cfg::FP, NP = Cfg::NP;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16_t* sKf = reinterpret_cast<bf16_t*>(smem + KdaPrepLds::OFF_KF);
+  float* sG = reinterpret_cast<float*>(smem + KdaPrepLds::OFF_G);
+  float* sN = reinterpret_cast<float*>(smem + KdaPrepLds::OFF_N);
+  float* sBeta = reinterpret_cast<float*>(smem + KdaPrepLds::OFF_SMALL);
+  float* sMax = sBeta + C;
+  float* sMu = sMax + C;
+  float* sVf = sMu + C;  // (unused here)
+  float* sGC = sVf + C;
+  float* sMisc = sGC + 3 * D;
+  (void)sVf;
+
+  // workgroup -> (chunk of the launch, chain): consecutive workgroups take the
+  // chains of one chunk, which share the rows of the token-major inputs
+  const int n_chain = a.n_chain;
+  const int gchunk = blockIdx.x / n_chain, chain = blockIdx.x % n_chain;
+  int lo = 0, hi = a.seg.n_seg;  // segment: last s with base[s] <= gchunk (uniform search)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cks.base[mid] <= gchunk) lo = mid; else hi = mid;
+  }
+  const int c0 = a.seg.off[lo] + (gchunk - cks.base[lo]) * C;
+  const int nv = min(C, a.seg.off[lo + 1] - c0);
+
+  kda_chunk_factors<D, false, false>(a, c0, nv, chain, sKf, (bf16_t*)nullptr, sG, sN, sBeta, sMax, sMu, sGC,
+                                     sMisc);
+
+  const int tid = threadIdx.x;
+  unsigned char* rec = ws + (size_t)blockIdx.x * KREC_BYTES;
+  {  // X = N diag(b), row t by the four threads 4t .. 4t+3 (16 entries each)
+    const int t = tid >> 2, cb = (tid & 3) * 16;
+    float x[16];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int tp = cb + j;
+      x[j] = (tp <= t) ? sN[t * NP + tp] * sBeta[tp] : 0.f;
+      m = fmaxf(m, fabsf(x[j]));
+    }
+    m = dpp_max_step(m, 0);  // the row's four lanes: a quad
+    m = dpp_max_step(m, 1);
+    int e = 0;
+    if (m > 0.f) {
+      frexpf(m, &e);
+      e -= 14;  // row maximum into [2^13, 2^14)
+    }
+    const float sc = ldexpf(1.f, -e);
+    f16x8 lo8, hi8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo8[j] = (f16_t)(x[j] * sc);
+      hi8[j] = (f16_t)(x[8 + j] * sc);
+    }
+    f16x8* dst = reinterpret_cast<f16x8*>(rec + KREC_X + (t * C + cb) * 2);
+    dst[0] = lo8;
+    dst[1] = hi8;
+    if ((tid & 3) == 0) reinterpret_cast<float*>(rec + KREC_XS)[t] = ldexpf(1.f, e);
+  }
+  {  // decayed keys: tokens 4 tq .. 4 tq + 3, channels 8 db .. 8 db + 7
+    const int tq = tid & 15, db = tid >> 4;
+    float hC[8];
+    lds_f8(sG + (C - 1) * FP + 8 * db, hC);
+    float kd[8][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tq + r;
+      float kv[8], hv[8];
+      lds_keys8(sKf + t * FP + 8 * db, kv);
+      lds_f8(sG + t * FP + 8 * db, hv);
+      f16x8 kb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kb[j] = (f16_t)(kv[j] * __expf(hv[j]));
+        kd[j][r] = kv[j] * __expf(hC[j] - hv[j]);
+      }
+      *reinterpret_cast<f16x8*>(rec + KREC_KB + (t * D + 8 * db) * 2) = kb;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (f16_t)kd[j][r];
+      *reinterpret_cast<f16x4*>(rec + KREC_KD + ((8 * db + j) * C + 4 * tq) * 2) = v;
+    }
+  }
+  const float muC = sMisc[0];
+  if (tid < C) reinterpret_cast<float*>(rec + KREC_VF)[tid] = __expf(muC - sMu[tid]);
+  if (tid < D) {
+    reinterpret_cast<float*>(rec + KREC_RS)[tid] = __expf(sGC[tid]);
+    reinterpret_cast<float*>(rec + KREC_RU)[tid] = __expf(sGC[tid] - muC);
+  }
+  if (tid == 0) {
+    reinterpret_cast<float*>(rec + KREC_M)[0] = muC;
+    reinterpret_cast<float*>(rec + KREC_M)[1] = sMisc[1];
+  }
+}
+
 }  // namespace
 
 bool kda_build_supported(int d, bool in_f32) { return d == 64 || (d == 128 && !in_f32); }
 
-hipError_t launch_build_kda(int d, bool in_f32, const BuildArgs& a, int n_blocks, hipStream_t stream) {
+namespace {
+bool use_two_pass(int d, bool in_f32, const SegTable& seg) {
+  if (d != 128 || in_f32) return false;
+  for (int s = 0; s < seg.n_seg; ++s)
+    if (seg.off[s + 1] - seg.off[s] > kDelta2MaxSegLen) return false;
+  return true;
+}
+}  // namespace
+
+size_t kda_workspace_bytes(int d, bool in_f32, const SegTable& seg, int n_chain) {
+  return use_two_pass(d, in_f32, seg) ? (size_t)chunk_table(seg, nullptr) * n_chain * KREC_BYTES : 0;
+}
+
+hipError_t launch_build_kda(int d, bool in_f32, const BuildArgs& a, int n_blocks, void* ws, hipStream_t stream) {
+  if (ws && use_two_pass(d, in_f32, a.seg)) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_prep_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, KdaPrepLds::LDS);
+    if (attr != hipSuccess) return attr;
+    ChunkTable ct;
+    const int n_chunks = chunk_table(a.seg, &ct);
+    hipLaunchKernelGGL(kda_prep_kernel, dim3(n_chunks * a.n_chain), dim3(256), KdaPrepLds::LDS, stream, a, ct,
+                       reinterpret_cast<unsigned char*>(ws));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_kda_state(a, ct, ws, stream);
+  }
   if (d == 128 && !in_f32) return launch_t<128, false>(a, n_blocks, stream);
   if (d == 64) return in_f32 ? launch_t<64, true>(a, n_blocks, stream) : launch_t<64, false>(a, n_blocks, stream);
   return hipErrorInvalidValue;

@@ -113,10 +113,47 @@ size_t seam_workspace_bytes(int n_seg, int w, int n_chain);
 hipError_t launch_seam_prep(int d, bool in_f32, const SeamArgs& a, float* ws, hipStream_t stream);
 // seam step of the naive, scalar and diagonal families (seam_elem.hip)
 hipError_t launch_seam_elem(int fam, int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
-// KDA build (build_kda.hip): one workgroup per unit, no workspace; built for
-// d = 64 (bf16 or fp32 tokens) and d = 128 (bf16 tokens).
+// Chunk table of a two-kernel build launch: records are dense over the launch's
+// 64-token chunks, record (base[s] + c) * n_chain + chain holding chunk c of
+// segment s on that chain.
+struct ChunkTable {
+  int32_t base[kMaxSegPerLaunch + 1];  // chunks of the segments before s
+};
+inline int chunk_table(const SegTable& seg, ChunkTable* ct) {
+  int n = 0;
+  for (int s = 0; s < seg.n_seg; ++s) {
+    if (ct) ct->base[s] = n;
+    n += (seg.off[s + 1] - seg.off[s] + 63) / 64;
+  }
+  if (ct) ct->base[seg.n_seg] = n;
+  return n;
+}
+
+// KDA build (build_kda.hip), built for d = 64 (bf16 or fp32 tokens) and d = 128
+// (bf16 tokens).  With d = 128, bf16 tokens and segments of at most
+// kDelta2MaxSegLen tokens it runs as a factor pass writing one record per
+// (chunk, chain) into a workspace of kda_workspace_bytes() and the delta state
+// pass in its KDA mode (build_delta2.hip); otherwise as one kernel without
+// workspace (ws may then be NULL).
 bool kda_build_supported(int d, bool in_f32);
-hipError_t launch_build_kda(int d, bool in_f32, const BuildArgs& a, int n_blocks, hipStream_t stream);
+size_t kda_workspace_bytes(int d, bool in_f32, const SegTable& seg, int n_chain);
+hipError_t launch_build_kda(int d, bool in_f32, const BuildArgs& a, int n_blocks, void* ws, hipStream_t stream);
+// Record of one (chunk, chain) of the KDA factor pass: the decayed keys
+// Kb = K o e^H (fp16 [64][128]) and Kd = (K o e^(H_C - H))^T (fp16 [128][64]),
+// X = (I + M)^-1 diag(b) (fp16 [64][64], each row scaled by a power of two) with
+// the row scales, the value weights exp(mu_C - mu_t) [64], the row factors
+// exp(G_C) and exp(G_C - mu_C) [128 each], and mu_C, exp(mu_C).
+constexpr int KREC_KB = 0;
+constexpr int KREC_KD = KREC_KB + 64 * 128 * 2;
+constexpr int KREC_X = KREC_KD + 128 * 64 * 2;
+constexpr int KREC_XS = KREC_X + 64 * 64 * 2;
+constexpr int KREC_VF = KREC_XS + 64 * 4;
+constexpr int KREC_RS = KREC_VF + 64 * 4;
+constexpr int KREC_RU = KREC_RS + 128 * 4;
+constexpr int KREC_M = KREC_RU + 128 * 4;
+constexpr int KREC_BYTES = KREC_M + 16;
+// the delta state pass in its KDA mode (build_delta2.hip), over the records of a factor pass
+hipError_t launch_kda_state(const BuildArgs& a, const ChunkTable& ct, const void* ws, hipStream_t stream);
 // seam step of the KDA family (seam_kda.hip): no workspace
 hipError_t launch_seam_kda(int d, bool in_f32, const SeamArgs& a, hipStream_t stream);
 // rotary re-rotation of n_seg x n_chain pairs in place (rerotate.hip): S <- R S,

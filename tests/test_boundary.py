@@ -130,9 +130,13 @@ def test_piece_split_workspace_size(lib):
 
 
 def test_kda_workspace_sizes(lib):
-    """The KDA build and seam step take no workspace; its dense composition
-    takes the delta family's."""
-    assert ws_size(lib, fam=KDA) == (0, 0)
+    """The d = 128 bf16 KDA build takes one 42,512-byte factor record per 64-token
+    chunk and chain (decayed keys, X, gate factors); other KDA builds and the
+    seam step take none; its dense composition takes the delta family's."""
+    assert ws_size(lib, fam=KDA) == (0, 2 * 2 * 42512)
+    assert ws_size(lib, fam=KDA, offsets=(0, 1, 65, 200), n_chain=3) == (0, (1 + 1 + 3) * 3 * 42512)
+    assert ws_size(lib, fam=KDA, offsets=(0, 2049)) == (0, 0)
+    assert ws_size(lib, fam=KDA, d=64) == (0, 0)
     assert ws_size(lib, fam=KDA, d=64, dtype=F32) == (0, 0)
     for want_prefix in (0, 1):
         a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)

@@ -75,6 +75,23 @@ def test_kda_strong_and_zero_gates(pattern):
     check_build(tk, "kda_strong_gates_" + pattern)
 
 
+def test_kda_strong_gates_bf16_d128():
+    """Strong and zero gates through the d = 128 factor-record path (fp16 decayed
+    keys: entries decayed below fp16's range vanish, which the relative error
+    of the unit does not see)."""
+    tk = synth.kda(n_seg=2, L=130, n_chain=2)
+    r = np.random.default_rng(12)
+    tk.log_gate = np.where(r.random(tk.log_gate.shape) < 0.5, -30.0, 0.0)
+    check_build(tk, "kda_strong_bf16_d128")
+
+
+def test_kda_segment_lengths_of_both_paths():
+    """2048 tokens (longest of the factor-record path) and 2049 (single kernel)."""
+    for L in (2048, 2049):
+        tk = synth.kda(n_seg=1, L=L, n_chain=2, gate_scale=1.0 / 64)
+        check_build(tk, "kda_long_%d" % L)
+
+
 def test_kda_build_then_compose_matches_sequential():
     """Cold path end to end on the GPU (KDA build, ordered dense composition)
     against straight recurrence over the whole request, with slow gates."""
