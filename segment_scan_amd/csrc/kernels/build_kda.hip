@@ -227,29 +227,27 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
   __syncthreads();
 
   // ---- Gram M[i][j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc), i > j ------------
-  // Waves 0-2: one 32 x 32 MFMA tile each of products of decayed keys, both
+  // Each wave forms one 32 x 32 MFMA tile of products of decayed keys, both
   // factors decayed against a reference token between the row and the column
   // tokens (so both are <= |k|); parts of a tile whose row and column refer to
   // different references are discarded (their factors are <= |k| as well):
   //   wave 0: rows 32..63 x columns 0..31, reference 31
-  //   wave 1: rows 16a+16..16a+31 x columns 16a..16a+15 (a = 0, 2 in 16-row
-  //           halves), references 15 and 47
+  //   wave 1: rows 32a+16..32a+31 x columns 32a..32a+15 (a = 0, 1), references 32a+15
   //   wave 2: rows 16a+8..16a+15 x columns 16a..16a+7 (a = 0..3), references 16a+7
-  if (wave < 3) {
+  //   wave 3: rows 8a+4..8a+7 x columns 8a..8a+3 (a = 0..7), references 8a+3
+  // which leaves the sixteen 4 x 4 diagonal blocks, summed term by term.
+  {
+    const int sh = 5 - wave;  // log2 of the row group size in the tile: 16, 8, 4 (wave 0: one group of 32)
     int ra, rb, ref;
     if (wave == 0) {
       ra = 32 + l32;
       rb = l32;
       ref = 31;
-    } else if (wave == 1) {
-      ra = l32 < 16 ? 16 + l32 : 32 + l32;
-      rb = l32 < 16 ? l32 : 16 + l32;
-      ref = l32 < 16 ? 15 : 47;
     } else {
-      const int qa = l32 >> 3;
-      ra = 16 * qa + 8 + (l32 & 7);
-      rb = 16 * qa + (l32 & 7);
-      ref = 16 * qa + 7;
+      const int ga = l32 >> sh, w = l32 & ((1 << sh) - 1);  // group, position in the group
+      ra = (ga << (sh + 1)) + (1 << sh) + w;
+      rb = (ga << (sh + 1)) + w;
+      ref = (ga << (sh + 1)) + (1 << sh) - 1;
     }
     f32x16 acc = zero16();
 #pragma unroll 2
@@ -267,27 +265,23 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
       if (wave == 0) {
         i = 32 + rho;
         keep = true;
-      } else if (wave == 1) {
-        i = rho < 16 ? 16 + rho : 32 + rho;
-        keep = (rho < 16) == (l32 < 16);
       } else {
-        i = 16 * (rho >> 3) + 8 + (rho & 7);
-        keep = (rho >> 3) == (l32 >> 3);
+        const int ga = rho >> sh;
+        i = (ga << (sh + 1)) + (1 << sh) + (rho & ((1 << sh) - 1));
+        keep = ga == (l32 >> sh);
       }
       if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
     }
   }
-  // The eight 8-token diagonal blocks term by term, two per wave; lane =
-  // (block, row i, channel quarter q).  Every lane reads every column token
+  // The sixteen 4-token diagonal blocks term by term; thread = (block, row i,
+  // channel quarter q).  Every thread reads every column token of its block
   // (straight-line loads); terms with j >= i are masked.
   {
-    const int q = lane & 3, i = (lane >> 2) & 7;
-    const int b0 = 8 * (2 * wave + (lane >> 5));
+    const int q = tid & 3, i = (tid >> 2) & 3;
+    const int b0 = 4 * (tid >> 4);
     const int ti = b0 + i;
     constexpr int QC = D / 4;
-    float acc[7];
-#pragma unroll
-    for (int j = 0; j < 7; ++j) acc[j] = 0.f;
+    float acc[3] = {0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int cc = 0; cc < QC; cc += 8) {
       const int c = q * QC + cc;
@@ -295,7 +289,7 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
       lds_keys8(sKf + ti * FP + c, ki);
       lds_f8(sG + ti * FP + c, hi);
 #pragma unroll
-      for (int j = 0; j < 7; ++j) {
+      for (int j = 0; j < 3; ++j) {
         float kj[8], hj[8];
         lds_keys8(sKf + (b0 + j) * FP + c, kj);
         lds_f8(sG + (b0 + j) * FP + c, hj);
@@ -306,14 +300,14 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
       }
     }
 #pragma unroll
-    for (int j = 0; j < 7; ++j) {
+    for (int j = 0; j < 3; ++j) {
       acc[j] += __shfl_xor(acc[j], 1, 64);
       acc[j] += __shfl_xor(acc[j], 2, 64);
     }
     if (q == 0) {
       const float bi = sBeta[ti];
 #pragma unroll
-      for (int j = 0; j < 7; ++j)
+      for (int j = 0; j < 3; ++j)
         if (j < i) sN[ti * NP + b0 + j] = bi * acc[j];
     }
   }

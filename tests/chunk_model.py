@@ -22,9 +22,9 @@ inclusive prefixes G [C, dk], the per-token largest gate summed, mu_t =
 sum_{s<=t} max_c lg_sc, and the shifted prefixes H = G - mu (per channel
 non-increasing in t, <= 0); H_C, mu_C, G_C are the chunk's last rows:
     M[i,j]  = b_i sum_c k_ic k_jc exp(H_ic - H_jc)   (i > j, every term <= |k_i k_j|)
-              16-token diagonal blocks term by term; block row I > 0 against
-              the earlier tokens as (K_I o exp(H_I - H_r)) (K_<I o exp(H_r - H_<I))^T
-              with r = 16 I - 1, both factors <= |k|
+              block pairs of 32, 16, 8, 4 tokens through keys decayed against
+              the token between them (both factors <= |k|), the 4 x 4 diagonal
+              blocks term by term
     X       = (I + M)^-1 diag(b)
     Kb      = K o exp(H),  Kd = (K o exp(H_C - H))^T            (both <= |k|)
     U1      = diag(exp(G_C - mu_C)) U0 - Kd X (Kb U0),  g += mu_C   (T = exp(g) U)
@@ -141,20 +141,26 @@ def scalar_diag_build(k, v, lg, C=64):
     return g, S
 
 
-def kda_gram(K, b, H, bs=16):
-    """Strictly lower M[i,j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc) as the kernel forms it."""
+def kda_gram(K, b, H):
+    """Strictly lower M[i,j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc) as the kernels form it:
+    hierarchically, block pairs of size s = 32, 16, 8, 4 (rows s..2s-1 against columns
+    0..s-1 of every 2s-token block) through keys decayed against the reference token
+    2s*a + s - 1 between them (both factors <= |k|), and the sixteen 4 x 4 diagonal
+    blocks term by term."""
     C = K.shape[0]
     M = np.zeros((C, C))
-    for I in range(C // bs):
-        rows = slice(bs * I, bs * (I + 1))
-        for i in range(bs * I, bs * (I + 1)):
-            for j in range(bs * I, i):
-                M[i, j] = b[i] * np.sum(K[i] * K[j] * np.exp(H[i] - H[j]))
-        if I > 0:
-            r = bs * I - 1
+    for s in (32, 16, 8, 4):
+        for a0 in range(0, C, 2 * s):
+            r = a0 + s - 1
+            rows = slice(a0 + s, a0 + 2 * s)
+            cols = slice(a0, a0 + s)
             Kb = K[rows] * np.exp(H[rows] - H[r])
-            Ka = K[:bs * I] * np.exp(H[r] - H[:bs * I])
-            M[rows, :bs * I] = b[rows, None] * (Kb @ Ka.T)
+            Ka = K[cols] * np.exp(H[r] - H[cols])
+            M[rows, cols] = b[rows, None] * (Kb @ Ka.T)
+    for b0 in range(0, C, 4):
+        for i in range(b0, b0 + 4):
+            for j in range(b0, i):
+                M[i, j] = b[i] * np.sum(K[i] * K[j] * np.exp(H[i] - H[j]))
     return M
 
 
