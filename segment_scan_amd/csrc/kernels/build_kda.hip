@@ -51,8 +51,9 @@ struct KdaCfg {
   static constexpr int NRT = D / 32;          // row tiles of the state
   static constexpr int CT = D / 64;           // 32-column tiles per wave (d/2 columns)
   static constexpr int CPW = D / 2;
-  static constexpr int FP = D + 8;            // pitch of the staged keys and gate prefixes [t][d]
+  static constexpr int FP = D + 8;            // bf16 / fp32 pitch of the staged keys [t][d]
                                               // (rows 16-byte aligned for vector reads)
+  static constexpr int GP = D + 4;            // fp32 pitch of the gate prefixes [t][d]
   static constexpr int KP = D + 4;            // bf16 pitch of Kb [t][d]
   static constexpr int TP = C + 4;            // bf16 pitch of Kd [d][t] and of X [t][t']
   static constexpr int NP = C + 4;            // fp32 pitch of the Gram / inverse array (16-byte rows)
@@ -60,7 +61,7 @@ struct KdaCfg {
   static constexpr int KF_BYTES = (C * FP * (int)sizeof(KT) + 15) / 16 * 16;
   static constexpr int VP = D + 8;            // pitch of the staged values [t][d]
   static constexpr int V_BYTES = (C * VP * (int)sizeof(KT) + 15) / 16 * 16;
-  static constexpr int G_BYTES = C * FP * 4;
+  static constexpr int G_BYTES = C * GP * 4;
   static constexpr int KB_BYTES = NTK * C * KP * 2;
   static constexpr int KD_BYTES = NTK * D * TP * 2;
   static constexpr int A_BYTES_BF = NTD * C * TP * 2;
@@ -111,12 +112,12 @@ __device__ __forceinline__ void st_row8(float* p, const float (&x)[8]) {
 }
 
 template <int NT, typename KT>
-__device__ __forceinline__ Frag<NT> decayed_frag(const KT* sKf, const float* sH, int FP, int t, int ref, int c0,
-                                                 bool toward) {
+__device__ __forceinline__ Frag<NT> decayed_frag(const KT* sKf, const float* sH, int FP, int GP, int t, int ref,
+                                                 int c0, bool toward) {
   float k[8], ht[8], hr[8], x[8];
   lds_keys8(sKf + t * FP + c0, k);
-  lds_f8(sH + t * FP + c0, ht);
-  lds_f8(sH + ref * FP + c0, hr);
+  lds_f8(sH + t * GP + c0, ht);
+  lds_f8(sH + ref * GP + c0, hr);
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = k[j] * __expf(toward ? ht[j] - hr[j] : hr[j] - ht[j]);
   return split8<NT>(x);
@@ -143,14 +144,17 @@ __device__ __forceinline__ void split4_store(bf16_t* p, int term_stride, const f
 // per-channel prefixes in place as H = G - mu; the strictly lower Gram
 // M = diag(b) (K o e^H)(K o e^-H)^T formed without overflow; and N = (I + M)^-1,
 // left in sN.  Every thread of the 256-thread workgroup calls it (it holds
-// barriers); on return sKf, sG (= H), sN, sBeta, sMu, sGC and sMisc ([0] = mu_C,
-// [1] = exp(mu_C)) are valid.
-template <int D, bool IN_F32, bool WITH_V, typename KT>
+// barriers).  early() runs in every thread once H, sMu, sGC and sMisc ([0] =
+// mu_C, [1] = exp(mu_C)) are valid, before the Gram.  N_ON_G: sN shares the
+// memory of sG, so sG is valid only until the Gram (early() is its last
+// reader); otherwise sKf, sG, sN, sBeta, sMu, sGC and sMisc are all valid on
+// return.
+template <int D, bool IN_F32, bool WITH_V, bool N_ON_G, typename KT, typename Early>
 __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, int nv, int chain, KT* sKf, KT* sV,
                                                   float* sG, float* sN, float* sBeta, float* sMax, float* sMu,
-                                                  float* sGC, float* sMisc) {
+                                                  float* sGC, float* sMisc, Early early) {
   using Cfg = KdaCfg<D, IN_F32>;
-  constexpr int NTK = Cfg::NTK, NTD = Cfg::NTD, FP = Cfg::FP, VP = Cfg::VP, NP = Cfg::NP;
+  constexpr int NTK = Cfg::NTK, NTD = Cfg::NTD, FP = Cfg::FP, GP = Cfg::GP, VP = Cfg::VP, NP = Cfg::NP;
   const int n_chain = a.n_chain;
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
@@ -188,7 +192,7 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
       for (int j = 1; j < 8; ++j) mx = fmaxf(mx, lg[k][j]);
       st_row8(sKf + t * FP + db * 8, x[k]);
       if constexpr (WITH_V) st_row8(sV + t * VP + db * 8, vx[k]);
-      st_row8(sG + t * FP + db * 8, lg[k]);
+      st_row8(sG + t * GP + db * 8, lg[k]);
       // maximum over the token's D/8 lanes (aligned groups of 8 or 16 lanes)
       mx = dpp_max_step(mx, 0);
       mx = dpp_max_step(mx, 1);
@@ -207,7 +211,7 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
     float lgc[C], mxs[C];
 #pragma unroll
     for (int t = 0; t < C; ++t) {
-      lgc[t] = sG[t * FP + tid];
+      lgc[t] = sG[t * GP + tid];
       mxs[t] = sMax[t];
     }
     float acc = 0.f, mu = 0.f;
@@ -215,7 +219,7 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
     for (int t = 0; t < C; ++t) {
       acc += lgc[t];
       mu += mxs[t];
-      sG[t * FP + tid] = acc - mu;
+      sG[t * GP + tid] = acc - mu;
       if (tid == 0) sMu[t] = mu;
     }
     sGC[tid] = acc;
@@ -225,6 +229,7 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
     }
   }
   __syncthreads();
+  early();
 
   // ---- Gram M[i][j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc), i > j ------------
   // Each wave forms one 32 x 32 MFMA tile of products of decayed keys, both
@@ -236,80 +241,79 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
   //   wave 2: rows 16a+8..16a+15 x columns 16a..16a+7 (a = 0..3), references 16a+7
   //   wave 3: rows 8a+4..8a+7 x columns 8a..8a+3 (a = 0..7), references 8a+3
   // which leaves the sixteen 4 x 4 diagonal blocks, summed term by term.
-  {
-    const int sh = 5 - wave;  // log2 of the row group size in the tile: 16, 8, 4 (wave 0: one group of 32)
-    int ra, rb, ref;
-    if (wave == 0) {
-      ra = 32 + l32;
-      rb = l32;
-      ref = 31;
-    } else {
-      const int ga = l32 >> sh, w = l32 & ((1 << sh) - 1);  // group, position in the group
-      ra = (ga << (sh + 1)) + (1 << sh) + w;
-      rb = (ga << (sh + 1)) + w;
-      ref = (ga << (sh + 1)) + (1 << sh) - 1;
-    }
-    f32x16 acc = zero16();
+  const int sh = 5 - wave;  // log2 of the row group size in the tile: 16, 8, 4 (wave 0: one group of 32)
+  int ra, rb, ref;
+  if (wave == 0) {
+    ra = 32 + l32;
+    rb = l32;
+    ref = 31;
+  } else {
+    const int ga = l32 >> sh, w = l32 & ((1 << sh) - 1);  // group, position in the group
+    ra = (ga << (sh + 1)) + (1 << sh) + w;
+    rb = (ga << (sh + 1)) + w;
+    ref = (ga << (sh + 1)) + (1 << sh) - 1;
+  }
+  f32x16 acc = zero16();
 #pragma unroll 2
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int cc = 16 * ks + 8 * h;
-      const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, FP, ra, ref, cc, true);
-      const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, rb, ref, cc, false);
-      mma<NTK, NTK>(acc, fa, fb);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rho = acc_row(r, lane);
-      int i;
-      bool keep;
-      if (wave == 0) {
-        i = 32 + rho;
-        keep = true;
-      } else {
-        const int ga = rho >> sh;
-        i = (ga << (sh + 1)) + (1 << sh) + (rho & ((1 << sh) - 1));
-        keep = ga == (l32 >> sh);
-      }
-      if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
-    }
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int cc = 16 * ks + 8 * h;
+    const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, FP, GP, ra, ref, cc, true);
+    const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, GP, rb, ref, cc, false);
+    mma<NTK, NTK>(acc, fa, fb);
   }
   // The sixteen 4-token diagonal blocks term by term; thread = (block, row i,
   // channel quarter q).  Every thread reads every column token of its block
   // (straight-line loads); terms with j >= i are masked.
+  const int q = tid & 3, i4 = (tid >> 2) & 3;
+  const int b0 = 4 * (tid >> 4);
+  const int ti = b0 + i4;
+  float dacc[3] = {0.f, 0.f, 0.f};
   {
-    const int q = tid & 3, i = (tid >> 2) & 3;
-    const int b0 = 4 * (tid >> 4);
-    const int ti = b0 + i;
     constexpr int QC = D / 4;
-    float acc[3] = {0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int cc = 0; cc < QC; cc += 8) {
       const int c = q * QC + cc;
       float ki[8], hi[8];
       lds_keys8(sKf + ti * FP + c, ki);
-      lds_f8(sG + ti * FP + c, hi);
+      lds_f8(sG + ti * GP + c, hi);
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         float kj[8], hj[8];
         lds_keys8(sKf + (b0 + j) * FP + c, kj);
-        lds_f8(sG + (b0 + j) * FP + c, hj);
+        lds_f8(sG + (b0 + j) * GP + c, hj);
         float term = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) term = fmaf(ki[e] * kj[e], __expf(hi[e] - hj[e]), term);
-        acc[j] += (j < i) ? term : 0.f;
+        dacc[j] += (j < i4) ? term : 0.f;
       }
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      acc[j] += __shfl_xor(acc[j], 1, 64);
-      acc[j] += __shfl_xor(acc[j], 2, 64);
+      dacc[j] += __shfl_xor(dacc[j], 1, 64);
+      dacc[j] += __shfl_xor(dacc[j], 2, 64);
     }
-    if (q == 0) {
-      const float bi = sBeta[ti];
+  }
+  if constexpr (N_ON_G) __syncthreads();  // every reader of sG is done: sN takes its memory
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < i) sN[ti * NP + b0 + j] = bi * acc[j];
+  for (int r = 0; r < 16; ++r) {
+    const int rho = acc_row(r, lane);
+    int i;
+    bool keep;
+    if (wave == 0) {
+      i = 32 + rho;
+      keep = true;
+    } else {
+      const int ga = rho >> sh;
+      i = (ga << (sh + 1)) + (1 << sh) + (rho & ((1 << sh) - 1));
+      keep = ga == (l32 >> sh);
     }
+    if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
+  }
+  if (q == 0) {
+    const float bi = sBeta[ti];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < i4) sN[ti * NP + b0 + j] = bi * dacc[j];
   }
   __syncthreads();
 
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   using Cfg = KdaCfg<D, IN_F32>;
   using KT = typename Cfg::KT;
   constexpr int NTK = Cfg::NTK, NTD = Cfg::NTD, NRT = Cfg::NRT, CT = Cfg::CT, CPW = Cfg::CPW;
-  constexpr int FP = Cfg::FP, KP = Cfg::KP, TP = Cfg::TP, NP = Cfg::NP, VP = Cfg::VP;
+  constexpr int FP = Cfg::FP, GP = Cfg::GP, KP = Cfg::KP, TP = Cfg::TP, NP = Cfg::NP, VP = Cfg::VP;
   constexpr int KBS = C * KP;  // term stride (elements) of Kb
   constexpr int KDS = D * TP;  // term stride of Kd
   constexpr int ATS = C * TP;  // term stride of X
@@ -445,7 +449,8 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    kda_chunk_factors<D, IN_F32, true>(a, c0, nv, chain, sKf, sV, sG, sN, sBeta, sMax, sMu, sGC, sMisc);
+    kda_chunk_factors<D, IN_F32, true, false>(a, c0, nv, chain, sKf, sV, sG, sN, sBeta, sMax, sMu, sGC, sMisc,
+                                              [] {});
     if (wave == 0) g_acc += (double)sMisc[0];  // mu_C; every lane of wave 0 keeps the same sum
 
     // ---- X = N diag(beta) split to bf16 terms; decayed key copies ------------
@@ -473,14 +478,14 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
       // tokens 4*tq .. 4*tq+3, channels 8*db .. 8*db+7
       const int tq = tid & 15, db = tid >> 4;
       float hC[8];
-      lds_f8(sG + (C - 1) * FP + 8 * db, hC);
+      lds_f8(sG + (C - 1) * GP + 8 * db, hC);
       float kd[8][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * tq + r;
         float kv[8], hv[8], kb[8];
         lds_keys8(sKf + t * FP + 8 * db, kv);
-        lds_f8(sG + t * FP + 8 * db, hv);
+        lds_f8(sG + t * GP + 8 * db, hv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           kb[j] = kv[j] * __expf(hv[j]);
@@ -596,26 +601,30 @@ hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
 // ---------------------------------------------------------------------------------
 // Factor pass of the two-kernel build (d = 128, bf16 tokens): one 256-thread
 // workgroup per (chunk, chain), all independent, so the latency of the scans,
-// the Gram and the inverse hides behind other workgroups (72 KB of LDS: two per
-// CU).  It writes the chunk's record (layout in launch.h): the decayed keys as
-// fp16 (every factor <= 1, so no scaling), X with a power-of-two scale per row
-// (row maximum into [2^13, 2^14)), and the gate factors; the state pass then
-// runs the delta state kernel's three products on them.
+// the Gram and the inverse hides behind other workgroups.  It writes the
+// chunk's record (layout in launch.h): the decayed keys as fp16 (every factor
+// <= 1, so no scaling) and the gate factors as soon as H is known, then X with
+// a power-of-two scale per row (row maximum into [2^13, 2^14)); the state pass
+// runs the delta state kernel's three products on them.  The Gram / inverse
+// array takes the memory of the gate prefixes once the Gram has read them
+// (51 KB of LDS: three workgroups per CU).
 struct KdaPrepLds {
   using Cfg = KdaCfg<128, false>;
   static constexpr int OFF_KF = 0;
   static constexpr int OFF_G = OFF_KF + Cfg::KF_BYTES;
-  static constexpr int OFF_N = OFF_G + Cfg::G_BYTES;
-  static constexpr int OFF_SMALL = OFF_N + C * Cfg::NP * 4;
-  static constexpr int LDS = OFF_SMALL + (4 * C + 3 * 128 + 4) * 4;
-  static_assert(LDS <= 80 * 1024, "two workgroups per CU");
+  static constexpr int OFF_N = OFF_G;  // after the Gram
+  static constexpr int OFF_SMALL = OFF_G + Cfg::G_BYTES;
+  // beta, token max gate, mu, G_C, misc
+  static constexpr int LDS = OFF_SMALL + (3 * C + 128 + 4) * 4;
+  static_assert(C * Cfg::NP * 4 <= Cfg::G_BYTES, "the Gram fits in the gate prefixes' memory");
+  static_assert(3 * LDS <= 160 * 1024 - 3 * 1024, "three workgroups per CU");
   static_assert(KREC_BYTES % 16 == 0 && KREC_KD % 16 == 0 && KREC_X % 16 == 0, "16-byte record pieces");
 };
 
-__global__ __launch_bounds__(256, 2) void kda_prep_kernel(const BuildArgs a, const ChunkTable cks, unsigned char* ws) {
+__global__ __launch_bounds__(256, 3) void kda_prep_kernel(const BuildArgs a, const ChunkTable cks, unsigned char* ws) {
   constexpr int D = 128;
   using Cfg = KdaCfg<D, false>;
-  constexpr int FP = Cfg::FP, NP = Cfg::NP;
+  constexpr int FP = Cfg::FP, GP = Cfg::GP, NP = Cfg::NP;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* sKf = reinterpret_cast<bf16_t*>(smem + KdaPrepLds::OFF_KF);
   float* sG = reinterpret_cast<float*>(smem + KdaPrepLds::OFF_G);
@@ -623,10 +632,8 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(const BuildArgs a, con
   float* sBeta = reinterpret_cast<float*>(smem + KdaPrepLds::OFF_SMALL);
   float* sMax = sBeta + C;
   float* sMu = sMax + C;
-  float* sVf = sMu + C;  // (unused here)
-  float* sGC = sVf + C;
-  float* sMisc = sGC + 3 * D;
-  (void)sVf;
+  float* sGC = sMu + C;
+  float* sMisc = sGC + D;
 
   // workgroup -> (chunk of the launch, chain): consecutive workgroups take the
   // chains of one chunk, which share the rows of the token-major inputs
@@ -639,12 +646,51 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(const BuildArgs a, con
   }
   const int c0 = a.seg.off[lo] + (gchunk - cks.base[lo]) * C;
   const int nv = min(C, a.seg.off[lo + 1] - c0);
-
-  kda_chunk_factors<D, false, false>(a, c0, nv, chain, sKf, (bf16_t*)nullptr, sG, sN, sBeta, sMax, sMu, sGC,
-                                     sMisc);
-
   const int tid = threadIdx.x;
   unsigned char* rec = ws + (size_t)blockIdx.x * KREC_BYTES;
+
+  // decayed keys (tokens 4 tq .. 4 tq + 3, channels 8 db .. 8 db + 7) and the
+  // gate factors, written while H is still in LDS
+  auto early = [&] {
+    const int tq = tid & 15, db = tid >> 4;
+    float hC[8];
+    lds_f8(sG + (C - 1) * GP + 8 * db, hC);
+    float kd[8][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tq + r;
+      float kv[8], hv[8];
+      lds_keys8(sKf + t * FP + 8 * db, kv);
+      lds_f8(sG + t * GP + 8 * db, hv);
+      f16x8 kb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kb[j] = (f16_t)(kv[j] * __expf(hv[j]));
+        kd[j][r] = kv[j] * __expf(hC[j] - hv[j]);
+      }
+      *reinterpret_cast<f16x8*>(rec + KREC_KB + (t * D + 8 * db) * 2) = kb;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (f16_t)kd[j][r];
+      *reinterpret_cast<f16x4*>(rec + KREC_KD + ((8 * db + j) * C + 4 * tq) * 2) = v;
+    }
+    const float muC = sMisc[0];
+    if (tid < C) reinterpret_cast<float*>(rec + KREC_VF)[tid] = __expf(muC - sMu[tid]);
+    if (tid < D) {
+      reinterpret_cast<float*>(rec + KREC_RS)[tid] = __expf(sGC[tid]);
+      reinterpret_cast<float*>(rec + KREC_RU)[tid] = __expf(sGC[tid] - muC);
+    }
+    if (tid == 0) {
+      reinterpret_cast<float*>(rec + KREC_M)[0] = muC;
+      reinterpret_cast<float*>(rec + KREC_M)[1] = sMisc[1];
+    }
+  };
+  kda_chunk_factors<D, false, false, true>(a, c0, nv, chain, sKf, (bf16_t*)nullptr, sG, sN, sBeta, sMax, sMu, sGC,
+                                           sMisc, early);
+
   {  // X = N diag(b), row t by the four threads 4t .. 4t+3 (16 entries each)
     const int t = tid >> 2, cb = (tid & 3) * 16;
     float x[16];
@@ -673,43 +719,6 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(const BuildArgs a, con
     dst[0] = lo8;
     dst[1] = hi8;
     if ((tid & 3) == 0) reinterpret_cast<float*>(rec + KREC_XS)[t] = ldexpf(1.f, e);
-  }
-  {  // decayed keys: tokens 4 tq .. 4 tq + 3, channels 8 db .. 8 db + 7
-    const int tq = tid & 15, db = tid >> 4;
-    float hC[8];
-    lds_f8(sG + (C - 1) * FP + 8 * db, hC);
-    float kd[8][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * tq + r;
-      float kv[8], hv[8];
-      lds_keys8(sKf + t * FP + 8 * db, kv);
-      lds_f8(sG + t * FP + 8 * db, hv);
-      f16x8 kb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        kb[j] = (f16_t)(kv[j] * __expf(hv[j]));
-        kd[j][r] = kv[j] * __expf(hC[j] - hv[j]);
-      }
-      *reinterpret_cast<f16x8*>(rec + KREC_KB + (t * D + 8 * db) * 2) = kb;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (f16_t)kd[j][r];
-      *reinterpret_cast<f16x4*>(rec + KREC_KD + ((8 * db + j) * C + 4 * tq) * 2) = v;
-    }
-  }
-  const float muC = sMisc[0];
-  if (tid < C) reinterpret_cast<float*>(rec + KREC_VF)[tid] = __expf(muC - sMu[tid]);
-  if (tid < D) {
-    reinterpret_cast<float*>(rec + KREC_RS)[tid] = __expf(sGC[tid]);
-    reinterpret_cast<float*>(rec + KREC_RU)[tid] = __expf(sGC[tid] - muC);
-  }
-  if (tid == 0) {
-    reinterpret_cast<float*>(rec + KREC_M)[0] = muC;
-    reinterpret_cast<float*>(rec + KREC_M)[1] = sMisc[1];
   }
 }
 
