@@ -204,28 +204,50 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
   if (tid < C) sBeta[tid] = (tid < nv) ? load1<IN_F32>(a.beta, (size_t)(c0 + tid) * n_chain + chain) : 0.f;
   __syncthreads();
 
-  // ---- per-channel prefixes (one thread per channel): G_C, and in place of
-  // the gates H_t = G_t - mu_t, with mu_t (the same in every thread: the
-  // same sums in the same order) recorded by thread 0
-  if (tid < D) {
-    float lgc[C], mxs[C];
-#pragma unroll
-    for (int t = 0; t < C; ++t) {
-      lgc[t] = sG[t * GP + tid];
-      mxs[t] = sMax[t];
-    }
+  // ---- per-channel prefixes: G_C, and in place of the gates H_t = G_t - mu_t.
+  // Thread c < D takes channel c over the first half of the chunk, thread D + c
+  // the same channel over the second half (local prefixes, then the first
+  // half's totals added after the barrier).  mu_t is the same in every thread
+  // of a half (the same sums in the same order); threads 0 and D record it.
+  constexpr int HC = C / 2;
+  const int part = tid / D, ch = tid % D;
+  float gl[HC], ml[HC];
+  if (tid < 2 * D) {
     float acc = 0.f, mu = 0.f;
 #pragma unroll
-    for (int t = 0; t < C; ++t) {
-      acc += lgc[t];
-      mu += mxs[t];
-      sG[t * GP + tid] = acc - mu;
-      if (tid == 0) sMu[t] = mu;
+    for (int t4 = 0; t4 < HC / 4; ++t4) {
+      const f32x4 m4 = *reinterpret_cast<const f32x4*>(sMax + part * HC + 4 * t4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 4 * t4 + j;
+        acc += sG[(part * HC + t) * GP + ch];
+        mu += m4[j];
+        gl[t] = acc;
+        ml[t] = mu;
+      }
     }
-    sGC[tid] = acc;
-    if (tid == 0) {
-      sMisc[0] = mu;
-      sMisc[1] = __expf(mu);
+    if (part == 0) {
+#pragma unroll
+      for (int t = 0; t < HC; ++t) sG[t * GP + ch] = gl[t] - ml[t];
+      if (ch == 0)
+#pragma unroll
+        for (int t = 0; t < HC; ++t) sMu[t] = ml[t];
+      sGC[ch] = acc;  // G at the half's end
+      if (ch == 0) sMisc[2] = mu;
+    }
+  }
+  __syncthreads();
+  if (part == 1) {
+    const float g0 = sGC[ch], m0 = sMisc[2];
+#pragma unroll
+    for (int t = 0; t < HC; ++t) sG[(HC + t) * GP + ch] = (g0 + gl[t]) - (m0 + ml[t]);
+    sGC[ch] = g0 + gl[HC - 1];  // (this thread's own entry)
+    if (ch == 0) {
+#pragma unroll
+      for (int t = 0; t < HC; ++t) sMu[HC + t] = m0 + ml[t];
+      const float muC = m0 + ml[HC - 1];
+      sMisc[0] = muC;
+      sMisc[1] = __expf(muC);
     }
   }
   __syncthreads();
@@ -261,38 +283,35 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
     const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, GP, rb, ref, cc, false);
     mma<NTK, NTK>(acc, fa, fb);
   }
-  // The sixteen 4-token diagonal blocks term by term; thread = (block, row i,
-  // channel quarter q).  Every thread reads every column token of its block
-  // (straight-line loads); terms with j >= i are masked.
-  const int q = tid & 3, i4 = (tid >> 2) & 3;
-  const int b0 = 4 * (tid >> 4);
-  const int ti = b0 + i4;
-  float dacc[3] = {0.f, 0.f, 0.f};
-  {
-    constexpr int QC = D / 4;
-#pragma unroll 1
-    for (int cc = 0; cc < QC; cc += 8) {
-      const int c = q * QC + cc;
-      float ki[8], hi[8];
-      lds_keys8(sKf + ti * FP + c, ki);
-      lds_f8(sG + ti * GP + c, hi);
+  // The sixteen 4-token diagonal blocks term by term: the 16 threads of block
+  // b = tid / 16 take 8 channels each (at d = 64 the second 8 idle) and form
+  // the block's six pairs (1,0), (2,0), (2,1), (3,0), (3,1), (3,2), summed over
+  // the 16 lanes.
+  const int dblk = tid >> 4, dsub = tid & 15;
+  const int b0 = 4 * dblk;
+  float dacc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (8 * dsub < D) {
+    float kk[4][8], hh[4][8];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        float kj[8], hj[8];
-        lds_keys8(sKf + (b0 + j) * FP + c, kj);
-        lds_f8(sG + (b0 + j) * GP + c, hj);
+    for (int r = 0; r < 4; ++r) {
+      lds_keys8(sKf + (b0 + r) * FP + 8 * dsub, kk[r]);
+      lds_f8(sG + (b0 + r) * GP + 8 * dsub, hh[r]);
+    }
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < i; ++j, ++p) {
         float term = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) term = fmaf(ki[e] * kj[e], __expf(hi[e] - hj[e]), term);
-        dacc[j] += (j < i4) ? term : 0.f;
+        for (int e = 0; e < 8; ++e) term = fmaf(kk[i][e] * kk[j][e], __expf(hh[i][e] - hh[j][e]), term);
+        dacc[p] = term;
       }
-    }
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      dacc[j] += __shfl_xor(dacc[j], 1, 64);
-      dacc[j] += __shfl_xor(dacc[j], 2, 64);
-    }
   }
+#pragma unroll
+  for (int p = 0; p < 6; ++p)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) dacc[p] += __shfl_xor(dacc[p], o, 64);
   if constexpr (N_ON_G) __syncthreads();  // every reader of sG is done: sN takes its memory
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -309,11 +328,12 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
     }
     if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
   }
-  if (q == 0) {
-    const float bi = sBeta[ti];
+  if (dsub == 0) {
+    int p = 0;
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < i4) sN[ti * NP + b0 + j] = bi * dacc[j];
+    for (int i = 1; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < i; ++j, ++p) sN[(b0 + i) * NP + b0 + j] = sBeta[b0 + i] * dacc[p];
   }
   __syncthreads();
 
