@@ -65,17 +65,12 @@ __device__ __forceinline__ f16x8 lds_a_perm_h(const f16_t* p, int off) {
 }
 
 // Elements 8m .. 8m+7 of an accumulator tile, times 2^-e, as an fp16 B fragment
-// (e is wave-uniform; e = 0 skips the multiply).
+// (e is wave-uniform).
 __device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, int e) {
   f16x8 f;
-  if (e == 0) {
+  const float s = __builtin_amdgcn_ldexpf(1.f, -e);  // (no branch on e: none between the products)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = (f16_t)acc[8 * m + j];
-  } else {
-    const float s = ldexpf(1.f, -e);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = (f16_t)(acc[8 * m + j] * s);
-  }
+  for (int j = 0; j < 8; ++j) f[j] = (f16_t)(acc[8 * m + j] * s);
   return f;
 }
 
@@ -299,15 +294,13 @@ struct StateLdsT {  // one staging buffer
 // per-row factors exp(G_C) (S) and exp(G_C - mu_C) (U) in place of the scalar
 // exp(G_C) in step 3; g accumulates mu_C.
 // 8 waves: wave w keeps the 32 state columns 32 (w & 3) .. of U (w < 4) or S
-// (w >= 4) in accumulators.  The loads of chunk c+1 are in flight while chunk c
-// is computed.  NBUF = 2: chunk c+1 is staged into the other LDS buffer (one
-// barrier per chunk, one workgroup per CU); NBUF = 1: into the same buffer
-// after a barrier (two per chunk), at half the LDS and at most 128 registers,
-// so that two workgroups share a CU and cover each other's waits.
-template <int NBUF, bool KDA>
-__global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(const BuildArgs a,
-                                                                             const ChunkTable cks,
-                                                                             const unsigned char* ws) {
+// (w >= 4) in accumulators.  One staging buffer: chunk c+1 is loaded after chunk
+// c's products and stored over the buffer after a barrier (two per chunk); at
+// about 60 KB of LDS and at most 128 registers two workgroups share a CU and
+// cover each other's waits.
+template <bool KDA>
+__global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, const ChunkTable cks,
+                                                             const unsigned char* ws) {
   using StateLds = StateLdsT<KDA>;
   constexpr int RB = KDA ? KREC_BYTES : REC_BYTES;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -385,9 +378,9 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
       fin[2] = reinterpret_cast<const float*>(rec + REC_RS)[tid];
     }
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&] {
     const int tid = opaque(threadIdx.x);
-    unsigned char* base = smem + buf * StateLds::BUF;
+    unsigned char* base = smem;
     const int id = tid & 255, tb = id & 15, db = id >> 4;
     if (tid < 256) {  // keys: exact bf16 -> fp16 (KDA: Kb, already fp16), row-major
       f16_t* sK = reinterpret_cast<f16_t*>(base + StateLds::O_K);
@@ -451,16 +444,14 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
   };
 
   load_chunk(0);
-  store_chunk(0);
+  store_chunk();
   __syncthreads();
 
   for (int c = 0; c < n_ck; ++c) {
-    // NBUF = 2: the next chunk's loads fly during this chunk's products; NBUF = 1:
-    // they are issued after them (no staging registers live across the products)
-    // and the other workgroup on the CU runs meanwhile.
-    if (NBUF == 2 && c + 1 < n_ck) load_chunk(c + 1);
+    // (the next chunk's loads are issued after the products, so no staging
+    // registers live across them; the other workgroup on the CU runs meanwhile)
     {
-      const unsigned char* base = smem + (NBUF == 2 ? (c & 1) : 0) * StateLds::BUF;
+      const unsigned char* base = smem;
       const f16_t* sK = reinterpret_cast<const f16_t*>(base + StateLds::O_K);
       const f16_t* sKt = reinterpret_cast<const f16_t*>(base + StateLds::O_KT);
       const bf16_t* sVt = reinterpret_cast<const bf16_t*>(base + StateLds::O_V);
@@ -594,15 +585,11 @@ __global__ __launch_bounds__(512, NBUF == 1 ? 4 : 2) void delta_state_kernel(con
       }
     }
     if (c + 1 < n_ck) {  // (one branch, so the staging registers die with it)
-      if (NBUF == 1) {
-        load_chunk(c + 1);
-        __syncthreads();  // every wave is done with the buffer
-      }
-      store_chunk(NBUF == 2 ? (c + 1) & 1 : 0);
-    } else if (NBUF == 1) {
+      load_chunk(c + 1);
+      __syncthreads();  // every wave is done with the buffer
+      store_chunk();
       __syncthreads();
     }
-    __syncthreads();
   }
 
   const int lane = threadIdx.x & 63;
@@ -621,19 +608,13 @@ size_t delta2_workspace_bytes(const SegTable& seg, int n_chain) {
 }
 
 namespace {
-// The delta state pass keeps one staging buffer (two workgroups per CU); the KDA
-// mode stages three more 16-byte pieces per thread (its transposed keys come
-// from the record), which at the one-buffer register budget spills, so it keeps
-// two buffers and one workgroup per CU.
 template <bool KDA>
 hipError_t launch_state(const BuildArgs& a, const ChunkTable& ct, const unsigned char* w, hipStream_t stream) {
-  constexpr int NBUF = KDA ? 2 : 1;
-  constexpr int lds = NBUF * StateLdsT<KDA>::BUF;
+  constexpr int lds = StateLdsT<KDA>::BUF;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&delta_state_kernel<NBUF, KDA>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      reinterpret_cast<const void*>(&delta_state_kernel<KDA>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((delta_state_kernel<NBUF, KDA>), dim3(a.seg.n_seg * a.n_chain), dim3(512), lds, stream, a, ct,
-                     w);
+  hipLaunchKernelGGL((delta_state_kernel<KDA>), dim3(a.seg.n_seg * a.n_chain), dim3(512), lds, stream, a, ct, w);
   return hipGetLastError();
 }
 }  // namespace
