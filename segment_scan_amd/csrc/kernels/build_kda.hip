@@ -22,17 +22,22 @@
 // Every factor is at most 1 whatever the gates, and the result equals running
 // the tokens one by one (the tests check this algebra against the token-by-
 // token oracle).  The Gram terms exp(H_ic - H_jc) are formed without overflow:
-// blocks of earlier tokens are scaled against a reference token between the
-// two blocks (both factors <= 1), and the four 16-token diagonal blocks are
-// summed term by term.
+// block pairs of 32, 16, 8 and 4 tokens go through keys decayed against a
+// reference token between the two blocks (both factors <= 1), and the sixteen
+// 4-token diagonal blocks are summed term by term.
 //
-// Mapping (one workgroup of 4 waves per unit, as the delta build): the state
-// [U | S] (d x 2d fp32) lives in MFMA accumulators for the whole segment,
-// waves 0-1 holding U and waves 2-3 S, d/2 columns each.  Per chunk the keys,
-// gate prefixes, the decayed key copies (split into bf16 terms) and X sit in
-// LDS; the off-diagonal Gram blocks run on bf16 MFMA with operands decayed on
-// the fly; the 64 x 64 inverse takes its 32 x 32 diagonal blocks by forward
-// substitution and the off-diagonal block by two MFMA products.
+// Two forms.  For d = 128 with bf16 tokens and segments of at most 2048 tokens
+// the chunks' factors come from a parallel factor pass (kda_prep_kernel, one
+// workgroup per chunk and chain) that writes a record per chunk (layout in
+// launch.h), and the delta state kernel of build_delta2.hip runs the three
+// products on the records.  Otherwise one workgroup of 4 waves per unit does
+// both (build_kda_kernel): the state [U | S] (d x 2d fp32) lives in MFMA
+// accumulators for the whole segment, waves 0-1 holding U and waves 2-3 S, d/2
+// columns each, and per chunk the keys, gate prefixes, the decayed key copies
+// (split into bf16 terms) and X sit in LDS.  In both, the off-diagonal Gram
+// blocks run on bf16 MFMA with operands decayed on the fly, and the 64 x 64
+// inverse takes its 32 x 32 diagonal blocks by forward substitution and the
+// off-diagonal block by two MFMA products.
 #include <type_traits>
 
 #include "common.h"
