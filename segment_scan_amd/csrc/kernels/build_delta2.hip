@@ -64,11 +64,10 @@ __device__ __forceinline__ f16x8 lds_a_perm_h(const f16_t* p, int off) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Elements 8m .. 8m+7 of an accumulator tile, times 2^-e, as an fp16 B fragment
-// (e is wave-uniform).
-__device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, int e) {
+// Elements 8m .. 8m+7 of an accumulator tile, times the wave-uniform s, as an
+// fp16 B fragment (always multiplied: no branch separates the products).
+__device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, float s) {
   f16x8 f;
-  const float s = __builtin_amdgcn_ldexpf(1.f, -e);  // (no branch on e: none between the products)
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = (f16_t)(acc[8 * m + j] * s);
   return f;
@@ -461,14 +460,16 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
       const int h = lane >> 5, l32 = lane & 31;
       const float eGC = sF[2 * C];
       f32x16 W[2];
-      // ---- step 1: Y = K Z ----------------------------------------------------------
+      // ---- step 1: Y = K Z (S waves: exp(G_C) K Z, the factor folded into Z's conversion)
       {
         float m = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(Z[rt][r]));
-        const int ez = f16_scale_exp(wave_max_uniform(m));
+        const float gz = s_wave ? eGC : 1.f;
+        const int ez = f16_scale_exp(wave_max_uniform(m) * gz);
+        const float sz = gz * ldexpf(1.f, -ez);
         const f16_t* pK = sK + l32 * KP + 4 * h;
         W[0] = zero16();
         W[1] = zero16();
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) {
-            const f16x8 fb = acc_as_b_h(Z[rt], mm, ez);
+            const f16x8 fb = acc_as_b_h(Z[rt], mm, sz);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
           }
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
               const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
                                    __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
 #pragma unroll
-              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] = fmaf(ew[j], v4[j], -eGC * W[tt][4 * q + j]);
+              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] = fmaf(ew[j], v4[j], -W[tt][4 * q + j]);  // (W carries exp(G_C))
             }
         }
         float m = 0.f;
@@ -513,10 +514,11 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
         const int er = f16_scale_exp(wave_max_uniform(m));
         const f16_t* pA = sA0 + l32 * TP + 4 * h;
         f16x8 fb[2][2];
+        const float sr = ldexpf(1.f, -er);
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) fb[tp][mm] = acc_as_b_h(W[tp], mm, er);
+          for (int mm = 0; mm < 2; ++mm) fb[tp][mm] = acc_as_b_h(W[tp], mm, sr);
         W[0] = zero16();
         W[1] = zero16();
 #pragma unroll
@@ -566,11 +568,12 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
           }
         }
         const f16_t* pKt = sKt + l32 * TP + 4 * h;
+        const float sx = ldexpf(1.f, -ex);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) {
-            const f16x8 fb = acc_as_b_h(W[tt], mm, ex);
+            const f16x8 fb = acc_as_b_h(W[tt], mm, sx);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
               Z[rt] = mfma32h(lds_a_perm_h(pKt, 32 * rt * TP + 32 * tt + 16 * mm), fb, Z[rt]);
