@@ -128,6 +128,21 @@ __device__ __forceinline__ Frag<NT> decayed_frag(const KT* sKf, const float* sH,
   return split8<NT>(x);
 }
 
+// The same eight decayed keys as one fp16 fragment (every value is at most |k|
+// in magnitude, so fp16 holds it with 11 significant bits).
+template <typename KT>
+__device__ __forceinline__ f16x8 decayed_frag_h(const KT* sKf, const float* sH, int FP, int GP, int t, int ref, int c0,
+                                               bool toward) {
+  float k[8], ht[8], hr[8];
+  lds_keys8(sKf + t * FP + c0, k);
+  lds_f8(sH + t * GP + c0, ht);
+  lds_f8(sH + ref * GP + c0, hr);
+  f16x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (f16_t)(k[j] * __expf(toward ? ht[j] - hr[j] : hr[j] - ht[j]));
+  return f;
+}
+
 template <int NT>
 __device__ __forceinline__ void split4_store(bf16_t* p, int term_stride, const float (&x)[4]) {
   float r[4] = {x[0], x[1], x[2], x[3]};
@@ -150,11 +165,14 @@ __device__ __forceinline__ void split4_store(bf16_t* p, int term_stride, const f
 // M = diag(b) (K o e^H)(K o e^-H)^T formed without overflow; and N = (I + M)^-1,
 // left in sN.  Every thread of the 256-thread workgroup calls it (it holds
 // barriers).  early() runs in every thread once H, sMu, sGC and sMisc ([0] =
-// mu_C, [1] = exp(mu_C)) are valid, before the Gram.  N_ON_G: sN shares the
+// mu_C, [1] = exp(mu_C)) are valid, before the Gram.  GRAM_F16: the Gram's
+// decayed keys enter the MFMA as one fp16 term each (bf16 tokens: the Gram then
+// carries about 2^-11 relative error, the class of the fp16 X it feeds)
+// instead of bf16 terms.  N_ON_G: sN shares the
 // memory of sG, so sG is valid only until the Gram (early() is its last
 // reader); otherwise sKf, sG, sN, sBeta, sMu, sGC and sMisc are all valid on
 // return.
-template <int D, bool IN_F32, bool WITH_V, bool N_ON_G, typename KT, typename Early>
+template <int D, bool IN_F32, bool WITH_V, bool N_ON_G, typename KT, typename Early, bool GRAM_F16 = false>
 __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, int nv, int chain, KT* sKf, KT* sV,
                                                   float* sG, float* sN, float* sBeta, float* sMax, float* sMu,
                                                   float* sGC, float* sMisc, Early early) {
@@ -284,9 +302,14 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
 #pragma unroll 2
   for (int ks = 0; ks < D / 16; ++ks) {
     const int cc = 16 * ks + 8 * h;
-    const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, FP, GP, ra, ref, cc, true);
-    const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, GP, rb, ref, cc, false);
-    mma<NTK, NTK>(acc, fa, fb);
+    if constexpr (GRAM_F16) {
+      acc = mfma32h(decayed_frag_h(sKf, sG, FP, GP, ra, ref, cc, true),
+                    decayed_frag_h(sKf, sG, FP, GP, rb, ref, cc, false), acc);
+    } else {
+      const Frag<NTK> fa = decayed_frag<NTK>(sKf, sG, FP, GP, ra, ref, cc, true);
+      const Frag<NTK> fb = decayed_frag<NTK>(sKf, sG, FP, GP, rb, ref, cc, false);
+      mma<NTK, NTK>(acc, fa, fb);
+    }
   }
   // The sixteen 4-token diagonal blocks term by term: the 16 threads of block
   // b = tid / 16 take 8 channels each (at d = 64 the second 8 idle) and form
@@ -713,8 +736,8 @@ __global__ __launch_bounds__(256, 3) void kda_prep_kernel(const BuildArgs a, con
       reinterpret_cast<float*>(rec + KREC_M)[1] = sMisc[1];
     }
   };
-  kda_chunk_factors<D, false, false, true>(a, c0, nv, chain, sKf, (bf16_t*)nullptr, sG, sN, sBeta, sMax, sMu, sGC,
-                                           sMisc, early);
+  kda_chunk_factors<D, false, false, true, bf16_t, decltype(early), true>(a, c0, nv, chain, sKf, (bf16_t*)nullptr, sG,
+                                                                        sN, sBeta, sMax, sMu, sGC, sMisc, early);
 
   {  // X = N diag(b), row t by the four threads 4t .. 4t+3 (16 entries each)
     const int t = tid >> 2, cb = (tid & 3) * 16;
