@@ -85,6 +85,23 @@ def test_kda_strong_gates_bf16_d128():
     check_build(tk, "kda_strong_bf16_d128")
 
 
+def test_kda_bf16_d128_ragged():
+    """The factor-record path with segments that are not multiples of the
+    64-token chunk (tail chunks of 1, 63, 1, 2 and 8 tokens, a 1-token segment)."""
+    lengths = [1, 63, 64, 65, 130, 200]
+    tk = synth.kda(n_seg=1, L=sum(lengths), n_chain=3, gate_scale=1.0 / 16)
+    check_build(tk, "kda_ragged_d128", synth.ragged_offsets(lengths))
+
+
+def test_kda_many_ragged_segments_two_launches():
+    """300 ragged segments (1..130 tokens) on the factor-record path: two
+    launches that reuse one workspace, sized for the larger."""
+    rng = np.random.default_rng(5)
+    lengths = [int(x) for x in rng.integers(1, 131, 300)]
+    tk = synth.kda(n_seg=1, L=sum(lengths), n_chain=2, gate_scale=1.0 / 16)
+    check_build(tk, "kda_300seg", synth.ragged_offsets(lengths))
+
+
 def test_kda_segment_lengths_of_both_paths():
     """2048 tokens (longest of the factor-record path) and 2049 (single kernel)."""
     for L in (2048, 2049):
