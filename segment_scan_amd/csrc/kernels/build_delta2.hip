@@ -158,39 +158,11 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
   __syncthreads();
 
   // ---- N = (I + M)^-1 in 32 x 32 blocks ---------------------------------------------
-  // Diagonal blocks by forward substitution, lane 32 b + c owning column c of
-  // block b: N_bb[r][c] = delta_rc - sum_{k<r} M_bb[r][k] N_bb[k][c], rows of
-  // M read as LDS broadcasts (entries on and above the diagonal are zero).
-  {
-    const int b = lane >> 5, c = l32;
-    const float* Mb = sM + 32 * b * MP + 32 * b;
-    float x[32];
+  // The diagonal blocks in 16-blocks (common.h), then the upper-right block of
+  // N, which is zero.
+  inv_diag32_blocks(sM, MP, lane);
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      float acc0 = 0.f, acc1 = 0.f;
-      const float* Mr = Mb + r * MP;
-#pragma unroll
-      for (int k4 = 0; k4 < r / 4; ++k4) {
-        const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
-        acc0 = fmaf(m4[0], x[4 * k4], acc0);
-        acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
-        acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
-        acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
-      }
-#pragma unroll
-      for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
-      x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
-    }
-    __syncthreads();  // every lane is done reading M_bb
-    float* Nb = sM + 32 * b * MP + 32 * b;
-#pragma unroll
-    for (int r = 0; r < 32; ++r) Nb[r * MP + c] = x[r];
-    // the upper-right block of N is zero
-    if (b == 0) {
-#pragma unroll
-      for (int r = 0; r < 32; ++r) sM[r * MP + 32 + c] = 0.f;
-    }
-  }
+  for (int r = 0; r < 16; ++r) sM[(16 * (lane >> 5) + r) * MP + 32 + l32] = 0.f;  // rows 0..31
   __syncthreads();
   // Off-diagonal block N_10 = -N_11 (M_10 N_00): two 32 x 32 x 32 products on
   // bf16 MFMA with both operands split into two terms (about 2^-16 relative).

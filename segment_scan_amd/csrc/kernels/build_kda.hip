@@ -366,36 +366,10 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
   __syncthreads();
 
   // ---- N = (I + M)^-1 in 32 x 32 blocks, by wave 0 (the others wait) ---------
-  // Diagonal blocks by forward substitution, lane 32 b + c owning column c of
-  // block b: N_bb[r][c] = delta_rc - sum_{k<r} M_bb[r][k] N_bb[k][c], rows of M
-  // read as LDS broadcasts (only entries below the diagonal are read); then
-  // N_10 = -N_11 (M_10 N_00) as two 32 x 32 x 32 products on MFMA with both
-  // operands split into bf16 terms.
-  if (wave == 0) {
-    const int b = lane >> 5, c = l32;
-    const float* Mb = sN + 32 * b * NP + 32 * b;
-    float x[32];
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      float acc0 = 0.f, acc1 = 0.f;
-      const float* Mr = Mb + r * NP;
-#pragma unroll
-      for (int k4 = 0; k4 < r / 4; ++k4) {
-        const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
-        acc0 = fmaf(m4[0], x[4 * k4], acc0);
-        acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
-        acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
-        acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
-      }
-#pragma unroll
-      for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
-      x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
-    }
-    // (the wave's lanes have all read M_bb: a wave runs in lockstep, and the
-    // writes below touch only N_bb's own block)
-#pragma unroll
-    for (int r = 0; r < 32; ++r) sN[(32 * b + r) * NP + 32 * b + c] = x[r];
-  }
+  // The diagonal blocks in 16-blocks (common.h); then N_10 = -N_11 (M_10 N_00)
+  // as two 32 x 32 x 32 products on MFMA with both operands split into bf16
+  // terms.
+  if (wave == 0) inv_diag32_blocks(sN, NP, lane);
   __syncthreads();
   {
     auto prod = [&](const float* Ab, const float* Bb) {  // 32 x 32 blocks of sN; Ab Bb

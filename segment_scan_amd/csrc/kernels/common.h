@@ -250,6 +250,101 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
   return x;
 }
 
+// ---- (I + M)^-1 of the two 32 x 32 diagonal blocks of a 64 x 64 array -----------
+// M strictly lower triangular in sM (fp32, pitch P floats, P % 4 == 0, rows
+// 16-byte aligned); on return the two diagonal 32 x 32 blocks hold N_bb =
+// (I + M_bb)^-1 in full (ones on the diagonal, zeros above), the rest of sM
+// untouched.  Run by one whole wave, with no workgroup barrier inside (the
+// caller orders it against other waves).  Each 32-block is split in two:
+//   the four 16 x 16 diagonal blocks by forward substitution, lane 16 q + c
+//   owning column c of block q (rows of M read as LDS broadcasts, only entries
+//   below the diagonal);
+//   the off-diagonal 16 x 16 block of each 32-block, N_10 = -N_11 (M_10 N_00),
+//   as two 16x16x16 bf16 MFMA products with both operands split into two
+//   terms (about 2^-16 relative), the first product's result feeding the
+//   second from registers.
+// (16x16x16 layout: lane l holds A[l % 16][4 (l / 16) + j], B[4 (l / 16) + j][l % 16]
+// and D[4 (l / 16) + j][l % 16], j = 0..3.)
+__device__ __forceinline__ void bf16_split4(const float (&x)[4], bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hi[j] = (bf16_t)x[j];
+    lo[j] = (bf16_t)(x[j] - (float)hi[j]);
+  }
+}
+__device__ __forceinline__ f32x4 mma16_split(const float (&a)[4], const float (&b)[4], f32x4 c) {
+  bf16x4 ah, al, bh, bl;
+  bf16_split4(a, ah, al);
+  bf16_split4(b, bh, bl);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+}
+// The wave's LDS operations issued so far have completed (lgkmcnt(0) alone:
+// the gfx9 s_waitcnt field layout, vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void inv_diag32_blocks(float* sM, int P, int lane) {
+  {  // 16 x 16 diagonal blocks
+    const int q = lane >> 4, c = lane & 15;
+    const float* Mb = sM + 16 * q * P + 16 * q;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc0 = 0.f, acc1 = 0.f;
+      const float* Mr = Mb + r * P;
+#pragma unroll
+      for (int k4 = 0; k4 < r / 4; ++k4) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + 4 * k4);
+        acc0 = fmaf(m4[0], x[4 * k4], acc0);
+        acc1 = fmaf(m4[1], x[4 * k4 + 1], acc1);
+        acc0 = fmaf(m4[2], x[4 * k4 + 2], acc0);
+        acc1 = fmaf(m4[3], x[4 * k4 + 3], acc1);
+      }
+#pragma unroll
+      for (int k = r & ~3; k < r; ++k) acc0 = fmaf(Mr[k], x[k], acc0);
+      x[r] = (r < c) ? 0.f : ((r == c) ? 1.f : -(acc0 + acc1));
+    }
+    wave_lds_sync();  // every lane has read its block of M
+    float* Nb = sM + 16 * q * P + 16 * q;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Nb[r * P + c] = x[r];
+    // the upper-right 16 x 16 block of each 32-block is zero: lane 32 b + 16 h + c
+    // clears rows 32 b + 8 h .. + 7, column 32 b + 16 + c
+    const int b = lane >> 5, h = (lane >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sM[(32 * b + 8 * h + r) * P + 32 * b + 16 + c] = 0.f;
+  }
+  wave_lds_sync();
+  const int i16 = lane & 15, k4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int o = 32 * b;
+    float a[4], bb[4], p[4];
+    const f32x4 m10 = *reinterpret_cast<const f32x4*>(sM + (o + 16 + i16) * P + o + k4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] = m10[j];
+      bb[j] = sM[(o + k4 + j) * P + o + i16];  // N_00
+    }
+    const f32x4 P10 = mma16_split(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});  // M_10 N_00
+    const f32x4 n11 = *reinterpret_cast<const f32x4*>(sM + (o + 16 + i16) * P + o + 16 + k4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] = n11[j];
+      p[j] = P10[j];
+    }
+    const f32x4 Q = mma16_split(a, p, f32x4{0.f, 0.f, 0.f, 0.f});  // N_11 (M_10 N_00)
+    wave_lds_sync();  // every lane has read M_10
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sM[(o + 16 + k4 + j) * P + o + i16] = -Q[j];
+  }
+  wave_lds_sync();
+}
+
 // LDS tile of bf16 with 64 columns (128 B rows), 16-byte column chunks
 // XOR-swizzled by (row & 7): consecutive rows read at the same logical chunk
 // hit distinct banks, and an 8-row transposed write does too.
