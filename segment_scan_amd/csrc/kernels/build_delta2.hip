@@ -146,14 +146,21 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
       g11 = mfma32(f1, f1, g11);
     }
   }
-  // M = strict_lower(diag(beta) K K^T) into LDS (row-major; upper part unused)
+  // A0 = (I + B L)^-1 B with B = diag(beta), L = strict_lower(K K^T), formed as
+  // B (I + L B)^-1 (the two are equal: B (I + L B) = (I + B L) B), so that the
+  // weights scale columns of the Gram here (one factor per lane) and rows of
+  // the inverse at the end (one factor per row, folded into its fp16 scale).
+  // M = L B into LDS (row-major; upper part unused)
   __syncthreads();
+  {
+    const float b0 = sBeta[l32], b1 = sBeta[32 + l32];  // the lane's columns
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = acc_row(r, lane);
-    sM[row * MP + l32] = (row > l32) ? sBeta[row] * g00[r] : 0.f;
-    sM[(32 + row) * MP + l32] = sBeta[32 + row] * g10[r];
-    sM[(32 + row) * MP + 32 + l32] = (row > l32) ? sBeta[32 + row] * g11[r] : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const int row = acc_row(r, lane);
+      sM[row * MP + l32] = (row > l32) ? b0 * g00[r] : 0.f;
+      sM[(32 + row) * MP + l32] = b0 * g10[r];
+      sM[(32 + row) * MP + 32 + l32] = (row > l32) ? b1 * g11[r] : 0.f;
+    }
   }
   __syncthreads();
 
@@ -201,26 +208,25 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
   }
   __syncthreads();
 
-  // ---- A0 = N diag(beta) (column j scaled by beta_j); rows to fp16 with row scales --
+  // ---- A0 = diag(beta) N (row t scaled by beta_t); rows to fp16 with row scales -----
   unsigned char* rec = ws + (size_t)blockIdx.x * REC_BYTES;
   {
     const int t = lane;  // row of A0
-    float* Ar = sM + t * MP;
+    const float* Ar = sM + t * MP;
     float m = 0.f;
 #pragma unroll
     for (int j4 = 0; j4 < C / 4; ++j4) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(Ar + 4 * j4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] *= sBeta[4 * j4 + j];
-      *reinterpret_cast<f32x4*>(Ar + 4 * j4) = v;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(Ar + 4 * j4);
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
+    const float bt = sBeta[t];
+    m *= fabsf(bt);
     int e = 0;
     if (m > 0.f) {
       frexpf(m, &e);
       e -= 14;  // row maximum into [2^13, 2^14)
     }
-    const float s = ldexpf(1.f, -e);
+    const float s = bt * ldexpf(1.f, -e);
     f16x8* dst = reinterpret_cast<f16x8*>(rec + REC_A + t * C * 2);
 #pragma unroll
     for (int j8 = 0; j8 < C / 8; ++j8) {

@@ -16,6 +16,9 @@
 // is a generalised WY product whose two sides carry the keys decayed in
 // opposite directions:
 //   M[i,j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc)   (i > j),  X = (I + M)^-1 diag(b)
+//   (formed as X = diag(b) (I + L diag(b))^-1 with L the Gram without the
+//   weights: the two are equal, and the weights then scale the Gram's columns
+//   and the inverse's rows)
 //   Kb = K o exp(H),  Kd = (K o exp(H_C - H))^T
 //   U <- diag(exp(G_C - mu_C)) U - Kd X (Kb U),   g += mu_C
 //   S <- diag(exp(G_C)) S + Kd X (diag(exp(mu_C - mu)) V - exp(mu_C) Kb S)
@@ -162,8 +165,8 @@ __device__ __forceinline__ void split4_store(bf16_t* p, int term_stride, const f
 // The factor phases of one 64-token chunk, shared by the single-kernel build and
 // the factor pass: stage the chunk's keys (and values), gates and weights;
 // per-channel prefixes in place as H = G - mu; the strictly lower Gram
-// M = diag(b) (K o e^H)(K o e^-H)^T formed without overflow; and N = (I + M)^-1,
-// left in sN.  Every thread of the 256-thread workgroup calls it (it holds
+// L diag(b), L = (K o e^H)(K o e^-H)^T, formed without overflow; and
+// N = (I + L diag(b))^-1, left in sN (X = diag(b) N).  Every thread of the 256-thread workgroup calls it (it holds
 // barriers).  early() runs in every thread once H, sMu, sGC and sMisc ([0] =
 // mu_C, [1] = exp(mu_C)) are valid, before the Gram.  GRAM_F16: the Gram's
 // decayed keys enter the MFMA as one fp16 term each (bf16 tokens: the Gram then
@@ -276,7 +279,7 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
   __syncthreads();
   early();
 
-  // ---- Gram M[i][j] = b_i sum_c k_ic k_jc exp(H_ic - H_jc), i > j ------------
+  // ---- Gram L[i][j] b_j = b_j sum_c k_ic k_jc exp(H_ic - H_jc), i > j ---------
   // Each wave forms one 32 x 32 MFMA tile of products of decayed keys, both
   // factors decayed against a reference token between the row and the column
   // tokens (so both are <= |k|); parts of a tile whose row and column refer to
@@ -354,14 +357,14 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
       i = (ga << (sh + 1)) + (1 << sh) + (rho & ((1 << sh) - 1));
       keep = ga == (l32 >> sh);
     }
-    if (keep) sN[i * NP + rb] = sBeta[i] * acc[r];
+    if (keep) sN[i * NP + rb] = sBeta[rb] * acc[r];
   }
   if (dsub == 0) {
     int p = 0;
 #pragma unroll
     for (int i = 1; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < i; ++j, ++p) sN[(b0 + i) * NP + b0 + j] = sBeta[b0 + i] * dacc[p];
+      for (int j = 0; j < i; ++j, ++p) sN[(b0 + i) * NP + b0 + j] = sBeta[b0 + j] * dacc[p];
   }
   __syncthreads();
 
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
                                               [] {});
     if (wave == 0) g_acc += (double)sMisc[0];  // mu_C; every lane of wave 0 keeps the same sum
 
-    // ---- X = N diag(beta) split to bf16 terms; decayed key copies ------------
+    // ---- X = diag(beta) N split to bf16 terms; decayed key copies ------------
     {
       const int t = tid >> 2;
       const int cb = (tid & 3) * 16;
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
       for (int half = 0; half < 2; ++half) {
         float x0[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x0[j] = nv16[8 * half + j] * sBeta[cb + 8 * half + j];
+        for (int j = 0; j < 8; ++j) x0[j] = nv16[8 * half + j] * sBeta[t];
         const Frag<NTD> f0 = split8<NTD>(x0);
 #pragma unroll
         for (int i = 0; i < NTD; ++i) st8(sA + i * ATS + t * TP + cb + 8 * half, f0.t[i]);
@@ -713,24 +716,26 @@ __global__ __launch_bounds__(256, 3) void kda_prep_kernel(const BuildArgs a, con
   kda_chunk_factors<D, false, false, true, bf16_t, decltype(early), true>(a, c0, nv, chain, sKf, (bf16_t*)nullptr, sG,
                                                                         sN, sBeta, sMax, sMu, sGC, sMisc, early);
 
-  {  // X = N diag(b), row t by the four threads 4t .. 4t+3 (16 entries each)
+  {  // X = diag(b) N, row t by the four threads 4t .. 4t+3 (16 entries each)
     const int t = tid >> 2, cb = (tid & 3) * 16;
     float x[16];
     float m = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int tp = cb + j;
-      x[j] = (tp <= t) ? sN[t * NP + tp] * sBeta[tp] : 0.f;
+      x[j] = (tp <= t) ? sN[t * NP + tp] : 0.f;
       m = fmaxf(m, fabsf(x[j]));
     }
     m = dpp_max_step(m, 0);  // the row's four lanes: a quad
     m = dpp_max_step(m, 1);
+    const float bt = sBeta[t];
+    m *= fabsf(bt);
     int e = 0;
     if (m > 0.f) {
       frexpf(m, &e);
       e -= 14;  // row maximum into [2^13, 2^14)
     }
-    const float sc = ldexpf(1.f, -e);
+    const float sc = bt * ldexpf(1.f, -e);
     f16x8 lo8, hi8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
