@@ -16,10 +16,10 @@
 // Nothing in A0 depends on the running state, so the per-chunk factors are a
 // separate, fully parallel job:
 //  - delta_prep: one wave per (segment, chunk, chain) builds the Gram matrix on
-//    MFMA, inverts (I + M) in 32 x 32 blocks (diagonal blocks by forward
-//    substitution in fp32, the off-diagonal block by two MFMA products), and
-//    writes A0 (fp16, each row scaled by a power of two) with the gate prefix G
-//    to a workspace;
+//    MFMA, inverts (I + M) in 32 x 32 blocks (each diagonal block from four
+//    16 x 16 forward substitutions in fp32 and 16x16 MFMA products, the
+//    off-diagonal block by two MFMA products), and writes A0 (fp16, each row
+//    scaled by a power of two) with the gate prefix G to a workspace;
 //  - delta_state: one workgroup per (segment, chain) keeps [U | S] in MFMA
 //    accumulators (8 waves x 32 columns) and, per chunk, stages K (row-major
 //    and transposed), V and A0 in LDS and runs the three products.
