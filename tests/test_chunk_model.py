@@ -27,6 +27,51 @@ def test_in_place_inverse_order():
     np.testing.assert_allclose(N @ (np.eye(64) + M), np.eye(64), atol=1e-12)
 
 
+def test_two_level_block_inverse():
+    """The factor passes' order: each 32 x 32 diagonal block from its two 16 x 16
+    diagonal inverses and N_10 = -N_11 (M_10 N_00) at 16, then the same formula
+    for the 32 x 32 off-diagonal block."""
+    r = np.random.default_rng(2)
+    M = np.tril(r.standard_normal((64, 64)) * 0.1, -1)
+
+    def two_by_two(M, h, inv_diag):
+        A, C, D = M[:h, :h], M[h:, :h], M[h:, h:]
+        N00, N11 = inv_diag(A), inv_diag(D)
+        N = np.zeros_like(M)
+        N[:h, :h], N[h:, h:] = N00, N11
+        N[h:, :h] = -N11 @ (C @ N00)
+        return N
+
+    def sub16(A):  # forward substitution, column by column
+        n = A.shape[0]
+        N = np.zeros((n, n))
+        for c in range(n):
+            x = np.zeros(n)
+            for rr in range(n):
+                x[rr] = 0.0 if rr < c else (1.0 if rr == c else -A[rr, :rr] @ x[:rr])
+            N[:, c] = x
+        return N
+
+    N = two_by_two(M, 32, lambda B: two_by_two(B, 16, sub16))
+    np.testing.assert_allclose(N @ (np.eye(64) + M), np.eye(64), atol=1e-12)
+
+
+def test_weights_on_columns_then_rows():
+    """A0 = (I + diag(b) L)^-1 diag(b) equals diag(b) (I + L diag(b))^-1 (L the
+    strictly lower Gram), the form the factor passes compute; zero weights
+    (tokens past a segment's end) included."""
+    r = np.random.default_rng(3)
+    K = r.standard_normal((64, 128))
+    K /= np.linalg.norm(K, axis=1, keepdims=True)
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal(64)))
+    b[50:] = 0.0
+    L = np.tril(K @ K.T, -1)
+    B = np.diag(b)
+    lhs = np.linalg.inv(np.eye(64) + B @ L) @ B
+    rhs = B @ np.linalg.inv(np.eye(64) + L @ B)
+    np.testing.assert_allclose(rhs, lhs, atol=1e-12)
+
+
 @pytest.mark.parametrize("gate_scale", [1.0, 1.0 / 64, 0.0])
 @pytest.mark.parametrize("L", [256, 200, 64, 5])
 def test_delta_chunked_build_matches_oracle(gate_scale, L):
