@@ -281,6 +281,16 @@ def warm_seam_layer(layer: int, n_seg=WARM_SEGS, w=WARM_W, n_head=WARM_HEADS, d=
                   {"workload": "gdn_warm100k", "layer": layer, "n_seg": n_seg, "w": w})
 
 
+def warm_seam_layer_kda(layer: int, n_seg=WARM_SEGS, w=WARM_W, n_head=WARM_HEADS, d=WARM_D, dtype="bf16",
+                        gate_scale=1.0 / 8) -> Tokens:
+    """Seam-window tokens of one KDA layer: as warm_seam_layer, the log gates
+    drawn per token and key channel."""
+    q, k, v, beta, _ = _draw_delta_tokens(15, n_seg * w, n_head, d, dtype, None, layer=layer)
+    lg = round_to(-_softplus(rng(15, T_GATE, layer).standard_normal((n_seg * w, n_head, d))) * gate_scale, dtype)
+    return Tokens(KDA, dtype, n_head, d, d, k, v, q, beta, lg, False, None,
+                  {"workload": "kda_warm100k", "layer": layer, "n_seg": n_seg, "w": w})
+
+
 def concat_chains(parts):
     """Concatenate per-layer token batches along the chain axis (chain = layer*heads + head)."""
     p0 = parts[0]

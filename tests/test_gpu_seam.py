@@ -109,6 +109,45 @@ def test_warm_reuse_full_size_layers_0_and_29():
         assert_units_close("full.o.l%d" % layer, ow, rw, TOL["bf16"])
 
 
+def test_kda_warm_reuse_full_size_layers_0_and_29():
+    """The warm request with KDA layers (480 chains, per-channel gates) in one
+    launch, as the benchmark runs it; layers 0 and 29 compared element by element."""
+    import torch
+    from segment_scan_amd.synth import KDA
+    H, d, n_seg, w = synth.WARM_HEADS, synth.WARM_D, synth.WARM_SEGS, synth.WARM_W
+    announce("kda_warm_full", "chains", 480)
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    nt = n_seg * w
+    q = torch.nn.functional.normalize(torch.randn((nt, 480, d), device="cuda", generator=gen), dim=-1).to(torch.bfloat16)
+    k = torch.nn.functional.normalize(torch.randn((nt, 480, d), device="cuda", generator=gen), dim=-1).to(torch.bfloat16)
+    v = torch.randn((nt, 480, d), device="cuda", generator=gen).to(torch.bfloat16)
+    beta = torch.sigmoid(torch.randn((nt, 480), device="cuda", generator=gen)).to(torch.bfloat16)
+    lg = (-torch.nn.functional.softplus(torch.randn((nt, 480, d), device="cuda", generator=gen)) / 8).to(torch.bfloat16)
+    U = torch.randn((n_seg, 480, d, d), device="cuda", generator=gen) * (0.5 / np.sqrt(d))
+    S = torch.randn((n_seg, 480, d, d), device="cuda", generator=gen)
+    g = torch.zeros((n_seg, 480), device="cuda")
+    layers = (0, 29)
+    parts = [synth.warm_seam_layer_kda(layer) for layer in layers]
+    pairs = [synth.warm_pairs_layer(layer) for layer in layers]
+    for li, layer in enumerate(layers):
+        sl = slice(layer * H, (layer + 1) * H)
+        up = upload_tokens(parts[li], with_q=True)
+        q[:, sl], k[:, sl], v[:, sl], beta[:, sl], lg[:, sl] = up["q"], up["k"], up["v"], up["beta"], up["log_gate"]
+        U[:, sl] = dev_f32(pairs[li][1])
+        S[:, sl] = dev_f32(pairs[li][2])
+    res = api.seam_step(KDA, w, q, k, v, beta, lg, body=(g, U, S))
+    torch.cuda.synchronize()
+    S_run, o = host(res["S_run"]), host(res["o"])
+    for li, layer in enumerate(layers):
+        sl = slice(layer * H, (layer + 1) * H)
+        tk = parts[li]
+        ref = oracle.seam(KDA, n_seg, w, tk.q, tk.k, tk.v, tk.beta, tk.log_gate, body=pairs[li])
+        assert_units_close("kda_full.S_run.l%d" % layer, S_run[sl], ref["S_run"], TOL["bf16"], unit_dims=1)
+        ow = o[:, sl].reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
+        rw = ref["o"].reshape(n_seg, w, H, -1).transpose(0, 2, 1, 3)
+        assert_units_close("kda_full.o.l%d" % layer, ow, rw, TOL["bf16"])
+
+
 def test_seam_many_chains_ragged_window():
     """72 chains (one workgroup per chain), w = 13 (a full and a partial
     8-token sub-chunk), random body pairs, nonzero start state."""
