@@ -12,23 +12,29 @@
 //
 // Work split.  Columns of the state are independent under both operations
 // (T acts on the d_k axis, a window token writes k_t v_t^T column by column),
-// so a workgroup owns one chain and a group of 32-column blocks (all of them
-// when there are enough chains to fill the GPU, one when there are few, so
-// that few chains still spread over many CUs; the workgroups of one chain are
-// placed on one XCD and share its L2 copy of U).  Wave (rb, cb) keeps the
-// 32 x 32 state tile at rows 32 rb, columns 32 cb of the group in MFMA
-// accumulators for the whole chain.
+// so a workgroup owns one unit (a chain, or a block of one chain's segments)
+// and NCT 32-column tiles of its state.  It has one wave per 32-row block:
+// wave rb keeps the state tiles at rows 32 rb .. 32 rb + 31 in MFMA
+// accumulators for the whole chain, and computes the same rows of every
+// product T = U S.  The workgroups of one unit take block ids that are equal
+// modulo 8, so the round-robin dispatch puts them on one XCD, where they share
+// its L2 copy of each U.
 //
 // Operands.  Products run on 32x32x16 fp16 MFMA with both fp32 operands as
-// hi + lo fp16 terms, keeping hi*hi + hi*lo + lo*hi: about 2^-22 relative, the
-// fp32 class, in three products where three-term bf16 needs six.  Each U (fp32
-// in HBM) is split once per workgroup into LDS, each row scaled by a power of
-// two (a thread holds a contiguous piece of a row, so the row maximum is a
-// short DPP reduction).  After every update the state is split once into
-// column-major hi/lo arrays in LDS, each column scaled by a power of two from
-// the column maxima the four row-block waves leave behind; every product then
-// reads its B fragments from there.  The next pair's U and S tile are in
-// flight during the current segment.
+// sums of NT fp16 terms (each the nearest fp16 of the remaining residual),
+// keeping the term pairs i + j < NT: NT = 3 (six products) leaves about 2^-33
+// of each operand, below fp32's own rounding, and is used wherever the pairs
+// and tokens are fp32; NT = 2 (three products, about 2^-22) serves the seam
+// step with bf16 tokens, whose outputs carry bf16 input precision anyway.
+// U (fp32 in HBM) is the A operand: wave rb reads its 32 rows straight into
+// registers one pair ahead (lane l: row 32 rb + l % 32, 8 consecutive k per
+// 16-deep step), scales them by one power of two (from the largest magnitude
+// among them) and splits each slice just before its products, reloading the
+// slice with the next pair's values as soon as it is split.  The state is the
+// B operand: after every update each wave splits its tiles once into
+// column-major term arrays in LDS, each column scaled by a power of two from
+// the column maxima the row-block waves leave behind, and every product reads
+// its B fragments from there.
 //
 // Per seam window (sub-chunks of up to 8 tokens; the chunk form of the delta
 // rule with start state S, gate prefix G within the sub-chunk, n tokens; the
@@ -41,54 +47,53 @@
 #include "common.h"
 #include "../launch.h"
 
+// state tiles per workgroup of the seam step with bf16 tokens (1, 2 or 4)
+#ifndef HYPIC_SEAM_NCT
+#define HYPIC_SEAM_NCT 2
+#endif
+
 namespace hypic {
 
 namespace {
 
 constexpr int SUB = 8;  // window tokens per sub-chunk
 
-template <int D, int NCB, bool SEAM, bool IN_F32>
+template <int D, int NCT, int NT, bool SEAM, bool IN_F32>
 struct ChainCfg {
-  static constexpr int NRB = D / 32;          // row blocks (waves per column block)
-  static constexpr int NW = NRB * NCB;        // waves
-  static constexpr int NTH = 64 * NW;
-  static constexpr int COLS = 32 * NCB;       // state columns of the workgroup
-  static constexpr int NCG = (D / 32) / NCB;  // column groups per chain
-  static constexpr int UP = D + 8;            // fp16 pitch of U rows, state columns, window rows
-  static constexpr int TPR = NTH / D;         // threads per U row while staging
-  static constexpr int LDU = D / TPR / 4;     // float4 of U per thread
+  static constexpr int NRB = D / 32;          // waves: one per 32-row block
+  static constexpr int NTH = 64 * NRB;
+  static constexpr int COLS = 32 * NCT;       // state columns of a workgroup
+  static constexpr int NCG = (D / 32) / NCT;  // workgroups (column groups) per unit
+  static constexpr int KS = D / 16;           // 16-deep k steps of a product
+  static constexpr int BP = D + 8;            // fp16 pitch of a split state column and a window row
+  static constexpr int NTA = IN_F32 ? 2 : 1;  // fp16 terms of window key and query rows
   static constexpr int NTK = IN_F32 ? 3 : 1;  // bf16 terms of window keys in the update
   static constexpr int RPP = SUB + 4;         // fp32 pitch of R' columns
-  static constexpr int OFF_UH = 0;
-  static constexpr int OFF_UL = OFF_UH + D * UP * 2;
-  static constexpr int OFF_BH = OFF_UL + D * UP * 2;
-  static constexpr int OFF_BL = OFF_BH + COLS * UP * 2;
-  static constexpr int OFF_CM = OFF_BL + COLS * UP * 2;  // column maxima per row block [NRB][COLS]
-  static constexpr int OFF_RF = OFF_CM + NRB * COLS * 4;  // exponent of each U row
-  static constexpr int OFF_W = OFF_RF + D * 4;
+  static constexpr int OFF_B = 0;                                // [NT][COLS][BP] f16
+  static constexpr int OFF_CM = OFF_B + NT * COLS * BP * 2;      // [NRB][COLS] column maxima
+  static constexpr int OFF_W = OFF_CM + NRB * COLS * 4;
   // window (SEAM): [K; Q] rows scaled and split to fp16, their scales, K^T in
   // bf16 terms, V of the group's columns, R' (column-major), the window record
-  static constexpr int OFF_AH = OFF_W;
-  static constexpr int OFF_AL = OFF_AH + 2 * SUB * UP * 2;
-  static constexpr int OFF_AS = OFF_AL + (IN_F32 ? 2 * SUB * UP * 2 : 0);
-  static constexpr int OFF_KT = OFF_AS + 2 * SUB * 4;
-  static constexpr int OFF_V = OFF_KT + NTK * D * SUB * 2;
-  static constexpr int OFF_RP = OFF_V + SUB * COLS * 4;
+  static constexpr int OFF_A = OFF_W;                            // [NTA][2 SUB][BP] f16
+  static constexpr int OFF_AS = OFF_A + NTA * 2 * SUB * BP * 2;  // [2 SUB] f32
+  static constexpr int OFF_KT = OFF_AS + 2 * SUB * 4;            // [NTK][D][SUB] bf16
+  static constexpr int OFF_V = OFF_KT + NTK * D * SUB * 2;       // [SUB][COLS] f32
+  static constexpr int OFF_RP = OFF_V + SUB * COLS * 4;          // [COLS][RPP] f32
   static constexpr int OFF_REC = OFF_RP + COLS * RPP * 4;
   static constexpr int LDS = SEAM ? OFF_REC + SEAM_REC_FLOATS * 4 : OFF_W;
-  // window token chunks of 8 elements: K and Q rows, then V rows of the group
+  // window token chunks of 8 elements: K and Q rows, then V rows of the group's columns
   static constexpr int NWCH = 2 * SUB * (D / 8) + SUB * (COLS / 8);
   static constexpr int WPT = (NWCH + NTH - 1) / NTH;  // chunks per thread
+  static_assert(NCG >= 1 && NCG * NCT == D / 32, "column groups");
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(TPR >= 2 && TPR <= 8 && LDU % 2 == 0, "U staging");
-  static_assert(2 * SUB * (D / 8) <= NTH || !SEAM, "window rows: one chunk per thread");
+  static_assert(2 * SUB * (D / 8) == NTH || !SEAM, "window rows: one chunk per thread");
 };
 
 struct ChainArgs {
   const float* g;     // pairs [n_seg, n_chain]; U, S [n_seg, n_chain, D, D]
   const float* U;
   const float* S;     // nullptr: no pairs (seam windows only)
-  const float* S_in;  // [n_chain, D, D] or nullptr (zero)
+  const float* S_in;  // [n_units, D, D] or nullptr (zero)
   float* S_out;       // may equal S_in
   float* prefix;      // compose: state before each segment, or nullptr
   float* g_tot;
@@ -119,170 +124,214 @@ __device__ __forceinline__ int split_exp(float m) {
   return e - 15;
 }
 
-// x (already scaled) -> fp16 hi and lo, both rounded to nearest:
-// |x - hi| <= 2^-11 |x| and |x - hi - lo| <= 2^-22 |x| in fp16's normal range
+// NT fp16 terms of an operand fragment
+template <int N>
+struct HFrag {
+  f16x8 t[N];
+};
+
+// 8 values (already scaled) as N fp16 terms, each the nearest fp16 of the
+// remaining residual (the residuals are exact in fp32)
+template <int N>
+__device__ __forceinline__ HFrag<N> split8h(const float (&x)[8]) {
+  HFrag<N> f;
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = x[j];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f16_t t = (f16_t)r[j];
+      f.t[i][j] = t;
+      if (i + 1 < N) r[j] -= (float)t;
+    }
+  }
+  return f;
+}
+
 __device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f16_t hi_h(float x) { return (f16_t)x; }
-__device__ __forceinline__ f16_t lo_h(float x, f16_t hi) { return (f16_t)(x - (float)hi); }
+// acc += A B on 32x32x16 fp16 MFMA, term pairs i + j < max(NA, NB), small first
+template <int NA, int NB>
+__device__ __forceinline__ void mmah(f32x16& acc, const HFrag<NA>& a, const HFrag<NB>& b) {
+  constexpr int N = NA > NB ? NA : NB;
+#pragma unroll
+  for (int s = N - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int j = s - i;
+      if (j >= 0 && j < NB) acc = mfma32h(a.t[i], b.t[j], acc);
+    }
+  }
+}
 
-template <int D, int NCB, bool SEAM, bool IN_F32>
-__global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainArgs a) {
-  using Cfg = ChainCfg<D, NCB, SEAM, IN_F32>;
-  constexpr int NRB = Cfg::NRB, NTH = Cfg::NTH, COLS = Cfg::COLS, NCG = Cfg::NCG;
-  constexpr int UP = Cfg::UP, TPR = Cfg::TPR, LDU = Cfg::LDU, NTK = Cfg::NTK, RPP = Cfg::RPP;
+// the same on 16x16x32 fp16 MFMA
+template <int NA, int NB>
+__device__ __forceinline__ void mmah16(f32x4& acc, const HFrag<NA>& a, const HFrag<NB>& b) {
+  constexpr int N = NA > NB ? NA : NB;
+#pragma unroll
+  for (int s = N - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int j = s - i;
+      if (j >= 0 && j < NB) acc = mfma16h(a.t[i], b.t[j], acc);
+    }
+  }
+}
+
+// PAIRS: the chain has cached pairs (always for composition; the seam step may
+// run its windows alone)
+template <int D, int NCT, int NT, bool SEAM, bool IN_F32, bool PAIRS>
+__global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a) {
+  using Cfg = ChainCfg<D, NCT, NT, SEAM, IN_F32>;
+  constexpr int NRB = Cfg::NRB, NTH = Cfg::NTH, COLS = Cfg::COLS, NCG = Cfg::NCG, KS = Cfg::KS;
+  constexpr int BP = Cfg::BP, NTA = Cfg::NTA, NTK = Cfg::NTK, RPP = Cfg::RPP;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  f16_t* sUh = reinterpret_cast<f16_t*>(smem + Cfg::OFF_UH);
-  f16_t* sUl = reinterpret_cast<f16_t*>(smem + Cfg::OFF_UL);
-  f16_t* sBh = reinterpret_cast<f16_t*>(smem + Cfg::OFF_BH);  // [col][row]
-  f16_t* sBl = reinterpret_cast<f16_t*>(smem + Cfg::OFF_BL);
+  f16_t* sB = reinterpret_cast<f16_t*>(smem + Cfg::OFF_B);    // [term][col][k]
   float* sCM = reinterpret_cast<float*>(smem + Cfg::OFF_CM);  // [row block][col]
-  int* sRE = reinterpret_cast<int*>(smem + Cfg::OFF_RF);  // power-of-two exponent of each U row
 
-  // ---- which chain, which columns ------------------------------------------------
-  // The NCG workgroups of one chain take block ids that are equal modulo 8, so
-  // the round-robin dispatch puts them on one XCD.
-  int chain, cgrp;
+  // ---- which unit, which columns ---------------------------------------------------
+  int unit, cgrp;
   if constexpr (NCG == 1) {
-    chain = blockIdx.x;
+    unit = blockIdx.x;
     cgrp = 0;
   } else {
-    const int blk = blockIdx.x / (8 * NCG), rem = blockIdx.x % (8 * NCG);
+    const int blk8 = blockIdx.x / (8 * NCG), rem = blockIdx.x % (8 * NCG);
     cgrp = rem / 8;
-    chain = blk * 8 + (rem % 8);
-    if (chain >= a.n_units) return;  // padding of the unit count to a multiple of 8
+    unit = blk8 * 8 + (rem % 8);
+    if (unit >= a.n_units) return;  // padding of the unit count to a multiple of 8
   }
   const bool ut = blockIdx.y == 1;  // this workgroup composes U_total instead of S
   const int n_chain = a.n_chain;
   const int col0 = cgrp * COLS;     // first state column of the workgroup
   // pairs of this unit: index pidx + s * n_chain for its segments s < nseg
-  const int blk = a.blk_len > 0 ? chain / n_chain : 0;
-  const int pidx = a.blk_len > 0 ? blk * a.blk_len * n_chain + chain % n_chain : chain;
+  const int blk = a.blk_len > 0 ? unit / n_chain : 0;
+  const int chain = a.blk_len > 0 ? unit % n_chain : unit;
+  const int pidx = a.blk_len > 0 ? blk * a.blk_len * n_chain + chain : unit;
   const int nseg = a.blk_len > 0 ? min(a.blk_len, a.n_seg - blk * a.blk_len) : a.n_seg;
-  const size_t chain_off = (size_t)chain * D * D;  // outputs, start state, tokens: by unit
+  const size_t unit_off = (size_t)unit * D * D;  // outputs and start state: by unit
   const size_t pair_off = (size_t)pidx * D * D;
   const size_t seg_stride = (size_t)n_chain * D * D;
-  const bool pairs = a.S != nullptr;
+  constexpr bool pairs = PAIRS;
 
   // Lane-derived indices.  refresh() re-derives them from an opaque copy of the
   // thread id at the top of each phase, so that addresses built from them are
   // recomputed where used instead of being kept live through the whole loop.
-  int tid, lane, rb, cb, l32, h, tcol;
+  int tid, lane, rb, l32, h;
   auto refresh = [&]() {
     tid = opaque((int)threadIdx.x);
     lane = tid & 63;
-    rb = (tid >> 6) % NRB;
-    cb = (tid >> 6) / NRB;
+    rb = tid >> 6;
     l32 = lane & 31;
     h = lane >> 5;
-    tcol = 32 * cb + l32;  // this lane's state column within the group
   };
   refresh();
 
-  // ---- U: loads, then the split into LDS -----------------------------------------
-  // thread t holds row t / TPR, float4 columns (t % TPR) + TPR i: the TPR
-  // threads of a row read whole 128-byte lines with each load instruction
-  f32x4 ureg[LDU];
-  // (seam mode: in two halves, the first flying through the whole previous
-  // segment, the second only through its product, which keeps the window phase
-  // lighter; compose mode: whole, one segment ahead)
-  auto issue_U = [&](int s, int i0, int i1) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.U + (size_t)s * seg_stride + pair_off) +
-                       (tid / TPR) * (D / 4) + tid % TPR;
-#pragma unroll
-    for (int i = 0; i < LDU; ++i)
-      if (i >= i0 && i < i1) ureg[i] = src[TPR * i];
+  // ---- U of a pair: this wave's 32 rows as A fragments ------------------------------
+  // slice ks of lane l: row 32 rb + l % 32, k = 16 ks + 8 (l / 32) + 0..7
+  f32x4 ur[KS][2];
+  auto u_src = [&](int s) {
+    return reinterpret_cast<const f32x4*>(a.U + (size_t)s * seg_stride + pair_off) +
+           ((size_t)(32 * rb + l32) * D + 8 * h) / 4;
   };
-  auto store_U = [&]() {
-    const int row = tid / TPR, c0 = 4 * (tid % TPR);
-    float m = 0.f;
+  auto issue_U = [&](int s) {
+    const f32x4* p = u_src(s);
 #pragma unroll
-    for (int i = 0; i < LDU; ++i)
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(ureg[i][0]), fabsf(ureg[i][1])), fmaxf(fabsf(ureg[i][2]), fabsf(ureg[i][3]))));
-    m = dpp_max_step(m, 0);  // the row's TPR threads are consecutive lanes
-    if (TPR >= 4) m = dpp_max_step(m, 1);
-    if (TPR >= 8) m = dpp_max_step(m, 2);
-    const int e = split_exp(m);
-    const float s = ldexpf(1.f, -e);
-#pragma unroll
-    for (int i = 0; i < LDU; ++i) {
-      f16x4 hv, lv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = ureg[i][j] * s;
-        hv[j] = hi_h(x);
-        lv[j] = lo_h(x, hv[j]);
-      }
-      *reinterpret_cast<f16x4*>(sUh + row * UP + c0 + 4 * TPR * i) = hv;
-      *reinterpret_cast<f16x4*>(sUl + row * UP + c0 + 4 * TPR * i) = lv;
+    for (int ks = 0; ks < KS; ++ks) {
+      ur[ks][0] = p[4 * ks];
+      ur[ks][1] = p[4 * ks + 1];
     }
-    if (tid % TPR == 0) sRE[row] = e;
   };
 
-  // ---- the state tile and its split ------------------------------------------------
-  // a tile of a [D][D] matrix at p: rows 8q + 4h + j (q, j < 4) of the lane's
-  // block; the lane offset is taken through opaque() so that its 16 addresses
-  // are formed at each use instead of being kept live across the segment loop
-  auto tile_ptr = [&](const float* base) {
-    return base + (size_t)opaque(32 * rb + 4 * h) * D + col0 + tcol;
+  // ---- the state tiles and their split -----------------------------------------------
+  // tile ct of a [D][D] matrix at base: element r of this lane is row
+  // 32 rb + 8 (r / 4) + 4 h + r % 4, column col0 + 32 ct + l32
+  auto tile_ptr = [&](const float* base, int ct) {
+    return base + (size_t)opaque(32 * rb + 4 * h) * D + col0 + 32 * ct + l32;
   };
-  f32x16 Si;  // S tile of the next pair
+  f32x16 St[NCT];  // the state
+  f32x16 Si[NCT];  // S of the next pair
   auto issue_Si = [&](int s) {
-    const float* p = tile_ptr(a.S + (size_t)s * seg_stride + pair_off);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float* p = tile_ptr(a.S + (size_t)s * seg_stride + pair_off, ct);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Si[4 * q + j] = p[(8 * q + j) * D];
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Si[ct][4 * q + j] = p[(8 * q + j) * D];
+    }
   };
-  auto store_tile = [&](float* base, const f32x16& t) {
-    float* p = const_cast<float*>(tile_ptr(base));
+  auto store_tiles = [&](float* base) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int ct = 0; ct < NCT; ++ct) {
+      float* p = const_cast<float*>(tile_ptr(base, ct));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[(8 * q + j) * D] = t[4 * q + j];
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[(8 * q + j) * D] = St[ct][4 * q + j];
+    }
   };
-  // the tile's share of its columns' maxima
-  auto put_cmax = [&](const f32x16& t) {
-    float m = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(t[r]));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (h == 0) sCM[rb * COLS + tcol] = m;
+  // results (after the last segment): the tiles, from registers, and the gate sum
+  auto store_results = [&]() {
+    store_tiles((ut ? a.U_tot : a.S_out) + unit_off);
+    if (!ut && a.g_tot && cgrp == 0 && threadIdx.x == 0) {
+      double acc = 0.0;
+      for (int s = 0; s < nseg; ++s) acc += (double)a.g[pidx + (size_t)s * n_chain];
+      a.g_tot[unit] = (float)acc;
+    }
   };
-  // after a barrier: the column's exponent, and the tile times f split into
+  // the wave's share of its columns' maxima
+  auto put_cmax = [&]() {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(St[ct][r]));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (h == 0) sCM[rb * COLS + 32 * ct + l32] = m;
+    }
+  };
+  // after a barrier: each column's exponent, and the tiles times f split into
   // the B arrays (f = exp(g) of the pair the split feeds, else 1)
-  int ec = 0;  // the lane's column is stored as x f 2^-ec
-  auto put_B = [&](const f32x16& t, float f) {
-    float m = 0.f;
+  int ec[NCT];  // the lane's column of tile ct is stored as x f 2^-ec
+  auto put_B = [&](float f) {
 #pragma unroll
-    for (int s = 0; s < NRB; ++s) m = fmaxf(m, sCM[s * COLS + tcol]);
-    ec = split_exp(m * f);
-    const float sc = ldexpf(1.f, -ec) * f;
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 32 * ct + l32;
+      float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f16x4 hv, lv;
+      for (int s = 0; s < NRB; ++s) m = fmaxf(m, sCM[s * COLS + c]);
+      ec[ct] = split_exp(m * f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = t[4 * q + j] * sc;
-        hv[j] = hi_h(x);
-        lv[j] = lo_h(x, hv[j]);
+      for (int q = 0; q < 4; ++q) {
+        float r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = ldexpf(St[ct][4 * q + j] * f, -ec[ct]);
+        const int off = c * BP + 32 * rb + 8 * q + 4 * h;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          f16x4 tv;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            tv[j] = (f16_t)r[j];
+            if (i + 1 < NT) r[j] -= (float)tv[j];
+          }
+          *reinterpret_cast<f16x4*>(sB + i * COLS * BP + off) = tv;
+        }
       }
-      const int off = tcol * UP + 32 * rb + 8 * q + 4 * h;
-      *reinterpret_cast<f16x4*>(sBh + off) = hv;
-      *reinterpret_cast<f16x4*>(sBl + off) = lv;
     }
   };
 
   // ---- seam windows: staging and the two products ------------------------------------
-  [[maybe_unused]] f16_t* sAh = reinterpret_cast<f16_t*>(smem + Cfg::OFF_AH);  // [2 SUB][UP]: K, Q rows
-  [[maybe_unused]] f16_t* sAl = reinterpret_cast<f16_t*>(smem + Cfg::OFF_AL);
-  [[maybe_unused]] float* sAS = reinterpret_cast<float*>(smem + Cfg::OFF_AS);     // 2^e of those rows
-  [[maybe_unused]] bf16_t* sKt = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KT);   // [NTK][D][SUB]
-  [[maybe_unused]] float* sV = reinterpret_cast<float*>(smem + Cfg::OFF_V);       // [SUB][COLS]
-  [[maybe_unused]] float* sRp = reinterpret_cast<float*>(smem + Cfg::OFF_RP);     // [COLS][RPP]
+  [[maybe_unused]] f16_t* sA = reinterpret_cast<f16_t*>(smem + Cfg::OFF_A);      // [NTA][2 SUB][BP]: K, Q rows
+  [[maybe_unused]] float* sAS = reinterpret_cast<float*>(smem + Cfg::OFF_AS);    // 2^e of those rows
+  [[maybe_unused]] bf16_t* sKt = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KT);  // [NTK][D][SUB]
+  [[maybe_unused]] float* sV = reinterpret_cast<float*>(smem + Cfg::OFF_V);      // [SUB][COLS]
+  [[maybe_unused]] float* sRp = reinterpret_cast<float*>(smem + Cfg::OFF_RP);    // [COLS][RPP]
   [[maybe_unused]] float* sRec = reinterpret_cast<float*>(smem + Cfg::OFF_REC);
   const int n_sub = SEAM ? (a.w + SUB - 1) / SUB : 0;
   using Raw = uint4[IN_F32 ? 2 : 1];
@@ -358,16 +407,13 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
         m = dpp_max_step(m, 2);
         if (D / 8 >= 16) m = dpp_max_step(m, 3);
         const int e = split_exp(m);
-        const float sc = ldexpf(1.f, -e);
-        f16x8 hv, lv;
+        float xs[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float xs = x[j] * sc;
-          hv[j] = hi_h(xs);
-          lv[j] = lo_h(xs, hv[j]);
-        }
-        *reinterpret_cast<f16x8*>(sAh + row * UP + 8 * d8) = hv;
-        if constexpr (IN_F32) *reinterpret_cast<f16x8*>(sAl + row * UP + 8 * d8) = lv;
+        for (int j = 0; j < 8; ++j) xs[j] = ldexpf(x[j], -e);
+        const HFrag<NTA> fa = split8h<NTA>(xs);
+#pragma unroll
+        for (int term = 0; term < NTA; ++term)
+          *reinterpret_cast<f16x8*>(sA + (term * 2 * SUB + row) * BP + 8 * d8) = fa.t[term];
         if (d8 == 0) sAS[row] = ldexpf(1.f, e);
         if (row < SUB) {  // keys, transposed, in bf16 terms: [term][d][t]
           float r8[8];
@@ -395,31 +441,28 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
   };
 
   // ---- start state -----------------------------------------------------------------
-  f32x16 St;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const size_t row = 32 * rb + acc_row(r, lane);
-    if (ut) {
-      St[r] = ((int)row == col0 + tcol) ? 1.f : 0.f;
-    } else {
-      St[r] = a.S_in ? a.S_in[chain_off + row * D + col0 + tcol] : 0.f;
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * rb + acc_row(r, lane), col = col0 + 32 * ct + l32;
+      if (ut) {
+        St[ct][r] = (row == col) ? 1.f : 0.f;
+      } else {
+        St[ct][r] = a.S_in ? a.S_in[unit_off + (size_t)row * D + col] : 0.f;
+      }
     }
-  }
-  if (!ut && a.prefix) store_tile(a.prefix + pair_off, St);  // prefix states follow the pairs' layout
-  put_cmax(St);
+  if (!ut && a.prefix) store_tiles(a.prefix + pair_off);  // prefix states follow the pairs' layout
+  put_cmax();
   float g_next = 0.f;
   if (pairs) {
-    issue_U(0, 0, LDU);
+    issue_U(0);
     if (!ut) issue_Si(0);
     g_next = ut ? 0.f : a.g[pidx];
   }
   if constexpr (SEAM) issue_window(0, 0);
   __syncthreads();
-  put_B(St, (SEAM || !pairs) ? 1.f : __expf(g_next));
-  if (pairs) {
-    store_U();
-    if (nseg > 1) issue_U(1, 0, SEAM ? LDU / 2 : LDU);
-  }
+  put_B((SEAM || !pairs) ? 1.f : __expf(g_next));
   if constexpr (SEAM) stage_window();
   __syncthreads();
 
@@ -436,30 +479,35 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
         const float* sCt = sRec;              // [t][s]: Abar[t][s] exp(G_n - G_t)
         const float* sW2 = sRec + SUB * SUB;  // [t][s]: ((tril(Q K^T) o Gamma) Abar)[t][s]
         const float* sEG = sRec + 2 * SUB * SUB;  // exp(G_t); [SUB] = exp(G_n)
-        // W1: [X; P] = [K; Q] S for the column block (its first row-block wave),
-        // on 16x16x32 MFMA: rows are the 8 keys and 8 queries, two 16-column tiles
-        if (rb == 0) {
+        // [X; P] = [K; Q] S for column block cb = rb (waves rb < NCT), on
+        // 16x16x32 MFMA: rows are the 8 keys and 8 queries, two 16-column tiles
+        if (rb < NCT) {
+          const int cb = rb;
           const int l16 = lane & 15, g = lane >> 4;
           f32x4 XP[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-          const f16_t* pah = sAh + l16 * UP + 8 * g;
-          const f16_t* pal = sAl + l16 * UP + 8 * g;
+          const f16_t* pa = sA + l16 * BP + 8 * g;
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks) {
-            const f16x8 fah = *reinterpret_cast<const f16x8*>(pah + 32 * ks);
+            HFrag<NTA> fa;
+#pragma unroll
+            for (int i = 0; i < NTA; ++i)
+              fa.t[i] = *reinterpret_cast<const f16x8*>(pa + i * 2 * SUB * BP + 32 * ks);
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
               const int col = 32 * cb + 16 * ct + l16;
-              const f16x8 fbh = *reinterpret_cast<const f16x8*>(sBh + col * UP + 32 * ks + 8 * g);
-              const f16x8 fbl = *reinterpret_cast<const f16x8*>(sBl + col * UP + 32 * ks + 8 * g);
-              XP[ct] = mfma16h(fah, fbl, XP[ct]);
-              XP[ct] = mfma16h(fah, fbh, XP[ct]);
-              if constexpr (IN_F32) {
-                const f16x8 fal = *reinterpret_cast<const f16x8*>(pal + 32 * ks);
-                XP[ct] = mfma16h(fal, fbh, XP[ct]);
-              }
+              HFrag<NT> fb;
+#pragma unroll
+              for (int i = 0; i < NT; ++i)
+                fb.t[i] = *reinterpret_cast<const f16x8*>(sB + (i * COLS + col) * BP + 32 * ks + 8 * g);
+              mmah16<NTA, NT>(XP[ct], fa, fb);
             }
             sched_fence();  // bounds how far ahead fragments are loaded
           }
+          // the exponent of column block cb (tile cb of the lanes' columns)
+          int ecb = ec[0];
+#pragma unroll
+          for (int ct = 1; ct < NCT; ++ct)
+            if (cb == ct) ecb = ec[ct];
           // lane (l16, g), tile ct: column 32 cb + 16 ct + l16, rows 4g + j: X of
           // token 4g + j (g < 2) or P of token 4(g - 2) + j (g >= 2).  Every lane
           // scales its rows; X lanes form R; P lanes gather the column's R and
@@ -467,13 +515,13 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             const int col = 32 * cb + 16 * ct + l16;
-            const float cs = ldexpf(1.f, __shfl(ec, (lane & 32) | (16 * ct + l16), 64));  // the column's exponent
+            const int ce = __shfl(ecb, 16 * ct + l16, 64);  // the column's exponent
             float v4[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int row = 4 * g + j;  // 0..7 keys, 8..15 queries
               const int t = row & 7;
-              const float x = XP[ct][j] * sAS[row] * cs;
+              const float x = ldexpf(XP[ct][j], ce) * sAS[row];
               v4[j] = g < 2 ? sV[t * COLS + col] - sEG[t] * x : sEG[t] * x;  // R, or exp(G) P
             }
             float Ra[SUB];  // R of the column's 8 tokens, from its two X lane groups
@@ -506,33 +554,39 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
           }
         }
         __syncthreads();
-        // W2: S = exp(G_n) S + K^T R' on every tile (k = the 8 tokens; lanes of
-        // the upper k half hold zeros)
+        // S = exp(G_n) S + K^T R' on every tile (k = the 8 tokens; lanes of the
+        // upper k half hold zeros)
         {
           const float eGn = sEG[SUB];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) St[r] *= eGn;
           Frag<NTK> fa;
-          Frag<3> fb;
           if (h == 0) {
 #pragma unroll
             for (int term = 0; term < NTK; ++term)
               fa.t[term] = *reinterpret_cast<const bf16x8*>(sKt + (term * D + 32 * rb + l32) * SUB);
-            const f32x4 r0 = *reinterpret_cast<const f32x4*>(sRp + tcol * RPP);
-            const f32x4 r1 = *reinterpret_cast<const f32x4*>(sRp + tcol * RPP + 4);
-            const float x[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-            fb = split8<3>(x);
           } else {
 #pragma unroll
             for (int term = 0; term < NTK; ++term) fa.t[term] = bf16x8{};
-#pragma unroll
-            for (int term = 0; term < 3; ++term) fb.t[term] = bf16x8{};
           }
-          mma<NTK, 3>(St, fa, fb);
-          put_cmax(St);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) St[ct][r] *= eGn;
+            Frag<3> fb;
+            if (h == 0) {
+              const f32x4 r0 = *reinterpret_cast<const f32x4*>(sRp + (32 * ct + l32) * RPP);
+              const f32x4 r1 = *reinterpret_cast<const f32x4*>(sRp + (32 * ct + l32) * RPP + 4);
+              const float x[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+              fb = split8<3>(x);
+            } else {
+#pragma unroll
+              for (int term = 0; term < 3; ++term) fb.t[term] = bf16x8{};
+            }
+            mma<NTK, 3>(St[ct], fa, fb);
+          }
+          put_cmax();
         }
         __syncthreads();
-        put_B(St, (sub + 1 == n_sub && pairs) ? __expf(g_next) : 1.f);
+        put_B((sub + 1 == n_sub && pairs) ? __expf(g_next) : 1.f);
         if (sub + 1 < n_sub) stage_window();
         __syncthreads();
       }
@@ -541,95 +595,103 @@ __global__ __launch_bounds__(64 * (D / 32) * NCB) void chain_kernel(const ChainA
     // ---- body pair: S <- exp(g) U S + S_B (or U_total <- U U_total) ----------------
     if (pairs) {
       refresh();
-      if (SEAM && seg + 1 < nseg) issue_U(seg + 1, LDU / 2, LDU);
-      // T = U (exp(g) S) 2^-ec / 2^e_row (+ S_B 2^-ec / 2^e_row): in seam mode the
-      // pair's state enters as the accumulator's start (all factors are powers of
-      // two), which frees its registers during the product; in compose mode it is
-      // added afterwards, which gives its loads the product's time to land
-      f32x16 T;
-      int er[16];  // the product's scale exponent per element (row and column)
+      const bool more = seg + 1 < nseg;
+      // T = (U 2^-eu) (exp(g) S 2^-ec), then S = T 2^(eu + ec) + S_B
+      float m = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        er[r] = sRE[32 * rb + acc_row(r, lane)] + ec;
-        T[r] = (ut || !SEAM) ? 0.f : ldexpf(Si[r], -er[r]);
-      }
-      {
-        const f16_t* ah = sUh + (32 * rb + l32) * UP + 8 * h;
-        const f16_t* al = sUl + (32 * rb + l32) * UP + 8 * h;
-        const f16_t* bh = sBh + tcol * UP + 8 * h;
-        const f16_t* bl = sBl + tcol * UP + 8 * h;
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const f16x8 fah = *reinterpret_cast<const f16x8*>(ah + 16 * ks);
-          const f16x8 fal = *reinterpret_cast<const f16x8*>(al + 16 * ks);
-          const f16x8 fbh = *reinterpret_cast<const f16x8*>(bh + 16 * ks);
-          const f16x8 fbl = *reinterpret_cast<const f16x8*>(bl + 16 * ks);
-          T = mfma32h(fal, fbh, T);
-          T = mfma32h(fah, fbl, T);
-          T = mfma32h(fah, fbh, T);
-          sched_fence();  // bounds how far ahead fragments are loaded
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(ur[ks][i][j]));
+      const int eu = split_exp(wave_max_uniform(m));
+      f32x16 T[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) T[ct] = zero16();
+      const f32x4* nxt = u_src(more ? seg + 1 : seg);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = ldexpf(ur[ks][0][j], -eu);
+          x[4 + j] = ldexpf(ur[ks][1][j], -eu);
         }
+        HFrag<NT> fa = split8h<NT>(x);
+        // (the split is complete before the slice's registers are reloaded)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) asm volatile("" : "+v"(fa.t[i])::"memory");
+        // the slice takes the next pair's values as soon as it is split (on the
+        // last pair it reads this pair again, so no path keeps the old slice)
+        ur[ks][0] = nxt[4 * ks];
+        ur[ks][1] = nxt[4 * ks + 1];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const f16_t* pb = sB + (32 * ct + l32) * BP + 16 * ks + 8 * h;
+          HFrag<NT> fb;
+#pragma unroll
+          for (int i = 0; i < NT; ++i) fb.t[i] = *reinterpret_cast<const f16x8*>(pb + i * COLS * BP);
+          mmah<NT, NT>(T[ct], fa, fb);
+        }
+        sched_fence();  // bounds how far ahead fragments are loaded
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        St[r] = ldexpf(T[r], er[r]);
-        if (!SEAM && !ut) St[r] += Si[r];
-      }
-      put_cmax(St);
-      if (seg + 1 < nseg) {
-        if (!ut && a.prefix) store_tile(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off, St);
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          St[ct][r] = ldexpf(T[ct][r], eu + ec[ct]);
+          if (!ut) St[ct][r] += Si[ct][r];
+        }
+      if (!more) store_results();
+      if (more) {
+        if (!ut) issue_Si(seg + 1);  // a whole step ahead
+        put_cmax();
+        if (!ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
         if (!ut) g_next = a.g[pidx + (size_t)(seg + 1) * n_chain];
-      }
-      __syncthreads();  // every wave is done with sU and sB
-      put_B(St, (SEAM || seg + 1 == nseg || ut) ? 1.f : __expf(g_next));
-      if (seg + 1 < nseg) {
-        store_U();
+        __syncthreads();  // every wave is done with sB
+        put_B((SEAM || ut) ? 1.f : __expf(g_next));
         if constexpr (SEAM) stage_window();
-        // the next pair's loads, after the staging work of this interval
-        if (!ut) issue_Si(seg + 1);
-        if (seg + 2 < nseg) issue_U(seg + 2, 0, SEAM ? LDU / 2 : LDU);
+        __syncthreads();
       }
-      __syncthreads();
     } else if constexpr (SEAM) {
       if (seg + 1 < nseg) {  // windows only: stage the next segment's first window
         stage_window();
         __syncthreads();
+      } else {
+        store_results();
       }
     }
   }
-
-  // ---- results: the tiles, from registers ------------------------------------------
-  float* dst = ut ? a.U_tot : a.S_out;
-  store_tile(dst + chain_off, St);
-  if (!ut && a.g_tot && cgrp == 0 && tid == 0) {
-    double acc = 0.0;
-    for (int s = 0; s < nseg; ++s) acc += (double)a.g[pidx + (size_t)s * n_chain];
-    a.g_tot[chain] = (float)acc;
-  }
 }
 
-template <int D, int NCB, bool SEAM, bool IN_F32>
-hipError_t launch_chain_t(const ChainArgs& a, bool want_ut, hipStream_t stream) {
-  using Cfg = ChainCfg<D, NCB, SEAM, IN_F32>;
+template <int D, int NCT, int NT, bool SEAM, bool IN_F32, bool PAIRS>
+hipError_t launch_chain_p(const ChainArgs& a, bool want_ut, hipStream_t stream) {
+  using Cfg = ChainCfg<D, NCT, NT, SEAM, IN_F32>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&chain_kernel<D, NCB, SEAM, IN_F32>),
+      reinterpret_cast<const void*>(&chain_kernel<D, NCT, NT, SEAM, IN_F32, PAIRS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (attr != hipSuccess) return attr;
   const int nx = Cfg::NCG == 1 ? a.n_units : ((a.n_units + 7) / 8) * 8 * Cfg::NCG;
-  hipLaunchKernelGGL((chain_kernel<D, NCB, SEAM, IN_F32>), dim3(nx, want_ut ? 2 : 1), dim3(Cfg::NTH), Cfg::LDS,
-                     stream, a);
+  hipLaunchKernelGGL((chain_kernel<D, NCT, NT, SEAM, IN_F32, PAIRS>), dim3(nx, want_ut ? 2 : 1),
+                     dim3(Cfg::NTH), Cfg::LDS, stream, a);
   return hipGetLastError();
 }
 
-// Few chains: split each over its column blocks (more workgroups, one per CU);
-// many chains: one workgroup per chain (no duplicated U staging).  The seam
-// step with fp32 tokens at d = 128 keeps two column blocks per workgroup, for
-// its larger window staging to fit in LDS.
-template <int D, bool SEAM, bool IN_F32>
-hipError_t launch_chain_d(const ChainArgs& a, bool want_ut, hipStream_t stream) {
-  constexpr int NCBT = (SEAM && IN_F32 && D == 128) ? 2 : D / 32;
-  if (a.n_units * (D / 32) <= 256) return launch_chain_t<D, 1, SEAM, IN_F32>(a, want_ut, stream);
-  return launch_chain_t<D, NCBT, SEAM, IN_F32>(a, want_ut, stream);
+template <int D, int NCT, int NT, bool SEAM, bool IN_F32>
+hipError_t launch_chain_t(const ChainArgs& a, bool want_ut, hipStream_t stream) {
+  if constexpr (SEAM) {
+    if (a.S == nullptr) return launch_chain_p<D, NCT, NT, SEAM, IN_F32, false>(a, want_ut, stream);
+  }
+  return launch_chain_p<D, NCT, NT, SEAM, IN_F32, true>(a, want_ut, stream);
+}
+
+// Composition of fp32 pairs (three fp16 terms per operand): one 32-column tile
+// per workgroup while that keeps the grid within about four workgroups per
+// CU, else two.
+template <int D>
+hipError_t launch_compose_d(const ChainArgs& a, bool want_ut, hipStream_t stream) {
+  if ((long)a.n_units * (D / 32) * (want_ut ? 2 : 1) <= 1024) return launch_chain_t<D, 1, 3, false, false>(a, want_ut, stream);
+  return launch_chain_t<D, 2, 3, false, false>(a, want_ut, stream);
 }
 
 }  // namespace
@@ -706,13 +768,13 @@ hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws
     a3.n_units = (int)units;
     hipError_t e;
     if (d == 128) {
-      e = launch_chain_d<128, false, false>(a1, true, stream);
-      if (e == hipSuccess) e = launch_chain_d<128, false, false>(a2, c.U_tot != nullptr, stream);
-      if (e == hipSuccess && wP) e = launch_chain_d<128, false, false>(a3, false, stream);
+      e = launch_compose_d<128>(a1, true, stream);
+      if (e == hipSuccess) e = launch_compose_d<128>(a2, c.U_tot != nullptr, stream);
+      if (e == hipSuccess && wP) e = launch_compose_d<128>(a3, false, stream);
     } else if (d == 64) {
-      e = launch_chain_d<64, false, false>(a1, true, stream);
-      if (e == hipSuccess) e = launch_chain_d<64, false, false>(a2, c.U_tot != nullptr, stream);
-      if (e == hipSuccess && wP) e = launch_chain_d<64, false, false>(a3, false, stream);
+      e = launch_compose_d<64>(a1, true, stream);
+      if (e == hipSuccess) e = launch_compose_d<64>(a2, c.U_tot != nullptr, stream);
+      if (e == hipSuccess && wP) e = launch_compose_d<64>(a3, false, stream);
     } else {
       e = hipErrorInvalidValue;
     }
@@ -731,8 +793,8 @@ hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws
   a.n_seg = c.n_seg;
   a.n_chain = c.n_chain;
   const bool ut = c.U_tot != nullptr;
-  if (d == 128) return launch_chain_d<128, false, false>(a, ut, stream);
-  if (d == 64) return launch_chain_d<64, false, false>(a, ut, stream);
+  if (d == 128) return launch_compose_d<128>(a, ut, stream);
+  if (d == 64) return launch_compose_d<64>(a, ut, stream);
   return hipErrorInvalidValue;
 }
 
@@ -752,10 +814,16 @@ hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& s, hipStream_t 
   a.n_seg = s.n_seg;
   a.n_chain = s.n_chain;
   a.w = s.w;
+  // bf16 tokens: two fp16 terms per body operand (the outputs are of bf16
+  // input precision); fp32 tokens: three
+  constexpr int NCT128 = HYPIC_SEAM_NCT;
+  constexpr int NCT64 = HYPIC_SEAM_NCT > 2 ? 2 : HYPIC_SEAM_NCT;
   if (d == 128)
-    return in_f32 ? launch_chain_d<128, true, true>(a, false, stream) : launch_chain_d<128, true, false>(a, false, stream);
+    return in_f32 ? launch_chain_t<128, 1, 3, true, true>(a, false, stream)
+                  : launch_chain_t<128, NCT128, 2, true, false>(a, false, stream);
   if (d == 64)
-    return in_f32 ? launch_chain_d<64, true, true>(a, false, stream) : launch_chain_d<64, true, false>(a, false, stream);
+    return in_f32 ? launch_chain_t<64, 1, 3, true, true>(a, false, stream)
+                  : launch_chain_t<64, NCT64, 2, true, false>(a, false, stream);
   return hipErrorInvalidValue;
 }
 

@@ -37,10 +37,31 @@ def test_retnet_scalar_build_full_size():
     _check_build(tk, "retnet")
 
 
-def test_gla_diag_build():
-    """16 heads, d = 128, 8 of the 64 x 512-token segments, bf16, per-channel gates."""
+def test_gla_diag_build_piece_split():
+    """16 heads, d = 128, 8 of the 64 x 512-token segments, bf16, per-channel
+    gates: 128 units, built as pieces joined by composition."""
     tk = synth.gla(n_seg=8)
     _check_build(tk, "gla")
+
+
+def test_gla_full_size_build_then_compose():
+    """The GLA workload at the shape the benchmark times: 64 segments x 512
+    tokens x 16 heads (1024 units, one unsplit launch), every unit against the
+    oracle, then the composition of all 64 segments of every head (GPU pairs)
+    against the oracle's composition of its own pairs."""
+    import torch
+    tk = synth.gla()
+    announce("gla_full", "units", 64 * 16)
+    d = upload_tokens(tk)
+    g, U, S = api.seg_build(DIAG, list(tk.offsets), d["k"], d["v"], None, d["log_gate"])
+    res = api.compose(DIAG, g, None, S, want_total=True)
+    torch.cuda.synchronize()
+    rg, rU, rS = oracle.build_pairs(DIAG, tk.offsets, tk.k, tk.v, None, tk.log_gate)
+    assert_units_close("gla_full.S", host(S), rS, TOL["bf16"])
+    assert_g_close("gla_full.g", host(g), rg, TOL["bf16"])
+    ref = oracle.compose(DIAG, rg, None, rS, want_total=True)
+    assert_units_close("gla_full.S_out", host(res["S_out"]), ref["S_out"], TOL["bf16"], unit_dims=1)
+    assert_g_close("gla_full.g_tot", host(res["g_tot"]), ref["g_tot"], TOL["bf16"])
 
 
 @pytest.mark.parametrize("scale", [1.0 / 16, 1.0 / 1024, 0.0])

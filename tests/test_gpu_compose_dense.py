@@ -95,14 +95,9 @@ def test_compose_dense_two_level_schedule():
 def test_compose_dense_scan_with_prefix_states():
     """Few chains with prefix states: the three-phase scan (37 segments -> 8 blocks,
     the last ragged; block pairs, block start states in order, then every block
-    again from its start state) must match the oracle, as the single pass must.
-
-    Tolerance: every prefix state of a 37-step chain of random dense pairs is
-    compared, not only the end state.  Each split-fp16 product rounds at about
-    2^-22 per operand, times |U||S| / |U S| ~ 7 for these random factors, and a
-    state carries the rounding of the previous steps scaled by the chain's
-    contraction (close to 1 here): about 1e-5 at the worst prefix state, for
-    either schedule, hence twice the fp32-class bound."""
+    again from its start state) must match the oracle, as the single pass must,
+    at the fp32-class bound on every prefix state and on U_total (a product of
+    37 random factors, whose rounding accumulates with nothing added)."""
     import torch
     g, U, S = synth.warm_pairs_layer(6, n_seg=37, n_head=5)
     g = (g - 0.03 * np.arange(g.size).reshape(g.shape) / g.size).astype(np.float32).astype(np.float64)
@@ -116,8 +111,49 @@ def test_compose_dense_scan_with_prefix_states():
     flat = api.compose(DELTA, dg, dU, dS, S_init=dI, want_prefix=True, want_total=True, workspace=None)
     torch.cuda.synchronize()
     ref = oracle.compose(DELTA, g, U, S, S_init=S_init, want_prefix=True, want_total=True)
-    for name, res, tol in (("scan", scan, 2e-5), ("flat", flat, 2e-5)):
+    for name, res, tol in (("scan", scan, 1e-5), ("flat", flat, 1e-5)):
         assert_units_close(name + ".S_out", host(res["S_out"]), ref["S_out"], tol, unit_dims=1)
         assert_units_close(name + ".prefix", host(res["prefix"]), ref["prefix"], tol)
         assert_g_close(name + ".g_tot", host(res["g_tot"]), ref["g_tot"], tol)
         assert_units_close(name + ".U_tot", host(res["U_tot"]), ref["U_tot"], tol, unit_dims=1)
+
+
+def test_compose_dense_warm_layer_full_length():
+    """One layer of the warm 100k-token request composed on its own: 196 random
+    fp32 pairs x 16 heads (one workgroup per 32-column tile), prefix states,
+    g_total and U_total, all at the fp32-class bound."""
+    g, U, S = synth.warm_pairs_layer(0)
+    _check(g, U, S, None, "warm_layer0_full")
+
+
+def test_compose_dense_warm_request_layers_0_and_29():
+    """The whole warm request's pairs (30 layers x 16 heads = 480 chains x 196
+    segments, fp32) composed in one call, with prefix states and totals; layers
+    0 and 29 (drawn by the seeded generator) are compared with the oracle at the
+    fp32-class bound, the other layers carry pairs of the same recipe drawn on
+    the GPU."""
+    import torch
+    H, d, n_seg = synth.WARM_HEADS, synth.WARM_D, synth.WARM_SEGS
+    n_chain = synth.WARM_LAYERS * H
+    announce("warm_request_compose", "chains", n_chain, "segs", n_seg)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    U = torch.randn((n_seg, n_chain, d, d), device="cuda", generator=gen) * (0.5 / np.sqrt(d))
+    S = torch.randn((n_seg, n_chain, d, d), device="cuda", generator=gen)
+    g = torch.zeros((n_seg, n_chain), device="cuda")
+    layers = (0, 29)
+    pairs = [synth.warm_pairs_layer(layer) for layer in layers]
+    for li, layer in enumerate(layers):
+        sl = slice(layer * H, (layer + 1) * H)
+        U[:, sl] = dev_f32(pairs[li][1])
+        S[:, sl] = dev_f32(pairs[li][2])
+    res = api.compose(DELTA, g, U, S, want_prefix=True, want_total=True)
+    torch.cuda.synchronize()
+    del U, S
+    for li, layer in enumerate(layers):
+        sl = slice(layer * H, (layer + 1) * H)
+        ref = oracle.compose(DELTA, *pairs[li], S_init=None, want_prefix=True, want_total=True)
+        name = "warm_req.l%d" % layer
+        assert_units_close(name + ".S_out", host(res["S_out"][sl]), ref["S_out"], 1e-5, unit_dims=1)
+        assert_units_close(name + ".prefix", host(res["prefix"][:, sl]), ref["prefix"], 1e-5)
+        assert_g_close(name + ".g_tot", host(res["g_tot"][sl]), ref["g_tot"], 1e-5)
+        assert_units_close(name + ".U_tot", host(res["U_tot"][sl]), ref["U_tot"], 1e-5, unit_dims=1)

@@ -75,23 +75,12 @@ def test_gdn_d64_bf16_and_d128_fp32():
     check_build(tk, "gdn_d128_f32")
 
 
-def test_gdn_cold_full_size_sampled_units():
+def test_gdn_cold_full_size_every_unit():
     """The 32k-token cold request at full size (32 heads x 64 segments x 512), in
-    the launch the benchmark times; the oracle recomputes a sample of units one by one."""
+    the launch the benchmark times; every one of the 2048 units against one
+    oracle pass over the whole request."""
     tk = synth.gdn_cold()
-    announce("gdn_cold_full", "units", 64 * 32)
-    g, U, S = gpu_build(tk)
-    g, U, S = host(g), host(U), host(S)
-    rng = np.random.default_rng(0)
-    units = [(0, 0), (63, 31), (31, 7)] + [tuple(x) for x in zip(rng.integers(0, 64, 9), rng.integers(0, 32, 9))]
-    for s, hh in units:
-        sub = tk.chains([hh])
-        t0, t1 = tk.offsets[s], tk.offsets[s + 1]
-        rg, rU, rS = oracle.build_pairs(DELTA, np.array([0, t1 - t0], np.int32), sub.k[t0:t1], sub.v[t0:t1],
-                                        sub.beta[t0:t1], sub.log_gate[t0:t1])
-        assert_units_close("full.S(%d,%d)" % (s, hh), S[s:s + 1, hh:hh + 1], rS, TOL["bf16"])
-        assert_units_close("full.U(%d,%d)" % (s, hh), U[s:s + 1, hh:hh + 1], rU, TOL["bf16"])
-        assert_g_close("full.g(%d,%d)" % (s, hh), g[s, hh], rg[0, 0], TOL["bf16"])
+    check_build(tk, "gdn_cold_full")
 
 
 def test_gdn_build_then_compose_matches_sequential():
