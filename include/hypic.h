@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 6
+#define HYPIC_ABI_VERSION 7
 
 typedef enum {
   HYPIC_OK = 0,
@@ -269,6 +269,33 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
  */
 hypic_status hypic_seam_step_workspace_size(hypic_family fam, int n_seg, int w, int n_chain, int d_k,
                                             int d_v, size_t* bytes);
+
+/*
+ * hypic_seam_step_noalloc -- hypic_seam_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid allocation.  The delta family's window records (see
+ * hypic_seam_step_workspace_size) go to a fixed scratch array of
+ * HYPIC_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on, from the first call there until the process ends, instead of a caller
+ * workspace.
+ *
+ * Arguments, layouts, results and errors as hypic_seam_step without the
+ * workspace.  Limit: the workspace size hypic_seam_step_workspace_size reports
+ * for the call must not exceed HYPIC_NOALLOC_SCRATCH_BYTES (576 bytes per
+ * 8-token sub-window and chain; the 100k-token warm request, 196 segments x
+ * 480 chains with w = 8, needs 54 MB); a larger call returns HYPIC_E_INVALID
+ * and enqueues nothing.  Other families use no scratch.
+ * Calls no allocating routine.  Every call on one GPU uses that GPU's single
+ * array: calls whose work overlaps on one GPU (on other streams, or from other
+ * host threads without ordering) race on it and give undefined results; calls
+ * ordered on one stream are safe.  Each call writes every record it reads, so
+ * nothing is cleared between calls.  The first call on a device looks up the
+ * array's device address with that device current (HYPIC_E_HIP if that fails).
+ */
+#define HYPIC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hypic_status hypic_seam_step_noalloc(hypic_family fam, int n_seg, int w, int n_chain, int d_k, int d_v,
+                                     const hypic_tokens* seam, const hypic_cpairs* body, float* S_run,
+                                     float* o_out, const hypic_pairs* window_out, void* stream);
 
 /*
  * hypic_rerotate -- move cached pairs to a new position under rotary position

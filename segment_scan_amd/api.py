@@ -65,10 +65,12 @@ def load_library(path: str = LIB_PATH):
         lib.hypic_seam_step.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P, P,
                                         ctypes.POINTER(Pairs), P, ctypes.c_size_t, P]
         lib.hypic_seam_step_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+        lib.hypic_seam_step_noalloc.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P,
+                                                P, ctypes.POINTER(Pairs), P]
         lib.hypic_rerotate.argtypes = [I, I, I, I, I, P, ctypes.c_double, ctypes.POINTER(Pairs), P]
         for f in (lib.hypic_seg_build, lib.hypic_seg_build_workspace_size, lib.hypic_compose,
                   lib.hypic_compose_workspace_size, lib.hypic_seam_step, lib.hypic_seam_step_workspace_size,
-                  lib.hypic_rerotate):
+                  lib.hypic_seam_step_noalloc, lib.hypic_rerotate):
             f.restype = I
         lib.hypic_last_error.restype = ctypes.c_char_p
         lib.hypic_last_error.argtypes = []
@@ -243,6 +245,32 @@ def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chai
     _check(load_library().hypic_seam_step(fam, n_seg, w, n_chain, d, v.shape[2], ctypes.byref(tk), bp,
                                           _ptr(S_run), _ptr(o_out), wp, _ptr(workspace), ws_bytes,
                                           _stream(stream)))
+    res = {"S_run": S_run, "o": o_out}
+    if window_out is not None:
+        res.update(wg=window_out[0], wU=window_out[1], wS=window_out[2])
+    return res
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HYPIC_NOALLOC_SCRATCH_BYTES
+
+
+def seam_step_noalloc(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chain=False, body=None,
+                      S_run=None, o_out=None, window_out=None, stream=None):
+    """seam_step on the library's fixed per-device scratch (hypic_seam_step_noalloc):
+    no workspace argument, and the library allocates nothing.  S_run (updated in
+    place) and o_out must be given, as must window_out if window pairs are wanted;
+    calls that overlap on one GPU race on the scratch."""
+    n_tok, n_chain, d = k.shape
+    if n_tok % w:
+        raise ValueError("window tokens must be n_seg * w")
+    if S_run is None or o_out is None:
+        raise ValueError("seam_step_noalloc takes preallocated S_run and o_out")
+    n_seg = n_tok // w
+    tk = _tokens(k, v, q, beta, log_gate, gate_per_chain)
+    bp = ctypes.byref(Pairs(_ptr(body[0]), _ptr(body[1]), _ptr(body[2]))) if body is not None else None
+    wp = ctypes.byref(Pairs(*[_ptr(x) for x in window_out])) if window_out is not None else None
+    _check(load_library().hypic_seam_step_noalloc(fam, n_seg, w, n_chain, d, v.shape[2], ctypes.byref(tk), bp,
+                                                  _ptr(S_run), _ptr(o_out), wp, _stream(stream)))
     res = {"S_run": S_run, "o": o_out}
     if window_out is not None:
         res.update(wg=window_out[0], wU=window_out[1], wS=window_out[2])

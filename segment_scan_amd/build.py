@@ -30,6 +30,7 @@ DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 def _sources():
     srcs = sorted(glob.glob(os.path.join(CSRC, "kernels", "*.hip")))
+    srcs += sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     srcs += sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
     return srcs
 

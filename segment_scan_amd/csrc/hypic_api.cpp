@@ -223,6 +223,16 @@ size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_cha
 
 }  // namespace
 
+hypic_status hypic::report_error(hypic_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
 extern "C" {
 
 const char* hypic_last_error(void) { return g_err.c_str(); }

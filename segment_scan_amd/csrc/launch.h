@@ -4,7 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/hypic.h"
+
 namespace hypic {
+
+// Sets the calling thread's error message (printf format) and returns st; the
+// message hypic_last_error reports.
+hypic_status report_error(hypic_status st, const char* fmt, ...);
 
 // Segments handled by one launch of a build kernel; their offsets travel by
 // value in the kernel arguments (no device-side table to allocate).

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert declared <= exported, declared - exported
     for name in declared:
         getattr(lib, name)
-    assert lib.hypic_abi_version() == 6
+    assert lib.hypic_abi_version() == 7
 
 
 def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
@@ -336,3 +336,18 @@ def rerotate_call(lib, fam=DELTA, n_seg=2, n_chain=2, dk=128, dv=128, pos=A["q"]
 def test_rerotate_rejects(lib, case, status):
     assert rerotate_call(lib, **case) == status
     assert lib.hypic_last_error()
+
+
+def test_seam_noalloc_rejects_more_records_than_its_scratch(lib):
+    """The no-allocation seam step refuses, before any HIP call, a call whose
+    window records exceed the library's fixed scratch: 1000 segments x 480
+    chains x 576 bytes = 276 MB > 64 MiB."""
+    t = toks(DELTA, q=True)
+    st = lib.hypic_seam_step_noalloc(DELTA, 1000, 8, 480, 128, 128, ctypes.byref(t), ctypes.byref(pairs(DELTA)),
+                                     A["Sinit"], A["o"], None, None)
+    assert st == INVALID
+    msg = api.last_error()
+    assert "scratch" in msg and str(1000 * 480 * 576) in msg
+    need = ctypes.c_size_t(0)
+    assert lib.hypic_seam_step_workspace_size(DELTA, 113, 8, 1024, 128, 128, ctypes.byref(need)) == 0
+    assert need.value <= api.NOALLOC_SCRATCH_BYTES  # the largest warm-request-like call that still fits
