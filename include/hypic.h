@@ -163,7 +163,7 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
  *    64-token chunk and chain a 42,512-byte factor record (the chunk's two
  *    decayed key copies and X as fp16, its gate factors), about 664 bytes per
  *    token and chain.
- *  - NAIVE, SCALAR, DIAG when there are few (segment, chain) units (fewer than
+ *  - NAIVE, SCALAR, DIAG when there are few (segment, chain) units (at most
  *    256) and every segment has at least two 64-token chunks: the segments are
  *    built as P = min(4, 512 / units, shortest segment's chunks) pieces of whole
  *    chunks, joined by the composition law [youleyou, linear-layer paragraph];

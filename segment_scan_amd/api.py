@@ -98,6 +98,43 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _want(name: str, t: Optional[torch.Tensor], shape, dtype=torch.float32):
+    """Raise ValueError unless t (if given) has exactly this shape (and dtype).
+
+    The library sizes every device range from the counts it is passed, so a
+    tensor of another shape would be read or written out of bounds: the check
+    runs here, before any pointer reaches the library."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+
+
+def _check_token_shapes(fam, n_tok, n_chain, d, k, v, q=None, beta=None, log_gate=None, gate_per_chain=False):
+    if k.dim() != 3:
+        raise ValueError("k must be [n_tok, n_chain, d] (got shape %s)" % (tuple(k.shape),))
+    _want("k", k, (n_tok, n_chain, d), None)
+    _want("v", v, (n_tok, n_chain, d), None)
+    _want("q", q, (n_tok, n_chain, d), None)
+    _want("beta", beta, (n_tok, n_chain), None)
+    if log_gate is not None:
+        if gate_per_chain:
+            shape = (n_chain,)
+        elif fam in (DIAG, KDA):
+            shape = (n_tok, n_chain, d)
+        else:
+            shape = (n_tok, n_chain)
+        _want("log_gate", log_gate, shape, None)
+
+
+def _check_pair_shapes(fam, what, n_seg, n_chain, d, g, U, S):
+    _want(what + ".g", g, _gate_shape(fam, (n_seg, n_chain), d))
+    _want(what + ".U", U, (n_seg, n_chain, d, d))
+    _want(what + ".S", S, (n_seg, n_chain, d, d))
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -150,8 +187,15 @@ def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor
     allocator for the call)."""
     off = _offsets(offsets)
     n_seg = len(offsets) - 1
+    if k.dim() != 3:
+        raise ValueError("k must be [n_tok, n_chain, d] (got shape %s)" % (tuple(k.shape),))
     n_tok, n_chain, d = k.shape
+    if n_seg < 1 or int(offsets[-1]) != n_tok:
+        raise ValueError("offsets must end at k.shape[0] = %d (got %s)" % (n_tok, int(offsets[-1])))
+    _check_token_shapes(fam, n_tok, n_chain, d, k, v, None, beta, log_gate, gate_per_chain)
     dev = k.device
+    if out is not None:
+        _check_pair_shapes(fam, "out", n_seg, n_chain, d, *out)
     if out is None:
         g = torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32)
         U = torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam in DENSE else None
@@ -186,7 +230,15 @@ def compose(fam: int, g, U, S, S_init=None, S_out=None, prefix_states=None, g_to
 
     workspace: "auto" takes one of the size compose_workspace_size() reports from
     torch's allocator, None runs the single-pass schedule, or a uint8 tensor."""
+    if S.dim() != 4:
+        raise ValueError("S must be [n_seg, n_chain, d_k, d_v] (got shape %s)" % (tuple(S.shape),))
     n_seg, n_chain, dk, dv = S.shape
+    _check_pair_shapes(fam, "pairs", n_seg, n_chain, dk, g, U, S)
+    _want("S_init", S_init, (n_chain, dk, dv))
+    _want("S_out", S_out, (n_chain, dk, dv))
+    _want("prefix_states", prefix_states, (n_seg, n_chain, dk, dv))
+    _want("g_total", g_total, _gate_shape(fam, (n_chain,), dk))
+    _want("U_total", U_total, (n_chain, dk, dk))
     dev = S.device
     if S_out is None:
         S_out = torch.empty((n_chain, dk, dv), device=dev, dtype=torch.float32)
@@ -214,6 +266,25 @@ def seam_step_workspace_size(fam: int, n_seg: int, w: int, n_chain: int, d: int)
     return out.value
 
 
+def _check_seam_shapes(fam, w, q, k, v, beta, log_gate, gate_per_chain, body, S_run, o_out, window_out):
+    if k.dim() != 3:
+        raise ValueError("k must be [n_seg * w, n_chain, d] (got shape %s)" % (tuple(k.shape),))
+    n_tok, n_chain, d = k.shape
+    if w < 1 or n_tok % w:
+        raise ValueError("window tokens must be n_seg * w")
+    n_seg = n_tok // w
+    if q is None:
+        raise ValueError("q is required")
+    _check_token_shapes(fam, n_tok, n_chain, d, k, v, q, beta, log_gate, gate_per_chain)
+    if body is not None:
+        _check_pair_shapes(fam, "body", n_seg, n_chain, d, *body)
+    if window_out is not None:
+        _check_pair_shapes(fam, "window_out", n_seg, n_chain, d, *window_out)
+    _want("S_run", S_run, (n_chain, d, d))
+    _want("o_out", o_out, (n_tok, n_chain, d))
+    return n_seg, n_chain, d
+
+
 def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chain=False, body=None,
               S_run=None, o_out=None, window_out=None, want_window_pairs=False, workspace=None, stream=None):
     """Seam-window step over [n_seg * w, n_chain, d] window tokens; S_run is updated in place.
@@ -221,10 +292,9 @@ def seam_step(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_per_chai
     body: None or (g, U, S) cached body pairs.  workspace: a uint8 device buffer
     of at least seam_step_workspace_size() bytes, or None to take one from
     torch's allocator for the call.  Returns dict with S_run, o and window pairs."""
-    n_tok, n_chain, d = k.shape
-    if n_tok % w:
-        raise ValueError("window tokens must be n_seg * w")
-    n_seg = n_tok // w
+    n_seg, n_chain, d = _check_seam_shapes(fam, w, q, k, v, beta, log_gate, gate_per_chain, body, S_run, o_out,
+                                           window_out)
+    n_tok = n_seg * w
     dev = k.device
     if S_run is None:
         S_run = torch.zeros((n_chain, d, v.shape[2]), device=dev, dtype=torch.float32)
@@ -260,12 +330,10 @@ def seam_step_noalloc(fam: int, w: int, q, k, v, beta=None, log_gate=None, gate_
     no workspace argument, and the library allocates nothing.  S_run (updated in
     place) and o_out must be given, as must window_out if window pairs are wanted;
     calls that overlap on one GPU race on the scratch."""
-    n_tok, n_chain, d = k.shape
-    if n_tok % w:
-        raise ValueError("window tokens must be n_seg * w")
     if S_run is None or o_out is None:
         raise ValueError("seam_step_noalloc takes preallocated S_run and o_out")
-    n_seg = n_tok // w
+    n_seg, n_chain, d = _check_seam_shapes(fam, w, q, k, v, beta, log_gate, gate_per_chain, body, S_run, o_out,
+                                           window_out)
     tk = _tokens(k, v, q, beta, log_gate, gate_per_chain)
     bp = ctypes.byref(Pairs(_ptr(body[0]), _ptr(body[1]), _ptr(body[2]))) if body is not None else None
     wp = ctypes.byref(Pairs(*[_ptr(x) for x in window_out])) if window_out is not None else None
@@ -282,7 +350,11 @@ def rerotate(fam: int, positions: torch.Tensor, S: torch.Tensor, U: Optional[tor
     """Rotary re-rotation of pairs [n_seg, n_chain, ...] in place: S <- R(p) S and,
     for the delta family, U <- R(p) U R(p)^T, with p = positions[s] (int32 on the
     GPU).  Returns (U, S)."""
+    if S.dim() != 4:
+        raise ValueError("S must be [n_seg, n_chain, d_k, d_v] (got shape %s)" % (tuple(S.shape),))
     n_seg, n_chain, dk, dv = S.shape
+    _want("S", S, (n_seg, n_chain, dk, dv))
+    _want("U", U, (n_seg, n_chain, dk, dk))
     if positions.dtype != torch.int32 or positions.shape != (n_seg,):
         raise ValueError("positions must be int32 of shape (n_seg,)")
     pr = Pairs(None, _ptr(U), _ptr(S))
