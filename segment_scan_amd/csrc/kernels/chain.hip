@@ -68,6 +68,7 @@ struct ChainCfg {
   static constexpr int BP = D + 8;            // fp16 pitch of a split state column and a window row
   static constexpr int NTA = IN_F32 ? 2 : 1;  // fp16 terms of window key and query rows
   static constexpr int NTK = IN_F32 ? 3 : 1;  // bf16 terms of window keys in the update
+  static constexpr int NTR = IN_F32 ? 3 : 2;  // bf16 terms of R' in the update
   static constexpr int RPP = SUB + 4;         // fp32 pitch of R' columns
   static constexpr int OFF_B = 0;                                // [NT][COLS][BP] f16
   static constexpr int OFF_CM = OFF_B + NT * COLS * BP * 2;      // [NRB][COLS] column maxima
@@ -150,6 +151,35 @@ __device__ __forceinline__ HFrag<N> split8h(const float (&x)[8]) {
   return f;
 }
 
+// The same for x s with s a power of two, exponent within fp32's normal range:
+// t0 = fp16(x s) and every residual exact in fp32 (each step one fused
+// multiply-add with an fp16 operand)
+template <int N>
+__device__ __forceinline__ HFrag<N> split8h_scaled(const float (&x)[8], float s) {
+  HFrag<N> f;
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f16_t t = (f16_t)(x[j] * s);
+    f.t[0][j] = t;
+    if (N > 1) r[j] = __builtin_fmaf(x[j], s, -(float)t);
+  }
+#pragma unroll
+  for (int i = 1; i < N; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f16_t t = (f16_t)r[j];
+      f.t[i][j] = t;
+      if (i + 1 < N) r[j] -= (float)t;
+    }
+  }
+  return f;
+}
+
+// 2^-e as a float, e clamped so that the factor stays a normal number (values
+// this far from 1 lose low bits in fp16 instead of overflowing the factor)
+__device__ __forceinline__ float pow2_neg(int e) { return ldexpf(1.f, -min(max(e, -100), 100)); }
+
 __device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -188,7 +218,7 @@ template <int D, int NCT, int NT, bool SEAM, bool IN_F32, bool PAIRS>
 __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a) {
   using Cfg = ChainCfg<D, NCT, NT, SEAM, IN_F32>;
   constexpr int NRB = Cfg::NRB, NTH = Cfg::NTH, COLS = Cfg::COLS, NCG = Cfg::NCG, KS = Cfg::KS;
-  constexpr int BP = Cfg::BP, NTA = Cfg::NTA, NTK = Cfg::NTK, RPP = Cfg::RPP;
+  constexpr int BP = Cfg::BP, NTA = Cfg::NTA, NTK = Cfg::NTK, NTR = Cfg::NTR, RPP = Cfg::RPP;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   f16_t* sB = reinterpret_cast<f16_t*>(smem + Cfg::OFF_B);    // [term][col][k]
@@ -305,23 +335,28 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
       float m = 0.f;
 #pragma unroll
       for (int s = 0; s < NRB; ++s) m = fmaxf(m, sCM[s * COLS + c]);
-      ec[ct] = split_exp(m * f);
+      ec[ct] = min(max(split_exp(m * f), -100), 100);
+      const float sc = f * ldexpf(1.f, -ec[ct]);  // exact: f times a normal power of two
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float r[4];
+        f16x4 tv[NT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = ldexpf(St[ct][4 * q + j] * f, -ec[ct]);
-        const int off = c * BP + 32 * rb + 8 * q + 4 * h;
+        for (int j = 0; j < 4; ++j) {
+          const float x = St[ct][4 * q + j];
+          tv[0][j] = (f16_t)(x * sc);
+          if (NT > 1) r[j] = __builtin_fmaf(x, sc, -(float)tv[0][j]);
+        }
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          f16x4 tv;
+        for (int i = 1; i < NT; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            tv[j] = (f16_t)r[j];
-            if (i + 1 < NT) r[j] -= (float)tv[j];
+            tv[i][j] = (f16_t)r[j];
+            if (i + 1 < NT) r[j] -= (float)tv[i][j];
           }
-          *reinterpret_cast<f16x4*>(sB + i * COLS * BP + off) = tv;
-        }
+        const int off = c * BP + 32 * rb + 8 * q + 4 * h;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) *reinterpret_cast<f16x4*>(sB + i * COLS * BP + off) = tv[i];
       }
     }
   };
@@ -340,31 +375,35 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
   float wrec_r[RPT];
   // loads of window (seg, sub): chunk i < 2 SUB (D / 8) is 8 elements of a K
   // (t < SUB) or Q row, the rest 8 values of a V row of the group's columns
+  // element offset of token tok0 + t of this chain: a uniform base plus a 32-bit
+  // per-lane part (t < SUB, n_chain D < 2^31 / SUB)
+  const uint32_t tok_stride = (uint32_t)n_chain * D;
+  auto tok_base = [&](size_t tok0) { return (tok0 * n_chain + chain) * D; };
   auto issue_window = [&](int seg, int sub) {
     const int n = min(SUB, a.w - sub * SUB);
-    const size_t tok0 = (size_t)seg * a.w + sub * SUB;
+    const size_t base = tok_base((size_t)seg * a.w + sub * SUB);
 #pragma unroll
     for (int k = 0; k < Cfg::WPT; ++k) {
       const int i = tid + k * NTH;
       int t = -1;
       const void* src = nullptr;
-      size_t off = 0;
+      uint32_t off = 0;
       if (i < 2 * SUB * (D / 8)) {
         const int row = i / (D / 8), d8 = i % (D / 8);
         t = row % SUB;
         src = row < SUB ? a.k : a.q;
-        off = ((tok0 + t) * n_chain + chain) * D + 8 * d8;
+        off = (uint32_t)t * tok_stride + 8 * d8;
       } else if (i < Cfg::NWCH) {
         const int j = i - 2 * SUB * (D / 8);
         t = j / (COLS / 8);
         src = a.v;
-        off = ((tok0 + t) * n_chain + chain) * D + col0 + 8 * (j % (COLS / 8));
+        off = (uint32_t)t * tok_stride + col0 + 8 * (j % (COLS / 8));
       }
 #pragma unroll
       for (int u = 0; u < (IN_F32 ? 2 : 1); ++u) wraw[k][u] = make_uint4(0, 0, 0, 0);
       if (t >= 0 && t < n) {
         const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(src) +
-                                                        off * (IN_F32 ? 4 : 2));
+                                                        (base + off) * (IN_F32 ? 4 : 2));
 #pragma unroll
         for (int u = 0; u < (IN_F32 ? 2 : 1); ++u) wraw[k][u] = p[u];
       }
@@ -406,11 +445,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
         m = dpp_max_step(m, 1);
         m = dpp_max_step(m, 2);
         if (D / 8 >= 16) m = dpp_max_step(m, 3);
-        const int e = split_exp(m);
-        float xs[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xs[j] = ldexpf(x[j], -e);
-        const HFrag<NTA> fa = split8h<NTA>(xs);
+        const int e = min(max(split_exp(m), -100), 100);
+        const HFrag<NTA> fa = split8h_scaled<NTA>(x, ldexpf(1.f, -e));
 #pragma unroll
         for (int term = 0; term < NTA; ++term)
           *reinterpret_cast<f16x8*>(sA + (term * 2 * SUB + row) * BP + 8 * d8) = fa.t[term];
@@ -440,18 +476,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
       if (tid + k * NTH < SEAM_REC_FLOATS) sRec[tid + k * NTH] = wrec_r[k];
   };
 
-  // ---- start state -----------------------------------------------------------------
+  // ---- start state (one branch around all the loads, so they fly together) ---------
+  if (!ut && a.S_in) {
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float* p = tile_ptr(a.S_in + unit_off, ct);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 32 * rb + acc_row(r, lane), col = col0 + 32 * ct + l32;
-      if (ut) {
-        St[ct][r] = (row == col) ? 1.f : 0.f;
-      } else {
-        St[ct][r] = a.S_in ? a.S_in[unit_off + (size_t)row * D + col] : 0.f;
-      }
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) St[ct][4 * q + j] = p[(8 * q + j) * D];
     }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        St[ct][r] = (ut && 32 * rb + acc_row(r, lane) == col0 + 32 * ct + l32) ? 1.f : 0.f;
+  }
   if (!ut && a.prefix) store_tiles(a.prefix + pair_off);  // prefix states follow the pairs' layout
   put_cmax();
   float g_next = 0.f;
@@ -472,19 +513,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
       for (int sub = 0; sub < n_sub; ++sub) {
         refresh();
         const int n = min(SUB, a.w - sub * SUB);
-        const size_t tok0 = (size_t)seg * a.w + sub * SUB;
+        const size_t obase = tok_base((size_t)seg * a.w + sub * SUB);
         // the next window's loads fly during this one and the body pair
         if (sub + 1 < n_sub) issue_window(seg, sub + 1);
         else if (seg + 1 < nseg) issue_window(seg + 1, 0);
         const float* sCt = sRec;              // [t][s]: Abar[t][s] exp(G_n - G_t)
         const float* sW2 = sRec + SUB * SUB;  // [t][s]: ((tril(Q K^T) o Gamma) Abar)[t][s]
         const float* sEG = sRec + 2 * SUB * SUB;  // exp(G_t); [SUB] = exp(G_n)
-        // [X; P] = [K; Q] S for column block cb = rb (waves rb < NCT), on
-        // 16x16x32 MFMA: rows are the 8 keys and 8 queries, two 16-column tiles
-        if (rb < NCT) {
-          const int cb = rb;
+        // [X; P] = [K; Q] S on 16x16x32 MFMA: rows are the 8 keys and 8 queries,
+        // one 16-column tile per wave (tiles ct16 = rb, rb + NRB, ... of the
+        // group's 2 NCT); then [R'; W2 R] = [C^T; W2] R on one 16x16x16 MFMA
+        // per tile, R in the B layout exactly where the X rows come out
+#pragma unroll
+        for (int ct16 = 0; ct16 < 2 * NCT; ++ct16) {
+          if (ct16 % NRB != rb) continue;
           const int l16 = lane & 15, g = lane >> 4;
-          f32x4 XP[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          const int col = 16 * ct16 + l16;  // the lane's column within the group
+          f32x4 XP = f32x4{0.f, 0.f, 0.f, 0.f};
           const f16_t* pa = sA + l16 * BP + 8 * g;
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks) {
@@ -492,64 +537,77 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
 #pragma unroll
             for (int i = 0; i < NTA; ++i)
               fa.t[i] = *reinterpret_cast<const f16x8*>(pa + i * 2 * SUB * BP + 32 * ks);
+            HFrag<NT> fb;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-              const int col = 32 * cb + 16 * ct + l16;
-              HFrag<NT> fb;
-#pragma unroll
-              for (int i = 0; i < NT; ++i)
-                fb.t[i] = *reinterpret_cast<const f16x8*>(sB + (i * COLS + col) * BP + 32 * ks + 8 * g);
-              mmah16<NTA, NT>(XP[ct], fa, fb);
-            }
-            sched_fence();  // bounds how far ahead fragments are loaded
+            for (int i = 0; i < NT; ++i)
+              fb.t[i] = *reinterpret_cast<const f16x8*>(sB + (i * COLS + col) * BP + 32 * ks + 8 * g);
+            mmah16<NTA, NT>(XP, fa, fb);
           }
-          // the exponent of column block cb (tile cb of the lanes' columns)
-          int ecb = ec[0];
+          // the column's exponent: tile col / 32 of lane col % 32
+          int ecc = ec[0];
 #pragma unroll
           for (int ct = 1; ct < NCT; ++ct)
-            if (cb == ct) ecb = ec[ct];
-          // lane (l16, g), tile ct: column 32 cb + 16 ct + l16, rows 4g + j: X of
-          // token 4g + j (g < 2) or P of token 4(g - 2) + j (g >= 2).  Every lane
-          // scales its rows; X lanes form R; P lanes gather the column's R and
-          // emit the outputs and R'.
+            if (ct16 / 2 == ct) ecc = ec[ct];
+          const int ce = __shfl(ecc, col & 31, 64);
+          // lane (l16, g): rows 4g + j of the tile -- X of token 4g + j (g < 2),
+          // P of token 4(g - 2) + j (g >= 2); R = V - exp(G) X on the X lanes
+          float v4[4];
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            const int col = 32 * cb + 16 * ct + l16;
-            const int ce = __shfl(ecb, 16 * ct + l16, 64);  // the column's exponent
-            float v4[4];
+          for (int j = 0; j < 4; ++j) {
+            const int row = 4 * g + j;  // 0..7 keys, 8..15 queries
+            const int t = row & 7;
+            const float x = ldexpf(XP[j], ce) * sAS[row];
+            v4[j] = g < 2 ? sV[t * COLS + col] - sEG[t] * x : sEG[t] * x;  // R, or exp(G) P
+          }
+          // B = R (k = token 4g + j on the X lanes, zero on the P lanes), scaled
+          // per column by a power of two and split into NT fp16 terms
+          float m = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) m = fmaxf(m, g < 2 ? fabsf(v4[j]) : 0.f);
+          m = fmaxf(m, __shfl_xor(m, 16, 64));
+          // every lane of the column (the P lanes too) takes the X lanes' exponent
+          const int er = __shfl(split_exp(m), l16, 64);
+          float rb4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rb4[j] = g < 2 ? ldexpf(v4[j], -er) : 0.f;
+          // A = [C^T; W2] (row l16, k = 4g + j; zero for k >= 8)
+          float a4[4] = {0.f, 0.f, 0.f, 0.f};
+          if (g < 2) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>((l16 < 8 ? sCt + l16 * SUB : sW2 + (l16 - 8) * SUB) +
+                                                             4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a4[j] = av[j];
+          }
+          f16x4 at[NT], bt[NT];
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int row = 4 * g + j;  // 0..7 keys, 8..15 queries
-              const int t = row & 7;
-              const float x = ldexpf(XP[ct][j], ce) * sAS[row];
-              v4[j] = g < 2 ? sV[t * COLS + col] - sEG[t] * x : sEG[t] * x;  // R, or exp(G) P
-            }
-            float Ra[SUB];  // R of the column's 8 tokens, from its two X lane groups
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              Ra[j] = __shfl(v4[j], l16, 64);
-              Ra[4 + j] = __shfl(v4[j], 16 + l16, 64);
-            }
-            if (g >= 2) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int t = 4 * (g - 2) + j;
-                const f32x4 w0 = *reinterpret_cast<const f32x4*>(sW2 + t * SUB);
-                const f32x4 w1 = *reinterpret_cast<const f32x4*>(sW2 + t * SUB + 4);
-                const f32x4 c0 = *reinterpret_cast<const f32x4*>(sCt + t * SUB);
-                const f32x4 c1 = *reinterpret_cast<const f32x4*>(sCt + t * SUB + 4);
-                const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-                const float c8[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                float o = v4[j], rp = 0.f;
-#pragma unroll
-                for (int s = 0; s < SUB; ++s) {
-                  o = fmaf(w8[s], Ra[s], o);  // W2 is lower triangular
-                  rp = fmaf(c8[s], Ra[s], rp);
-                }
-                if (t < n) a.o[((tok0 + t) * n_chain + chain) * D + col0 + col] = o;
-                sRp[col * RPP + t] = rp;
-                sched_fence();  // one token's record rows in registers at a time
+              at[i][j] = (f16_t)a4[j];
+              bt[i][j] = (f16_t)rb4[j];
+              if (i + 1 < NT) {
+                a4[j] -= (float)at[i][j];
+                rb4[j] -= (float)bt[i][j];
               }
+            }
+          f32x4 RW = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = NT - 1; s2 >= 0; --s2)
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+              if (s2 - i >= 0 && s2 - i < NT)
+                RW = __builtin_amdgcn_mfma_f32_16x16x16f16(at[i], bt[s2 - i], RW, 0, 0, 0);
+          // rows 0..7 (lanes g < 2): R' of token 4g + j; rows 8..15 (g >= 2): W2 R
+          if (g < 2) {
+            f32x4 rp;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rp[j] = ldexpf(RW[j], er);
+            *reinterpret_cast<f32x4*>(sRp + col * RPP + 4 * g) = rp;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int t = 4 * (g - 2) + j;
+              if (t < n) a.o[obase + (uint32_t)t * tok_stride + col0 + col] = v4[j] + ldexpf(RW[j], er);
             }
           }
         }
@@ -571,17 +629,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
           for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) St[ct][r] *= eGn;
-            Frag<3> fb;
+            Frag<NTR> fb;
             if (h == 0) {
               const f32x4 r0 = *reinterpret_cast<const f32x4*>(sRp + (32 * ct + l32) * RPP);
               const f32x4 r1 = *reinterpret_cast<const f32x4*>(sRp + (32 * ct + l32) * RPP + 4);
               const float x[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-              fb = split8<3>(x);
+              fb = split8<NTR>(x);
             } else {
 #pragma unroll
-              for (int term = 0; term < 3; ++term) fb.t[term] = bf16x8{};
+              for (int term = 0; term < NTR; ++term) fb.t[term] = bf16x8{};
             }
-            mma<NTK, 3>(St[ct], fa, fb);
+            mma<NTK, NTR>(St[ct], fa, fb);
           }
           put_cmax();
         }
@@ -605,6 +663,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
 #pragma unroll
           for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(ur[ks][i][j]));
       const int eu = split_exp(wave_max_uniform(m));
+      const float su = pow2_neg(eu);
       f32x16 T[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) T[ct] = zero16();
@@ -614,10 +673,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
         float x[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          x[j] = ldexpf(ur[ks][0][j], -eu);
-          x[4 + j] = ldexpf(ur[ks][1][j], -eu);
+          x[j] = ur[ks][0][j];
+          x[4 + j] = ur[ks][1][j];
         }
-        HFrag<NT> fa = split8h<NT>(x);
+        HFrag<NT> fa = split8h_scaled<NT>(x, su);
         // (the split is complete before the slice's registers are reloaded)
 #pragma unroll
         for (int i = 0; i < NT; ++i) asm volatile("" : "+v"(fa.t[i])::"memory");
@@ -639,7 +698,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          St[ct][r] = ldexpf(T[ct][r], eu + ec[ct]);
+          St[ct][r] = ldexpf(T[ct][r], min(max(eu, -100), 100) + ec[ct]);
           if (!ut) St[ct][r] += Si[ct][r];
         }
       if (!more) store_results();
@@ -686,11 +745,16 @@ hipError_t launch_chain_t(const ChainArgs& a, bool want_ut, hipStream_t stream) 
 }
 
 // Composition of fp32 pairs (three fp16 terms per operand): one 32-column tile
-// per workgroup while that keeps the grid within about four workgroups per
-// CU, else two.
+// per workgroup while the grid fits the CUs in one round (three such
+// workgroups per CU), else two tiles (two workgroups per CU, each U slice
+// split for twice the columns).
+#ifndef HYPIC_COMPOSE_NCT1_MAX
+#define HYPIC_COMPOSE_NCT1_MAX 768
+#endif
 template <int D>
 hipError_t launch_compose_d(const ChainArgs& a, bool want_ut, hipStream_t stream) {
-  if ((long)a.n_units * (D / 32) * (want_ut ? 2 : 1) <= 1024) return launch_chain_t<D, 1, 3, false, false>(a, want_ut, stream);
+  if ((long)a.n_units * (D / 32) * (want_ut ? 2 : 1) <= HYPIC_COMPOSE_NCT1_MAX)
+    return launch_chain_t<D, 1, 3, false, false>(a, want_ut, stream);
   return launch_chain_t<D, 2, 3, false, false>(a, want_ut, stream);
 }
 
