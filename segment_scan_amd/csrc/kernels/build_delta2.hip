@@ -220,12 +220,9 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
     const float bt = sBeta[t];
-    m *= fabsf(bt);
-    int e = 0;
-    if (m > 0.f) {
-      frexpf(m, &e);
-      e -= 14;  // row maximum into [2^13, 2^14)
-    }
+    // a row whose largest entry is already inside fp16's working range keeps
+    // scale 1 (the usual case), so the state pass can skip the row factors
+    const int e = f16_scale_exp(m * fabsf(bt));
     const float s = bt * ldexpf(1.f, -e);
     f16x8* dst = reinterpret_cast<f16x8*>(rec + REC_A + t * C * 2);
 #pragma unroll
@@ -406,8 +403,11 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
       float* sF = reinterpret_cast<float*>(base + StateLds::O_SM);
       sF[tid] = KDA ? fin[0] : __expf(fin[1] - fin[0]);  // value weight to the chunk end
       sF[C + tid] = fin[2];                               // row scale of A0
+      // (threads < C are wave 0: one vote) every row scale of the chunk is 1
+      const bool unit_rows = __ballot(fin[2] != 1.f) == 0;
       if (tid == 0) {
         sF[2 * C] = KDA ? fin[5] : __expf(fin[1]);
+        sF[2 * C + 1] = unit_rows ? 1.f : 0.f;
         g_acc += (double)fin[1];
       }
     }
@@ -437,6 +437,8 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
       const int lane = opaque(threadIdx.x) & 63;
       const int h = lane >> 5, l32 = lane & 31;
       const float eGC = sF[2 * C];
+      float fez;   // delta mode: W = K Z / fez after step 1
+      float f_er;  // W holds X' / f_er after step 2
       f32x16 W[2];
       // ---- step 1: Y = K Z (S waves: exp(G_C) K Z, the factor folded into Z's conversion)
       {
@@ -448,6 +450,7 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
         const float gz = s_wave ? eGC : 1.f;
         const int ez = f16_scale_exp(wave_max_uniform(m) * gz);
         const float sz = gz * ldexpf(1.f, -ez);
+        fez = KDA ? 1.f : ldexpf(1.f, ez);
         const f16_t* pK = sK + l32 * KP + 4 * h;
         W[0] = zero16();
         W[1] = zero16();
@@ -459,16 +462,18 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
           }
-        if (ez != 0) {
+        if (KDA && ez != 0) {
           const float f = ldexpf(1.f, ez);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) W[tt][r] *= f;
         }
+        // (delta mode: W = K Z 2^-ez; the factor 2^ez is applied where W is used)
       }
       // ---- step 2: R = diag(eW) V - exp(G_C) Y (S) or Y (U);  X' = (-)diag(rs) A0 R -----
       {
+        // S waves: R = diag(eW) V - W 2^ez; U waves: R = W, its factor 2^ez carried on
         if (s_wave) {
           // elements 4q .. 4q+3 of tile tt are tokens 32 tt + 8q + 4h + 0..3 of the lane's column
           const bf16_t* pV = sVt + (col0 + l32) * TP + 4 * h;
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
               const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
                                    __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
 #pragma unroll
-              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] = fmaf(ew[j], v4[j], -W[tt][4 * q + j]);  // (W carries exp(G_C))
+              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] = fmaf(W[tt][4 * q + j], -fez, ew[j] * v4[j]);  // (W carries exp(G_C))
             }
         }
         float m = 0.f;
@@ -506,16 +511,20 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
             for (int tt = tp; tt < 2; ++tt)
               W[tt] = mfma32h(lds_a_perm_h(pA, 32 * tt * TP + 32 * tp + 16 * mm), fb[tp][mm], W[tt]);
-        const float f_er = (s_wave ? 1.f : -1.f) * ldexpf(1.f, er);
-        const float* fac = sF + C + 4 * h;
+        // X' = W f_er (times the row scales of A0 unless all are 1)
+        f_er = (s_wave ? 1.f : -1.f) * ldexpf(1.f, er) * ((KDA || s_wave) ? 1.f : fez);
+        if (KDA || sF[2 * C + 1] == 0.f) {
+          const float* fac = sF + C + 4 * h;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 f4 = *reinterpret_cast<const f32x4*>(fac + 32 * tt + 8 * q) * f_er;
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 f4 = *reinterpret_cast<const f32x4*>(fac + 32 * tt + 8 * q) * f_er;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) W[tt][4 * q + j] *= f4[j];
-          }
+              for (int j = 0; j < 4; ++j) W[tt][4 * q + j] *= f4[j];
+            }
+          f_er = 1.f;
+        }
       }
       // ---- step 3: Z = (exp(G_C) | 1) Z + K^T X' ----------------------------------------
       {
@@ -524,7 +533,7 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
-        const int ex = f16_scale_exp(wave_max_uniform(m));
+        const int ex = f16_scale_exp(wave_max_uniform(m) * fabsf(f_er));
         if constexpr (KDA) {  // per-row factors exp(G_C) (S) or exp(G_C - mu_C) (U)
           const float sc = ldexpf(1.f, -ex);
           const float* rf = reinterpret_cast<const float*>(base + StateLds::O_RF) + (s_wave ? 0 : D) + 4 * h;
@@ -546,7 +555,7 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
           }
         }
         const f16_t* pKt = sKt + l32 * TP + 4 * h;
-        const float sx = ldexpf(1.f, -ex);
+        const float sx = f_er * ldexpf(1.f, -ex);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
