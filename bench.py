@@ -21,7 +21,11 @@ accumulation -- every (segment, head) pair (T_C, S(C|0)) built concurrently
 Prints one JSON line.  `value` is segment-tokens/s of the whole step; the
 `roofline` object is for the step's dominant kernel, timed with HIP events on
 the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
-sample of the same workload on this host's cores.
+sample of the same workload on all of this host's threads, and on one thread.
+The default run also carries a `warm` object: the warm request's seam step
+(composed segments/s, its roofline and oracle), the metric's second half.
+retnet and gla also report their composition alone as single-shot latency
+and as back-to-back throughput.
 """
 from __future__ import annotations
 
@@ -178,8 +182,10 @@ class Workload:
         """Enqueue one step; records ev0/ev1 around the dominant kernel."""
         raise NotImplementedError
 
-    def cpu_sample(self):
-        """Run the oracle on a bounded sample; returns (seconds, sample tokens, description)."""
+    def cpu_sample(self, n_threads=None):
+        """Run the oracle on a bounded sample with n_threads threads (all host
+        threads when None; the 1-thread run takes a smaller sample of the same
+        work); returns (seconds, sample tokens, description)."""
         raise NotImplementedError
 
 
@@ -240,17 +246,21 @@ class ColdRequest(Workload):
         ev1.record()
         self.api.compose(self.fam, self.g, self.U, self.S, S_out=self.S_out, workspace=self.cws)
 
-    def cpu_sample(self):
+    def cpu_sample(self, n_threads=None):
         import oracle
-        ns = self.n_seg  # the whole request: every segment and head, built and composed
+        # all threads: the whole request, every segment and head built and composed;
+        # one thread: its first 4 segments (all heads), a sixteenth of the work
+        ns = self.n_seg if n_threads is None else 4
         t1 = int(self.tk.offsets[ns])
         sl = slice(0, t1)
         t = time.perf_counter()
         g, U, S = oracle.build_pairs(self.fam, self.tk.offsets[:ns + 1], self.tk.k[sl], self.tk.v[sl],
-                                     self.tk.beta[sl], self.tk.log_gate[sl])
-        oracle.compose(self.fam, g, U, S)
+                                     self.tk.beta[sl], self.tk.log_gate[sl], n_threads=n_threads)
+        oracle.compose(self.fam, g, U, S, n_threads=n_threads)
         dt = time.perf_counter() - t
-        return dt, ns * self.L, "whole request (64 segments x 32 heads = 2048 units): build + ordered compose"
+        what = "whole request (64 segments x 32 heads = 2048 units)" if n_threads is None else \
+            "segments 0-3 of the request (x 32 heads = 128 units)"
+        return dt, int(self.tk.offsets[ns]), what + ": build + ordered compose"
 
     def config(self):
         return {"workload": self.name, "family": "gdn", "heads": self.H, "d": self.d, "segments": self.n_seg,
@@ -367,19 +377,52 @@ class ScalarOrDiag(Workload):
         ev1.record()
         self.api.compose(self.fam, b["g"], None, b["S"], S_out=b["S_out"])
 
-    def cpu_sample(self):
+    def cpu_sample(self, n_threads=None):
         import oracle
-        ns = self.n_seg
+        ns = self.n_seg if n_threads is None else max(1, self.n_seg // 8)
         t1 = int(self.tk.offsets[ns])
         sl = slice(0, t1)
         lg = self.tk.log_gate if self.tk.gate_per_chain else self.tk.log_gate[sl]
         t = time.perf_counter()
         g, U, S = oracle.build_pairs(self.fam, self.tk.offsets[:ns + 1], self.tk.k[sl], self.tk.v[sl], None, lg,
-                                     self.tk.gate_per_chain)
-        oracle.compose(self.fam, g, U, S)
+                                     self.tk.gate_per_chain, n_threads=n_threads)
+        oracle.compose(self.fam, g, U, S, n_threads=n_threads)
         dt = time.perf_counter() - t
-        return dt, ns * self.L, "whole workload (%d segments x %d heads): build + ordered compose" % (
-            self.n_seg, self.H)
+        return dt, ns * self.L, "%d of %d segments (x %d heads): build + ordered compose" % (
+            ns, self.n_seg, self.H)
+
+    def extra(self):
+        """The ordered composition of this workload's pairs on its own: single-shot
+        latency (each call alone, synchronised before and after, as a lone
+        request sees it) and steady state (back-to-back calls over the rotating
+        buffer sets)."""
+        import torch
+        b = self.sets[0]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for e0, e1 in ev:
+            torch.cuda.synchronize()
+            e0.record()
+            self.api.compose(self.fam, b["g"], None, b["S"], S_out=b["S_out"])
+            e1.record()
+            torch.cuda.synchronize()
+        single = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        reps = 50
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for i in range(reps):
+            bs = self.sets[i % self.n_sets]
+            self.api.compose(self.fam, bs["g"], None, bs["S"], S_out=bs["S_out"])
+        c1.record()
+        torch.cuda.synchronize()
+        steady = c0.elapsed_time(c1) / reps
+        gbytes = self.n_seg * self.H * (self.d * self.d * 4 + 4 * (self.d if self.fam == 2 else 1)) + \
+            self.H * self.d * self.d * 4
+        return {"compose": {"single_shot_ms_median": round(single[len(single) // 2], 4),
+                            "steady_state_ms": round(steady, 4),
+                            "steady_state_gbs": round(gbytes / (steady / 1e3) / 1e9, 1),
+                            "alg_bytes": gbytes,
+                            "composed_segs_per_s_steady": round(self.n_seg / (steady / 1e3), 1)}}
 
     def config(self):
         return {"workload": self.name, "family": "retnet" if self.fam == 1 else "gla", "heads": self.H, "d": self.d,
@@ -442,20 +485,26 @@ class WarmRequest(Workload):
                            S_run=self.S_run, o_out=self.o, workspace=self.ws)
         ev1.record()
 
-    def cpu_sample(self):
+    def cpu_sample(self, n_threads=None):
         import oracle
         from segment_scan_amd import synth
         from segment_scan_amd.synth import DELTA
-        n_layers = 2  # layers 0 and 1 in full (196 segments x 16 heads each)
+        # all threads: layers 0 and 1 in full (196 segments x 16 heads each); one
+        # thread: the first 49 segments of layer 0
+        n_layers = 2 if n_threads is None else 1
+        n_seg = self.n_seg if n_threads is None else self.n_seg // 4
         dt = 0.0
         for layer in range(n_layers):
-            tk = synth.warm_seam_layer(layer)
-            body = synth.warm_pairs_layer(layer)
+            tk = synth.warm_seam_layer(layer, n_seg=n_seg)
+            body = synth.warm_pairs_layer(layer, n_seg=n_seg)
             t = time.perf_counter()
-            oracle.seam(DELTA, self.n_seg, self.w, tk.q, tk.k, tk.v, tk.beta, tk.log_gate, body=body)
+            oracle.seam(DELTA, n_seg, self.w, tk.q, tk.k, tk.v, tk.beta, tk.log_gate, body=body,
+                        n_threads=n_threads)
             dt += time.perf_counter() - t
-        # the sample is n_layers / 30 of the request's work
-        return dt, self.tokens * n_layers / self.layers, "layers 0-1 of 30 in full (seam + compose), scaled"
+        # the sample's share of the request's work
+        frac = n_layers / self.layers * n_seg / self.n_seg
+        what = "layers 0-1 of 30 in full" if n_threads is None else "segments 0-48 of layer 0"
+        return dt, self.tokens * frac, what + " (seam + compose), scaled"
 
     def config(self):
         return {"workload": self.name, "family": "gdn", "layers": self.layers, "heads": self.H, "d": self.d,
@@ -497,19 +546,23 @@ class KdaWarmRequest(WarmRequest):
                            S_run=self.S_run, o_out=self.o)
         ev1.record()
 
-    def cpu_sample(self):
+    def cpu_sample(self, n_threads=None):
         import oracle
         from segment_scan_amd import synth
         from segment_scan_amd.synth import KDA
-        n_layers = 2
+        n_layers = 2 if n_threads is None else 1
+        n_seg = self.n_seg if n_threads is None else self.n_seg // 4
         dt = 0.0
         for layer in range(n_layers):
-            tk = synth.kda(n_seg=self.n_seg, L=self.w, n_chain=self.H, want_q=True)
-            body = synth.warm_pairs_layer(layer)
+            tk = synth.kda(n_seg=n_seg, L=self.w, n_chain=self.H, want_q=True)
+            body = synth.warm_pairs_layer(layer, n_seg=n_seg)
             t = time.perf_counter()
-            oracle.seam(KDA, self.n_seg, self.w, tk.q, tk.k, tk.v, tk.beta, tk.log_gate, body=body)
+            oracle.seam(KDA, n_seg, self.w, tk.q, tk.k, tk.v, tk.beta, tk.log_gate, body=body,
+                        n_threads=n_threads)
             dt += time.perf_counter() - t
-        return dt, self.tokens * n_layers / self.layers, "layers 0-1 of 30 in full (seam + compose), scaled"
+        frac = n_layers / self.layers * n_seg / self.n_seg
+        what = "layers 0-1 of 30 in full" if n_threads is None else "segments 0-48 of layer 0"
+        return dt, self.tokens * frac, what + " (seam + compose), scaled"
 
     def config(self):
         c = super().config()
@@ -552,19 +605,21 @@ class WarmRerotate(Workload):
         self.api.rerotate(DELTA, self.pos, self.S, self.U)
         ev1.record()
 
-    def cpu_sample(self):
+    def cpu_sample(self, n_threads=None):
         import oracle
         from segment_scan_amd import synth
         from segment_scan_amd.synth import DELTA
-        n_layers = 2
-        pos = np.random.default_rng(20260702).integers(-(1 << 20), 1 << 20, self.n_seg)
+        n_layers = 2 if n_threads is None else 1
+        n_seg = self.n_seg if n_threads is None else self.n_seg // 4
+        pos = np.random.default_rng(20260702).integers(-(1 << 20), 1 << 20, n_seg)
         dt = 0.0
         for layer in range(n_layers):
-            _, U, S = synth.warm_pairs_layer(layer)
+            _, U, S = synth.warm_pairs_layer(layer, n_seg=n_seg)
             t = time.perf_counter()
-            oracle.rerotate(DELTA, U, S, pos)
+            oracle.rerotate(DELTA, U, S, pos, n_threads=n_threads)
             dt += time.perf_counter() - t
-        return dt, self.tokens * n_layers / self.layers, "layers 0-1 of 30 in full (196 segments x 16 heads), scaled"
+        frac = n_layers / self.layers * n_seg / self.n_seg
+        return dt, self.tokens * frac, "%d layer(s) x %d segments x 16 heads, scaled" % (n_layers, n_seg)
 
     def config(self):
         return {"workload": self.name, "family": "gdn", "layers": self.layers, "heads": self.H, "d": self.d,
@@ -591,6 +646,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gdn_cold32k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="default workload only: skip the warm request's object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 1 GiB device copies (for scaling rocprofv3 byte counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -611,24 +668,7 @@ def main():
     import torch
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload]()
-    print("[bench] setting up %s" % wl.name, file=sys.stderr, flush=True)
-    wl.setup()
-    torch.cuda.synchronize()
-
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps + args.warmup)]
-    for i in range(args.warmup):
-        wl.step(*evs[i])
-    torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        wl.step(*evs[args.warmup + i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in evs[args.warmup:]]
-    k_ms = float(np.mean(kern_ms))
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step, kern_ms = measure(wl, args.steps, args.warmup)
 
     if args.copy_calibration:
         n = CALIBRATION_BYTES // 4
@@ -638,54 +678,103 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    copy_gbs = None if args.copy_calibration else copy_bandwidth()
 
-    # achievable HBM bandwidth on this machine: an elementwise kernel reading and
-    # writing 1 GiB each (out of place), timed with events
-    copy_gbs = None
-    if not args.copy_calibration:
-        n = CALIBRATION_BYTES // 4
-        src = torch.ones(n, device="cuda")
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(5):
-            torch.mul(src, 1.0, out=dst)
-        c1.record()
-        torch.cuda.synchronize()
-        copy_gbs = round(5 * 2 * CALIBRATION_BYTES / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
-        del src, dst
-
-    value = wl.tokens / (ms_per_step / 1e3)
-    achieved = wl.alg_bytes / (k_ms / 1e3) / 1e9
-    traffic = measured_traffic(wl.name, wl.kernel)
-    roofline = {"bound": "hbm", "kernel": wl.kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": wl.alg_bytes, "kernel_ms": round(k_ms, 4),
-                "kernel_ms_median": round(float(np.median(kern_ms)), 4),
-                "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 4),
-                "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 4),
-                "mfma_alg_tflops": round(wl.alg_flops / (k_ms / 1e3) / 1e12, 1),
-                "mfma_exec_tflops": round(wl.exec_flops / (k_ms / 1e3) / 1e12, 1),
-                "mfma_exec_frac": round(wl.exec_flops / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                "copy_gbs": copy_gbs,
-                "frac_of_copy": None if not copy_gbs else round(achieved / copy_gbs, 4)}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
-        dt, tokens, desc = wl.cpu_sample()
-        cpu = {"value": round(tokens / dt, 2), "unit": "segment-tokens/s", "cores": oracle.max_threads(),
-               "kind": "oracle", "sample": desc, "seconds": round(dt, 2), "cpu_model": cpu_model()}
-
-    out = {"metric": METRIC, "value": round(value, 1), "unit": "segment-tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+    roofline = roofline_obj(wl, kern_ms, copy_gbs)
+    cpu = None if args.no_cpu_baseline else cpu_obj(wl)
+    out = {"metric": METRIC, "value": round(wl.tokens / (ms_per_step / 1e3), 1), "unit": "segment-tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": wl.config(),
            "composed_segs_per_s": round(wl.composed / (ms_per_step / 1e3), 1),
            "roofline": roofline, "cpu_baseline": cpu}
+    if hasattr(wl, "extra"):
+        out.update(wl.extra())
+
+    # The metric's second half, composed segments per second, lives in the warm
+    # request: the default run also measures it (as its own object, after the
+    # cold request's buffers are released)
+    if args.workload == "gdn_cold32k" and not args.no_warm and not args.copy_calibration:
+        del wl
+        torch.cuda.empty_cache()
+        ww = WarmRequest()
+        w_ms, w_kern = measure(ww, args.steps, args.warmup)
+        out["warm"] = {"config": ww.config(), "ms_per_step": round(w_ms, 4),
+                       "composed_segs_per_s": round(ww.composed / (w_ms / 1e3), 1),
+                       "composed_head_segs_per_s": round(ww.composed * ww.H / (w_ms / 1e3), 1),
+                       "segment_tokens_per_s": round(ww.tokens / (w_ms / 1e3), 1),
+                       "roofline": roofline_obj(ww, w_kern, copy_gbs),
+                       "cpu_baseline": None if args.no_cpu_baseline else cpu_obj(ww)}
     print(json.dumps(out), flush=True)
+
+
+def measure(wl, steps, warmup):
+    """Set up, run `warmup` untimed steps, then time exactly `steps` (wall clock
+    around them, synchronised on both sides) and the dominant operation of each
+    with HIP events on the stream it runs on.  Returns (ms per step, op ms list)."""
+    import torch
+    print("[bench] setting up %s" % wl.name, file=sys.stderr, flush=True)
+    wl.setup()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps + warmup)]
+    for i in range(warmup):
+        wl.step(*evs[i])
+    torch.cuda.synchronize()
+    print("[bench] warmup done (%s)" % wl.name, file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.step(*evs[warmup + i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return elapsed * 1e3 / steps, [a.elapsed_time(b) for a, b in evs[warmup:]]
+
+
+def copy_bandwidth():
+    """Achievable HBM bandwidth on this machine: an elementwise kernel reading and
+    writing 1 GiB each (out of place), timed with events."""
+    import torch
+    n = CALIBRATION_BYTES // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    c1.record()
+    torch.cuda.synchronize()
+    gbs = round(5 * 2 * CALIBRATION_BYTES / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
+    del src, dst
+    return gbs
+
+
+def roofline_obj(wl, kern_ms, copy_gbs):
+    k_ms = float(np.mean(kern_ms))
+    achieved = wl.alg_bytes / (k_ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": wl.kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, wl.kernel),
+            "alg_bytes_per_launch": wl.alg_bytes, "kernel_ms": round(k_ms, 4),
+            "kernel_ms_median": round(float(np.median(kern_ms)), 4),
+            "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 4),
+            "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 4),
+            "mfma_alg_tflops": round(wl.alg_flops / (k_ms / 1e3) / 1e12, 1),
+            "mfma_exec_tflops": round(wl.exec_flops / (k_ms / 1e3) / 1e12, 1),
+            "mfma_exec_frac": round(wl.exec_flops / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "copy_gbs": copy_gbs, "frac_of_copy": None if not copy_gbs else round(achieved / copy_gbs, 4)}
+
+
+def cpu_obj(wl):
+    """The oracle timed on this host: all threads on the bounded sample, and one
+    thread on a smaller sample of the same work."""
+    import oracle
+    print("[bench] timing the oracle on a sample (%s)" % wl.name, file=sys.stderr, flush=True)
+    dt, tokens, desc = wl.cpu_sample()
+    dt1, tokens1, desc1 = wl.cpu_sample(n_threads=1)
+    return {"value": round(tokens / dt, 2), "unit": "segment-tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": desc, "seconds": round(dt, 2), "cpu_model": cpu_model(),
+            "single_thread": {"value": round(tokens1 / dt1, 2), "cores": 1, "sample": desc1,
+                              "seconds": round(dt1, 2)}}
 
 
 if __name__ == "__main__":
