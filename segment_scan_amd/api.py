@@ -190,8 +190,8 @@ def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor
     if k.dim() != 3:
         raise ValueError("k must be [n_tok, n_chain, d] (got shape %s)" % (tuple(k.shape),))
     n_tok, n_chain, d = k.shape
-    if n_seg < 1 or int(offsets[-1]) != n_tok:
-        raise ValueError("offsets must end at k.shape[0] = %d (got %s)" % (n_tok, int(offsets[-1])))
+    if n_seg < 1 or int(offsets[-1]) > n_tok:
+        raise ValueError("offsets must end within k.shape[0] = %d (got %s)" % (n_tok, int(offsets[-1])))
     _check_token_shapes(fam, n_tok, n_chain, d, k, v, None, beta, log_gate, gate_per_chain)
     dev = k.device
     if out is not None:

@@ -13,10 +13,11 @@
 // MFMA with the decay-weighted keys split into bf16 terms (values are exact
 // bf16 inputs).
 //
-// Grid: one workgroup (4 waves) per (segment, chain) unit.  Per chunk: the
-// 64 x d key and value tiles are loaded with 16-byte loads (8 tokens x 8
-// channels per thread), transposed in registers and written to LDS as
-// [channel][token] tiles, so each MFMA operand is one 16-byte LDS read.
+// Grid: one workgroup per (segment, chain) unit, 4d threads (8 waves at d =
+// 128, two 32 x 32 state tiles each).  Per chunk: the 64 x d key and value
+// tiles are loaded with 16-byte loads (4 tokens x 8 channels per thread; half
+// the threads keys and gates, half values), transposed in registers and written
+// to LDS as [channel][token] tiles, so each MFMA operand is one 16-byte LDS read.
 #include "common.h"
 #include "../launch.h"
 
@@ -66,19 +67,29 @@ __device__ __forceinline__ void cvt8(const Raw8<IN_F32>& r, float (&x)[8]) {
 // launches); launches of equal-length segments use the index order directly,
 // which keeps the table lookup (and the registers it costs this register-bound
 // kernel) out of their code.
-template <int FAM, int D, bool IN_F32, bool ORDERED>
-__global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
+// TOK: tokens per staging thread; the workgroup has 2 (C / TOK) (D / 8)
+// threads (half stage keys and gates, half values).
+#ifndef HYPIC_SD_WPE
+#define HYPIC_SD_WPE 2
+#endif
+template <int FAM, int D, bool IN_F32, bool ORDERED, int TOK>
+__global__ __launch_bounds__(2 * (C / TOK) * (D / 8)) __attribute__((amdgpu_waves_per_eu(HYPIC_SD_WPE)))
+void build_sd_kernel(const BuildArgs a) {
   constexpr int NTK = IN_F32 ? 3 : 2;  // bf16 terms of decay-weighted keys
   constexpr int NTV = IN_F32 ? 3 : 1;  // bf16 terms of values (bf16 inputs are exact)
   constexpr int NRT = D / 32;          // 32-row tiles along d
-  constexpr int TPW = NRT * NRT / 4;   // accumulator tiles per wave
+  constexpr int NTHR = 2 * (C / TOK) * (D / 8);
+  constexpr int NWAVE = NTHR / 64;     // waves of the workgroup
+  constexpr int TPW = NRT * NRT / NWAVE;  // accumulator tiles per wave
+  constexpr int NTB = C / TOK;         // token blocks of a chunk
+  static_assert(TPW >= 1 && NRT * NRT == TPW * NWAVE, "tiles per wave");
   constexpr bool DIAG = (FAM == 2);
   constexpr bool GATED = (FAM == 1 || FAM == 2);
 
   __shared__ __attribute__((aligned(16))) bf16_t sK[NTK][D * C];
   __shared__ __attribute__((aligned(16))) bf16_t sV[NTV][D * C];
   __shared__ float sW[C];        // scalar: weight exp(G_C - G_t)
-  __shared__ float sTot[8][D];   // diag: per-8-token block sums of log gates
+  __shared__ __attribute__((aligned(16))) float sTot[NTB][D];  // diag: per-token-block sums of log gates
   __shared__ float sGC[D];       // chunk log-transition (scalar: entry 0)
   __shared__ float sEGC[D];      // exp of it
 
@@ -99,33 +110,33 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
 
   double g_acc = 0.0;  // scalar: lane 0 of wave 0; diag: thread tid < D for channel tid
 
-  // staging role: threads [0, D) stage keys (and diagonal gates), [D, 2D) values
-  const bool is_k = tid < D;
-  const bool is_v = tid >= D && tid < 2 * D;
-  const int sid = is_k ? tid : tid - D;
-  const int tb = sid & 7;   // 8-token block
-  const int db = sid >> 3;  // 8-channel block
+  // staging role: the first half of the threads stage keys (and diagonal gates), the second values
+  const bool is_k = tid < NTHR / 2;
+  const bool is_v = !is_k;
+  const int sid = is_k ? tid : tid - NTHR / 2;
+  const int tb = sid % NTB;  // block of TOK tokens
+  const int db = sid / NTB;  // 8-channel block
   const void* src = is_k ? a.k : a.v;
 
   // raw inputs of the chunk being staged; the next chunk's are loaded while the
   // matrix cores work on this one
-  Raw8<IN_F32> rx[8];
-  Raw8<IN_F32> rg[8];
+  Raw8<IN_F32> rx[TOK];
+  Raw8<IN_F32> rg[TOK];
   float lg_scalar = 0.f;
   auto issue_loads = [&](int c0) {
     const int nv = min(C, t_end - c0);
-    if (is_k || is_v) {
+    {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int t = tb * 8 + r;
+      for (int r = 0; r < TOK; ++r) {
+        const int t = tb * TOK + r;
         rx[r] = ldraw8<IN_F32>(src, ((size_t)(c0 + min(t, nv - 1)) * n_chain + h) * D + db * 8, t < nv);
       }
     }
     if constexpr (DIAG) {
       if (is_k) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int t = tb * 8 + r;
+        for (int r = 0; r < TOK; ++r) {
+          const int t = tb * TOK + r;
           rg[r] = ldraw8<IN_F32>(a.lg, ((size_t)(c0 + min(t, nv - 1)) * n_chain + h) * D + db * 8, t < nv);
         }
       }
@@ -165,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) run[c] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
+        for (int r = 0; r < TOK; ++r) {
           float x[8];
           cvt8<IN_F32>(rg[r], x);
 #pragma unroll
@@ -177,32 +188,39 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
       __syncthreads();
       if (is_k) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float p = 0.f, t = 0.f;
+        for (int c = 0; c < 8; ++c) pre[c] = tot[c] = 0.f;
+        // block by block (two 16-byte reads each), so few reads are in flight
+#pragma unroll 2
+        for (int b = 0; b < NTB; ++b) {
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(&sTot[b][db * 8]);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(&sTot[b][db * 8 + 4]);
+          const float w = b < tb ? 1.f : 0.f;
 #pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const float x = sTot[b][db * 8 + c];
-            t += x;
-            if (b < tb) p += x;
+          for (int c = 0; c < 4; ++c) {
+            tot[c] += x0[c];
+            tot[4 + c] += x1[c];
+            pre[c] = fmaf(w, x0[c], pre[c]);
+            pre[4 + c] = fmaf(w, x1[c], pre[4 + c]);
           }
-          pre[c] = p;
-          tot[c] = t;
-          if (tb == 0) {
-            sGC[db * 8 + c] = t;
-            sEGC[db * 8 + c] = expf(t);
+        }
+        if (tb == 0) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            sGC[db * 8 + c] = tot[c];
+            sEGC[db * 8 + c] = expf(tot[c]);
           }
         }
       }
     }
 
     // ---- stage keys (decay-weighted, split) and values, transposed -------------
-    if (is_k || is_v) {
-      float x[8][8];  // [token r][channel c]
+    {
+      float x[TOK][8];  // [token r][channel c]
       float run[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) run[c] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int r = 0; r < TOK; ++r) {
         cvt8<IN_F32>(rx[r], x[r]);
         if (is_k && GATED) {
           if constexpr (DIAG) {
@@ -215,25 +233,42 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
             }
           } else {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[r][c] *= sW[tb * 8 + r];
+            for (int c = 0; c < 8; ++c) x[r][c] *= sW[tb * TOK + r];
           }
         }
       }
-      // column c of the block = 8 tokens of channel db*8+c -> one 16-byte LDS row chunk
+      // column c of the block = TOK tokens of channel db*8+c -> TOK / 8 of one
+      // 16-byte LDS row chunk (chunk tb TOK / 8 of the row, TOK-element part tb % (8 / TOK))
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        float col[8];
+        float col[TOK];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) col[r] = x[r][c];
+        for (int r = 0; r < TOK; ++r) col[r] = x[r][c];
         const int row = db * 8 + c;
+        const int off = swz64(row, (tb * TOK) / 8) + TOK * (tb % (8 / TOK));
+        using TokV = __attribute__((__vector_size__(TOK * sizeof(__bf16)))) __bf16;
         if (is_k) {
-          Frag<NTK> f = split8<NTK>(col);
 #pragma unroll
-          for (int i = 0; i < NTK; ++i) *reinterpret_cast<bf16x8*>(&sK[i][swz64(row, tb)]) = f.t[i];
+          for (int i = 0; i < NTK; ++i) {
+            TokV tv;
+#pragma unroll
+            for (int r = 0; r < TOK; ++r) {
+              tv[r] = (bf16_t)col[r];
+              if (i + 1 < NTK) col[r] -= (float)tv[r];
+            }
+            *reinterpret_cast<TokV*>(&sK[i][off]) = tv;
+          }
         } else {
-          Frag<NTV> f = split8<NTV>(col);
 #pragma unroll
-          for (int i = 0; i < NTV; ++i) *reinterpret_cast<bf16x8*>(&sV[i][swz64(row, tb)]) = f.t[i];
+          for (int i = 0; i < NTV; ++i) {
+            TokV tv;
+#pragma unroll
+            for (int r = 0; r < TOK; ++r) {
+              tv[r] = (bf16_t)col[r];
+              if (i + 1 < NTV) col[r] -= (float)tv[r];
+            }
+            *reinterpret_cast<TokV*>(&sV[i][off]) = tv;
+          }
         }
       }
     }
@@ -295,12 +330,17 @@ __global__ __launch_bounds__(256, 2) void build_sd_kernel(const BuildArgs a) {
   }
 }
 
+#ifndef HYPIC_SD_TOK
+#define HYPIC_SD_TOK 8
+#endif
 template <int FAM, int D, bool F32>
 hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
+  constexpr int TOK = HYPIC_SD_TOK;
+  constexpr int NTHR = 2 * (C / TOK) * (D / 8);
   if (seg_uniform(a.seg))
-    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, false>), dim3(n_blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, false, TOK>), dim3(n_blocks), dim3(NTHR), 0, stream, a);
   else
-    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, true>), dim3(n_blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, true, TOK>), dim3(n_blocks), dim3(NTHR), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@
 // Naive, scalar and diagonal families: T is I, exp(g) I or diag(exp(g)), so
 // the chain is elementwise, S <- a_s * S + S_s per element; a pure HBM stream,
 // one thread per 4 consecutive state elements, looping over the segments with
-// the next segment's loads in flight.  (The dense delta-family chain is in
+// the next eight segments' loads in flight.  (The dense delta-family chain is in
 // chain.hip.)
 #include "common.h"
 #include "../launch.h"
@@ -39,26 +39,42 @@ __global__ __launch_bounds__(256) void compose_elem_kernel(const ComposeArgs a) 
   } else {
     cur = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const f32x4* Sp = reinterpret_cast<const f32x4*>(a.S + pair0 * D * D) + v4;
-  f32x4 nxt = Sp[0];
-  float gn = 0.f;
-  if constexpr (FAM != 0) gn = a.g[pair0 * GL + (FAM == 2 ? row : 0)];
-  for (int s = 0; s < a.n_seg; ++s) {
-    const f32x4 Si = nxt;
-    const float gi = gn;
-    if (s + 1 < a.n_seg) {
-      nxt = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Sp) + (size_t)(s + 1) * seg_stride);
-      if constexpr (FAM != 0) gn = a.g[(pair0 + (size_t)(s + 1) * n_chain) * GL + (FAM == 2 ? row : 0)];
-    }
-    if (a.prefix) {
-      reinterpret_cast<f32x4*>(a.prefix + (size_t)s * seg_stride + chain_off)[v4] = cur;
-    }
-    if constexpr (FAM == 0) {
-      cur = cur + Si;
-    } else {
-      const float e = expf(gi);
+  const float* Sp = a.S + pair0 * D * D + 4 * (size_t)v4;
+  // PF segments' loads in flight per thread (a register ring refilled group by
+  // group), so that few threads per chain still keep the memory system busy
+  constexpr int PF = 8;
+  f32x4 buf[PF];
+  float gb[PF];
+  auto issue = [&](int s0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) cur[j] = fmaf(e, cur[j], Si[j]);
+    for (int j = 0; j < PF; ++j) {
+      const int s = min(s0 + j, a.n_seg - 1);  // past the end: a reread, never used
+      buf[j] = *reinterpret_cast<const f32x4*>(Sp + (size_t)s * seg_stride);
+      if constexpr (FAM != 0) gb[j] = a.g[(pair0 + (size_t)s * n_chain) * GL + (FAM == 2 ? row : 0)];
+    }
+  };
+  issue(0);
+  for (int s0 = 0; s0 < a.n_seg; s0 += PF) {
+    f32x4 cb[PF];
+    float cg[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      cb[j] = buf[j];
+      cg[j] = FAM != 0 ? gb[j] : 0.f;
+    }
+    if (s0 + PF < a.n_seg) issue(s0 + PF);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int s = s0 + j;
+      if (s >= a.n_seg) break;
+      if (a.prefix) reinterpret_cast<f32x4*>(a.prefix + (size_t)s * seg_stride + chain_off)[v4] = cur;
+      if constexpr (FAM == 0) {
+        cur = cur + cb[j];
+      } else {
+        const float e = expf(cg[j]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cur[k] = fmaf(e, cur[k], cb[j][k]);
+      }
     }
   }
   reinterpret_cast<f32x4*>(a.S_out + chain_off)[v4] = cur;

@@ -23,7 +23,7 @@ def bf(*shape):
 def test_seg_build_shapes():
     k, v, b, lg = bf(N_TOK, H, D), bf(N_TOK, H, D), bf(N_TOK, H), bf(N_TOK, H)
     with pytest.raises(ValueError, match="offsets must end"):
-        api.seg_build(DELTA, [0, 64, 100], k, v, b, lg)
+        api.seg_build(DELTA, [0, 64, 200], k, v, b, lg)
     with pytest.raises(ValueError, match="v has shape"):
         api.seg_build(DELTA, OFF, k, bf(N_TOK, H, D + 1), b, lg)
     with pytest.raises(ValueError, match="beta has shape"):
