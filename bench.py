@@ -48,6 +48,8 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "build_delta": ["segment_scan_amd/csrc/kernels/build_delta2.hip"],
+    "build_compose": ["segment_scan_amd/csrc/kernels/build_delta2.hip", "segment_scan_amd/csrc/kernels/chain.hip",
+                      "segment_scan_amd/csrc/hypic_api.cpp"],
     "build_sd": ["segment_scan_amd/csrc/kernels/build_sd.hip", "segment_scan_amd/csrc/kernels/compose.hip"],
     "seam": ["segment_scan_amd/csrc/kernels/chain.hip", "segment_scan_amd/csrc/kernels/seam_prep.hip"],
     "compose": ["segment_scan_amd/csrc/kernels/compose.hip", "segment_scan_amd/csrc/kernels/chain.hip"],
@@ -81,6 +83,7 @@ def measured_traffic(workload: str, kernel: str):
 # device kernels that make up each timed operation (substrings of their symbol names)
 KERNEL_SYMBOLS = {
     "build_delta": ["delta_prep_kernel", "delta_state_kernel", "build_delta_kernel"],
+    "build_compose": ["delta_prep_kernel", "delta_state_kernel", "chain_kernel"],
     "build_sd": ["build_sd_kernel", "compose_elem_kernel"],
     "seam": ["seam_prep_kernel", "chain_kernel"],
     "compose": ["chain_kernel", "compose_elem_kernel"],
@@ -266,6 +269,42 @@ class ColdRequest(Workload):
         return {"workload": self.name, "family": "gdn", "heads": self.H, "d": self.d, "segments": self.n_seg,
                 "segment_len": self.L, "tokens": self.tokens, "inputs": "bf16", "accumulate": "fp32",
                 "step": "hypic_seg_build (2048 units) + hypic_compose (32 chains x 64)"}
+
+
+class PipelinedColdRequest(ColdRequest):
+    """The cold GDN request in one call (hypic_seg_build_compose): groups of 16
+    segments built on the caller's stream, each group composed on a second
+    stream while the next is built, the group pairs composed in order last.
+    The timed operation is the whole call; its algorithmic bytes are the
+    build's (tokens in, pairs out) plus the final states."""
+    name = "gdn_cold32k_pipelined"
+    kernel = "build_compose"
+    op_dispatches = 14   # 4 x (factor pass, state pass, group composition) + final composition (x 2 for U)
+    step_dispatches = 14
+
+    def __init__(self):
+        super().__init__()
+        self.alg_bytes += self.H * self.d * self.d * 4
+
+    def setup(self):
+        import torch
+        super().setup()
+        n_ws = self.api.seg_build_compose_workspace_size(self.fam, self.offsets, self.H, self.d, torch.bfloat16,
+                                                         self.api.BC_PIPELINED)
+        self.ws = torch.empty(n_ws, device="cuda", dtype=torch.uint8)
+
+    def step(self, ev0, ev1):
+        ev0.record()
+        self.api.seg_build_compose(self.fam, self.offsets, self.k, self.v, self.beta, self.lg,
+                                   out=(self.g, self.U, self.S), S_out=self.S_out, mode=self.api.BC_PIPELINED,
+                                   workspace=self.ws)
+        ev1.record()
+
+    def config(self):
+        c = super().config()
+        c.update(workload=self.name, step="hypic_seg_build_compose (2048 units in 4 groups of 16 segments, "
+                                          "each group composed on a second stream while the next is built)")
+        return c
 
 
 class RaggedRequest(ColdRequest):
@@ -629,6 +668,7 @@ class WarmRerotate(Workload):
 
 WORKLOADS = {
     "gdn_cold32k": ColdRequest,
+    "gdn_cold32k_pipelined": PipelinedColdRequest,
     "retnet": lambda: ScalarOrDiag("retnet", 1, 16, 1024, 8, 128),
     "gla": lambda: ScalarOrDiag("gla", 2, 64, 512, 16, 128),
     "gdn_warm100k": WarmRequest,

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 7
+#define HYPIC_ABI_VERSION 8
 
 typedef enum {
   HYPIC_OK = 0,
@@ -212,6 +212,59 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
                            const hypic_cpairs* in, const float* S_init, float* S_out,
                            float* prefix_states, float* g_total, float* U_total,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hypic_seg_build_compose -- a cold request in one call: every (segment, chain)
+ * pair built as by hypic_seg_build, and every chain's pairs composed in index
+ * order as by hypic_compose.
+ *
+ * [youleyou, segment-parallelism paragraph]: cold segments are prefilled in
+ * parallel by scatter workers and a combine worker composes their results in
+ * order, the combine step overlapping the scatter; [hwlabs, section 병렬 콜드
+ * 프리필]: the pieces are joined by operator composition.  Two schedules:
+ *   HYPIC_BC_SEQUENTIAL  every pair built in one pass, then composed (the
+ *                        blocked scan of hypic_compose where it applies), all
+ *                        on the caller's stream;
+ *   HYPIC_BC_PIPELINED   the segments built in groups of consecutive segments
+ *                        (enough units to fill the GPU once); each group, once
+ *                        built, composed into one pair per chain on a second
+ *                        stream of the library while the caller's stream builds
+ *                        the next group; the group pairs then composed in order
+ *                        on the caller's stream.  The second stream waits only
+ *                        on events recorded on the caller's stream, and the
+ *                        caller's stream on it before the last composition, so
+ *                        the call is ordered on `stream` like any other (and can
+ *                        be captured into a graph from it).  The library creates
+ *                        that stream and its events once per host thread and
+ *                        device, on the first call.
+ * On one MI355X the sequential schedule is the faster at the 32k-token cold
+ * request's shape (the two phases share the CUs' slots when overlapped).
+ *
+ *   out            the built pairs, as for hypic_seg_build.
+ *   S_init, S_out, g_total, U_total   as for hypic_compose (no prefix states).
+ *   mode           HYPIC_BC_SEQUENTIAL or HYPIC_BC_PIPELINED.
+ *   workspace      device scratch of at least
+ *                  hypic_seg_build_compose_workspace_size() bytes for `mode`
+ *                  (NULL allowed when that is 0): the build's workspace, then
+ *                  the composition's (sequential) or each group's pair
+ *                  (pipelined).  Contents ignored on entry, undefined on exit.
+ * The pairs equal those of hypic_seg_build; S_out, g_total and U_total equal
+ * those of hypic_compose up to the rounding of the grouping.
+ * Errors as for hypic_seg_build and hypic_compose.
+ */
+enum { HYPIC_BC_SEQUENTIAL = 0, HYPIC_BC_PIPELINED = 1 };
+hypic_status hypic_seg_build_compose(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain,
+                                     int d_k, int d_v, const hypic_tokens* in, const hypic_pairs* out,
+                                     const float* S_init, float* S_out, float* g_total, float* U_total, int mode,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* hypic_seg_build_compose_workspace_size -- bytes of workspace that call needs
+ * for the schedule `mode` (other arguments as for
+ * hypic_seg_build_workspace_size; may be 0 in the sequential mode); enqueues
+ * nothing. */
+hypic_status hypic_seg_build_compose_workspace_size(hypic_family fam, int n_seg, const int32_t* seg_offsets,
+                                                    int n_chain, int d_k, int d_v, hypic_dtype dtype, int mode,
+                                                    size_t* bytes);
 
 /*
  * hypic_compose_workspace_size -- bytes of workspace that enable the blocked

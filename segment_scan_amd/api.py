@@ -61,6 +61,10 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.c_size_t, P]
         lib.hypic_seg_build_workspace_size.argtypes = [I, I, P, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.hypic_compose.argtypes = [I, I, I, I, I, ctypes.POINTER(Pairs), P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.hypic_seg_build_compose.argtypes = [I, I, P, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P,
+                                                P, P, P, I, P, ctypes.c_size_t, P]
+        lib.hypic_seg_build_compose_workspace_size.argtypes = [I, I, P, I, I, I, I, I,
+                                                               ctypes.POINTER(ctypes.c_size_t)]
         lib.hypic_compose_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.hypic_seam_step.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Tokens), ctypes.POINTER(Pairs), P, P,
                                         ctypes.POINTER(Pairs), P, ctypes.c_size_t, P]
@@ -70,7 +74,8 @@ def load_library(path: str = LIB_PATH):
         lib.hypic_rerotate.argtypes = [I, I, I, I, I, P, ctypes.c_double, ctypes.POINTER(Pairs), P]
         for f in (lib.hypic_seg_build, lib.hypic_seg_build_workspace_size, lib.hypic_compose,
                   lib.hypic_compose_workspace_size, lib.hypic_seam_step, lib.hypic_seam_step_workspace_size,
-                  lib.hypic_seam_step_noalloc, lib.hypic_rerotate):
+                  lib.hypic_seam_step_noalloc, lib.hypic_rerotate, lib.hypic_seg_build_compose,
+                  lib.hypic_seg_build_compose_workspace_size):
             f.restype = I
         lib.hypic_last_error.restype = ctypes.c_char_p
         lib.hypic_last_error.argtypes = []
@@ -214,6 +219,66 @@ def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor
     _check(load_library().hypic_seg_build(fam, n_seg, off, n_chain, d, v.shape[2], ctypes.byref(tk),
                                           ctypes.byref(pr), _ptr(workspace), ws_bytes, _stream(stream)))
     return g, U, S
+
+
+BC_SEQUENTIAL, BC_PIPELINED = 0, 1  # schedules of seg_build_compose
+
+
+def seg_build_compose_workspace_size(fam: int, offsets: Sequence[int], n_chain: int, d: int,
+                                     dtype: torch.dtype, mode: int = BC_SEQUENTIAL) -> int:
+    """Bytes of device workspace seg_build_compose needs for this batch and schedule."""
+    out = ctypes.c_size_t(0)
+    code = HYPIC_F32 if dtype == torch.float32 else HYPIC_BF16
+    _check(load_library().hypic_seg_build_compose_workspace_size(fam, len(offsets) - 1, _offsets(offsets), n_chain,
+                                                                 d, d, code, int(mode), ctypes.byref(out)))
+    return out.value
+
+
+def seg_build_compose(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor, beta=None,
+                      log_gate=None, gate_per_chain: bool = False, out=None, S_init=None, S_out=None,
+                      g_total=None, U_total=None, want_total: bool = False, mode: int = BC_SEQUENTIAL,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Build every (segment, chain) pair and compose each chain's pairs in order
+    (hypic_seg_build_compose).  Returns (g, U or None, S) and a dict with S_out,
+    g_tot, U_tot; `out` may pass preallocated (g, U, S), `workspace` a uint8
+    device buffer of at least seg_build_compose_workspace_size() bytes."""
+    off = _offsets(offsets)
+    n_seg = len(offsets) - 1
+    if k.dim() != 3:
+        raise ValueError("k must be [n_tok, n_chain, d] (got shape %s)" % (tuple(k.shape),))
+    n_tok, n_chain, d = k.shape
+    if n_seg < 1 or int(offsets[-1]) > n_tok:
+        raise ValueError("offsets must end within k.shape[0] = %d (got %s)" % (n_tok, int(offsets[-1])))
+    _check_token_shapes(fam, n_tok, n_chain, d, k, v, None, beta, log_gate, gate_per_chain)
+    if out is not None:
+        _check_pair_shapes(fam, "out", n_seg, n_chain, d, *out)
+    _want("S_init", S_init, (n_chain, d, d))
+    _want("S_out", S_out, (n_chain, d, d))
+    _want("g_total", g_total, _gate_shape(fam, (n_chain,), d))
+    _want("U_total", U_total, (n_chain, d, d))
+    dev = k.device
+    if out is None:
+        out = (torch.empty(_gate_shape(fam, (n_seg, n_chain), d), device=dev, dtype=torch.float32),
+               torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32) if fam in DENSE else None,
+               torch.empty((n_seg, n_chain, d, d), device=dev, dtype=torch.float32))
+    g, U, S = out
+    if S_out is None:
+        S_out = torch.empty((n_chain, d, d), device=dev, dtype=torch.float32)
+    if want_total and g_total is None:
+        g_total = torch.empty(_gate_shape(fam, (n_chain,), d), device=dev, dtype=torch.float32)
+    if want_total and fam in DENSE and U_total is None:
+        U_total = torch.empty((n_chain, d, d), device=dev, dtype=torch.float32)
+    if workspace is None:
+        need = seg_build_compose_workspace_size(fam, offsets, n_chain, d, k.dtype, mode)
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    tk = _tokens(k, v, None, beta, log_gate, gate_per_chain)
+    pr = Pairs(_ptr(g), _ptr(U), _ptr(S))
+    _check(load_library().hypic_seg_build_compose(fam, n_seg, off, n_chain, d, v.shape[2], ctypes.byref(tk),
+                                                  ctypes.byref(pr), _ptr(S_init), _ptr(S_out), _ptr(g_total),
+                                                  _ptr(U_total), int(mode), _ptr(workspace), ws_bytes,
+                                                  _stream(stream)))
+    return g, U, S, {"S_out": S_out, "g_tot": g_total, "U_tot": U_total}
 
 
 def compose_workspace_size(fam: int, n_seg: int, n_chain: int, d: int, want_prefix: bool = False) -> int:

@@ -221,6 +221,162 @@ size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_cha
   return P > 1 ? piece_bytes(fam, n_seg, P, n_chain, d) : 0;
 }
 
+// Launches the build of segments [s0, s1) of a validated batch (global segment
+// indices; outputs at their places in `out`), over a workspace of at least
+// build_workspace() bytes for those segments.
+hypic_status build_range(int fam, int n_seg, const int32_t* seg_offsets, int s0, int s1, int n_chain, int d,
+                         bool f32, const hypic_tokens* in, const hypic_pairs* out, void* workspace,
+                         hipStream_t stream) {
+  (void)n_seg;
+  hypic::BuildArgs a;
+  a.k = in->k;
+  a.v = in->v;
+  a.beta = in->beta;
+  a.lg = in->log_gate;
+  a.g = out->g;
+  a.U = out->U;
+  a.S = out->S;
+  a.n_chain = n_chain;
+  a.gate_per_chain = in->gate_per_chain ? 1 : 0;
+  const int ns_all = s1 - s0;
+  const int32_t* offs = seg_offsets + s0;  // offsets of the range (absolute token positions)
+  const int P = piece_count(fam, ns_all, offs, n_chain);
+  if (P > 1) {
+    // build the pieces into the workspace, then compose each segment's pieces
+    std::vector<int32_t> poff((size_t)ns_all * P + 1);
+    for (int s = 0; s < ns_all; ++s) {
+      const int nc = (offs[s + 1] - offs[s] + 63) / 64;
+      for (int p = 0; p < P; ++p) poff[(size_t)s * P + p] = offs[s] + 64 * (int)((long)p * nc / P);
+    }
+    poff[(size_t)ns_all * P] = offs[ns_all];
+    const size_t n_pairs = (size_t)ns_all * P * n_chain;
+    float* pg = reinterpret_cast<float*>(workspace);
+    float* pS = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) +
+                                         ((n_pairs * gate_len(fam, d) * 4 + 255) & ~(size_t)255));
+    a.g = pg;
+    a.S = pS;
+    const int n_piece = ns_all * P;
+    for (int q0 = 0; q0 < n_piece; q0 += hypic::kMaxSegPerLaunch) {
+      const int ns = std::min(hypic::kMaxSegPerLaunch, n_piece - q0);
+      fill_seg_table(&a.seg, poff.data(), q0, ns);
+      hipError_t e = hypic::launch_build_sd(fam, d, f32, a, ns * n_chain, stream);
+      if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
+    }
+    hypic::ComposeArgs c{};
+    c.g = pg;
+    c.S = pS;
+    c.S_out = out->S + (size_t)s0 * n_chain * d * d;
+    c.g_tot = out->g + (size_t)s0 * n_chain * gate_len(fam, d);
+    c.n_seg = P;
+    c.n_chain = n_chain;
+    c.n_out = ns_all * n_chain;
+    hipError_t e = hypic::launch_compose_elem(fam, d, c, stream);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build piece composition launch");
+    return HYPIC_OK;
+  }
+  for (int q0 = s0; q0 < s1; q0 += hypic::kMaxSegPerLaunch) {
+    const int ns = std::min(hypic::kMaxSegPerLaunch, s1 - q0);
+    fill_seg_table(&a.seg, seg_offsets, q0, ns);
+    const int blocks = ns * n_chain;
+    hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, workspace, stream)
+                   : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, a, blocks, workspace, stream)
+                                        : hypic::launch_build_sd(fam, d, f32, a, blocks, stream);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
+  }
+  return HYPIC_OK;
+}
+
+// ---- the cold request in one call: groups of segments built on the caller's
+// stream, each group composed on a second stream while the next is built ------
+
+// Segments per group: enough (segment, chain) units to fill the GPU once
+// (two workgroups per CU of 256), at most kMaxGroups groups.
+constexpr int kMaxGroups = 32;
+#ifndef HYPIC_GROUP_UNITS
+#define HYPIC_GROUP_UNITS 512
+#endif
+int group_len(int n_seg, int n_chain) {
+  int len = std::max(1, (HYPIC_GROUP_UNITS + n_chain - 1) / n_chain);
+  if ((n_seg + len - 1) / len > kMaxGroups) len = (n_seg + kMaxGroups - 1) / kMaxGroups;
+  return len;
+}
+
+struct FusedLayout {
+  int glen, n_grp;
+  size_t build_ws, g_off, U_off, S_off, total;
+};
+
+// Sequential mode: one group (the whole batch), and the blocked composition's
+// workspace after the build's.  Pipelined mode: groups, each group's pair.
+FusedLayout fused_layout(int fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32, int mode) {
+  FusedLayout L;
+  if (mode == HYPIC_BC_SEQUENTIAL) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    L.glen = n_seg;
+    L.n_grp = 1;
+    L.build_ws = build_workspace(fam, n_seg, seg_offsets, n_chain, d, f32);
+    L.g_off = L.U_off = L.S_off = up(L.build_ws);
+    L.total = L.g_off + (dense(fam) ? hypic::compose_workspace_bytes(d, n_seg, n_chain, false) : 0);
+    return L;
+  }
+  L.glen = group_len(n_seg, n_chain);
+  L.n_grp = (n_seg + L.glen - 1) / L.glen;
+  L.build_ws = 0;
+  for (int s0 = 0; s0 < n_seg; s0 += L.glen) {
+    const int ns = std::min(L.glen, n_seg - s0);
+    L.build_ws = std::max(L.build_ws, build_workspace(fam, ns, seg_offsets + s0, n_chain, d, f32));
+  }
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t units = (size_t)L.n_grp * n_chain;
+  L.g_off = up(L.build_ws);
+  L.U_off = L.g_off + up(units * gate_len(fam, d) * 4);
+  L.S_off = L.U_off + (dense(fam) ? up(units * d * d * 4) : 0);
+  L.total = L.S_off + units * d * d * 4;
+  return L;
+}
+
+// The second stream and the events of the calling host thread on the current
+// device, created on first use and kept (default priority, non-blocking).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[kMaxGroups + 1] = {};
+};
+hipError_t side_stream(SideStream** out) {
+  static thread_local SideStream per_dev[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = per_dev[dev];
+  if (!ss.s) {
+    e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    for (auto& ev : ss.ev) {
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
+// Ordered composition of n pairs per chain (flat single pass, no workspace).
+hipError_t compose_range(int fam, int d, const float* g, const float* U, const float* S, int n, int n_chain,
+                         const float* S_init, float* S_out, float* g_tot, float* U_tot, hipStream_t st) {
+  hypic::ComposeArgs c{};
+  c.g = g;
+  c.U = U;
+  c.S = S;
+  c.S_init = S_init;
+  c.S_out = S_out;
+  c.g_tot = g_tot;
+  c.U_tot = U_tot;
+  c.n_seg = n;
+  c.n_chain = n_chain;
+  c.n_out = n_chain;
+  return dense(fam) ? hypic::launch_compose_chain(d, c, nullptr, 0, st) : hypic::launch_compose_elem(fam, d, c, st);
+}
+
 }  // namespace
 
 hypic_status hypic::report_error(hypic_status st, const char* fmt, ...) {
@@ -283,59 +439,120 @@ hypic_status hypic_seg_build(hypic_family fam, int n_seg, const int32_t* seg_off
   }
   TRY(check_overlaps(ins, outs));
 
-  hypic::BuildArgs a;
-  a.k = in->k;
-  a.v = in->v;
-  a.beta = in->beta;
-  a.lg = in->log_gate;
-  a.g = out->g;
-  a.U = out->U;
-  a.S = out->S;
-  a.n_chain = n_chain;
-  a.gate_per_chain = in->gate_per_chain ? 1 : 0;
-  const int P = piece_count(fam, n_seg, seg_offsets, n_chain);
-  if (P > 1) {
-    // build the pieces into the workspace, then compose each segment's pieces
-    std::vector<int32_t> poff((size_t)n_seg * P + 1);
-    for (int s = 0; s < n_seg; ++s) {
-      const int nc = (seg_offsets[s + 1] - seg_offsets[s] + 63) / 64;
-      for (int p = 0; p < P; ++p) poff[(size_t)s * P + p] = seg_offsets[s] + 64 * (int)((long)p * nc / P);
-    }
-    poff[(size_t)n_seg * P] = seg_offsets[n_seg];
-    const size_t n_pairs = (size_t)n_seg * P * n_chain;
-    float* pg = reinterpret_cast<float*>(workspace);
-    float* pS = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) +
-                                         ((n_pairs * gate_len(fam, d) * 4 + 255) & ~(size_t)255));
-    a.g = pg;
-    a.S = pS;
-    const int n_piece = n_seg * P;
-    for (int s0 = 0; s0 < n_piece; s0 += hypic::kMaxSegPerLaunch) {
-      const int ns = std::min(hypic::kMaxSegPerLaunch, n_piece - s0);
-      fill_seg_table(&a.seg, poff.data(), s0, ns);
-      hipError_t e = hypic::launch_build_sd(fam, d, f32, a, ns * n_chain, (hipStream_t)stream);
-      if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
-    }
+  hypic_status st = build_range(fam, n_seg, seg_offsets, 0, n_seg, n_chain, d, f32, in, out, workspace,
+                                (hipStream_t)stream);
+  if (st != HYPIC_OK) return st;
+  return ok();
+}
+
+hypic_status hypic_seg_build_compose_workspace_size(hypic_family fam, int n_seg, const int32_t* seg_offsets,
+                                                    int n_chain, int d_k, int d_v, hypic_dtype dtype, int mode,
+                                                    size_t* bytes) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  TRY(check_offsets(n_seg, seg_offsets));
+  if (dtype != HYPIC_F32 && dtype != HYPIC_BF16) return fail(HYPIC_E_INVALID, "unknown dtype %d", (int)dtype);
+  if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
+  if (mode != HYPIC_BC_SEQUENTIAL && mode != HYPIC_BC_PIPELINED) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
+  *bytes = fused_layout(fam, n_seg, seg_offsets, n_chain, d_k, dtype == HYPIC_F32, mode).total;
+  return ok();
+}
+
+hypic_status hypic_seg_build_compose(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d_k,
+                                     int d_v, const hypic_tokens* in, const hypic_pairs* out, const float* S_init,
+                                     float* S_out, float* g_total, float* U_total, int mode, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
+  if (mode != HYPIC_BC_SEQUENTIAL && mode != HYPIC_BC_PIPELINED) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
+  const int d = d_k;
+  TRY(check_offsets(n_seg, seg_offsets));
+  const size_t n_tok = (size_t)seg_offsets[n_seg];
+  std::vector<Range> ins, outs;
+  TRY(check_tokens(fam, in, n_tok, n_chain, d, false, &ins));
+  if (!out) return fail(HYPIC_E_INVALID, "out is NULL");
+  if (!out->S) return fail(HYPIC_E_INVALID, "out.S is NULL");
+  if (!out->g) return fail(HYPIC_E_INVALID, "out.g is NULL");
+  if (dense(fam) && !out->U) return fail(HYPIC_E_INVALID, "out.U is required for the delta and KDA families");
+  if (!dense(fam) && out->U) return fail(HYPIC_E_INVALID, "out.U is only defined for the delta and KDA families");
+  if (!S_out) return fail(HYPIC_E_INVALID, "S_out is NULL");
+  if (U_total && !dense(fam)) return fail(HYPIC_E_INVALID, "U_total is only defined for the delta and KDA families");
+  TRY(check_aligned(out->S, "out.S"));
+  TRY(check_aligned(out->g, "out.g"));
+  if (out->U) TRY(check_aligned(out->U, "out.U"));
+  TRY(check_aligned(S_out, "S_out"));
+  if (S_init) TRY(check_aligned(S_init, "S_init"));
+  if (g_total) TRY(check_aligned(g_total, "g_total"));
+  if (U_total) TRY(check_aligned(U_total, "U_total"));
+  const bool f32 = in->dtype == HYPIC_F32;
+  if (fam == HYPIC_KDA && !hypic::kda_build_supported(d, f32))
+    return fail(HYPIC_E_UNSUPPORTED, "the KDA build is built for d = 64 and for d = 128 with bf16 tokens");
+  const size_t units = (size_t)n_seg * n_chain;
+  const size_t sbytes = (size_t)n_chain * d * d * 4;
+  outs.push_back({out->S, units * d * d * 4, "out.S"});
+  outs.push_back({out->g, units * gate_len(fam, d) * 4, "out.g"});
+  if (out->U) outs.push_back({out->U, units * d * d * 4, "out.U"});
+  if (S_init && S_init != S_out) ins.push_back({S_init, sbytes, "S_init"});
+  outs.push_back({S_out, sbytes, "S_out"});
+  if (g_total) outs.push_back({g_total, (size_t)n_chain * gate_len(fam, d) * 4, "g_total"});
+  if (U_total) outs.push_back({U_total, sbytes, "U_total"});
+  const FusedLayout L = fused_layout(fam, n_seg, seg_offsets, n_chain, d, f32, mode);
+  if (L.total > 0 && !workspace) return fail(HYPIC_E_INVALID, "workspace is NULL (%zu bytes required)", L.total);
+  if (workspace_bytes < L.total)
+    return fail(HYPIC_E_INVALID, "workspace too small: %zu bytes given, %zu required", workspace_bytes, L.total);
+  if (L.total > 0) {
+    TRY(check_aligned(workspace, "workspace"));
+    outs.push_back({workspace, L.total, "workspace"});
+  }
+  TRY(check_overlaps(ins, outs));
+
+  hipStream_t sa = (hipStream_t)stream;
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  float* gg = reinterpret_cast<float*>(ws + L.g_off);
+  float* gU = dense(fam) ? reinterpret_cast<float*>(ws + L.U_off) : nullptr;
+  float* gS = reinterpret_cast<float*>(ws + L.S_off);
+  const size_t gl = gate_len(fam, d);
+  if (L.n_grp == 1) {  // build, then compose (blocked schedule when it applies), on the caller's stream
+    TRY(build_range(fam, n_seg, seg_offsets, 0, n_seg, n_chain, d, f32, in, out, workspace, sa));
     hypic::ComposeArgs c{};
-    c.g = pg;
-    c.S = pS;
-    c.S_out = out->S;
-    c.g_tot = out->g;
-    c.n_seg = P;
+    c.g = out->g;
+    c.U = out->U;
+    c.S = out->S;
+    c.S_init = S_init;
+    c.S_out = S_out;
+    c.g_tot = g_total;
+    c.U_tot = U_total;
+    c.n_seg = n_seg;
     c.n_chain = n_chain;
-    c.n_out = n_seg * n_chain;
-    hipError_t e = hypic::launch_compose_elem(fam, d, c, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build piece composition launch");
+    c.n_out = n_chain;
+    const size_t cws = mode == HYPIC_BC_SEQUENTIAL ? L.total - L.g_off : 0;
+    hipError_t e = dense(fam) ? hypic::launch_compose_chain(d, c, cws ? ws + L.g_off : nullptr, cws, sa)
+                              : hypic::launch_compose_elem(fam, d, c, sa);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build_compose composition launch");
     return ok();
   }
-  for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
-    const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
-    fill_seg_table(&a.seg, seg_offsets, s0, ns);
-    const int blocks = ns * n_chain;
-    hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, workspace, (hipStream_t)stream)
-                   : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, a, blocks, workspace, (hipStream_t)stream)
-                                        : hypic::launch_build_sd(fam, d, f32, a, blocks, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
+  SideStream* side = nullptr;
+  hipError_t e = side_stream(&side);
+  if (e != hipSuccess) return hip_fail(e, "hypic_seg_build_compose second stream");
+  for (int gi = 0; gi < L.n_grp; ++gi) {
+    const int s0 = gi * L.glen, s1 = std::min(n_seg, s0 + L.glen);
+    // group gi built on the caller's stream (in stream order after group gi - 1)
+    TRY(build_range(fam, n_seg, seg_offsets, s0, s1, n_chain, d, f32, in, out, workspace, sa));
+    e = hipEventRecord(side->ev[gi], sa);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->ev[gi], 0);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build_compose event");
+    // ... and composed into one pair per chain on the second stream, while the
+    // caller's stream builds the next group
+    const size_t p0 = (size_t)s0 * n_chain;
+    e = compose_range(fam, d, out->g + p0 * gl, out->U ? out->U + p0 * d * d : nullptr, out->S + p0 * d * d,
+                      s1 - s0, n_chain, nullptr, gS + (size_t)gi * n_chain * d * d, gg + (size_t)gi * n_chain * gl,
+                      gU ? gU + (size_t)gi * n_chain * d * d : nullptr, side->s);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build_compose group composition launch");
   }
+  // join: the group pairs composed in order on the caller's stream
+  e = hipEventRecord(side->ev[kMaxGroups], side->s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(sa, side->ev[kMaxGroups], 0);
+  if (e != hipSuccess) return hip_fail(e, "hypic_seg_build_compose event");
+  e = compose_range(fam, d, gg, gU, gS, L.n_grp, n_chain, S_init, S_out, g_total, U_total, sa);
+  if (e != hipSuccess) return hip_fail(e, "hypic_seg_build_compose final composition launch");
   return ok();
 }
 

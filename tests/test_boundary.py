@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert declared <= exported, declared - exported
     for name in declared:
         getattr(lib, name)
-    assert lib.hypic_abi_version() == 7
+    assert lib.hypic_abi_version() == 8
 
 
 def toks(fam, dtype=BF16, q=False, beta=None, lg=None, gate_per_chain=0):
@@ -351,3 +351,24 @@ def test_seam_noalloc_rejects_more_records_than_its_scratch(lib):
     need = ctypes.c_size_t(0)
     assert lib.hypic_seam_step_workspace_size(DELTA, 113, 8, 1024, 128, 128, ctypes.byref(need)) == 0
     assert need.value <= api.NOALLOC_SCRATCH_BYTES  # the largest warm-request-like call that still fits
+
+
+def test_build_compose_requires_its_workspace(lib):
+    """hypic_seg_build_compose refuses a missing or short workspace before any HIP call."""
+    off = (ctypes.c_int32 * 3)(0, 64, 128)
+    t = toks(DELTA)
+    p = pairs(DELTA)
+    need = ctypes.c_size_t(0)
+    for mode in (0, 1):
+        assert lib.hypic_seg_build_compose_workspace_size(DELTA, 2, off, 2, 128, 128, BF16, mode,
+                                                          ctypes.byref(need)) == 0
+        assert need.value > 0
+        st = lib.hypic_seg_build_compose(DELTA, 2, off, 2, 128, 128, ctypes.byref(t), ctypes.byref(p), None,
+                                         A["Sout"], None, None, mode, None, 0, None)
+        assert st == INVALID and "workspace is NULL" in api.last_error()
+        st = lib.hypic_seg_build_compose(DELTA, 2, off, 2, 128, 128, ctypes.byref(t), ctypes.byref(p), None,
+                                         A["Sout"], None, None, mode, A["ws"], need.value - 256, None)
+        assert st == INVALID and "too small" in api.last_error()
+    st = lib.hypic_seg_build_compose(DELTA, 2, off, 2, 128, 128, ctypes.byref(t), ctypes.byref(p), None,
+                                     A["Sout"], None, None, 7, A["ws"], WS_BYTES, None)
+    assert st == INVALID and "mode" in api.last_error()
