@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <numeric>
 #include <string>
 #include <vector>
 
@@ -156,41 +157,52 @@ hypic_status check_offsets(int n_seg, const int32_t* seg_offsets) {
   return HYPIC_OK;
 }
 
-// Fills the launch table of segments [s0, s0 + ns), with the longest-first
-// workgroup order [youleyou, segment-parallelism paragraph: LPT scheduling of
-// uneven segments].
-void fill_seg_table(hypic::SegTable* t, const int32_t* seg_offsets, int s0, int ns) {
-  t->n_seg = ns;
-  t->seg_base = s0;
-  for (int i = 0; i <= ns; ++i) t->off[i] = seg_offsets[s0 + i];
-  int idx[hypic::kMaxSegPerLaunch];
-  for (int i = 0; i < ns; ++i) idx[i] = i;
-  std::stable_sort(idx, idx + ns, [&](int x, int y) {
-    return t->off[x + 1] - t->off[x] > t->off[y + 1] - t->off[y];
-  });
-  for (int i = 0; i < ns; ++i) t->order[i] = (uint8_t)idx[i];
+// Launch plan of the build of segments [s0, s1) (segment s spans tokens
+// [off[s], off[s + 1]); its output row is s) [youleyou, segment-parallelism
+// paragraph: LPT scheduling of uneven segments]: the segments sorted by length,
+// longest first (ties by index), and cut into launches of kMaxSegPerLaunch
+// consecutive entries of that order.  The longest segments of the whole range
+// start first, in the first launch, and the shortest end the last one.
+std::vector<hypic::SegTable> plan_launches(const int32_t* off, int s0, int s1) {
+  const int n = s1 - s0;
+  std::vector<int> idx(n);
+  std::iota(idx.begin(), idx.end(), s0);
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](int x, int y) { return off[x + 1] - off[x] > off[y + 1] - off[y]; });
+  constexpr int K = hypic::kMaxSegPerLaunch;
+  std::vector<hypic::SegTable> plan((n + K - 1) / K);
+  for (size_t l = 0; l < plan.size(); ++l) {
+    hypic::SegTable& t = plan[l];
+    const int q0 = (int)l * K, ns = std::min(K, n - q0);
+    const int first = idx[q0], len0 = off[first + 1] - off[first];
+    bool contiguous = true;
+    for (int i = 0; i < ns; ++i) {
+      const int sg = idx[q0 + i];
+      t.beg[i] = off[sg];
+      t.end[i] = off[sg + 1];
+      t.out[i] = sg;
+      contiguous = contiguous && sg == first + i && t.end[i] - t.beg[i] == len0;
+    }
+    t.n_seg = ns;
+    t.contiguous = contiguous ? 1 : 0;
+  }
+  return plan;
 }
 
 // Workspace of a delta build: the largest any of its launches needs (launches
 // run in stream order and reuse it).
 size_t delta_workspace(int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
   size_t need = 0;
-  hypic::SegTable t;
-  for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
-    fill_seg_table(&t, seg_offsets, s0, std::min(hypic::kMaxSegPerLaunch, n_seg - s0));
+  for (const hypic::SegTable& t : plan_launches(seg_offsets, 0, n_seg))
     need = std::max(need, hypic::build_delta_workspace(d, f32, t, n_chain));
-  }
   return need;
 }
 
 // The same for the KDA build's factor records.
 size_t kda_workspace(int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32) {
   size_t need = 0;
-  hypic::SegTable t;
-  for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
-    fill_seg_table(&t, seg_offsets, s0, std::min(hypic::kMaxSegPerLaunch, n_seg - s0));
+  for (const hypic::SegTable& t : plan_launches(seg_offsets, 0, n_seg))
     need = std::max(need, hypic::kda_workspace_bytes(d, f32, t, n_chain));
-  }
   return need;
 }
 
@@ -255,11 +267,9 @@ hypic_status build_range(int fam, int n_seg, const int32_t* seg_offsets, int s0,
                                          ((n_pairs * gate_len(fam, d) * 4 + 255) & ~(size_t)255));
     a.g = pg;
     a.S = pS;
-    const int n_piece = ns_all * P;
-    for (int q0 = 0; q0 < n_piece; q0 += hypic::kMaxSegPerLaunch) {
-      const int ns = std::min(hypic::kMaxSegPerLaunch, n_piece - q0);
-      fill_seg_table(&a.seg, poff.data(), q0, ns);
-      hipError_t e = hypic::launch_build_sd(fam, d, f32, a, ns * n_chain, stream);
+    for (const hypic::SegTable& t : plan_launches(poff.data(), 0, ns_all * P)) {
+      a.seg = t;
+      hipError_t e = hypic::launch_build_sd(fam, d, f32, a, t.n_seg * n_chain, stream);
       if (e != hipSuccess) return hip_fail(e, "hypic_seg_build launch");
     }
     hypic::ComposeArgs c{};
@@ -274,10 +284,9 @@ hypic_status build_range(int fam, int n_seg, const int32_t* seg_offsets, int s0,
     if (e != hipSuccess) return hip_fail(e, "hypic_seg_build piece composition launch");
     return HYPIC_OK;
   }
-  for (int q0 = s0; q0 < s1; q0 += hypic::kMaxSegPerLaunch) {
-    const int ns = std::min(hypic::kMaxSegPerLaunch, s1 - q0);
-    fill_seg_table(&a.seg, seg_offsets, q0, ns);
-    const int blocks = ns * n_chain;
+  for (const hypic::SegTable& t : plan_launches(seg_offsets, s0, s1)) {
+    a.seg = t;
+    const int blocks = t.n_seg * n_chain;
     hipError_t e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta(d, f32, a, blocks, workspace, stream)
                    : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, a, blocks, workspace, stream)
                                         : hypic::launch_build_sd(fam, d, f32, a, blocks, stream);
@@ -718,9 +727,9 @@ hypic_status hypic_seam_step(hypic_family fam, int n_seg, int w, int n_chain, in
     b.gate_per_chain = seam->gate_per_chain ? 1 : 0;
     std::vector<int32_t> woff((size_t)n_seg + 1);
     for (int i = 0; i <= n_seg; ++i) woff[i] = i * w;
-    for (int s0 = 0; s0 < n_seg; s0 += hypic::kMaxSegPerLaunch) {
-      const int ns = std::min(hypic::kMaxSegPerLaunch, n_seg - s0);
-      fill_seg_table(&b.seg, woff.data(), s0, ns);
+    for (const hypic::SegTable& t : plan_launches(woff.data(), 0, n_seg)) {
+      b.seg = t;
+      const int ns = t.n_seg;
       e = (fam == HYPIC_DELTA) ? hypic::launch_build_delta_single(d, f32, b, ns * n_chain, (hipStream_t)stream)
           : (fam == HYPIC_KDA) ? hypic::launch_build_kda(d, f32, b, ns * n_chain, nullptr, (hipStream_t)stream)
                                : hypic::launch_build_sd(fam, d, f32, b, ns * n_chain, (hipStream_t)stream);

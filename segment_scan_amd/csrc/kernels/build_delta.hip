@@ -96,11 +96,11 @@ __global__ __launch_bounds__(256, (IN_F32 ? 1 : 2)) void build_delta_kernel(cons
   const int lane0 = lane_id();
   const int wave = wave_id();
   const int n_chain = a.n_chain;
-  const int s_local = a.seg.order[blockIdx.x / n_chain];  // longest segments first
+  const int slot = blockIdx.x / n_chain;  // longest segments first
   const int chain = blockIdx.x % n_chain;
-  const int t_begin = a.seg.off[s_local];
-  const int t_end = a.seg.off[s_local + 1];
-  const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + chain;
+  const int t_begin = a.seg.beg[slot];
+  const int t_end = a.seg.end[slot];
+  const size_t unit = (size_t)a.seg.out[slot] * n_chain + chain;
   const bool s_wave = wave >= 2;
   const int col0 = (wave & 1) * CPW;  // first state column of this wave (within U or S)
 
@@ -413,7 +413,7 @@ namespace {
 bool use_delta2(int d, bool in_f32, const SegTable& seg) {
   if (d != 128 || in_f32) return false;
   for (int s = 0; s < seg.n_seg; ++s)
-    if (seg.off[s + 1] - seg.off[s] > kDelta2MaxSegLen) return false;
+    if (seg_len(seg, s) > kDelta2MaxSegLen) return false;
   return true;
 }
 }  // namespace

@@ -94,8 +94,8 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
     const int mid = (lo + hi) >> 1;
     if (cks.base[mid] <= gchunk) lo = mid; else hi = mid;
   }
-  const int c0 = a.seg.off[lo] + (gchunk - cks.base[lo]) * C;
-  const int nv = min(C, a.seg.off[lo + 1] - c0);
+  const int c0 = a.seg.beg[lo] + (gchunk - cks.base[lo]) * C;
+  const int nv = min(C, a.seg.end[lo] - c0);
   const int lane = threadIdx.x;
   const int h = lane >> 5, l32 = lane & 31;
 
@@ -283,11 +283,11 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
   const bool s_wave = wave >= 4;
   const int col0 = (wave & 3) * 32;
   const int n_chain = a.n_chain;
-  const int s_local = a.seg.order[blockIdx.x / n_chain];  // longest segments first
+  const int s_local = blockIdx.x / n_chain;  // slot: longest segments first
   const int chain = blockIdx.x % n_chain;
-  const int t_begin = a.seg.off[s_local], t_end = a.seg.off[s_local + 1];
+  const int t_begin = a.seg.beg[s_local], t_end = a.seg.end[s_local];
   const int n_ck = (t_end - t_begin + C - 1) / C;
-  const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + chain;
+  const size_t unit = (size_t)a.seg.out[s_local] * n_chain + chain;
 
   f32x16 Z[4];
   {

@@ -413,8 +413,8 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
   __syncthreads();
 }
 
-// ORDERED: workgroup rows follow the launch's longest-first order (ragged
-// launches only; equal lengths use the index order without the lookup).
+// ORDERED: workgroup rows read their segment from the launch's slot table
+// (ragged launches); a contiguous launch of equal lengths computes it.
 template <int D, bool IN_F32, bool ORDERED>
 __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   using Cfg = KdaCfg<D, IN_F32>;
@@ -445,11 +445,12 @@ __global__ __launch_bounds__(256, 1) void build_kda_kernel(const BuildArgs a) {
   const int lane0 = lane_id();
   const int wave = wave_id();
   const int n_chain = a.n_chain;
-  const int s_local = ORDERED ? a.seg.order[blockIdx.x / n_chain] : (int)blockIdx.x / n_chain;
+  const int slot = (int)blockIdx.x / n_chain;
   const int chain = blockIdx.x % n_chain;
-  const int t_begin = a.seg.off[s_local];
-  const int t_end = a.seg.off[s_local + 1];
-  const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + chain;
+  const int len0 = a.seg.end[0] - a.seg.beg[0];
+  const int t_begin = ORDERED ? a.seg.beg[slot] : a.seg.beg[0] + slot * len0;
+  const int t_end = ORDERED ? a.seg.end[slot] : t_begin + len0;
+  const size_t unit = (size_t)(ORDERED ? a.seg.out[slot] : a.seg.out[0] + slot) * n_chain + chain;
   const bool s_wave = wave >= 2;
   const int col0 = (wave & 1) * CPW;
 
@@ -669,8 +670,8 @@ __global__ __launch_bounds__(256, 3) void kda_prep_kernel(const BuildArgs a, con
     const int mid = (lo + hi) >> 1;
     if (cks.base[mid] <= gchunk) lo = mid; else hi = mid;
   }
-  const int c0 = a.seg.off[lo] + (gchunk - cks.base[lo]) * C;
-  const int nv = min(C, a.seg.off[lo + 1] - c0);
+  const int c0 = a.seg.beg[lo] + (gchunk - cks.base[lo]) * C;
+  const int nv = min(C, a.seg.end[lo] - c0);
   const int tid = threadIdx.x;
   unsigned char* rec = ws + (size_t)blockIdx.x * KREC_BYTES;
 
@@ -757,7 +758,7 @@ namespace {
 bool use_two_pass(int d, bool in_f32, const SegTable& seg) {
   if (d != 128 || in_f32) return false;
   for (int s = 0; s < seg.n_seg; ++s)
-    if (seg.off[s + 1] - seg.off[s] > kDelta2MaxSegLen) return false;
+    if (seg_len(seg, s) > kDelta2MaxSegLen) return false;
   return true;
 }
 }  // namespace

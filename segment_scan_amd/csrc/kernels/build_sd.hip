@@ -33,18 +33,13 @@ struct Raw8 {
   uint4 w[IN_F32 ? 2 : 1];
 };
 
+// 8 consecutive elements at byte offset voff + soff of a buffer (zeros past its end).
 template <bool IN_F32>
-__device__ __forceinline__ Raw8<IN_F32> ldraw8(const void* base, size_t idx, bool valid) {
-  Raw8<IN_F32> r;
-  if constexpr (IN_F32) {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + idx);
-    r.w[0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
-    r.w[1] = valid ? p[1] : make_uint4(0, 0, 0, 0);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-    r.w[0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
-  }
-  return r;
+__device__ __forceinline__ Raw8<IN_F32> ldraw8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  Raw8<IN_F32> x;
+  x.w[0] = buffer_load16(r, voff, soff);
+  if constexpr (IN_F32) x.w[1] = buffer_load16(r, voff + 16, soff);
+  return x;
 }
 
 template <bool IN_F32>
@@ -63,14 +58,17 @@ __device__ __forceinline__ void cvt8(const Raw8<IN_F32>& r, float (&x)[8]) {
   }
 }
 
-// ORDERED: workgroup rows follow the launch's longest-first order (ragged
-// launches); launches of equal-length segments use the index order directly,
-// which keeps the table lookup (and the registers it costs this register-bound
+// ORDERED: workgroup rows read their segment from the launch's slot table
+// (ragged launches); a contiguous launch of equal lengths computes it, which
+// keeps the table lookup (and the registers it costs this register-bound
 // kernel) out of their code.
 // TOK: tokens per staging thread; the workgroup has 2 (C / TOK) (D / 8)
 // threads (half stage keys and gates, half values).
 #ifndef HYPIC_SD_WPE
 #define HYPIC_SD_WPE 2
+#endif
+#ifndef HYPIC_SD_SUB
+#define HYPIC_SD_SUB 4
 #endif
 template <int FAM, int D, bool IN_F32, bool ORDERED, int TOK>
 __global__ __launch_bounds__(2 * (C / TOK) * (D / 8)) __attribute__((amdgpu_waves_per_eu(HYPIC_SD_WPE)))
@@ -98,11 +96,12 @@ void build_sd_kernel(const BuildArgs a) {
   const int wave = wave_id();
   const int n_chain = a.n_chain;
   const int u_local = blockIdx.x;
-  const int s_local = ORDERED ? a.seg.order[u_local / n_chain] : u_local / n_chain;
+  const int slot = u_local / n_chain;
   const int h = u_local % n_chain;
-  const int t_begin = a.seg.off[s_local];
-  const int t_end = a.seg.off[s_local + 1];
-  const size_t unit = (size_t)(a.seg.seg_base + s_local) * n_chain + h;
+  const int len0 = a.seg.end[0] - a.seg.beg[0];
+  const int t_begin = ORDERED ? a.seg.beg[slot] : a.seg.beg[0] + slot * len0;
+  const int t_end = ORDERED ? a.seg.end[slot] : t_begin + len0;
+  const size_t unit = (size_t)(ORDERED ? a.seg.out[slot] : a.seg.out[0] + slot) * n_chain + h;
 
   f32x16 acc[TPW];
 #pragma unroll
@@ -110,35 +109,38 @@ void build_sd_kernel(const BuildArgs a) {
 
   double g_acc = 0.0;  // scalar: lane 0 of wave 0; diag: thread tid < D for channel tid
 
-  // staging role: the first half of the threads stage keys (and diagonal gates), the second values
-  const bool is_k = tid < NTHR / 2;
+  // staging role: the first half of the waves stage keys (and diagonal gates),
+  // the second values (a wave-uniform choice, so the source is a scalar base)
+  const bool is_k = wave_id_uniform() < NWAVE / 2;
   const bool is_v = !is_k;
   const int sid = is_k ? tid : tid - NTHR / 2;
   const int tb = sid % NTB;  // block of TOK tokens
   const int db = sid / NTB;  // 8-channel block
   const void* src = is_k ? a.k : a.v;
+  constexpr uint32_t ESZ = IN_F32 ? 4 : 2;
+  const uint32_t row_bytes = (uint32_t)n_chain * D * ESZ;  // one token of all chains
+  const uint32_t voff = (uint32_t)(tb * TOK) * row_bytes + db * 8 * ESZ;
 
   // raw inputs of the chunk being staged; the next chunk's are loaded while the
-  // matrix cores work on this one
+  // matrix cores work on this one.  Buffer loads over the chunk's valid rows:
+  // tokens past the segment's end read as zeros.
   Raw8<IN_F32> rx[TOK];
   Raw8<IN_F32> rg[TOK];
   float lg_scalar = 0.f;
   auto issue_loads = [&](int c0) {
     const int nv = min(C, t_end - c0);
+    const size_t row0 = ((size_t)c0 * n_chain + h) * D * ESZ;  // byte offset of token c0, chain h
+    const uint32_t bytes = (uint32_t)(nv - 1) * row_bytes + D * ESZ;
     {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const char*>(src) + row0, bytes);
 #pragma unroll
-      for (int r = 0; r < TOK; ++r) {
-        const int t = tb * TOK + r;
-        rx[r] = ldraw8<IN_F32>(src, ((size_t)(c0 + min(t, nv - 1)) * n_chain + h) * D + db * 8, t < nv);
-      }
+      for (int r = 0; r < TOK; ++r) rx[r] = ldraw8<IN_F32>(rs, voff, r * row_bytes);
     }
     if constexpr (DIAG) {
       if (is_k) {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const char*>(a.lg) + row0, bytes);
 #pragma unroll
-        for (int r = 0; r < TOK; ++r) {
-          const int t = tb * TOK + r;
-          rg[r] = ldraw8<IN_F32>(a.lg, ((size_t)(c0 + min(t, nv - 1)) * n_chain + h) * D + db * 8, t < nv);
-        }
+        for (int r = 0; r < TOK; ++r) rg[r] = ldraw8<IN_F32>(rs, voff, r * row_bytes);
       }
     }
     if constexpr (FAM == 1) {
@@ -214,60 +216,66 @@ void build_sd_kernel(const BuildArgs a) {
     }
 
     // ---- stage keys (decay-weighted, split) and values, transposed -------------
+    // in sub-blocks of SUB tokens (fewer live registers than the whole block)
     {
-      float x[TOK][8];  // [token r][channel c]
+      constexpr int SUB = TOK < HYPIC_SD_SUB ? TOK : HYPIC_SD_SUB;
       float run[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) run[c] = 0.f;
 #pragma unroll
-      for (int r = 0; r < TOK; ++r) {
-        cvt8<IN_F32>(rx[r], x[r]);
-        if (is_k && GATED) {
-          if constexpr (DIAG) {
-            float lgr[8];
-            cvt8<IN_F32>(rg[r], lgr);
+      for (int r0 = 0; r0 < TOK; r0 += SUB) {
+        float x[SUB][8];  // [token r][channel c]
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              run[c] += lgr[c];
-              x[r][c] *= __expf(tot[c] - (pre[c] + run[c]));
+        for (int r = 0; r < SUB; ++r) {
+          cvt8<IN_F32>(rx[r0 + r], x[r]);
+          if (is_k && GATED) {
+            if constexpr (DIAG) {
+              float lgr[8];
+              cvt8<IN_F32>(rg[r0 + r], lgr);
+#pragma unroll
+              for (int c = 0; c < 8; ++c) {
+                run[c] += lgr[c];
+                x[r][c] *= __expf(tot[c] - (pre[c] + run[c]));
+              }
+            } else {
+#pragma unroll
+              for (int c = 0; c < 8; ++c) x[r][c] *= sW[tb * TOK + r0 + r];
+            }
+          }
+        }
+        // column c of the sub-block = SUB tokens of channel db*8+c: part of one
+        // 16-byte LDS row chunk (chunk (tb TOK + r0) / 8 of the row)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float col[SUB];
+#pragma unroll
+          for (int r = 0; r < SUB; ++r) col[r] = x[r][c];
+          const int row = db * 8 + c;
+          const int t0 = tb * TOK + r0;
+          const int off = swz64(row, t0 / 8) + t0 % 8;
+          using SubV = __attribute__((__vector_size__(SUB * sizeof(__bf16)))) __bf16;
+          if (is_k) {
+#pragma unroll
+            for (int i = 0; i < NTK; ++i) {
+              SubV tv;
+#pragma unroll
+              for (int r = 0; r < SUB; ++r) {
+                tv[r] = (bf16_t)col[r];
+                if (i + 1 < NTK) col[r] -= (float)tv[r];
+              }
+              *reinterpret_cast<SubV*>(&sK[i][off]) = tv;
             }
           } else {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[r][c] *= sW[tb * TOK + r];
-          }
-        }
-      }
-      // column c of the block = TOK tokens of channel db*8+c -> TOK / 8 of one
-      // 16-byte LDS row chunk (chunk tb TOK / 8 of the row, TOK-element part tb % (8 / TOK))
+            for (int i = 0; i < NTV; ++i) {
+              SubV tv;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float col[TOK];
-#pragma unroll
-        for (int r = 0; r < TOK; ++r) col[r] = x[r][c];
-        const int row = db * 8 + c;
-        const int off = swz64(row, (tb * TOK) / 8) + TOK * (tb % (8 / TOK));
-        using TokV = __attribute__((__vector_size__(TOK * sizeof(__bf16)))) __bf16;
-        if (is_k) {
-#pragma unroll
-          for (int i = 0; i < NTK; ++i) {
-            TokV tv;
-#pragma unroll
-            for (int r = 0; r < TOK; ++r) {
-              tv[r] = (bf16_t)col[r];
-              if (i + 1 < NTK) col[r] -= (float)tv[r];
+              for (int r = 0; r < SUB; ++r) {
+                tv[r] = (bf16_t)col[r];
+                if (i + 1 < NTV) col[r] -= (float)tv[r];
+              }
+              *reinterpret_cast<SubV*>(&sV[i][off]) = tv;
             }
-            *reinterpret_cast<TokV*>(&sK[i][off]) = tv;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < NTV; ++i) {
-            TokV tv;
-#pragma unroll
-            for (int r = 0; r < TOK; ++r) {
-              tv[r] = (bf16_t)col[r];
-              if (i + 1 < NTV) col[r] -= (float)tv[r];
-            }
-            *reinterpret_cast<TokV*>(&sV[i][off]) = tv;
           }
         }
       }

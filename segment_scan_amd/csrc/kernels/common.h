@@ -50,6 +50,22 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave index as a wave-uniform (scalar) value, for branches and addresses
+// the compiler must know to be uniform.
+__device__ __forceinline__ int wave_id_uniform() { return __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6; }
+
+// Raw buffer resource over `bytes` bytes from `p` (gfx9 word 3: 32-bit data
+// format, no swizzle, no index stride).  A buffer load whose offset lies at or
+// past `bytes` returns zeros and touches no memory, so ragged tails need no
+// branch or clamp.  Offsets are 32-bit: voffset per lane plus soffset per wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Compiler-only fence: memory operations are not moved across it.  Used inside
 // unrolled MFMA loops to bound how far ahead LDS fragments are loaded (and so

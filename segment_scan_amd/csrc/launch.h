@@ -16,25 +16,24 @@ hypic_status report_error(hypic_status st, const char* fmt, ...);
 // value in the kernel arguments (no device-side table to allocate).
 constexpr int kMaxSegPerLaunch = 240;
 
+// Slot i of a launch (workgroup row i) builds the segment of tokens
+// [beg[i], end[i]) into output row out[i].  The host fills the slots in
+// longest-processing-time order over the whole batch: all segments sorted by
+// length, longest first (ties by index), launches taking consecutive runs of
+// that order -- so in a ragged batch the longest units start first, in the
+// first launch, and the short ones fill the tails.
 struct SegTable {
-  int32_t off[kMaxSegPerLaunch + 1];  // token offsets of this launch's segments
-  // Longest-processing-time order: workgroup row i of the launch builds segment
-  // order[i] (the segments sorted by length, longest first, ties by index), so
-  // that in a ragged batch the long units start first and the short ones fill
-  // the tail.
-  uint8_t order[kMaxSegPerLaunch];
-  int n_seg;     // segments in this launch
-  int seg_base;  // global index of the first one
+  int32_t beg[kMaxSegPerLaunch];
+  int32_t end[kMaxSegPerLaunch];
+  int32_t out[kMaxSegPerLaunch];
+  int n_seg;  // slots in this launch
+  // 1: equal lengths and consecutive segments (slot i is segment out[0] + i,
+  // tokens from beg[0] + i (end[0] - beg[0])), so kernels may skip the lookup
+  int contiguous;
 };
-static_assert(kMaxSegPerLaunch <= 256, "order entries are 8-bit");
 
-// True when every segment of the launch has the same length: the longest-first
-// order is then the index order and kernels may skip the table lookup.
-inline bool seg_uniform(const SegTable& t) {
-  for (int s = 1; s < t.n_seg; ++s)
-    if (t.off[s + 1] - t.off[s] != t.off[1] - t.off[0]) return false;
-  return true;
-}
+inline int seg_len(const SegTable& t, int s) { return t.end[s] - t.beg[s]; }
+inline bool seg_uniform(const SegTable& t) { return t.contiguous != 0; }
 
 struct BuildArgs {
   const void* k;
@@ -129,7 +128,7 @@ inline int chunk_table(const SegTable& seg, ChunkTable* ct) {
   int n = 0;
   for (int s = 0; s < seg.n_seg; ++s) {
     if (ct) ct->base[s] = n;
-    n += (seg.off[s + 1] - seg.off[s] + 63) / 64;
+    n += (seg_len(seg, s) + 63) / 64;
   }
   if (ct) ct->base[seg.n_seg] = n;
   return n;

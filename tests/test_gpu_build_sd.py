@@ -96,6 +96,19 @@ def test_many_segments_span_launches():
     _check_build(tk, "many_segs", synth.ragged_offsets(lengths))
 
 
+@pytest.mark.parametrize("kind", ["scalar", "gla"])
+def test_longest_first_across_launches(kind):
+    """260 ragged segments whose longest sit at the end of the batch: the
+    launches are cut from the batch's longest-first order (first launch the
+    240 longest, second the 20 shortest)."""
+    rng = np.random.default_rng(7)
+    lengths = [int(x) for x in rng.integers(1, 150, 250)] + [900 + 13 * i for i in range(10)]
+    n_tok = sum(lengths)
+    tk = (synth.mamba2_like(n_seg=1, L=n_tok, n_chain=2) if kind == "scalar"
+          else synth.gla(n_seg=1, L=n_tok, n_chain=2))
+    _check_build(tk, "lpt_" + kind, synth.ragged_offsets(lengths))
+
+
 # ----------------------------------------------------------------- compose
 
 

@@ -112,6 +112,17 @@ def test_gdn_many_ragged_segments_two_launches():
     check_build(tk, "gdn_300seg", synth.ragged_offsets(lengths))
 
 
+def test_gdn_longest_first_across_launches():
+    """250 segments, the two longest (2100 and 2400 tokens, beyond the two-kernel
+    path) at the end of the batch: sorted longest first over the whole batch, the
+    first launch holds them (and takes the single-kernel path) with the 238 next
+    longest, the second launch the 10 shortest (two-kernel path)."""
+    rng = np.random.default_rng(6)
+    lengths = [int(x) for x in rng.integers(1, 200, 248)] + [2100, 2400]
+    tk = synth.gdn_cold(n_seg=1, L=sum(lengths), n_chain=2, gate_scale=1.0 / 32)
+    check_build(tk, "gdn_lpt_2launch", synth.ragged_offsets(lengths))
+
+
 def test_deltanet_ungated_d128():
     """DeltaNet (no gate, log_gate NULL) through the d = 128 bf16 path."""
     tk = synth.gdn_cold(n_seg=3, L=192, n_chain=2)

@@ -102,6 +102,16 @@ def test_kda_many_ragged_segments_two_launches():
     check_build(tk, "kda_300seg", synth.ragged_offsets(lengths))
 
 
+def test_kda_longest_first_across_launches():
+    """250 segments, the two longest (2100 and 2400 tokens) last in the batch:
+    the first launch (longest first over the batch) holds them and takes the
+    single-kernel path, the second launch the 10 shortest, the factor-record path."""
+    rng = np.random.default_rng(6)
+    lengths = [int(x) for x in rng.integers(1, 200, 248)] + [2100, 2400]
+    tk = synth.kda(n_seg=1, L=sum(lengths), n_chain=2, gate_scale=1.0 / 16)
+    check_build(tk, "kda_lpt_2launch", synth.ragged_offsets(lengths))
+
+
 def test_kda_segment_lengths_of_both_paths():
     """2048 tokens (longest of the factor-record path) and 2049 (single kernel)."""
     for L in (2048, 2049):
