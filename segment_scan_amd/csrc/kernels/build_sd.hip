@@ -62,34 +62,40 @@ __device__ __forceinline__ void cvt8(const Raw8<IN_F32>& r, float (&x)[8]) {
 // (ragged launches); a contiguous launch of equal lengths computes it, which
 // keeps the table lookup (and the registers it costs this register-bound
 // kernel) out of their code.
-// TOK: tokens per staging thread; the workgroup has 2 (C / TOK) (D / 8)
-// threads (half stage keys and gates, half values).
+//
+// Staging: each thread stages 4 tokens (token block tb) x 8 channels (channel
+// block db) of the keys (with their gates) and of the values, so the key work
+// (decay weights, splits) is spread evenly over all waves.  A wave covers 8
+// token blocks x 8 channel blocks: every load instruction reads 8 token rows of
+// 128 contiguous bytes, and its transposed LDS writes spread evenly over the
+// banks.  Wave w owns accumulator row tile w.
 #ifndef HYPIC_SD_WPE
 #define HYPIC_SD_WPE 2
 #endif
-#ifndef HYPIC_SD_SUB
-#define HYPIC_SD_SUB 4
-#endif
-template <int FAM, int D, bool IN_F32, bool ORDERED, int TOK>
-__global__ __launch_bounds__(2 * (C / TOK) * (D / 8)) __attribute__((amdgpu_waves_per_eu(HYPIC_SD_WPE)))
+constexpr int TB = 4;        // tokens per staging thread
+constexpr int NTB = C / TB;  // token blocks of a chunk
+
+__device__ __forceinline__ uint32_t word_at(const uint4& u, int j) {
+  return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
+}
+
+template <int FAM, int D, bool IN_F32, bool ORDERED>
+__global__ __launch_bounds__(NTB * (D / 8)) __attribute__((amdgpu_waves_per_eu(HYPIC_SD_WPE)))
 void build_sd_kernel(const BuildArgs a) {
   constexpr int NTK = IN_F32 ? 3 : 2;  // bf16 terms of decay-weighted keys
   constexpr int NTV = IN_F32 ? 3 : 1;  // bf16 terms of values (bf16 inputs are exact)
   constexpr int NRT = D / 32;          // 32-row tiles along d
-  constexpr int NTHR = 2 * (C / TOK) * (D / 8);
-  constexpr int NWAVE = NTHR / 64;     // waves of the workgroup
-  constexpr int TPW = NRT * NRT / NWAVE;  // accumulator tiles per wave
-  constexpr int NTB = C / TOK;         // token blocks of a chunk
-  static_assert(TPW >= 1 && NRT * NRT == TPW * NWAVE, "tiles per wave");
+  constexpr int NTHR = NTB * (D / 8);
+  static_assert(NTHR / 64 == NRT, "one accumulator row tile per wave");
   constexpr bool DIAG = (FAM == 2);
-  constexpr bool GATED = (FAM == 1 || FAM == 2);
+  constexpr uint32_t ESZ = IN_F32 ? 4 : 2;
 
   __shared__ __attribute__((aligned(16))) bf16_t sK[NTK][D * C];
   __shared__ __attribute__((aligned(16))) bf16_t sV[NTV][D * C];
-  __shared__ float sW[C];        // scalar: weight exp(G_C - G_t)
-  __shared__ __attribute__((aligned(16))) float sTot[NTB][D];  // diag: per-token-block sums of log gates
-  __shared__ float sGC[D];       // chunk log-transition (scalar: entry 0)
-  __shared__ float sEGC[D];      // exp of it
+  __shared__ __attribute__((aligned(16))) float sW[C];  // scalar: weight exp(G_C - G_t)
+  // diag: per-block sums of log gates, then the sums over the blocks after each
+  __shared__ __attribute__((aligned(16))) float sSuf[DIAG ? NTB : 1][D + 4];
+  __shared__ __attribute__((aligned(16))) float sEGC[D];  // exp of the chunk log-transition (scalar: entry 0)
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -103,53 +109,52 @@ void build_sd_kernel(const BuildArgs a) {
   const int t_end = ORDERED ? a.seg.end[slot] : t_begin + len0;
   const size_t unit = (size_t)(ORDERED ? a.seg.out[slot] : a.seg.out[0] + slot) * n_chain + h;
 
-  f32x16 acc[TPW];
+  f32x16 acc[NRT];  // tile (row tile wave, column tile i)
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) acc[i] = zero16();
+  for (int i = 0; i < NRT; ++i) acc[i] = zero16();
 
-  double g_acc = 0.0;  // scalar: lane 0 of wave 0; diag: thread tid < D for channel tid
+  double g_acc = 0.0;  // scalar: thread 0; diag: thread tid < D for channel tid
 
-  // staging role: the first half of the waves stage keys (and diagonal gates),
-  // the second values (a wave-uniform choice, so the source is a scalar base)
-  const bool is_k = wave_id_uniform() < NWAVE / 2;
-  const bool is_v = !is_k;
-  const int sid = is_k ? tid : tid - NTHR / 2;
-  const int tb = sid % NTB;  // block of TOK tokens
-  const int db = sid / NTB;  // 8-channel block
-  const void* src = is_k ? a.k : a.v;
-  constexpr uint32_t ESZ = IN_F32 ? 4 : 2;
+  const int tb = 8 * (wave & 1) + (lane & 7);  // 16 token blocks: two waves' worth
+  const int db = 8 * (wave >> 1) + (lane >> 3);
   const uint32_t row_bytes = (uint32_t)n_chain * D * ESZ;  // one token of all chains
-  const uint32_t voff = (uint32_t)(tb * TOK) * row_bytes + db * 8 * ESZ;
+  const uint32_t voff = (uint32_t)(tb * TB) * row_bytes + db * 8 * ESZ;
 
   // raw inputs of the chunk being staged; the next chunk's are loaded while the
   // matrix cores work on this one.  Buffer loads over the chunk's valid rows:
   // tokens past the segment's end read as zeros.
-  Raw8<IN_F32> rx[TOK];
-  Raw8<IN_F32> rg[TOK];
+  Raw8<IN_F32> rk[TB], rv[TB], rg[DIAG ? TB : 1];
   float lg_scalar = 0.f;
+  // Issued unconditionally, also past the segment's last chunk (an empty range:
+  // zeros, no memory touched), so the loop carries one set of load registers.
   auto issue_loads = [&](int c0) {
     const int nv = min(C, t_end - c0);
     const size_t row0 = ((size_t)c0 * n_chain + h) * D * ESZ;  // byte offset of token c0, chain h
-    const uint32_t bytes = (uint32_t)(nv - 1) * row_bytes + D * ESZ;
-    {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const char*>(src) + row0, bytes);
+    const uint32_t bytes = nv > 0 ? (uint32_t)(nv - 1) * row_bytes + D * ESZ : 0u;
+    const __amdgpu_buffer_rsrc_t rsk = buffer_rsrc(reinterpret_cast<const char*>(a.k) + row0, bytes);
+    const __amdgpu_buffer_rsrc_t rsv = buffer_rsrc(reinterpret_cast<const char*>(a.v) + row0, bytes);
 #pragma unroll
-      for (int r = 0; r < TOK; ++r) rx[r] = ldraw8<IN_F32>(rs, voff, r * row_bytes);
+    for (int r = 0; r < TB; ++r) {
+      rk[r] = ldraw8<IN_F32>(rsk, voff, r * row_bytes);
+      rv[r] = ldraw8<IN_F32>(rsv, voff, r * row_bytes);
     }
     if constexpr (DIAG) {
-      if (is_k) {
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const char*>(a.lg) + row0, bytes);
+      const __amdgpu_buffer_rsrc_t rsg = buffer_rsrc(reinterpret_cast<const char*>(a.lg) + row0, bytes);
 #pragma unroll
-        for (int r = 0; r < TOK; ++r) rg[r] = ldraw8<IN_F32>(rs, voff, r * row_bytes);
-      }
+      for (int r = 0; r < TB; ++r) rg[r] = ldraw8<IN_F32>(rsg, voff, r * row_bytes);
     }
     if constexpr (FAM == 1) {
-      if (wave == 0) {
-        lg_scalar = 0.f;
-        if (lane < nv)
-          lg_scalar = a.gate_per_chain ? reinterpret_cast<const float*>(a.lg)[h]
-                                       : load1<IN_F32>(a.lg, (size_t)(c0 + lane) * n_chain + h);
-      }
+      // token c0 + lane's gate (zero past the end): a per-chain fp32 constant, or
+      // per token (the buffer then covers the chunk's valid tokens of chain h)
+      const bool per_tok = !a.gate_per_chain;
+      const uint32_t gbytes = per_tok && nv > 0 ? ((uint32_t)(nv - 1) * n_chain + 1) * ESZ : 0u;
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(reinterpret_cast<const char*>(a.lg) + ((size_t)c0 * n_chain + h) * ESZ, gbytes);
+      const uint32_t go = (uint32_t)lane * n_chain * ESZ;
+      const float tok = IN_F32 ? __uint_as_float(buffer_load4(rs, go, 0))
+                               : __uint_as_float((uint32_t)buffer_load2(rs, go, 0) << 16);
+      const float chn = per_tok ? 0.f : reinterpret_cast<const float*>(a.lg)[h];
+      lg_scalar = tok + (lane < nv ? chn : 0.f);
     }
   };
   issue_loads(t_begin);
@@ -162,7 +167,6 @@ void build_sd_kernel(const BuildArgs a) {
         const float GC = __shfl(G, 63, 64);
         sW[lane] = expf(GC - G);
         if (lane == 0) {
-          sGC[0] = GC;
           sEGC[0] = expf(GC);
           g_acc += (double)GC;
         }
@@ -170,152 +174,164 @@ void build_sd_kernel(const BuildArgs a) {
       __syncthreads();
     }
 
-    // ---- gates: diagonal prefix per channel (key-staging threads) ---------------
-    float pre[8], tot[8];
+    // ---- gates: per channel, the sum over the tokens after this thread's block
+    float sfx[8];
     if constexpr (DIAG) {
-      if (is_k) {
-        float run[8];
+      {
+        float tot[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) run[c] = 0.f;
+        for (int c = 0; c < 8; ++c) tot[c] = 0.f;
 #pragma unroll
-        for (int r = 0; r < TOK; ++r) {
+        for (int r = 0; r < TB; ++r) {
           float x[8];
           cvt8<IN_F32>(rg[r], x);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) run[c] += x[c];
+          for (int c = 0; c < 8; ++c) tot[c] += x[c];
         }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sTot[tb][db * 8 + c] = run[c];
+        *reinterpret_cast<f32x4*>(&sSuf[tb][db * 8]) = f32x4{tot[0], tot[1], tot[2], tot[3]};
+        *reinterpret_cast<f32x4*>(&sSuf[tb][db * 8 + 4]) = f32x4{tot[4], tot[5], tot[6], tot[7]};
       }
       __syncthreads();
-      if (is_k) {
+      if (tid < D) {  // channel tid: block sums -> sums over the later blocks, and the chunk total
+        float blk[NTB];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) pre[c] = tot[c] = 0.f;
-        // block by block (two 16-byte reads each), so few reads are in flight
-#pragma unroll 2
-        for (int b = 0; b < NTB; ++b) {
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(&sTot[b][db * 8]);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(&sTot[b][db * 8 + 4]);
-          const float w = b < tb ? 1.f : 0.f;
+        for (int b = 0; b < NTB; ++b) blk[b] = sSuf[b][tid];
+        float run = 0.f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            tot[c] += x0[c];
-            tot[4 + c] += x1[c];
-            pre[c] = fmaf(w, x0[c], pre[c]);
-            pre[4 + c] = fmaf(w, x1[c], pre[4 + c]);
-          }
+        for (int b = NTB - 1; b >= 0; --b) {
+          sSuf[b][tid] = run;
+          run += blk[b];
         }
-        if (tb == 0) {
+        sEGC[tid] = expf(run);
+        g_acc += (double)run;
+      }
+      __syncthreads();
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sSuf[tb][db * 8]);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sSuf[tb][db * 8 + 4]);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            sGC[db * 8 + c] = tot[c];
-            sEGC[db * 8 + c] = expf(tot[c]);
-          }
-        }
+      for (int c = 0; c < 4; ++c) {
+        sfx[c] = s0[c];
+        sfx[4 + c] = s1[c];
       }
     }
 
     // ---- stage keys (decay-weighted, split) and values, transposed -------------
-    // in sub-blocks of SUB tokens (fewer live registers than the whole block)
+    // the 4 tokens of channel db*8+c are one 8-byte piece of LDS row db*8+c
     {
-      constexpr int SUB = TOK < HYPIC_SD_SUB ? TOK : HYPIC_SD_SUB;
-      float run[8];
+      const int t0 = tb * TB;
+      bf16x4 kt[NTK][8];  // [term][channel], token r in element r
+      {
+        float run[8];  // diag: log gates of this block's tokens after token r
 #pragma unroll
-      for (int c = 0; c < 8; ++c) run[c] = 0.f;
+        for (int c = 0; c < 8; ++c) run[c] = 0.f;
+        f32x4 w4;
+        if constexpr (FAM == 1) w4 = *reinterpret_cast<const f32x4*>(&sW[t0]);
 #pragma unroll
-      for (int r0 = 0; r0 < TOK; r0 += SUB) {
-        float x[SUB][8];  // [token r][channel c]
+        for (int r = TB - 1; r >= 0; --r) {
+          float x[8];
+          cvt8<IN_F32>(rk[r], x);
+          if constexpr (DIAG) {
+            float lgr[8];
+            cvt8<IN_F32>(rg[r], lgr);
 #pragma unroll
-        for (int r = 0; r < SUB; ++r) {
-          cvt8<IN_F32>(rx[r0 + r], x[r]);
-          if (is_k && GATED) {
-            if constexpr (DIAG) {
-              float lgr[8];
-              cvt8<IN_F32>(rg[r0 + r], lgr);
-#pragma unroll
-              for (int c = 0; c < 8; ++c) {
-                run[c] += lgr[c];
-                x[r][c] *= __expf(tot[c] - (pre[c] + run[c]));
-              }
-            } else {
-#pragma unroll
-              for (int c = 0; c < 8; ++c) x[r][c] *= sW[tb * TOK + r0 + r];
+            for (int c = 0; c < 8; ++c) {
+              x[c] *= __expf(sfx[c] + run[c]);
+              run[c] += lgr[c];
             }
+          } else if constexpr (FAM == 1) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] *= w4[r];
           }
-        }
-        // column c of the sub-block = SUB tokens of channel db*8+c: part of one
-        // 16-byte LDS row chunk (chunk (tb TOK + r0) / 8 of the row)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float col[SUB];
-#pragma unroll
-          for (int r = 0; r < SUB; ++r) col[r] = x[r][c];
-          const int row = db * 8 + c;
-          const int t0 = tb * TOK + r0;
-          const int off = swz64(row, t0 / 8) + t0 % 8;
-          using SubV = __attribute__((__vector_size__(SUB * sizeof(__bf16)))) __bf16;
-          if (is_k) {
+          for (int c = 0; c < 8; ++c) {
+            float y = x[c];
 #pragma unroll
             for (int i = 0; i < NTK; ++i) {
-              SubV tv;
-#pragma unroll
-              for (int r = 0; r < SUB; ++r) {
-                tv[r] = (bf16_t)col[r];
-                if (i + 1 < NTK) col[r] -= (float)tv[r];
-              }
-              *reinterpret_cast<SubV*>(&sK[i][off]) = tv;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < NTV; ++i) {
-              SubV tv;
-#pragma unroll
-              for (int r = 0; r < SUB; ++r) {
-                tv[r] = (bf16_t)col[r];
-                if (i + 1 < NTV) col[r] -= (float)tv[r];
-              }
-              *reinterpret_cast<SubV*>(&sV[i][off]) = tv;
+              const bf16_t hb = (bf16_t)y;
+              kt[i][c][r] = hb;
+              if (i + 1 < NTK) y -= (float)hb;
             }
           }
         }
       }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int off = swz64(db * 8 + c, t0 / 8) + t0 % 8;
+#pragma unroll
+        for (int i = 0; i < NTK; ++i) *reinterpret_cast<bf16x4*>(&sK[i][off]) = kt[i][c];
+      }
+      if constexpr (IN_F32) {
+        bf16x4 vt[NTV][8];
+#pragma unroll
+        for (int r = 0; r < TB; ++r) {
+          float x[8];
+          cvt8<IN_F32>(rv[r], x);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float y = x[c];
+#pragma unroll
+            for (int i = 0; i < NTV; ++i) {
+              const bf16_t hb = (bf16_t)y;
+              vt[i][c][r] = hb;
+              if (i + 1 < NTV) y -= (float)hb;
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int off = swz64(db * 8 + c, t0 / 8) + t0 % 8;
+#pragma unroll
+          for (int i = 0; i < NTV; ++i) *reinterpret_cast<bf16x4*>(&sV[i][off]) = vt[i][c];
+        }
+      } else {
+        // bf16 values are exact: a 16-bit transpose (byte permutes), no conversion
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t w01 = __builtin_amdgcn_perm(word_at(rv[1].w[0], c / 2), word_at(rv[0].w[0], c / 2), sel);
+          const uint32_t w23 = __builtin_amdgcn_perm(word_at(rv[3].w[0], c / 2), word_at(rv[2].w[0], c / 2), sel);
+          const int off = swz64(db * 8 + c, t0 / 8) + t0 % 8;
+          *reinterpret_cast<uint2*>(&sV[0][off]) = make_uint2(w01, w23);
+        }
+      }
     }
-    if (c0 + C < t_end) issue_loads(c0 + C);
+    issue_loads(c0 + C);
     __syncthreads();
 
-    if constexpr (DIAG) {
-      if (tid < D) g_acc += (double)sGC[tid];
-    }
-
     // ---- decay the running state to the chunk end, then add Ktil^T V ----------
+    if constexpr (FAM == 1) {
+      const float e = sEGC[0];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tt = wave * TPW + i;
-      const int rt = tt / NRT;
-      if constexpr (FAM == 1) {
-        const float e = sEGC[0];
+      for (int i = 0; i < NRT; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] *= e;
-      } else if constexpr (DIAG) {
+    } else if constexpr (DIAG) {
+      // rows 32 wave + acc_row(r, lane): four runs of 4 consecutive rows
+      float e[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] *= sEGC[32 * rt + acc_row(r, lane)];
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(&sEGC[32 * wave + 8 * j + 4 * (lane >> 5)]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) e[4 * j + m] = q[m];
       }
+#pragma unroll
+      for (int i = 0; i < NRT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= e[r];
     }
 #pragma unroll
     for (int ks = 0; ks < C / 16; ++ks) {
       const int chunk = 2 * ks + (lane >> 5);
+      Frag<NTK> fa;
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int tt = wave * TPW + i;
-        const int rt = tt / NRT, ct = tt % NRT;
-        Frag<NTK> fa;
+      for (int j = 0; j < NTK; ++j)
+        fa.t[j] = *reinterpret_cast<const bf16x8*>(&sK[j][swz64(32 * wave + (lane & 31), chunk)]);
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
         Frag<NTV> fb;
 #pragma unroll
-        for (int j = 0; j < NTK; ++j)
-          fa.t[j] = *reinterpret_cast<const bf16x8*>(&sK[j][swz64(32 * rt + (lane & 31), chunk)]);
-#pragma unroll
         for (int j = 0; j < NTV; ++j)
-          fb.t[j] = *reinterpret_cast<const bf16x8*>(&sV[j][swz64(32 * ct + (lane & 31), chunk)]);
+          fb.t[j] = *reinterpret_cast<const bf16x8*>(&sV[j][swz64(32 * i + (lane & 31), chunk)]);
         mma<NTK, NTV>(acc[i], fa, fb);
       }
     }
@@ -325,11 +341,9 @@ void build_sd_kernel(const BuildArgs a) {
   // ---- write S(C|0) and g ------------------------------------------------------
   float* S = a.S + unit * D * D;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int tt = wave * TPW + i;
-    const int rt = tt / NRT, ct = tt % NRT;
+  for (int i = 0; i < NRT; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[(size_t)(32 * rt + acc_row(r, lane)) * D + 32 * ct + (lane & 31)] = acc[i][r];
+    for (int r = 0; r < 16; ++r) S[(size_t)(32 * wave + acc_row(r, lane)) * D + 32 * i + (lane & 31)] = acc[i][r];
   }
   if constexpr (DIAG) {
     if (tid < D) a.g[unit * D + tid] = (float)g_acc;
@@ -338,17 +352,13 @@ void build_sd_kernel(const BuildArgs a) {
   }
 }
 
-#ifndef HYPIC_SD_TOK
-#define HYPIC_SD_TOK 8
-#endif
 template <int FAM, int D, bool F32>
 hipError_t launch_t(const BuildArgs& a, int n_blocks, hipStream_t stream) {
-  constexpr int TOK = HYPIC_SD_TOK;
-  constexpr int NTHR = 2 * (C / TOK) * (D / 8);
+  constexpr int NTHR = NTB * (D / 8);
   if (seg_uniform(a.seg))
-    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, false, TOK>), dim3(n_blocks), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, false>), dim3(n_blocks), dim3(NTHR), 0, stream, a);
   else
-    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, true, TOK>), dim3(n_blocks), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((build_sd_kernel<FAM, D, F32, true>), dim3(n_blocks), dim3(NTHR), 0, stream, a);
   return hipGetLastError();
 }
 

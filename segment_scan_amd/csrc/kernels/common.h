@@ -61,6 +61,12 @@ __device__ __forceinline__ int wave_id_uniform() { return __builtin_amdgcn_readf
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -362,8 +368,11 @@ __device__ __forceinline__ void inv_diag32_blocks(float* sM, int P, int lane) {
 }
 
 // LDS tile of bf16 with 64 columns (128 B rows), 16-byte column chunks
-// XOR-swizzled by (row & 7): consecutive rows read at the same logical chunk
-// hit distinct banks, and an 8-row transposed write does too.
-__device__ __forceinline__ int swz64(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+// XOR-swizzled by (row & 7) ^ ((row >> 3) & 7): 8 consecutive rows read at the
+// same logical chunk hit distinct banks, and so do rows 8 apart (a transposed
+// write of one channel from 8 channel blocks).
+__device__ __forceinline__ int swz64(int row, int chunk) {
+  return row * 64 + ((chunk ^ (row & 7) ^ ((row >> 3) & 7)) << 3);
+}
 
 }  // namespace hypic
