@@ -4,7 +4,8 @@
 
 Compiles every source under csrc/ to an object in csrc/_build/ and links the
 shared library next to this file.  Always recompiles sources newer than their
-object; `force=True` recompiles everything.
+object; `force=True` recompiles everything.  HYPIC_EXTRA_FLAGS (environment)
+adds compiler flags, for instance a -D that selects a kernel variant.
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ ROOT = os.path.dirname(HERE)
 ARCH = os.environ.get("HYPIC_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I" + os.path.join(ROOT, "include"),
+COMMON = [*os.environ.get("HYPIC_EXTRA_FLAGS", "").split(), "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I" + os.path.join(ROOT, "include"),
           "-Wall", "-Wno-unused-function"]
 # packed fp32 instructions are kept out of generated code on purpose
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

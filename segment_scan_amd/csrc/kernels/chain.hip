@@ -151,6 +151,18 @@ __device__ __forceinline__ HFrag<N> split8h(const float (&x)[8]) {
   return f;
 }
 
+// x s rounded to fp32 and hidden from the optimiser.  The leading fp16 term of
+// a split is the fp16 rounding of this value, and the residual is taken from the
+// exact product with one fused multiply-add; left visible, the product may be
+// fused into one use of the term (an fp16 conversion of the exact product) and
+// not into another (fp16 of the fp32 product), and where the two roundings
+// differ the stored term and the residual disagree by an fp16 ulp.
+__device__ __forceinline__ float mul_opaque(float x, float s) {
+  float p = x * s;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
 // The same for x s with s a power of two, exponent within fp32's normal range:
 // t0 = fp16(x s) and every residual exact in fp32 (each step one fused
 // multiply-add with an fp16 operand)
@@ -160,7 +172,7 @@ __device__ __forceinline__ HFrag<N> split8h_scaled(const float (&x)[8], float s)
   float r[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const f16_t t = (f16_t)(x[j] * s);
+    const f16_t t = (f16_t)mul_opaque(x[j], s);
     f.t[0][j] = t;
     if (N > 1) r[j] = __builtin_fmaf(x[j], s, -(float)t);
   }
@@ -212,10 +224,21 @@ __device__ __forceinline__ void mmah16(f32x4& acc, const HFrag<NA>& a, const HFr
   }
 }
 
+// Waves per SIMD the register allocation must leave room for: the state
+// tiles, the prefetched U slices and S_B tiles fit 2 waves (seam step) or 3
+// (composition) without spills, and that many workgroups also fit the LDS of
+// a CU, so more chains run at once (left to itself the compiler gives the seam
+// step over 256 registers: one workgroup per CU).
+template <int D, int NCT, int NT, bool SEAM, bool IN_F32>
+constexpr int chain_min_waves() {
+  return SEAM ? 2 : 3;
+}
+
 // PAIRS: the chain has cached pairs (always for composition; the seam step may
 // run its windows alone)
 template <int D, int NCT, int NT, bool SEAM, bool IN_F32, bool PAIRS>
-__global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a) {
+__global__ __launch_bounds__(64 * (D / 32), (chain_min_waves<D, NCT, NT, SEAM, IN_F32>())) void chain_kernel(
+    const ChainArgs a) {
   using Cfg = ChainCfg<D, NCT, NT, SEAM, IN_F32>;
   constexpr int NRB = Cfg::NRB, NTH = Cfg::NTH, COLS = Cfg::COLS, NCG = Cfg::NCG, KS = Cfg::KS;
   constexpr int BP = Cfg::BP, NTA = Cfg::NTA, NTK = Cfg::NTK, NTR = Cfg::NTR, RPP = Cfg::RPP;
@@ -344,7 +367,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float x = St[ct][4 * q + j];
-          tv[0][j] = (f16_t)(x * sc);
+          tv[0][j] = (f16_t)mul_opaque(x, sc);
           if (NT > 1) r[j] = __builtin_fmaf(x, sc, -(float)tv[0][j]);
         }
 #pragma unroll
@@ -503,7 +526,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
   }
   if constexpr (SEAM) issue_window(0, 0);
   __syncthreads();
-  put_B((SEAM || !pairs) ? 1.f : __expf(g_next));
+  put_B((SEAM || !pairs) ? 1.f : expf(g_next));
   if constexpr (SEAM) stage_window();
   __syncthreads();
 
@@ -644,7 +667,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
           put_cmax();
         }
         __syncthreads();
-        put_B((sub + 1 == n_sub && pairs) ? __expf(g_next) : 1.f);
+        put_B((sub + 1 == n_sub && pairs) ? expf(g_next) : 1.f);
         if (sub + 1 < n_sub) stage_window();
         __syncthreads();
       }
@@ -708,7 +731,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
         if (!ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
         if (!ut) g_next = a.g[pidx + (size_t)(seg + 1) * n_chain];
         __syncthreads();  // every wave is done with sB
-        put_B((SEAM || ut) ? 1.f : __expf(g_next));
+        put_B((SEAM || ut) ? 1.f : expf(g_next));
         if constexpr (SEAM) stage_window();
         __syncthreads();
       }
@@ -721,6 +744,469 @@ __global__ __launch_bounds__(64 * (D / 32)) void chain_kernel(const ChainArgs a)
       }
     }
   }
+}
+
+
+// =====================================================================================
+// d = 128: one workgroup per unit, the whole state in MFMA accumulators
+// =====================================================================================
+// Work split.  Four waves; wave w keeps state columns 32w .. 32w+31, all 128
+// rows, as four 32x32 accumulator tiles and uses them directly as the B
+// operand of every product: elements 8m .. 8m+7 of a tile are a B fragment
+// whose k order (rows 16m + 8(j >> 2) + 4h + (j & 3)) the A operand matches
+// (common.h), so the state never goes through LDS and each column's scale is
+// lane-local.  U is the A operand: each step wave rb splits rows 32 rb ..
+// 32 rb + 31 (prefetched into registers a step ahead, 1 KB per load
+// instruction) into NT fp16 terms in LDS with one power of two per row block,
+// and every wave reads all of U from there.  The split rows are stored with
+// bits 2 and 3 of k swapped inside each 16-wide block, so that an A fragment
+// in the accumulator's k order is one 16-byte read.  The split is software
+// pipelined: two split-U buffers, the body product of pair s reading one while
+// the waves split pair s + 1 into the other between its MFMAs, each register
+// slice reloaded with pair s + 2 as soon as it is split; the next pair's S_B
+// and gate are loaded a step ahead.  One workgroup per CU thus keeps about two
+// pairs' bytes in flight, and a composition step has one barrier.
+//
+// Seam windows (bf16 tokens): [X; P] = [K; Q] S on 32x32x16 MFMA (K rows 0..7,
+// Q rows 8..15 of A; the upper 16 rows zero); each lane then holds X and P of
+// four tokens of its column, takes the other four from its partner lane, and
+// forms R = V - e^G X, R' = C^T R (lane half 0) or O = e^G P + W2 R (lane half
+// 1) in fp32; S <- e^{G_n} S + K^T R' as a rank-8 bf16 MFMA update.
+template <int NT, bool SEAM>
+struct WideCfg {
+  static constexpr int D = 128;
+  static constexpr int NTH = 256;
+  static constexpr int UP = D + 8;  // fp16 pitch of a split row: 272 bytes, 16-byte reads free of bank conflicts
+  static constexpr int UBUF = NT * D * UP * 2;                // bytes of one split U: [NT][D][UP] f16
+  static constexpr int OFF_U = 0;                              // two of them: pairs s and s + 1
+  static constexpr int OFF_EU = OFF_U + 2 * UBUF;              // [2][4] int: row-block exponents
+  static constexpr int OFF_A = OFF_EU + 32;                    // [2 SUB][UP] f16: K, Q rows, scaled
+  static constexpr int OFF_AS = OFF_A + 2 * SUB * UP * 2;      // [2 SUB] f32: 2^e of those rows
+  static constexpr int OFF_KT = OFF_AS + 2 * SUB * 4;          // [D][SUB] bf16: K^T
+  static constexpr int OFF_V = OFF_KT + D * SUB * 2;           // [SUB][D] f32
+  static constexpr int OFF_REC = OFF_V + SUB * D * 4;          // the window record
+  static constexpr int LDS = SEAM ? OFF_REC + SEAM_REC_FLOATS * 4 : OFF_A;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// position of k offset o (0..15) inside its 16-wide block: bits 2 and 3 swapped
+__device__ __forceinline__ constexpr int kperm(int o) { return (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1); }
+
+template <int N>
+struct H4 {
+  f16x4 t[N];
+};
+// 4 values times s (a power of two) as N fp16 terms, as split8h_scaled
+template <int N>
+__device__ __forceinline__ H4<N> split4h_scaled(const f32x4& x, float s) {
+  H4<N> f;
+  float r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16_t t = (f16_t)mul_opaque(x[j], s);
+    f.t[0][j] = t;
+    if (N > 1) r[j] = __builtin_fmaf(x[j], s, -(float)t);
+  }
+#pragma unroll
+  for (int i = 1; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16_t t = (f16_t)r[j];
+      f.t[i][j] = t;
+      if (i + 1 < N) r[j] -= (float)t;
+    }
+  return f;
+}
+
+__device__ __forceinline__ void buffer_store4(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+
+template <int NT, bool SEAM, bool PAIRS>
+__global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
+  using Cfg = WideCfg<NT, SEAM>;
+  constexpr int D = 128, UP = Cfg::UP;
+  constexpr uint32_t MAT = D * D * 4;  // bytes of one [D][D] fp32 matrix
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  f16_t* sU = reinterpret_cast<f16_t*>(smem + Cfg::OFF_U);
+  int* sEU = reinterpret_cast<int*>(smem + Cfg::OFF_EU);
+
+  const int unit = blockIdx.x;
+  const bool ut = blockIdx.y == 1;  // this workgroup composes U_total instead of S
+  const int n_chain = a.n_chain;
+  const int blk = a.blk_len > 0 ? unit / n_chain : 0;
+  const int chain = a.blk_len > 0 ? unit % n_chain : unit;
+  const int pidx = a.blk_len > 0 ? blk * a.blk_len * n_chain + chain : unit;
+  const int nseg = a.blk_len > 0 ? min(a.blk_len, a.n_seg - blk * a.blk_len) : a.n_seg;
+  const size_t unit_off = (size_t)unit * D * D;
+  const size_t pair_off = (size_t)pidx * D * D;
+  const size_t seg_stride = (size_t)n_chain * D * D;
+  const int wv = wave_id_uniform();  // columns 32 wv .. (and U rows 32 wv .. for the split)
+
+  // ---- the state tiles: element r of tile rt is row 32 rt + acc_row(r), column 32 wv + l32
+  f32x16 St[4], SB[4];
+  auto tile_voff = [&]() {
+    const int lane = opaque((int)threadIdx.x) & 63;
+    return (uint32_t)(((4 * (lane >> 5)) * D + 32 * wv + (lane & 31)) * 4);
+  };
+  auto tile_soff = [](int rt, int r) { return (uint32_t)((32 * rt + 8 * (r >> 2) + (r & 3)) * D * 4); };
+  auto load_tiles = [&](const float* base, f32x16 (&dst)[4]) {
+    const auto rs = buffer_rsrc(base, MAT);
+    const uint32_t vo = tile_voff();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[rt][r] = __uint_as_float(buffer_load4(rs, vo, tile_soff(rt, r)));
+  };
+  auto store_tiles = [&](float* base) {
+    const auto rs = buffer_rsrc(base, MAT);
+    const uint32_t vo = tile_voff();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) buffer_store4(St[rt][r], rs, vo, tile_soff(rt, r));
+  };
+
+  // ---- U of a pair: wave wv's rows, 16 loads of 1 KB (lane: row 32 wv + 2i + h, columns 4 l32 ..)
+  f32x4 ur[16];
+  auto issue_U = [&](int s) {
+    const auto rs = buffer_rsrc(a.U + (size_t)s * seg_stride + pair_off, MAT);
+    const int lane = opaque((int)threadIdx.x) & 63;
+    const uint32_t vo = (uint32_t)(((lane >> 5) * D + 4 * (lane & 31)) * 4);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = buffer_load16(rs, vo, (uint32_t)((32 * wv + 2 * i) * D * 4));
+      ur[i] = f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+    }
+  };
+  // split into LDS buffer b (NT fp16 terms, k permuted inside 16-blocks) with
+  // the row block's power of two: u_exp() once, then u_chunk(i) for each slice
+  auto u_exp = [&](int b) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(ur[i][j]));
+    const int eu = min(max(split_exp(wave_max_uniform(m)), -100), 100);
+    if ((threadIdx.x & 63) == 0) sEU[4 * b + wv] = eu;
+    return eu;
+  };
+  auto u_chunk = [&](int b, int i, float su) {
+    const int lane = opaque((int)threadIdx.x) & 63;
+    const int c = lane & 31;
+    f16_t* dst = sU + b * (Cfg::UBUF / 2) + (32 * wv + 2 * i + (lane >> 5)) * UP + 16 * (c >> 2) + kperm(4 * (c & 3));
+    const H4<NT> f = split4h_scaled<NT>(ur[i], su);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f16x4*>(dst + t * D * UP) = f.t[t];
+  };
+  // one slice of U of pair s reloaded (after its split)
+  auto reload_U = [&](int s, int i) {
+    const auto rs = buffer_rsrc(a.U + (size_t)s * seg_stride + pair_off, MAT);
+    const int lane = opaque((int)threadIdx.x) & 63;
+    const uint32_t vo = (uint32_t)(((lane >> 5) * D + 4 * (lane & 31)) * 4);
+    const uint4 v = buffer_load16(rs, vo, (uint32_t)((32 * wv + 2 * i) * D * 4));
+    ur[i] = f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+  };
+  auto split_U = [&](int b) {
+    const float su = ldexpf(1.f, -u_exp(b));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u_chunk(b, i, su);
+  };
+
+  // exponent of the lane's column: its 64 values and the partner lane's, times f
+  auto col_exp = [&](float f) {
+    float m = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(St[rt][r]));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    return min(max(split_exp(m * f), -100), 100);
+  };
+  // k step ks of the state as an NT-term B fragment, times sc
+  auto state_frag = [&](int ks, float sc) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = St[ks >> 1][8 * (ks & 1) + j];
+    return split8h_scaled<NT>(x, sc);
+  };
+
+  // ---- body pair: S <- exp(g) U S + S_B (U_total <- U U_total) ----------------------
+  // From split buffer cur, while the registers' pair (the next one) is split
+  // into buffer nxt between the MFMAs and each of its slices is then reloaded
+  // with pair s2.  On the last steps this split and reload are repeated work on
+  // a buffer nobody reads and a pair already loaded: no branch in the loop.
+  // The A fragments of k step ks + 1 are read while step ks multiplies.
+  auto body = [&](float f, int cur, int nxt, int s2, int sb) {
+    const auto sb_rs = buffer_rsrc(a.S + (size_t)max(sb, 0) * seg_stride + pair_off, MAT);
+    const int ec = col_exp(f);
+    const float sc = f * ldexpf(1.f, -ec);
+    const float su = ldexpf(1.f, -u_exp(nxt));
+    f32x16 T[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) T[rt] = zero16();
+    const int lane = opaque((int)threadIdx.x) & 63;
+    const f16_t* pa = sU + cur * (Cfg::UBUF / 2) + (lane & 31) * UP + 8 * (lane >> 5);
+    HFrag<NT> fa[2][4];
+    auto read_a = [&](HFrag<NT>(&dst)[4], int ks) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          dst[rt].t[t] = *reinterpret_cast<const f16x8*>(pa + (t * D + 32 * rt) * UP + 16 * ks);
+    };
+    read_a(fa[0], 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 1 < 8) read_a(fa[(ks + 1) & 1], ks + 1);
+      if (ks < 4 && sb >= 0) {  // S_B tile ks: its loads spread over the k steps, not one burst
+        const uint32_t vo = tile_voff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) SB[ks][r] = __uint_as_float(buffer_load4(sb_rs, vo, tile_soff(ks, r)));
+      }
+      const HFrag<NT> fb = state_frag(ks, sc);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) mmah<NT, NT>(T[rt], fa[ks & 1][rt], fb);
+#pragma unroll
+      for (int i = 2 * ks; i < 2 * ks + 2; ++i) {
+        u_chunk(nxt, i, su);
+        reload_U(s2, i);
+      }
+      sched_fence();
+    }
+    if (ut) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int e = sEU[4 * cur + rt] + ec;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) St[rt][r] = ldexpf(T[rt][r], e);
+      }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int e = sEU[4 * cur + rt] + ec;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) St[rt][r] = ldexpf(T[rt][r], e) + SB[rt][r];
+      }
+    }
+  };
+
+  // ---- seam windows ------------------------------------------------------------------
+  [[maybe_unused]] f16_t* sA = reinterpret_cast<f16_t*>(smem + Cfg::OFF_A);
+  [[maybe_unused]] float* sAS = reinterpret_cast<float*>(smem + Cfg::OFF_AS);
+  [[maybe_unused]] uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + Cfg::OFF_KT);
+  [[maybe_unused]] float* sV = reinterpret_cast<float*>(smem + Cfg::OFF_V);
+  [[maybe_unused]] float* sRec = reinterpret_cast<float*>(smem + Cfg::OFF_REC);
+  const int n_sub = SEAM ? (a.w + SUB - 1) / SUB : 0;
+  uint4 wraw[2];  // chunk tid: 8 values of a K (rows 0..7) or Q row; chunk 256 + tid: of a V row
+  float wrec_r = 0.f;
+  const uint32_t tok_stride = (uint32_t)n_chain * D;
+  auto tok_base = [&](size_t tok0) { return (tok0 * n_chain + chain) * D; };
+  auto issue_window = [&](int seg, int sub) {
+    const int tid = opaque((int)threadIdx.x);
+    const int n = min(SUB, a.w - sub * SUB);
+    const size_t base = tok_base((size_t)seg * a.w + sub * SUB);
+    const int row = tid >> 4, d8 = tid & 15, t = row & (SUB - 1);
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(row < SUB ? a.k : a.q);
+    wraw[0] = t < n ? *reinterpret_cast<const uint4*>(src + base + (uint32_t)t * tok_stride + 8 * d8)
+                    : make_uint4(0, 0, 0, 0);
+    wraw[1] = make_uint4(0, 0, 0, 0);
+    if (tid < SUB * (D / 8) && t < n)
+      wraw[1] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.v) + base +
+                                                (uint32_t)t * tok_stride + 8 * d8);
+    const float* rec = a.wrec + ((size_t)(seg * n_sub + sub) * n_chain + chain) * SEAM_REC_FLOATS;
+    if (tid < SEAM_REC_FLOATS) wrec_r = rec[tid];
+  };
+  auto stage_window = [&]() {
+    const int tid = opaque((int)threadIdx.x);
+    const int row = tid >> 4, d8 = tid & 15, t = row & (SUB - 1);
+    const uint32_t u[4] = {wraw[0].x, wraw[0].y, wraw[0].z, wraw[0].w};
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(u[j] << 16);
+      x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+    }
+    // a K or Q row scaled by the power of two of its maximum (the row's 16
+    // chunks are one 16-lane DPP row), one fp16 term (exact for bf16 values)
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+    m = dpp_max_step(m, 0);
+    m = dpp_max_step(m, 1);
+    m = dpp_max_step(m, 2);
+    m = dpp_max_step(m, 3);
+    const int e = min(max(split_exp(m), -100), 100);
+    const float s = ldexpf(1.f, -e);
+    f16x4 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = (f16_t)(x[j] * s);
+      hi[j] = (f16_t)(x[4 + j] * s);
+    }
+    // columns 8 d8 + j of block d8 / 2 at positions kperm(8 (d8 & 1) + j)
+    f16_t* dst = sA + row * UP + 16 * (d8 >> 1) + 4 * (d8 & 1);
+    *reinterpret_cast<f16x4*>(dst) = lo;
+    *reinterpret_cast<f16x4*>(dst + 8) = hi;
+    if (d8 == 0) sAS[row] = ldexpf(1.f, e);
+    if (row < SUB) {  // keys, transposed, as they are (bf16)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sKt[(8 * d8 + 2 * j) * SUB + t] = (uint16_t)(u[j] & 0xffffu);
+        sKt[(8 * d8 + 2 * j + 1) * SUB + t] = (uint16_t)(u[j] >> 16);
+      }
+    }
+    if (tid < SUB * (D / 8)) {  // values of token t, columns 8 d8 ..
+      const uint32_t w[4] = {wraw[1].x, wraw[1].y, wraw[1].z, wraw[1].w};
+      float* dv = sV + t * D + 8 * d8;
+      *reinterpret_cast<f32x4*>(dv) = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                            __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+      *reinterpret_cast<f32x4*>(dv + 4) = f32x4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                                                __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u)};
+    }
+    if (tid < SEAM_REC_FLOATS) sRec[tid] = wrec_r;
+  };
+  // one window sub-chunk of n tokens on the running state (LDS staged)
+  auto window = [&](int seg, int sub) {
+    const int n = min(SUB, a.w - sub * SUB);
+    const int lane = opaque((int)threadIdx.x) & 63;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int ec = col_exp(1.f);
+    const float sc = ldexpf(1.f, -ec);
+    f32x16 XP = zero16();
+    {
+      const f16_t* pa = sA + (l32 & 15) * UP + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const HFrag<NT> fb = state_frag(ks, sc);
+        HFrag<1> fa;
+        fa.t[0] = *reinterpret_cast<const f16x8*>(pa + 16 * ks);
+        if (l32 >= 2 * SUB) fa.t[0] = f16x8{};
+        mmah<1, NT>(XP, fa, fb);
+      }
+    }
+    // elements j < 4: X of token 4h + j; elements 4 + j: P of token 4h + j
+    const int c = 32 * wv + l32;
+    const float cs = ldexpf(1.f, ec);
+    float R4[4], P4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * h + j;
+      const float eg = sRec[2 * SUB * SUB + t];
+      R4[j] = sV[t * D + c] - eg * (XP[j] * cs * sAS[t]);
+      P4[j] = eg * (XP[4 + j] * cs * sAS[SUB + t]);
+    }
+    float R8[SUB], EP[SUB];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float ro = __shfl_xor(R4[j], 32, 64), po = __shfl_xor(P4[j], 32, 64);
+      R8[j] = h ? ro : R4[j];
+      R8[4 + j] = h ? R4[j] : ro;
+      EP[j] = h ? po : P4[j];
+      EP[4 + j] = h ? P4[j] : po;
+    }
+    // lane half 0: R' = C^T R; lane half 1: O = e^G P + W2 R (fp32)
+    float acc[SUB];
+    const float* coef = sRec + (h ? SUB * SUB : 0);
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(coef + t * SUB);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(coef + t * SUB + 4);
+      float s = h ? EP[t] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s = fmaf(c0[u], R8[u], s);
+        s = fmaf(c1[u], R8[4 + u], s);
+      }
+      acc[t] = s;
+    }
+    if (h) {
+      const size_t obase = tok_base((size_t)seg * a.w + sub * SUB);
+#pragma unroll
+      for (int t = 0; t < SUB; ++t)
+        if (t < n) a.o[obase + (uint32_t)t * tok_stride + c] = acc[t];
+    }
+    // S <- exp(G_n) S + K^T R' (k = the 8 tokens in lane half 0; half 1 zeros)
+    const float eGn = sRec[2 * SUB * SUB + SUB];
+    Frag<2> fb;
+    {
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < SUB; ++t) x[t] = h ? 0.f : acc[t];
+      fb = split8<2>(x);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Frag<1> fa;
+      fa.t[0] = *reinterpret_cast<const bf16x8*>(sKt + (32 * rt + l32) * SUB);
+      if (h) fa.t[0] = bf16x8{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) St[rt][r] *= eGn;
+      mma<1, 2>(St[rt], fa, fb);
+    }
+  };
+
+  // ---- start state, first loads --------------------------------------------------------
+  if (!ut && a.S_in) {
+    load_tiles(a.S_in + unit_off, St);
+  } else {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        St[rt][r] = (ut && 32 * rt + acc_row(r, lane) == 32 * wv + (lane & 31)) ? 1.f : 0.f;
+  }
+  if (!ut && a.prefix) store_tiles(a.prefix + pair_off);  // prefix states follow the pairs' layout
+  float g_cur = 0.f;
+  if (PAIRS) {
+    issue_U(0);
+    if (!ut) g_cur = a.g[pidx];
+    split_U(0);
+    if (nseg > 1) issue_U(1);
+  }
+  if constexpr (SEAM) issue_window(0, 0);
+  if constexpr (!SEAM) __syncthreads();
+
+  for (int seg = 0; seg < nseg; ++seg) {
+    const bool more = seg + 1 < nseg;
+    if constexpr (SEAM) {
+      for (int sub = 0; sub < n_sub; ++sub) {
+        stage_window();
+        __syncthreads();
+        if (sub + 1 < n_sub) issue_window(seg, sub + 1);
+        else if (more) issue_window(seg + 1, 0);
+        window(seg, sub);
+        if (sub + 1 < n_sub) __syncthreads();  // before the window area is staged again
+      }
+    }
+    if (PAIRS) {
+      const float g_nxt = (more && !ut) ? a.g[pidx + (size_t)(seg + 1) * n_chain] : 0.f;
+      body(ut ? 1.f : expf(g_cur), seg & 1, (seg + 1) & 1, min(seg + 2, nseg - 1), ut ? -1 : seg);
+      g_cur = g_nxt;
+      if (more && !ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
+    }
+    __syncthreads();  // every wave is done with this step's LDS
+  }
+
+  store_tiles((ut ? a.U_tot : a.S_out) + unit_off);
+  if (!ut && a.g_tot && threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int s = 0; s < nseg; ++s) acc += (double)a.g[pidx + (size_t)s * n_chain];
+    a.g_tot[unit] = (float)acc;
+  }
+}
+
+template <int NT, bool SEAM, bool PAIRS>
+hipError_t launch_wide_p(const ChainArgs& a, bool want_ut, hipStream_t stream) {
+  using Cfg = WideCfg<NT, SEAM>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&chain_wide_kernel<NT, SEAM, PAIRS>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg::LDS);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((chain_wide_kernel<NT, SEAM, PAIRS>), dim3(a.n_units, want_ut ? 2 : 1), dim3(Cfg::NTH),
+                     Cfg::LDS, stream, a);
+  return hipGetLastError();
 }
 
 template <int D, int NCT, int NT, bool SEAM, bool IN_F32, bool PAIRS>
@@ -753,6 +1239,12 @@ hipError_t launch_chain_t(const ChainArgs& a, bool want_ut, hipStream_t stream) 
 #endif
 template <int D>
 hipError_t launch_compose_d(const ChainArgs& a, bool want_ut, hipStream_t stream) {
+  // d = 128: two fp16 terms per operand.  With the leading term rounded once
+  // (mul_opaque) the products carry about 2^-22 of each operand, below the
+  // rounding of the matrix cores' own fp32 accumulation on these sums: composed
+  // states of random fp32 pairs come out within about 1e-7 of the fp64
+  // recurrence with two terms as with three.
+  if constexpr (D == 128) return launch_wide_p<2, false, true>(a, want_ut, stream);
   if ((long)a.n_units * (D / 32) * (want_ut ? 2 : 1) <= HYPIC_COMPOSE_NCT1_MAX)
     return launch_chain_t<D, 1, 3, false, false>(a, want_ut, stream);
   return launch_chain_t<D, 2, 3, false, false>(a, want_ut, stream);
@@ -882,9 +1374,11 @@ hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& s, hipStream_t 
   // input precision); fp32 tokens: three
   constexpr int NCT128 = HYPIC_SEAM_NCT;
   constexpr int NCT64 = HYPIC_SEAM_NCT > 2 ? 2 : HYPIC_SEAM_NCT;
-  if (d == 128)
-    return in_f32 ? launch_chain_t<128, 1, 3, true, true>(a, false, stream)
-                  : launch_chain_t<128, NCT128, 2, true, false>(a, false, stream);
+  if (d == 128) {
+    if (in_f32) return launch_chain_t<128, 1, 3, true, true>(a, false, stream);
+    return a.S == nullptr ? launch_wide_p<2, true, false>(a, false, stream)
+                          : launch_wide_p<2, true, true>(a, false, stream);
+  }
   if (d == 64)
     return in_f32 ? launch_chain_t<64, 1, 3, true, true>(a, false, stream)
                   : launch_chain_t<64, NCT64, 2, true, false>(a, false, stream);
