@@ -938,7 +938,9 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   // a buffer nobody reads and a pair already loaded: no branch in the loop.
   // The A fragments of k step ks + 1 are read while step ks multiplies.
   auto body = [&](float f, int cur, int nxt, int s2, int sb) {
-    const auto sb_rs = buffer_rsrc(a.S + (size_t)max(sb, 0) * seg_stride + pair_off, MAT);
+    // (sb < 0: a resource of no bytes, whose loads return zeros and read nothing,
+    // so no branch splits the loop)
+    const auto sb_rs = buffer_rsrc(a.S + (size_t)max(sb, 0) * seg_stride + pair_off, sb >= 0 ? MAT : 0u);
     const int ec = col_exp(f);
     const float sc = f * ldexpf(1.f, -ec);
     const float su = ldexpf(1.f, -u_exp(nxt));
@@ -955,22 +957,34 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
         for (int t = 0; t < NT; ++t)
           dst[rt].t[t] = *reinterpret_cast<const f16x8*>(pa + (t * D + 32 * rt) * UP + 16 * ks);
     };
+    HFrag<NT> fb[2];
     read_a(fa[0], 0);
+    fb[0] = state_frag(0, sc);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      if (ks + 1 < 8) read_a(fa[(ks + 1) & 1], ks + 1);
-      if (ks < 4 && sb >= 0) {  // S_B tile ks: its loads spread over the k steps, not one burst
+      if (ks + 1 < 8) {
+        read_a(fa[(ks + 1) & 1], ks + 1);
+        fb[(ks + 1) & 1] = state_frag(ks + 1, sc);
+      }
+      if (ks < 4) {  // S_B tile ks: its loads spread over the k steps, not one burst
         const uint32_t vo = tile_voff();
 #pragma unroll
         for (int r = 0; r < 16; ++r) SB[ks][r] = __uint_as_float(buffer_load4(sb_rs, vo, tile_soff(ks, r)));
       }
-      const HFrag<NT> fb = state_frag(ks, sc);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) mmah<NT, NT>(T[rt], fa[ks & 1][rt], fb);
+      for (int rt = 0; rt < 4; ++rt) mmah<NT, NT>(T[rt], fa[ks & 1][rt], fb[ks & 1]);
 #pragma unroll
       for (int i = 2 * ks; i < 2 * ks + 2; ++i) {
         u_chunk(nxt, i, su);
         reload_U(s2, i);
+      }
+      // issue order inside the k step: every MFMA followed by a few of the
+      // step's independent VALU instructions (the next fragments and the
+      // split), so that they run in the MFMAs' shadow instead of after them
+#pragma unroll
+      for (int m = 0; m < 4 * (NT * (NT + 1) / 2); ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
       sched_fence();
     }

@@ -37,7 +37,32 @@ __global__ __launch_bounds__(64) void seam_prep_kernel(const SeamArgs a, float* 
   const size_t tok0 = (size_t)seg * a.w + t0;
   const int lane = threadIdx.x;
 
-  // ---- the sub-chunk's keys and queries (fp32), zero past n ----------------------
+  // ---- bf16 tokens: [K; Q] K^T on 16x16x32 bf16 MFMA (exact products), operands
+  // straight from memory: lane (row l16, group g) holds k = 32 ks + 8 g .. of K
+  // row l16 (Q row l16 - 8) as A and of key l16 as B; output row 4 g + j, column l16
+  if constexpr (!IN_F32) {
+    const int l16 = lane & 15, g = lane >> 4, t = l16 & (SUB - 1);
+    const uint16_t* arow = reinterpret_cast<const uint16_t*>(l16 < SUB ? a.k : a.q) +
+                           ((tok0 + t) * n_chain + chain) * D + 8 * g;
+    const uint16_t* brow = reinterpret_cast<const uint16_t*>(a.k) + ((tok0 + t) * n_chain + chain) * D + 8 * g;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      bf16x8 fa{}, fb{};
+      if (t < n) fa = *reinterpret_cast<const bf16x8*>(arow + 32 * ks);
+      if (l16 < SUB && t < n) fb = *reinterpret_cast<const bf16x8*>(brow + 32 * ks);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+    }
+    if (l16 < SUB) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        (r < SUB ? sKK : sQK)[(r & (SUB - 1)) * SUB + l16] = acc[j];
+      }
+    }
+  }
+  // ---- fp32 tokens: the sub-chunk's keys and queries (fp32), zero past n ----------
+  if constexpr (IN_F32)
   for (int i = lane; i < 2 * SUB * (D / 8); i += 64) {
     const int which = i / (SUB * (D / 8)), j = i % (SUB * (D / 8));
     const int t = j / (D / 8), d8 = j % (D / 8);
@@ -63,7 +88,7 @@ __global__ __launch_bounds__(64) void seam_prep_kernel(const SeamArgs a, float* 
   __syncthreads();
 
   // ---- lane p: one of the 28 products k_t.k_s (s < t) or 36 products q_t.k_s (s <= t)
-  {
+  if constexpr (IN_F32) {
     int t, s;
     bool kk;
     if (lane < SUB * (SUB - 1) / 2) {
