@@ -780,12 +780,15 @@ struct WideCfg {
   static constexpr int UBUF = NT * D * UP * 2;                // bytes of one split U: [NT][D][UP] f16
   static constexpr int OFF_U = 0;                              // two of them: pairs s and s + 1
   static constexpr int OFF_EU = OFF_U + 2 * UBUF;              // [2][4] int: row-block exponents
-  static constexpr int OFF_A = OFF_EU + 32;                    // [2 SUB][UP] f16: K, Q rows, scaled
-  static constexpr int OFF_AS = OFF_A + 2 * SUB * UP * 2;      // [2 SUB] f32: 2^e of those rows
-  static constexpr int OFF_KT = OFF_AS + 2 * SUB * 4;          // [D][SUB] bf16: K^T
-  static constexpr int OFF_V = OFF_KT + D * SUB * 2;           // [SUB][D] f32
-  static constexpr int OFF_REC = OFF_V + SUB * D * 4;          // the window record
-  static constexpr int LDS = SEAM ? OFF_REC + SEAM_REC_FLOATS * 4 : OFF_A;
+  // two window areas (window i in area i & 1), each:
+  static constexpr int W_A = 0;                                // [2 SUB][UP] f16: K, Q rows, scaled
+  static constexpr int W_AS = W_A + 2 * SUB * UP * 2;          // [2 SUB] f32: 2^e of those rows
+  static constexpr int W_KT = W_AS + 2 * SUB * 4;              // [D][SUB] bf16: K^T
+  static constexpr int W_V = W_KT + D * SUB * 2;               // [SUB][D] f32
+  static constexpr int W_REC = W_V + SUB * D * 4;              // the window record
+  static constexpr int WBUF = W_REC + SEAM_REC_FLOATS * 4;
+  static constexpr int OFF_W = OFF_EU + 32;
+  static constexpr int LDS = SEAM ? OFF_W + 2 * WBUF : OFF_W;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -937,7 +940,7 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   // with pair s2.  On the last steps this split and reload are repeated work on
   // a buffer nobody reads and a pair already loaded: no branch in the loop.
   // The A fragments of k step ks + 1 are read while step ks multiplies.
-  auto body = [&](float f, int cur, int nxt, int s2, int sb) {
+  auto body = [&](float f, int cur, int nxt, int s2, int sb, auto&& hook) {
     // (sb < 0: a resource of no bytes, whose loads return zeros and read nothing,
     // so no branch splits the loop)
     const auto sb_rs = buffer_rsrc(a.S + (size_t)max(sb, 0) * seg_stride + pair_off, sb >= 0 ? MAT : 0u);
@@ -978,6 +981,7 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
         u_chunk(nxt, i, su);
         reload_U(s2, i);
       }
+      if (ks == 3) hook();
       // issue order inside the k step: every MFMA followed by a few of the
       // step's independent VALU instructions (the next fragments and the
       // split), so that they run in the MFMAs' shadow instead of after them
@@ -1006,17 +1010,15 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   };
 
   // ---- seam windows ------------------------------------------------------------------
-  [[maybe_unused]] f16_t* sA = reinterpret_cast<f16_t*>(smem + Cfg::OFF_A);
-  [[maybe_unused]] float* sAS = reinterpret_cast<float*>(smem + Cfg::OFF_AS);
-  [[maybe_unused]] uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + Cfg::OFF_KT);
-  [[maybe_unused]] float* sV = reinterpret_cast<float*>(smem + Cfg::OFF_V);
-  [[maybe_unused]] float* sRec = reinterpret_cast<float*>(smem + Cfg::OFF_REC);
+  auto warea = [&](int buf) { return smem + Cfg::OFF_W + buf * Cfg::WBUF; };
   const int n_sub = SEAM ? (a.w + SUB - 1) / SUB : 0;
+  const int n_win = n_sub * nseg;  // windows in order: i = seg * n_sub + sub
   uint4 wraw[2];  // chunk tid: 8 values of a K (rows 0..7) or Q row; chunk 256 + tid: of a V row
   float wrec_r = 0.f;
   const uint32_t tok_stride = (uint32_t)n_chain * D;
   auto tok_base = [&](size_t tok0) { return (tok0 * n_chain + chain) * D; };
-  auto issue_window = [&](int seg, int sub) {
+  auto issue_window = [&](int wi) {
+    const int seg = wi / n_sub, sub = wi % n_sub;
     const int tid = opaque((int)threadIdx.x);
     const int n = min(SUB, a.w - sub * SUB);
     const size_t base = tok_base((size_t)seg * a.w + sub * SUB);
@@ -1031,7 +1033,12 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     const float* rec = a.wrec + ((size_t)(seg * n_sub + sub) * n_chain + chain) * SEAM_REC_FLOATS;
     if (tid < SEAM_REC_FLOATS) wrec_r = rec[tid];
   };
-  auto stage_window = [&]() {
+  auto stage_window = [&](int buf) {
+    f16_t* sA = reinterpret_cast<f16_t*>(warea(buf) + Cfg::W_A);
+    float* sAS = reinterpret_cast<float*>(warea(buf) + Cfg::W_AS);
+    uint16_t* sKt = reinterpret_cast<uint16_t*>(warea(buf) + Cfg::W_KT);
+    float* sV = reinterpret_cast<float*>(warea(buf) + Cfg::W_V);
+    float* sRec = reinterpret_cast<float*>(warea(buf) + Cfg::W_REC);
     const int tid = opaque((int)threadIdx.x);
     const int row = tid >> 4, d8 = tid & 15, t = row & (SUB - 1);
     const uint32_t u[4] = {wraw[0].x, wraw[0].y, wraw[0].z, wraw[0].w};
@@ -1081,7 +1088,12 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     if (tid < SEAM_REC_FLOATS) sRec[tid] = wrec_r;
   };
   // one window sub-chunk of n tokens on the running state (LDS staged)
-  auto window = [&](int seg, int sub) {
+  auto window = [&](int seg, int sub, int buf) {
+    const f16_t* sA = reinterpret_cast<const f16_t*>(warea(buf) + Cfg::W_A);
+    const float* sAS = reinterpret_cast<const float*>(warea(buf) + Cfg::W_AS);
+    const uint16_t* sKt = reinterpret_cast<const uint16_t*>(warea(buf) + Cfg::W_KT);
+    const float* sV = reinterpret_cast<const float*>(warea(buf) + Cfg::W_V);
+    const float* sRec = reinterpret_cast<const float*>(warea(buf) + Cfg::W_REC);
     const int n = min(SUB, a.w - sub * SUB);
     const int lane = opaque((int)threadIdx.x) & 63;
     const int h = lane >> 5, l32 = lane & 31;
@@ -1176,29 +1188,50 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   if (PAIRS) {
     issue_U(0);
     if (!ut) g_cur = a.g[pidx];
+  }
+  // window staging: window i + 1 goes to area (i + 1) & 1 while window i is
+  // in use, and the loads of window i + 2 are issued once i + 1 is staged
+  [[maybe_unused]] auto stage_next = [&](int wi) {
+    if (wi + 1 < n_win) {
+      stage_window((wi + 1) & 1);
+      if (wi + 2 < n_win) issue_window(wi + 2);
+    }
+  };
+  if constexpr (SEAM) {
+    issue_window(0);
+    stage_window(0);
+    if (n_win > 1) issue_window(1);
+  }
+  if (PAIRS) {
     split_U(0);
     if (nseg > 1) issue_U(1);
   }
-  if constexpr (SEAM) issue_window(0, 0);
-  if constexpr (!SEAM) __syncthreads();
+  __syncthreads();
 
   for (int seg = 0; seg < nseg; ++seg) {
     const bool more = seg + 1 < nseg;
+    const int wlast = seg * n_sub + n_sub - 1;  // the segment's last window
     if constexpr (SEAM) {
       for (int sub = 0; sub < n_sub; ++sub) {
-        stage_window();
-        __syncthreads();
-        if (sub + 1 < n_sub) issue_window(seg, sub + 1);
-        else if (more) issue_window(seg + 1, 0);
-        window(seg, sub);
-        if (sub + 1 < n_sub) __syncthreads();  // before the window area is staged again
+        const int wi = seg * n_sub + sub;
+        window(seg, sub, wi & 1);
+        if (sub + 1 < n_sub) {  // another window before the body: staged now
+          stage_next(wi);
+          __syncthreads();
+        }
       }
     }
     if (PAIRS) {
       const float g_nxt = (more && !ut) ? a.g[pidx + (size_t)(seg + 1) * n_chain] : 0.f;
-      body(ut ? 1.f : expf(g_cur), seg & 1, (seg + 1) & 1, min(seg + 2, nseg - 1), ut ? -1 : seg);
+      // (seam step: the next segment's first window is staged during the product)
+      auto hook = [&]() {
+        if constexpr (SEAM) stage_next(wlast);
+      };
+      body(ut ? 1.f : expf(g_cur), seg & 1, (seg + 1) & 1, min(seg + 2, nseg - 1), ut ? -1 : seg, hook);
       g_cur = g_nxt;
       if (more && !ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
+    } else if constexpr (SEAM) {
+      stage_next(wlast);
     }
     __syncthreads();  // every wave is done with this step's LDS
   }
