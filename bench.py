@@ -150,6 +150,44 @@ def ingest_counters(wl, fetch_csv: str, write_csv: str, steps: int, cmds):
     return db[workload]
 
 
+def counter_summary(paths):
+    """Markdown table of the library's kernels in rocprofv3 --pmc runs
+    (counter_collection.csv files, one pass each): per kernel, the mean of each
+    counter per dispatch, and per wave the VALU and MFMA instructions and the
+    fraction of wave cycles spent waiting on dependencies."""
+    import csv
+    import re
+    vals = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if "hypic" not in r["Kernel_Name"]:
+                    continue
+                name = re.sub(r"hypic::(\(anonymous namespace\)::)?", "", r["Kernel_Name"])
+                name = re.sub(r"\(.*", "", name).replace("void ", "")
+                key = (name, r["Counter_Name"])
+                d = vals.setdefault(key, {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    kernels = sorted({k for k, _ in vals})
+    counters = sorted({c for _, c in vals})
+    mean = {key: float(np.mean(list(d.values()))) for key, d in vals.items()}
+    lines = ["| counter | " + " | ".join("`%s`" % k for k in kernels) + " |",
+             "|---|" + "---|" * len(kernels)]
+    for c in counters:
+        lines.append("| %s | " % c + " | ".join("%.4g" % mean[(k, c)] if (k, c) in mean else "" for k in kernels)
+                     + " |")
+
+    def ratio(k, a, b):
+        return mean[(k, a)] / mean[(k, b)] if (k, a) in mean and mean.get((k, b)) else None
+    for label, a, b in (("VALU instructions per wave", "SQ_INSTS_VALU", "SQ_WAVES"),
+                        ("MFMA instructions per wave", "SQ_INSTS_MFMA", "SQ_WAVES"),
+                        ("LDS instructions per wave", "SQ_INSTS_LDS", "SQ_WAVES"),
+                        ("wave cycles waiting on dependencies", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")):
+        r = [ratio(k, a, b) for k in kernels]
+        lines.append("| *%s* | " % label + " | ".join("" if x is None else "%.3g" % x for x in r) + " |")
+    return "\n".join(lines)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -693,7 +731,12 @@ def main():
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="record HBM traffic of --workload from two rocprofv3 counter runs (no GPU needed)")
     ap.add_argument("--counter-commands", nargs="*", default=[], help="the rocprofv3 commands, for the record")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="print per-kernel means of rocprofv3 --pmc counter_collection.csv files and exit")
     args = ap.parse_args()
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
+        return
     if args.ingest_counters:
         wl = WORKLOADS[args.workload]()
         rec = ingest_counters(wl, args.ingest_counters[0], args.ingest_counters[1], args.steps,

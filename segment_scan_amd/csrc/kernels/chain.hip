@@ -894,26 +894,32 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     if ((threadIdx.x & 63) == 0) sEU[4 * b + wv] = eu;
     return eu;
   };
-  auto u_chunk = [&](int b, int i, float su) {
+  // the lane's place in split buffer b (slice i adds 2 i rows)
+  auto u_dst = [&](int b) {
     const int lane = opaque((int)threadIdx.x) & 63;
     const int c = lane & 31;
-    f16_t* dst = sU + b * (Cfg::UBUF / 2) + (32 * wv + 2 * i + (lane >> 5)) * UP + 16 * (c >> 2) + kperm(4 * (c & 3));
+    return sU + b * (Cfg::UBUF / 2) + (32 * wv + (lane >> 5)) * UP + 16 * (c >> 2) + kperm(4 * (c & 3));
+  };
+  auto u_chunk = [&](f16_t* dst, int i, float su) {
     const H4<NT> f = split4h_scaled<NT>(ur[i], su);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) *reinterpret_cast<f16x4*>(dst + t * D * UP) = f.t[t];
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f16x4*>(dst + (t * D + 2 * i) * UP) = f.t[t];
   };
-  // one slice of U of pair s reloaded (after its split)
-  auto reload_U = [&](int s, int i) {
-    const auto rs = buffer_rsrc(a.U + (size_t)s * seg_stride + pair_off, MAT);
+  // the lane's offset in a slice load of U
+  auto u_voff = [&]() {
     const int lane = opaque((int)threadIdx.x) & 63;
-    const uint32_t vo = (uint32_t)(((lane >> 5) * D + 4 * (lane & 31)) * 4);
+    return (uint32_t)(((lane >> 5) * D + 4 * (lane & 31)) * 4);
+  };
+  // one slice of U of a pair reloaded (after its split)
+  auto reload_U = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, int i) {
     const uint4 v = buffer_load16(rs, vo, (uint32_t)((32 * wv + 2 * i) * D * 4));
     ur[i] = f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
   };
   auto split_U = [&](int b) {
     const float su = ldexpf(1.f, -u_exp(b));
+    f16_t* dst = u_dst(b);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) u_chunk(b, i, su);
+    for (int i = 0; i < 16; ++i) u_chunk(dst, i, su);
   };
 
   // exponent of the lane's column: its 64 values and the partner lane's, times f
@@ -925,6 +931,14 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
       for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(St[rt][r]));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     return min(max(split_exp(m * f), -100), 100);
+  };
+  // k step ks of the state as a one-term B fragment, times sc (the window
+  // products feed outputs and updates of bf16-token precision)
+  auto state_frag1 = [&](int ks, float sc) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = St[ks >> 1][8 * (ks & 1) + j];
+    return split8h_scaled<1>(x, sc);
   };
   // k step ks of the state as an NT-term B fragment, times sc
   auto state_frag = [&](int ks, float sc) {
@@ -947,6 +961,9 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     const int ec = col_exp(f);
     const float sc = f * ldexpf(1.f, -ec);
     const float su = ldexpf(1.f, -u_exp(nxt));
+    f16_t* udst = u_dst(nxt);
+    const auto u_rs = buffer_rsrc(a.U + (size_t)s2 * seg_stride + pair_off, MAT);
+    const uint32_t u_vo = u_voff();
     f32x16 T[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) T[rt] = zero16();
@@ -978,8 +995,8 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
       for (int rt = 0; rt < 4; ++rt) mmah<NT, NT>(T[rt], fa[ks & 1][rt], fb[ks & 1]);
 #pragma unroll
       for (int i = 2 * ks; i < 2 * ks + 2; ++i) {
-        u_chunk(nxt, i, su);
-        reload_U(s2, i);
+        u_chunk(udst, i, su);
+        reload_U(u_rs, u_vo, i);
       }
       if (ks == 3) hook();
       // issue order inside the k step: every MFMA followed by a few of the
@@ -1088,7 +1105,11 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     if (tid < SEAM_REC_FLOATS) sRec[tid] = wrec_r;
   };
   // one window sub-chunk of n tokens on the running state (LDS staged)
-  auto window = [&](int seg, int sub, int buf) {
+  // With fold (a body pair follows) the update is left as S + K^T R' / e^{G_n}
+  // and e^{G_n} is returned for the body's state scale, saving the multiply of
+  // every state element (unless e^{G_n} is so small that 1 / e^{G_n} could
+  // overflow); else e^{G_n} is applied here and 1 returned.
+  auto window = [&](int seg, int sub, int buf, bool fold) {
     const f16_t* sA = reinterpret_cast<const f16_t*>(warea(buf) + Cfg::W_A);
     const float* sAS = reinterpret_cast<const float*>(warea(buf) + Cfg::W_AS);
     const uint16_t* sKt = reinterpret_cast<const uint16_t*>(warea(buf) + Cfg::W_KT);
@@ -1104,11 +1125,11 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
       const f16_t* pa = sA + (l32 & 15) * UP + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const HFrag<NT> fb = state_frag(ks, sc);
+        const HFrag<1> fb = state_frag1(ks, sc);
         HFrag<1> fa;
         fa.t[0] = *reinterpret_cast<const f16x8*>(pa + 16 * ks);
         if (l32 >= 2 * SUB) fa.t[0] = f16x8{};
-        mmah<1, NT>(XP, fa, fb);
+        mmah<1, 1>(XP, fa, fb);
       }
     }
     // elements j < 4: X of token 4h + j; elements 4 + j: P of token 4h + j
@@ -1154,22 +1175,29 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     }
     // S <- exp(G_n) S + K^T R' (k = the 8 tokens in lane half 0; half 1 zeros)
     const float eGn = sRec[2 * SUB * SUB + SUB];
+    const bool folded = fold && eGn >= 0x1p-60f;  // (uniform)
+    const float rs = folded ? 1.f / eGn : 1.f;
     Frag<2> fb;
     {
       float x[8];
 #pragma unroll
-      for (int t = 0; t < SUB; ++t) x[t] = h ? 0.f : acc[t];
+      for (int t = 0; t < SUB; ++t) x[t] = h ? 0.f : acc[t] * rs;
       fb = split8<2>(x);
+    }
+    if (!folded) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) St[rt][r] *= eGn;
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       Frag<1> fa;
       fa.t[0] = *reinterpret_cast<const bf16x8*>(sKt + (32 * rt + l32) * SUB);
       if (h) fa.t[0] = bf16x8{};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) St[rt][r] *= eGn;
       mma<1, 2>(St[rt], fa, fb);
     }
+    return folded ? eGn : 1.f;
   };
 
   // ---- start state, first loads --------------------------------------------------------
@@ -1211,10 +1239,11 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   for (int seg = 0; seg < nseg; ++seg) {
     const bool more = seg + 1 < nseg;
     const int wlast = seg * n_sub + n_sub - 1;  // the segment's last window
+    float wfac = 1.f;                           // gate factor the last window left to the body
     if constexpr (SEAM) {
       for (int sub = 0; sub < n_sub; ++sub) {
         const int wi = seg * n_sub + sub;
-        window(seg, sub, wi & 1);
+        wfac = window(seg, sub, wi & 1, PAIRS && sub + 1 == n_sub);
         if (sub + 1 < n_sub) {  // another window before the body: staged now
           stage_next(wi);
           __syncthreads();
@@ -1227,7 +1256,7 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
       auto hook = [&]() {
         if constexpr (SEAM) stage_next(wlast);
       };
-      body(ut ? 1.f : expf(g_cur), seg & 1, (seg + 1) & 1, min(seg + 2, nseg - 1), ut ? -1 : seg, hook);
+      body(ut ? 1.f : expf(g_cur) * wfac, seg & 1, (seg + 1) & 1, min(seg + 2, nseg - 1), ut ? -1 : seg, hook);
       g_cur = g_nxt;
       if (more && !ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
     } else if constexpr (SEAM) {
