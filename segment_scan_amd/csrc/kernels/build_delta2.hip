@@ -65,11 +65,20 @@ __device__ __forceinline__ f16x8 lds_a_perm_h(const f16_t* p, int off) {
 }
 
 // Elements 8m .. 8m+7 of an accumulator tile, times the wave-uniform s, as an
-// fp16 B fragment (always multiplied: no branch separates the products).
+// fp16 B fragment.
 __device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, float s) {
   f16x8 f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = (f16_t)(acc[8 * m + j] * s);
+  return f;
+}
+// The same for s = 1 (NEG: s = -1): the conversion alone, the sign a source
+// modifier.  Blocks whose power-of-two scale is 1 -- the usual case -- take it.
+template <bool NEG>
+__device__ __forceinline__ f16x8 acc_as_b_unit(const f32x16& acc, int m) {
+  f16x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (f16_t)(NEG ? -acc[8 * m + j] : acc[8 * m + j]);
   return f;
 }
 
@@ -449,19 +458,35 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(Z[rt][r]));
         const float gz = s_wave ? eGC : 1.f;
         const int ez = f16_scale_exp(wave_max_uniform(m) * gz);
-        const float sz = gz * ldexpf(1.f, -ez);
+        // delta mode, U waves: -Z, so that X' comes out with its sign (U <- U - K^T A0 K U)
+        const float sz = KDA ? gz * ldexpf(1.f, -ez) : (s_wave ? 1.f : -1.f) * gz * ldexpf(1.f, -ez);
         fez = KDA ? 1.f : ldexpf(1.f, ez);
         const f16_t* pK = sK + l32 * KP + 4 * h;
         W[0] = zero16();
         W[1] = zero16();
+        // (delta mode, U waves with scale 1: the conversion alone, sign as a modifier)
+        const bool unit = !KDA && !s_wave && ez == 0;
+        if (unit) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+          for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const f16x8 fb = acc_as_b_h(Z[rt], mm, sz);
+            for (int mm = 0; mm < 2; ++mm) {
+              const f16x8 fb = acc_as_b_unit<true>(Z[rt], mm);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
-          }
+              for (int tt = 0; tt < 2; ++tt)
+                W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
+            }
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+              const f16x8 fb = acc_as_b_h(Z[rt], mm, sz);
+#pragma unroll
+              for (int tt = 0; tt < 2; ++tt)
+                W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
+            }
+        }
         if (KDA && ez != 0) {
           const float f = ldexpf(1.f, ez);
 #pragma unroll
@@ -512,7 +537,8 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
             for (int tt = tp; tt < 2; ++tt)
               W[tt] = mfma32h(lds_a_perm_h(pA, 32 * tt * TP + 32 * tp + 16 * mm), fb[tp][mm], W[tt]);
         // X' = W f_er (times the row scales of A0 unless all are 1)
-        f_er = (s_wave ? 1.f : -1.f) * ldexpf(1.f, er) * ((KDA || s_wave) ? 1.f : fez);
+        if constexpr (KDA) f_er = (s_wave ? 1.f : -1.f) * ldexpf(1.f, er);
+        else f_er = ldexpf(1.f, er) * (s_wave ? 1.f : fez);
         if (KDA || sF[2 * C + 1] == 0.f) {
           const float* fac = sF + C + 4 * h;
 #pragma unroll
