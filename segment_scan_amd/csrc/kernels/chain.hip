@@ -788,7 +788,9 @@ struct WideCfg {
   static constexpr int W_REC = W_V + SUB * D * 4;              // the window record
   static constexpr int WBUF = W_REC + SEAM_REC_FLOATS * 4;
   static constexpr int OFF_W = OFF_EU + 32;
-  static constexpr int LDS = SEAM ? OFF_W + 2 * WBUF : OFF_W;
+  static constexpr int OFF_Z = OFF_W + 2 * WBUF;                // a zero row, read by the lanes whose
+  static constexpr int ZROW = UP * 2;                          // operand rows are padding
+  static constexpr int LDS = SEAM ? OFF_Z + ZROW : OFF_W;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -1122,13 +1124,12 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     const float sc = ldexpf(1.f, -ec);
     f32x16 XP = zero16();
     {
-      const f16_t* pa = sA + (l32 & 15) * UP + 8 * h;
+      const f16_t* pa = (l32 < 2 * SUB ? sA + l32 * UP : reinterpret_cast<const f16_t*>(smem + Cfg::OFF_Z)) + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const HFrag<1> fb = state_frag1(ks, sc);
         HFrag<1> fa;
         fa.t[0] = *reinterpret_cast<const f16x8*>(pa + 16 * ks);
-        if (l32 >= 2 * SUB) fa.t[0] = f16x8{};
         mmah<1, 1>(XP, fa, fb);
       }
     }
@@ -1190,11 +1191,12 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) St[rt][r] *= eGn;
     }
+    const uint16_t* pk = h ? reinterpret_cast<const uint16_t*>(smem + Cfg::OFF_Z) : sKt + l32 * SUB;
+    const int pk_step = h ? 0 : 32 * SUB;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       Frag<1> fa;
-      fa.t[0] = *reinterpret_cast<const bf16x8*>(sKt + (32 * rt + l32) * SUB);
-      if (h) fa.t[0] = bf16x8{};
+      fa.t[0] = *reinterpret_cast<const bf16x8*>(pk + rt * pk_step);
       mma<1, 2>(St[rt], fa, fb);
     }
     return folded ? eGn : 1.f;
@@ -1226,6 +1228,7 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     }
   };
   if constexpr (SEAM) {
+    if (threadIdx.x < Cfg::ZROW / 4) reinterpret_cast<float*>(smem + Cfg::OFF_Z)[threadIdx.x] = 0.f;
     issue_window(0);
     stage_window(0);
     if (n_win > 1) issue_window(1);
