@@ -47,7 +47,7 @@
 #include "common.h"
 #include "../launch.h"
 
-// state tiles per workgroup of the seam step with bf16 tokens (1, 2 or 4)
+// state tiles per workgroup of the d = 64 seam step with bf16 tokens (1 or 2)
 #ifndef HYPIC_SEAM_NCT
 #define HYPIC_SEAM_NCT 2
 #endif
@@ -756,16 +756,17 @@ __global__ __launch_bounds__(64 * (D / 32), (chain_min_waves<D, NCT, NT, SEAM, I
 // whose k order (rows 16m + 8(j >> 2) + 4h + (j & 3)) the A operand matches
 // (common.h), so the state never goes through LDS and each column's scale is
 // lane-local.  U is the A operand: each step wave rb splits rows 32 rb ..
-// 32 rb + 31 (prefetched into registers a step ahead, 1 KB per load
-// instruction) into NT fp16 terms in LDS with one power of two per row block,
-// and every wave reads all of U from there.  The split rows are stored with
-// bits 2 and 3 of k swapped inside each 16-wide block, so that an A fragment
-// in the accumulator's k order is one 16-byte read.  The split is software
-// pipelined: two split-U buffers, the body product of pair s reading one while
-// the waves split pair s + 1 into the other between its MFMAs, each register
-// slice reloaded with pair s + 2 as soon as it is split; the next pair's S_B
-// and gate are loaded a step ahead.  One workgroup per CU thus keeps about two
-// pairs' bytes in flight, and a composition step has one barrier.
+// 32 rb + 31 (loaded into registers a step ahead, 1 KB per load instruction)
+// into NT fp16 terms in LDS with one power of two per row block, and every
+// wave reads all of U from there.  The split rows are stored with bits 2 and 3
+// of k swapped inside each 16-wide block, so that an A fragment in the
+// accumulator's k order is one 16-byte read.  Two workgroups share a CU (one
+// split buffer and one window area each, about 80 KB of LDS): while one waits
+// on a barrier, an LDS read or the S_B loads after its product, the other's
+// MFMA and VALU work runs.  (One workgroup per CU with two split buffers, the
+// next pair split between the MFMAs of the current product, measured 10 %
+// slower on the seam step: per wave it issues the same VALU work and hides
+// less of its waiting.)
 //
 // Seam windows (bf16 tokens): [X; P] = [K; Q] S on 32x32x16 MFMA (K rows 0..7,
 // Q rows 8..15 of A; the upper 16 rows zero); each lane then holds X and P of
@@ -777,21 +778,20 @@ struct WideCfg {
   static constexpr int D = 128;
   static constexpr int NTH = 256;
   static constexpr int UP = D + 8;  // fp16 pitch of a split row: 272 bytes, 16-byte reads free of bank conflicts
-  static constexpr int UBUF = NT * D * UP * 2;                // bytes of one split U: [NT][D][UP] f16
-  static constexpr int OFF_U = 0;                              // two of them: pairs s and s + 1
-  static constexpr int OFF_EU = OFF_U + 2 * UBUF;              // [2][4] int: row-block exponents
-  // two window areas (window i in area i & 1), each:
+  static constexpr int OFF_U = 0;                              // split U: [NT][D][UP] f16
+  static constexpr int OFF_EU = OFF_U + NT * D * UP * 2;       // [4] int: row-block exponents
+  // the window area:
   static constexpr int W_A = 0;                                // [2 SUB][UP] f16: K, Q rows, scaled
   static constexpr int W_AS = W_A + 2 * SUB * UP * 2;          // [2 SUB] f32: 2^e of those rows
   static constexpr int W_KT = W_AS + 2 * SUB * 4;              // [D][SUB] bf16: K^T
   static constexpr int W_V = W_KT + D * SUB * 2;               // [SUB][D] f32
   static constexpr int W_REC = W_V + SUB * D * 4;              // the window record
   static constexpr int WBUF = W_REC + SEAM_REC_FLOATS * 4;
-  static constexpr int OFF_W = OFF_EU + 32;
-  static constexpr int OFF_Z = OFF_W + 2 * WBUF;                // a zero row, read by the lanes whose
+  static constexpr int OFF_W = OFF_EU + 16;
+  static constexpr int OFF_Z = OFF_W + WBUF;                   // a zero row, read by the lanes whose
   static constexpr int ZROW = UP * 2;                          // operand rows are padding
   static constexpr int LDS = SEAM ? OFF_Z + ZROW : OFF_W;
-  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
 };
 
 // position of k offset o (0..15) inside its 16-wide block: bits 2 and 3 swapped
@@ -828,7 +828,7 @@ __device__ __forceinline__ void buffer_store4(float v, __amdgpu_buffer_rsrc_t r,
 }
 
 template <int NT, bool SEAM, bool PAIRS>
-__global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
+__global__ __launch_bounds__(256, 2) void chain_wide_kernel(const ChainArgs a) {
   using Cfg = WideCfg<NT, SEAM>;
   constexpr int D = 128, UP = Cfg::UP;
   constexpr uint32_t MAT = D * D * 4;  // bytes of one [D][D] fp32 matrix
@@ -849,7 +849,7 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   const int wv = wave_id_uniform();  // columns 32 wv .. (and U rows 32 wv .. for the split)
 
   // ---- the state tiles: element r of tile rt is row 32 rt + acc_row(r), column 32 wv + l32
-  f32x16 St[4], SB[4];
+  f32x16 St[4];
   auto tile_voff = [&]() {
     const int lane = opaque((int)threadIdx.x) & 63;
     return (uint32_t)(((4 * (lane >> 5)) * D + 32 * wv + (lane & 31)) * 4);
@@ -884,44 +884,26 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
       ur[i] = f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
     }
   };
-  // split into LDS buffer b (NT fp16 terms, k permuted inside 16-blocks) with
-  // the row block's power of two: u_exp() once, then u_chunk(i) for each slice
-  auto u_exp = [&](int b) {
+  // split into LDS (NT fp16 terms, k permuted inside 16-blocks) with the row
+  // block's power of two
+  auto split_U = [&]() {
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(ur[i][j]));
     const int eu = min(max(split_exp(wave_max_uniform(m)), -100), 100);
-    if ((threadIdx.x & 63) == 0) sEU[4 * b + wv] = eu;
-    return eu;
-  };
-  // the lane's place in split buffer b (slice i adds 2 i rows)
-  auto u_dst = [&](int b) {
+    if ((threadIdx.x & 63) == 0) sEU[wv] = eu;
+    const float su = ldexpf(1.f, -eu);
     const int lane = opaque((int)threadIdx.x) & 63;
     const int c = lane & 31;
-    return sU + b * (Cfg::UBUF / 2) + (32 * wv + (lane >> 5)) * UP + 16 * (c >> 2) + kperm(4 * (c & 3));
-  };
-  auto u_chunk = [&](f16_t* dst, int i, float su) {
-    const H4<NT> f = split4h_scaled<NT>(ur[i], su);
+    f16_t* dst = sU + (32 * wv + (lane >> 5)) * UP + 16 * (c >> 2) + kperm(4 * (c & 3));
 #pragma unroll
-    for (int t = 0; t < NT; ++t) *reinterpret_cast<f16x4*>(dst + (t * D + 2 * i) * UP) = f.t[t];
-  };
-  // the lane's offset in a slice load of U
-  auto u_voff = [&]() {
-    const int lane = opaque((int)threadIdx.x) & 63;
-    return (uint32_t)(((lane >> 5) * D + 4 * (lane & 31)) * 4);
-  };
-  // one slice of U of a pair reloaded (after its split)
-  auto reload_U = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, int i) {
-    const uint4 v = buffer_load16(rs, vo, (uint32_t)((32 * wv + 2 * i) * D * 4));
-    ur[i] = f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
-  };
-  auto split_U = [&](int b) {
-    const float su = ldexpf(1.f, -u_exp(b));
-    f16_t* dst = u_dst(b);
+    for (int i = 0; i < 16; ++i) {  // slice i: rows 32 wv + 2 i + (lane >> 5)
+      const H4<NT> f = split4h_scaled<NT>(ur[i], su);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) u_chunk(dst, i, su);
+      for (int t = 0; t < NT; ++t) *reinterpret_cast<f16x4*>(dst + (t * D + 2 * i) * UP) = f.t[t];
+    }
   };
 
   // exponent of the lane's column: its 64 values and the partner lane's, times f
@@ -951,87 +933,53 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   };
 
   // ---- body pair: S <- exp(g) U S + S_B (U_total <- U U_total) ----------------------
-  // From split buffer cur, while the registers' pair (the next one) is split
-  // into buffer nxt between the MFMAs and each of its slices is then reloaded
-  // with pair s2.  On the last steps this split and reload are repeated work on
-  // a buffer nobody reads and a pair already loaded: no branch in the loop.
-  // The A fragments of k step ks + 1 are read while step ks multiplies.
-  auto body = [&](float f, int cur, int nxt, int s2, int sb, auto&& hook) {
-    // (sb < 0: a resource of no bytes, whose loads return zeros and read nothing,
-    // so no branch splits the loop)
-    const auto sb_rs = buffer_rsrc(a.S + (size_t)max(sb, 0) * seg_stride + pair_off, sb >= 0 ? MAT : 0u);
+  // The product from the split U; then S_B of pair sb (sb < 0: none), its 64
+  // loads in flight together.
+  auto body = [&](float f, int sb) {
     const int ec = col_exp(f);
     const float sc = f * ldexpf(1.f, -ec);
-    const float su = ldexpf(1.f, -u_exp(nxt));
-    f16_t* udst = u_dst(nxt);
-    const auto u_rs = buffer_rsrc(a.U + (size_t)s2 * seg_stride + pair_off, MAT);
-    const uint32_t u_vo = u_voff();
     f32x16 T[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) T[rt] = zero16();
     const int lane = opaque((int)threadIdx.x) & 63;
-    const f16_t* pa = sU + cur * (Cfg::UBUF / 2) + (lane & 31) * UP + 8 * (lane >> 5);
-    HFrag<NT> fa[2][4];
-    auto read_a = [&](HFrag<NT>(&dst)[4], int ks) {
+    const f16_t* pa = sU + (lane & 31) * UP + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const HFrag<NT> fb = state_frag(ks, sc);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        HFrag<NT> fa;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) fa.t[t] = *reinterpret_cast<const f16x8*>(pa + (t * D + 32 * rt) * UP + 16 * ks);
+        mmah<NT, NT>(T[rt], fa, fb);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int e = sEU[rt] + ec;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) St[rt][r] = ldexpf(T[rt][r], e);
+    }
+    if (sb >= 0) {
+      const auto rs = buffer_rsrc(a.S + (size_t)sb * seg_stride + pair_off, MAT);
+      const uint32_t vo = tile_voff();
+      f32x16 SB[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          dst[rt].t[t] = *reinterpret_cast<const f16x8*>(pa + (t * D + 32 * rt) * UP + 16 * ks);
-    };
-    HFrag<NT> fb[2];
-    read_a(fa[0], 0);
-    fb[0] = state_frag(0, sc);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (ks + 1 < 8) {
-        read_a(fa[(ks + 1) & 1], ks + 1);
-        fb[(ks + 1) & 1] = state_frag(ks + 1, sc);
-      }
-      if (ks < 4) {  // S_B tile ks: its loads spread over the k steps, not one burst
-        const uint32_t vo = tile_voff();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) SB[ks][r] = __uint_as_float(buffer_load4(sb_rs, vo, tile_soff(ks, r)));
-      }
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) mmah<NT, NT>(T[rt], fa[ks & 1][rt], fb[ks & 1]);
-#pragma unroll
-      for (int i = 2 * ks; i < 2 * ks + 2; ++i) {
-        u_chunk(udst, i, su);
-        reload_U(u_rs, u_vo, i);
-      }
-      if (ks == 3) hook();
-      // issue order inside the k step: every MFMA followed by a few of the
-      // step's independent VALU instructions (the next fragments and the
-      // split), so that they run in the MFMAs' shadow instead of after them
-#pragma unroll
-      for (int m = 0; m < 4 * (NT * (NT + 1) / 2); ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
+        for (int r = 0; r < 16; ++r) SB[rt][r] = __uint_as_float(buffer_load4(rs, vo, tile_soff(rt, r)));
       sched_fence();
-    }
-    if (ut) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int e = sEU[4 * cur + rt] + ec;
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) St[rt][r] = ldexpf(T[rt][r], e);
-      }
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int e = sEU[4 * cur + rt] + ec;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) St[rt][r] = ldexpf(T[rt][r], e) + SB[rt][r];
-      }
+        for (int r = 0; r < 16; ++r) St[rt][r] += SB[rt][r];
     }
   };
 
   // ---- seam windows ------------------------------------------------------------------
-  auto warea = [&](int buf) { return smem + Cfg::OFF_W + buf * Cfg::WBUF; };
-  const int n_sub = SEAM ? (a.w + SUB - 1) / SUB : 0;
-  const int n_win = n_sub * nseg;  // windows in order: i = seg * n_sub + sub
+  unsigned char* const warea = smem + Cfg::OFF_W;
+  const int n_sub = SEAM ? (a.w + SUB - 1) / SUB : 1;
+  const int n_win = SEAM ? n_sub * nseg : 0;  // windows in order: i = seg * n_sub + sub
   uint4 wraw[2];  // chunk tid: 8 values of a K (rows 0..7) or Q row; chunk 256 + tid: of a V row
   float wrec_r = 0.f;
   const uint32_t tok_stride = (uint32_t)n_chain * D;
@@ -1052,12 +1000,12 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
     const float* rec = a.wrec + ((size_t)(seg * n_sub + sub) * n_chain + chain) * SEAM_REC_FLOATS;
     if (tid < SEAM_REC_FLOATS) wrec_r = rec[tid];
   };
-  auto stage_window = [&](int buf) {
-    f16_t* sA = reinterpret_cast<f16_t*>(warea(buf) + Cfg::W_A);
-    float* sAS = reinterpret_cast<float*>(warea(buf) + Cfg::W_AS);
-    uint16_t* sKt = reinterpret_cast<uint16_t*>(warea(buf) + Cfg::W_KT);
-    float* sV = reinterpret_cast<float*>(warea(buf) + Cfg::W_V);
-    float* sRec = reinterpret_cast<float*>(warea(buf) + Cfg::W_REC);
+  auto stage_window = [&]() {
+    f16_t* sA = reinterpret_cast<f16_t*>(warea + Cfg::W_A);
+    float* sAS = reinterpret_cast<float*>(warea + Cfg::W_AS);
+    uint16_t* sKt = reinterpret_cast<uint16_t*>(warea + Cfg::W_KT);
+    float* sV = reinterpret_cast<float*>(warea + Cfg::W_V);
+    float* sRec = reinterpret_cast<float*>(warea + Cfg::W_REC);
     const int tid = opaque((int)threadIdx.x);
     const int row = tid >> 4, d8 = tid & 15, t = row & (SUB - 1);
     const uint32_t u[4] = {wraw[0].x, wraw[0].y, wraw[0].z, wraw[0].w};
@@ -1111,12 +1059,12 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
   // and e^{G_n} is returned for the body's state scale, saving the multiply of
   // every state element (unless e^{G_n} is so small that 1 / e^{G_n} could
   // overflow); else e^{G_n} is applied here and 1 returned.
-  auto window = [&](int seg, int sub, int buf, bool fold) {
-    const f16_t* sA = reinterpret_cast<const f16_t*>(warea(buf) + Cfg::W_A);
-    const float* sAS = reinterpret_cast<const float*>(warea(buf) + Cfg::W_AS);
-    const uint16_t* sKt = reinterpret_cast<const uint16_t*>(warea(buf) + Cfg::W_KT);
-    const float* sV = reinterpret_cast<const float*>(warea(buf) + Cfg::W_V);
-    const float* sRec = reinterpret_cast<const float*>(warea(buf) + Cfg::W_REC);
+  auto window = [&](int seg, int sub, bool fold) {
+    const f16_t* sA = reinterpret_cast<const f16_t*>(warea + Cfg::W_A);
+    const float* sAS = reinterpret_cast<const float*>(warea + Cfg::W_AS);
+    const uint16_t* sKt = reinterpret_cast<const uint16_t*>(warea + Cfg::W_KT);
+    const float* sV = reinterpret_cast<const float*>(warea + Cfg::W_V);
+    const float* sRec = reinterpret_cast<const float*>(warea + Cfg::W_REC);
     const int n = min(SUB, a.w - sub * SUB);
     const int lane = opaque((int)threadIdx.x) & 63;
     const int h = lane >> 5, l32 = lane & 31;
@@ -1214,58 +1162,43 @@ __global__ __launch_bounds__(256, 1) void chain_wide_kernel(const ChainArgs a) {
         St[rt][r] = (ut && 32 * rt + acc_row(r, lane) == 32 * wv + (lane & 31)) ? 1.f : 0.f;
   }
   if (!ut && a.prefix) store_tiles(a.prefix + pair_off);  // prefix states follow the pairs' layout
-  float g_cur = 0.f;
-  if (PAIRS) {
-    issue_U(0);
-    if (!ut) g_cur = a.g[pidx];
-  }
-  // window staging: window i + 1 goes to area (i + 1) & 1 while window i is
-  // in use, and the loads of window i + 2 are issued once i + 1 is staged
-  [[maybe_unused]] auto stage_next = [&](int wi) {
-    if (wi + 1 < n_win) {
-      stage_window((wi + 1) & 1);
-      if (wi + 2 < n_win) issue_window(wi + 2);
-    }
-  };
+  // Each step: stage the step's first window and split U (loaded a step ahead),
+  // then the windows, then the body pair.  Window i + 1 is loaded while window
+  // i is in use.
   if constexpr (SEAM) {
     if (threadIdx.x < Cfg::ZROW / 4) reinterpret_cast<float*>(smem + Cfg::OFF_Z)[threadIdx.x] = 0.f;
     issue_window(0);
-    stage_window(0);
-    if (n_win > 1) issue_window(1);
   }
-  if (PAIRS) {
-    split_U(0);
-    if (nseg > 1) issue_U(1);
-  }
-  __syncthreads();
-
+  if (PAIRS) issue_U(0);
   for (int seg = 0; seg < nseg; ++seg) {
-    const bool more = seg + 1 < nseg;
-    const int wlast = seg * n_sub + n_sub - 1;  // the segment's last window
-    float wfac = 1.f;                           // gate factor the last window left to the body
+    const float g_cur = (PAIRS && !ut) ? a.g[pidx + (size_t)seg * n_chain] : 0.f;
+    __syncthreads();  // every wave is done with the previous step's LDS
+    if constexpr (SEAM) {
+      stage_window();
+      if (seg * n_sub + 1 < n_win) issue_window(seg * n_sub + 1);
+    }
+    if (PAIRS) {
+      split_U();
+      if (seg + 1 < nseg) issue_U(seg + 1);  // in flight during this step
+    }
+    __syncthreads();
+    float wfac = 1.f;  // gate factor the last window leaves to the body
     if constexpr (SEAM) {
       for (int sub = 0; sub < n_sub; ++sub) {
         const int wi = seg * n_sub + sub;
-        wfac = window(seg, sub, wi & 1, PAIRS && sub + 1 == n_sub);
-        if (sub + 1 < n_sub) {  // another window before the body: staged now
-          stage_next(wi);
+        wfac = window(seg, sub, PAIRS && sub + 1 == n_sub);
+        if (sub + 1 < n_sub) {
+          __syncthreads();
+          stage_window();
+          if (wi + 2 < n_win) issue_window(wi + 2);
           __syncthreads();
         }
       }
     }
     if (PAIRS) {
-      const float g_nxt = (more && !ut) ? a.g[pidx + (size_t)(seg + 1) * n_chain] : 0.f;
-      // (seam step: the next segment's first window is staged during the product)
-      auto hook = [&]() {
-        if constexpr (SEAM) stage_next(wlast);
-      };
-      body(ut ? 1.f : expf(g_cur) * wfac, seg & 1, (seg + 1) & 1, min(seg + 2, nseg - 1), ut ? -1 : seg, hook);
-      g_cur = g_nxt;
-      if (more && !ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
-    } else if constexpr (SEAM) {
-      stage_next(wlast);
+      body(ut ? 1.f : expf(g_cur) * wfac, ut ? -1 : seg);
+      if (seg + 1 < nseg && !ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
     }
-    __syncthreads();  // every wave is done with this step's LDS
   }
 
   store_tiles((ut ? a.U_tot : a.S_out) + unit_off);
@@ -1451,7 +1384,6 @@ hipError_t launch_seam_chain(int d, bool in_f32, const SeamArgs& s, hipStream_t 
   a.w = s.w;
   // bf16 tokens: two fp16 terms per body operand (the outputs are of bf16
   // input precision); fp32 tokens: three
-  constexpr int NCT128 = HYPIC_SEAM_NCT;
   constexpr int NCT64 = HYPIC_SEAM_NCT > 2 ? 2 : HYPIC_SEAM_NCT;
   if (d == 128) {
     if (in_f32) return launch_chain_t<128, 1, 3, true, true>(a, false, stream);
