@@ -166,15 +166,26 @@ __device__ __forceinline__ float mul_opaque(float x, float s) {
 // The same for x s with s a power of two, exponent within fp32's normal range:
 // t0 = fp16(x s) and every residual exact in fp32 (each step one fused
 // multiply-add with an fp16 operand)
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+// fp16 of two products x s, one conversion instruction for the pair
+__device__ __forceinline__ f16x2_t cvt2h_scaled(float x0, float x1, float s) {
+  return __builtin_convertvector((f32x2_t){mul_opaque(x0, s), mul_opaque(x1, s)}, f16x2_t);
+}
+
 template <int N>
 __device__ __forceinline__ HFrag<N> split8h_scaled(const float (&x)[8], float s) {
   HFrag<N> f;
   float r[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const f16_t t = (f16_t)mul_opaque(x[j], s);
-    f.t[0][j] = t;
-    if (N > 1) r[j] = __builtin_fmaf(x[j], s, -(float)t);
+  for (int j = 0; j < 8; j += 2) {
+    const f16x2_t t = cvt2h_scaled(x[j], x[j + 1], s);
+    f.t[0][j] = t[0];
+    f.t[0][j + 1] = t[1];
+    if (N > 1) {
+      r[j] = __builtin_fmaf(x[j], s, -(float)t[0]);
+      r[j + 1] = __builtin_fmaf(x[j + 1], s, -(float)t[1]);
+    }
   }
 #pragma unroll
   for (int i = 1; i < N; ++i) {
@@ -807,10 +818,14 @@ __device__ __forceinline__ H4<N> split4h_scaled(const f32x4& x, float s) {
   H4<N> f;
   float r[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f16_t t = (f16_t)mul_opaque(x[j], s);
-    f.t[0][j] = t;
-    if (N > 1) r[j] = __builtin_fmaf(x[j], s, -(float)t);
+  for (int j = 0; j < 4; j += 2) {
+    const f16x2_t t = cvt2h_scaled(x[j], x[j + 1], s);
+    f.t[0][j] = t[0];
+    f.t[0][j + 1] = t[1];
+    if (N > 1) {
+      r[j] = __builtin_fmaf(x[j], s, -(float)t[0]);
+      r[j + 1] = __builtin_fmaf(x[j + 1], s, -(float)t[1]);
+    }
   }
 #pragma unroll
   for (int i = 1; i < N; ++i)
@@ -1169,18 +1184,21 @@ __global__ __launch_bounds__(256, 2) void chain_wide_kernel(const ChainArgs a) {
     if (threadIdx.x < Cfg::ZROW / 4) reinterpret_cast<float*>(smem + Cfg::OFF_Z)[threadIdx.x] = 0.f;
     issue_window(0);
   }
-  if (PAIRS) issue_U(0);
+  float g_cur = 0.f;
+  if (PAIRS) {
+    issue_U(0);
+    if (!ut) g_cur = a.g[pidx];
+  }
   for (int seg = 0; seg < nseg; ++seg) {
-    const float g_cur = (PAIRS && !ut) ? a.g[pidx + (size_t)seg * n_chain] : 0.f;
     __syncthreads();  // every wave is done with the previous step's LDS
-    if constexpr (SEAM) {
-      stage_window();
-      if (seg * n_sub + 1 < n_win) issue_window(seg * n_sub + 1);
-    }
-    if (PAIRS) {
-      split_U();
-      if (seg + 1 < nseg) issue_U(seg + 1);  // in flight during this step
-    }
+    // (the registers staged here were loaded a step ago; the next loads are
+    // issued after them, so that no wait for these covers the new ones)
+    if constexpr (SEAM) stage_window();
+    if (PAIRS) split_U();
+    const bool more = PAIRS && seg + 1 < nseg;
+    const float g_nxt = (more && !ut) ? a.g[pidx + (size_t)(seg + 1) * n_chain] : 0.f;
+    if (SEAM && seg * n_sub + 1 < n_win) issue_window(seg * n_sub + 1);
+    if (more) issue_U(seg + 1);  // in flight during this step
     __syncthreads();
     float wfac = 1.f;  // gate factor the last window leaves to the body
     if constexpr (SEAM) {
@@ -1199,6 +1217,7 @@ __global__ __launch_bounds__(256, 2) void chain_wide_kernel(const ChainArgs a) {
       body(ut ? 1.f : expf(g_cur) * wfac, ut ? -1 : seg);
       if (seg + 1 < nseg && !ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
     }
+    g_cur = g_nxt;
   }
 
   store_tiles((ut ? a.U_tot : a.S_out) + unit_off);
