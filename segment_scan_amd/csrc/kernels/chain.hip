@@ -950,6 +950,49 @@ __global__ __launch_bounds__(256, 2) void chain_wide_kernel(const ChainArgs a) {
   // ---- body pair: S <- exp(g) U S + S_B (U_total <- U U_total) ----------------------
   // The product from the split U; then S_B of pair sb (sb < 0: none), its 64
   // loads in flight together.
+  // Composition alone (one workgroup per CU when the chains are few): the
+  // state's B fragments are formed half by half, so that each half of the
+  // state registers takes S_B's tiles while the other half's product runs.
+  auto body_split = [&](float f, int sb) {
+    const int ec = col_exp(f);
+    const float sc = f * ldexpf(1.f, -ec);
+    // (sb < 0: a resource of no bytes, whose loads return zeros)
+    const auto rs = buffer_rsrc(a.S + (size_t)max(sb, 0) * seg_stride + pair_off, sb >= 0 ? MAT : 0u);
+    const uint32_t vo = tile_voff();
+    f32x16 T[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) T[rt] = zero16();
+    const int lane = opaque((int)threadIdx.x) & 63;
+    const f16_t* pa = sU + (lane & 31) * UP + 8 * (lane >> 5);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {  // k steps 4 hf .. 4 hf + 3 read state tiles 2 hf, 2 hf + 1
+      HFrag<NT> fb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fb[k] = state_frag(4 * hf + k, sc);
+#pragma unroll
+      for (int rt = 2 * hf; rt < 2 * hf + 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) St[rt][r] = __uint_as_float(buffer_load4(rs, vo, tile_soff(rt, r)));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          HFrag<NT> fa;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            fa.t[t] = *reinterpret_cast<const f16x8*>(pa + (t * D + 32 * rt) * UP + 16 * (4 * hf + k));
+          mmah<NT, NT>(T[rt], fa, fb[k]);
+        }
+        sched_fence();
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int e = sEU[rt] + ec;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) St[rt][r] = ldexpf(T[rt][r], e) + St[rt][r];
+    }
+  };
   auto body = [&](float f, int sb) {
     const int ec = col_exp(f);
     const float sc = f * ldexpf(1.f, -ec);
@@ -1214,7 +1257,8 @@ __global__ __launch_bounds__(256, 2) void chain_wide_kernel(const ChainArgs a) {
       }
     }
     if (PAIRS) {
-      body(ut ? 1.f : expf(g_cur) * wfac, ut ? -1 : seg);
+      if constexpr (SEAM) body(ut ? 1.f : expf(g_cur) * wfac, ut ? -1 : seg);
+      else body_split(ut ? 1.f : expf(g_cur), ut ? -1 : seg);
       if (seg + 1 < nseg && !ut && a.prefix) store_tiles(a.prefix + (size_t)(seg + 1) * seg_stride + pair_off);
     }
     g_cur = g_nxt;
