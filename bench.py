@@ -83,10 +83,10 @@ def measured_traffic(workload: str, kernel: str):
 # device kernels that make up each timed operation (substrings of their symbol names)
 KERNEL_SYMBOLS = {
     "build_delta": ["delta_prep_kernel", "delta_state_kernel", "build_delta_kernel"],
-    "build_compose": ["delta_prep_kernel", "delta_state_kernel", "chain_kernel"],
+    "build_compose": ["delta_prep_kernel", "delta_state_kernel", "chain_kernel", "chain_wide_kernel"],
     "build_sd": ["build_sd_kernel", "compose_elem_kernel"],
-    "seam": ["seam_prep_kernel", "chain_kernel"],
-    "compose": ["chain_kernel", "compose_elem_kernel"],
+    "seam": ["seam_prep_kernel", "chain_kernel", "chain_wide_kernel"],
+    "compose": ["chain_kernel", "chain_wide_kernel", "compose_elem_kernel"],
     "rerotate": ["rerotate_kernel"],
     "build_kda": ["kda_prep_kernel", "delta_state_kernel", "build_kda_kernel"],
     "seam_kda": ["seam_kda_kernel"],
@@ -185,6 +185,27 @@ def counter_summary(paths):
                         ("wave cycles waiting on dependencies", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")):
         r = [ratio(k, a, b) for k in kernels]
         lines.append("| *%s* | " % label + " | ".join("" if x is None else "%.3g" % x for x in r) + " |")
+    return "\n".join(lines)
+
+
+def trace_summary(path, top=8):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv: the
+    `top` kernels by total time, with calls, total, mean, min and max duration."""
+    import csv
+    import re
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"].replace("(anonymous namespace)::", "").replace("hypic::", "")
+            name = re.sub(r"\(.*", "", name).replace("void ", "")
+            rows.append((name[:80], int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
+                         float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[2])
+    lines = ["| kernel | calls | total ms | mean us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    for n, c, t, a, lo, hi, pct in rows[:top]:
+        lines.append("| `%s` | %d | %.3f | %.1f | %.1f | %.1f | %.1f |" % (n, c, t / 1e6, a / 1e3, lo / 1e3, hi / 1e3,
+                                                                          pct))
     return "\n".join(lines)
 
 
@@ -317,8 +338,8 @@ class PipelinedColdRequest(ColdRequest):
     build's (tokens in, pairs out) plus the final states."""
     name = "gdn_cold32k_pipelined"
     kernel = "build_compose"
-    op_dispatches = 14   # 4 x (factor pass, state pass, group composition) + final composition (x 2 for U)
-    step_dispatches = 14
+    op_dispatches = 13   # 4 x (factor pass, state pass, group composition) + final composition
+    step_dispatches = 13
 
     def __init__(self):
         super().__init__()
@@ -733,9 +754,14 @@ def main():
     ap.add_argument("--counter-commands", nargs="*", default=[], help="the rocprofv3 commands, for the record")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
                     help="print per-kernel means of rocprofv3 --pmc counter_collection.csv files and exit")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print the top kernels of a rocprofv3 --stats kernel_stats.csv and exit")
     args = ap.parse_args()
     if args.counter_summary:
         print(counter_summary(args.counter_summary))
+        return
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
         return
     if args.ingest_counters:
         wl = WORKLOADS[args.workload]()
