@@ -797,7 +797,7 @@ def main():
            "data": "synthetic", "config": wl.config(),
            "composed_segs_per_s": round(wl.composed / (ms_per_step / 1e3), 1),
            "roofline": roofline, "cpu_baseline": cpu}
-    if hasattr(wl, "extra"):
+    if hasattr(wl, "extra") and not args.copy_calibration:  # (the calibration copies end a counter run)
         out.update(wl.extra())
 
     # The metric's second half, composed segments per second, lives in the warm

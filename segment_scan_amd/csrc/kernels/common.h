@@ -192,6 +192,12 @@ __device__ __forceinline__ float wave_max(float x) {
 // The same with DPP moves inside each 16-lane row (swap neighbours, swap
 // pairs, mirror within 8, mirror within 16) and the four row maxima read into
 // scalar registers: no LDS traffic.  The result is wave-uniform.
+// x of lane + N within the lane's row of 16 (0 where that is past the row)
+template <int N>
+__device__ __forceinline__ float dpp_row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float dpp_max_step(float x, int ctrl_sel) {
   int y;
   const int xi = __builtin_bit_cast(int, x);
