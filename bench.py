@@ -10,6 +10,8 @@ accumulation -- every (segment, head) pair (T_C, S(C|0)) built concurrently
 (hypic_compose).  Other workloads (`--workload`):
   retnet        8 heads x 16 segments x 1024, scalar decay: build + compose
   gla           16 heads x 64 segments x 512, diagonal gates: build + compose
+  gdn_cold32k_fused   the cold request in one call, the composition folded into
+                the build as a tree (the last build workgroup at a node composes it)
   gdn_warm100k  30 layers x 16 heads, 196 cached segments, w = 8: seam step fused
                 with the composition of every cached body pair
   gdn_ragged32k the cold request with uneven segments (58 .. 2048 tokens)
@@ -61,7 +63,8 @@ KERNEL_SOURCES = {
 
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kernel] + ["segment_scan_amd/csrc/kernels/common.h"]:
+    for rel in KERNEL_SOURCES[kernel] + ["segment_scan_amd/csrc/kernels/common.h",
+                                         "segment_scan_amd/csrc/kernels/split_f16.h"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -83,7 +86,8 @@ def measured_traffic(workload: str, kernel: str):
 # device kernels that make up each timed operation (substrings of their symbol names)
 KERNEL_SYMBOLS = {
     "build_delta": ["delta_prep_kernel", "delta_state_kernel", "build_delta_kernel"],
-    "build_compose": ["delta_prep_kernel", "delta_state_kernel", "chain_kernel", "chain_wide_kernel"],
+    "build_compose": ["delta_prep_kernel", "delta_state_kernel", "chain_kernel", "chain_wide_kernel",
+                      "zero_ints_kernel"],
     "build_sd": ["build_sd_kernel", "compose_elem_kernel"],
     "seam": ["seam_prep_kernel", "chain_kernel", "chain_wide_kernel"],
     "compose": ["chain_kernel", "chain_wide_kernel", "compose_elem_kernel"],
@@ -363,6 +367,39 @@ class PipelinedColdRequest(ColdRequest):
         c = super().config()
         c.update(workload=self.name, step="hypic_seg_build_compose (2048 units in 4 groups of 16 segments, "
                                           "each group composed on a second stream while the next is built)")
+        return c
+
+
+class FusedColdRequest(PipelinedColdRequest):
+    """The cold GDN request in one call with the composition folded into the
+    build (hypic_seg_build_compose, fused schedule): each build workgroup counts
+    its pair's arrival at a node of a binary tree over the 64 segments of its
+    chain, and the last arrival at a node composes it.  The timed operation is
+    the whole call."""
+    name = "gdn_cold32k_fused"
+    kernel = "build_compose"
+    op_dispatches = 3    # counter reset, factor pass, state pass (with the composition)
+    step_dispatches = 3
+
+    def setup(self):
+        import torch
+        ColdRequest.setup(self)
+        n_ws = self.api.seg_build_compose_workspace_size(self.fam, self.offsets, self.H, self.d, torch.bfloat16,
+                                                         self.api.BC_FUSED)
+        self.ws = torch.empty(n_ws, device="cuda", dtype=torch.uint8)
+
+    def step(self, ev0, ev1):
+        ev0.record()
+        self.api.seg_build_compose(self.fam, self.offsets, self.k, self.v, self.beta, self.lg,
+                                   out=(self.g, self.U, self.S), S_out=self.S_out, mode=self.api.BC_FUSED,
+                                   workspace=self.ws)
+        ev1.record()
+
+    def config(self):
+        c = ColdRequest.config(self)
+        c.update(workload=self.name, step="hypic_seg_build_compose, fused schedule (2048 units; the composition "
+                                          "as a tree per chain, each node composed by the last build workgroup "
+                                          "to reach it)")
         return c
 
 
@@ -728,6 +765,7 @@ class WarmRerotate(Workload):
 WORKLOADS = {
     "gdn_cold32k": ColdRequest,
     "gdn_cold32k_pipelined": PipelinedColdRequest,
+    "gdn_cold32k_fused": FusedColdRequest,
     "retnet": lambda: ScalarOrDiag("retnet", 1, 16, 1024, 8, 128),
     "gla": lambda: ScalarOrDiag("gla", 2, 64, 512, 16, 128),
     "gdn_warm100k": WarmRequest,

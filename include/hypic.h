@@ -237,22 +237,34 @@ hypic_status hypic_compose(hypic_family fam, int n_seg, int n_chain, int d_k, in
  *                        be captured into a graph from it).  The library creates
  *                        that stream and its events once per host thread and
  *                        device, on the first call.
+ *   HYPIC_BC_FUSED       the composition folded into the build: the segments
+ *                        are the leaves of a binary tree per chain, and a build
+ *                        workgroup that has written its pair counts its arrival
+ *                        at the parent node (a device-wide atomic counter); the
+ *                        last arrival composes the node's two children and moves
+ *                        up, so composition overlaps the build with no workgroup
+ *                        waiting on another.  It applies to the delta family at
+ *                        d = 128 with bf16 tokens, segments of at most 2048
+ *                        tokens, two or more segments and no S_init; elsewhere
+ *                        the call runs the sequential schedule.  Calls that
+ *                        overlap on one workspace race.
  * On one MI355X the sequential schedule is the faster at the 32k-token cold
  * request's shape (the two phases share the CUs' slots when overlapped).
  *
  *   out            the built pairs, as for hypic_seg_build.
  *   S_init, S_out, g_total, U_total   as for hypic_compose (no prefix states).
- *   mode           HYPIC_BC_SEQUENTIAL or HYPIC_BC_PIPELINED.
+ *   mode           HYPIC_BC_SEQUENTIAL, HYPIC_BC_PIPELINED or HYPIC_BC_FUSED.
  *   workspace      device scratch of at least
  *                  hypic_seg_build_compose_workspace_size() bytes for `mode`
  *                  (NULL allowed when that is 0): the build's workspace, then
- *                  the composition's (sequential) or each group's pair
- *                  (pipelined).  Contents ignored on entry, undefined on exit.
+ *                  the composition's (sequential), each group's pair
+ *                  (pipelined), or the tree's counters and node pairs (fused).
+ *                  Contents ignored on entry, undefined on exit.
  * The pairs equal those of hypic_seg_build; S_out, g_total and U_total equal
  * those of hypic_compose up to the rounding of the grouping.
  * Errors as for hypic_seg_build and hypic_compose.
  */
-enum { HYPIC_BC_SEQUENTIAL = 0, HYPIC_BC_PIPELINED = 1 };
+enum { HYPIC_BC_SEQUENTIAL = 0, HYPIC_BC_PIPELINED = 1, HYPIC_BC_FUSED = 2 };
 hypic_status hypic_seg_build_compose(hypic_family fam, int n_seg, const int32_t* seg_offsets, int n_chain,
                                      int d_k, int d_v, const hypic_tokens* in, const hypic_pairs* out,
                                      const float* S_init, float* S_out, float* g_total, float* U_total, int mode,

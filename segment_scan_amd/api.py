@@ -221,7 +221,7 @@ def seg_build(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torch.Tensor
     return g, U, S
 
 
-BC_SEQUENTIAL, BC_PIPELINED = 0, 1  # schedules of seg_build_compose
+BC_SEQUENTIAL, BC_PIPELINED, BC_FUSED = 0, 1, 2  # schedules of seg_build_compose
 
 
 def seg_build_compose_workspace_size(fam: int, offsets: Sequence[int], n_chain: int, d: int,

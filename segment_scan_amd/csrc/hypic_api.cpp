@@ -238,9 +238,10 @@ size_t build_workspace(int fam, int n_seg, const int32_t* seg_offsets, int n_cha
 // build_workspace() bytes for those segments.
 hypic_status build_range(int fam, int n_seg, const int32_t* seg_offsets, int s0, int s1, int n_chain, int d,
                          bool f32, const hypic_tokens* in, const hypic_pairs* out, void* workspace,
-                         hipStream_t stream) {
+                         hipStream_t stream, const hypic::FuseArgs* fuse = nullptr) {
   (void)n_seg;
   hypic::BuildArgs a;
+  if (fuse) a.fuse = *fuse;
   a.k = in->k;
   a.v = in->v;
   a.beta = in->beta;
@@ -313,13 +314,43 @@ int group_len(int n_seg, int n_chain) {
 struct FusedLayout {
   int glen, n_grp;
   size_t build_ws, g_off, U_off, S_off, total;
+  bool fused = false;  // fused schedule: counters at cnt_off, node pairs at g_off, U_off, S_off
+  int P = 0;
+  size_t cnt_off = 0;
 };
+
+// The fused schedule applies to the delta build's two-kernel path (d = 128, bf16
+// tokens, segments of at most kDelta2MaxSegLen tokens), at least two segments
+// and no start state; elsewhere the call runs the sequential schedule.
+bool fused_applies(int fam, int n_seg, const int32_t* seg_offsets, int d, bool f32) {
+  if (fam != HYPIC_DELTA || d != 128 || f32 || n_seg < 2) return false;
+  for (int s = 0; s < n_seg; ++s)
+    if (seg_offsets[s + 1] - seg_offsets[s] > hypic::kDelta2MaxSegLen) return false;
+  return true;
+}
 
 // Sequential mode: one group (the whole batch), and the blocked composition's
 // workspace after the build's.  Pipelined mode: groups, each group's pair.
-FusedLayout fused_layout(int fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32, int mode) {
+FusedLayout fused_layout(int fam, int n_seg, const int32_t* seg_offsets, int n_chain, int d, bool f32, int mode,
+                         bool has_init) {
   FusedLayout L;
-  if (mode == HYPIC_BC_SEQUENTIAL) {
+  if (mode == HYPIC_BC_FUSED && !has_init && fused_applies(fam, n_seg, seg_offsets, d, f32)) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    L.fused = true;
+    L.glen = n_seg;
+    L.n_grp = 1;
+    L.P = 1;
+    while (L.P < n_seg) L.P *= 2;
+    const size_t nodes = (size_t)L.P * n_chain;
+    L.build_ws = build_workspace(fam, n_seg, seg_offsets, n_chain, d, f32);
+    L.cnt_off = up(L.build_ws);
+    L.g_off = L.cnt_off + up(nodes * 4);
+    L.U_off = L.g_off + up(nodes * 4);
+    L.S_off = L.U_off + nodes * d * d * 4;
+    L.total = L.S_off + nodes * d * d * 4;
+    return L;
+  }
+  if (mode != HYPIC_BC_PIPELINED) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     L.glen = n_seg;
     L.n_grp = 1;
@@ -461,8 +492,12 @@ hypic_status hypic_seg_build_compose_workspace_size(hypic_family fam, int n_seg,
   TRY(check_offsets(n_seg, seg_offsets));
   if (dtype != HYPIC_F32 && dtype != HYPIC_BF16) return fail(HYPIC_E_INVALID, "unknown dtype %d", (int)dtype);
   if (!bytes) return fail(HYPIC_E_INVALID, "bytes is NULL");
-  if (mode != HYPIC_BC_SEQUENTIAL && mode != HYPIC_BC_PIPELINED) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
-  *bytes = fused_layout(fam, n_seg, seg_offsets, n_chain, d_k, dtype == HYPIC_F32, mode).total;
+  if (mode != HYPIC_BC_SEQUENTIAL && mode != HYPIC_BC_PIPELINED && mode != HYPIC_BC_FUSED)
+    return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
+  // (fused: enough also for the sequential schedule it runs when given a start state)
+  const bool f32 = dtype == HYPIC_F32;
+  *bytes = std::max(fused_layout(fam, n_seg, seg_offsets, n_chain, d_k, f32, mode, false).total,
+                    fused_layout(fam, n_seg, seg_offsets, n_chain, d_k, f32, mode, true).total);
   return ok();
 }
 
@@ -471,7 +506,8 @@ hypic_status hypic_seg_build_compose(hypic_family fam, int n_seg, const int32_t*
                                      float* S_out, float* g_total, float* U_total, int mode, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   TRY(check_common(fam, n_seg, n_chain, d_k, d_v));
-  if (mode != HYPIC_BC_SEQUENTIAL && mode != HYPIC_BC_PIPELINED) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
+  if (mode != HYPIC_BC_SEQUENTIAL && mode != HYPIC_BC_PIPELINED && mode != HYPIC_BC_FUSED)
+    return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
   const int d = d_k;
   TRY(check_offsets(n_seg, seg_offsets));
   const size_t n_tok = (size_t)seg_offsets[n_seg];
@@ -503,7 +539,7 @@ hypic_status hypic_seg_build_compose(hypic_family fam, int n_seg, const int32_t*
   outs.push_back({S_out, sbytes, "S_out"});
   if (g_total) outs.push_back({g_total, (size_t)n_chain * gate_len(fam, d) * 4, "g_total"});
   if (U_total) outs.push_back({U_total, sbytes, "U_total"});
-  const FusedLayout L = fused_layout(fam, n_seg, seg_offsets, n_chain, d, f32, mode);
+  const FusedLayout L = fused_layout(fam, n_seg, seg_offsets, n_chain, d, f32, mode, S_init != nullptr);
   if (L.total > 0 && !workspace) return fail(HYPIC_E_INVALID, "workspace is NULL (%zu bytes required)", L.total);
   if (workspace_bytes < L.total)
     return fail(HYPIC_E_INVALID, "workspace too small: %zu bytes given, %zu required", workspace_bytes, L.total);
@@ -519,6 +555,22 @@ hypic_status hypic_seg_build_compose(hypic_family fam, int n_seg, const int32_t*
   float* gU = dense(fam) ? reinterpret_cast<float*>(ws + L.U_off) : nullptr;
   float* gS = reinterpret_cast<float*>(ws + L.S_off);
   const size_t gl = gate_len(fam, d);
+  if (L.fused) {  // the build with the composition folded into its state pass
+    hypic::FuseArgs f;
+    f.cnt = reinterpret_cast<int*>(ws + L.cnt_off);
+    f.g = gg;
+    f.U = gU;
+    f.S = gS;
+    f.S_out = S_out;
+    f.g_tot = g_total;
+    f.U_tot = U_total;
+    f.P = L.P;
+    f.n_seg = n_seg;
+    hipError_t e = hypic::launch_zero_ints(f.cnt, (size_t)L.P * n_chain, sa);
+    if (e != hipSuccess) return hip_fail(e, "hypic_seg_build_compose counter reset");
+    TRY(build_range(fam, n_seg, seg_offsets, 0, n_seg, n_chain, d, f32, in, out, workspace, sa, &f));
+    return ok();
+  }
   if (L.n_grp == 1) {  // build, then compose (blocked schedule when it applies), on the caller's stream
     TRY(build_range(fam, n_seg, seg_offsets, 0, n_seg, n_chain, d, f32, in, out, workspace, sa));
     hypic::ComposeArgs c{};

@@ -33,6 +33,7 @@
 // so only rounding error remains: about 2^-12 per product, near 4e-4 relative
 // on 512-token GDN segments.  Longer segments use build_delta.hip.
 #include "common.h"
+#include "split_f16.h"
 #include "../launch.h"
 
 namespace hypic {
@@ -266,6 +267,133 @@ struct StateLdsT {  // one staging buffer
   static constexpr int BUF = O_RF + (KDA ? 2 * D * 4 : 0);
 };
 
+// ---- the fused composition (hypic_seg_build_compose, fused schedule) -----------------
+// Node k of the tree over P leaves: its leftmost leaf, and the node that holds its
+// pair (a node whose right subtree is empty stands for its left child).
+__device__ __forceinline__ int fuse_leftmost(int k, int P) {
+  while (k < P) k *= 2;
+  return k - P;
+}
+__device__ __forceinline__ int fuse_resolve(int k, int P, int n_seg) {
+  while (k < P && fuse_leftmost(2 * k + 1, P) >= n_seg) k *= 2;
+  return k;
+}
+
+// LDS of the node composition: U of the right child split into two fp16 terms
+// (A operand, k bits 2 and 3 swapped inside 16-blocks so that a fragment is one
+// 16-byte read), then the exponents of its 16-row blocks.
+constexpr int FUSE_UP = D + 8;
+constexpr int FUSE_OFF_E = 2 * D * FUSE_UP * 2;
+constexpr int FUSE_LDS = FUSE_OFF_E + 64;
+
+// Pair (g, U, S) of node k's children, composed in order: g = g_L + g_R,
+// U = U_R U_L, S = exp(g_R) U_R S_L + S_R ([youleyou, linear-layer paragraph]:
+// S(C1.C2) = T(C2) S(C1) + S(C2), T = exp(g) U).  Eight waves: wave w computes
+// columns 32 (w & 3) .. of U (w < 4) or S (w >= 4) with the left child's columns
+// as the B operand and U_R as A, both in two fp16 terms (fp32-class products,
+// as in the dense chain kernel); row tiles one at a time, each stored as it is
+// finished.  (Not inlined: the state pass around it keeps its own register
+// allocation.)
+// (The arguments are the values it needs, not the kernel's argument block, which
+// would then be copied to scratch memory.)
+__device__ __noinline__ void fuse_compose(const FuseArgs f, const float* pg, const float* pU, const float* pS,
+                                          int n_chain, int k, int chain, unsigned char* smem) {
+  const int P = f.P;
+  const int L = fuse_resolve(2 * k, P, f.n_seg), R = fuse_resolve(2 * k + 1, P, f.n_seg);
+  auto unit = [&](int r) { return (size_t)(r >= P ? r - P : r) * n_chain + chain; };
+  const float* gsrc_L = L >= P ? pg : f.g;
+  const float* gsrc_R = R >= P ? pg : f.g;
+  const float* U_L = (L >= P ? pU : f.U) + unit(L) * D * D;
+  const float* S_L = (L >= P ? pS : f.S) + unit(L) * D * D;
+  const float* U_R = (R >= P ? pU : f.U) + unit(R) * D * D;
+  const float* S_R = (R >= P ? pS : f.S) + unit(R) * D * D;
+  const float gL = gsrc_L[unit(L)], gR = gsrc_R[unit(R)];
+  const bool root = k == 1;
+  float* U_o = root ? f.U_tot : f.U + unit(k) * D * D;
+  float* S_o = root ? f.S_out + (size_t)chain * D * D : f.S + unit(k) * D * D;
+  if (root && U_o) U_o += (size_t)chain * D * D;
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = opaque((int)threadIdx.x) & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const bool uh = wave < 4;  // U columns (else S columns)
+  const int cb = (wave & 3) * 32;
+  f16_t* sU = reinterpret_cast<f16_t*>(smem);
+  int* sE = reinterpret_cast<int*>(smem + FUSE_OFF_E);
+
+  // U_R split: wave w rows 16 w .. 16 w + 15, lane rows 16 w + 2 i + h, columns 4 l32 ..
+  {
+    f32x4 ur[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      ur[i] = *reinterpret_cast<const f32x4*>(U_R + (size_t)(16 * wave + 2 * i + h) * D + 4 * l32);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(ur[i][j]));
+    const int eu = min(max(split_exp(wave_max_uniform(m)), -100), 100);
+    if (lane == 0) sE[wave] = eu;
+    const float su = ldexpf(1.f, -eu);
+    f16_t* dst = sU + (16 * wave + h) * FUSE_UP + 16 * (l32 >> 2) + kperm(4 * (l32 & 3));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const H4<2> t = split4h_scaled<2>(ur[i], su);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) *reinterpret_cast<f16x4*>(dst + (tt * D + 2 * i) * FUSE_UP) = t.t[tt];
+    }
+  }
+  // the left child's columns (B operand), in the accumulator layout
+  f32x16 Z[4];
+  {
+    const float* src = (uh ? U_L : S_L) + cb + l32;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Z[rt][r] = src[(size_t)(32 * rt + acc_row(r, lane)) * D];
+  }
+  __syncthreads();  // the split is in LDS
+  const float fs = uh ? 1.f : expf(gR);
+  float m = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(Z[rt][r]));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));  // the partner lane holds the column's other rows
+  const int ec = min(max(split_exp(m * fs), -100), 100);
+  const float sc = fs * ldexpf(1.f, -ec);
+  const f16_t* pa = sU + l32 * FUSE_UP + 8 * h;
+  float* dst = uh ? U_o : S_o;
+#pragma unroll 1
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x16 T = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = Z[ks >> 1][8 * (ks & 1) + j];
+      const HFrag<2> fb = split8h_scaled<2>(x, sc);
+      HFrag<2> fa;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        fa.t[tt] = *reinterpret_cast<const f16x8*>(pa + (tt * D + 32 * rt) * FUSE_UP + 16 * ks);
+      mmah<2, 2>(T, fa, fb);
+    }
+    const int e0 = sE[2 * rt] + ec, e1 = sE[2 * rt + 1] + ec;  // rows 32 rt + 0..15, + 16..31
+    if (dst) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const size_t o = (size_t)(32 * rt + acc_row(r, lane)) * D + cb + l32;
+        float y = ldexpf(T[r], r < 8 ? e0 : e1);
+        if (!uh) y += S_R[o];
+        dst[o] = y;
+      }
+    }
+  }
+  float* g_o = root ? (f.g_tot ? f.g_tot + chain : nullptr) : f.g + unit(k);
+  if (threadIdx.x == 0 && g_o) *g_o = gL + gR;
+}
+
 // Per chunk, in the frame scaled by the chunk's gate (the gated delta rule is
 // the ungated one on values v_t exp(-G_t), then scaled by exp(G_C)):
 //   U <- U + K^T (-A0 (K U))
@@ -281,7 +409,9 @@ struct StateLdsT {  // one staging buffer
 // c's products and stored over the buffer after a barrier (two per chunk); at
 // about 60 KB of LDS and at most 128 registers two workgroups share a CU and
 // cover each other's waits.
-template <bool KDA>
+// FUSE (delta mode): the fused composition follows the unit's pair (a separate
+// instantiation, so the plain build carries none of its code).
+template <bool KDA, bool FUSE = false>
 __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, const ChunkTable cks,
                                                              const unsigned char* ws) {
   using StateLds = StateLdsT<KDA>;
@@ -615,23 +745,70 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) dst[(size_t)(32 * rt + acc_row(r, lane)) * D + col0 + (lane & 31)] = Z[rt][r];
   if (threadIdx.x == 0) a.g[unit] = (float)g_acc;
+
+  // ---- fused composition: count this pair's arrival at its parent; the last
+  // arrival at a node composes it and goes on to the node's parent ----------------
+  if constexpr (FUSE && !KDA) {
+    {
+      __shared__ int s_last;
+      const FuseArgs f = a.fuse;
+      for (int k = (f.P + a.seg.out[s_local]) >> 1; k >= 1; k >>= 1) {
+        // release at device scope: this workgroup's pair (or node) written back
+        // to where every CU sees it, by every thread, before the count
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          const int need = fuse_leftmost(2 * k + 1, f.P) < f.n_seg ? 2 : 1;
+          s_last = atomicAdd(f.cnt + (size_t)k * n_chain + chain, 1) + 1 == need;
+        }
+        __syncthreads();
+        if (!s_last) break;
+        // acquire (the last arrival only): the siblings' pairs, not stale copies
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (fuse_leftmost(2 * k + 1, f.P) < f.n_seg) fuse_compose(f, a.g, a.U, a.S, n_chain, k, chain, smem);
+      }
+    }
+  }
 }
 
 }  // namespace
+
+namespace {
+__global__ void zero_ints_kernel(int* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_zero_ints(int* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 size_t delta2_workspace_bytes(const SegTable& seg, int n_chain) {
   return (size_t)chunk_table(seg, nullptr) * n_chain * REC_BYTES;
 }
 
 namespace {
+template <bool KDA, bool FUSE>
+hipError_t launch_state_t(const BuildArgs& a, const ChunkTable& ct, const unsigned char* w, hipStream_t stream) {
+  // (the fused composition splits a 128 x 128 operand into the same LDS)
+  constexpr int lds = (FUSE && FUSE_LDS > StateLdsT<KDA>::BUF) ? FUSE_LDS : StateLdsT<KDA>::BUF;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&delta_state_kernel<KDA, FUSE>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((delta_state_kernel<KDA, FUSE>), dim3(a.seg.n_seg * a.n_chain), dim3(512), lds, stream, a, ct,
+                     w);
+  return hipGetLastError();
+}
 template <bool KDA>
 hipError_t launch_state(const BuildArgs& a, const ChunkTable& ct, const unsigned char* w, hipStream_t stream) {
-  constexpr int lds = StateLdsT<KDA>::BUF;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&delta_state_kernel<KDA>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((delta_state_kernel<KDA>), dim3(a.seg.n_seg * a.n_chain), dim3(512), lds, stream, a, ct, w);
-  return hipGetLastError();
+  if constexpr (!KDA) {
+    if (a.fuse.cnt) return launch_state_t<false, true>(a, ct, w, stream);
+  }
+  return launch_state_t<KDA, false>(a, ct, w, stream);
 }
 }  // namespace
 

@@ -35,6 +35,26 @@ struct SegTable {
 inline int seg_len(const SegTable& t, int s) { return t.end[s] - t.beg[s]; }
 inline bool seg_uniform(const SegTable& t) { return t.contiguous != 0; }
 
+// Composition fused into the delta build (hypic_seg_build_compose, fused
+// schedule): the request's segments are the leaves of a binary tree per chain
+// (leaf i at heap index P + i, node k over its children 2k and 2k + 1; a node
+// whose right subtree holds no segment stands for its left child).  A build
+// workgroup that has written its pair counts its arrival at the parent node;
+// the last arrival composes the node's two children into the node's pair and
+// moves up, the root's pair going to S_out, g_tot and U_tot.  No workgroup waits
+// for another.
+struct FuseArgs {
+  int* cnt = nullptr;  // [P][n_chain] arrival counters, zero on entry (nullptr: not fused)
+  float* g = nullptr;  // node pairs: g [P][n_chain], U and S [P][n_chain][d][d] (index k < P)
+  float* U = nullptr;
+  float* S = nullptr;
+  float* S_out = nullptr;  // the root: S [n_chain][d][d], g [n_chain], U (or nullptr)
+  float* g_tot = nullptr;
+  float* U_tot = nullptr;
+  int P = 0;      // leaves: a power of two >= n_seg
+  int n_seg = 0;  // segments of the request
+};
+
 struct BuildArgs {
   const void* k;
   const void* v;
@@ -46,6 +66,7 @@ struct BuildArgs {
   int n_chain;
   int gate_per_chain;
   SegTable seg;
+  FuseArgs fuse;  // delta build, two-kernel path only
 };
 
 struct ComposeArgs {
@@ -102,6 +123,9 @@ hipError_t launch_build_delta_single(int d, bool in_f32, const BuildArgs& a, int
 // the two-kernel path (build_delta2.hip)
 size_t delta2_workspace_bytes(const SegTable& seg, int n_chain);
 hipError_t launch_build_delta2(const BuildArgs& a, void* ws, hipStream_t stream);
+// zero n ints (the fused composition's counters) with a kernel, so the call can
+// be captured into a graph
+hipError_t launch_zero_ints(int* p, size_t n, hipStream_t stream);
 hipError_t launch_compose_elem(int fam, int d, const ComposeArgs& a, hipStream_t stream);
 // dense composition and the delta seam step on the column-split chain kernel (chain.hip)
 // With a workspace of compose_workspace_bytes() (0 when the schedule does not

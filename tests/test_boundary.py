@@ -359,7 +359,7 @@ def test_build_compose_requires_its_workspace(lib):
     t = toks(DELTA)
     p = pairs(DELTA)
     need = ctypes.c_size_t(0)
-    for mode in (0, 1):
+    for mode in (0, 1, 2):
         assert lib.hypic_seg_build_compose_workspace_size(DELTA, 2, off, 2, 128, 128, BF16, mode,
                                                           ctypes.byref(need)) == 0
         assert need.value > 0

@@ -1,6 +1,9 @@
-"""GPU parity: hypic_seg_build_compose (groups of segments built on the
-caller's stream, each group composed on a second stream while the next is
-built, the group pairs composed in order at the end) against the oracle."""
+"""GPU parity: hypic_seg_build_compose against the oracle, in its three
+schedules: sequential (build, then compose), pipelined (groups of segments
+built on the caller's stream, each group composed on a second stream while the
+next is built, the group pairs composed in order at the end) and fused (the
+composition folded into the delta build's state pass as a tree whose last
+arrival at each node composes it)."""
 import numpy as np
 import pytest
 
@@ -27,11 +30,12 @@ def _run(tk, offsets, S0=None, want_total=True, mode=api.BC_PIPELINED):
     return g, U, S, res
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 def test_cold_request_full_size(mode):
     """The 32k-token cold request (32 heads x 64 segments x 512 tokens), in the
-    sequential schedule and in the pipelined one (four groups of 16 segments);
-    S_out, g_total and U_total against the oracle's composition of its own pairs."""
+    sequential schedule, the pipelined one (four groups of 16 segments) and the
+    fused one; S_out, g_total and U_total against the oracle's composition of
+    its own pairs."""
     tk = synth.gdn_cold()
     announce("build_compose_cold", "mode", mode)
     g, U, S, res = _run(tk, tk.offsets, mode=mode)
@@ -80,3 +84,30 @@ def test_one_group_and_ragged():
     g, U, S, res = _run(tk, offsets)
     Sseq, _ = oracle.sequential(DELTA, tk.k, tk.v, tk.beta, tk.log_gate)
     assert_units_close("one_group.S_out", host(res["S_out"]), Sseq, TOL["bf16"], unit_dims=1)
+
+
+@pytest.mark.parametrize("lengths", [[64, 64], [1, 63, 64, 65, 200, 130, 7], [24] * 600])
+def test_fused_tree_shapes(lengths):
+    """The fused schedule on trees of 2 leaves, of 7 ragged segments (a 1-token
+    one; the tree's right edge has nodes with one child) and of 600 segments (3
+    build launches whose workgroups meet at the upper nodes): S_out, g_total and
+    U_total against the straight recurrence over all tokens, and a second call
+    bit for bit equal to the first."""
+    import torch
+    n_chain = 2 if len(lengths) > 100 else 3
+    tk = synth.gdn_cold(n_seg=1, L=sum(lengths), n_chain=n_chain, gate_scale=1.0 / 64)
+    offsets = synth.ragged_offsets(lengths)
+    announce("build_compose_fused", "segs", len(lengths), "chains", n_chain)
+    g, U, S, res = _run(tk, offsets, mode=api.BC_FUSED)
+    Sseq, _ = oracle.sequential(DELTA, tk.k, tk.v, tk.beta, tk.log_gate)
+    assert_units_close("fused.S_out", host(res["S_out"]), Sseq, TOL["bf16"], unit_dims=1)
+    # the composition alone: the oracle composing the pairs this call built
+    # (fp32 pairs: the fp32 class for the composed state)
+    ref = oracle.compose(DELTA, host(g), host(U), host(S), want_total=True)
+    assert_units_close("fused.S_out_vs_own_pairs", host(res["S_out"]), ref["S_out"], TOL["f32"], unit_dims=1)
+    assert_g_close("fused.g_tot", host(res["g_tot"]), ref["g_tot"], TOL["f32"])
+    assert_units_close("fused.U_tot", host(res["U_tot"]), ref["U_tot"], TOL["bf16"], unit_dims=1)
+    _, _, _, res2 = _run(tk, offsets, mode=api.BC_FUSED)
+    torch.cuda.synchronize()
+    for key in ("S_out", "g_tot", "U_tot"):
+        assert torch.equal(res[key], res2[key]), key + " differs between two fused calls"
