@@ -201,9 +201,10 @@ hypic_status hypic_seg_build_workspace_size(hypic_family fam, int n_seg, const i
  *                  and at least 8 segments it lets the composition run as a
  *                  scan: blocks of consecutive segments are composed in
  *                  parallel (by associativity, [hwlabs, section 세그먼트 누적
- *                  전이 연산자]), each chain then composes its block pairs in
- *                  order, and, if prefix_states are requested, every block is
- *                  run again from its start state in parallel to emit them.
+ *                  전이 연산자]); without prefix_states the block pairs are then
+ *                  reduced pairwise in parallel levels down to two; with them
+ *                  each chain composes its block pairs in order and every block
+ *                  is run again from its start state in parallel to emit them.
  *                  The result equals the single-pass one up to rounding.
  * Errors as for hypic_seg_build (a workspace that is smaller than required or
  * overlaps another argument is HYPIC_E_INVALID).
@@ -281,8 +282,9 @@ hypic_status hypic_seg_build_compose_workspace_size(hypic_family fam, int n_seg,
 /*
  * hypic_compose_workspace_size -- bytes of workspace that enable the blocked
  * schedule of hypic_compose for these sizes (0: not used): per (block, chain)
- * its g, U and S, and with want_prefix = 1 (prefix_states will be requested)
- * also its start state.  *bytes receives the size; enqueues nothing.
+ * its g, U and S, and with want_prefix = 0 the pairs of the first reduction
+ * level (half as many), with want_prefix = 1 (prefix_states will be requested)
+ * each block's start state instead.  *bytes receives the size; enqueues nothing.
  */
 hypic_status hypic_compose_workspace_size(hypic_family fam, int n_seg, int n_chain, int d_k, int d_v,
                                           int want_prefix, size_t* bytes);

@@ -1073,12 +1073,22 @@ __global__ __launch_bounds__(256, 2) void chain_wide_kernel(const ChainArgs a) {
     if (threadIdx.x < Cfg::ZROW / 4) reinterpret_cast<float*>(smem + Cfg::OFF_Z)[threadIdx.x] = 0.f;
     issue_window(0);
   }
-  float g_cur = 0.f;
-  if (PAIRS) {
-    issue_U(0);
-    if (!ut) g_cur = a.g[pidx];
+  // Composition from the zero state (U_total: the identity): the first step's
+  // result is the first pair's S (U) itself, loaded instead of multiplied.
+  int seg0 = 0;
+  if constexpr (!SEAM) {
+    if (PAIRS && (ut || !a.S_in) && nseg > 0) {
+      load_tiles((ut ? a.U : a.S) + pair_off, St);
+      seg0 = 1;
+      if (nseg > 1 && !ut && a.prefix) store_tiles(a.prefix + seg_stride + pair_off);
+    }
   }
-  for (int seg = 0; seg < nseg; ++seg) {
+  float g_cur = 0.f;
+  if (PAIRS && seg0 < nseg) {
+    issue_U(seg0);
+    if (!ut) g_cur = a.g[pidx + (size_t)seg0 * n_chain];
+  }
+  for (int seg = seg0; seg < nseg; ++seg) {
     __syncthreads();  // every wave is done with the previous step's LDS
     // (the registers staged here were loaded a step ago; the next loads are
     // issued after them, so that no wait for these covers the new ones)
@@ -1174,14 +1184,18 @@ hipError_t launch_compose_d(const ChainArgs& a, bool want_ut, hipStream_t stream
 }  // namespace
 
 namespace {
-// Two-level schedule for few chains: about 128 (block, chain) units compose
-// their blocks in parallel, then each chain composes its block pairs in order.
-// With prefix states a third level re-runs every block from its start state in
-// parallel (a three-phase scan [hwlabs, section 세그먼트 누적 전이 연산자: the
-// composition is associative]).
+// Blocked schedule for few chains: about 256 (d = 128; d = 64: 128) (block,
+// chain) units compose their blocks in parallel (two workgroups per CU with
+// their U products).  Without prefix states the block pairs are then reduced
+// pairwise, each level composing consecutive pairs two by two in parallel, down
+// to two, which the last launch composes with the start state.  With prefix
+// states each chain instead composes its block pairs in order, recording every
+// block's start state, and a third level re-runs every block from its start
+// state in parallel (a three-phase scan [hwlabs, section 세그먼트 누적 전이 연산자:
+// the composition is associative]).
 bool tree_plan(int d, int n_seg, int n_chain, bool /*prefix*/, int* blk_len, int* n_blocks) {
   if (n_seg < 8 || n_chain * (d / 32) > 256) return false;
-  int nb = std::max(2, std::min(n_seg / 4, 128 / n_chain));
+  int nb = std::max(2, std::min(n_seg / 4, (d == 128 ? 256 : 128) / n_chain));
   const int bl = (n_seg + nb - 1) / nb;
   *blk_len = bl;
   *n_blocks = (n_seg + bl - 1) / bl;
@@ -1190,11 +1204,16 @@ bool tree_plan(int d, int n_seg, int n_chain, bool /*prefix*/, int* blk_len, int
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
+// Pairs of `units` (g, U, S), 256-byte aligned parts.
+size_t pairs_bytes(size_t units, int d) { return align256(units * 4) + 2 * units * d * d * 4; }
+
 size_t compose_workspace_bytes(int d, int n_seg, int n_chain, bool prefix) {
   int bl, nb;
   if (!tree_plan(d, n_seg, n_chain, prefix, &bl, &nb)) return 0;
   const size_t units = (size_t)nb * n_chain;
-  return align256(units * 4) + (prefix ? 3 : 2) * units * d * d * 4;  // g, U, S (and start state) per block
+  // the block pairs; with prefix states a start state per block, else the pairs
+  // of the next level of the pairwise reduction
+  return pairs_bytes(units, d) + (prefix ? units * d * d * 4 : pairs_bytes((size_t)((nb + 1) / 2) * n_chain, d));
 }
 
 hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -1243,18 +1262,48 @@ hipError_t launch_compose_chain(int d, const ComposeArgs& c, void* ws, size_t ws
     a3.n_chain = c.n_chain;
     a3.blk_len = bl;
     a3.n_units = (int)units;
-    hipError_t e;
-    if (d == 128) {
-      e = launch_compose_d<128>(a1, true, stream);
-      if (e == hipSuccess) e = launch_compose_d<128>(a2, c.U_tot != nullptr, stream);
-      if (e == hipSuccess && wP) e = launch_compose_d<128>(a3, false, stream);
-    } else if (d == 64) {
-      e = launch_compose_d<64>(a1, true, stream);
-      if (e == hipSuccess) e = launch_compose_d<64>(a2, c.U_tot != nullptr, stream);
-      if (e == hipSuccess && wP) e = launch_compose_d<64>(a3, false, stream);
-    } else {
-      e = hipErrorInvalidValue;
+    auto launch = [&](const ChainArgs& x, bool want_ut) {
+      return d == 128 ? launch_compose_d<128>(x, want_ut, stream)
+                      : d == 64 ? launch_compose_d<64>(x, want_ut, stream) : hipErrorInvalidValue;
+    };
+    hipError_t e = launch(a1, true);
+    if (!wP) {
+      // no prefix states: the block pairs reduced pairwise (each level composes
+      // consecutive pairs two by two, in parallel) until at most two are left
+      float* g_cur = wg;
+      float* U_cur = wU;
+      float* S_cur = wS;
+      unsigned char* nxt = reinterpret_cast<unsigned char*>(ws) + pairs_bytes(units, d);
+      float* g_nx = reinterpret_cast<float*>(nxt);
+      float* U_nx = reinterpret_cast<float*>(nxt + align256((size_t)((nb + 1) / 2) * c.n_chain * 4));
+      float* S_nx = U_nx + (size_t)((nb + 1) / 2) * c.n_chain * d * d;
+      int n = nb;
+      while (e == hipSuccess && n > 2) {
+        const int n2 = (n + 1) / 2;
+        ChainArgs al{};
+        al.g = g_cur;
+        al.U = U_cur;
+        al.S = S_cur;
+        al.S_out = S_nx;
+        al.g_tot = g_nx;
+        al.U_tot = U_nx;
+        al.n_seg = n;
+        al.n_chain = c.n_chain;
+        al.blk_len = 2;
+        al.n_units = n2 * c.n_chain;
+        e = launch(al, true);
+        std::swap(g_cur, g_nx);
+        std::swap(U_cur, U_nx);
+        std::swap(S_cur, S_nx);
+        n = n2;
+      }
+      a2.g = g_cur;
+      a2.U = U_cur;
+      a2.S = S_cur;
+      a2.n_seg = n;
     }
+    if (e == hipSuccess) e = launch(a2, c.U_tot != nullptr);
+    if (e == hipSuccess && wP) e = launch(a3, false);
     return e;
   }
   ChainArgs a{};

@@ -87,15 +87,19 @@ def ws_size(lib, fam=DELTA, offsets=(0, 64, 128), n_chain=2, d=128, dtype=BF16):
 
 def test_compose_workspace_size(lib):
     """The blocked schedule applies to the dense family with few chains: one block
-    pair (g, U, S) per (block, chain), about 128 units, and with prefix states
-    each block's start state too."""
+    pair (g, U, S) per (block, chain), about 256 units at d = 128; without prefix
+    states also the pairs of the first pairwise reduction level (half as many),
+    with prefix states each block's start state instead."""
     def cws(fam=DELTA, n_seg=64, n_chain=32, d=128, prefix=0):
         out = ctypes.c_size_t(7)
         st = lib.hypic_compose_workspace_size(fam, n_seg, n_chain, d, d, prefix, ctypes.byref(out))
         return st, out.value
-    units = 4 * 32  # 64 segments in 4 blocks of 16, 32 chains
-    assert cws() == (0, ((units * 4 + 255) // 256) * 256 + 2 * units * 128 * 128 * 4)
-    assert cws(prefix=1) == (0, ((units * 4 + 255) // 256) * 256 + 3 * units * 128 * 128 * 4)
+
+    def pairs(units):
+        return ((units * 4 + 255) // 256) * 256 + 2 * units * 128 * 128 * 4
+    units = 8 * 32  # 64 segments in 8 blocks of 8, 32 chains
+    assert cws() == (0, pairs(units) + pairs(units // 2))
+    assert cws(prefix=1) == (0, pairs(units) + units * 128 * 128 * 4)
     assert cws(n_chain=480) == (0, 0)
     assert cws(n_seg=4) == (0, 0)
     assert cws(fam=SCALAR) == (0, 0)
