@@ -267,7 +267,7 @@ class ColdRequest(Workload):
     kernel = "build_delta"
     fam = 3  # delta
     op_dispatches = 2    # factor pass, state pass
-    step_dispatches = 4  # + the two-level composition
+    step_dispatches = 6  # + the blocked composition (blocks, two pairwise levels, the last pair)
 
     def __init__(self):
         self.n_seg, self.L, self.H, self.d = 64, 512, 32, 128
@@ -434,7 +434,7 @@ class KdaRequest(ColdRequest):
     kernel = "build_kda"
     fam = 4  # kda
     op_dispatches = 2    # factor pass, state pass
-    step_dispatches = 4  # + the two-level composition
+    step_dispatches = 6  # + the blocked composition (blocks, two pairwise levels, the last pair)
 
     def __init__(self):
         super().__init__()
