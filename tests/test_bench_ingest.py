@@ -36,10 +36,10 @@ def _run(tmp_path, monkeypatch, wl, step_kernels, op_kib, other_kib, steps, warm
                                  ["cmd"])
 
 
-def test_cold_request_two_op_dispatches_of_four(tmp_path, monkeypatch):
+def test_cold_request_two_op_dispatches_of_six(tmp_path, monkeypatch):
     wl = bench.WORKLOADS["gdn_cold32k"]()
-    kernels = ["hypic::delta_prep_kernel(x)", "hypic::delta_state_kernel<1>(x)", "hypic::chain_kernel<128, 4>(x)",
-               "hypic::chain_kernel<128, 1>(x)"]
+    kernels = ["hypic::delta_prep_kernel(x)", "hypic::delta_state_kernel<1>(x)"] + \
+        ["hypic::chain_wide_kernel<2, false, true>(x)"] * 4
     rec = _run(tmp_path, monkeypatch, wl, kernels, op_kib=1000.0, other_kib=7777.0, steps=20, warmup=5,
                copy_kib=524288.0)
     # two op dispatches of 1000 KiB per step; 1 GiB copy reads 512 MiB -> scale 2
