@@ -282,7 +282,7 @@ def seg_build_compose(fam: int, offsets: Sequence[int], k: torch.Tensor, v: torc
 
 
 def compose_workspace_size(fam: int, n_seg: int, n_chain: int, d: int, want_prefix: bool = False) -> int:
-    """Bytes of device workspace that enable compose's two-level schedule (0: none)."""
+    """Bytes of device workspace that enable compose's blocked schedule (0: none)."""
     out = ctypes.c_size_t(0)
     _check(load_library().hypic_compose_workspace_size(fam, n_seg, n_chain, d, d, int(bool(want_prefix)),
                                                        ctypes.byref(out)))

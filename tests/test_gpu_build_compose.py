@@ -111,3 +111,19 @@ def test_fused_tree_shapes(lengths):
     torch.cuda.synchronize()
     for key in ("S_out", "g_tot", "U_tot"):
         assert torch.equal(res[key], res2[key]), key + " differs between two fused calls"
+
+
+def test_fused_without_totals():
+    """The fused schedule asked for S_out alone (no g_total, no U_total: the root
+    writes neither), against the sequential schedule's S_out."""
+    import torch
+    lengths = [64] * 12
+    tk = synth.gdn_cold(n_seg=1, L=sum(lengths), n_chain=4, gate_scale=1.0 / 64)
+    offsets = synth.ragged_offsets(lengths)
+    announce("build_compose_fused_no_totals")
+    _, _, _, res = _run(tk, offsets, want_total=False, mode=api.BC_FUSED)
+    _, _, _, ref = _run(tk, offsets, want_total=False, mode=api.BC_SEQUENTIAL)
+    torch.cuda.synchronize()
+    assert res.get("g_tot") is None and res.get("U_tot") is None
+    assert_units_close("fused_no_totals.S_out", host(res["S_out"]), host(ref["S_out"]).astype(np.float64),
+                       TOL["f32"], unit_dims=1)
