@@ -65,8 +65,8 @@ __device__ __forceinline__ f16x8 lds_a_perm_h(const f16_t* p, int off) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Elements 8m .. 8m+7 of an accumulator tile, times the wave-uniform s, as an
-// fp16 B fragment.
+// Elements 8m .. 8m+7 of an accumulator tile, times s, as an fp16 B fragment
+// (s is the power-of-two scale of the lane's column: lanes l and l ^ 32 agree).
 __device__ __forceinline__ f16x8 acc_as_b_h(const f32x16& acc, int m, float s) {
   f16x8 f;
 #pragma unroll
@@ -82,6 +82,17 @@ __device__ __forceinline__ f16x8 acc_as_b_unit(const f32x16& acc, int m) {
   for (int j = 0; j < 8; ++j) f[j] = (f16_t)(NEG ? -acc[8 * m + j] : acc[8 * m + j]);
   return f;
 }
+
+// Largest magnitude over the accumulator column that lanes l and l ^ 32 hold
+// together (as a B operand a column spans both halves of the wave, so its two
+// lanes must agree on one scale).  m >= 0: bit patterns order like the values.
+// xaddr = 4 (lane ^ 32).
+__device__ __forceinline__ float pair_max(float m, int xaddr) {
+  const unsigned a = __float_as_uint(m);
+  const unsigned b = (unsigned)__builtin_amdgcn_ds_bpermute(xaddr, (int)a);
+  return __uint_as_float(a > b ? a : b);
+}
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 
 // =====================================================================================
 // delta_prep: per (chunk, chain) A0 = (I + strict_lower(diag(b) K K^T))^-1 diag(b)
@@ -457,13 +468,14 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
       for (int r = 0; r < 4; ++r)
         raw[r] = *reinterpret_cast<const uint4*>(rec + KREC_KB + ((tb * 4 + r) * D + db * 8) * 2);
     } else {
-      const uint16_t* src = reinterpret_cast<const uint16_t*>(tid < 256 ? a.k : a.v);
+      // K (waves 0-3) or V (waves 4-7) over the chunk's valid tokens only: a
+      // buffer load past them returns zeros, which tokens past the end must be
+      const uint32_t row_bytes = (uint32_t)n_chain * D * 2;
+      const char* src = reinterpret_cast<const char*>(wave_id_uniform() >= 4 ? a.v : a.k) +
+                        ((size_t)c0 * n_chain + chain) * D * 2;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, (uint32_t)(nv - 1) * row_bytes + D * 2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb * 4 + r;
-        raw[r] = *reinterpret_cast<const uint4*>(src + ((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * D + db * 8);
-        if (t >= nv) raw[r] = make_uint4(0, 0, 0, 0);  // tokens past the end must be zero
-      }
+      for (int r = 0; r < 4; ++r) raw[r] = buffer_load16(rs, (uint32_t)(tb * 4) * row_bytes + db * 16, r * row_bytes);
     }
     // A0 (X) row tid / 8, entries 8 (tid % 8) ..
     raw[4] = *reinterpret_cast<const uint4*>(rec + (KDA ? KREC_X : REC_A) + tid * 16);
@@ -575,49 +587,58 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
       const float* sF = reinterpret_cast<const float*>(base + StateLds::O_SM);
       const int lane = opaque(threadIdx.x) & 63;
       const int h = lane >> 5, l32 = lane & 31;
+      const int xaddr = (lane ^ 32) << 2;
+      // the scale of an operand column: its own (delta mode) or the wave's (KDA)
+      auto col_max = [&](float m) { return KDA ? wave_max_uniform(m) : pair_max(m, xaddr); };
       const float eGC = sF[2 * C];
       float fez;   // delta mode: W = K Z / fez after step 1
       float f_er;  // W holds X' / f_er after step 2
       f32x16 W[2];
-      // ---- step 1: Y = K Z (S waves: exp(G_C) K Z, the factor folded into Z's conversion)
+      // Delta mode: every operand scale below is per column (lanes l and l ^ 32
+      // agree on it), and the products of a column carry its factor to where it is
+      // used; KDA: one scale per wave and operand.
+      // ---- step 1: Y = K Z.  Delta mode, S waves: S <- exp(G_C) S first, so that
+      // step 1 and step 3 use the decayed state alike (KDA: the factor folded into
+      // Z's conversion; its per-row factors come in step 3) -------------------------
       {
+        if (!KDA && s_wave) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Z[rt][r] *= eGC;
+        }
         float m = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(Z[rt][r]));
-        const float gz = s_wave ? eGC : 1.f;
-        const int ez = f16_scale_exp(wave_max_uniform(m) * gz);
+        const float gz = (KDA && s_wave) ? eGC : 1.f;
+        const int ez = f16_scale_exp(col_max(m) * gz);
         // delta mode, U waves: -Z, so that X' comes out with its sign (U <- U - K^T A0 K U)
-        const float sz = KDA ? gz * ldexpf(1.f, -ez) : (s_wave ? 1.f : -1.f) * gz * ldexpf(1.f, -ez);
+        const float sz = KDA ? gz * ldexpf(1.f, -ez) : (s_wave ? 1.f : -1.f) * ldexpf(1.f, -ez);
         fez = KDA ? 1.f : ldexpf(1.f, ez);
         const f16_t* pK = sK + l32 * KP + 4 * h;
         W[0] = zero16();
         W[1] = zero16();
-        // (delta mode, U waves with scale 1: the conversion alone, sign as a modifier)
-        const bool unit = !KDA && !s_wave && ez == 0;
-        if (unit) {
+        auto product = [&](auto conv) {
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
-              const f16x8 fb = acc_as_b_unit<true>(Z[rt], mm);
+              const f16x8 fb = conv(Z[rt], mm);
 #pragma unroll
               for (int tt = 0; tt < 2; ++tt)
                 W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
             }
+        };
+        // (delta mode, every column at scale 1: the conversion alone, the sign a modifier)
+        if (!KDA && !wave_any(ez != 0)) {
+          if (s_wave) product([](const f32x16& z, int mm) { return acc_as_b_unit<false>(z, mm); });
+          else product([](const f32x16& z, int mm) { return acc_as_b_unit<true>(z, mm); });
         } else {
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-              const f16x8 fb = acc_as_b_h(Z[rt], mm, sz);
-#pragma unroll
-              for (int tt = 0; tt < 2; ++tt)
-                W[tt] = mfma32h(lds_a_perm_h(pK, 32 * tt * KP + 32 * rt + 16 * mm), fb, W[tt]);
-            }
+          product([&](const f32x16& z, int mm) { return acc_as_b_h(z, mm, sz); });
         }
-        if (KDA && ez != 0) {
+        if (KDA && wave_any(ez != 0)) {
           const float f = ldexpf(1.f, ez);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
@@ -649,14 +670,20 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
-        const int er = f16_scale_exp(wave_max_uniform(m));
+        const int er = f16_scale_exp(col_max(m));
         const f16_t* pA = sA0 + l32 * TP + 4 * h;
+        if (!KDA && wave_any(er != 0)) {  // (delta mode: R converted once, scaled in place where needed)
+          const float sr = ldexpf(1.f, -er);
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) W[tp][r] *= sr;
+        }
         f16x8 fb[2][2];
-        const float sr = ldexpf(1.f, -er);
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) fb[tp][mm] = acc_as_b_h(W[tp], mm, sr);
+          for (int mm = 0; mm < 2; ++mm) fb[tp][mm] = KDA ? acc_as_b_h(W[tp], mm, ldexpf(1.f, -er)) : acc_as_b_unit<false>(W[tp], mm);
         W[0] = zero16();
         W[1] = zero16();
 #pragma unroll
@@ -682,14 +709,16 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
           f_er = 1.f;
         }
       }
-      // ---- step 3: Z = (exp(G_C) | 1) Z + K^T X' ----------------------------------------
+      // ---- step 3: Z = Z (delta; S waves decayed in step 1) or diag(row factors) Z
+      // (KDA) + K^T X' ---------------------------------------------------------------
       {
         float m = 0.f;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(W[tt][r]));
-        const int ex = f16_scale_exp(wave_max_uniform(m) * fabsf(f_er));
+        const int ex = f16_scale_exp(col_max(m) * fabsf(f_er));
+        const bool any_ex = wave_any(ex != 0);
         if constexpr (KDA) {  // per-row factors exp(G_C) (S) or exp(G_C - mu_C) (U)
           const float sc = ldexpf(1.f, -ex);
           const float* rf = reinterpret_cast<const float*>(base + StateLds::O_RF) + (s_wave ? 0 : D) + 4 * h;
@@ -701,27 +730,31 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
 #pragma unroll
               for (int j = 0; j < 4; ++j) Z[rt][4 * q + j] *= f4[j];
             }
-        } else {
-          const float pre = (s_wave ? eGC : 1.f) * ldexpf(1.f, -ex);
-          if (s_wave || ex != 0) {
+        } else if (any_ex) {
+          const float pre = ldexpf(1.f, -ex);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+          for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) Z[rt][r] *= pre;
-          }
+            for (int r = 0; r < 16; ++r) Z[rt][r] *= pre;
         }
         const f16_t* pKt = sKt + l32 * TP + 4 * h;
         const float sx = f_er * ldexpf(1.f, -ex);
+        if (!KDA && wave_any(sx != 1.f)) {  // (delta mode: X' converted once, scaled in place where needed)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) W[tt][r] *= sx;
+        }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) {
-            const f16x8 fb = acc_as_b_h(W[tt], mm, sx);
+            const f16x8 fb = KDA ? acc_as_b_h(W[tt], mm, sx) : acc_as_b_unit<false>(W[tt], mm);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
               Z[rt] = mfma32h(lds_a_perm_h(pKt, 32 * rt * TP + 32 * tt + 16 * mm), fb, Z[rt]);
           }
-        if (ex != 0) {
+        if (any_ex) {
           const float f = ldexpf(1.f, ex);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
