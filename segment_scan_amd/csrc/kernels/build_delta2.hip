@@ -23,13 +23,15 @@
 //  - delta_state: one workgroup per (segment, chain) keeps [U | S] in MFMA
 //    accumulators (8 waves x 32 columns) and, per chunk, stages K (row-major
 //    and transposed), V and A0 in LDS and runs the three products.
-// The workspace makes the state pass a plain stream with one barrier per
-// chunk and lets the latency-bound inverse hide behind other workgroups.
+// The workspace makes the state pass a plain stream (two barriers per chunk,
+// around the staging) and lets the latency-bound inverse hide behind other
+// workgroups.
 //
 // Operands enter the matrix cores as fp16 (fp32 accumulate).  bf16 keys are
 // exact in fp16 within its normal range (normalised delta-rule keys are);
 // derived operands are rounded once, each block scaled by a power of two
-// chosen from its largest magnitude (f16_scale_exp in common.h; A0 per row),
+// chosen from its largest magnitude (f16_scale_exp in common.h; A0 per row, the
+// state pass's operands per column),
 // so only rounding error remains: about 2^-12 per product, near 4e-4 relative
 // on 512-token GDN segments.  Longer segments use build_delta.hip.
 #include "common.h"

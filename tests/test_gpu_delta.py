@@ -130,6 +130,27 @@ def test_deltanet_ungated_d128():
     check_build(tk, "deltanet_d128")
 
 
+def test_value_channels_of_very_different_scales():
+    """Value channels scaled by powers of two from 2^-20 to 2^17 (the values stay bf16
+    numbers).  Each state column depends on its own value channel only, so every
+    column of S keeps the bf16 bound on its own: the state pass scales its fp16
+    operands per column, and the scaled conversion paths all run here."""
+    tk = synth.gdn_cold(n_seg=2, n_chain=2, gate_scale=1.0 / 16)
+    e = np.array([-20, -9, -3, 0, 5, 11, 17])[np.arange(tk.dv) % 7]
+    tk.v = tk.v * np.exp2(e)
+    g, U, S = gpu_build(tk)
+    rg, rU, rS = oracle.build_pairs(DELTA, tk.offsets, tk.k, tk.v, tk.beta, tk.log_gate)
+    tol = TOL[tk.dtype]
+    Sg = np.asarray(host(S), np.float64)
+    col_err = np.linalg.norm(Sg - rS, axis=-2) / np.linalg.norm(rS, axis=-2)  # [seg, chain, column]
+    assert np.isfinite(Sg).all()
+    worst = float(col_err.max())
+    print("  max per-column rel err S %.2e" % worst, flush=True)
+    assert worst <= tol, "column %s: %.3e" % (np.unravel_index(int(col_err.argmax()), col_err.shape), worst)
+    assert_units_close("scaled_v.U", host(U), rU, tol)
+    assert_g_close("scaled_v.g", host(g), rg, tol)
+
+
 def test_explicit_workspace_reused_across_calls():
     """A caller-owned workspace of the queried size serves two different batches;
     results equal those of calls with their own workspace."""
