@@ -590,15 +590,14 @@ __global__ __launch_bounds__(512, 4) void delta_state_kernel(const BuildArgs a, 
       const int lane = opaque(threadIdx.x) & 63;
       const int h = lane >> 5, l32 = lane & 31;
       const int xaddr = (lane ^ 32) << 2;
-      // the scale of an operand column: its own (delta mode) or the wave's (KDA)
-      auto col_max = [&](float m) { return KDA ? wave_max_uniform(m) : pair_max(m, xaddr); };
+      // the scale of an operand column: over the two lanes that hold it
+      auto col_max = [&](float m) { return pair_max(m, xaddr); };
       const float eGC = sF[2 * C];
       float fez;   // delta mode: W = K Z / fez after step 1
       float f_er;  // W holds X' / f_er after step 2
       f32x16 W[2];
-      // Delta mode: every operand scale below is per column (lanes l and l ^ 32
-      // agree on it), and the products of a column carry its factor to where it is
-      // used; KDA: one scale per wave and operand.
+      // Every operand scale below is per column (lanes l and l ^ 32 agree on it),
+      // and the products of a column carry its factor to where it is used.
       // ---- step 1: Y = K Z.  Delta mode, S waves: S <- exp(G_C) S first, so that
       // step 1 and step 3 use the decayed state alike (KDA: the factor folded into
       // Z's conversion; its per-row factors come in step 3) -------------------------

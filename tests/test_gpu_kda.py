@@ -85,6 +85,27 @@ def test_kda_strong_gates_bf16_d128():
     check_build(tk, "kda_strong_bf16_d128")
 
 
+def test_kda_value_channels_of_very_different_scales():
+    """Value channels scaled by powers of two from 2^-20 to 2^17 through the d = 128
+    factor-record path: each column of S depends on its own value channel only and
+    keeps the bf16 bound on its own (the state pass scales its operands per column)."""
+    tk = synth.kda(n_seg=2, n_chain=2)
+    e = np.array([-20, -9, -3, 0, 5, 11, 17])[np.arange(tk.dv) % 7]
+    tk.v = tk.v * np.exp2(e)
+    announce("kda_scaled_v", "chains", tk.n_chain, "segs", len(tk.offsets) - 1)
+    g, U, S = gpu_build(tk, tk.offsets)
+    rg, rU, rS = oracle.build_pairs(KDA, tk.offsets, tk.k, tk.v, tk.beta, tk.log_gate)
+    tol = TOL[tk.dtype]
+    S = np.asarray(S, np.float64)
+    assert np.isfinite(S).all()
+    col_err = np.linalg.norm(S - rS, axis=-2) / np.linalg.norm(rS, axis=-2)  # [seg, chain, column]
+    worst = float(col_err.max())
+    print("  max per-column rel err S %.2e" % worst, flush=True)
+    assert worst <= tol, "column %s: %.3e" % (np.unravel_index(int(col_err.argmax()), col_err.shape), worst)
+    assert_g_close("kda_scaled_v.g", g, rg, tol)
+    assert_units_close("kda_scaled_v.U", U, rU, tol)
+
+
 def test_kda_bf16_d128_ragged():
     """The factor-record path with segments that are not multiples of the
     64-token chunk (tail chunks of 1, 63, 1, 2 and 8 tokens, a 1-token segment)."""
