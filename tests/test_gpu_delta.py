@@ -130,6 +130,16 @@ def test_deltanet_ungated_d128():
     check_build(tk, "deltanet_d128")
 
 
+def test_gdn_strong_and_zero_gates_d128():
+    """Log gates of -30 or 0 per token through the d = 128 bf16 path: chunks whose
+    total decay underflows fp32 (the state is forgotten) next to undecayed ones,
+    tails of 2 tokens."""
+    tk = synth.gdn_cold(n_seg=2, L=130, n_chain=2)
+    r = np.random.default_rng(21)
+    tk.log_gate = np.where(r.random(tk.log_gate.shape) < 0.5, -30.0, 0.0)
+    check_build(tk, "gdn_strong_gates_d128")
+
+
 def test_value_channels_of_very_different_scales():
     """Value channels scaled by powers of two from 2^-20 to 2^17 (the values stay bf16
     numbers).  Each state column depends on its own value channel only, so every
