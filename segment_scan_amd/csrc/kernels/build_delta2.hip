@@ -122,35 +122,37 @@ __global__ __launch_bounds__(64, 2) void delta_prep_kernel(const BuildArgs a, co
   const int lane = threadIdx.x;
   const int h = lane >> 5, l32 = lane & 31;
 
-  // ---- per-token scalars: lane t holds token t; gate prefix by a wave scan --------
-  float beta = 0.f, lg = 0.f;
-  if (lane < nv) {
-    const size_t idx = (size_t)(c0 + lane) * n_chain + chain;
-    beta = load1<false>(a.beta, idx);
-    if (a.lg) lg = load1<false>(a.lg, idx);
-  }
-  const float G = wave_incl_scan(lg);
-  sBeta[lane] = beta;
-
-  // ---- the chunk's keys into LDS (bf16 rows, in the space M takes later) ----------
-  // Instruction i loads rows 4i .. 4i + 3 whole (lane l: row 4i + l / 16,
-  // channels 8 (l % 16) ..), so every load touches only four key rows.
+  // ---- the chunk's keys (bf16 rows, into LDS in the space M takes later), and
+  // weight and gate of token lane: all loads issued before any is waited on.
+  // Instruction i loads rows 4i .. 4i + 3 whole (lane l: row 4i + l / 16, channels
+  // 8 (l % 16) ..); buffer loads over the chunk's valid tokens read zeros past them.
   constexpr int KSP = D + 8;  // 16-bit pitch of the staged rows (272 bytes)
   static_assert(C * KSP * 2 <= C * MP * 4, "key staging fits in the M array");
   bf16_t* sKs = reinterpret_cast<bf16_t*>(sM);
+  const size_t e0 = (size_t)c0 * n_chain + chain;  // element (token c0, chain)
+  uint4 kr[C / 4];
   {
-    const uint4* kb = reinterpret_cast<const uint4*>(a.k);
-    uint4 kr[C / 4];
+    const uint32_t row_bytes = (uint32_t)n_chain * D * 2;
+    const __amdgpu_buffer_rsrc_t rk =
+        buffer_rsrc(reinterpret_cast<const char*>(a.k) + e0 * D * 2, (uint32_t)(nv - 1) * row_bytes + D * 2);
+    const uint32_t vo = (uint32_t)(lane >> 4) * row_bytes + (lane & 15) * 16;
 #pragma unroll
-    for (int i = 0; i < C / 4; ++i) {
-      const int t = 4 * i + (lane >> 4);
-      kr[i] = kb[((size_t)(c0 + min(t, nv - 1)) * n_chain + chain) * (D / 8) + (lane & 15)];
-      if (t >= nv) kr[i] = make_uint4(0, 0, 0, 0);  // tokens past the end must be zero
-    }
-#pragma unroll
-    for (int i = 0; i < C / 4; ++i)
-      *reinterpret_cast<uint4*>(sKs + (4 * i + (lane >> 4)) * KSP + 8 * (lane & 15)) = kr[i];
+    for (int i = 0; i < C / 4; ++i) kr[i] = buffer_load16(rk, vo, 4 * i * row_bytes);
   }
+  const uint32_t sb = (uint32_t)(nv - 1) * n_chain * 2 + 2, so = (uint32_t)lane * n_chain * 2;
+  const float beta =
+      __uint_as_float((uint32_t)buffer_load2(buffer_rsrc(reinterpret_cast<const char*>(a.beta) + e0 * 2, sb), so, 0)
+                      << 16);
+  const float lg =
+      a.lg ? __uint_as_float((uint32_t)buffer_load2(buffer_rsrc(reinterpret_cast<const char*>(a.lg) + e0 * 2, sb), so, 0)
+                             << 16)
+           : 0.f;
+  // ---- per-token scalars: lane t holds token t; gate prefix by a wave scan --------
+  const float G = wave_incl_scan(lg);
+  sBeta[lane] = beta;
+#pragma unroll
+  for (int i = 0; i < C / 4; ++i)
+    *reinterpret_cast<uint4*>(sKs + (4 * i + (lane >> 4)) * KSP + 8 * (lane & 15)) = kr[i];
   __syncthreads();
 
   // ---- Gram K K^T on bf16 MFMA (exact products) ------------------------------------
