@@ -193,6 +193,8 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
   // lanes); every load of the chunk is issued before the first store
   constexpr int NIT = C * (D / 8) / 256;
   static_assert(NIT * 256 == C * (D / 8), "every lane runs every staging step");
+  // (the weights' load joins the others: one memory round trip before the stores)
+  const float beta = (tid < C && tid < nv) ? load1<IN_F32>(a.beta, (size_t)(c0 + tid) * n_chain + chain) : 0.f;
   {
     float x[NIT][8], lg[NIT][8], vx[NIT][8];
 #pragma unroll
@@ -227,7 +229,7 @@ __device__ __forceinline__ void kda_chunk_factors(const BuildArgs& a, int c0, in
       if (db == 0) sMax[t] = mx;
     }
   }
-  if (tid < C) sBeta[tid] = (tid < nv) ? load1<IN_F32>(a.beta, (size_t)(c0 + tid) * n_chain + chain) : 0.f;
+  if (tid < C) sBeta[tid] = beta;
   __syncthreads();
 
   // ---- per-channel prefixes: G_C, and in place of the gates H_t = G_t - mu_t.
