@@ -1,9 +1,10 @@
 """GPU parity: value channels of very different sizes, on every dense build path, on
 the dense composition and on the seam-window step.
 
-The delta rule acts on each value channel on its own (a column of S depends on
-its own channel of v only), so scaling channel j by 2^e_j scales column j of
-every state by the same power of two.  With e_j running from -20 to 17, a
+The recurrences of the linear layers ([youleyou, linear-layer paragraph]; the
+delta rule S <- a (I - b k k^T) S + b k v^T) act on each value channel on its
+own (a column of S depends on its own channel of v only), so scaling channel j
+by 2^e_j scales column j of every state by the same power of two.  With e_j running from -20 to 17, a
 kernel whose fp16 operands share one scale across columns loses the small
 columns; each column of S is therefore held to the tolerance on its own
 (relative Frobenius error per column).  The d = 128 bf16 state pass has its own
